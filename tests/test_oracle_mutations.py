@@ -1,0 +1,145 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin fails.
+
+Each mutation swaps one oracle function for a subtly wrong variant; the named
+pin test must then raise AssertionError. This shows the pins constrain the
+oracle itself rather than restating it.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.e4m3 as e4m3
+import oracle.gemm as gemm
+import oracle.quant as quant
+
+import test_oracle_e4m3 as pins_codec
+import test_oracle_gemm as pins_gemm
+import test_oracle_quant as pins_quant
+
+_orig_encode = e4m3.encode
+
+
+def _encode_ties_away(v):
+    v32 = np.asarray(v, dtype=np.float32)
+    mag = np.minimum(np.abs(v32.astype(np.float64)), 448.0)
+    pos = e4m3._POS
+    hi = np.minimum(np.searchsorted(pos, mag, side="left"), 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    pick_hi = (pos[hi] - mag) <= (mag - pos[lo])  # ties go up
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return code | (np.signbit(v32).astype(np.uint8) << 7)
+
+
+def _encode_no_signed_zero(v):
+    c = _orig_encode(v)
+    return np.where((c & 0x7F) == 0, 0, c).astype(np.uint8)
+
+
+def _quant_group_reciprocal(x, group_size, eps=1e-10):
+    xf = np.asarray(x, np.float32)
+    m, k = xf.shape
+    g = k // group_size
+    xg = xf.reshape(m, g, group_size)
+    amax = np.maximum(np.max(np.abs(xg), axis=2), np.float32(eps)).astype(np.float32)
+    s = (amax / np.float32(448)).astype(np.float32)
+    inv = (np.float32(1) / s).astype(np.float32)
+    codes = _orig_encode((xg * inv[..., None]).astype(np.float32)).reshape(m, k)
+    return codes, s
+
+
+def _quant_group_eps_on_scale(x, group_size, eps=1e-10):
+    xf = np.asarray(x, np.float32)
+    m, k = xf.shape
+    g = k // group_size
+    xg = xf.reshape(m, g, group_size)
+    amax = np.max(np.abs(xg), axis=2).astype(np.float32)
+    s = np.maximum((amax / np.float32(448)).astype(np.float32), np.float32(eps))
+    codes = _orig_encode((xg / s[..., None]).astype(np.float32)).reshape(m, k)
+    return codes, s
+
+
+def _mm_channelwise_no_bias(a, b, sa, sb, bias=None):
+    return _orig_mm_cw(a, b, sa, sb, None)
+
+
+def _mm_channelwise_scales_swapped(a, b, sa, sb, bias=None):
+    out = e4m3.decode(a) @ e4m3.decode(b).T
+    out = out * np.asarray(sb, np.float64)[: out.shape[0], None] if len(sb) >= out.shape[0] else out
+    out = out * np.asarray(sa, np.float64).mean()
+    if bias is not None:
+        out = out + np.asarray(bias, np.float64)[None, :]
+    return out
+
+
+def _mm_blockwise_kblock_scale_index(a, b, sa, sb, bias=None, block_n=128, block_k=128):
+    A = e4m3.decode(a)
+    B = e4m3.decode(b)
+    m, k = A.shape
+    n = B.shape[0]
+    out = np.zeros((m, n))
+    for kb in range(-(-k // block_k)):
+        ks = slice(kb * block_k, min(k, (kb + 1) * block_k))
+        # mistake: weight scale taken from the first N-block for every column
+        out += (A[:, ks] @ B[:, ks].T) * np.asarray(sa, np.float64)[:, kb][:, None] \
+            * np.asarray(sb, np.float64)[0, kb]
+    if bias is not None:
+        out = out + np.asarray(bias, np.float64)[None, :]
+    return out
+
+
+def _padded_rows_floor(m, ra):
+    return (m // ra) * ra
+
+
+def _scales_col_major_wrong_ld(scales, m_pad):
+    scales = np.asarray(scales, np.float32)
+    m, g = scales.shape
+    out = np.full(g * m_pad, np.nan, np.float32)
+    for gi in range(g):
+        out[gi * m:gi * m + m] = scales[:, gi]  # ld = M instead of M_pad
+    return out
+
+
+def _decode_table_subnormal_off():
+    t = e4m3.decode_table()
+    t = t.copy()
+    for c in list(range(1, 8)) + list(range(0x81, 0x88)):
+        t[c] = t[c] / 2.0  # subnormal step taken as 2^-10
+    return t
+
+
+_orig_mm_cw = gemm.scaled_mm_channelwise
+
+MUTATIONS = [
+    ("encode ties away from zero", [(e4m3, "encode", _encode_ties_away), (oracle, "encode", _encode_ties_away),
+                                   (quant, "encode", _encode_ties_away)],
+     pins_codec.test_encode_midpoints_ties_to_even_and_neighbours),
+    ("encode drops the sign of zero", [(e4m3, "encode", _encode_no_signed_zero),
+                                      (oracle, "encode", _encode_no_signed_zero)],
+     pins_codec.test_encode_specific_cases),
+    ("quant multiplies by reciprocal", [(oracle, "quant_per_token_group", _quant_group_reciprocal)],
+     pins_quant.test_worked_examples),
+    ("quant applies eps to the scale", [(oracle, "quant_per_token_group", _quant_group_eps_on_scale)],
+     pins_quant.test_worked_examples),
+    ("channelwise drops bias", [(oracle, "scaled_mm_channelwise", _mm_channelwise_no_bias)],
+     pins_gemm.test_worked_example),
+    ("channelwise mixes up scales", [(oracle, "scaled_mm_channelwise", _mm_channelwise_scales_swapped)],
+     pins_gemm.test_worked_example),
+    ("blockwise uses one N-block scale", [(oracle, "scaled_mm_blockwise", _mm_blockwise_kblock_scale_index)],
+     lambda: pins_gemm.test_blockwise_exact_rational(3, 5, 256, 2, 128)),
+    ("padded rows rounds down", [(oracle, "padded_rows", _padded_rows_floor)],
+     lambda: pins_quant.test_padded_rows(5, 4, 8)),
+    ("col-major scales use ld M", [(oracle, "scales_col_major", _scales_col_major_wrong_ld)],
+     pins_quant.test_scales_col_major_layout),
+    ("decode subnormal step wrong", [(oracle, "decode_table", _decode_table_subnormal_off)],
+     pins_codec.test_landmark_values),
+]
+
+
+@pytest.mark.parametrize("name,patches,pin", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pin_catches_mutation(monkeypatch, name, patches, pin):
+    pin()  # the pin passes on the real oracle
+    for mod, attr, fn in patches:
+        monkeypatch.setattr(mod, attr, fn)
+    with pytest.raises(AssertionError):
+        pin()
