@@ -1,0 +1,250 @@
+// C ABI of the FP8 W8A8 library: argument validation, config resolution and
+// kernel dispatch. Validation runs entirely on the host before any HIP call,
+// so every argument error is reported without touching the device.
+#include <stdarg.h>
+
+#include <cstdio>
+#include <string>
+
+#include "fp8w8a8.h"
+#include "kernels.h"
+#include "tile_table.h"
+
+using namespace fp8w8a8;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return FP8_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FP8_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Common checks of the quantizer arguments.
+int check_quant(const char* fn, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                const uint8_t* q, int64_t ldq, const float* scale, float eps) {
+  if (M < 0 || K < 0) return fail(FP8_ERR_INVALID, "%s: negative size (M=%lld K=%lld)", fn, (long long)M, (long long)K);
+  if (M == 0) return FP8_OK;
+  if (!x || !q || !scale) return fail(FP8_ERR_INVALID, "%s: null pointer", fn);
+  if (K == 0 || K % 16 != 0) return fail(FP8_ERR_INVALID, "%s: K=%lld must be a positive multiple of 16", fn, (long long)K);
+  if (ldx < K || ldq < K) return fail(FP8_ERR_INVALID, "%s: leading dimension smaller than K", fn);
+  if (ldx % 8 != 0 || ldq % 16 != 0 || !aligned(x, 16) || !aligned(q, 16))
+    return fail(FP8_ERR_INVALID, "%s: rows of x and q must be 16-byte aligned", fn);
+  if (!aligned(scale, 4)) return fail(FP8_ERR_INVALID, "%s: scale must be 4-byte aligned", fn);
+  if (!(eps >= 0.0f)) return fail(FP8_ERR_INVALID, "%s: eps must be >= 0", fn);
+  return FP8_OK;
+}
+
+int check_gemm(const char* fn, const uint8_t* a, const uint8_t* b, const float* sa,
+               const float* sb, const uint16_t* bias, const uint16_t* out, int64_t M, int64_t N,
+               int64_t K, int64_t lda, int64_t ldb, int64_t ldc) {
+  if (M < 0 || N < 0 || K < 0) return fail(FP8_ERR_INVALID, "%s: negative size", fn);
+  if (M == 0) return FP8_OK;
+  if (!a || !b || !sa || !sb || !out) return fail(FP8_ERR_INVALID, "%s: null pointer", fn);
+  if (N == 0 || K == 0 || K % 16 != 0)
+    return fail(FP8_ERR_INVALID, "%s: N must be positive and K a positive multiple of 16 (N=%lld K=%lld)", fn,
+                (long long)N, (long long)K);
+  if (lda < K || ldb < K || ldc < N) return fail(FP8_ERR_INVALID, "%s: leading dimension too small", fn);
+  if (lda % 16 || ldb % 16 || ldc % 8 || !aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16))
+    return fail(FP8_ERR_INVALID, "%s: rows of a, b and out must be 16-byte aligned", fn);
+  if (!aligned(sa, 4) || !aligned(sb, 16)) return fail(FP8_ERR_INVALID, "%s: misaligned scales", fn);
+  if (bias && !aligned(bias, 8)) return fail(FP8_ERR_INVALID, "%s: bias must be 8-byte aligned", fn);
+  return FP8_OK;
+}
+
+int resolve_config(int kind, int64_t M, int64_t N, int64_t K, const fp8_tile_config* cfg,
+                   fp8_tile_config* out) {
+  if (!cfg || cfg->variant == FP8_VARIANT_DEFAULT) {
+    lookup_config(kind, N, K, M, out);
+    // a table entry snapped from a nearby M may not fit this M
+    if (out->variant == FP8_VARIANT_SKINNY && M > variant_info(FP8_VARIANT_SKINNY).bm)
+      default_config(kind, N, K, M, out);
+    return FP8_OK;
+  }
+  const VariantInfo vi = variant_info(cfg->variant);
+  if (!vi.exists) return fail(FP8_ERR_INVALID, "unknown kernel variant %d", cfg->variant);
+  if (cfg->split_k < 1) return fail(FP8_ERR_INVALID, "split_k must be >= 1");
+  if (cfg->variant == FP8_VARIANT_SKINNY && (M > vi.bm || cfg->split_k != 1))
+    return fail(FP8_ERR_INVALID, "the skinny variant takes M <= %d and split_k == 1", vi.bm);
+  *out = *cfg;
+  out->bm = vi.bm; out->bn = vi.bn; out->bk = vi.bk; out->waves = vi.waves;
+  return FP8_OK;
+}
+
+// Effective split count: never more splits than 128-deep K steps.
+void split_plan(int64_t K, int split_k, int* splits, int* per) {
+  const int64_t kt = (K + 127) / 128;
+  int64_t s = split_k < 1 ? 1 : split_k;
+  if (s > kt) s = kt;
+  const int64_t p = (kt + s - 1) / s;
+  *per = (int)p;
+  *splits = (int)((kt + p - 1) / p);
+}
+
+int run_gemm(const char* fn, int kind, const uint8_t* a, const uint8_t* b, const float* sa,
+             int64_t sa_ld, const float* sb, const uint16_t* bias, uint16_t* out, int64_t M,
+             int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, void* ws,
+             size_t ws_bytes, const fp8_tile_config* cfg_in, hipStream_t stream) {
+  fp8_tile_config cfg;
+  int st = resolve_config(kind, M, N, K, cfg_in, &cfg);
+  if (st) return st;
+  GemmArgs p{};
+  p.a = a; p.b = b; p.sa = sa; p.sa_ld = sa_ld; p.sb = sb; p.bias = bias; p.out = out;
+  p.M = M; p.N = N; p.K = K; p.lda = lda; p.ldb = ldb; p.ldc = ldc;
+  int splits = 1, per = (int)((K + 127) / 128);
+  if (cfg.variant != FP8_VARIANT_SKINNY) split_plan(K, cfg.split_k, &splits, &per);
+  p.split_k = splits;
+  p.k_tiles_per_split = per;
+  if (splits > 1) {
+    // ws layout: kCounterBytes of arrival counters (zero between calls), then partials
+    const size_t need = variant_workspace_bytes(cfg.variant, splits, M, N);
+    if (!ws || ws_bytes < need)
+      return fail(FP8_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
+    if (!aligned(ws, 256)) return fail(FP8_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
+    const int64_t tiles = variant_tiles(cfg.variant, M, N);
+    if (tiles > kMaxSplitTiles)
+      return fail(FP8_ERR_UNSUPPORTED, "%s: split-K over %lld output tiles (max %lld)", fn,
+                  (long long)tiles, (long long)kMaxSplitTiles);
+    p.ws_count = static_cast<int*>(ws);
+    p.ws_part = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
+  }
+  return hip_status(launch_gemm(kind, cfg.variant, p, stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t fp8_padded_rows(int64_t M, int32_t row_alignment) {
+  if (M < 0 || row_alignment < 1) return -1;
+  return (M + row_alignment - 1) / row_alignment * row_alignment;
+}
+
+int fp8_quant_per_token(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                        int64_t ldq, float* scale, float eps, hipStream_t stream) {
+  int st = check_quant("fp8_quant_per_token", x, M, K, ldx, q, ldq, scale, eps);
+  if (st) return st;
+  if (M == 0) return ok();
+  return hip_status(launch_quant_per_token(x, M, K, ldx, q, ldq, scale, eps, stream),
+                    "fp8_quant_per_token");
+}
+
+int fp8_quant_per_token_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                              int32_t group_size, int32_t row_alignment, uint8_t* q, int64_t ldq,
+                              float* scale, float eps, hipStream_t stream) {
+  const char* fn = "fp8_quant_per_token_group";
+  if (row_alignment < 1) return fail(FP8_ERR_INVALID, "%s: row_alignment must be >= 1", fn);
+  if (group_size <= 0) return fail(FP8_ERR_INVALID, "%s: group_size must be positive", fn);
+  if (K % group_size != 0)
+    return fail(FP8_ERR_INVALID, "%s: K=%lld must be divisible by group_size=%d", fn, (long long)K, group_size);
+  if (!(group_size == 16 || group_size == 32 || group_size == 64 || group_size == 128))
+    return fail(FP8_ERR_UNSUPPORTED, "%s: group_size %d not in {16, 32, 64, 128}", fn, group_size);
+  int st = check_quant(fn, x, M, K, ldx, q, ldq, scale, eps);
+  if (st) return st;
+  if (M == 0) return ok();
+  const int64_t m_pad = fp8_padded_rows(M, row_alignment);
+  return hip_status(launch_quant_per_token_group(x, M, K, ldx, group_size, m_pad, q, ldq, scale,
+                                                 eps, stream),
+                    fn);
+}
+
+int fp8_scaled_mm_channelwise_ex(const uint8_t* a, const uint8_t* b, const float* a_scale,
+                                 const float* b_scale, const uint16_t* bias, uint16_t* out,
+                                 int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                                 int64_t ldc, void* ws, size_t ws_bytes,
+                                 const fp8_tile_config* cfg, hipStream_t stream) {
+  const char* fn = "fp8_scaled_mm_channelwise";
+  int st = check_gemm(fn, a, b, a_scale, b_scale, bias, out, M, N, K, lda, ldb, ldc);
+  if (st) return st;
+  if (M == 0) return ok();
+  return run_gemm(fn, FP8_KIND_CHANNELWISE, a, b, a_scale, 0, b_scale, bias, out, M, N, K, lda,
+                  ldb, ldc, ws, ws_bytes, cfg, stream);
+}
+
+int fp8_scaled_mm_channelwise(const uint8_t* a, const uint8_t* b, const float* a_scale,
+                              const float* b_scale, const uint16_t* bias, uint16_t* out,
+                              int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                              int64_t ldc, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return fp8_scaled_mm_channelwise_ex(a, b, a_scale, b_scale, bias, out, M, N, K, lda, ldb, ldc,
+                                      ws, ws_bytes, nullptr, stream);
+}
+
+int fp8_scaled_mm_blockwise_ex(const uint8_t* a, const uint8_t* b, const float* a_scale,
+                               int64_t a_scale_ld, const float* b_scale, const uint16_t* bias,
+                               uint16_t* out, int64_t M, int64_t N, int64_t K, int64_t lda,
+                               int64_t ldb, int64_t ldc, void* ws, size_t ws_bytes,
+                               const fp8_tile_config* cfg, hipStream_t stream) {
+  const char* fn = "fp8_scaled_mm_blockwise";
+  int st = check_gemm(fn, a, b, a_scale, b_scale, bias, out, M, N, K, lda, ldb, ldc);
+  if (st) return st;
+  if (M == 0) return ok();
+  if (N % 128 != 0 || K % 128 != 0)
+    return fail(FP8_ERR_UNSUPPORTED, "%s: N=%lld and K=%lld must be multiples of 128", fn, (long long)N,
+                (long long)K);
+  if (a_scale_ld < M) return fail(FP8_ERR_INVALID, "%s: a_scale_ld=%lld < M=%lld", fn, (long long)a_scale_ld, (long long)M);
+  return run_gemm(fn, FP8_KIND_BLOCKWISE, a, b, a_scale, a_scale_ld, b_scale, bias, out, M, N, K,
+                  lda, ldb, ldc, ws, ws_bytes, cfg, stream);
+}
+
+int fp8_scaled_mm_blockwise(const uint8_t* a, const uint8_t* b, const float* a_scale,
+                            int64_t a_scale_ld, const float* b_scale, const uint16_t* bias,
+                            uint16_t* out, int64_t M, int64_t N, int64_t K, int64_t lda,
+                            int64_t ldb, int64_t ldc, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  return fp8_scaled_mm_blockwise_ex(a, b, a_scale, a_scale_ld, b_scale, bias, out, M, N, K, lda,
+                                    ldb, ldc, ws, ws_bytes, nullptr, stream);
+}
+
+size_t fp8_scaled_mm_workspace_size(int32_t kind, int64_t M, int64_t N, int64_t K,
+                                    const fp8_tile_config* cfg_in) {
+  if ((kind != FP8_KIND_CHANNELWISE && kind != FP8_KIND_BLOCKWISE) || M < 0 || N < 0 || K < 0)
+    return (size_t)-1;
+  if (M == 0 || N == 0 || K == 0) return 0;
+  fp8_tile_config cfg;
+  if (resolve_config(kind, M, N, K, cfg_in, &cfg)) return (size_t)-1;
+  if (cfg.variant == FP8_VARIANT_SKINNY) return 0;
+  int splits, per;
+  split_plan(K, cfg.split_k, &splits, &per);
+  return variant_workspace_bytes(cfg.variant, splits, M, N);
+}
+
+int fp8_tile_config_lookup(int32_t kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* out) {
+  if ((kind != FP8_KIND_CHANNELWISE && kind != FP8_KIND_BLOCKWISE) || N <= 0 || K <= 0 || M < 0 || !out)
+    return fail(FP8_ERR_INVALID, "fp8_tile_config_lookup: bad arguments");
+  return lookup_config(kind, N, K, M, out);
+}
+
+int fp8_tile_config_default(int32_t kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* out) {
+  if ((kind != FP8_KIND_CHANNELWISE && kind != FP8_KIND_BLOCKWISE) || N <= 0 || K <= 0 || M < 0 || !out)
+    return fail(FP8_ERR_INVALID, "fp8_tile_config_default: bad arguments");
+  return default_config(kind, N, K, M, out);
+}
+
+int fp8_tile_config_set_dir(const char* dir) {
+  set_config_dir(dir);
+  return FP8_OK;
+}
+
+const char* fp8_last_error(void) { return g_last_error.c_str(); }
+
+int32_t fp8_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Host-side launchers of the gfx950 kernels (arguments validated by the caller).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8w8a8 {
+
+hipError_t launch_quant_per_token(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                  uint8_t* q, int64_t ldq, float* scale, float eps,
+                                  hipStream_t stream);
+
+hipError_t launch_quant_per_token_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                        int group_size, int64_t m_pad, uint8_t* q, int64_t ldq,
+                                        float* scale, float eps, hipStream_t stream);
+
+enum GemmKind { kChannelwise = 0, kBlockwise = 1 };
+
+struct GemmArgs {
+  const uint8_t* a;
+  const uint8_t* b;
+  const float* sa;     // channelwise: [M]; blockwise: column-major, (m, kb) at kb*sa_ld + m
+  int64_t sa_ld;
+  const float* sb;     // channelwise: [N]; blockwise: [N/128][K/128]
+  const uint16_t* bias;  // [N] or null
+  uint16_t* out;
+  int64_t M, N, K, lda, ldb, ldc;
+  float* ws_part;      // split-K partial tiles (null when split_k == 1)
+  int* ws_count;       // split-K arrival counters, one per output tile
+  int split_k;
+  int k_tiles_per_split;  // 128-deep K steps handled by one split
+};
+
+// Geometry of a compiled kernel variant.
+struct VariantInfo {
+  int bm, bn, bk, waves;
+  bool exists;
+};
+VariantInfo variant_info(int variant);
+
+// Number of output tiles the variant launches for (M, N).
+int64_t variant_tiles(int variant, int64_t M, int64_t N);
+
+// Split-K workspace layout: a fixed region of arrival counters (one int per
+// output tile, at most kMaxSplitTiles tiles) at the start, then the fp32
+// partial tiles. The counter region sits at the same place for every shape,
+// so the all-zero state each call leaves behind holds for the next call
+// whatever its shape.
+constexpr int64_t kMaxSplitTiles = 65536;
+constexpr size_t kCounterBytes = (size_t)kMaxSplitTiles * sizeof(int);
+
+// Bytes of split-K workspace for (variant, split_k, M, N); 0 when split_k == 1.
+size_t variant_workspace_bytes(int variant, int split_k, int64_t M, int64_t N);
+
+hipError_t launch_gemm(int kind, int variant, const GemmArgs& args, hipStream_t stream);
+
+}  // namespace fp8w8a8

@@ -1,0 +1,242 @@
+"""Torch-facing wrappers over the C ABI (marshalling only).
+
+torch provides device memory and the current HIP stream; every computation
+runs in the library's gfx950 kernels. FP8 tensors are raw OCP E4M3 codes held
+as ``torch.uint8`` (``torch.float8_e4m3fn`` tensors are accepted and viewed as
+bytes).
+
+User-facing calls mirror the pages' functions:
+* ``linear_channelwise`` -- the channelwise branch of ``apply_fp8_linear``
+  (PR 34331 digest, "Key source excerpts"): per-token activation quant, then
+  the scaled GEMM with per-channel weight scales and a fused bias.
+* ``quant_per_token_group`` -- the row-padded per-token-group quant (PR 27896
+  digest, "Key source excerpts"): returns codes [M_pad, K] and scales as an
+  [M_pad, K/G] view of [K/G, M_pad] storage.
+* ``linear_blockwise`` -- the blockwise linear of the same digest, with the
+  row slice and the bias folded into the GEMM's epilogue.
+"""
+import ctypes
+import threading
+
+import torch
+
+from . import _lib
+from ._lib import KIND_BLOCKWISE, KIND_CHANNELWISE, TileConfig, VARIANTS, check
+
+__all__ = [
+    "padded_rows", "quant_per_token", "quant_per_token_group", "scaled_mm_channelwise",
+    "scaled_mm_blockwise", "linear_channelwise", "linear_blockwise", "tile_config",
+    "default_tile_config", "set_config_dir", "workspace_bytes", "make_config",
+]
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _as_codes(t, name):
+    if t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn), got {t.dtype}")
+    return t
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def make_config(variant, split_k=1):
+    """TileConfig for an explicit kernel variant name (see _lib.VARIANTS)."""
+    return TileConfig(VARIANTS[variant] if isinstance(variant, str) else int(variant), 0, 0, 0,
+                      int(split_k), 0)
+
+
+# ---------------------------------------------------------------- workspace
+class _WorkspacePool:
+    """One zero-filled split-K workspace per (device, stream), grown on demand.
+    The kernels leave the arrival counters at zero after every call."""
+
+    def __init__(self):
+        self._lock = threading.Lock()
+        self._bufs = {}
+
+    def get(self, device, nbytes):
+        if nbytes == 0:
+            return None
+        key = (device, torch.cuda.current_stream(device).cuda_stream)
+        with self._lock:
+            buf = self._bufs.get(key)
+            if buf is None or buf.numel() < nbytes:
+                size = max(nbytes, 1 << 20)
+                buf = torch.zeros(size, dtype=torch.uint8, device=device)
+                self._bufs[key] = buf
+            return buf
+
+
+_ws = _WorkspacePool()
+
+
+def workspace_bytes(kind, m, n, k, config=None):
+    cfg = ctypes.byref(config) if config is not None else None
+    v = _lib.load().fp8_scaled_mm_workspace_size(kind, m, n, k, cfg)
+    if v == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid arguments for workspace size")
+    return v
+
+
+# ---------------------------------------------------------------- quantization
+def padded_rows(m, row_alignment=4):
+    v = _lib.load().fp8_padded_rows(m, row_alignment)
+    if v < 0:
+        raise ValueError("invalid M or row_alignment")
+    return v
+
+
+def quant_per_token(x, eps=1e-10, out=None, scale=None):
+    """bf16 [M, K] -> (E4M3 codes uint8 [M, K], fp32 scales [M])."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise TypeError("x must be a 2-D bf16 tensor")
+    _need_cuda(x)
+    m, k = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    q = out if out is not None else torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    s = scale if scale is not None else torch.empty((m,), dtype=torch.float32, device=x.device)
+    check(_lib.load().fp8_quant_per_token(_p(x), m, k, x.stride(0), _p(q), q.stride(0), _p(s),
+                                          float(eps), _stream(x)))
+    return q, s
+
+
+def quant_per_token_group(x, group_size=128, eps=1e-10, row_alignment=4, out=None,
+                          scale_storage=None):
+    """bf16 [M, K] -> (codes uint8 [M_pad, K], scales fp32 [M_pad, K/G] with
+    stride (1, M_pad)). Rows M..M_pad-1 of both are left unwritten."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise TypeError("x must be a 2-D bf16 tensor")
+    _need_cuda(x)
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    m, k = x.shape
+    if group_size <= 0 or k % group_size != 0:
+        raise ValueError("the last dimension of x must be divisible by group_size")
+    m_pad = padded_rows(m, row_alignment)
+    q = out if out is not None else torch.empty((m_pad, k), dtype=torch.uint8, device=x.device)
+    st = scale_storage if scale_storage is not None else torch.empty(
+        (k // group_size, m_pad), dtype=torch.float32, device=x.device)
+    check(_lib.load().fp8_quant_per_token_group(_p(x), m, k, x.stride(0), group_size,
+                                                row_alignment, _p(q), q.stride(0), _p(st),
+                                                float(eps), _stream(x)))
+    return q, st.transpose(0, 1)
+
+
+# ---------------------------------------------------------------- GEMMs
+def scaled_mm_channelwise(a, b, a_scale, b_scale, bias=None, out=None, config=None):
+    """a codes [M, K], b codes [N, K] (K-contiguous), a_scale fp32 [M],
+    b_scale fp32 [N], bias bf16 [N] or None -> bf16 [M, N]."""
+    a = _as_codes(a, "a")
+    b = _as_codes(b, "b")
+    _need_cuda(a, b, a_scale, b_scale, bias)
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k:
+        raise ValueError("a and b disagree on K")
+    if a_scale.dtype != torch.float32 or b_scale.dtype != torch.float32:
+        raise TypeError("scales must be fp32")
+    if a_scale.numel() < m or b_scale.numel() < n or not a_scale.is_contiguous() or \
+            not b_scale.is_contiguous():
+        raise ValueError("a_scale [M] and b_scale [N] must be contiguous")
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() < n or
+                             not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous bf16 [N] tensor")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    cfg = config if config is not None else TileConfig(-1, 0, 0, 0, 1, 0)
+    nws = workspace_bytes(KIND_CHANNELWISE, m, n, k, cfg)
+    ws = _ws.get(a.device, nws)
+    check(_lib.load().fp8_scaled_mm_channelwise_ex(
+        _p(a), _p(b), _p(a_scale), _p(b_scale), _p(bias), _p(out), m, n, k, a.stride(0),
+        b.stride(0), out.stride(0), _p(ws), nws, ctypes.byref(cfg), _stream(a)))
+    return out
+
+
+def scaled_mm_blockwise(a, b, a_scale, b_scale, bias=None, m=None, out=None, config=None):
+    """a codes [>=M, K]; b codes [N, K]; a_scale an [M_pad, K/128] view with
+    stride(0) == 1 (as returned by quant_per_token_group); b_scale fp32
+    [N/128, K/128]; only the first m rows (default: all of a) are computed."""
+    a = _as_codes(a, "a")
+    b = _as_codes(b, "b")
+    _need_cuda(a, b, a_scale, b_scale, bias)
+    m = a.shape[0] if m is None else int(m)
+    k = a.shape[1]
+    n = b.shape[0]
+    if b.shape[1] != k:
+        raise ValueError("a and b disagree on K")
+    if a_scale.dtype != torch.float32 or b_scale.dtype != torch.float32:
+        raise TypeError("scales must be fp32")
+    if a_scale.dim() != 2 or a_scale.stride(0) != 1:
+        raise ValueError("a_scale must be column-major ([M_pad, K/128] with stride(0) == 1)")
+    if not b_scale.is_contiguous():
+        raise ValueError("b_scale must be contiguous [N/128, K/128]")
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() < n or
+                             not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous bf16 [N] tensor")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    cfg = config if config is not None else TileConfig(-1, 0, 0, 0, 1, 0)
+    nws = workspace_bytes(KIND_BLOCKWISE, m, n, k, cfg)
+    ws = _ws.get(a.device, nws)
+    check(_lib.load().fp8_scaled_mm_blockwise_ex(
+        _p(a), _p(b), _p(a_scale), a_scale.stride(1), _p(b_scale), _p(bias), _p(out), m, n, k,
+        a.stride(0), b.stride(0), out.stride(0), _p(ws), nws, ctypes.byref(cfg), _stream(a)))
+    return out
+
+
+# ---------------------------------------------------------------- linears
+def linear_channelwise(x, w_q, w_s, bias=None, eps=1e-10, config=None):
+    """y = x @ W^T with per-token FP8 activation quant and per-channel weight
+    scales. x bf16 [..., K]; w_q codes [N, K]; w_s fp32 [N]; bias bf16 [N]."""
+    shape = x.shape
+    x2 = x.reshape(-1, shape[-1])
+    q, s = quant_per_token(x2, eps)
+    out = scaled_mm_channelwise(q, w_q, s, w_s, bias, config=config)
+    return out.view(*shape[:-1], w_q.shape[0])
+
+
+def linear_blockwise(x, w_q, w_s, bias=None, block_size=(128, 128), eps=1e-10,
+                     row_alignment=4, config=None):
+    """Blockwise FP8 linear: group-128 activation quant into row-padded buffers,
+    then the blockwise GEMM over the first M rows with the bias fused."""
+    if tuple(block_size) != (128, 128):
+        raise _lib.Fp8Error(_lib.FP8_ERR_UNSUPPORTED, "only 128x128 weight blocks are supported")
+    shape = x.shape
+    x2 = x.reshape(-1, shape[-1])
+    q, s = quant_per_token_group(x2, block_size[1], eps, row_alignment)
+    out = scaled_mm_blockwise(q, w_q, s, w_s, bias, m=x2.shape[0], config=config)
+    return out.view(*shape[:-1], w_q.shape[0])
+
+
+# ---------------------------------------------------------------- tile table
+def tile_config(kind, n, k, m):
+    """(config dict, hit) for the table lookup of (kind, N, K, M)."""
+    c = TileConfig()
+    r = _lib.load().fp8_tile_config_lookup(kind, n, k, m, ctypes.byref(c))
+    if r < 0:
+        check(r)
+    return c.as_dict(), bool(r == 1)
+
+
+def default_tile_config(kind, n, k, m):
+    c = TileConfig()
+    check(_lib.load().fp8_tile_config_default(kind, n, k, m, ctypes.byref(c)))
+    return c.as_dict()
+
+
+def set_config_dir(path):
+    _lib.load().fp8_tile_config_set_dir(None if path is None else str(path).encode())

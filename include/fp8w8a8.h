@@ -1,0 +1,242 @@
+/*
+ * fp8w8a8.h -- C ABI of the MI355X (gfx950) FP8 W8A8 quantized-linear library.
+ *
+ * The library implements the FP8 W8A8 linear hot path described by three
+ * prhub.com.cn digests of sglang pull requests:
+ *   [PR34331] "Tune FP8 GEMM Triton tiles on L40S and enable them by default"
+ *             -- channelwise scaled GEMM and its per-(N, K, device) tile table
+ *             with nearest-M lookup, null entries and a kill switch.
+ *   [PR31340] "Fix FP8 Triton dtype selection on A100"
+ *             -- the FP8 format is torch's float8_e4m3fn (OCP E4M3).
+ *   [PR27896] "Remove the per-call padding overhead of the FP8 blockwise GEMM"
+ *             -- row-padded per-token-group quantization with column-major
+ *             scales feeding a blockwise (1x128 activation, 128x128 weight)
+ *             scaled GEMM.
+ *
+ * Conventions for every function below
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates device memory and never frees caller memory.
+ *   - bf16 values are passed as their raw 16-bit patterns (uint16_t).
+ *   - FP8 values are raw OCP E4M3 codes (uint8_t): sign, 4 exponent bits with
+ *     bias 7, 3 mantissa bits; no infinities; 0x7F/0xFF are NaN; max 448.
+ *   - Matrices are row-major with an explicit leading dimension (elements).
+ *     Base pointers and leading dimensions must keep every row 16-byte aligned.
+ *   - Every compute call is asynchronous on `stream` (a hipStream_t; NULL is
+ *     the default stream) and returns a status code; it never throws or aborts.
+ *     Argument validation happens on the host before anything is launched.
+ *   - M == 0 is a successful no-op.
+ *
+ * Status codes: FP8_OK (0); FP8_ERR_INVALID (-1) bad argument (null pointer,
+ * negative size, misalignment, K not a multiple of the group size, leading
+ * dimension too small); FP8_ERR_UNSUPPORTED (-2) a valid request this build
+ * has no kernel for (group size outside {16,32,64,128}, blockwise N or K not a
+ * multiple of 128, block size other than 128x128); FP8_ERR_WORKSPACE (-3)
+ * workspace too small; FP8_ERR_HIP (-4) a HIP runtime error. fp8_last_error()
+ * returns a message for the last failure on the calling thread.
+ */
+#ifndef FP8W8A8_H
+#define FP8W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  FP8_OK = 0,
+  FP8_ERR_INVALID = -1,
+  FP8_ERR_UNSUPPORTED = -2,
+  FP8_ERR_WORKSPACE = -3,
+  FP8_ERR_HIP = -4,
+};
+
+enum { FP8_KIND_CHANNELWISE = 0, FP8_KIND_BLOCKWISE = 1 };
+
+/* Kernel variants a tile config can name. */
+enum {
+  FP8_VARIANT_DEFAULT = -1, /* let the library choose */
+  FP8_VARIANT_SKINNY = 0,   /* M <= 16 rows: one 16-row MFMA tile, weight streamed once */
+  FP8_VARIANT_T64x64 = 1,   /* 64x64 block tile, 4 waves */
+  FP8_VARIANT_T128x128 = 2, /* 128x128 block tile, 4 waves */
+  FP8_VARIANT_T256x128 = 3, /* 256x128 block tile, 8 waves */
+  FP8_VARIANT_T256x256 = 4, /* 256x256 block tile, 8 waves */
+  FP8_VARIANT_COUNT = 5,
+};
+
+/* One tile configuration of the scaled GEMM. The PR34331 digest ("Key source
+ * excerpts") keys a tile by block sizes M/N/K plus launch parameters; here
+ * `variant` names a compiled gfx950 kernel (its block sizes are fixed and are
+ * reported in bm/bn/bk/waves) and `split_k` divides the K loop over that many
+ * workgroups whose fp32 partial sums are reduced inside the same launch. */
+typedef struct fp8_tile_config {
+  int32_t variant;
+  int32_t bm, bn, bk; /* block tile (filled in by the library) */
+  int32_t split_k;    /* >= 1 */
+  int32_t waves;      /* waves per workgroup (filled in by the library) */
+} fp8_tile_config;
+
+/* ------------------------------------------------------------------------ */
+/* Quantization                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Rows of the row-padded buffers: ceil(M / row_alignment) * row_alignment.
+ * [PR27896, "Key source excerpts": the row-padded quant aligns the row count
+ * up to row_alignment, 4 by default.] Returns -1 if M < 0 or row_alignment < 1. */
+int64_t fp8_padded_rows(int64_t M, int32_t row_alignment);
+
+/* Dynamic per-token FP8 quantization (one scale per row).
+ * For each row m < M:  s[m] = fp32(max(max_k |x[m,k]|, eps) / 448),
+ *                      q[m,k] = E4M3_RNE(clamp(fp32(x[m,k] / s[m]), -448, 448)).
+ * This is the activation quantization that feeds the channelwise GEMM of
+ * [PR34331, "Key source excerpts", apply_fp8_linear], where the quantized
+ * input and its per-token scale arrive already made; it is the per-token-group
+ * quantization below with one group spanning the row.
+ *   x      bf16 [M][ldx], ldx >= K         (input, read only)
+ *   q      E4M3 [M][ldq], ldq >= K         (output codes)
+ *   scale  fp32 [M]                         (output scales)
+ *   eps    clamp of the row absmax (1e-10 in the pages' quantizer)
+ * K must be a positive multiple of 16. */
+int fp8_quant_per_token(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                        uint8_t* q, int64_t ldq, float* scale, float eps,
+                        hipStream_t stream);
+
+/* Dynamic per-token-group FP8 quantization into row-padded buffers.
+ * [PR27896, "Implementation" step 1 and "Key source excerpts",
+ * the row-padded per-token-group quant function; "Risks and impact" for the
+ * untouched tail rows.] For each row m < M and group g < K/G:
+ *   s = fp32(max(max_{k in g} |x[m,k]|, eps) / 448),  scale[g*M_pad + m] = s,
+ *   q[m,k] = E4M3_RNE(clamp(fp32(x[m,k] / s), -448, 448))  for k in group g,
+ * with M_pad = fp8_padded_rows(M, row_alignment). The scales are therefore
+ * column-major: logically (M_pad, K/G) with unit stride along rows.
+ * Rows M..M_pad-1 of q and of every scale column are NOT written.
+ *   x            bf16 [M][ldx], ldx >= K
+ *   group_size   G in {16, 32, 64, 128}  (others: FP8_ERR_UNSUPPORTED)
+ *   row_alignment >= 1 (the pages use 4)
+ *   q            E4M3 [M_pad][ldq], ldq >= K (only rows < M written)
+ *   scale        fp32 [K/G][M_pad]
+ * K must be a positive multiple of G. */
+int fp8_quant_per_token_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                              int32_t group_size, int32_t row_alignment,
+                              uint8_t* q, int64_t ldq, float* scale, float eps,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Scaled GEMMs                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Channelwise FP8 scaled GEMM with fused epilogue.
+ * [PR34331, "Key source excerpts", apply_fp8_linear: the scaled matmul takes
+ * the quantized input, the FP8 weight, the per-token input scale, the
+ * per-channel weight scale, the output dtype and a fused bias.]
+ *   out[m,n] = bf16_RNE( a_scale[m] * b_scale[n] * sum_k dec(a[m,k]) dec(b[n,k])
+ *                        + bias[n] ),   m < M, n < N,
+ * accumulated in fp32 on the FP8 matrix cores.
+ *   a        E4M3 [M][lda], lda >= K            (activations)
+ *   b        E4M3 [N][ldb], ldb >= K            (weight, K-contiguous; the
+ *            pages view it as [K, N]: N = its second dim, K its first)
+ *   a_scale  fp32 [M];  b_scale fp32 [N]
+ *   bias     bf16 [N] or NULL
+ *   out      bf16 [M][ldc], ldc >= N            (only rows < M written)
+ *   ws, ws_bytes  split-K workspace (see fp8_scaled_mm_workspace_size), 256-byte
+ *            aligned; may be NULL/0 when the chosen config needs none. Its
+ *            first 256 KiB hold per-tile arrival counters and must be
+ *            zero-filled before the first use; every call leaves them zero
+ *            again, so one workspace serves calls of any shape. The rest holds
+ *            fp32 partial tiles and needs no initialisation. Calls that run
+ *            concurrently must not share one workspace.
+ * K must be a positive multiple of 16. */
+int fp8_scaled_mm_channelwise(const uint8_t* a, const uint8_t* b,
+                              const float* a_scale, const float* b_scale,
+                              const uint16_t* bias, uint16_t* out,
+                              int64_t M, int64_t N, int64_t K,
+                              int64_t lda, int64_t ldb, int64_t ldc,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* As fp8_scaled_mm_channelwise with an explicit tile config (NULL or variant
+ * FP8_VARIANT_DEFAULT = table lookup / default heuristic). Used by the sweep. */
+int fp8_scaled_mm_channelwise_ex(const uint8_t* a, const uint8_t* b,
+                                 const float* a_scale, const float* b_scale,
+                                 const uint16_t* bias, uint16_t* out,
+                                 int64_t M, int64_t N, int64_t K,
+                                 int64_t lda, int64_t ldb, int64_t ldc,
+                                 void* ws, size_t ws_bytes,
+                                 const fp8_tile_config* cfg, hipStream_t stream);
+
+/* Blockwise FP8 scaled GEMM (1x128 activation groups, 128x128 weight blocks).
+ * [PR27896, "Key source excerpts", the blockwise linear: group-128
+ * activation quant into row-padded buffers, a blockwise scaled matmul of the
+ * [N, K] weight with block_size [128, 128], rows beyond M dropped, bias added.]
+ *   out[m,n] = bf16_RNE( sum_kb a_scale[kb*a_scale_ld + m] * b_scale[(n/128)*KB + kb]
+ *                        * sum_{k in block kb} dec(a[m,k]) dec(b[n,k]) + bias[n] ),
+ *   KB = K/128, m < M, n < N. The per-block partial sum is promoted to fp32
+ *   and scaled before it joins the accumulator.
+ *   a            E4M3 [>=M][lda]   (rows >= M are never read)
+ *   a_scale      fp32 column-major, (m, kb) at kb*a_scale_ld + m;
+ *                a_scale_ld >= M (the row-padded M_pad of the quantizer)
+ *   b            E4M3 [N][ldb];  b_scale fp32 [N/128][K/128] row-major
+ *   bias, out, ws as for the channelwise GEMM.
+ * N and K must be multiples of 128 (else FP8_ERR_UNSUPPORTED). */
+int fp8_scaled_mm_blockwise(const uint8_t* a, const uint8_t* b,
+                            const float* a_scale, int64_t a_scale_ld,
+                            const float* b_scale,
+                            const uint16_t* bias, uint16_t* out,
+                            int64_t M, int64_t N, int64_t K,
+                            int64_t lda, int64_t ldb, int64_t ldc,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+int fp8_scaled_mm_blockwise_ex(const uint8_t* a, const uint8_t* b,
+                               const float* a_scale, int64_t a_scale_ld,
+                               const float* b_scale,
+                               const uint16_t* bias, uint16_t* out,
+                               int64_t M, int64_t N, int64_t K,
+                               int64_t lda, int64_t ldb, int64_t ldc,
+                               void* ws, size_t ws_bytes,
+                               const fp8_tile_config* cfg, hipStream_t stream);
+
+/* Workspace bytes the GEMM of `kind` needs for (M, N, K) with `cfg` (NULL =
+ * the config the library would pick). 0 when no workspace is needed.
+ * Returns (size_t)-1 on invalid arguments. */
+size_t fp8_scaled_mm_workspace_size(int32_t kind, int64_t M, int64_t N, int64_t K,
+                                    const fp8_tile_config* cfg);
+
+/* ------------------------------------------------------------------------ */
+/* Tile-config table                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* Resolve the tile config for (kind, N, K, M). [PR34331, "Implementation"
+ * steps 1 and 5 and "Key source excerpts": one JSON table per (N, K, device,
+ * dtype), keys are M values, the entry whose key is nearest to M wins (ties:
+ * the smaller key), a null entry or a missing table means "keep the default
+ * path", and an environment kill switch disables the tables.]
+ * Tables are read once per (kind, N, K) from the config directory, file name
+ * "N={N},K={K},device_name=gfx950,dtype=fp8_w8a8_{channelwise|blockwise}.json".
+ * The kill switch is FP8W8A8_TUNED_CONFIGS=0.
+ * Fills *out with the config used (table hit or default heuristic) and returns
+ * 1 for a table hit, 0 for the default, FP8_ERR_INVALID on bad arguments. */
+int fp8_tile_config_lookup(int32_t kind, int64_t N, int64_t K, int64_t M,
+                           fp8_tile_config* out);
+
+/* The default heuristic alone (no table). Returns 0 or FP8_ERR_INVALID. */
+int fp8_tile_config_default(int32_t kind, int64_t N, int64_t K, int64_t M,
+                            fp8_tile_config* out);
+
+/* Set the directory tables are read from (NULL: back to the default, which is
+ * $FP8W8A8_CONFIG_DIR or the "configs" directory next to the library) and
+ * drop every cached table. Returns FP8_OK. */
+int fp8_tile_config_set_dir(const char* dir);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* fp8_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t fp8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8W8A8_H */

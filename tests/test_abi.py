@@ -1,0 +1,216 @@
+"""CPU-only checks of the C-ABI library: it loads without a GPU, exports every
+function include/fp8w8a8.h declares, rejects bad arguments on the host before
+touching the device, and implements the tile-table semantics (nearest M with
+ties to the smaller key, null entries, missing or malformed files, the kill
+switch)."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+from fp8_w8a8_quantized_token_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8w8a8.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 13
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_version_and_padded_rows(lib):
+    assert lib.fp8_version() >= 100
+    for m, ra, want in [(0, 4, 0), (1, 4, 4), (5, 4, 8), (13, 4, 16), (31, 4, 32), (7, 1, 7)]:
+        assert lib.fp8_padded_rows(m, ra) == want
+    assert lib.fp8_padded_rows(-1, 4) == -1
+    assert lib.fp8_padded_rows(3, 0) == -1
+
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
+
+
+def _err(lib):
+    return lib.fp8_last_error().decode()
+
+
+def test_quant_argument_errors(lib):
+    q = lib.fp8_quant_per_token
+    assert q(None, 4, 128, 128, FAKE, 128, FAKE, 1e-10, None) == _lib.FP8_ERR_INVALID
+    assert "null" in _err(lib)
+    assert q(FAKE, 4, 100, 100, FAKE, 100, FAKE, 1e-10, None) == _lib.FP8_ERR_INVALID
+    assert "multiple of 16" in _err(lib)
+    assert q(FAKE, 4, 128, 64, FAKE, 128, FAKE, 1e-10, None) == _lib.FP8_ERR_INVALID
+    assert q(FAKE, -1, 128, 128, FAKE, 128, FAKE, 1e-10, None) == _lib.FP8_ERR_INVALID
+    assert q(ctypes.c_void_p(0x10002), 4, 128, 128, FAKE, 128, FAKE, 1e-10, None) == _lib.FP8_ERR_INVALID
+    assert q(FAKE, 4, 128, 128, FAKE, 128, FAKE, -1.0, None) == _lib.FP8_ERR_INVALID
+    # M == 0 is a successful no-op even with null pointers
+    assert q(None, 0, 128, 128, None, 128, None, 1e-10, None) == _lib.FP8_OK
+
+    g = lib.fp8_quant_per_token_group
+    assert g(FAKE, 4, 7168, 7168, 256, 4, FAKE, 7168, FAKE, 1e-10, None) == _lib.FP8_ERR_UNSUPPORTED
+    assert "group_size" in _err(lib)
+    assert g(FAKE, 4, 7168 + 64, 7232, 128, 4, FAKE, 7232, FAKE, 1e-10, None) == _lib.FP8_ERR_INVALID
+    assert "divisible" in _err(lib)
+    assert g(FAKE, 4, 7168, 7168, 128, 0, FAKE, 7168, FAKE, 1e-10, None) == _lib.FP8_ERR_INVALID
+    assert g(None, 0, 7168, 7168, 128, 4, None, 7168, None, 1e-10, None) == _lib.FP8_OK
+
+
+def test_gemm_argument_errors(lib):
+    cw = lib.fp8_scaled_mm_channelwise
+    assert cw(None, FAKE, FAKE, FAKE, None, FAKE, 4, 256, 512, 512, 512, 256, None, 0, None) == _lib.FP8_ERR_INVALID
+    assert cw(FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 256, 500, 512, 512, 256, None, 0, None) == _lib.FP8_ERR_INVALID
+    assert cw(FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 256, 512, 256, 512, 256, None, 0, None) == _lib.FP8_ERR_INVALID
+    assert cw(FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10002), FAKE, 4, 256, 512, 512, 512, 256, None, 0,
+              None) == _lib.FP8_ERR_INVALID
+    assert cw(None, None, None, None, None, None, 0, 256, 512, 512, 512, 256, None, 0, None) == _lib.FP8_OK
+    bw = lib.fp8_scaled_mm_blockwise
+    assert bw(FAKE, FAKE, FAKE, 4, FAKE, None, FAKE, 4, 200, 512, 512, 512, 200, None, 0, None) == _lib.FP8_ERR_UNSUPPORTED
+    assert bw(FAKE, FAKE, FAKE, 4, FAKE, None, FAKE, 4, 256, 528, 528, 528, 256, None, 0, None) == _lib.FP8_ERR_UNSUPPORTED
+    assert bw(FAKE, FAKE, FAKE, 2, FAKE, None, FAKE, 4, 256, 512, 512, 512, 256, None, 0, None) == _lib.FP8_ERR_INVALID
+    assert "a_scale_ld" in _err(lib)
+
+
+def test_workspace_errors(lib):
+    cfg = _lib.TileConfig(_lib.VARIANTS["t64x64"], 0, 0, 0, 4, 0)
+    need = lib.fp8_scaled_mm_workspace_size(0, 64, 256, 1024, ctypes.byref(cfg))
+    # fixed counter region (65536 ints) + 4 tiles x 4 splits x 64 x 64 fp32
+    assert need == 65536 * 4 + 4 * 4 * 64 * 64 * 4
+    r = lib.fp8_scaled_mm_channelwise_ex(FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 256, 1024, 1024,
+                                         1024, 256, FAKE, need - 1, ctypes.byref(cfg), None)
+    assert r == _lib.FP8_ERR_WORKSPACE
+    skinny = _lib.TileConfig(_lib.VARIANTS["skinny"], 0, 0, 0, 1, 0)
+    assert lib.fp8_scaled_mm_workspace_size(0, 16, 4096, 4096, ctypes.byref(skinny)) == 0
+    bad = _lib.TileConfig(_lib.VARIANTS["skinny"], 0, 0, 0, 1, 0)
+    r = lib.fp8_scaled_mm_channelwise_ex(FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 256, 1024, 1024,
+                                         1024, 256, None, 0, ctypes.byref(bad), None)
+    assert r == _lib.FP8_ERR_INVALID and "skinny" in _err(lib)
+    unknown = _lib.TileConfig(99, 0, 0, 0, 1, 0)
+    r = lib.fp8_scaled_mm_channelwise_ex(FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 256, 1024, 1024,
+                                         1024, 256, None, 0, ctypes.byref(unknown), None)
+    assert r == _lib.FP8_ERR_INVALID
+
+
+# ---------------------------------------------------------------- tile table
+def _lookup(lib, kind, n, k, m):
+    c = _lib.TileConfig()
+    r = lib.fp8_tile_config_lookup(kind, n, k, m, ctypes.byref(c))
+    return r, c.as_dict()
+
+
+def _write(dirpath, n, k, table, kind="channelwise"):
+    p = os.path.join(dirpath, f"N={n},K={k},device_name=gfx950,dtype=fp8_w8a8_{kind}.json")
+    with open(p, "w") as f:
+        f.write(table if isinstance(table, str) else json.dumps(table))
+    return p
+
+
+@pytest.fixture
+def table_dir(lib, tmp_path, monkeypatch):
+    monkeypatch.delenv("FP8W8A8_TUNED_CONFIGS", raising=False)
+    lib.fp8_tile_config_set_dir(str(tmp_path).encode())
+    yield str(tmp_path)
+    lib.fp8_tile_config_set_dir(None)
+
+
+def test_table_nearest_m_and_ties(lib, table_dir):
+    _write(table_dir, 4096, 4096, {
+        "1": {"variant": "skinny", "split_k": 1},
+        "64": {"variant": "t64x64", "split_k": 4},
+        "128": {"variant": "t128x128", "split_k": 2},
+        "512": None,
+        "4096": {"variant": "t256x256", "split_k": 1},
+    })
+    assert _lookup(lib, 0, 4096, 4096, 1) == (1, {"variant": "skinny", "bm": 32, "bn": 16, "bk": 512,
+                                                  "split_k": 1, "waves": 8})
+    assert _lookup(lib, 0, 4096, 4096, 40)[1]["variant"] == "t64x64"       # |40-64| < |40-1|
+    assert _lookup(lib, 0, 4096, 4096, 96)[1]["variant"] == "t64x64"       # tie 64/128 -> smaller
+    assert _lookup(lib, 0, 4096, 4096, 97)[1]["variant"] == "t128x128"
+    r, c = _lookup(lib, 0, 4096, 4096, 600)                                # nearest is the null entry
+    assert r == 0 and c == _default(lib, 0, 4096, 4096, 600)
+    assert _lookup(lib, 0, 4096, 4096, 100000)[1]["variant"] == "t256x256"
+    # the other kind and other shapes have no table
+    assert _lookup(lib, 1, 4096, 4096, 64)[0] == 0
+    assert _lookup(lib, 0, 4096, 12288, 64)[0] == 0
+
+
+def _default(lib, kind, n, k, m):
+    c = _lib.TileConfig()
+    assert lib.fp8_tile_config_default(kind, n, k, m, ctypes.byref(c)) == 0
+    return c.as_dict()
+
+
+def test_table_kill_switch(lib, table_dir, monkeypatch):
+    _write(table_dir, 4096, 4096, {"64": {"variant": "t128x128", "split_k": 2}})
+    assert _lookup(lib, 0, 4096, 4096, 64)[0] == 1
+    for off in ("0", "false", "OFF"):
+        monkeypatch.setenv("FP8W8A8_TUNED_CONFIGS", off)
+        assert _lookup(lib, 0, 4096, 4096, 64) == (0, _default(lib, 0, 4096, 4096, 64))
+    monkeypatch.setenv("FP8W8A8_TUNED_CONFIGS", "1")
+    assert _lookup(lib, 0, 4096, 4096, 64)[0] == 1
+
+
+def test_table_malformed_and_missing(lib, table_dir):
+    _write(table_dir, 1024, 1024, "{not json")
+    _write(table_dir, 2048, 1024, {"64": {"variant": "no-such-kernel"}})
+    _write(table_dir, 3072, 1024, {"sixty": {"variant": "t64x64"}})
+    for n in (1024, 2048, 3072, 5120):
+        assert _lookup(lib, 0, n, 1024, 64) == (0, _default(lib, 0, n, 1024, 64))
+
+
+def test_table_blockwise_kind(lib, table_dir):
+    _write(table_dir, 7168, 7168, {"16": {"variant": "skinny"}, "256": {"variant": "t64x64", "split_k": 3}},
+           kind="blockwise")
+    assert _lookup(lib, 1, 7168, 7168, 13)[1]["variant"] == "skinny"
+    assert _lookup(lib, 1, 7168, 7168, 256)[1] == {"variant": "t64x64", "bm": 64, "bn": 64, "bk": 128,
+                                                   "split_k": 3, "waves": 4}
+    assert _lookup(lib, 0, 7168, 7168, 256)[0] == 0
+
+
+def test_default_heuristic_shapes(lib):
+    assert _default(lib, 0, 4096, 4096, 1)["variant"] == "skinny"
+    assert _default(lib, 0, 4096, 4096, 32)["variant"] == "skinny"
+    for m in (64, 512, 4096, 8192):
+        c = _default(lib, 0, 4096, 4096, m)
+        assert c["variant"] != "skinny" and c["split_k"] >= 1
+
+
+def test_shipped_tables_parse(lib):
+    """Every table shipped next to the library parses and names real kernels."""
+    lib.fp8_tile_config_set_dir(None)
+    cfg_dir = os.path.join(os.path.dirname(_lib.LIB_PATH), "configs")
+    if not os.path.isdir(cfg_dir):
+        pytest.skip("no shipped tables")
+    for name in os.listdir(cfg_dir):
+        m = re.match(r"N=(\d+),K=(\d+),device_name=gfx950,dtype=fp8_w8a8_(channelwise|blockwise)\.json",
+                     name)
+        assert m, name
+        n, k, kind = int(m.group(1)), int(m.group(2)), m.group(3)
+        table = json.load(open(os.path.join(cfg_dir, name)))
+        for key, val in table.items():
+            r, c = _lookup(lib, 0 if kind == "channelwise" else 1, n, k, int(key))
+            if val is None:
+                assert r == 0
+            else:
+                assert r == 1 and c["variant"] == val["variant"], (name, key)

@@ -1,0 +1,215 @@
+"""GPU parity of the scaled GEMMs against the fp64 oracle.
+
+Inputs are quantized by the oracle (never by the HIP path) and the same bytes
+go to both sides. Acceptance (oracle.check_gemm): max|err| <= 1e-2 max|ref| and
+per element |err| <= 2^-6 |ref| + tau, tau being the fp32 summation bound of
+the K-term accumulation. Full outputs are compared up to a few million
+elements; larger workloads compare a sample of rows (rows are independent),
+always including the first and last rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_w8a8_quantized_token_amd import ops, synth
+from gpu_common import (act_group, act_per_token, bf16_to_f64, device, gpu, sample_rows, say,
+                        weight_blockwise, weight_channelwise)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(out_rows, ref, tau, label):
+    res = oracle.check_gemm(out_rows, ref, tau)
+    say(label, {k: (round(v, 8) if isinstance(v, float) else v) for k, v in res.items()})
+    assert res["ok"], (label, res)
+    assert res["cosine"] > 0.9999
+    return res
+
+
+def _channelwise_case(wl, m, n, k, outliers, with_bias, config=None, sample=True):
+    a, sa = act_per_token(wl, m, k, outliers)
+    b, sb = weight_channelwise(wl, n, k)
+    bias = synth.bias(wl, n) if with_bias else None
+    say("channelwise", wl, m, n, k, config.as_dict() if config is not None else "table/default")
+    out = ops.scaled_mm_channelwise(gpu(a), gpu(b), gpu(sa), gpu(sb),
+                                    gpu(bias) if bias is not None else None, config=config)
+    torch.cuda.synchronize()
+    rows = sample_rows(m) if (sample and m * n > 4_000_000) else np.arange(m)
+    bias64 = bias.float().numpy() if bias is not None else None
+    ref = oracle.scaled_mm_channelwise(a[rows], b, sa[rows], sb, bias64)
+    tau = oracle.summation_bound_channelwise(a[rows], b, sa[rows], sb)
+    got = bf16_to_f64(out)[rows]
+    return _check(got, ref, tau, f"cw {wl} M={m} N={n} K={k}"), out
+
+
+CW_CASES = (
+    [("small", 16, 256, 512, 0.0, False)]
+    + [("o_proj", m, 4096, 4096, 0.01, False)
+       for m in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192)]
+    + [("qwen3_8b", m, n, k, 0.0, True) for n, k in ((6144, 4096), (4096, 12288), (24576, 4096))
+       for m in (1, 64, 512, 8192)]
+)
+
+
+@pytest.mark.parametrize("wl,m,n,k,outl,bias", CW_CASES, ids=[f"{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in CW_CASES])
+def test_channelwise_workloads(wl, m, n, k, outl, bias):
+    _channelwise_case(wl, m, n, k, outl, bias)
+
+
+def _blockwise_case(wl, m, n, k, config=None, with_bias=False, poison=False):
+    a, sa = act_group(wl, m, k)
+    b, sb = weight_blockwise(wl, n, k)
+    bias = synth.bias(wl, n) if with_bias else None
+    m_pad = ops.padded_rows(m, 4)
+    a_dev = torch.full((m_pad, k), 0x7F if poison else 0, dtype=torch.uint8, device=device())
+    a_dev[:m] = gpu(a)
+    s_store = torch.full((k // 128, m_pad), float("nan") if poison else 0.0, dtype=torch.float32,
+                         device=device())
+    s_store[:, :m] = gpu(sa.T.copy())
+    say("blockwise", wl, m, n, k, "poison" if poison else "", config.as_dict() if config is not None else "")
+    out = ops.scaled_mm_blockwise(a_dev, gpu(b), s_store.transpose(0, 1), gpu(sb),
+                                  gpu(bias) if bias is not None else None, m=m, config=config)
+    torch.cuda.synchronize()
+    rows = sample_rows(m) if m * n > 4_000_000 else np.arange(m)
+    bias64 = bias.float().numpy() if bias is not None else None
+    ref = oracle.scaled_mm_blockwise(a[rows], b, sa[rows], sb, bias64)
+    tau = oracle.summation_bound_blockwise(a[rows], b, sa[rows], sb)
+    got = bf16_to_f64(out)[rows]
+    assert out.shape == (m, n)
+    return _check(got, ref, tau, f"bw {wl} M={m} N={n} K={k}"), out
+
+
+BW_CASES = ([("block_7168", m, 7168, 7168) for m in (1, 2, 3, 5, 7, 13, 31, 64, 256)]
+            + [("block_moe", m, n, k) for n, k in ((3072, 4096), (4096, 1536)) for m in (1, 4, 16, 64, 4096)])
+
+
+@pytest.mark.parametrize("wl,m,n,k", BW_CASES, ids=[f"{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in BW_CASES])
+def test_blockwise_workloads(wl, m, n, k):
+    _blockwise_case(wl, m, n, k)
+
+
+# ---------------------------------------------------------------- every kernel variant
+VARIANT_CASES = [(v, sk) for v, sk in (("skinny", 1), ("t64x64", 1), ("t64x64", 3), ("t128x128", 1),
+                                       ("t128x128", 2), ("t256x128", 1), ("t256x128", 4),
+                                       ("t256x256", 1), ("t256x256", 2))]
+
+
+@pytest.mark.parametrize("variant,split_k", VARIANT_CASES, ids=[f"{v}-sk{s}" for v, s in VARIANT_CASES])
+def test_channelwise_variants_ragged(variant, split_k):
+    """Ragged M, N and K tails (K a multiple of 16 but not of 128)."""
+    m = 29 if variant == "skinny" else 300
+    n, k = 392, 1040
+    cfg = ops.make_config(variant, split_k)
+    _channelwise_case("ragged", m, n, k, 0.0, True, config=cfg, sample=False)
+
+
+BW_VARIANTS = [(v, sk) for v, sk in (("skinny", 1), ("t64x64", 1), ("t64x64", 5), ("t128x128", 1),
+                                     ("t128x128", 3), ("t256x128", 2))]
+
+
+@pytest.mark.parametrize("variant,split_k", BW_VARIANTS, ids=[f"{v}-sk{s}" for v, s in BW_VARIANTS])
+def test_blockwise_variants(variant, split_k):
+    m = 30 if variant == "skinny" else 200
+    _blockwise_case("bw-variants", m, 640, 1280, config=ops.make_config(variant, split_k),
+                    with_bias=True)
+
+
+def test_blockwise_poisoned_pad_rows_do_not_leak():
+    """Pad rows filled with NaN codes and NaN scales: the first M rows must be
+    bit-identical to a run with zero pads (rows are independent)."""
+    for m in (1, 3, 5, 13, 31):
+        _, clean = _blockwise_case("block_7168", m, 7168, 7168)
+        _, dirty = _blockwise_case("block_7168", m, 7168, 7168, poison=True)
+        assert torch.equal(clean.view(torch.int16), dirty.view(torch.int16)), m
+
+
+def test_deterministic_repeat():
+    for cfg in (None, ops.make_config("t128x128", 4), ops.make_config("t64x64", 2)):
+        _, o1 = _channelwise_case("o_proj", 256, 4096, 4096, 0.01, False, config=cfg, sample=False)
+        _, o2 = _channelwise_case("o_proj", 256, 4096, 4096, 0.01, False, config=cfg, sample=False)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_split_k_agrees_within_tolerance():
+    outs = []
+    for cfg in (ops.make_config("t64x64", 1), ops.make_config("t64x64", 8)):
+        _, o = _channelwise_case("o_proj", 128, 4096, 4096, 0.01, False, config=cfg, sample=False)
+        outs.append(bf16_to_f64(o))
+    diff = np.abs(outs[0] - outs[1])
+    assert np.max(diff) <= 2.0 ** -6 * np.max(np.abs(outs[0]))
+
+
+def test_exact_identities():
+    """Bit-exact cases: all-ones operands with power-of-two scales; A = 0 gives
+    bf16(bias); identity-pattern weight reproduces dec(A) * scales."""
+    dev = device()
+    k = 512
+    a = torch.full((20, k), 0x38, dtype=torch.uint8, device=dev)
+    b = torch.full((48, k), 0x38, dtype=torch.uint8, device=dev)
+    sa = torch.full((20,), 2.0 ** -3, device=dev)
+    sb = torch.full((48,), 2.0 ** -5, device=dev)
+    for cfg in (ops.make_config("skinny"), ops.make_config("t64x64", 2)):
+        out = ops.scaled_mm_channelwise(a, b, sa, sb, config=cfg)
+        torch.cuda.synchronize()
+        assert torch.all(out.float() == k * 2.0 ** -8)
+    bias = synth.bias("ident", 48)
+    z = torch.zeros((20, k), dtype=torch.uint8, device=dev)
+    out = ops.scaled_mm_channelwise(z, b, sa, sb, gpu(bias))
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu().view(torch.int16), bias.expand(20, 48).contiguous().view(torch.int16))
+    codes = synth.random_codes("ident-a", (20, 128))
+    eye = torch.zeros((128, 128), dtype=torch.uint8)
+    eye[torch.arange(128), torch.arange(128)] = 0x38
+    sa2 = torch.tensor([2.0 ** -(i % 5) for i in range(20)], dtype=torch.float32)
+    out = ops.scaled_mm_channelwise(gpu(codes), gpu(eye), gpu(sa2), torch.full((128,), 4.0, device=dev))
+    torch.cuda.synchronize()
+    want = oracle.bf16_round(oracle.decode(codes.numpy()) * sa2.numpy()[:, None].astype(np.float64) * 4.0)
+    assert np.array_equal(bf16_to_f64(out), want)
+
+
+def test_blockwise_uniform_scales_match_channelwise():
+    m, n, k = 64, 1024, 2048
+    a = synth.random_codes("uni-a", (m, k))
+    b = synth.random_codes("uni-b", (n, k))
+    sa = synth.positive_scales("uni-sa", (m,))
+    sbb = synth.positive_scales("uni-sb", (n // 128,))
+    out_c = ops.scaled_mm_channelwise(gpu(a), gpu(b), gpu(sa), gpu(sbb.repeat_interleave(128)))
+    s_store = gpu(sa[None, :].repeat(k // 128, 1).contiguous())
+    out_b = ops.scaled_mm_blockwise(gpu(a), gpu(b), s_store.transpose(0, 1),
+                                    gpu(sbb[:, None].repeat(1, k // 128).contiguous()))
+    torch.cuda.synchronize()
+    oc, ob = bf16_to_f64(out_c), bf16_to_f64(out_b)
+    assert np.max(np.abs(oc - ob)) <= 2.0 ** -6 * np.max(np.abs(oc))
+
+
+def test_empty_m_is_noop():
+    dev = device()
+    a = torch.empty((0, 512), dtype=torch.uint8, device=dev)
+    b = torch.zeros((256, 512), dtype=torch.uint8, device=dev)
+    out = ops.scaled_mm_channelwise(a, b, torch.empty(0, device=dev), torch.ones(256, device=dev))
+    assert out.shape == (0, 256)
+
+
+def test_linear_wrappers_match_oracle():
+    """The user-facing linears (quant + GEMM) against the oracle pipeline."""
+    x = synth.activations("linear", 37, 1024)
+    w = synth.weights("linear", 384, 1024).numpy()
+    bias = synth.bias("linear", 384)
+    wq, ws = oracle.quant_weight_per_channel(w)
+    say("linear_channelwise")
+    y = ops.linear_channelwise(gpu(x), gpu(wq), gpu(ws), gpu(bias))
+    torch.cuda.synchronize()
+    aq, as_ = oracle.quant_per_token(x.float().numpy())
+    ref = oracle.scaled_mm_channelwise(aq, wq, as_, ws, bias.float().numpy())
+    tau = oracle.summation_bound_channelwise(aq, wq, as_, ws)
+    _check(bf16_to_f64(y), ref, tau, "linear_channelwise")
+    bq, bs = oracle.quant_weight_blockwise(w)
+    say("linear_blockwise")
+    y = ops.linear_blockwise(gpu(x), gpu(bq), gpu(bs), gpu(bias))
+    torch.cuda.synchronize()
+    gq, gs = oracle.quant_per_token_group(x.float().numpy(), 128)
+    ref = oracle.scaled_mm_blockwise(gq, bq, gs, bs, bias.float().numpy())
+    tau = oracle.summation_bound_blockwise(gq, bq, gs, bs)
+    assert y.shape == (37, 384)
+    _check(bf16_to_f64(y), ref, tau, "linear_blockwise")
