@@ -1,0 +1,234 @@
+"""Benchmark of the FP8 W8A8 linear hot path on one MI355X.
+
+One step = one pass of the whole hot path over the o_proj workload (N = K =
+4096, M in 1, 2, 4, ..., 8192): for every M, the channelwise linear (per-token
+quant, tile-config lookup, channelwise scaled GEMM with its fused epilogue and
+in-launch split-K reduction) and the blockwise linear (row-padded group-128
+quant, lookup, blockwise scaled GEMM). Inputs are synthetic and resident in HBM
+before timing starts; every (M, kind) has its own weight copy, so a step
+touches ~1 GB and the 256 MB last-level cache cannot serve the weights.
+
+Output: one JSON line. ``value`` is the step's GEMM TFLOP/s (sum of 2MNK over
+the step time, quant included in the time). ``roofline`` reports the kernel
+with the largest share of GPU time, timed with HIP events on the stream the
+kernels run on. ``cpu_baseline`` times the CPU oracle on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FP8 scaled-GEMM TFLOP/s and GB/s vs roofline, Qwen3-8B shapes, M=1..8192"
+PEAK_TFLOPS_FP8 = 5000.0  # MI355X dense FP8 MFMA
+PEAK_GBPS = 8000.0        # MI355X HBM3E
+RIDGE = PEAK_TFLOPS_FP8 * 1e12 / (PEAK_GBPS * 1e9)
+MS = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192]
+N = K = 4096
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--per-m", action="store_true", help="also print a per-(M, kind) table")
+    return ap.parse_args()
+
+
+def gemm_bytes(kind, m, n, k, bias=False):
+    b = m * k + n * k + 2 * m * n + (2 * n if bias else 0)
+    if kind == "channelwise":
+        b += 4 * m + 4 * n
+    else:
+        b += 4 * m * (k // 128) + 4 * (n // 128) * (k // 128)
+    return b
+
+
+def quant_bytes(m, k, group):
+    return 3 * m * k + 4 * m * (k // group)
+
+
+class Launch:
+    """One kernel launch of the step with its label and algorithmic cost."""
+
+    def __init__(self, label, fn, flops, nbytes):
+        self.label, self.fn, self.flops, self.nbytes = label, fn, flops, nbytes
+
+
+def build_step(torch, ops, synth, dev):
+    launches = []
+    w_host = synth.weights("o_proj", N, K).to(torch.bfloat16)
+    for kind in ("channelwise", "blockwise"):
+        for m in MS:
+            x = synth.activations("o_proj", m, K, outlier_frac=0.01).to(dev)
+            w = w_host.to(dev)
+            if kind == "channelwise":
+                wq, ws = ops.quant_per_token(w)           # per-output-channel weight quant
+                q = torch.empty((m, K), dtype=torch.uint8, device=dev)
+                s = torch.empty((m,), dtype=torch.float32, device=dev)
+                out = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+                cfg, _ = ops.tile_config(0, N, K, m)
+                label_q = "quant_per_token"
+                label_g = f"gemm_channelwise[{cfg['variant']}]"
+
+                def fq(x=x, q=q, s=s):
+                    ops.quant_per_token(x, out=q, scale=s)
+
+                def fg(q=q, s=s, wq=wq, ws=ws, out=out):
+                    ops.scaled_mm_channelwise(q, wq, s, ws, out=out)
+                qb = quant_bytes(m, K, K)
+            else:
+                # codes from the group-128 quant of the weight rows, scales as
+                # synthetic 128x128 block scales (timing does not depend on them)
+                wq, _ = ops.quant_per_token_group(w, 128, row_alignment=1)
+                wq = wq.contiguous()
+                ws = synth.positive_scales("o_proj/wblk", (N // 128, K // 128)).to(dev)
+                m_pad = ops.padded_rows(m, 4)
+                q = torch.empty((m_pad, K), dtype=torch.uint8, device=dev)
+                st = torch.empty((K // 128, m_pad), dtype=torch.float32, device=dev)
+                out = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+                cfg, _ = ops.tile_config(1, N, K, m)
+                label_q = "quant_per_token_group"
+                label_g = f"gemm_blockwise[{cfg['variant']}]"
+
+                def fq(x=x, q=q, st=st):
+                    ops.quant_per_token_group(x, 128, row_alignment=4, out=q, scale_storage=st)
+
+                def fg(q=q, st=st, wq=wq, ws=ws, out=out, m=m):
+                    ops.scaled_mm_blockwise(q, wq, st.transpose(0, 1), ws, m=m, out=out)
+                qb = quant_bytes(m, K, 128)
+            launches.append(Launch(label_q, fq, 0, qb))
+            launches.append(Launch(label_g, fg, 2 * m * N * K, gemm_bytes(kind, m, N, K)))
+            launches[-1].m, launches[-1].kind = m, kind
+            launches[-2].m, launches[-2].kind = m, kind
+    torch.cuda.synchronize()
+    return launches
+
+
+def cpu_baseline():
+    """The oracle (numpy, fp64 GEMM) on a bounded sample of the same workload."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    from fp8_w8a8_quantized_token_amd import synth
+
+    cores = len(os.sched_getaffinity(0))
+    with threadpoolctl.threadpool_limits(limits=cores):
+        threads = max([d.get("num_threads", 1) for d in threadpoolctl.threadpool_info()] or [1])
+        w = synth.weights("o_proj", N, K).numpy()
+        wq_c, ws_c = oracle.quant_weight_per_channel(w)
+        wq_b, ws_b = oracle.quant_weight_blockwise(w)
+        sample = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]
+        flops = 0
+        t0 = time.perf_counter()
+        for m in sample:
+            x = synth.activations("o_proj", m, K, outlier_frac=0.01).float().numpy()
+            q, s = oracle.quant_per_token(x)
+            oracle.scaled_mm_channelwise(q, wq_c, s, ws_c)
+            qg, sg = oracle.quant_per_token_group(x, 128)
+            oracle.scaled_mm_blockwise(qg, wq_b, sg, ws_b)
+            flops += 2 * (2 * m * N * K)
+        dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"o_proj N=K=4096, M in {sample}, channelwise + blockwise linear "
+                      f"(quant + fp64 GEMM), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is described in the design notes but not built.", flush=True)
+        sys.exit(2)
+    import torch
+
+    from fp8_w8a8_quantized_token_amd import _lib, ops, synth
+
+    _lib.load()
+    dev = torch.device("cuda:0")
+    launches = build_step(torch, ops, synth, dev)
+    flops_step = sum(l.flops for l in launches)
+    bytes_step = sum(l.nbytes for l in launches)
+
+    for _ in range(args.warmup):
+        for l in launches:
+            l.fn()
+    torch.cuda.synchronize()
+
+    # events on the stream the kernels are launched on (torch's current stream)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in launches] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, l in enumerate(launches):
+            ev[s][i][0].record()
+            l.fn()
+            ev[s][i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+
+    per_label = {}
+    per_m = {}
+    for i, l in enumerate(launches):
+        durs = [ev[s][i][0].elapsed_time(ev[s][i][1]) * 1e-3 for s in range(args.steps)]
+        d = per_label.setdefault(l.label, {"count": 0, "time": 0.0, "flops": 0, "bytes": 0})
+        d["count"] += len(durs)
+        d["time"] += sum(durs)
+        d["flops"] += l.flops * len(durs)
+        d["bytes"] += l.nbytes * len(durs)
+        key = f"{l.kind}/{'quant' if l.flops == 0 else 'gemm'}/M={l.m}"
+        per_m[key] = {"us": 1e6 * sorted(durs)[len(durs) // 2], "flops": l.flops, "bytes": l.nbytes}
+
+    dom_label, dom = max(per_label.items(), key=lambda kv: kv[1]["time"])
+    avg = dom["time"] / dom["count"]
+    flops_launch = dom["flops"] / dom["count"]
+    bytes_launch = dom["bytes"] / dom["count"]
+    if flops_launch > 0 and flops_launch / bytes_launch >= RIDGE:
+        roof = {"bound": "mfma", "achieved": flops_launch / avg / 1e12, "peak": PEAK_TFLOPS_FP8,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": bytes_launch / avg / 1e9, "peak": PEAK_GBPS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom_label
+    roof["avg_launch_us"] = avg * 1e6
+    roof["launches_per_step"] = dom["count"] // args.steps
+
+    result = {
+        "metric": METRIC,
+        "value": flops_step / step_s / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": "o_proj N=K=4096, M in 1..8192 (powers of 2); channelwise and "
+                               "blockwise FP8 linear (quant + scaled GEMM) per M",
+                   "gemm_gflop_per_step": flops_step / 1e9, "bytes_per_step": bytes_step},
+        "gbps": bytes_step / step_s / 1e9,
+        "roofline": roof,
+    }
+    if args.per_m:
+        result["per_m"] = per_m
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
