@@ -89,9 +89,10 @@ int resolve_config(int kind, int64_t M, int64_t N, int64_t K, const fp8_tile_con
   return FP8_OK;
 }
 
-// Effective split count: never more splits than 128-deep K steps.
-void split_plan(int64_t K, int split_k, int* splits, int* per) {
-  const int64_t kt = (K + 127) / 128;
+// Effective split count: never more splits than the variant's K stages;
+// `per` counts stages of the variant's depth bk.
+void split_plan(int64_t K, int bk, int split_k, int* splits, int* per) {
+  const int64_t kt = (K + bk - 1) / bk;
   int64_t s = split_k < 1 ? 1 : split_k;
   if (s > kt) s = kt;
   const int64_t p = (kt + s - 1) / s;
@@ -110,7 +111,7 @@ int run_gemm(const char* fn, int kind, const uint8_t* a, const uint8_t* b, const
   p.a = a; p.b = b; p.sa = sa; p.sa_ld = sa_ld; p.sb = sb; p.bias = bias; p.out = out;
   p.M = M; p.N = N; p.K = K; p.lda = lda; p.ldb = ldb; p.ldc = ldc;
   int splits = 1, per = (int)((K + 127) / 128);
-  if (cfg.variant != FP8_VARIANT_SKINNY) split_plan(K, cfg.split_k, &splits, &per);
+  if (cfg.variant != FP8_VARIANT_SKINNY) split_plan(K, cfg.bk, cfg.split_k, &splits, &per);
   p.split_k = splits;
   p.k_tiles_per_split = per;
   if (splits > 1) {
@@ -222,7 +223,7 @@ size_t fp8_scaled_mm_workspace_size(int32_t kind, int64_t M, int64_t N, int64_t 
   if (resolve_config(kind, M, N, K, cfg_in, &cfg)) return (size_t)-1;
   if (cfg.variant == FP8_VARIANT_SKINNY) return 0;
   int splits, per;
-  split_plan(K, cfg.split_k, &splits, &per);
+  split_plan(K, cfg.bk, cfg.split_k, &splits, &per);
   return variant_workspace_bytes(cfg.variant, splits, M, N);
 }
 

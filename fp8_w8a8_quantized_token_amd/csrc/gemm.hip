@@ -74,32 +74,86 @@ __device__ __forceinline__ void store_out4(const GemmArgs& p, int64_t m, int64_t
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel: BM x BN block tile, 128-deep K steps, WM x WN waves, each wave
-// a (BM/WM) x (BN/WN) sub-tile of 16x16 MFMA tiles. A and B K-slices are
-// staged through LDS, double buffered: global loads of step k+1 are issued
-// into registers before the MFMAs of step k and written to the other LDS
-// buffer after them, with one barrier per step. LDS rows are 128 bytes made of
-// eight 16-byte chunks; chunk c of row r is stored at position c ^ (r & 7), so
-// the 16 lanes that read one chunk column of 16 consecutive rows hit distinct
-// bank groups.
+// Tiled kernel: BM x BN block tile, 128-byte K stages, WM x WN waves, each wave
+// a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA tiles (V_MFMA_F32_32X32X64_F8F6F4,
+// two per stage). A and B stages are staged through LDS, double buffered:
+// global loads of stage s+1 are issued into registers before the MFMAs of
+// stage s and written to the other LDS buffer after them, one barrier per
+// stage. LDS rows are 128 bytes of eight 16-byte chunks placed by swz().
+// MFMA operand layout: lane l holds row l % 32 and, for the 64-byte K step s
+// of the stage, bytes [64s + 32h, 64s + 32h + 32) with h = l / 32 (the same
+// assignment for both operands). The weight is the first operand, so the
+// 32x32 result is out^T: lane l holds m = l % 32 and, in register r,
+// n = 8*(r/4) + 4*(l/32) + r%4 -- four consecutive n per register quad.
 // Split-K: blockIdx.y selects a K range; every split writes its fp32 partial
-// tile to the workspace, and the last split to arrive (arrival counter per
-// tile) sums the partials in split order -- deterministic -- applies the
-// epilogue and re-arms the counter to zero.
+// tile to the workspace with agent-coherent stores, and the last split to
+// arrive (arrival counter per tile) sums the partials in split order --
+// deterministic -- applies the epilogue and re-arms the counter to zero.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int KIND>
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Physical 16-byte chunk position of logical chunk c in an LDS row r of CH
+// chunks. For 128-byte rows (CH = 8) the xor key (r & 7) ^ ((r >> 3) & 1)
+// gives every 8 consecutive rows distinct positions (32 banks serve 8 lanes
+// of a 128-bit access per cycle) and every 16 consecutive rows distinct (row
+// parity, position) pairs (64 banks serve 16 lanes per cycle). Rows of 256
+// bytes or more start on the same bank, so the key is r & 15, distinct over 16
+// consecutive rows. Either way fragment reads of one chunk column and
+// row-wise stores are free of bank conflicts.
+template <int CH>
+__device__ __forceinline__ int swz(int r, int c) {
+  if (CH == 8) return c ^ ((r & 7) ^ ((r >> 3) & 1));
+  return c ^ (r & 15);
+}
+
+// Output-tile order: workgroups are dealt round-robin to the 8 XCDs (each with
+// its own L2), so consecutive workgroup ids are re-mapped to give every XCD a
+// contiguous range of tiles, and tiles are walked in groups of GM tile rows,
+// column by column inside a group, so the tiles resident on one XCD at a time
+// share A row panels and B column panels in its L2.
+__device__ __forceinline__ void tile_coords(int64_t id, int64_t tiles_m, int64_t tiles_n,
+                                            int64_t* tm, int64_t* tn) {
+  constexpr int64_t kXcd = 8, GM = 4;
+  const int64_t total = tiles_m * tiles_n;
+  int64_t t = id;
+  if (total % kXcd == 0) t = (id % kXcd) * (total / kXcd) + id / kXcd;
+  const int64_t per_group = GM * tiles_n;
+  const int64_t group = t / per_group;
+  const int64_t first = group * GM;
+  const int64_t gm = (tiles_m - first) < GM ? (tiles_m - first) : GM;
+  const int64_t in = t - group * per_group;
+  *tm = first + in % gm;
+  *tn = in / gm;
+}
+
+__device__ __forceinline__ f32x16 mfma32_fp8(const i32x8& w, const i32x8& x, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, x, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int KIND>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmArgs p) {
   constexpr int NT = WM * WN * 64;
-  constexpr int BK = 128;
+  constexpr int CH = BK / 16;          // 16-byte chunks per LDS row
+  constexpr int KS = BK / 64;          // 64-deep MFMA steps per stage
+  constexpr int KB = BK / 128;         // 128-wide scale blocks per stage
   constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int TM = WTM / 16, TN = WTN / 16;
-  constexpr int A_CH = BM * 8 / NT;
-  constexpr int B_CH = BN * 8 / NT;
-  static_assert(A_CH >= 1 && B_CH >= 1 && BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/threads");
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int A_CH = BM * CH / NT;
+  constexpr int B_CH = BN * CH / NT;
+  static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+  static_assert(A_CH >= 1 && B_CH >= 1 && BM * CH % NT == 0 && BN * CH % NT == 0, "tile/threads");
+  static_assert(BK == 128 || BK == 256 || BK == 512, "stage depth");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t* const a_lds = lds;                  // [2][BM][128]
-  uint8_t* const b_lds = lds + 2 * BM * BK;    // [2][BN][128]
+  uint8_t* const a_lds = lds;                  // [2][BM][BK]
+  uint8_t* const b_lds = lds + 2 * BM * BK;    // [2][BN][BK]
   __shared__ int last_flag;
 
   const int tid = threadIdx.x;
@@ -107,57 +161,64 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmArgs p) {
   const int wave = tid >> 6;
   const int wm = wave / WN;
   const int wn = wave % WN;
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
 
   const int64_t tiles_n = (p.N + BN - 1) / BN;
+  const int64_t tiles_m = (p.M + BM - 1) / BM;
   const int64_t tile = blockIdx.x;
-  const int64_t m0 = (tile / tiles_n) * BM;
-  const int64_t n0 = (tile % tiles_n) * BN;
+  int64_t tile_m, tile_n;
+  tile_coords(tile, tiles_m, tiles_n, &tile_m, &tile_n);
+  const int64_t m0 = tile_m * BM;
+  const int64_t n0 = tile_n * BN;
   const int split = blockIdx.y;
+  // this split's K range, in BK-deep stages (the host plans splits in stages)
   const int64_t kt_all = (p.K + BK - 1) / BK;
   const int64_t kt_begin = (int64_t)split * p.k_tiles_per_split;
   int64_t kt_end = kt_begin + p.k_tiles_per_split;
   if (kt_end > kt_all) kt_end = kt_all;
 
-  f32x4 acc[TM][TN];
+  f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TN; ++j) acc[i][j] = zero16();
 
   uint4 ra[A_CH], rb[B_CH];
-  float sa_nxt[TM], sb_nxt[TN];
+  float sa_nxt[KB][TM], sb_nxt[KB][TN];
 
   auto gload = [&](int64_t kt) {
     const int64_t k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int id = tid + i * NT;
-      const int r = id >> 3, c = id & 7;
+      const int r = id / CH, c = id % CH;
       const int64_t gm = m0 + r, gk = k0 + c * 16;
-      ra[i] = (gm < p.M && gk < p.K)
-                  ? load16(p.a + gm * p.lda + gk)
-                  : make_uint4(0, 0, 0, 0);
+      ra[i] = (gm < p.M && gk < p.K) ? load16(p.a + gm * p.lda + gk) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       const int id = tid + i * NT;
-      const int r = id >> 3, c = id & 7;
+      const int r = id / CH, c = id % CH;
       const int64_t gn = n0 + r, gk = k0 + c * 16;
-      rb[i] = (gn < p.N && gk < p.K)
-                  ? load16(p.b + gn * p.ldb + gk)
-                  : make_uint4(0, 0, 0, 0);
+      rb[i] = (gn < p.N && gk < p.K) ? load16(p.b + gn * p.ldb + gk) : make_uint4(0, 0, 0, 0);
     }
     if (KIND == kBlockwise) {
-      const int64_t kb_all = p.K / BK;
+      const int64_t kb_all = p.K / 128;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int64_t m = m0 + wm * WTM + i * 16 + (lane & 15);
-        sa_nxt[i] = (m < p.M) ? p.sa[kt * p.sa_ld + m] : 0.0f;
-      }
+      for (int b = 0; b < KB; ++b) {
+        const int64_t kb = kt * KB + b;
+        const bool kb_ok = kb < kb_all;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t n = n0 + wn * WTN + j * 16;
-        sb_nxt[j] = (n < p.N) ? p.sb[(n / 128) * kb_all + kt] : 0.0f;
+        for (int i = 0; i < TM; ++i) {
+          const int64_t m = m0 + wm * WTM + i * 32 + r32;
+          sa_nxt[b][i] = (kb_ok && m < p.M) ? p.sa[kb * p.sa_ld + m] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int64_t n = n0 + wn * WTN + j * 32;
+          sb_nxt[b][j] = (kb_ok && n < p.N) ? p.sb[(n / 128) * kb_all + kb] : 0.0f;
+        }
       }
     }
   };
@@ -167,206 +228,288 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int id = tid + i * NT;
-      const int r = id >> 3, c = id & 7;
-      *reinterpret_cast<uint4*>(ab + r * BK + ((c ^ (r & 7)) << 4)) = ra[i];
+      const int r = id / CH, c = id % CH;
+      *reinterpret_cast<uint4*>(ab + r * BK + (swz<CH>(r, c) << 4)) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       const int id = tid + i * NT;
-      const int r = id >> 3, c = id & 7;
-      *reinterpret_cast<uint4*>(bb + r * BK + ((c ^ (r & 7)) << 4)) = rb[i];
+      const int r = id / CH, c = id % CH;
+      *reinterpret_cast<uint4*>(bb + r * BK + (swz<CH>(r, c) << 4)) = rb[i];
     }
   };
+  // operand fragment of row r for 64-deep step s: chunks 4s+2h and 4s+2h+1
+  auto frag = [&](const uint8_t* base, int r, int s) {
+    const uint8_t* row = base + r * BK;
+    const int c0 = 4 * s + 2 * h;
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + (swz<CH>(r, c0) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + (swz<CH>(r, c0 + 1) << 4));
+    return join(lo, hi);
+  };
 
-  float sa_cur[TM], sb_cur[TN];
+  float sa_cur[KB][TM], sb_cur[KB][TN];
   if (kt_begin < kt_end) {
     gload(kt_begin);
     swrite(0);
   }
   __syncthreads();
 
-  const int g = lane >> 4;
   for (int64_t kt = kt_begin; kt < kt_end; ++kt) {
     const int buf = (int)((kt - kt_begin) & 1);
     const bool has_next = kt + 1 < kt_end;
     if (KIND == kBlockwise) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) sa_cur[i] = sa_nxt[i];
+      for (int b = 0; b < KB; ++b) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) sb_cur[j] = sb_nxt[j];
+        for (int i = 0; i < TM; ++i) sa_cur[b][i] = sa_nxt[b][i];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) sb_cur[b][j] = sb_nxt[b][j];
+      }
     }
     if (has_next) gload(kt + 1);
 
     const uint8_t* ab = a_lds + buf * BM * BK;
     const uint8_t* bb = b_lds + buf * BN * BK;
-    i32x8 af[TM], bf[TN];
+    if (KIND == kChannelwise) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int r = wm * WTM + i * 16 + (lane & 15);
-      const uint4 lo = *reinterpret_cast<const uint4*>(ab + r * BK + (((2 * g) ^ (r & 7)) << 4));
-      const uint4 hi = *reinterpret_cast<const uint4*>(ab + r * BK + (((2 * g + 1) ^ (r & 7)) << 4));
-      af[i] = join(lo, hi);
-    }
+      for (int s = 0; s < KS; ++s) {
+        i32x8 af[TM], bf[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int r = wn * WTN + j * 16 + (lane & 15);
-      const uint4 lo = *reinterpret_cast<const uint4*>(bb + r * BK + (((2 * g) ^ (r & 7)) << 4));
-      const uint4 hi = *reinterpret_cast<const uint4*>(bb + r * BK + (((2 * g + 1) ^ (r & 7)) << 4));
-      bf[j] = join(lo, hi);
-    }
+        for (int i = 0; i < TM; ++i) af[i] = frag(ab, wm * WTM + i * 32 + r32, s);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int j = 0; j < TN; ++j) bf[j] = frag(bb, wn * WTN + j * 32 + r32, s);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        if (KIND == kChannelwise) {
-          acc[i][j] = mfma_fp8(bf[j], af[i], acc[i][j]);
-        } else {
-          const f32x4 t = mfma_fp8(bf[j], af[i], f32x4{0.f, 0.f, 0.f, 0.f});
-          const float sc = sa_cur[i] * sb_cur[j];
-          acc[i][j] += t * sc;
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma32_fp8(bf[j], af[i], acc[i][j]);
+      }
+    } else {
+      // each 128-deep K block's partial product is scaled before it joins
+      // the accumulator
+#pragma unroll
+      for (int b = 0; b < KB; ++b) {
+        i32x8 af0[TM], af1[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          af0[i] = frag(ab, wm * WTM + i * 32 + r32, 2 * b);
+          af1[i] = frag(ab, wm * WTM + i * 32 + r32, 2 * b + 1);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const i32x8 bf0 = frag(bb, wn * WTN + j * 32 + r32, 2 * b);
+          const i32x8 bf1 = frag(bb, wn * WTN + j * 32 + r32, 2 * b + 1);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            f32x16 t = mfma32_fp8(bf0, af0[i], zero16());
+            t = mfma32_fp8(bf1, af1[i], t);
+            const float sc = sa_cur[b][i] * sb_cur[b][j];
+            acc[i][j] += t * sc;
+          }
         }
       }
+    }
 
     if (has_next) swrite(buf ^ 1);
     __syncthreads();
   }
 
   if (p.split_k > 1) {
-    // partial layout: [tile][split][TM*TN][NT] float4 (register order)
-    f32x4* part = reinterpret_cast<f32x4*>(p.ws_part) +
-                  ((tile * p.split_k) * (TM * TN)) * NT;
-    f32x4* mine = part + (int64_t)split * (TM * TN) * NT;
+    // Partial tiles live in the workspace as [tile][split][TM*TN*16][NT]
+    // floats (register order, so every store and load is coalesced). Every
+    // access to them is an agent-scope atomic: stores write through to the
+    // device coherence point and loads read from it, so no L2-wide
+    // write-back or invalidate fence is needed between XCDs.
+    constexpr int Q = TM * TN * 16;
+    float* part = p.ws_part + (tile * p.split_k) * (int64_t)Q * NT;
+    float* mine = part + (int64_t)split * Q * NT;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) mine[(i * TN + j) * NT + tid] = acc[i][j];
-    __threadfence();
-    __syncthreads();
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __hip_atomic_store(mine + ((i * TN + j) * 16 + r) * NT + tid, acc[i][j][r],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+    __syncthreads();                 // ... and so have the whole workgroup's
     if (tid == 0) {
       const int old = atomicAdd(p.ws_count + tile, 1);
       last_flag = (old == p.split_k - 1);
     }
     __syncthreads();
     if (!last_flag) return;
-    __threadfence();
+    // last split to arrive: sum the partials in split order (deterministic)
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        f32x4 s = part[(i * TN + j) * NT + tid];
-        for (int sp = 1; sp < p.split_k; ++sp) s += part[((int64_t)sp * TM * TN + i * TN + j) * NT + tid];
-        acc[i][j] = s;
-      }
-    if (tid == 0) p.ws_count[tile] = 0;
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t idx = (int64_t)((i * TN + j) * 16 + r) * NT + tid;
+          float v = __hip_atomic_load(part + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int sp = 1; sp < p.split_k; ++sp)
+            v += __hip_atomic_load(part + (int64_t)sp * Q * NT + idx, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+          acc[i][j][r] = v;
+        }
+    if (tid == 0) __hip_atomic_store(p.ws_count + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t m = m0 + wm * WTM + i * 16 + (lane & 15);
+    const int64_t m = m0 + wm * WTM + i * 32 + r32;
     const float sa_m = (KIND == kChannelwise && m < p.M) ? p.sa[m] : 1.0f;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int64_t n = n0 + wn * WTN + j * 16 + 4 * g;
-      store_out4<KIND>(p, m, n, acc[i][j], sa_m);
-    }
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = n0 + wn * WTN + j * 32 + 8 * q + 4 * h;
+        store_out4<KIND>(p, m, n,
+                         f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                               acc[i][j][4 * q + 3]},
+                         sa_m);
+      }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Skinny kernel for M <= 16*MT: the weight is read exactly once, straight into
-// registers (no LDS staging: each weight byte feeds one MFMA). A workgroup owns
-// one 16-wide column tile of the output; its W waves split K into 512-byte
-// chunks (wave w takes chunks w, w+W, ...), each lane loading four 32-byte
-// pieces of its weight row per chunk. The W partial 16x16 tiles are summed
-// through LDS in wave order (deterministic) and wave 0 runs the epilogue.
-// The activation rows (at most 32) stay cache-resident and are re-read per
-// chunk; lanes whose row is >= M load nothing.
+// Skinny kernel for M <= 16*MT: the weight is streamed from HBM exactly once.
+// A workgroup of 8 waves owns one 16-row weight tile (16 output columns) and
+// walks K in 4 KB chunks. For each chunk, wave w reads weight rows 2w and 2w+1
+// with contiguous 1 KB load instructions (lane i takes bytes 16i..16i+15 of
+// each 1 KB segment) -- reading 16 rows per instruction instead, as the MFMA
+// operand layout would, measured markedly slower on HBM -- and the chunk is
+// re-laid out through LDS ([16 rows][4096 B], 16-byte chunk c of row r at
+// position c ^ r, so the 16 rows of one fragment read hit distinct banks).
+// Wave w then runs the four 128-deep MFMAs of K bytes [512w, 512w+512) of the
+// chunk, with the activation fragments loaded straight from global memory
+// (cache-resident, rows >= M not loaded). The next chunk's loads are issued
+// before the current chunk's MFMAs. The eight partial 16x16 tiles are summed
+// through LDS in wave order (deterministic) and wave t stores row tile t.
+// MFMA K assignment: lane group g = l/16 holds bytes [32g, 32g + 32) of each
+// 128-byte K block for both operands.
 // ---------------------------------------------------------------------------
-template <int MT, int W, int KIND>
-__global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs p) {
-  __shared__ f32x4 red[W][MT][64];
+namespace {
+constexpr int kStreamWaves = 8;
+constexpr int kStreamChunk = 4096;
+}  // namespace
+
+template <int MT>
+struct StreamRegs {
+  uint4 b[2][4];          // rows 2w, 2w+1; four 1 KB segments
+  uint4 a[MT][4][2];      // activation fragments: 4 K blocks x 32 bytes
+};
+
+template <int MT>
+__device__ __forceinline__ void stream_load(const GemmArgs& p, StreamRegs<MT>& r, int64_t k0,
+                                            int64_t n0, int wave, int lane) {
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int64_t n = n0 + 2 * wave + rr;
+    const uint8_t* row = p.b + (n < p.N ? n : 0) * p.ldb;
+#pragma unroll
+    for (int sgm = 0; sgm < 4; ++sgm) {
+      const int64_t off = k0 + sgm * 1024 + lane * 16;
+      r.b[rr][sgm] = (n < p.N && off < p.K) ? load16_nt(row + off) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  const int g = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int64_t m = t * 16 + (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t off = k0 + wave * 512 + j * 128 + g * 32;
+      const bool ok0 = m < p.M && off < p.K;        // K is a multiple of 16 only
+      const bool ok1 = m < p.M && off + 16 < p.K;
+      r.a[t][j][0] = ok0 ? load16(p.a + m * p.lda + off) : make_uint4(0, 0, 0, 0);
+      r.a[t][j][1] = ok1 ? load16(p.a + m * p.lda + off + 16) : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+template <int MT, int KIND>
+__global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs p) {
+  __shared__ uint4 wt[16 * (kStreamChunk / 16)];  // 64 KB: one weight chunk
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;
+  const int r16 = lane & 15;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t nrow = n0 + (lane & 15);
-  const bool n_ok = nrow < p.N;
-  const int64_t kc_all = (p.K + 511) / 512;
   const int64_t kb_all = p.K / 128;
 
   f32x4 acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint8_t* brow = p.b + nrow * p.ldb;
-  for (int64_t kc = wave; kc < kc_all; kc += W) {
-    uint4 bq[4][2];
-    uint4 aq[MT][4][2];
+  StreamRegs<MT> cur;
+  stream_load<MT>(p, cur, 0, n0, wave, lane);
+  for (int64_t k0 = 0; k0 < p.K; k0 += kStreamChunk) {
+    __syncthreads();  // the previous chunk's fragment reads are done
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t off = kc * 512 + j * 128 + g * 32;
-      const bool k0 = off < p.K, k1 = off + 16 < p.K;
-      bq[j][0] = (n_ok && k0) ? load16_nt(brow + off)
-                              : make_uint4(0, 0, 0, 0);
-      bq[j][1] = (n_ok && k1) ? load16_nt(brow + off + 16)
-                              : make_uint4(0, 0, 0, 0);
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = 2 * wave + rr;
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const int64_t m = t * 16 + (lane & 15);
-        const bool m_ok = m < p.M;
-        const uint8_t* arow = p.a + m * p.lda;
-        aq[t][j][0] = (m_ok && k0) ? load16(arow + off) : make_uint4(0, 0, 0, 0);
-        aq[t][j][1] = (m_ok && k1) ? load16(arow + off + 16) : make_uint4(0, 0, 0, 0);
+      for (int sgm = 0; sgm < 4; ++sgm) {
+        const int c = sgm * 64 + lane;
+        wt[r * (kStreamChunk / 16) + (c ^ r)] = cur.b[rr][sgm];
       }
     }
+    __syncthreads();
+    StreamRegs<MT> use = cur;
+    if (k0 + kStreamChunk < p.K) stream_load<MT>(p, cur, k0 + kStreamChunk, n0, wave, lane);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const i32x8 bf = join(bq[j][0], bq[j][1]);
+      const int64_t kbase = k0 + wave * 512 + j * 128;
+      if (kbase >= p.K) break;
+      const int c0 = (wave * 512 + j * 128 + g * 32) / 16;
+      const uint4 lo = wt[r16 * (kStreamChunk / 16) + (c0 ^ r16)];
+      const uint4 hi = wt[r16 * (kStreamChunk / 16) + ((c0 + 1) ^ r16)];
+      const i32x8 bf = join(lo, hi);
       if (KIND == kChannelwise) {
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[t] = mfma_fp8(bf, join(aq[t][j][0], aq[t][j][1]), acc[t]);
+        for (int t = 0; t < MT; ++t) acc[t] = mfma_fp8(bf, join(use.a[t][j][0], use.a[t][j][1]), acc[t]);
       } else {
-        const int64_t kb = kc * 4 + j;
-        if (kb < kb_all) {
-          const float sb = p.sb[(n0 / 128) * kb_all + kb];
+        const int64_t kb = kbase / 128;
+        const float sb = p.sb[(n0 / 128) * kb_all + kb];
 #pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            const int64_t m = t * 16 + (lane & 15);
-            const float sa = (m < p.M) ? p.sa[kb * p.sa_ld + m] : 0.0f;
-            const f32x4 r = mfma_fp8(bf, join(aq[t][j][0], aq[t][j][1]), f32x4{0.f, 0.f, 0.f, 0.f});
-            acc[t] += r * (sa * sb);
-          }
+        for (int t = 0; t < MT; ++t) {
+          const int64_t m = t * 16 + r16;
+          const float sa = (m < p.M) ? p.sa[kb * p.sa_ld + m] : 0.0f;
+          const f32x4 part =
+              mfma_fp8(bf, join(use.a[t][j][0], use.a[t][j][1]), f32x4{0.f, 0.f, 0.f, 0.f});
+          acc[t] += part * (sa * sb);
         }
       }
     }
   }
 
-#pragma unroll
-  for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
+  // cross-wave reduction through the (now idle) weight buffer
   __syncthreads();
-  if (wave != 0) return;
+  f32x4* red = reinterpret_cast<f32x4*>(wt);  // [W][MT][64]
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    f32x4 s = red[0][t][lane];
+  for (int t = 0; t < MT; ++t) red[(wave * MT + t) * 64 + lane] = acc[t];
+  __syncthreads();
+  if (wave >= MT) return;
+  const int t = wave;
+  f32x4 sum = red[t * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < W; ++w) s += red[w][t][lane];
-    const int64_t m = t * 16 + (lane & 15);
-    const float sa_m = (KIND == kChannelwise && m < p.M) ? p.sa[m] : 1.0f;
-    store_out4<KIND>(p, m, n0 + 4 * g, s, sa_m);
-  }
+  for (int w = 1; w < kStreamWaves; ++w) sum += red[(w * MT + t) * 64 + lane];
+  const int64_t m = t * 16 + r16;
+  const float sa_m = (KIND == kChannelwise && m < p.M) ? p.sa[m] : 1.0f;
+  store_out4<KIND>(p, m, n0 + 4 * g, sum, sa_m);
 }
 
 // ---------------------------------------------------------------------------
 // Variant table and launch.
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kSkinnyWaves = 8;
 
-template <int BM, int BN, int WM, int WN, int KIND>
+template <int BM, int BN, int WM, int WN, int BK, int KIND>
 hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  const size_t lds = (size_t)2 * (BM + BN) * 128;
-  auto kern = gemm_tile_kernel<BM, BN, WM, WN, KIND>;
+  const size_t lds = (size_t)2 * (BM + BN) * BK;
+  auto kern = gemm_tile_kernel<BM, BN, WM, WN, BK, KIND>;
   static bool lds_attr_set = false;  // per instantiation; setting it twice is harmless
   if (lds > 65536 && !lds_attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -383,17 +526,23 @@ template <int KIND>
 hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
   switch (variant) {
     case 0: {  // FP8_VARIANT_SKINNY
-      const dim3 grid((unsigned)((p.N + 15) / 16)), block(kSkinnyWaves * 64);
+      const dim3 grid((unsigned)((p.N + 15) / 16)), block(kStreamWaves * 64);
       if (p.M <= 16)
-        hipLaunchKernelGGL((gemm_skinny_kernel<1, kSkinnyWaves, KIND>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((gemm_skinny_kernel<1, KIND>), grid, block, 0, stream, p);
       else
-        hipLaunchKernelGGL((gemm_skinny_kernel<2, kSkinnyWaves, KIND>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((gemm_skinny_kernel<2, KIND>), grid, block, 0, stream, p);
       return hipGetLastError();
     }
-    case 1: return launch_tile<64, 64, 2, 2, KIND>(p, stream);
-    case 2: return launch_tile<128, 128, 2, 2, KIND>(p, stream);
-    case 3: return launch_tile<256, 128, 4, 2, KIND>(p, stream);
-    case 4: return launch_tile<256, 256, 2, 4, KIND>(p, stream);
+    case 1: return launch_tile<64, 64, 2, 2, 512, KIND>(p, stream);
+    case 2: return launch_tile<128, 128, 2, 2, 128, KIND>(p, stream);
+    case 3: return launch_tile<256, 128, 2, 2, 128, KIND>(p, stream);
+    case 4: return launch_tile<256, 256, 2, 2, 128, KIND>(p, stream);
+    case 5: return launch_tile<256, 256, 2, 4, 128, KIND>(p, stream);
+    case 6: return launch_tile<256, 128, 4, 2, 128, KIND>(p, stream);
+    case 7: return launch_tile<128, 128, 2, 4, 128, KIND>(p, stream);
+    case 8: return launch_tile<128, 64, 2, 2, 256, KIND>(p, stream);
+    case 9: return launch_tile<64, 128, 2, 2, 256, KIND>(p, stream);
+    case 10: return launch_tile<128, 128, 2, 2, 256, KIND>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -401,11 +550,17 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
 
 VariantInfo variant_info(int variant) {
   switch (variant) {
-    case 0: return {32, 16, 512, kSkinnyWaves, true};
-    case 1: return {64, 64, 128, 4, true};
+    case 0: return {32, 16, 4096, 8, true};
+    case 1: return {64, 64, 512, 4, true};
     case 2: return {128, 128, 128, 4, true};
-    case 3: return {256, 128, 128, 8, true};
-    case 4: return {256, 256, 128, 8, true};
+    case 3: return {256, 128, 128, 4, true};
+    case 4: return {256, 256, 128, 4, true};
+    case 5: return {256, 256, 128, 8, true};
+    case 6: return {256, 128, 128, 8, true};
+    case 7: return {128, 128, 128, 8, true};
+    case 8: return {128, 64, 256, 4, true};
+    case 9: return {64, 128, 256, 4, true};
+    case 10: return {128, 128, 256, 4, true};
     default: return {0, 0, 0, 0, false};
   }
 }

@@ -171,6 +171,12 @@ int variant_from_name(const std::string& n) {
   if (n == "t128x128") return FP8_VARIANT_T128x128;
   if (n == "t256x128") return FP8_VARIANT_T256x128;
   if (n == "t256x256") return FP8_VARIANT_T256x256;
+  if (n == "t256x256w8") return FP8_VARIANT_T256x256W8;
+  if (n == "t256x128w8") return FP8_VARIANT_T256x128W8;
+  if (n == "t128x128w8") return FP8_VARIANT_T128x128W8;
+  if (n == "t128x64k256") return FP8_VARIANT_T128x64K256;
+  if (n == "t64x128k256") return FP8_VARIANT_T64x128K256;
+  if (n == "t128x128k256") return FP8_VARIANT_T128x128K256;
   return -100;
 }
 

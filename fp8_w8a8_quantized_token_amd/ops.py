@@ -24,7 +24,7 @@ from . import _lib
 from ._lib import KIND_BLOCKWISE, KIND_CHANNELWISE, TileConfig, VARIANTS, check
 
 __all__ = [
-    "padded_rows", "quant_per_token", "quant_per_token_group", "scaled_mm_channelwise",
+    "prepare", "padded_rows", "quant_per_token", "quant_per_token_group", "scaled_mm_channelwise",
     "scaled_mm_blockwise", "linear_channelwise", "linear_blockwise", "tile_config",
     "default_tile_config", "set_config_dir", "workspace_bytes", "make_config",
 ]
@@ -240,3 +240,63 @@ def default_tile_config(kind, n, k, m):
 
 def set_config_dir(path):
     _lib.load().fp8_tile_config_set_dir(None if path is None else str(path).encode())
+
+
+# ---------------------------------------------------------------- prepared launches
+class Prepared:
+    """A launch with every argument resolved up front: calling it is one ctypes
+    call on the stream that was current when it was prepared. For hot loops
+    whose tensors and shapes do not change (the benchmark, serving loops)."""
+
+    def __init__(self, fn, args, name):
+        self._fn, self._args, self.name = fn, args, name
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            check(st)
+
+
+def prepare(op, *args, **kwargs):
+    """prepare("quant_per_token", x, out=q, scale=s), prepare("quant_per_token_group",
+    x, group_size, row_alignment=4, out=q, scale_storage=st),
+    prepare("scaled_mm_channelwise", a, b, a_scale, b_scale, bias=None, out=out, config=None),
+    prepare("scaled_mm_blockwise", a, b, a_scale, b_scale, bias=None, m=None, out=out,
+    config=None): validate once (by running the op once) and return a Prepared."""
+    lib = _lib.load()
+    globals()[op](*args, **kwargs)  # validates and raises on bad arguments
+    if op == "quant_per_token":
+        x = args[0]
+        q, s = kwargs["out"], kwargs["scale"]
+        a = (_p(x), x.shape[0], x.shape[1], x.stride(0), _p(q), q.stride(0), _p(s),
+             ctypes.c_float(kwargs.get("eps", 1e-10)), _stream(x))
+        return Prepared(lib.fp8_quant_per_token, a, op)
+    if op == "quant_per_token_group":
+        x, g = args[0], args[1]
+        q, st = kwargs["out"], kwargs["scale_storage"]
+        a = (_p(x), x.shape[0], x.shape[1], x.stride(0), g, kwargs.get("row_alignment", 4), _p(q),
+             q.stride(0), _p(st), ctypes.c_float(kwargs.get("eps", 1e-10)), _stream(x))
+        return Prepared(lib.fp8_quant_per_token_group, a, op)
+    if op in ("scaled_mm_channelwise", "scaled_mm_blockwise"):
+        a_, b_, sa, sb = _as_codes(args[0], "a"), _as_codes(args[1], "b"), args[2], args[3]
+        bias, out = kwargs.get("bias"), kwargs["out"]
+        cfg = kwargs.get("config") or TileConfig(-1, 0, 0, 0, 1, 0)
+        n, k = b_.shape[0], a_.shape[1]
+        if op == "scaled_mm_channelwise":
+            m = a_.shape[0]
+            nws = workspace_bytes(KIND_CHANNELWISE, m, n, k, cfg)
+            ws = _ws.get(a_.device, nws)
+            a = (_p(a_), _p(b_), _p(sa), _p(sb), _p(bias), _p(out), m, n, k, a_.stride(0),
+                 b_.stride(0), out.stride(0), _p(ws), nws, ctypes.byref(cfg), _stream(a_))
+            pr = Prepared(lib.fp8_scaled_mm_channelwise_ex, a, op)
+        else:
+            m = kwargs.get("m") or a_.shape[0]
+            nws = workspace_bytes(KIND_BLOCKWISE, m, n, k, cfg)
+            ws = _ws.get(a_.device, nws)
+            a = (_p(a_), _p(b_), _p(sa), sa.stride(1), _p(sb), _p(bias), _p(out), m, n, k,
+                 a_.stride(0), b_.stride(0), out.stride(0), _p(ws), nws, ctypes.byref(cfg),
+                 _stream(a_))
+            pr = Prepared(lib.fp8_scaled_mm_blockwise_ex, a, op)
+        pr._keep = (cfg, ws)  # keep the config struct and workspace alive
+        return pr
+    raise ValueError(f"unknown op {op}")

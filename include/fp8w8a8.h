@@ -59,12 +59,18 @@ enum { FP8_KIND_CHANNELWISE = 0, FP8_KIND_BLOCKWISE = 1 };
 /* Kernel variants a tile config can name. */
 enum {
   FP8_VARIANT_DEFAULT = -1, /* let the library choose */
-  FP8_VARIANT_SKINNY = 0,   /* M <= 16 rows: one 16-row MFMA tile, weight streamed once */
-  FP8_VARIANT_T64x64 = 1,   /* 64x64 block tile, 4 waves */
-  FP8_VARIANT_T128x128 = 2, /* 128x128 block tile, 4 waves */
-  FP8_VARIANT_T256x128 = 3, /* 256x128 block tile, 8 waves */
-  FP8_VARIANT_T256x256 = 4, /* 256x256 block tile, 8 waves */
-  FP8_VARIANT_COUNT = 5,
+  FP8_VARIANT_SKINNY = 0,      /* M <= 32 rows: weight streamed once, K split over waves */
+  FP8_VARIANT_T64x64 = 1,      /* 64x64 block tile, 512-deep K stages, 4 waves */
+  FP8_VARIANT_T128x128 = 2,    /* 128x128 block tile, 4 waves */
+  FP8_VARIANT_T256x128 = 3,    /* 256x128 block tile, 4 waves */
+  FP8_VARIANT_T256x256 = 4,    /* 256x256 block tile, 4 waves */
+  FP8_VARIANT_T256x256W8 = 5,  /* 256x256 block tile, 8 waves */
+  FP8_VARIANT_T256x128W8 = 6,  /* 256x128 block tile, 8 waves */
+  FP8_VARIANT_T128x128W8 = 7,  /* 128x128 block tile, 8 waves */
+  FP8_VARIANT_T128x64K256 = 8, /* 128x64 block tile, 256-deep K stages, 4 waves */
+  FP8_VARIANT_T64x128K256 = 9, /* 64x128 block tile, 256-deep K stages, 4 waves */
+  FP8_VARIANT_T128x128K256 = 10, /* 128x128 block tile, 256-deep K stages, 4 waves */
+  FP8_VARIANT_COUNT = 11,
 };
 
 /* One tile configuration of the scaled GEMM. The PR34331 digest ("Key source

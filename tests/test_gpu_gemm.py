@@ -92,7 +92,10 @@ def test_blockwise_workloads(wl, m, n, k):
 # ---------------------------------------------------------------- every kernel variant
 VARIANT_CASES = [(v, sk) for v, sk in (("skinny", 1), ("t64x64", 1), ("t64x64", 3), ("t128x128", 1),
                                        ("t128x128", 2), ("t256x128", 1), ("t256x128", 4),
-                                       ("t256x256", 1), ("t256x256", 2))]
+                                       ("t256x256", 1), ("t256x256", 2), ("t256x256w8", 1),
+                                       ("t256x128w8", 2), ("t128x128w8", 1), ("t128x64k256", 1),
+                                       ("t128x64k256", 3), ("t64x128k256", 2), ("t128x128k256", 1),
+                                       ("t128x128k256", 2))]
 
 
 @pytest.mark.parametrize("variant,split_k", VARIANT_CASES, ids=[f"{v}-sk{s}" for v, s in VARIANT_CASES])
@@ -104,8 +107,10 @@ def test_channelwise_variants_ragged(variant, split_k):
     _channelwise_case("ragged", m, n, k, 0.0, True, config=cfg, sample=False)
 
 
-BW_VARIANTS = [(v, sk) for v, sk in (("skinny", 1), ("t64x64", 1), ("t64x64", 5), ("t128x128", 1),
-                                     ("t128x128", 3), ("t256x128", 2))]
+BW_VARIANTS = [(v, sk) for v, sk in (("skinny", 1), ("t64x64", 1), ("t64x64", 2), ("t128x128", 1),
+                                     ("t128x128", 3), ("t256x128", 2), ("t256x128w8", 1),
+                                     ("t128x128w8", 2), ("t128x64k256", 1), ("t128x64k256", 2),
+                                     ("t64x128k256", 1), ("t128x128k256", 2))]
 
 
 @pytest.mark.parametrize("variant,split_k", BW_VARIANTS, ids=[f"{v}-sk{s}" for v, s in BW_VARIANTS])
@@ -213,3 +218,12 @@ def test_linear_wrappers_match_oracle():
     tau = oracle.summation_bound_blockwise(gq, bq, gs, bs)
     assert y.shape == (37, 384)
     _check(bf16_to_f64(y), ref, tau, "linear_blockwise")
+
+
+def test_split_k_back_to_back_calls_see_fresh_partials():
+    """Two split-K calls of the same shape on different data, back to back on
+    one workspace: the second must not read the first call's partial tiles."""
+    for cfg in (ops.make_config("t64x64", 4), ops.make_config("t128x128k256", 2)):
+        _channelwise_case("o_proj", 192, 4096, 4096, 0.01, False, config=cfg, sample=False)
+        _channelwise_case("qwen3_8b", 192, 4096, 4096, 0.0, True, config=cfg, sample=False)
+        _channelwise_case("o_proj", 192, 4096, 4096, 0.01, False, config=cfg, sample=False)
