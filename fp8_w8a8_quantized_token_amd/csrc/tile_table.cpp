@@ -266,33 +266,41 @@ bool tables_enabled() {
 }  // namespace
 
 int default_config(int kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* out) {
-  const int cus = 256;  // MI355X compute units
-  const int64_t kt_all = (K + 127) / 128;
+  // Measured on MI355X (o_proj N = K = 4096): the weight-streaming kernel up
+  // to 32 rows, then ever larger tiles as M grows. A tile is taken only if it
+  // gives at least half the 256 compute units a workgroup; the 64x64 tile is
+  // the fallback. Split-K never won in those measurements, so it is left to
+  // the tuned tables.
+  (void)K;
   fp8_tile_config c{};
   c.split_k = 1;
   if (M <= 32) {
     c.variant = FP8_VARIANT_SKINNY;
   } else {
-    c.variant = -1;
-    const int order[] = {FP8_VARIANT_T256x256, FP8_VARIANT_T256x128, FP8_VARIANT_T128x128,
-                         FP8_VARIANT_T64x64};
-    for (int v : order) {
-      // the blockwise 256x256 tile runs out of registers; keep it for explicit use
-      if (kind == FP8_KIND_BLOCKWISE && v == FP8_VARIANT_T256x256) continue;
-      const int64_t tiles = variant_tiles(v, M, N);
-      const int64_t rounds = (tiles + cus - 1) / cus;
-      if ((double)tiles / (double)(rounds * cus) >= 0.75) {
-        c.variant = v;
+    int order[4];
+    int n = 0;
+    if (M <= 256) {
+      order[n++] = FP8_VARIANT_T64x64;
+    } else if (M <= 512) {
+      order[n++] = FP8_VARIANT_T128x64K256;
+    } else if (M <= 1024) {
+      order[n++] = FP8_VARIANT_T128x128K256;
+      order[n++] = FP8_VARIANT_T128x64K256;
+    } else if (M <= 2048) {
+      order[n++] = FP8_VARIANT_T256x128W8;
+      order[n++] = FP8_VARIANT_T128x128K256;
+    } else {
+      // the blockwise 256x256 tiles run out of registers
+      if (kind != FP8_KIND_BLOCKWISE) order[n++] = FP8_VARIANT_T256x256W8;
+      order[n++] = FP8_VARIANT_T256x128W8;
+      order[n++] = FP8_VARIANT_T128x128K256;
+    }
+    c.variant = FP8_VARIANT_T64x64;
+    for (int i = 0; i < n; ++i) {
+      if (variant_tiles(order[i], M, N) >= 128) {
+        c.variant = order[i];
         break;
       }
-    }
-    if (c.variant < 0) {
-      c.variant = M >= 128 ? FP8_VARIANT_T128x128 : FP8_VARIANT_T64x64;
-      const int64_t tiles = variant_tiles(c.variant, M, N);
-      int64_t sk = (cus + tiles - 1) / tiles;
-      const int64_t max_sk = std::max<int64_t>(1, kt_all / 4);
-      sk = std::max<int64_t>(1, std::min<int64_t>(sk, max_sk));
-      c.split_k = (int)sk;
     }
   }
   const VariantInfo vi = variant_info(c.variant);
