@@ -53,13 +53,14 @@ __global__ __launch_bounds__(256) void quant_per_token_kernel(
   float m = wave_part[0];
   for (int w = 1; w < (nthr >> 6); ++w) m = fmaxf(m, wave_part[w]);
   const float s = fmaxf(m, eps) / kE4M3Max;
+  const float y = 1.0f / s;
   if (threadIdx.x == 0) scale[row] = s;
 #pragma unroll
   for (int i = 0; i < UNITS; ++i) {
     const int u = threadIdx.x + i * nthr;
     if (u < units) {
-      const uint2 lo = quant8_bf16(v[i][0], s);
-      const uint2 hi = quant8_bf16(v[i][1], s);
+      const uint2 lo = quant8_bf16(v[i][0], s, y);
+      const uint2 hi = quant8_bf16(v[i][1], s, y);
       *reinterpret_cast<uint4*>(qr + (int64_t)u * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
   }
@@ -86,11 +87,12 @@ __global__ __launch_bounds__(256) void quant_per_token_long_kernel(
   float m = wave_part[0];
   for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, wave_part[w]);
   const float s = fmaxf(m, eps) / kE4M3Max;
+  const float y = 1.0f / s;
   if (threadIdx.x == 0) scale[row] = s;
   for (int64_t u = threadIdx.x; u < units; u += blockDim.x) {
     const uint4* src = reinterpret_cast<const uint4*>(xr + u * 16);
-    const uint2 lo = quant8_bf16(src[0], s);
-    const uint2 hi = quant8_bf16(src[1], s);
+    const uint2 lo = quant8_bf16(src[0], s, y);
+    const uint2 hi = quant8_bf16(src[1], s, y);
     *reinterpret_cast<uint4*>(qr + u * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
 }
@@ -121,9 +123,10 @@ __global__ __launch_bounds__(256) void quant_group_kernel(
 #pragma unroll
   for (int off = TPG / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
   const float s = fmaxf(amax, eps) / kE4M3Max;
+  const float y = 1.0f / s;
   if (live) {
-    const uint2 lo = quant8_bf16(v0, s);
-    const uint2 hi = quant8_bf16(v1, s);
+    const uint2 lo = quant8_bf16(v0, s, y);
+    const uint2 hi = quant8_bf16(v1, s, y);
     *reinterpret_cast<uint4*>(q + row * ldq + col_unit * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
     if ((col_unit & (TPG - 1)) == 0) {
       const int64_t g = col_unit / TPG;
