@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-m", action="store_true", help="also print a per-(M, kind) table")
+    ap.add_argument("--profile-label", default="",
+                    help="run only the step's launches with this label (after a plain 256 MiB "
+                         "device copy used to calibrate HBM byte counters), for rocprofv3 --pmc")
     return ap.parse_args()
 
 
@@ -109,6 +112,33 @@ def build_step(torch, ops, synth, dev):
     return launches
 
 
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "fp8_w8a8_quantized_token_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(label):
+    """HBM bytes per launch of `label` from a committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (profiles/*_traffic.txt), or None when there is none or
+    the kernel sources changed since the counters were taken."""
+    import glob
+    cur = kernel_source_hash()
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*_traffic.txt")):
+        kv = {}
+        with open(path) as fh:
+            for line in fh:
+                if ": " in line and not line.startswith(" "):
+                    k, v = line.rstrip("\n").split(": ", 1)
+                    kv[k] = v
+        if kv.get("label") == label and kv.get("source_sha256") == cur:
+            return float(kv["traffic_bytes_per_launch"])
+    return None
+
+
 def cpu_baseline():
     """The oracle (numpy, fp64 GEMM) on a bounded sample of the same workload."""
     import numpy as np
@@ -152,6 +182,23 @@ def main():
     _lib.load()
     dev = torch.device("cuda:0")
     launches = build_step(torch, ops, synth, dev)
+    if args.profile_label:
+        # counter collection: a plain copy of known size, then the labelled launches
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        sel = [l for l in launches if l.label == args.profile_label]
+        if not sel:
+            sys.exit(f"no launch labelled {args.profile_label}")
+        for l in sel:
+            l.fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"profiled": args.profile_label, "launches": len(sel),
+                          "m": [getattr(l, "m", None) for l in sel],
+                          "bytes": [l.nbytes for l in sel], "flops": [l.flops for l in sel]}),
+              flush=True)
+        return
     flops_step = sum(l.flops for l in launches)
     bytes_step = sum(l.nbytes for l in launches)
 
@@ -197,7 +244,7 @@ def main():
         roof = {"bound": "hbm", "achieved": bytes_launch / avg / 1e9, "peak": PEAK_GBPS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom_label)
     roof["kernel"] = dom_label
     roof["avg_launch_us"] = avg * 1e6
     roof["launches_per_step"] = dom["count"] // args.steps
