@@ -10,8 +10,11 @@ touches ~1 GB and the 256 MB last-level cache cannot serve the weights.
 
 Output: one JSON line. ``value`` is the step's GEMM TFLOP/s (sum of 2MNK over
 the step time, quant included in the time). ``roofline`` reports the kernel
-with the largest share of GPU time, timed with HIP events on the stream the
-kernels run on. ``cpu_baseline`` times the CPU oracle on a bounded sample.
+with the largest share of GPU time: an untimed pass with HIP events around
+every launch picks it, and inside the timed steps HIP events (on the stream
+the kernels run on) bracket only that kernel's launches, so the step time is
+not inflated by per-launch event records. ``cpu_baseline`` times the CPU
+oracle on a bounded sample.
 """
 import argparse
 import json
@@ -207,33 +210,53 @@ def main():
             l.fn()
     torch.cuda.synchronize()
 
-    # events on the stream the kernels are launched on (torch's current stream)
+    # Identification pass (untimed): events around every launch give each
+    # kernel's share of the step and the per-(kind, M) table.
+    probe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in launches]
+    for (e0, e1), l in zip(probe, launches):
+        e0.record()
+        l.fn()
+        e1.record()
+    torch.cuda.synchronize()
+    share = {}
+    per_m = {}
+    for (e0, e1), l in zip(probe, launches):
+        us = e0.elapsed_time(e1) * 1e3
+        share[l.label] = share.get(l.label, 0.0) + us
+        key = f"{l.kind}/{'quant' if l.flops == 0 else 'gemm'}/M={l.m}"
+        per_m[key] = {"us_event": us, "flops": l.flops, "bytes": l.nbytes}
+    dom_label = max(share, key=share.get)
+    dom_idx = [i for i, l in enumerate(launches) if l.label == dom_label]
+
+    # Timed region: K whole steps; HIP events (on the launch stream, torch's
+    # current stream) bracket only the dominant kernel's launches.
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in launches] for _ in range(args.steps)]
+           for _ in dom_idx] for _ in range(args.steps)]
+    dom_set = set(dom_idx)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
+        j = 0
         for i, l in enumerate(launches):
-            ev[s][i][0].record()
-            l.fn()
-            ev[s][i][1].record()
+            if i in dom_set:
+                ev[s][j][0].record()
+                l.fn()
+                ev[s][j][1].record()
+                j += 1
+            else:
+                l.fn()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
 
-    per_label = {}
-    per_m = {}
-    for i, l in enumerate(launches):
-        durs = [ev[s][i][0].elapsed_time(ev[s][i][1]) * 1e-3 for s in range(args.steps)]
-        d = per_label.setdefault(l.label, {"count": 0, "time": 0.0, "flops": 0, "bytes": 0})
-        d["count"] += len(durs)
-        d["time"] += sum(durs)
-        d["flops"] += l.flops * len(durs)
-        d["bytes"] += l.nbytes * len(durs)
-        key = f"{l.kind}/{'quant' if l.flops == 0 else 'gemm'}/M={l.m}"
-        per_m[key] = {"us": 1e6 * sorted(durs)[len(durs) // 2], "flops": l.flops, "bytes": l.nbytes}
-
-    dom_label, dom = max(per_label.items(), key=lambda kv: kv[1]["time"])
+    dom = {"count": 0, "time": 0.0, "flops": 0, "bytes": 0}
+    for s in range(args.steps):
+        for j, i in enumerate(dom_idx):
+            dom["count"] += 1
+            dom["time"] += ev[s][j][0].elapsed_time(ev[s][j][1]) * 1e-3
+            dom["flops"] += launches[i].flops
+            dom["bytes"] += launches[i].nbytes
     avg = dom["time"] / dom["count"]
     flops_launch = dom["flops"] / dom["count"]
     bytes_launch = dom["bytes"] / dom["count"]
