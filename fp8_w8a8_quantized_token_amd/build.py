@@ -26,6 +26,8 @@ FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Wall",
     "-Wno-unused-function",
+    # M0 is clobbered on purpose by the LDS-DMA loads (see gemm.hip)
+    "-Wno-inline-asm",
 ]
 
 

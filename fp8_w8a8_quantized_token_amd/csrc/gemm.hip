@@ -373,6 +373,221 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Deep-pipeline tiled kernel (channelwise): BM x BN block tile, 64-byte K
+// stages, WM x WN waves with 32x32 MFMA tiles as above. Global -> LDS copies
+// use the LDS-DMA form of the 16-byte global load (global_load_lds_dwordx4:
+// each lane's 16 bytes land at M0 + 16*lane, no registers involved), so
+// NSTAGE LDS stages can be in flight at once: while stage s is multiplied,
+// stages s+1 .. s+NSTAGE-1 are loading. Each wave issues exactly
+// (BM + BN) / 16 / waves such loads per stage; before the barrier that
+// publishes stage s a wave waits until its own outstanding loads are only
+// those of the later stages (vmcnt counts in issue order), and the barrier
+// then also guarantees every wave has finished multiplying stage s-1, whose
+// buffer the next loads overwrite.
+// The loads are written as inline assembly because the compiler, unable to
+// tell which LDS stage a read depends on, would otherwise wait for every
+// outstanding LDS-DMA load before each LDS read and serialize the pipeline;
+// waits the compiler inserts for its own loads count these too and can only
+// wait longer, never shorter.
+// LDS rows are 64 bytes (four 16-byte chunks); chunk c of row r sits at
+// position c ^ ((r >> 2) & 3), which gives the 16 lanes of one fragment read
+// (16 consecutive rows, one chunk column) 16 distinct 16-byte bank groups.
+// A DMA instruction covers 16 rows x 64 bytes, so lane i fetches the global
+// chunk that belongs at LDS position i. Rows at or beyond M (or N) fetch a
+// valid row instead (their outputs are never stored); K must be a multiple
+// of 64 (the host falls back to the register-staged kernel otherwise).
+// ---------------------------------------------------------------------------
+// M0 carries the (wave-uniform) LDS destination; no other instruction of these
+// kernels reads M0 (gfx9-class LDS instructions do not use it).
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0v)
+               : "memory", "m0");
+}
+
+// s_waitcnt with vmcnt = N and the other counters unconstrained (gfx9 layout:
+// vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ int swz64(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+template <int BM, int BN, int WM, int WN, int NSTAGE>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmArgs p) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int NW = WM * WN;
+  constexpr int BK = 64;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int A_BLK = BM / 16, B_BLK = BN / 16;        // 1 KB DMA blocks per stage
+  constexpr int A_PER = A_BLK / NW, B_PER = B_BLK / NW;  // per wave
+  constexpr int PER_WAVE = A_PER + B_PER;
+  constexpr int STAGE_BYTES = (BM + BN) * BK;
+  static_assert(A_BLK % NW == 0 && B_BLK % NW == 0, "DMA blocks per wave");
+  static_assert(TM >= 1 && TN >= 1, "wave tile");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "stages");
+  static_assert(PER_WAVE * (NSTAGE - 1) < 64, "vmcnt range");
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int last_flag;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+
+  const int64_t tiles_n = (p.N + BN - 1) / BN;
+  const int64_t tiles_m = (p.M + BM - 1) / BM;
+  const int64_t tile = blockIdx.x;
+  int64_t tile_m, tile_n;
+  tile_coords(tile, tiles_m, tiles_n, &tile_m, &tile_n);
+  const int64_t m0 = tile_m * BM;
+  const int64_t n0 = tile_n * BN;
+  const int split = blockIdx.y;
+  const int64_t kt_all = p.K / BK;
+  const int64_t kt_begin = (int64_t)split * p.k_tiles_per_split;
+  int64_t kt_end = kt_begin + p.k_tiles_per_split;
+  if (kt_end > kt_all) kt_end = kt_all;
+
+  // per-lane source rows of this wave's DMA blocks (clamped into the matrix)
+  const int lrow = lane >> 2, lpos = lane & 3;
+  const uint8_t* a_src[A_PER];
+  int a_chunk[A_PER];
+#pragma unroll
+  for (int i = 0; i < A_PER; ++i) {
+    const int r = (wave * A_PER + i) * 16 + lrow;
+    int64_t gm = m0 + r;
+    if (gm >= p.M) gm = p.M - 1;
+    a_src[i] = p.a + gm * p.lda;
+    a_chunk[i] = swz64(r, lpos);  // logical chunk stored at position lpos
+  }
+  const uint8_t* b_src[B_PER];
+  int b_chunk[B_PER];
+#pragma unroll
+  for (int i = 0; i < B_PER; ++i) {
+    const int r = (wave * B_PER + i) * 16 + lrow;
+    int64_t gn = n0 + r;
+    if (gn >= p.N) gn = p.N - 1;
+    b_src[i] = p.b + gn * p.ldb;
+    b_chunk[i] = swz64(r, lpos);
+  }
+  auto issue = [&](int64_t kt) {
+    const int buf = (int)((kt - kt_begin) % NSTAGE);
+    const uint32_t a_base = lds_base + buf * STAGE_BYTES;
+    const uint32_t b_base = a_base + BM * BK;
+    const int64_t k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i)
+      lds_dma16(a_src[i] + k0 + a_chunk[i] * 16, a_base + (wave * A_PER + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < B_PER; ++i)
+      lds_dma16(b_src[i] + k0 + b_chunk[i] * 16, b_base + (wave * B_PER + i) * 1024);
+  };
+  auto frag = [&](const uint8_t* base, int r) {
+    const uint8_t* row = base + r * BK;
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + (swz64(r, 2 * h) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + (swz64(r, 2 * h + 1) << 4));
+    return join(lo, hi);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = zero16();
+
+  for (int q = 0; q < NSTAGE - 1; ++q)
+    if (kt_begin + q < kt_end) issue(kt_begin + q);
+
+  for (int64_t kt = kt_begin; kt < kt_end; ++kt) {
+    const int64_t later = kt_end - 1 - kt;  // stages issued after this one (so far)
+    if (later >= NSTAGE - 2) {
+      if (NSTAGE - 2 == 2) wait_vmcnt<2 * PER_WAVE>();
+      else if (NSTAGE - 2 == 1) wait_vmcnt<PER_WAVE>();
+      else wait_vmcnt<0>();
+    } else if (later == 1) {
+      wait_vmcnt<PER_WAVE>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (kt + NSTAGE - 1 < kt_end) issue(kt + NSTAGE - 1);
+
+    const int buf = (int)((kt - kt_begin) % NSTAGE);
+    const uint8_t* ab = lds + buf * STAGE_BYTES;
+    const uint8_t* bb = ab + BM * BK;
+    i32x8 af[TM], bf[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = frag(ab, wm * WTM + i * 32 + r32);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bf[j] = frag(bb, wn * WTN + j * 32 + r32);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32_fp8(bf[j], af[i], acc[i][j]);
+  }
+
+  if (p.split_k > 1) {
+    constexpr int Q = TM * TN * 16;
+    float* part = p.ws_part + (tile * p.split_k) * (int64_t)Q * NT;
+    float* mine = part + (int64_t)split * Q * NT;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __hip_atomic_store(mine + ((i * TN + j) * 16 + r) * NT + tid, acc[i][j][r],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const int old = atomicAdd(p.ws_count + tile, 1);
+      last_flag = (old == p.split_k - 1);
+    }
+    __syncthreads();
+    if (!last_flag) return;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t idx = (int64_t)((i * TN + j) * 16 + r) * NT + tid;
+          float v = __hip_atomic_load(part + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int sp = 1; sp < p.split_k; ++sp)
+            v += __hip_atomic_load(part + (int64_t)sp * Q * NT + idx, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+          acc[i][j][r] = v;
+        }
+    if (tid == 0) __hip_atomic_store(p.ws_count + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t m = m0 + wm * WTM + i * 32 + r32;
+    const float sa_m = (m < p.M) ? p.sa[m] : 1.0f;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = n0 + wn * WTN + j * 32 + 8 * q + 4 * h;
+        store_out4<kChannelwise>(p, m, n,
+                                 f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                       acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]},
+                                 sa_m);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Skinny kernel for M <= 16*MT: the weight is streamed from HBM exactly once.
 // A workgroup of 8 waves owns one 16-row weight tile (16 output columns) and
 // walks K in 4 KB chunks. For each chunk, wave w reads weight rows 2w and 2w+1
@@ -522,6 +737,23 @@ hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int WM, int WN, int NSTAGE>
+hipError_t launch_dma(const GemmArgs& p, hipStream_t stream) {
+  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  const size_t lds = (size_t)NSTAGE * (BM + BN) * 64;
+  auto kern = gemm_dma_kernel<BM, BN, WM, WN, NSTAGE>;
+  static bool lds_attr_set = false;
+  if (lds > 65536 && !lds_attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    lds_attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles, (unsigned)p.split_k), dim3(WM * WN * 64), lds,
+                     stream, p);
+  return hipGetLastError();
+}
+
 template <int KIND>
 hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
   switch (variant) {
@@ -543,6 +775,15 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
     case 8: return launch_tile<128, 64, 2, 2, 256, KIND>(p, stream);
     case 9: return launch_tile<64, 128, 2, 2, 256, KIND>(p, stream);
     case 10: return launch_tile<128, 128, 2, 2, 256, KIND>(p, stream);
+    case 11:
+      if (KIND != kChannelwise || p.K % 64 != 0) return launch_tile<256, 256, 2, 4, 128, KIND>(p, stream);
+      return launch_dma<256, 256, 2, 4, 4>(p, stream);
+    case 12:
+      if (KIND != kChannelwise || p.K % 64 != 0) return launch_tile<256, 128, 4, 2, 128, KIND>(p, stream);
+      return launch_dma<256, 128, 4, 2, 4>(p, stream);
+    case 13:
+      if (KIND != kChannelwise || p.K % 64 != 0) return launch_tile<128, 128, 2, 2, 256, KIND>(p, stream);
+      return launch_dma<128, 128, 2, 2, 4>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -561,6 +802,11 @@ VariantInfo variant_info(int variant) {
     case 8: return {128, 64, 256, 4, true};
     case 9: return {64, 128, 256, 4, true};
     case 10: return {128, 128, 256, 4, true};
+    // deep-pipeline (LDS-DMA) variants, channelwise with K % 64 == 0; other
+    // requests run the register-staged kernel of the same tile shape
+    case 11: return {256, 256, 64, 8, true};
+    case 12: return {256, 128, 64, 8, true};
+    case 13: return {128, 128, 64, 4, true};
     default: return {0, 0, 0, 0, false};
   }
 }

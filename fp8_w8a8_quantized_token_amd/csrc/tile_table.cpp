@@ -177,6 +177,9 @@ int variant_from_name(const std::string& n) {
   if (n == "t128x64k256") return FP8_VARIANT_T128x64K256;
   if (n == "t64x128k256") return FP8_VARIANT_T64x128K256;
   if (n == "t128x128k256") return FP8_VARIANT_T128x128K256;
+  if (n == "t256x256dma") return FP8_VARIANT_T256x256DMA;
+  if (n == "t256x128dma") return FP8_VARIANT_T256x128DMA;
+  if (n == "t128x128dma") return FP8_VARIANT_T128x128DMA;
   return -100;
 }
 

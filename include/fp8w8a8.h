@@ -70,7 +70,13 @@ enum {
   FP8_VARIANT_T128x64K256 = 8, /* 128x64 block tile, 256-deep K stages, 4 waves */
   FP8_VARIANT_T64x128K256 = 9, /* 64x128 block tile, 256-deep K stages, 4 waves */
   FP8_VARIANT_T128x128K256 = 10, /* 128x128 block tile, 256-deep K stages, 4 waves */
-  FP8_VARIANT_COUNT = 11,
+  /* deep pipeline: 4 LDS stages of 64-deep K filled by LDS-DMA loads; used for
+     channelwise GEMMs with K % 64 == 0, other requests run the register-staged
+     kernel of the same tile shape */
+  FP8_VARIANT_T256x256DMA = 11, /* 256x256 block tile, 8 waves */
+  FP8_VARIANT_T256x128DMA = 12, /* 256x128 block tile, 8 waves */
+  FP8_VARIANT_T128x128DMA = 13, /* 128x128 block tile, 4 waves */
+  FP8_VARIANT_COUNT = 14,
 };
 
 /* One tile configuration of the scaled GEMM. The PR34331 digest ("Key source

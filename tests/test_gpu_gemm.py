@@ -227,3 +227,24 @@ def test_split_k_back_to_back_calls_see_fresh_partials():
         _channelwise_case("o_proj", 192, 4096, 4096, 0.01, False, config=cfg, sample=False)
         _channelwise_case("qwen3_8b", 192, 4096, 4096, 0.0, True, config=cfg, sample=False)
         _channelwise_case("o_proj", 192, 4096, 4096, 0.01, False, config=cfg, sample=False)
+
+
+DMA_CASES = [(v, sk, m, n, k) for v, sk, m, n, k in (
+    ("t256x256dma", 1, 300, 392, 1024), ("t256x256dma", 3, 300, 392, 1024),
+    ("t256x128dma", 1, 300, 392, 1024), ("t256x128dma", 2, 513, 200, 2048),
+    ("t128x128dma", 1, 300, 392, 1024), ("t128x128dma", 4, 129, 392, 4096),
+    ("t256x256dma", 1, 1, 256, 64), ("t256x256dma", 1, 4096, 4096, 4096))]
+
+
+@pytest.mark.parametrize("variant,split_k,m,n,k", DMA_CASES,
+                         ids=[f"{c[0]}-sk{c[1]}-M{c[2]}-N{c[3]}-K{c[4]}" for c in DMA_CASES])
+def test_channelwise_dma_variants(variant, split_k, m, n, k):
+    """The LDS-DMA pipelined tiles (K a multiple of 64): ragged M and N, one to
+    many stages, split-K, and a full-size o_proj tile grid."""
+    _channelwise_case("dma", m, n, k, 0.0, True, config=ops.make_config(variant, split_k))
+
+
+def test_dma_variant_falls_back_when_k_not_multiple_of_64():
+    _channelwise_case("dma-fallback", 200, 264, 1040, 0.0, True, config=ops.make_config("t256x256dma", 1),
+                      sample=False)
+    _blockwise_case("dma-fallback-bw", 64, 256, 1024, config=ops.make_config("t128x128dma", 1))
