@@ -73,6 +73,99 @@ __device__ __forceinline__ void store_out4(const GemmArgs& p, int64_t m, int64_t
   }
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Scale (channelwise), add the bias and round to bf16 the 4 outputs a lane
+// owns at columns n..n+3 of row m; columns >= N give unspecified values.
+template <int KIND>
+__device__ __forceinline__ uint2 pack_out4(const GemmArgs& p, int64_t n, f32x4 v, float sa_m) {
+  float o[4] = {v[0], v[1], v[2], v[3]};
+  if (n + 3 < p.N) {
+    if (KIND == kChannelwise) {
+      const float4 sb = *reinterpret_cast<const float4*>(p.sb + n);
+      o[0] = o[0] * sa_m * sb.x; o[1] = o[1] * sa_m * sb.y;
+      o[2] = o[2] * sa_m * sb.z; o[3] = o[3] * sa_m * sb.w;
+    }
+    if (p.bias) {
+      const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
+      o[0] += bf16_to_f32(bb.x & 0xffffu); o[1] += bf16_to_f32(bb.x >> 16);
+      o[2] += bf16_to_f32(bb.y & 0xffffu); o[3] += bf16_to_f32(bb.y >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (n + r < p.N) {
+        if (KIND == kChannelwise) o[r] = o[r] * sa_m * p.sb[n + r];
+        if (p.bias) o[r] += bf16_to_f32(p.bias[n + r]);
+      }
+    }
+  }
+  return make_uint2(f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16),
+                    f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16));
+}
+
+// Epilogue of the 32x32-MFMA tile kernels, staged through LDS so that the
+// output leaves in whole rows. Each lane packs its 4-column groups (the out^T
+// layout: row m = l % 32, columns 8q + 4h .. +3 in registers 4q .. 4q+3) into
+// a [BM][BN] bf16 tile in LDS, whose 16-byte chunk c of row r sits at
+// c ^ sw(r); then consecutive threads copy consecutive 16-byte chunks of a
+// row to global memory. Stored straight from the MFMA layout, one store
+// instruction covered 32 rows 16 bytes each and the output went out at a
+// fraction of the write bandwidth. sw(r) = r % CH for rows of 256 bytes or
+// more, (r / 2) % 8 for 128-byte rows: conflict-free for both phases. The LDS
+// must hold BM * BN * 2 bytes; the function begins with a barrier, so the
+// caller may still be reading it.
+template <int BM, int BN, int WM, int WN, int KIND>
+__device__ __forceinline__ void store_tile(const GemmArgs& p,
+                                           const f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
+                                           uint8_t* lds, int64_t m0, int64_t n0, int wm, int wn,
+                                           int h, int r32, int tid) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int CH = BN / 8;  // 16-byte chunks per tile row
+  static_assert(CH == 8 || CH == 16 || CH == 32, "tile width");
+  auto sw = [](int r) { return CH >= 16 ? (r & (CH - 1)) : ((r >> 1) & (CH - 1)); };
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int ml = wm * WTM + i * 32 + r32;
+    const int64_t m = m0 + ml;
+    const float sa_m = (KIND == kChannelwise && m < p.M) ? p.sa[m] : 1.0f;
+    uint8_t* row = lds + ml * (BN * 2);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = wn * WTN + j * 32 + 8 * q + 4 * h;
+        const uint2 v = pack_out4<KIND>(
+            p, n0 + nl,
+            f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]},
+            sa_m);
+        *reinterpret_cast<uint2*>(row + (((nl >> 3) ^ sw(ml)) << 4) + (h << 3)) = v;
+      }
+  }
+  __syncthreads();
+  static_assert((BM * CH) % NT == 0, "copy-out split");
+#pragma unroll 4
+  for (int idx = tid; idx < BM * CH; idx += NT) {
+    const int rl = idx / CH, c = idx % CH;
+    const int64_t m = m0 + rl;
+    const int64_t n = n0 + c * 8;
+    if (m >= p.M || n >= p.N) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(lds + rl * (BN * 2) + ((c ^ sw(rl)) << 4));
+    uint16_t* dst = p.out + m * p.ldc + n;
+    if (n + 8 <= p.N) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (n + r < p.N) dst[r] = (uint16_t)(w[r >> 1] >> (16 * (r & 1)));
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Tiled kernel: BM x BN block tile, 128-byte K stages, WM x WN waves, each wave
 // a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA tiles (V_MFMA_F32_32X32X64_F8F6F4,
@@ -90,7 +183,6 @@ __device__ __forceinline__ void store_out4(const GemmArgs& p, int64_t m, int64_t
 // arrive (arrival counter per tile) sums the partials in split order --
 // deterministic -- applies the epilogue and re-arms the counter to zero.
 // ---------------------------------------------------------------------------
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Physical 16-byte chunk position of logical chunk c in an LDS row r of CH
 // chunks. For 128-byte rows (CH = 8) the xor key (r & 7) ^ ((r >> 3) & 1)
@@ -355,21 +447,53 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmArgs p) {
     if (tid == 0) __hip_atomic_store(p.ws_count + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
+  static_assert(BM * BN * 2 <= 2 * (BM + BN) * BK, "output tile fits the LDS stages");
+  store_tile<BM, BN, WM, WN, KIND>(p, acc, lds, m0, n0, wm, wn, h, r32, tid);
+}
+
+// Fence-free deterministic split-K for the 32x32-MFMA kernels (the scheme of
+// the tiled kernel above): every split stores its partial tile to the
+// workspace with agent-scope relaxed stores, the workgroup drains its stores
+// and counts itself in with one atomic; the last to arrive sums the partials in
+// split order into acc, re-arms the counter and returns true. The others
+// return false and must exit. *flag is workgroup-shared scratch.
+template <int TM, int TN, int NT>
+__device__ __forceinline__ bool splitk_reduce(const GemmArgs& p, f32x16 (&acc)[TM][TN],
+                                              int64_t tile, int split, int tid, int* flag) {
+  constexpr int Q = TM * TN * 16;
+  float* part = p.ws_part + (tile * p.split_k) * (int64_t)Q * NT;
+  float* mine = part + (int64_t)split * Q * NT;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int64_t m = m0 + wm * WTM + i * 32 + r32;
-    const float sa_m = (KIND == kChannelwise && m < p.M) ? p.sa[m] : 1.0f;
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + wn * WTN + j * 32 + 8 * q + 4 * h;
-        store_out4<KIND>(p, m, n,
-                         f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                               acc[i][j][4 * q + 3]},
-                         sa_m);
-      }
+      for (int r = 0; r < 16; ++r)
+        __hip_atomic_store(mine + ((i * TN + j) * 16 + r) * NT + tid, acc[i][j][r], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const int old = atomicAdd(p.ws_count + tile, 1);
+    *flag = (old == p.split_k - 1);
   }
+  __syncthreads();
+  if (!*flag) return false;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t idx = (int64_t)((i * TN + j) * 16 + r) * NT + tid;
+        float v = __hip_atomic_load(part + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int sp = 1; sp < p.split_k; ++sp)
+          v += __hip_atomic_load(part + (int64_t)sp * Q * NT + idx, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        acc[i][j][r] = v;
+      }
+  if (tid == 0) __hip_atomic_store(p.ws_count + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -405,12 +529,27 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
                : "memory", "m0");
 }
 
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset: one VGPR per stream instead of a 64-bit pointer.
+__device__ __forceinline__ void lds_dma16_s(const uint8_t* sbase, uint32_t voff, uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0v)
+               : "memory", "m0");
+}
+
 // s_waitcnt with vmcnt = N and the other counters unconstrained (gfx9 layout:
 // vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14, expcnt 6:4, lgkmcnt 11:8).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// The same, and every LDS read of this wave complete (lgkmcnt = 0).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
 __device__ __forceinline__ int swz64(int r, int c) { return c ^ ((r >> 2) & 3); }
@@ -429,7 +568,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmArgs p) {
   static_assert(A_BLK % NW == 0 && B_BLK % NW == 0, "DMA blocks per wave");
   static_assert(TM >= 1 && TN >= 1, "wave tile");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "stages");
-  static_assert(PER_WAVE * (NSTAGE - 1) < 64, "vmcnt range");
+  static_assert(PER_WAVE * NSTAGE < 64, "vmcnt range");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int last_flag;
@@ -456,39 +595,34 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmArgs p) {
   int64_t kt_end = kt_begin + p.k_tiles_per_split;
   if (kt_end > kt_all) kt_end = kt_all;
 
-  // per-lane source rows of this wave's DMA blocks (clamped into the matrix)
+  // per-lane byte offsets of this wave's DMA rows (clamped into the matrix;
+  // the launcher guarantees they fit in 32 bits)
   const int lrow = lane >> 2, lpos = lane & 3;
-  const uint8_t* a_src[A_PER];
-  int a_chunk[A_PER];
+  uint32_t a_off[A_PER], b_off[B_PER];
 #pragma unroll
   for (int i = 0; i < A_PER; ++i) {
     const int r = (wave * A_PER + i) * 16 + lrow;
     int64_t gm = m0 + r;
     if (gm >= p.M) gm = p.M - 1;
-    a_src[i] = p.a + gm * p.lda;
-    a_chunk[i] = swz64(r, lpos);  // logical chunk stored at position lpos
+    a_off[i] = (uint32_t)(gm * p.lda + swz64(r, lpos) * 16);  // logical chunk at position lpos
   }
-  const uint8_t* b_src[B_PER];
-  int b_chunk[B_PER];
 #pragma unroll
   for (int i = 0; i < B_PER; ++i) {
     const int r = (wave * B_PER + i) * 16 + lrow;
     int64_t gn = n0 + r;
     if (gn >= p.N) gn = p.N - 1;
-    b_src[i] = p.b + gn * p.ldb;
-    b_chunk[i] = swz64(r, lpos);
+    b_off[i] = (uint32_t)(gn * p.ldb + swz64(r, lpos) * 16);
   }
+  auto slot = [&](int64_t kt) { return (int)((kt - kt_begin) % NSTAGE); };
   auto issue = [&](int64_t kt) {
-    const int buf = (int)((kt - kt_begin) % NSTAGE);
-    const uint32_t a_base = lds_base + buf * STAGE_BYTES;
+    const uint32_t a_base = lds_base + slot(kt) * STAGE_BYTES;
     const uint32_t b_base = a_base + BM * BK;
-    const int64_t k0 = kt * BK;
+    const uint8_t* ak = p.a + kt * BK;
+    const uint8_t* bk = p.b + kt * BK;
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i)
-      lds_dma16(a_src[i] + k0 + a_chunk[i] * 16, a_base + (wave * A_PER + i) * 1024);
+    for (int i = 0; i < A_PER; ++i) lds_dma16_s(ak, a_off[i], a_base + (wave * A_PER + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < B_PER; ++i)
-      lds_dma16(b_src[i] + k0 + b_chunk[i] * 16, b_base + (wave * B_PER + i) * 1024);
+    for (int i = 0; i < B_PER; ++i) lds_dma16_s(bk, b_off[i], b_base + (wave * B_PER + i) * 1024);
   };
   auto frag = [&](const uint8_t* base, int r) {
     const uint8_t* row = base + r * BK;
@@ -503,88 +637,256 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = zero16();
 
-  for (int q = 0; q < NSTAGE - 1; ++q)
+  // Pipeline: stage kt's fragments are in registers while its MFMAs run. The
+  // B fragments of stage kt+1 go to a second register set; each A fragment of
+  // kt+1 is read into the registers of kt's A fragment as soon as kt's MFMAs
+  // on it have issued (128 accumulators plus fragments fit the 256 registers
+  // of a wave at two waves per SIMD). The ring slot of stage kt is free once
+  // its fragments are in registers, so stage kt+NSTAGE is issued into it,
+  // keeping NSTAGE-1 stages of DMA in flight behind the one being read.
+  i32x8 fa[TM], fb0[TN], fb1[TN];
+  for (int q = 0; q < NSTAGE; ++q)
     if (kt_begin + q < kt_end) issue(kt_begin + q);
+  if (kt_begin < kt_end) {
+    const int64_t issued_after = kt_end - 1 - kt_begin;  // stages issued after the first
+    if (issued_after >= NSTAGE - 1) wait_vmcnt<(NSTAGE - 1) * PER_WAVE>();
+    else if (issued_after == 2) wait_vmcnt<2 * PER_WAVE>();
+    else if (issued_after == 1) wait_vmcnt<PER_WAVE>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    const uint8_t* ab = lds + slot(kt_begin) * STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[i] = frag(ab, wm * WTM + i * 32 + r32);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb0[j] = frag(ab + BM * BK, wn * WTN + j * 32 + r32);
+  }
+  // One stage with a successor. Every path reaches the barrier with
+  // lgkmcnt = 0, so the MFMAs never wait on the reads issued beside them.
+  auto step_read = [&](int64_t kt, const i32x8 (&bc)[TN], i32x8 (&bn)[TN]) {
+    const int64_t later = kt_end - 2 - kt;  // stages issued after kt+1 so far
+    if (later >= NSTAGE - 2) wait_vmcnt<(NSTAGE - 2) * PER_WAVE>();
+    else if (later == 1) wait_vmcnt<PER_WAVE>();
+    else wait_vmcnt<0>();
+    wait_vmcnt_lgkm0<63>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + NSTAGE < kt_end) issue(kt + NSTAGE);
+    const uint8_t* ab = lds + slot(kt + 1) * STAGE_BYTES;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bn[j] = frag(ab + BM * BK, wn * WTN + j * 32 + r32);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32_fp8(bc[j], fa[i], acc[i][j]);
+      fa[i] = frag(ab, wm * WTM + i * 32 + r32);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * TN, 0);  // B reads of kt+1
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);  // MFMAs on A fragment i
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // A fragment i of kt+1
+    }
+  };
+  auto step_last = [&](const i32x8 (&bc)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32_fp8(bc[j], fa[i], acc[i][j]);
+  };
+  for (int64_t kt = kt_begin; kt + 1 < kt_end; ++kt) {
+    step_read(kt, fb0, fb1);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb0[j] = fb1[j];
+  }
+  if (kt_begin < kt_end) step_last(fb0);
 
-  for (int64_t kt = kt_begin; kt < kt_end; ++kt) {
-    const int64_t later = kt_end - 1 - kt;  // stages issued after this one (so far)
-    if (later >= NSTAGE - 2) {
-      if (NSTAGE - 2 == 2) wait_vmcnt<2 * PER_WAVE>();
-      else if (NSTAGE - 2 == 1) wait_vmcnt<PER_WAVE>();
-      else wait_vmcnt<0>();
-    } else if (later == 1) {
-      wait_vmcnt<PER_WAVE>();
+  if (p.split_k > 1 && !splitk_reduce<TM, TN, NT>(p, acc, tile, split, tid, &last_flag)) return;
+
+  static_assert(BM * BN * 2 <= NSTAGE * STAGE_BYTES, "output tile fits the LDS ring");
+  store_tile<BM, BN, WM, WN, kChannelwise>(p, acc, lds, m0, n0, wm, wn, h, r32, tid);
+}
+
+// ---------------------------------------------------------------------------
+// Panel-ring kernel (channelwise, K % 128 == 0): square BM x BM tile,
+// 128-byte K stages, WM x WN waves of 32x32 MFMA tiles as above. A stage is
+// two panels -- its A rows, then its B rows, BM rows x 128 bytes each, rows in
+// the 128-byte layout of the tiled kernel (swz<8>) -- and panel q (stage q/2,
+// B if q is odd) lives in slot q % 5 of a five-slot LDS ring. One LDS-DMA
+// instruction moves 8 whole 128-byte row pieces, one cache line per row:
+// measured on MI355X with every CU streaming, that feeds a CU about 1.45x
+// faster from L2 than the 16 half-line pieces of the 64-byte-stage kernel,
+// which bounds that kernel at large M. The MFMAs walk a stage in two 64-deep
+// halves with the fragment pipeline of that kernel (next fragments read while
+// the current ones are multiplied). One barrier per stage, between its halves:
+// it makes the next stage's panels visible and frees the two slots of the
+// finished stage s, which at once take the B panel of stage s+2 and the A
+// panel of stage s+3 (panels 2s+5 and 2s+6), so three panels stay in flight.
+// ---------------------------------------------------------------------------
+template <int BM, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
+  constexpr int BN = BM;
+  constexpr int NP = 5;                // ring slots
+  constexpr int NT = WM * WN * 64;
+  constexpr int NW = WM * WN;
+  constexpr int BK = 128;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int PANEL = BM * BK;       // bytes per panel
+  constexpr int PPW = BM / 8 / NW;     // DMA instructions per wave per panel
+  static_assert(TM >= 1 && TN >= 1, "wave tile");
+  static_assert(PPW >= 1 && (BM / 8) % NW == 0, "panel rows per wave");
+  static_assert(NP * PANEL <= 163840, "ring fits the LDS");
+  static_assert(PPW * NP < 64, "vmcnt range");
+  static_assert(BM * BN * 2 <= NP * PANEL, "output tile fits the ring");
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+
+  const int64_t tiles_n = (p.N + BN - 1) / BN;
+  const int64_t tiles_m = (p.M + BM - 1) / BM;
+  const int64_t tile = blockIdx.x;
+  int64_t tile_m, tile_n;
+  tile_coords(tile, tiles_m, tiles_n, &tile_m, &tile_n);
+  const int64_t m0 = tile_m * BM;
+  const int64_t n0 = tile_n * BN;
+  const int split = blockIdx.y;
+  const int64_t kt_all = p.K / BK;
+  const int64_t kt_begin = (int64_t)split * p.k_tiles_per_split;
+  int64_t kt_end = kt_begin + p.k_tiles_per_split;
+  if (kt_end > kt_all) kt_end = kt_all;
+  const int64_t nst = kt_end - kt_begin;  // stages of this split (may be <= 0)
+
+  // DMA addressing. Instruction i of a wave covers panel rows
+  // rb_i = (wave * PPW + i) * 8 .. +7, lane l row rb_i + l / 8, and fetches
+  // logical chunk swz<8>(row, l % 8), which lands at position l % 8 of the
+  // row in LDS; the swizzle depends on the row through l / 8 and the parity
+  // of rb_i / 8 only. Rows past the matrix read its last row (never stored).
+  const int lrow = lane >> 3;
+  uint32_t lchunk[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) lchunk[par] = (uint32_t)(swz<8>(par * 8 + lrow, lane & 7) << 4);
+  const uint32_t m_last = (uint32_t)(p.M - 1), n_last = (uint32_t)(p.N - 1);
+  auto issue_panel = [&](int64_t kt, bool is_b, int slot) {
+    const uint8_t* src = (is_b ? p.b : p.a) + kt * BK;
+    const uint32_t r0 = (uint32_t)(is_b ? n0 : m0);
+    const uint32_t last = is_b ? n_last : m_last;
+    const uint32_t ld = (uint32_t)(is_b ? p.ldb : p.lda);
+    const uint32_t dst = lds_base + (uint32_t)slot * PANEL + wave * PPW * 1024;
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      const int rb = (wave * PPW + i) * 8;
+      uint32_t row = r0 + rb + lrow;
+      row = row < last ? row : last;
+      lds_dma16_s(src, row * ld + lchunk[(wave * PPW + i) & 1], dst + i * 1024);
+    }
+  };
+  // Per-lane byte offsets, within a panel, of the two 16-byte chunks of this
+  // lane's A fragment row for each 64-deep half kh (chunks 4kh + 2h, +1). The
+  // swizzle depends on the row only through row % 16, the same for every
+  // 32-row fragment of every wave, so A fragment i adds i * 32 * BK and B
+  // fragment j adds (wn * WTN - wm * WTM + j * 32) * BK.
+  uint32_t fo[2][2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      fo[kh][t] = (uint32_t)((wm * WTM + r32) * BK + (swz<8>(r32, 4 * kh + 2 * h + t) << 4));
+  const int b_shift = (wn * WTN - wm * WTM) * BK;
+  auto frag_at = [&](const uint8_t* base, int kh) {
+    return join(*reinterpret_cast<const uint4*>(base + fo[kh][0]),
+                *reinterpret_cast<const uint4*>(base + fo[kh][1]));
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = zero16();
+
+  i32x8 fa[TM], fb0[TN], fb1[TN];
+  // MFMAs on (fa, fb0) while the next half's fragments are read from the
+  // slots (sa, sb): B into fb1 first, each A fragment into fa right after its
+  // MFMAs; then fb1 becomes the current B.
+  auto half = [&](int sa, int sb, int kh) {
+    const uint8_t* pa = lds + sa * PANEL;
+    const uint8_t* pb = lds + sb * PANEL + b_shift;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb1[j] = frag_at(pb + j * 32 * BK, kh);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32_fp8(fb0[j], fa[i], acc[i][j]);
+      fa[i] = frag_at(pa + i * 32 * BK, kh);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * TN, 0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb0[j] = fb1[j];
+  };
+  auto wrap = [](int x) { return x >= NP ? x - NP : x; };
+
+  if (nst > 0) {
+    // prologue: panels 0 .. min(5, 2 nst) - 1 into slots 0 .. 4
+    issue_panel(kt_begin, false, 0);
+    issue_panel(kt_begin, true, 1);
+    if (nst > 1) {
+      issue_panel(kt_begin + 1, false, 2);
+      issue_panel(kt_begin + 1, true, 3);
+      if (nst > 2) {
+        issue_panel(kt_begin + 2, false, 4);
+        wait_vmcnt<3 * PPW>();
+      } else {
+        wait_vmcnt<2 * PPW>();
+      }
     } else {
       wait_vmcnt<0>();
     }
     __builtin_amdgcn_s_barrier();
-    if (kt + NSTAGE - 1 < kt_end) issue(kt + NSTAGE - 1);
-
-    const int buf = (int)((kt - kt_begin) % NSTAGE);
-    const uint8_t* ab = lds + buf * STAGE_BYTES;
-    const uint8_t* bb = ab + BM * BK;
-    i32x8 af[TM], bf[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[i] = frag(ab, wm * WTM + i * 32 + r32);
+    for (int i = 0; i < TM; ++i) fa[i] = frag_at(lds + i * 32 * BK, 0);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bf[j] = frag(bb, wn * WTN + j * 32 + r32);
+    for (int j = 0; j < TN; ++j) fb0[j] = frag_at(lds + PANEL + b_shift + j * 32 * BK, 0);
+  }
+  int cs = 0;  // slot of the current stage's A panel; its B panel is in wrap(cs + 1)
+  for (int64_t s = 0; s + 1 < nst; ++s) {
+    const int cs1 = wrap(cs + 1);
+    // first half of stage s; its second half's fragments come from the same slots
+    half(cs, cs1, 1);
+    // stage s+1 (panels 2s+2, 2s+3) complete: panels up to 2s+4 are issued,
+    // so at most panel 2s+4 may still be outstanding
+    if (s + 2 < nst) wait_vmcnt<PPW>();
+    else wait_vmcnt<0>();
+    wait_vmcnt_lgkm0<63>();
+    __builtin_amdgcn_s_barrier();
+    // every wave is done with stage s: its slots take panels 2s+5 and 2s+6
+    if (s + 2 < nst) issue_panel(kt_begin + s + 2, true, cs);
+    if (s + 3 < nst) issue_panel(kt_begin + s + 3, false, cs1);
+    cs = wrap(cs + 2);
+    half(cs, wrap(cs + 1), 0);
+  }
+  if (nst > 0) {  // last stage: both halves from the slots already in LDS
+    half(cs, wrap(cs + 1), 1);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32_fp8(bf[j], af[i], acc[i][j]);
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32_fp8(fb0[j], fa[i], acc[i][j]);
   }
 
-  if (p.split_k > 1) {
-    constexpr int Q = TM * TN * 16;
-    float* part = p.ws_part + (tile * p.split_k) * (int64_t)Q * NT;
-    float* mine = part + (int64_t)split * Q * NT;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          __hip_atomic_store(mine + ((i * TN + j) * 16 + r) * NT + tid, acc[i][j][r],
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-      const int old = atomicAdd(p.ws_count + tile, 1);
-      last_flag = (old == p.split_k - 1);
-    }
-    __syncthreads();
-    if (!last_flag) return;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t idx = (int64_t)((i * TN + j) * 16 + r) * NT + tid;
-          float v = __hip_atomic_load(part + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          for (int sp = 1; sp < p.split_k; ++sp)
-            v += __hip_atomic_load(part + (int64_t)sp * Q * NT + idx, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-          acc[i][j][r] = v;
-        }
-    if (tid == 0) __hip_atomic_store(p.ws_count + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int64_t m = m0 + wm * WTM + i * 32 + r32;
-    const float sa_m = (m < p.M) ? p.sa[m] : 1.0f;
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + wn * WTN + j * 32 + 8 * q + 4 * h;
-        store_out4<kChannelwise>(p, m, n,
-                                 f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                       acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]},
-                                 sa_m);
-      }
-  }
+  // the ring is idle from here on: its first word serves as the split flag
+  if (p.split_k > 1 && !splitk_reduce<TM, TN, NT>(p, acc, tile, split, tid, reinterpret_cast<int*>(lds)))
+    return;
+  store_tile<BM, BN, WM, WN, kChannelwise>(p, acc, lds, m0, n0, wm, wn, h, r32, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -737,6 +1039,23 @@ hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int BM, int WM, int WN>
+hipError_t launch_panel(const GemmArgs& p, hipStream_t stream) {
+  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BM - 1) / BM);
+  const size_t lds = (size_t)5 * BM * 128;
+  auto kern = gemm_panel_kernel<BM, WM, WN>;
+  static bool lds_attr_set = false;
+  if (lds > 65536 && !lds_attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    lds_attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles, (unsigned)p.split_k), dim3(WM * WN * 64), lds,
+                     stream, p);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, int NSTAGE>
 hipError_t launch_dma(const GemmArgs& p, hipStream_t stream) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
@@ -752,6 +1071,15 @@ hipError_t launch_dma(const GemmArgs& p, hipStream_t stream) {
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles, (unsigned)p.split_k), dim3(WM * WN * 64), lds,
                      stream, p);
   return hipGetLastError();
+}
+
+// The LDS-DMA tiles take whole 64-byte K stages, channelwise scales only, and
+// per-lane row offsets that fit the 32-bit offset of the DMA instruction.
+template <int KIND>
+bool dma_eligible(const GemmArgs& p) {
+  const uint64_t lim = 0xFFFFFFFFull - 64;
+  return KIND == kChannelwise && p.K % 64 == 0 && (uint64_t)(p.M - 1) * (uint64_t)p.lda <= lim &&
+         (uint64_t)(p.N - 1) * (uint64_t)p.ldb <= lim;
 }
 
 template <int KIND>
@@ -776,14 +1104,17 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
     case 9: return launch_tile<64, 128, 2, 2, 256, KIND>(p, stream);
     case 10: return launch_tile<128, 128, 2, 2, 256, KIND>(p, stream);
     case 11:
-      if (KIND != kChannelwise || p.K % 64 != 0) return launch_tile<256, 256, 2, 4, 128, KIND>(p, stream);
+      if (!dma_eligible<KIND>(p)) return launch_tile<256, 256, 2, 4, 128, KIND>(p, stream);
       return launch_dma<256, 256, 2, 4, 4>(p, stream);
     case 12:
-      if (KIND != kChannelwise || p.K % 64 != 0) return launch_tile<256, 128, 4, 2, 128, KIND>(p, stream);
+      if (!dma_eligible<KIND>(p)) return launch_tile<256, 128, 4, 2, 128, KIND>(p, stream);
       return launch_dma<256, 128, 4, 2, 4>(p, stream);
     case 13:
-      if (KIND != kChannelwise || p.K % 64 != 0) return launch_tile<128, 128, 2, 2, 256, KIND>(p, stream);
+      if (!dma_eligible<KIND>(p)) return launch_tile<128, 128, 2, 2, 256, KIND>(p, stream);
       return launch_dma<128, 128, 2, 2, 4>(p, stream);
+    case 14:  // the fallback keeps the 128-deep stages the split plan counts in
+      if (!dma_eligible<KIND>(p) || p.K % 128 != 0) return launch_tile<256, 256, 2, 4, 128, KIND>(p, stream);
+      return launch_panel<256, 2, 4>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -807,6 +1138,8 @@ VariantInfo variant_info(int variant) {
     case 11: return {256, 256, 64, 8, true};
     case 12: return {256, 128, 64, 8, true};
     case 13: return {128, 128, 64, 4, true};
+    // panel-ring LDS-DMA variant, channelwise with K % 128 == 0
+    case 14: return {256, 256, 128, 8, true};
     default: return {0, 0, 0, 0, false};
   }
 }

@@ -180,6 +180,7 @@ int variant_from_name(const std::string& n) {
   if (n == "t256x256dma") return FP8_VARIANT_T256x256DMA;
   if (n == "t256x128dma") return FP8_VARIANT_T256x128DMA;
   if (n == "t128x128dma") return FP8_VARIANT_T128x128DMA;
+  if (n == "t256x256panel") return FP8_VARIANT_T256x256PANEL;
   return -100;
 }
 

@@ -76,7 +76,11 @@ enum {
   FP8_VARIANT_T256x256DMA = 11, /* 256x256 block tile, 8 waves */
   FP8_VARIANT_T256x128DMA = 12, /* 256x128 block tile, 8 waves */
   FP8_VARIANT_T128x128DMA = 13, /* 128x128 block tile, 4 waves */
-  FP8_VARIANT_COUNT = 14,
+  /* LDS-DMA ring of 128-byte-deep panels (whole cache-line row pieces), five
+   * 32 KB slots: channelwise only, K % 128 == 0; other requests run the
+   * register-staged 256x256 8-wave kernel. */
+  FP8_VARIANT_T256x256PANEL = 14, /* 256x256 block tile, 8 waves */
+  FP8_VARIANT_COUNT = 15,
 };
 
 /* One tile configuration of the scaled GEMM. The PR34331 digest ("Key source

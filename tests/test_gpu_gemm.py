@@ -248,3 +248,24 @@ def test_dma_variant_falls_back_when_k_not_multiple_of_64():
     _channelwise_case("dma-fallback", 200, 264, 1040, 0.0, True, config=ops.make_config("t256x256dma", 1),
                       sample=False)
     _blockwise_case("dma-fallback-bw", 64, 256, 1024, config=ops.make_config("t128x128dma", 1))
+
+
+PANEL_CASES = [
+    (1, 300, 392, 1024), (3, 300, 392, 1024), (2, 513, 200, 2048), (1, 1, 256, 128),
+    (1, 257, 264, 256), (1, 300, 392, 384), (4, 129, 392, 4096), (3, 64, 520, 1280),
+    (1, 4096, 4096, 4096)]
+
+
+@pytest.mark.parametrize("split_k,m,n,k", PANEL_CASES,
+                         ids=[f"sk{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in PANEL_CASES])
+def test_channelwise_panel_variant(split_k, m, n, k):
+    """The panel-ring LDS-DMA tile (K a multiple of 128): one to many stages
+    (odd and even panel counts against the five-slot ring), ragged M and N,
+    split-K with uneven splits, and a full o_proj tile grid."""
+    _channelwise_case("panel", m, n, k, 0.0, True, config=ops.make_config("t256x256panel", split_k))
+
+
+def test_panel_variant_falls_back_when_k_not_multiple_of_128():
+    _channelwise_case("panel-fallback", 200, 264, 1088, 0.0, True,
+                      config=ops.make_config("t256x256panel", 2), sample=False)
+    _blockwise_case("panel-fallback-bw", 64, 256, 1024, config=ops.make_config("t256x256panel", 1))
