@@ -537,6 +537,18 @@ __device__ __forceinline__ void lds_dma16_s(const uint8_t* sbase, uint32_t voff,
                : "memory", "m0");
 }
 
+// The 4-byte form: each lane's 4 bytes land at M0 + 4 * lane.
+__device__ __forceinline__ void lds_dma4_s(const uint8_t* sbase, uint32_t voff, uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0v)
+               : "memory", "m0");
+}
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
 // s_waitcnt with vmcnt = N and the other counters unconstrained (gfx9 layout:
 // vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14, expcnt 6:4, lgkmcnt 11:8).
 template <int N>
@@ -706,37 +718,63 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Panel-ring kernel (channelwise, K % 128 == 0): square BM x BM tile,
-// 128-byte K stages, WM x WN waves of 32x32 MFMA tiles as above. A stage is
-// two panels -- its A rows, then its B rows, BM rows x 128 bytes each, rows in
-// the 128-byte layout of the tiled kernel (swz<8>) -- and panel q (stage q/2,
-// B if q is odd) lives in slot q % 5 of a five-slot LDS ring. One LDS-DMA
-// instruction moves 8 whole 128-byte row pieces, one cache line per row:
-// measured on MI355X with every CU streaming, that feeds a CU about 1.45x
-// faster from L2 than the 16 half-line pieces of the 64-byte-stage kernel,
-// which bounds that kernel at large M. The MFMAs walk a stage in two 64-deep
-// halves with the fragment pipeline of that kernel (next fragments read while
-// the current ones are multiplied). One barrier per stage, between its halves:
-// it makes the next stage's panels visible and frees the two slots of the
-// finished stage s, which at once take the B panel of stage s+2 and the A
-// panel of stage s+3 (panels 2s+5 and 2s+6), so three panels stay in flight.
+// Panel-ring kernel (K % 128 == 0): BM x BN block tile, 128-byte K stages,
+// WM x WN waves of 32x32 MFMA tiles as above. A stage is two panels -- its
+// A rows, then its B rows, 128 bytes each, in the 128-byte row layout of the
+// tiled kernel (swz<8>) -- and panel q (stage q/2, B if q is odd) lives in
+// slot q % 5 of a five-slot LDS ring. One LDS-DMA instruction moves 8 whole
+// 128-byte row pieces, one cache line per row: measured on MI355X with every
+// CU streaming, that feeds a CU about 1.45x faster from L2 than the 16
+// half-line pieces of the 64-byte-stage kernel, which bounds that kernel at
+// large M. The MFMAs walk a stage in two 64-deep halves with the fragment
+// pipeline of that kernel (next fragments read while the current ones are
+// multiplied). One barrier per stage, between its halves: it makes the next
+// stage's panels visible and frees the two slots of the finished stage s,
+// which at once take the B panel of stage s+2 and the A panel of stage s+3
+// (panels 2s+5 and 2s+6), so three panels stay in flight.
+// Blockwise: the stage is one 128-deep scale block. Its two MFMA halves
+// accumulate into a separate partial tile that is scaled by
+// a_scale[m][kb] * b_scale[nb][kb] before it joins the accumulator. The
+// stage's scales ride with its B panel: the DMA also copies the BM activation
+// scales of block kb (the waves split them) and, per wave, the tile's weight
+// block scales into the spare end of the B slot.
 // ---------------------------------------------------------------------------
-template <int BM, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int KIND>
+struct PanelGeom {
+  static constexpr int NW = WM * WN;
+  static constexpr int NBLK = BN / 128;                        // weight scale blocks per tile
+  static constexpr int SA_BYTES = KIND == kBlockwise ? BM * 4 : 0;
+  static constexpr int SB_BYTES = KIND == kBlockwise ? NW * 16 : 0;
+  static constexpr int B_BYTES = BN * 128 + SA_BYTES + SB_BYTES;
+  static constexpr int SLOT = (BM * 128 > B_BYTES ? BM * 128 : B_BYTES + 1023) / 1024 * 1024;
+  static constexpr int LDS = 5 * SLOT;
+};
+
+template <int BM, int BN, int WM, int WN, int KIND>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
-  constexpr int BN = BM;
+  using G = PanelGeom<BM, BN, WM, WN, KIND>;
+  constexpr bool BW = KIND == kBlockwise;
   constexpr int NP = 5;                // ring slots
   constexpr int NT = WM * WN * 64;
   constexpr int NW = WM * WN;
   constexpr int BK = 128;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int PANEL = BM * BK;       // bytes per panel
-  constexpr int PPW = BM / 8 / NW;     // DMA instructions per wave per panel
+  constexpr int SLOT = G::SLOT;
+  constexpr int PPA = BM / 8 / NW;     // DMA instructions per wave per A panel
+  constexpr int PPB = BN / 8 / NW;     // ... per B panel (rows only)
+  constexpr int PPB_ALL = PPB + (BW ? 2 : 0);  // B panel with its scale copies
+  constexpr int SA_OFF = BN * BK;      // scale area inside a B slot
+  constexpr int SB_OFF = SA_OFF + G::SA_BYTES;
+  constexpr int SA_LANES = BM / 4 / NW;  // lanes of a wave's 16-byte activation-scale DMA
   static_assert(TM >= 1 && TN >= 1, "wave tile");
-  static_assert(PPW >= 1 && (BM / 8) % NW == 0, "panel rows per wave");
-  static_assert(NP * PANEL <= 163840, "ring fits the LDS");
-  static_assert(PPW * NP < 64, "vmcnt range");
-  static_assert(BM * BN * 2 <= NP * PANEL, "output tile fits the ring");
+  static_assert(PPA >= 1 && PPB >= 1 && (BM / 8) % NW == 0 && (BN / 8) % NW == 0, "panel rows per wave");
+  static_assert(G::LDS <= 163840, "ring fits the LDS");
+  static_assert(2 * PPA + PPB_ALL < 64, "vmcnt range");
+  static_assert(BM * BN * 2 <= G::LDS, "output tile fits the ring");
+  static_assert(!BW || (SA_LANES >= 1 && SA_LANES <= 64 && BM % (4 * NW) == 0 && G::NBLK <= 4 &&
+                        WTN <= 128 && 128 % WTN == 0),
+                "blockwise scale layout");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
@@ -764,7 +802,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   const int64_t nst = kt_end - kt_begin;  // stages of this split (may be <= 0)
 
   // DMA addressing. Instruction i of a wave covers panel rows
-  // rb_i = (wave * PPW + i) * 8 .. +7, lane l row rb_i + l / 8, and fetches
+  // rb_i = (wave * PP + i) * 8 .. +7, lane l row rb_i + l / 8, and fetches
   // logical chunk swz<8>(row, l % 8), which lands at position l % 8 of the
   // row in LDS; the swizzle depends on the row through l / 8 and the parity
   // of rb_i / 8 only. Rows past the matrix read its last row (never stored).
@@ -772,19 +810,45 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   uint32_t lchunk[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) lchunk[par] = (uint32_t)(swz<8>(par * 8 + lrow, lane & 7) << 4);
-  const uint32_t m_last = (uint32_t)(p.M - 1), n_last = (uint32_t)(p.N - 1);
-  auto issue_panel = [&](int64_t kt, bool is_b, int slot) {
-    const uint8_t* src = (is_b ? p.b : p.a) + kt * BK;
-    const uint32_t r0 = (uint32_t)(is_b ? n0 : m0);
-    const uint32_t last = is_b ? n_last : m_last;
-    const uint32_t ld = (uint32_t)(is_b ? p.ldb : p.lda);
-    const uint32_t dst = lds_base + (uint32_t)slot * PANEL + wave * PPW * 1024;
+  auto issue_rows = [&](const uint8_t* src, uint32_t r0, uint32_t last, uint32_t ld, uint32_t dst,
+                        auto pp) {
+    constexpr int PP = decltype(pp)::value;
 #pragma unroll
-    for (int i = 0; i < PPW; ++i) {
-      const int rb = (wave * PPW + i) * 8;
-      uint32_t row = r0 + rb + lrow;
+    for (int i = 0; i < PP; ++i) {
+      uint32_t row = r0 + (wave * PP + i) * 8 + lrow;
       row = row < last ? row : last;
-      lds_dma16_s(src, row * ld + lchunk[(wave * PPW + i) & 1], dst + i * 1024);
+      lds_dma16_s(src, row * ld + lchunk[(wave * PP + i) & 1], dst + i * 1024);
+    }
+  };
+  auto issue_a = [&](int64_t kt, int slot) {
+    issue_rows(p.a + kt * BK, (uint32_t)m0, (uint32_t)(p.M - 1), (uint32_t)p.lda,
+               lds_base + (uint32_t)slot * SLOT + wave * PPA * 1024, IntC<PPA>());
+  };
+  auto issue_b = [&](int64_t kt, int slot) {
+    const uint32_t sbase = lds_base + (uint32_t)slot * SLOT;
+    issue_rows(p.b + kt * BK, (uint32_t)n0, (uint32_t)(p.N - 1), (uint32_t)p.ldb,
+               sbase + wave * PPB * 1024, IntC<PPB>());
+    if constexpr (BW) {
+      // activation scales of block kt, rows m0 .. m0+BM-1 (column-major, ld
+      // sa_ld; 16-byte pieces clamped into the column): wave w copies rows
+      // [w * BM / NW, (w + 1) * BM / NW) with SA_LANES lanes
+      {
+        int64_t r = m0 + (int64_t)(wave * SA_LANES + (lane < SA_LANES ? lane : 0)) * 4;
+        if (r > p.sa_ld - 4) r = p.sa_ld - 4;
+        // lane 0 is always active, so the instruction always issues and
+        // counts once in this wave's vmcnt
+        if (lane < SA_LANES)
+          lds_dma16_s(reinterpret_cast<const uint8_t*>(p.sa + kt * p.sa_ld), (uint32_t)(r * 4),
+                      sbase + SA_OFF + wave * SA_LANES * 16);
+      }
+      // weight block scales b_scale[n0 / 128 + l][kt], lanes l < NBLK, one
+      // 16-byte copy per wave (lane 0 always active, as above)
+      {
+        const int64_t kb_all = p.K / 128;
+        if (lane < G::NBLK)
+          lds_dma4_s(reinterpret_cast<const uint8_t*>(p.sb + kt),
+                     (uint32_t)(((n0 >> 7) + lane) * kb_all * 4), sbase + SB_OFF + wave * 16);
+      }
     }
   };
   // Per-lane byte offsets, within a panel, of the two 16-byte chunks of this
@@ -809,20 +873,43 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = zero16();
+  // blockwise: the current stage's partial tile and scales
+  f32x16 part[BW ? TM : 1][BW ? TN : 1];
+  float sc_a[BW ? TM : 1], sc_b[BW ? TN : 1];
 
   i32x8 fa[TM], fb0[TN], fb1[TN];
   // MFMAs on (fa, fb0) while the next half's fragments are read from the
   // slots (sa, sb): B into fb1 first, each A fragment into fa right after its
-  // MFMAs; then fb1 becomes the current B.
+  // MFMAs; then fb1 becomes the current B. kh is the half being read: when it
+  // is 1 the MFMAs are the first half of their stage (whose second half is
+  // being read), when 0 the second half (the next stage is being read).
   auto half = [&](int sa, int sb, int kh) {
-    const uint8_t* pa = lds + sa * PANEL;
-    const uint8_t* pb = lds + sb * PANEL + b_shift;
+    const uint8_t* pa = lds + sa * SLOT;
+    const uint8_t* pb = lds + sb * SLOT + b_shift;
+    if constexpr (BW) {
+      if (kh == 1) {  // this stage's scales, while its B slot is still ours
+        const uint8_t* sc = lds + sb * SLOT;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          sc_a[i] = *reinterpret_cast<const float*>(sc + SA_OFF + (wm * WTM + i * 32 + r32) * 4);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          sc_b[j] = *reinterpret_cast<const float*>(sc + SB_OFF + wave * 16 +
+                                                     ((wn * WTN + j * 32) >> 7) * 4);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb1[j] = frag_at(pb + j * 32 * BK, kh);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32_fp8(fb0[j], fa[i], acc[i][j]);
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (BW) {
+          part[i][j] = mfma32_fp8(fb0[j], fa[i], kh == 1 ? zero16() : part[i][j]);
+        } else {
+          acc[i][j] = mfma32_fp8(fb0[j], fa[i], acc[i][j]);
+        }
+      }
       fa[i] = frag_at(pa + i * 32 * BK, kh);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * TN, 0);
@@ -834,20 +921,29 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb0[j] = fb1[j];
   };
+  // blockwise: the finished stage's partial tile joins the accumulator
+  auto promote = [&]() {
+    if constexpr (BW) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] += part[i][j] * (sc_a[i] * sc_b[j]);
+    }
+  };
   auto wrap = [](int x) { return x >= NP ? x - NP : x; };
 
   if (nst > 0) {
     // prologue: panels 0 .. min(5, 2 nst) - 1 into slots 0 .. 4
-    issue_panel(kt_begin, false, 0);
-    issue_panel(kt_begin, true, 1);
+    issue_a(kt_begin, 0);
+    issue_b(kt_begin, 1);
     if (nst > 1) {
-      issue_panel(kt_begin + 1, false, 2);
-      issue_panel(kt_begin + 1, true, 3);
+      issue_a(kt_begin + 1, 2);
+      issue_b(kt_begin + 1, 3);
       if (nst > 2) {
-        issue_panel(kt_begin + 2, false, 4);
-        wait_vmcnt<3 * PPW>();
+        issue_a(kt_begin + 2, 4);
+        wait_vmcnt<2 * PPA + PPB_ALL>();
       } else {
-        wait_vmcnt<2 * PPW>();
+        wait_vmcnt<PPA + PPB_ALL>();
       }
     } else {
       wait_vmcnt<0>();
@@ -856,7 +952,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) fa[i] = frag_at(lds + i * 32 * BK, 0);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) fb0[j] = frag_at(lds + PANEL + b_shift + j * 32 * BK, 0);
+    for (int j = 0; j < TN; ++j) fb0[j] = frag_at(lds + SLOT + b_shift + j * 32 * BK, 0);
   }
   int cs = 0;  // slot of the current stage's A panel; its B panel is in wrap(cs + 1)
   for (int64_t s = 0; s + 1 < nst; ++s) {
@@ -864,29 +960,34 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
     // first half of stage s; its second half's fragments come from the same slots
     half(cs, cs1, 1);
     // stage s+1 (panels 2s+2, 2s+3) complete: panels up to 2s+4 are issued,
-    // so at most panel 2s+4 may still be outstanding
-    if (s + 2 < nst) wait_vmcnt<PPW>();
+    // so at most panel 2s+4 (an A panel) may still be outstanding
+    if (s + 2 < nst) wait_vmcnt<PPA>();
     else wait_vmcnt<0>();
     wait_vmcnt_lgkm0<63>();
     __builtin_amdgcn_s_barrier();
     // every wave is done with stage s: its slots take panels 2s+5 and 2s+6
-    if (s + 2 < nst) issue_panel(kt_begin + s + 2, true, cs);
-    if (s + 3 < nst) issue_panel(kt_begin + s + 3, false, cs1);
+    if (s + 2 < nst) issue_b(kt_begin + s + 2, cs);
+    if (s + 3 < nst) issue_a(kt_begin + s + 3, cs1);
     cs = wrap(cs + 2);
     half(cs, wrap(cs + 1), 0);
+    promote();
   }
   if (nst > 0) {  // last stage: both halves from the slots already in LDS
     half(cs, wrap(cs + 1), 1);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32_fp8(fb0[j], fa[i], acc[i][j]);
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (BW) part[i][j] = mfma32_fp8(fb0[j], fa[i], part[i][j]);
+        else acc[i][j] = mfma32_fp8(fb0[j], fa[i], acc[i][j]);
+      }
+    promote();
   }
 
   // the ring is idle from here on: its first word serves as the split flag
   if (p.split_k > 1 && !splitk_reduce<TM, TN, NT>(p, acc, tile, split, tid, reinterpret_cast<int*>(lds)))
     return;
-  store_tile<BM, BN, WM, WN, kChannelwise>(p, acc, lds, m0, n0, wm, wn, h, r32, tid);
+  store_tile<BM, BN, WM, WN, KIND>(p, acc, lds, m0, n0, wm, wn, h, r32, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -1039,11 +1140,11 @@ hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BM, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int KIND>
 hipError_t launch_panel(const GemmArgs& p, hipStream_t stream) {
-  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BM - 1) / BM);
-  const size_t lds = (size_t)5 * BM * 128;
-  auto kern = gemm_panel_kernel<BM, WM, WN>;
+  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  const size_t lds = (size_t)PanelGeom<BM, BN, WM, WN, KIND>::LDS;
+  auto kern = gemm_panel_kernel<BM, BN, WM, WN, KIND>;
   static bool lds_attr_set = false;
   if (lds > 65536 && !lds_attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1082,6 +1183,20 @@ bool dma_eligible(const GemmArgs& p) {
          (uint64_t)(p.N - 1) * (uint64_t)p.ldb <= lim;
 }
 
+// The panel tiles take whole 128-byte K stages and 32-bit DMA row offsets;
+// blockwise also 16-byte aligned activation-scale columns (ld % 4 == 0).
+template <int KIND>
+bool panel_eligible(const GemmArgs& p) {
+  const uint64_t lim = 0xFFFFFFFFull - 128;
+  if (p.K % 128 != 0 || (uint64_t)(p.M - 1) * (uint64_t)p.lda > lim ||
+      (uint64_t)(p.N - 1) * (uint64_t)p.ldb > lim)
+    return false;
+  if (KIND == kBlockwise)
+    return p.sa_ld % 4 == 0 && (reinterpret_cast<uintptr_t>(p.sa) & 15) == 0 &&
+           (uint64_t)p.sa_ld * 4 <= lim;
+  return true;
+}
+
 template <int KIND>
 hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
   switch (variant) {
@@ -1112,9 +1227,14 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
     case 13:
       if (!dma_eligible<KIND>(p)) return launch_tile<128, 128, 2, 2, 256, KIND>(p, stream);
       return launch_dma<128, 128, 2, 2, 4>(p, stream);
-    case 14:  // the fallback keeps the 128-deep stages the split plan counts in
-      if (!dma_eligible<KIND>(p) || p.K % 128 != 0) return launch_tile<256, 256, 2, 4, 128, KIND>(p, stream);
-      return launch_panel<256, 2, 4>(p, stream);
+    // panel variants: the fallbacks keep the tile shape and the 128-deep
+    // stages the split plan counts in
+    case 14:
+      if (KIND != kChannelwise || !panel_eligible<KIND>(p)) return launch_tile<256, 256, 2, 4, 128, KIND>(p, stream);
+      return launch_panel<256, 256, 2, 4, kChannelwise>(p, stream);
+    case 15:
+      if (!panel_eligible<KIND>(p)) return launch_tile<256, 128, 4, 2, 128, KIND>(p, stream);
+      return launch_panel<256, 128, 4, 2, KIND>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1140,6 +1260,7 @@ VariantInfo variant_info(int variant) {
     case 13: return {128, 128, 64, 4, true};
     // panel-ring LDS-DMA variant, channelwise with K % 128 == 0
     case 14: return {256, 256, 128, 8, true};
+    case 15: return {256, 128, 128, 8, true};
     default: return {0, 0, 0, 0, false};
   }
 }

@@ -181,6 +181,7 @@ int variant_from_name(const std::string& n) {
   if (n == "t256x128dma") return FP8_VARIANT_T256x128DMA;
   if (n == "t128x128dma") return FP8_VARIANT_T128x128DMA;
   if (n == "t256x256panel") return FP8_VARIANT_T256x256PANEL;
+  if (n == "t256x128panel") return FP8_VARIANT_T256x128PANEL;
   return -100;
 }
 
@@ -271,38 +272,44 @@ bool tables_enabled() {
 
 int default_config(int kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* out) {
   // Measured on MI355X (o_proj N = K = 4096): the weight-streaming kernel up
-  // to 32 rows, then ever larger tiles as M grows. A tile is taken only if it
-  // gives at least half the 256 compute units a workgroup; the 64x64 tile is
-  // the fallback. Split-K never won in those measurements, so it is left to
-  // the tuned tables.
-  (void)K;
+  // to 32 rows, then ever larger tiles as M grows. From M = 1024 up, GEMMs
+  // whose K is a multiple of 128 take the panel-ring LDS-DMA tiles (both
+  // kinds; 256x256 channelwise only), which beat the register-staged tiles of
+  // the same shape at every M measured. A tile is taken only if it gives the
+  // chip enough workgroups (256x256: every compute unit, the others half of
+  // them); the 64x64 tile is the fallback. Split-K never won in those
+  // measurements, so it is left to the tuned tables.
+  const bool cw = kind != FP8_KIND_BLOCKWISE;
+  const bool k128 = K % 128 == 0, k64 = cw && K % 64 == 0;
   fp8_tile_config c{};
   c.split_k = 1;
   if (M <= 32) {
     c.variant = FP8_VARIANT_SKINNY;
   } else {
-    int order[4];
+    struct Cand {
+      int variant;
+      int64_t min_tiles;
+    };
+    Cand order[5];
     int n = 0;
     if (M <= 256) {
-      order[n++] = FP8_VARIANT_T64x64;
+      order[n++] = {FP8_VARIANT_T64x64, 128};
     } else if (M <= 512) {
-      order[n++] = FP8_VARIANT_T128x64K256;
-    } else if (M <= 1024) {
-      order[n++] = FP8_VARIANT_T128x128K256;
-      order[n++] = FP8_VARIANT_T128x64K256;
-    } else if (M <= 2048) {
-      order[n++] = FP8_VARIANT_T256x128W8;
-      order[n++] = FP8_VARIANT_T128x128K256;
+      order[n++] = {FP8_VARIANT_T128x64K256, 128};
+    } else if (M < 1024) {
+      order[n++] = {FP8_VARIANT_T128x128K256, 128};
+      order[n++] = {FP8_VARIANT_T128x64K256, 128};
     } else {
-      // the blockwise 256x256 tiles run out of registers
-      if (kind != FP8_KIND_BLOCKWISE) order[n++] = FP8_VARIANT_T256x256W8;
-      order[n++] = FP8_VARIANT_T256x128W8;
-      order[n++] = FP8_VARIANT_T128x128K256;
+      if (k128 && cw) order[n++] = {FP8_VARIANT_T256x256PANEL, 256};
+      if (k128) order[n++] = {FP8_VARIANT_T256x128PANEL, 64};
+      if (k64) order[n++] = {FP8_VARIANT_T256x128DMA, 128};
+      order[n++] = {FP8_VARIANT_T256x128W8, 128};  // blockwise: 256x256 runs out of registers
+      order[n++] = {FP8_VARIANT_T128x128K256, 128};
     }
     c.variant = FP8_VARIANT_T64x64;
     for (int i = 0; i < n; ++i) {
-      if (variant_tiles(order[i], M, N) >= 128) {
-        c.variant = order[i];
+      if (variant_tiles(order[i].variant, M, N) >= order[i].min_tiles) {
+        c.variant = order[i].variant;
         break;
       }
     }

@@ -80,7 +80,11 @@ enum {
    * 32 KB slots: channelwise only, K % 128 == 0; other requests run the
    * register-staged 256x256 8-wave kernel. */
   FP8_VARIANT_T256x256PANEL = 14, /* 256x256 block tile, 8 waves */
-  FP8_VARIANT_COUNT = 15,
+  /* The same ring with a 256x128 tile, both kinds (blockwise: K-block scales
+   * staged with the B panels); other requests run the register-staged
+   * 256x128 8-wave kernel. */
+  FP8_VARIANT_T256x128PANEL = 15, /* 256x128 block tile, 8 waves */
+  FP8_VARIANT_COUNT = 16,
 };
 
 /* One tile configuration of the scaled GEMM. The PR34331 digest ("Key source

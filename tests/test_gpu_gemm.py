@@ -57,11 +57,11 @@ def test_channelwise_workloads(wl, m, n, k, outl, bias):
     _channelwise_case(wl, m, n, k, outl, bias)
 
 
-def _blockwise_case(wl, m, n, k, config=None, with_bias=False, poison=False):
+def _blockwise_case(wl, m, n, k, config=None, with_bias=False, poison=False, row_align=4):
     a, sa = act_group(wl, m, k)
     b, sb = weight_blockwise(wl, n, k)
     bias = synth.bias(wl, n) if with_bias else None
-    m_pad = ops.padded_rows(m, 4)
+    m_pad = ops.padded_rows(m, row_align)
     a_dev = torch.full((m_pad, k), 0x7F if poison else 0, dtype=torch.uint8, device=device())
     a_dev[:m] = gpu(a)
     s_store = torch.full((k // 128, m_pad), float("nan") if poison else 0.0, dtype=torch.float32,
@@ -269,3 +269,39 @@ def test_panel_variant_falls_back_when_k_not_multiple_of_128():
     _channelwise_case("panel-fallback", 200, 264, 1088, 0.0, True,
                       config=ops.make_config("t256x256panel", 2), sample=False)
     _blockwise_case("panel-fallback-bw", 64, 256, 1024, config=ops.make_config("t256x256panel", 1))
+
+
+BW_PANEL_CASES = [
+    (1, 300, 384, 1024, False), (3, 300, 384, 1024, True), (1, 1, 128, 128, False),
+    (1, 257, 256, 384, False), (2, 513, 640, 2048, True), (4, 129, 384, 4096, False),
+    (1, 4096, 4096, 4096, False)]
+
+
+@pytest.mark.parametrize("split_k,m,n,k,bias", BW_PANEL_CASES,
+                         ids=[f"sk{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}{'-bias' if c[4] else ''}"
+                              for c in BW_PANEL_CASES])
+def test_blockwise_panel_variant(split_k, m, n, k, bias):
+    """The 256x128 panel-ring tile, blockwise: per-stage scales staged with the
+    B panels, one to many stages, ragged M, uneven split-K, bias, full grid."""
+    _blockwise_case("bw-panel", m, n, k, config=ops.make_config("t256x128panel", split_k), with_bias=bias)
+
+
+def test_blockwise_panel_poisoned_padding():
+    """Padded activation rows hold NaN codes and NaN scales; no valid row may see them."""
+    _blockwise_case("bw-panel-poison", 301, 384, 1024, config=ops.make_config("t256x128panel", 2),
+                    poison=True)
+
+
+def test_blockwise_panel_falls_back_on_unaligned_scale_column():
+    """An activation-scale column stride that is not a multiple of 4 takes the
+    register-staged kernel of the same tile."""
+    _blockwise_case("bw-panel-ld", 301, 384, 1024, config=ops.make_config("t256x128panel", 2), row_align=1)
+
+
+CW_PANEL128_CASES = [(1, 300, 392, 1024), (2, 300, 392, 1024), (1, 2048, 4096, 4096)]
+
+
+@pytest.mark.parametrize("split_k,m,n,k", CW_PANEL128_CASES,
+                         ids=[f"sk{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in CW_PANEL128_CASES])
+def test_channelwise_panel128_variant(split_k, m, n, k):
+    _channelwise_case("cw-panel128", m, n, k, 0.0, True, config=ops.make_config("t256x128panel", split_k))
