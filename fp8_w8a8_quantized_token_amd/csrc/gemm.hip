@@ -722,7 +722,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmArgs p) {
 // WM x WN waves of 32x32 MFMA tiles as above. A stage is two panels -- its
 // A rows, then its B rows, 128 bytes each, in the 128-byte row layout of the
 // tiled kernel (swz<8>) -- and panel q (stage q/2, B if q is odd) lives in
-// slot q % 5 of a five-slot LDS ring. One LDS-DMA instruction moves 8 whole
+// slot q % NP of an NP-slot LDS ring. One LDS-DMA instruction moves 8 whole
 // 128-byte row pieces, one cache line per row: measured on MI355X with every
 // CU streaming, that feeds a CU about 1.45x faster from L2 than the 16
 // half-line pieces of the 64-byte-stage kernel, which bounds that kernel at
@@ -730,8 +730,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmArgs p) {
 // pipeline of that kernel (next fragments read while the current ones are
 // multiplied). One barrier per stage, between its halves: it makes the next
 // stage's panels visible and frees the two slots of the finished stage s,
-// which at once take the B panel of stage s+2 and the A panel of stage s+3
-// (panels 2s+5 and 2s+6), so three panels stay in flight.
+// which at once take panels 2s+NP and 2s+NP+1, so NP-2 panels stay in flight.
+// Every variant uses five slots: large tiles fill the LDS with them, and for
+// small tiles several workgroups share a compute unit, which measured faster
+// than deeper rings (more bytes in flight per workgroup, fewer workgroups).
 // Blockwise: the stage is one 128-deep scale block. Its two MFMA halves
 // accumulate into a separate partial tile that is scaled by
 // a_scale[m][kb] * b_scale[nb][kb] before it joins the accumulator. The
@@ -739,22 +741,34 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmArgs p) {
 // scales of block kb (the waves split them) and, per wave, the tile's weight
 // block scales into the spare end of the B slot.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int KIND>
+template <int BM, int BN, int WM, int WN, int KIND, int NP>
 struct PanelGeom {
   static constexpr int NW = WM * WN;
-  static constexpr int NBLK = BN / 128;                        // weight scale blocks per tile
+  static constexpr int NBLK = (BN + 127) / 128;                // weight scale blocks per tile
   static constexpr int SA_BYTES = KIND == kBlockwise ? BM * 4 : 0;
   static constexpr int SB_BYTES = KIND == kBlockwise ? NW * 16 : 0;
   static constexpr int B_BYTES = BN * 128 + SA_BYTES + SB_BYTES;
   static constexpr int SLOT = (BM * 128 > B_BYTES ? BM * 128 : B_BYTES + 1023) / 1024 * 1024;
-  static constexpr int LDS = 5 * SLOT;
+  static constexpr int LDS = NP * SLOT;
 };
 
-template <int BM, int BN, int WM, int WN, int KIND>
+// Wait until at most the c newest DMA panels of this wave are outstanding,
+// c <= C, those panels alternating A (PA instructions), B (PB), A, ... from
+// the oldest of them.
+template <int C, int PA, int PB>
+__device__ __forceinline__ void wait_panels(int64_t c) {
+  if constexpr (C <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (c >= C) wait_vmcnt<((C + 1) / 2) * PA + (C / 2) * PB>();
+    else wait_panels<C - 1, PA, PB>(c);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int KIND, int NP>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
-  using G = PanelGeom<BM, BN, WM, WN, KIND>;
+  using G = PanelGeom<BM, BN, WM, WN, KIND, NP>;
   constexpr bool BW = KIND == kBlockwise;
-  constexpr int NP = 5;                // ring slots
   constexpr int NT = WM * WN * 64;
   constexpr int NW = WM * WN;
   constexpr int BK = 128;
@@ -770,7 +784,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   static_assert(TM >= 1 && TN >= 1, "wave tile");
   static_assert(PPA >= 1 && PPB >= 1 && (BM / 8) % NW == 0 && (BN / 8) % NW == 0, "panel rows per wave");
   static_assert(G::LDS <= 163840, "ring fits the LDS");
-  static_assert(2 * PPA + PPB_ALL < 64, "vmcnt range");
+  static_assert(NP >= 4, "ring depth");
+  static_assert(((NP - 1) / 2) * PPA + ((NP - 2) / 2) * PPB_ALL < 64, "vmcnt range");
   static_assert(BM * BN * 2 <= G::LDS, "output tile fits the ring");
   static_assert(!BW || (SA_LANES >= 1 && SA_LANES <= 64 && BM % (4 * NW) == 0 && G::NBLK <= 4 &&
                         WTN <= 128 && 128 % WTN == 0),
@@ -932,42 +947,39 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   };
   auto wrap = [](int x) { return x >= NP ? x - NP : x; };
 
+  const int64_t np_all = 2 * nst;  // panels of this split
+  auto issue_panel = [&](int64_t q, int slot) {
+    if (q & 1) issue_b(kt_begin + (q >> 1), slot);
+    else issue_a(kt_begin + (q >> 1), slot);
+  };
   if (nst > 0) {
-    // prologue: panels 0 .. min(5, 2 nst) - 1 into slots 0 .. 4
-    issue_a(kt_begin, 0);
-    issue_b(kt_begin, 1);
-    if (nst > 1) {
-      issue_a(kt_begin + 1, 2);
-      issue_b(kt_begin + 1, 3);
-      if (nst > 2) {
-        issue_a(kt_begin + 2, 4);
-        wait_vmcnt<2 * PPA + PPB_ALL>();
-      } else {
-        wait_vmcnt<PPA + PPB_ALL>();
-      }
-    } else {
-      wait_vmcnt<0>();
-    }
+    // prologue: panels 0 .. min(NP, 2 nst) - 1 into slots 0 .. NP-1, then
+    // stage 0 (panels 0 and 1) complete
+    const int64_t first = np_all < NP ? np_all : NP;
+    for (int64_t q = 0; q < first; ++q) issue_panel(q, (int)q);
+    wait_panels<NP - 2, PPA, PPB_ALL>(first - 2);
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int i = 0; i < TM; ++i) fa[i] = frag_at(lds + i * 32 * BK, 0);
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb0[j] = frag_at(lds + SLOT + b_shift + j * 32 * BK, 0);
   }
-  int cs = 0;  // slot of the current stage's A panel; its B panel is in wrap(cs + 1)
+  int cs = 0;  // slot of the current stage's A panel (2s % NP); its B panel is in wrap(cs + 1)
   for (int64_t s = 0; s + 1 < nst; ++s) {
     const int cs1 = wrap(cs + 1);
     // first half of stage s; its second half's fragments come from the same slots
     half(cs, cs1, 1);
-    // stage s+1 (panels 2s+2, 2s+3) complete: panels up to 2s+4 are issued,
-    // so at most panel 2s+4 (an A panel) may still be outstanding
-    if (s + 2 < nst) wait_vmcnt<PPA>();
-    else wait_vmcnt<0>();
+    // stage s+1 (panels 2s+2, 2s+3) complete: panels up to 2s+NP-1 are
+    // issued, so panels 2s+4 .. may still be outstanding
+    {
+      const int64_t later = np_all - 2 * s - 4;
+      wait_panels<NP - 4, PPA, PPB_ALL>(later < NP - 4 ? later : NP - 4);
+    }
     wait_vmcnt_lgkm0<63>();
     __builtin_amdgcn_s_barrier();
-    // every wave is done with stage s: its slots take panels 2s+5 and 2s+6
-    if (s + 2 < nst) issue_b(kt_begin + s + 2, cs);
-    if (s + 3 < nst) issue_a(kt_begin + s + 3, cs1);
+    // every wave is done with stage s: its slots take panels 2s+NP, 2s+NP+1
+    if (2 * s + NP < np_all) issue_panel(2 * s + NP, cs);
+    if (2 * s + NP + 1 < np_all) issue_panel(2 * s + NP + 1, cs1);
     cs = wrap(cs + 2);
     half(cs, wrap(cs + 1), 0);
     promote();
@@ -1140,11 +1152,11 @@ hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int KIND>
+template <int BM, int BN, int WM, int WN, int KIND, int NP>
 hipError_t launch_panel(const GemmArgs& p, hipStream_t stream) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  const size_t lds = (size_t)PanelGeom<BM, BN, WM, WN, KIND>::LDS;
-  auto kern = gemm_panel_kernel<BM, BN, WM, WN, KIND>;
+  const size_t lds = (size_t)PanelGeom<BM, BN, WM, WN, KIND, NP>::LDS;
+  auto kern = gemm_panel_kernel<BM, BN, WM, WN, KIND, NP>;
   static bool lds_attr_set = false;
   if (lds > 65536 && !lds_attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1231,10 +1243,19 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
     // stages the split plan counts in
     case 14:
       if (KIND != kChannelwise || !panel_eligible<KIND>(p)) return launch_tile<256, 256, 2, 4, 128, KIND>(p, stream);
-      return launch_panel<256, 256, 2, 4, kChannelwise>(p, stream);
+      return launch_panel<256, 256, 2, 4, kChannelwise, 5>(p, stream);
     case 15:
       if (!panel_eligible<KIND>(p)) return launch_tile<256, 128, 4, 2, 128, KIND>(p, stream);
-      return launch_panel<256, 128, 4, 2, KIND>(p, stream);
+      return launch_panel<256, 128, 4, 2, KIND, 5>(p, stream);
+    case 16:
+      if (!panel_eligible<KIND>(p)) return launch_tile<128, 128, 2, 2, 128, KIND>(p, stream);
+      return launch_panel<128, 128, 2, 2, KIND, 5>(p, stream);
+    case 17:
+      if (!panel_eligible<KIND>(p)) return launch_tile<128, 64, 2, 2, 128, KIND>(p, stream);
+      return launch_panel<128, 64, 2, 2, KIND, 5>(p, stream);
+    case 18:
+      if (!panel_eligible<KIND>(p)) return launch_tile<64, 64, 2, 2, 128, KIND>(p, stream);
+      return launch_panel<64, 64, 2, 2, KIND, 5>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1261,6 +1282,9 @@ VariantInfo variant_info(int variant) {
     // panel-ring LDS-DMA variant, channelwise with K % 128 == 0
     case 14: return {256, 256, 128, 8, true};
     case 15: return {256, 128, 128, 8, true};
+    case 16: return {128, 128, 128, 4, true};
+    case 17: return {128, 64, 128, 4, true};
+    case 18: return {64, 64, 128, 4, true};
     default: return {0, 0, 0, 0, false};
   }
 }

@@ -182,6 +182,9 @@ int variant_from_name(const std::string& n) {
   if (n == "t128x128dma") return FP8_VARIANT_T128x128DMA;
   if (n == "t256x256panel") return FP8_VARIANT_T256x256PANEL;
   if (n == "t256x128panel") return FP8_VARIANT_T256x128PANEL;
+  if (n == "t128x128panel") return FP8_VARIANT_T128x128PANEL;
+  if (n == "t128x64panel") return FP8_VARIANT_T128x64PANEL;
+  if (n == "t64x64panel") return FP8_VARIANT_T64x64PANEL;
   return -100;
 }
 
@@ -272,38 +275,47 @@ bool tables_enabled() {
 
 int default_config(int kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* out) {
   // Measured on MI355X (o_proj N = K = 4096): the weight-streaming kernel up
-  // to 32 rows, then ever larger tiles as M grows. From M = 1024 up, GEMMs
-  // whose K is a multiple of 128 take the panel-ring LDS-DMA tiles (both
-  // kinds; 256x256 channelwise only), which beat the register-staged tiles of
-  // the same shape at every M measured. A tile is taken only if it gives the
-  // chip enough workgroups (256x256: every compute unit, the others half of
-  // them); the 64x64 tile is the fallback. Split-K never won in those
-  // measurements, so it is left to the tuned tables.
+  // to 32 rows, then ever larger tiles as M grows. GEMMs whose K is a
+  // multiple of 128 take the panel-ring LDS-DMA tiles (both kinds; 256x256
+  // channelwise only), which beat the register-staged tiles of the same
+  // shape at every M measured: 64x64 up to M = 256, 128x64 up to 1024,
+  // 256x128 up to 2048, then 256x256 where it gives every compute unit a
+  // workgroup. Without that K the register-staged tiles run (channelwise with
+  // K % 64 == 0: the 64-byte-stage DMA tiles at large M); a large tile is
+  // taken only if it gives at least half the compute units a workgroup, the
+  // 64x64 tile being the fallback. Split-K never won in those measurements,
+  // so it is left to the tuned tables.
   const bool cw = kind != FP8_KIND_BLOCKWISE;
   const bool k128 = K % 128 == 0, k64 = cw && K % 64 == 0;
   fp8_tile_config c{};
   c.split_k = 1;
   if (M <= 32) {
     c.variant = FP8_VARIANT_SKINNY;
+  } else if (k128 && M <= 256) {
+    c.variant = FP8_VARIANT_T64x64PANEL;
+  } else if (k128 && M <= 1024) {
+    c.variant = FP8_VARIANT_T128x64PANEL;
+  } else if (k128) {
+    c.variant = FP8_VARIANT_T256x128PANEL;
+    if (M > 2048 && cw && variant_tiles(FP8_VARIANT_T256x256PANEL, M, N) >= 256)
+      c.variant = FP8_VARIANT_T256x256PANEL;
   } else {
     struct Cand {
       int variant;
       int64_t min_tiles;
     };
-    Cand order[5];
+    Cand order[4];
     int n = 0;
     if (M <= 256) {
       order[n++] = {FP8_VARIANT_T64x64, 128};
     } else if (M <= 512) {
       order[n++] = {FP8_VARIANT_T128x64K256, 128};
-    } else if (M < 1024) {
+    } else if (M <= 1024) {
       order[n++] = {FP8_VARIANT_T128x128K256, 128};
       order[n++] = {FP8_VARIANT_T128x64K256, 128};
     } else {
-      if (k128 && cw) order[n++] = {FP8_VARIANT_T256x256PANEL, 256};
-      if (k128) order[n++] = {FP8_VARIANT_T256x128PANEL, 64};
       if (k64) order[n++] = {FP8_VARIANT_T256x128DMA, 128};
-      order[n++] = {FP8_VARIANT_T256x128W8, 128};  // blockwise: 256x256 runs out of registers
+      order[n++] = {FP8_VARIANT_T256x128W8, 128};
       order[n++] = {FP8_VARIANT_T128x128K256, 128};
     }
     c.variant = FP8_VARIANT_T64x64;

@@ -37,28 +37,33 @@ MS = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192]
 
 
 def candidates(kind, m, n, k):
-    """Kernel variants worth timing at this M (the blockwise 256x256 tiles run
-    out of registers and are left out for that kind; the LDS-DMA variants are
-    channelwise only and need K % 64 == 0, the panel variant K % 128 == 0)."""
+    """Kernel variants worth timing at this M: register-staged tiles always;
+    the LDS-DMA tiles where their K condition holds (64-byte stages:
+    channelwise, K % 64 == 0; panel rings: K % 128 == 0); the blockwise
+    256x256 register-staged tiles run out of registers and are left out."""
     if m <= 32:
         return [("skinny", 1)]
     c = []
+    k128 = k % 128 == 0
     if m <= 1024:
-        c += [("t64x64", 1), ("t64x64", 2), ("t128x64k256", 1), ("t64x128k256", 1),
-              ("t128x128k256", 1)]
+        c += [("t64x64", 1), ("t128x64k256", 1), ("t64x128k256", 1), ("t128x128k256", 1)]
+        if k128:
+            c += [("t64x64panel", 1), ("t64x64panel", 2), ("t128x64panel", 1)]
     if m >= 256:
         c += [("t128x128", 1), ("t128x128k256", 1), ("t256x128w8", 1)]
         if kind == "channelwise" and k % 64 == 0:
             c += [("t128x128dma", 1), ("t256x128dma", 1)]
-        if k % 128 == 0:
-            c += [("t256x128panel", 1), ("t256x128panel", 2)]
+        if k128:
+            c += [("t128x64panel", 1), ("t128x128panel", 1), ("t256x128panel", 1)]
     if m >= 1024:
         c += [("t256x128", 1)]
+        if k128:
+            c += [("t256x128panel", 2)]
         if kind == "channelwise":
             c += [("t256x256w8", 1)]
             if k % 64 == 0:
                 c += [("t256x256dma", 1)]
-            if k % 128 == 0:
+            if k128:
                 c += [("t256x256panel", 1)]
     out = []
     for v in c:

@@ -84,7 +84,13 @@ enum {
    * staged with the B panels); other requests run the register-staged
    * 256x128 8-wave kernel. */
   FP8_VARIANT_T256x128PANEL = 15, /* 256x128 block tile, 8 waves */
-  FP8_VARIANT_COUNT = 16,
+  /* Smaller panel-ring tiles (4 waves; five-slot rings of 40-85 KB, so
+   * several workgroups share a compute unit); fallbacks as above, same tile
+   * shape. */
+  FP8_VARIANT_T128x128PANEL = 16, /* 128x128 block tile, 4 waves */
+  FP8_VARIANT_T128x64PANEL = 17,  /* 128x64 block tile, 4 waves */
+  FP8_VARIANT_T64x64PANEL = 18,   /* 64x64 block tile, 4 waves */
+  FP8_VARIANT_COUNT = 19,
 };
 
 /* One tile configuration of the scaled GEMM. The PR34331 digest ("Key source

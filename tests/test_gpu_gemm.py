@@ -305,3 +305,21 @@ CW_PANEL128_CASES = [(1, 300, 392, 1024), (2, 300, 392, 1024), (1, 2048, 4096, 4
                          ids=[f"sk{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in CW_PANEL128_CASES])
 def test_channelwise_panel128_variant(split_k, m, n, k):
     _channelwise_case("cw-panel128", m, n, k, 0.0, True, config=ops.make_config("t256x128panel", split_k))
+
+
+SMALL_PANEL_CASES = [(v, kind, sk, m, n, k) for v in ("t128x128panel", "t128x64panel", "t64x64panel")
+                     for kind, sk, m, n, k in (("cw", 1, 300, 392, 1024), ("cw", 3, 129, 392, 4096),
+                                               ("cw", 1, 1, 64, 128), ("bw", 2, 300, 384, 1024),
+                                               ("bw", 1, 65, 256, 384))]
+
+
+@pytest.mark.parametrize("variant,kind,split_k,m,n,k", SMALL_PANEL_CASES,
+                         ids=[f"{c[0]}-{c[1]}-sk{c[2]}-M{c[3]}-N{c[4]}-K{c[5]}" for c in SMALL_PANEL_CASES])
+def test_small_panel_variants(variant, kind, split_k, m, n, k):
+    """The 4-wave panel-ring tiles, both kinds: ragged M and N, one to many
+    stages, uneven split-K."""
+    cfg = ops.make_config(variant, split_k)
+    if kind == "cw":
+        _channelwise_case("small-panel", m, n, k, 0.0, True, config=cfg)
+    else:
+        _blockwise_case("small-panel", m, n, k, config=cfg, with_bias=True)
