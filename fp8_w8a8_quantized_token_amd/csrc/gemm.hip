@@ -720,20 +720,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmArgs p) {
 // ---------------------------------------------------------------------------
 // Panel-ring kernel (K % 128 == 0): BM x BN block tile, 128-byte K stages,
 // WM x WN waves of 32x32 MFMA tiles as above. A stage is two panels -- its
-// A rows, then its B rows, 128 bytes each, in the 128-byte row layout of the
-// tiled kernel (swz<8>) -- and panel q (stage q/2, B if q is odd) lives in
-// slot q % NP of an NP-slot LDS ring. One LDS-DMA instruction moves 8 whole
-// 128-byte row pieces, one cache line per row: measured on MI355X with every
-// CU streaming, that feeds a CU about 1.45x faster from L2 than the 16
-// half-line pieces of the 64-byte-stage kernel, which bounds that kernel at
-// large M. The MFMAs walk a stage in two 64-deep halves with the fragment
-// pipeline of that kernel (next fragments read while the current ones are
-// multiplied). One barrier per stage, between its halves: it makes the next
-// stage's panels visible and frees the two slots of the finished stage s,
-// which at once take panels 2s+NP and 2s+NP+1, so NP-2 panels stay in flight.
-// Every variant uses five slots: large tiles fill the LDS with them, and for
-// small tiles several workgroups share a compute unit, which measured faster
-// than deeper rings (more bytes in flight per workgroup, fewer workgroups).
+// B (weight) rows, then its A rows, 128 bytes each, in the 128-byte row
+// layout of the tiled kernel (swz<8>) -- and panel q (stage q/2, A if q is
+// odd) lives in slot q % NP of an NP-slot LDS ring. The weight panel goes
+// first because it comes from HBM while the activation panel is mostly an L2
+// hit: with the order the refill below implies, the first panel of a stage
+// is issued two stages before it is needed and the second one stage before,
+// and this order measured up to 1.45x faster for the small tiles. One
+// LDS-DMA instruction moves 8 whole 128-byte row pieces, one cache line per
+// row: measured on MI355X with every CU streaming, that feeds a CU about
+// 1.45x faster from L2 than the 16 half-line pieces of the 64-byte-stage
+// kernel, which bounds that kernel at large M. The MFMAs walk a stage in two
+// 64-deep halves with the fragment pipeline of that kernel (next fragments
+// read while the current ones are multiplied). One barrier per stage, between
+// its halves: it makes the next stage's panels visible and frees the two
+// slots of the finished stage s, which at once take panels 2s+NP and
+// 2s+NP+1, so NP-2 panels stay in flight. Large tiles fill the LDS with five
+// 32 KB slots. For small tiles, five slots let several workgroups share a
+// compute unit; deeper rings (more weight bytes in flight per workgroup, fewer
+// workgroups) measured faster only at small M, so both are variants.
 // Blockwise: the stage is one 128-deep scale block. Its two MFMA halves
 // accumulate into a separate partial tile that is scaled by
 // a_scale[m][kb] * b_scale[nb][kb] before it joins the accumulator. The
@@ -753,15 +758,15 @@ struct PanelGeom {
 };
 
 // Wait until at most the c newest DMA panels of this wave are outstanding,
-// c <= C, those panels alternating A (PA instructions), B (PB), A, ... from
-// the oldest of them.
-template <int C, int PA, int PB>
+// c <= C, those panels alternating P0 instructions, P1, P0, ... from the
+// oldest of them.
+template <int C, int P0, int P1>
 __device__ __forceinline__ void wait_panels(int64_t c) {
   if constexpr (C <= 0) {
     wait_vmcnt<0>();
   } else {
-    if (c >= C) wait_vmcnt<((C + 1) / 2) * PA + (C / 2) * PB>();
-    else wait_panels<C - 1, PA, PB>(c);
+    if (c >= C) wait_vmcnt<((C + 1) / 2) * P0 + (C / 2) * P1>();
+    else wait_panels<C - 1, P0, P1>(c);
   }
 }
 
@@ -785,7 +790,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   static_assert(PPA >= 1 && PPB >= 1 && (BM / 8) % NW == 0 && (BN / 8) % NW == 0, "panel rows per wave");
   static_assert(G::LDS <= 163840, "ring fits the LDS");
   static_assert(NP >= 4, "ring depth");
-  static_assert(((NP - 1) / 2) * PPA + ((NP - 2) / 2) * PPB_ALL < 64, "vmcnt range");
+  static_assert(((NP - 1) / 2) * PPB_ALL + ((NP - 2) / 2) * PPA < 64, "vmcnt range");
   static_assert(BM * BN * 2 <= G::LDS, "output tile fits the ring");
   static_assert(!BW || (SA_LANES >= 1 && SA_LANES <= 64 && BM % (4 * NW) == 0 && G::NBLK <= 4 &&
                         WTN <= 128 && 128 % WTN == 0),
@@ -949,31 +954,32 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
 
   const int64_t np_all = 2 * nst;  // panels of this split
   auto issue_panel = [&](int64_t q, int slot) {
-    if (q & 1) issue_b(kt_begin + (q >> 1), slot);
-    else issue_a(kt_begin + (q >> 1), slot);
+    if (q & 1) issue_a(kt_begin + (q >> 1), slot);
+    else issue_b(kt_begin + (q >> 1), slot);
   };
   if (nst > 0) {
     // prologue: panels 0 .. min(NP, 2 nst) - 1 into slots 0 .. NP-1, then
-    // stage 0 (panels 0 and 1) complete
+    // stage 0 (panels 0 and 1) complete; the outstanding ones start with a
+    // B panel
     const int64_t first = np_all < NP ? np_all : NP;
     for (int64_t q = 0; q < first; ++q) issue_panel(q, (int)q);
-    wait_panels<NP - 2, PPA, PPB_ALL>(first - 2);
+    wait_panels<NP - 2, PPB_ALL, PPA>(first - 2);
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[i] = frag_at(lds + i * 32 * BK, 0);
+    for (int i = 0; i < TM; ++i) fa[i] = frag_at(lds + SLOT + i * 32 * BK, 0);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) fb0[j] = frag_at(lds + SLOT + b_shift + j * 32 * BK, 0);
+    for (int j = 0; j < TN; ++j) fb0[j] = frag_at(lds + b_shift + j * 32 * BK, 0);
   }
-  int cs = 0;  // slot of the current stage's A panel (2s % NP); its B panel is in wrap(cs + 1)
+  int cs = 0;  // slot of the current stage's B panel (2s % NP); its A panel is in wrap(cs + 1)
   for (int64_t s = 0; s + 1 < nst; ++s) {
     const int cs1 = wrap(cs + 1);
     // first half of stage s; its second half's fragments come from the same slots
-    half(cs, cs1, 1);
+    half(cs1, cs, 1);
     // stage s+1 (panels 2s+2, 2s+3) complete: panels up to 2s+NP-1 are
-    // issued, so panels 2s+4 .. may still be outstanding
+    // issued, so panels 2s+4 .. (from a B panel on) may still be outstanding
     {
       const int64_t later = np_all - 2 * s - 4;
-      wait_panels<NP - 4, PPA, PPB_ALL>(later < NP - 4 ? later : NP - 4);
+      wait_panels<NP - 4, PPB_ALL, PPA>(later < NP - 4 ? later : NP - 4);
     }
     wait_vmcnt_lgkm0<63>();
     __builtin_amdgcn_s_barrier();
@@ -981,11 +987,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
     if (2 * s + NP < np_all) issue_panel(2 * s + NP, cs);
     if (2 * s + NP + 1 < np_all) issue_panel(2 * s + NP + 1, cs1);
     cs = wrap(cs + 2);
-    half(cs, wrap(cs + 1), 0);
+    half(wrap(cs + 1), cs, 0);
     promote();
   }
   if (nst > 0) {  // last stage: both halves from the slots already in LDS
-    half(cs, wrap(cs + 1), 1);
+    half(wrap(cs + 1), cs, 1);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -1256,6 +1262,12 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
     case 18:
       if (!panel_eligible<KIND>(p)) return launch_tile<64, 64, 2, 2, 128, KIND>(p, stream);
       return launch_panel<64, 64, 2, 2, KIND, 5>(p, stream);
+    case 19:
+      if (!panel_eligible<KIND>(p)) return launch_tile<64, 64, 2, 2, 128, KIND>(p, stream);
+      return launch_panel<64, 64, 2, 2, KIND, 9>(p, stream);
+    case 20:
+      if (!panel_eligible<KIND>(p)) return launch_tile<128, 64, 2, 2, 128, KIND>(p, stream);
+      return launch_panel<128, 64, 2, 2, KIND, 7>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1285,6 +1297,8 @@ VariantInfo variant_info(int variant) {
     case 16: return {128, 128, 128, 4, true};
     case 17: return {128, 64, 128, 4, true};
     case 18: return {64, 64, 128, 4, true};
+    case 19: return {64, 64, 128, 4, true};
+    case 20: return {128, 64, 128, 4, true};
     default: return {0, 0, 0, 0, false};
   }
 }

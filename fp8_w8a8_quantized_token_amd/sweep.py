@@ -48,7 +48,8 @@ def candidates(kind, m, n, k):
     if m <= 1024:
         c += [("t64x64", 1), ("t128x64k256", 1), ("t64x128k256", 1), ("t128x128k256", 1)]
         if k128:
-            c += [("t64x64panel", 1), ("t64x64panel", 2), ("t128x64panel", 1)]
+            c += [("t64x64panel", 1), ("t64x64panel", 2), ("t128x64panel", 1),
+                  ("t64x64deep", 1), ("t64x64deep", 2), ("t128x64deep", 1)]
     if m >= 256:
         c += [("t128x128", 1), ("t128x128k256", 1), ("t256x128w8", 1)]
         if kind == "channelwise" and k % 64 == 0:

@@ -90,7 +90,11 @@ enum {
   FP8_VARIANT_T128x128PANEL = 16, /* 128x128 block tile, 4 waves */
   FP8_VARIANT_T128x64PANEL = 17,  /* 128x64 block tile, 4 waves */
   FP8_VARIANT_T64x64PANEL = 18,   /* 64x64 block tile, 4 waves */
-  FP8_VARIANT_COUNT = 19,
+  /* The same with deeper rings (9 and 7 slots): more weight bytes in flight
+   * per workgroup, fewer workgroups per compute unit; faster at small M. */
+  FP8_VARIANT_T64x64DEEP = 19,    /* 64x64 block tile, 4 waves */
+  FP8_VARIANT_T128x64DEEP = 20,   /* 128x64 block tile, 4 waves */
+  FP8_VARIANT_COUNT = 21,
 };
 
 /* One tile configuration of the scaled GEMM. The PR34331 digest ("Key source
