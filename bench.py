@@ -156,7 +156,7 @@ def cpu_baseline():
         w = synth.weights("o_proj", N, K).numpy()
         wq_c, ws_c = oracle.quant_weight_per_channel(w)
         wq_b, ws_b = oracle.quant_weight_blockwise(w)
-        sample = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096]
+        sample = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192]
         flops = 0
         t0 = time.perf_counter()
         for m in sample:
