@@ -1268,6 +1268,12 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
     case 20:
       if (!panel_eligible<KIND>(p)) return launch_tile<128, 64, 2, 2, 128, KIND>(p, stream);
       return launch_panel<128, 64, 2, 2, KIND, 7>(p, stream);
+    case 21:
+      if (!panel_eligible<KIND>(p)) return launch_tile<128, 128, 2, 4, 128, KIND>(p, stream);
+      return launch_panel<128, 128, 2, 4, KIND, 5>(p, stream);
+    case 22:
+      if (!panel_eligible<KIND>(p)) return launch_tile<128, 64, 4, 2, 128, KIND>(p, stream);
+      return launch_panel<128, 64, 4, 2, KIND, 5>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1299,6 +1305,8 @@ VariantInfo variant_info(int variant) {
     case 18: return {64, 64, 128, 4, true};
     case 19: return {64, 64, 128, 4, true};
     case 20: return {128, 64, 128, 4, true};
+    case 21: return {128, 128, 128, 8, true};
+    case 22: return {128, 64, 128, 8, true};
     default: return {0, 0, 0, 0, false};
   }
 }

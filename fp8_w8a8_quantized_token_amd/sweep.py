@@ -55,7 +55,9 @@ def candidates(kind, m, n, k):
         if kind == "channelwise" and k % 64 == 0:
             c += [("t128x128dma", 1), ("t256x128dma", 1)]
         if k128:
-            c += [("t128x64panel", 1), ("t128x128panel", 1), ("t256x128panel", 1)]
+            c += [("t128x64panel", 1), ("t128x128panel", 1), ("t256x128panel", 1),
+                  ("t128x64panel8", 1), ("t128x128panel8", 1), ("t128x128panel", 2),
+                  ("t128x128panel8", 2)]
     if m >= 1024:
         c += [("t256x128", 1)]
         if k128:

@@ -94,7 +94,10 @@ enum {
    * per workgroup, fewer workgroups per compute unit; faster at small M. */
   FP8_VARIANT_T64x64DEEP = 19,    /* 64x64 block tile, 4 waves */
   FP8_VARIANT_T128x64DEEP = 20,   /* 128x64 block tile, 4 waves */
-  FP8_VARIANT_COUNT = 21,
+  /* 8-wave forms of the small panel tiles (two waves per SIMD) */
+  FP8_VARIANT_T128x128PANEL8 = 21, /* 128x128 block tile, 8 waves */
+  FP8_VARIANT_T128x64PANEL8 = 22,  /* 128x64 block tile, 8 waves */
+  FP8_VARIANT_COUNT = 23,
 };
 
 /* One tile configuration of the scaled GEMM. The PR34331 digest ("Key source
