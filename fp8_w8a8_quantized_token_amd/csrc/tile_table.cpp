@@ -278,17 +278,17 @@ bool tables_enabled() {
 }  // namespace
 
 int default_config(int kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* out) {
-  // Measured on MI355X (o_proj N = K = 4096): the weight-streaming kernel up
-  // to 32 rows, then ever larger tiles as M grows. GEMMs whose K is a
-  // multiple of 128 take the panel-ring LDS-DMA tiles (both kinds; 256x256
-  // channelwise only), which beat the register-staged tiles of the same
-  // shape at every M measured: 64x64 up to M = 256, 128x64 up to 1024,
-  // 256x128 up to 2048, then 256x256 where it gives every compute unit a
-  // workgroup. Without that K the register-staged tiles run (channelwise with
-  // K % 64 == 0: the 64-byte-stage DMA tiles at large M); a large tile is
-  // taken only if it gives at least half the compute units a workgroup, the
-  // 64x64 tile being the fallback. Split-K never won in those measurements,
-  // so it is left to the tuned tables.
+  // Measured on MI355X (o_proj, qkv, down, gate_up and the blockwise shapes,
+  // HBM-resident weights): the weight-streaming kernel up to 32 rows, then,
+  // for K % 128 == 0, the panel-ring LDS-DMA tiles: 64x64 up to M = 256 (deep
+  // ring for channelwise), 128x64 up to 512 (deep ring for channelwise), the
+  // 8-wave 128x128 up to 1024, then 256x128, or channelwise 256x256 where it
+  // gives at least 192 workgroups (at M <= 1024 only if it fills all 256
+  // compute units). Without that K the register-staged tiles run
+  // (channelwise with K % 64 == 0: the 64-byte-stage DMA tiles at large M); a
+  // large tile is taken only if it gives at least half the compute units a
+  // workgroup, the 64x64 tile being the fallback. Split-K rarely won in those
+  // measurements, so it is left to the tuned tables.
   const bool cw = kind != FP8_KIND_BLOCKWISE;
   const bool k128 = K % 128 == 0, k64 = cw && K % 64 == 0;
   fp8_tile_config c{};
@@ -296,13 +296,15 @@ int default_config(int kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* o
   if (M <= 32) {
     c.variant = FP8_VARIANT_SKINNY;
   } else if (k128 && M <= 256) {
-    c.variant = FP8_VARIANT_T64x64PANEL;
+    c.variant = cw ? FP8_VARIANT_T64x64DEEP : FP8_VARIANT_T64x64PANEL;
+  } else if (k128 && M <= 512) {
+    c.variant = cw ? FP8_VARIANT_T128x64DEEP : FP8_VARIANT_T128x64PANEL;
   } else if (k128 && M <= 1024) {
-    c.variant = FP8_VARIANT_T128x64PANEL;
+    c.variant = FP8_VARIANT_T128x128PANEL8;
+    if (cw && variant_tiles(FP8_VARIANT_T256x256PANEL, M, N) >= 256) c.variant = FP8_VARIANT_T256x256PANEL;
   } else if (k128) {
     c.variant = FP8_VARIANT_T256x128PANEL;
-    if (M > 2048 && cw && variant_tiles(FP8_VARIANT_T256x256PANEL, M, N) >= 256)
-      c.variant = FP8_VARIANT_T256x256PANEL;
+    if (cw && variant_tiles(FP8_VARIANT_T256x256PANEL, M, N) >= 192) c.variant = FP8_VARIANT_T256x256PANEL;
   } else {
     struct Cand {
       int variant;
