@@ -112,7 +112,8 @@ __device__ __forceinline__ uint2 pack_out4(const GemmArgs& p, int64_t n, f32x4 v
 // row to global memory. Stored straight from the MFMA layout, one store
 // instruction covered 32 rows 16 bytes each and the output went out at a
 // fraction of the write bandwidth. sw(r) = r % CH for rows of 256 bytes or
-// more, (r / 2) % 8 for 128-byte rows: conflict-free for both phases. The LDS
+// more, (r / 2) % 8 for 128-byte rows, (r / 4) % 4 for 64-byte rows:
+// conflict-free for both phases. The LDS
 // must hold BM * BN * 2 bytes; the function begins with a barrier, so the
 // caller may still be reading it.
 template <int BM, int BN, int WM, int WN, int KIND>
@@ -124,8 +125,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p,
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int CH = BN / 8;  // 16-byte chunks per tile row
-  static_assert(CH == 8 || CH == 16 || CH == 32, "tile width");
-  auto sw = [](int r) { return CH >= 16 ? (r & (CH - 1)) : ((r >> 1) & (CH - 1)); };
+  static_assert(CH == 4 || CH == 8 || CH == 16 || CH == 32, "tile width");
+  auto sw = [](int r) {
+    return CH >= 16 ? (r & (CH - 1)) : CH == 8 ? ((r >> 1) & (CH - 1)) : ((r >> 2) & (CH - 1));
+  };
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -1274,6 +1277,13 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
     case 22:
       if (!panel_eligible<KIND>(p)) return launch_tile<128, 64, 4, 2, 128, KIND>(p, stream);
       return launch_panel<128, 64, 4, 2, KIND, 5>(p, stream);
+    // narrow deep-ring tiles for small M: more workgroups at the same bytes per CU
+    case 23:
+      if (!panel_eligible<KIND>(p)) return launch_tile<32, 32, 1, 1, 128, KIND>(p, stream);
+      return launch_panel<32, 32, 1, 1, KIND, 9>(p, stream);
+    case 24:
+      if (!panel_eligible<KIND>(p)) return launch_tile<64, 32, 2, 1, 128, KIND>(p, stream);
+      return launch_panel<64, 32, 2, 1, KIND, 7>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1307,6 +1317,8 @@ VariantInfo variant_info(int variant) {
     case 20: return {128, 64, 128, 4, true};
     case 21: return {128, 128, 128, 8, true};
     case 22: return {128, 64, 128, 8, true};
+    case 23: return {32, 32, 128, 1, true};
+    case 24: return {64, 32, 128, 2, true};
     default: return {0, 0, 0, 0, false};
   }
 }

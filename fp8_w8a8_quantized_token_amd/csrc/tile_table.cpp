@@ -189,6 +189,8 @@ int variant_from_name(const std::string& n) {
   if (n == "t128x64deep") return FP8_VARIANT_T128x64DEEP;
   if (n == "t128x128panel8") return FP8_VARIANT_T128x128PANEL8;
   if (n == "t128x64panel8") return FP8_VARIANT_T128x64PANEL8;
+  if (n == "t32x32deep") return FP8_VARIANT_T32x32DEEP;
+  if (n == "t64x32deep") return FP8_VARIANT_T64x32DEEP;
   return -100;
 }
 

@@ -50,6 +50,8 @@ def candidates(kind, m, n, k):
         if k128:
             c += [("t64x64panel", 1), ("t64x64panel", 2), ("t128x64panel", 1),
                   ("t64x64deep", 1), ("t64x64deep", 2), ("t128x64deep", 1)]
+            if m <= 256:
+                c += [("t32x32deep", 1), ("t64x32deep", 1)]
     if m >= 256:
         c += [("t128x128", 1), ("t128x128k256", 1), ("t256x128w8", 1)]
         if kind == "channelwise" and k % 64 == 0:

@@ -97,7 +97,11 @@ enum {
   /* 8-wave forms of the small panel tiles (two waves per SIMD) */
   FP8_VARIANT_T128x128PANEL8 = 21, /* 128x128 block tile, 8 waves */
   FP8_VARIANT_T128x64PANEL8 = 22,  /* 128x64 block tile, 8 waves */
-  FP8_VARIANT_COUNT = 23,
+  /* Narrow deep-ring tiles for small M (more workgroups for the same bytes
+   * per compute unit); fallbacks: register-staged tiles of the same shape. */
+  FP8_VARIANT_T32x32DEEP = 23,     /* 32x32 block tile, 1 wave, 9-slot ring */
+  FP8_VARIANT_T64x32DEEP = 24,     /* 64x32 block tile, 2 waves, 7-slot ring */
+  FP8_VARIANT_COUNT = 25,
 };
 
 /* One tile configuration of the scaled GEMM. The PR34331 digest ("Key source

@@ -325,7 +325,8 @@ def test_small_panel_variants(variant, kind, split_k, m, n, k):
         _blockwise_case("small-panel", m, n, k, config=cfg, with_bias=True)
 
 
-DEEP_CASES = [(v, kind, sk, m, n, k) for v in ("t64x64deep", "t128x64deep", "t128x128panel8", "t128x64panel8")
+DEEP_CASES = [(v, kind, sk, m, n, k) for v in ("t64x64deep", "t128x64deep", "t128x128panel8", "t128x64panel8",
+                                                "t32x32deep", "t64x32deep")
               for kind, sk, m, n, k in (("cw", 1, 300, 392, 1024), ("cw", 2, 129, 392, 4096),
                                         ("cw", 1, 1, 64, 128), ("cw", 1, 65, 256, 768),
                                         ("bw", 2, 300, 384, 1024), ("bw", 1, 65, 256, 768))]
@@ -342,3 +343,12 @@ def test_deep_ring_variants(variant, kind, split_k, m, n, k):
     else:
         _blockwise_case("deep-panel", m, n, k, config=cfg, with_bias=True)
 
+
+
+def test_narrow_tiles_fall_back_when_k_not_multiple_of_128():
+    """The register-staged 32x32 and 64x32 tiles behind the narrow panel
+    variants (channelwise K % 128 != 0), with split-K on a ragged M."""
+    _channelwise_case("narrow-fallback", 70, 200, 1088, 0.0, True, config=ops.make_config("t32x32deep", 2),
+                      sample=False)
+    _channelwise_case("narrow-fallback", 70, 200, 1088, 0.0, True, config=ops.make_config("t64x32deep", 3),
+                      sample=False)
