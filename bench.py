@@ -4,7 +4,9 @@ One step = one pass of the whole hot path over the o_proj workload (N = K =
 4096, M in 8192, 4096, ..., 1): for every M, the channelwise linear (per-token
 quant, tile-config lookup, channelwise scaled GEMM with its fused epilogue and
 in-launch split-K reduction) and the blockwise linear (row-padded group-128
-quant, lookup, blockwise scaled GEMM). Inputs are synthetic and resident in HBM
+quant, lookup, blockwise scaled GEMM). For M <= 4 each linear is one launch,
+the quantization fused into the skinny GEMM (it still writes the codes and
+scales); above, the quantizer and the GEMM are two launches. Inputs are synthetic and resident in HBM
 before timing starts; every (M, kind) has its own weight copy, so a step
 touches ~1 GB and the 256 MB last-level cache cannot serve the weights.
 
@@ -77,6 +79,8 @@ def build_step(torch, ops, synth, dev):
         for m in sorted(MS, reverse=True):
             x = synth.activations("o_proj", m, K, outlier_frac=0.01).to(dev)
             w = w_host.to(dev)
+            kind_id = ops.KIND_CHANNELWISE if kind == "channelwise" else ops.KIND_BLOCKWISE
+            fused = ops.linear_launches(kind_id, m, N, K) == 1
             if kind == "channelwise":
                 wq, ws = ops.quant_per_token(w)           # per-output-channel weight quant
                 q = torch.empty((m, K), dtype=torch.uint8, device=dev)
@@ -86,8 +90,11 @@ def build_step(torch, ops, synth, dev):
                 label_q = "quant_per_token"
                 label_g = f"gemm_channelwise[{cfg['variant']}]"
 
-                fq = ops.prepare("quant_per_token", x, out=q, scale=s)
-                fg = ops.prepare("scaled_mm_channelwise", q, wq, s, ws, out=out)
+                if fused:
+                    fl = ops.prepare("linear_channelwise", x, wq, ws, out=out, q=q, scale=s)
+                else:
+                    fq = ops.prepare("quant_per_token", x, out=q, scale=s)
+                    fg = ops.prepare("scaled_mm_channelwise", q, wq, s, ws, out=out)
                 qb = quant_bytes(m, K, K)
             else:
                 # codes from the group-128 quant of the weight rows, scales as
@@ -103,14 +110,27 @@ def build_step(torch, ops, synth, dev):
                 label_q = "quant_per_token_group"
                 label_g = f"gemm_blockwise[{cfg['variant']}]"
 
-                fq = ops.prepare("quant_per_token_group", x, 128, row_alignment=4, out=q,
-                                 scale_storage=st)
-                fg = ops.prepare("scaled_mm_blockwise", q, wq, st.transpose(0, 1), ws, m=m, out=out)
+                if fused:
+                    fl = ops.prepare("linear_blockwise", x, wq, ws, row_alignment=4, out=out, q=q,
+                                     scale=st)
+                else:
+                    fq = ops.prepare("quant_per_token_group", x, 128, row_alignment=4, out=q,
+                                     scale_storage=st)
+                    fg = ops.prepare("scaled_mm_blockwise", q, wq, st.transpose(0, 1), ws, m=m,
+                                     out=out)
                 qb = quant_bytes(m, K, 128)
-            launches.append(Launch(label_q, fq, 0, qb))
-            launches.append(Launch(label_g, fg, 2 * m * N * K, gemm_bytes(kind, m, N, K)))
-            launches[-1].m, launches[-1].kind = m, kind
-            launches[-2].m, launches[-2].kind = m, kind
+            if fused:
+                # x read once, codes and scales still written, codes not re-read
+                step = [Launch(f"linear_{kind}_fused[{cfg['variant']}]", fl, 2 * m * N * K,
+                               qb + gemm_bytes(kind, m, N, K) - m * K)]
+                step[0].part = "linear"
+            else:
+                step = [Launch(label_q, fq, 0, qb),
+                        Launch(label_g, fg, 2 * m * N * K, gemm_bytes(kind, m, N, K))]
+                step[0].part, step[1].part = "quant", "gemm"
+            for l in step:
+                l.m, l.kind = m, kind
+            launches += step
     torch.cuda.synchronize()
     return launches
 
@@ -224,7 +244,7 @@ def main():
     for (e0, e1), l in zip(probe, launches):
         us = e0.elapsed_time(e1) * 1e3
         share[l.label] = share.get(l.label, 0.0) + us
-        key = f"{l.kind}/{'quant' if l.flops == 0 else 'gemm'}/M={l.m}"
+        key = f"{l.kind}/{l.part}/M={l.m}"
         per_m[key] = {"us_event": us, "flops": l.flops, "bytes": l.nbytes}
     dom_label = max(share, key=share.get)
     dom_idx = [i for i, l in enumerate(launches) if l.label == dom_label]

@@ -61,6 +61,13 @@ SIGNATURES = {
                                            ctypes.POINTER(TileConfig), c_vp]),
     "fp8_scaled_mm_workspace_size": (c_size, [c_i32, c_i64, c_i64, c_i64,
                                               ctypes.POINTER(TileConfig)]),
+    "fp8_linear_channelwise": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64,
+                                       c_i64, c_i64, c_f32, c_vp, c_i64, c_vp, c_vp, c_size,
+                                       ctypes.POINTER(TileConfig), c_vp]),
+    "fp8_linear_blockwise": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64,
+                                     c_i64, c_i64, c_i32, c_f32, c_vp, c_i64, c_vp, c_vp, c_size,
+                                     ctypes.POINTER(TileConfig), c_vp]),
+    "fp8_linear_launches": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(TileConfig)]),
     "fp8_tile_config_lookup": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(TileConfig)]),
     "fp8_tile_config_default": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(TileConfig)]),
     "fp8_tile_config_set_dir": (c_i32, [ctypes.c_char_p]),

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "fp8w8a8.h"
@@ -130,6 +131,54 @@ int run_gemm(const char* fn, int kind, const uint8_t* a, const uint8_t* b, const
   return hip_status(launch_gemm(kind, cfg.variant, p, stream), fn);
 }
 
+// FP8W8A8_FUSED_LINEAR=0 turns the single-launch linear off (read per call).
+bool fused_linear_enabled() {
+  const char* v = std::getenv("FP8W8A8_FUSED_LINEAR");
+  return !(v && v[0] == '0' && v[1] == '\0');
+}
+
+bool linear_fuses(const fp8_tile_config& cfg, int64_t M) {
+  return cfg.variant == FP8_VARIANT_SKINNY && M <= kFusedRows && fused_linear_enabled();
+}
+
+// Activation quantization then scaled GEMM; one fused launch when the skinny
+// kernel serves M <= kFusedRows, else the quantizer and the GEMM back to back.
+int run_linear(const char* fn, int kind, const uint16_t* x, const uint8_t* b, const float* b_scale,
+               const uint16_t* bias, uint16_t* out, int64_t M, int64_t N, int64_t K, int64_t ldx,
+               int64_t ldb, int64_t ldc, int32_t row_alignment, float eps, uint8_t* q, int64_t ldq,
+               float* a_scale, void* ws, size_t ws_bytes, const fp8_tile_config* cfg_in,
+               hipStream_t stream) {
+  const bool bw = kind == FP8_KIND_BLOCKWISE;
+  if (bw && row_alignment < 1) return fail(FP8_ERR_INVALID, "%s: row_alignment must be >= 1", fn);
+  int st = check_quant(fn, x, M, K, ldx, q, ldq, a_scale, eps);
+  if (st) return st;
+  st = check_gemm(fn, q, b, a_scale, b_scale, bias, out, M, N, K, ldq, ldb, ldc);
+  if (st) return st;
+  if (M == 0) return ok();
+  if (bw && (N % 128 != 0 || K % 128 != 0))
+    return fail(FP8_ERR_UNSUPPORTED, "%s: N=%lld and K=%lld must be multiples of 128", fn, (long long)N,
+                (long long)K);
+  const int64_t m_pad = bw ? fp8_padded_rows(M, row_alignment) : M;
+  fp8_tile_config cfg;
+  st = resolve_config(kind, M, N, K, cfg_in, &cfg);
+  if (st) return st;
+  if (linear_fuses(cfg, M)) {
+    GemmArgs p{};
+    p.a = q; p.b = b; p.sa = a_scale; p.sa_ld = m_pad; p.sb = b_scale; p.bias = bias; p.out = out;
+    p.M = M; p.N = N; p.K = K; p.lda = ldq; p.ldb = ldb; p.ldc = ldc;
+    p.split_k = 1;
+    p.k_tiles_per_split = (int)((K + 127) / 128);
+    const QuantArgs qa{x, ldx, q, ldq, a_scale, m_pad, eps};
+    return hip_status(launch_linear_fused(kind, p, qa, stream), fn);
+  }
+  const hipError_t e = bw ? launch_quant_per_token_group(x, M, K, ldx, 128, m_pad, q, ldq, a_scale, eps, stream)
+                          : launch_quant_per_token(x, M, K, ldx, q, ldq, a_scale, eps, stream);
+  st = hip_status(e, fn);
+  if (st) return st;
+  return run_gemm(fn, kind, q, b, a_scale, m_pad, b_scale, bias, out, M, N, K, ldq, ldb, ldc, ws,
+                  ws_bytes, &cfg, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -225,6 +274,34 @@ size_t fp8_scaled_mm_workspace_size(int32_t kind, int64_t M, int64_t N, int64_t 
   int splits, per;
   split_plan(K, cfg.bk, cfg.split_k, &splits, &per);
   return variant_workspace_bytes(cfg.variant, splits, M, N);
+}
+
+int fp8_linear_channelwise(const uint16_t* x, const uint8_t* b, const float* b_scale,
+                           const uint16_t* bias, uint16_t* out, int64_t M, int64_t N, int64_t K,
+                           int64_t ldx, int64_t ldb, int64_t ldc, float eps, uint8_t* q,
+                           int64_t ldq, float* a_scale, void* ws, size_t ws_bytes,
+                           const fp8_tile_config* cfg, hipStream_t stream) {
+  return run_linear("fp8_linear_channelwise", FP8_KIND_CHANNELWISE, x, b, b_scale, bias, out, M, N,
+                    K, ldx, ldb, ldc, 1, eps, q, ldq, a_scale, ws, ws_bytes, cfg, stream);
+}
+
+int fp8_linear_blockwise(const uint16_t* x, const uint8_t* b, const float* b_scale,
+                         const uint16_t* bias, uint16_t* out, int64_t M, int64_t N, int64_t K,
+                         int64_t ldx, int64_t ldb, int64_t ldc, int32_t row_alignment, float eps,
+                         uint8_t* q, int64_t ldq, float* a_scale, void* ws, size_t ws_bytes,
+                         const fp8_tile_config* cfg, hipStream_t stream) {
+  return run_linear("fp8_linear_blockwise", FP8_KIND_BLOCKWISE, x, b, b_scale, bias, out, M, N, K,
+                    ldx, ldb, ldc, row_alignment, eps, q, ldq, a_scale, ws, ws_bytes, cfg, stream);
+}
+
+int fp8_linear_launches(int32_t kind, int64_t M, int64_t N, int64_t K, const fp8_tile_config* cfg_in) {
+  if ((kind != FP8_KIND_CHANNELWISE && kind != FP8_KIND_BLOCKWISE) || M < 0 || N <= 0 || K <= 0)
+    return fail(FP8_ERR_INVALID, "fp8_linear_launches: bad arguments");
+  if (M == 0) return 0;
+  fp8_tile_config cfg;
+  const int st = resolve_config(kind, M, N, K, cfg_in, &cfg);
+  if (st) return st;
+  return linear_fuses(cfg, M) ? 1 : 2;
 }
 
 int fp8_tile_config_lookup(int32_t kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* out) {

@@ -1039,7 +1039,9 @@ struct StreamRegs {
   uint4 a[MT][4][2];      // activation fragments: 4 K blocks x 32 bytes
 };
 
-template <int MT>
+// Loads of one chunk: the weight rows always; the activation code fragments
+// unless the quantization is fused (FQ), where the codes come from LDS.
+template <int MT, bool FQ>
 __device__ __forceinline__ void stream_load(const GemmArgs& p, StreamRegs<MT>& r, int64_t k0,
                                             int64_t n0, int wave, int lane) {
 #pragma unroll
@@ -1052,6 +1054,7 @@ __device__ __forceinline__ void stream_load(const GemmArgs& p, StreamRegs<MT>& r
       r.b[rr][sgm] = (n < p.N && off < p.K) ? load16_nt(row + off) : make_uint4(0, 0, 0, 0);
     }
   }
+  if constexpr (FQ) return;
   const int g = lane >> 4;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
@@ -1067,57 +1070,181 @@ __device__ __forceinline__ void stream_load(const GemmArgs& p, StreamRegs<MT>& r
   }
 }
 
-template <int MT, int KIND>
-__global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs p) {
-  __shared__ uint4 wt[16 * (kStreamChunk / 16)];  // 64 KB: one weight chunk
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+// Fused quantization (M <= FR): thread tid owns the 8-element unit tid of
+// every row of a chunk (K elements [k0 + 8 tid, k0 + 8 tid + 8)), so the
+// quantizing work grows with M, not with the 16-row MFMA tile. Its bf16 loads
+// are issued before the chunk's weight loads: loads complete in issue order,
+// so the quantization waits only for the (cache-resident) activation while
+// the weight chunk is still arriving from HBM.
+template <int FR>
+__device__ __forceinline__ void fused_load_x(const GemmArgs& p, const QuantArgs& qa, uint4 (&xr)[FR],
+                                             int64_t k0, int tid) {
+  const int64_t k = k0 + 8 * tid;
+#pragma unroll
+  for (int i = 0; i < FR; ++i)
+    xr[i] = (i < p.M && k < p.K) ? load16(qa.x + i * qa.ldx + k) : make_uint4(0, 0, 0, 0);
+}
+
+// Max over each aligned group of 16 lanes, with DPP lane moves (no LDS
+// crossbar): xor 1 and xor 2 inside quads, then the 8-lane and 16-lane
+// mirrors, each pairing the two halves whose maxima are already uniform.
+__device__ __forceinline__ float max16_dpp(float v) {
+  auto mv = [](float x, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value,
+                                                      0xF, 0xF, false));
+  };
+  v = fmaxf(v, mv(v, IntC<0xB1>()));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, mv(v, IntC<0x4E>()));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, mv(v, IntC<0x141>()));  // row_half_mirror
+  v = fmaxf(v, mv(v, IntC<0x140>()));  // row_mirror
+  return v;
+}
+
+// FR > 0: the activation quantization is fused, for M <= FR rows (FR a power
+// of two, a compile-time row count so that the per-row work is straight-line
+// code the compiler can interleave).
+template <int MT, int KIND, int FR>
+__global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs p, QuantArgs qa) {
+  constexpr bool FQ = FR > 0;
+  static_assert(!FQ || (MT == 1 && FR <= 16), "the fused quantization serves one 16-row tile");
+  constexpr int CPR = kStreamChunk / 16;  // 16-byte LDS chunks per chunk row
+  __shared__ uint4 wt[16 * CPR];          // 64 KB: one weight chunk
+  // FQ: the activation codes of the chunk in the weight chunk's layout, their
+  // group scales (blockwise) and the row scales (per token)
+  __shared__ uint4 codes[FQ ? 16 * CPR : 1];
+  __shared__ float blk_scale[FQ ? 16 * (kStreamChunk / 128) : 1];
+  __shared__ float row_scale[FQ ? 16 : 1], row_inv[FQ ? 16 : 1];
+  __shared__ float row_part[FQ ? kStreamWaves * 16 : 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int g = lane >> 4;
   const int r16 = lane & 15;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int64_t kb_all = p.K / 128;
+  // with FQ, workgroup 0 also stores the codes and scales it computes
+  const bool writer = FQ && blockIdx.x == 0;
 
   f32x4 acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  uint4 xr[FQ ? FR : 1];
+  if constexpr (FQ) fused_load_x<FR>(p, qa, xr, 0, tid);
   StreamRegs<MT> cur;
-  stream_load<MT>(p, cur, 0, n0, wave, lane);
+  stream_load<MT, FQ>(p, cur, 0, n0, wave, lane);
+
+  if constexpr (FQ) {
+    // code rows FR..15 stay zero (rows M..FR-1 get the codes of zeros); none
+    // of their outputs is stored
+    for (int idx = tid + FR * CPR; idx < 16 * CPR; idx += kStreamWaves * 64)
+      codes[idx] = make_uint4(0, 0, 0, 0);
+    for (int idx = tid; idx < 16 * (kStreamChunk / 128); idx += kStreamWaves * 64) blk_scale[idx] = 0.0f;
+    if constexpr (KIND == kChannelwise) {
+      // per-token scales: absmax over the whole row (chunks after the first
+      // are read here once more), reduced over the workgroup through LDS
+      float am[FR];
+#pragma unroll
+      for (int i = 0; i < FR; ++i) am[i] = absmax8_bf16(xr[i]);  // zero where not loaded
+      for (int64_t k1 = kStreamChunk; k1 < p.K; k1 += kStreamChunk) {
+        uint4 xn[FR];
+        fused_load_x<FR>(p, qa, xn, k1, tid);
+#pragma unroll
+        for (int i = 0; i < FR; ++i) am[i] = fmaxf(am[i], absmax8_bf16(xn[i]));
+      }
+#pragma unroll
+      for (int i = 0; i < FR; ++i) {
+        const float w = wave_max(am[i]);
+        if (lane == 0) row_part[wave * 16 + i] = w;
+      }
+      __syncthreads();
+      if (tid < FR) {
+        float mx = row_part[tid];
+        for (int w = 1; w < kStreamWaves; ++w) mx = fmaxf(mx, row_part[w * 16 + tid]);
+        const float sc = fmaxf(mx, qa.eps) / kE4M3Max;
+        row_scale[tid] = sc;
+        row_inv[tid] = 1.0f / sc;
+        if (writer && tid < p.M) qa.scale[tid] = sc;
+      }
+    }
+  }
+
   for (int64_t k0 = 0; k0 < p.K; k0 += kStreamChunk) {
     __syncthreads();  // the previous chunk's fragment reads are done
+    if constexpr (FQ) {
+      // quantize this chunk's activation into `codes` (16-byte chunk c of row
+      // i at position c ^ i, as the weights); unit tid is bytes 8 tid .. +7
+      const int64_t k = k0 + 8 * tid;
+      const int pos = ((tid >> 1) << 4) + ((tid & 1) << 3);
+      const bool kin = k < p.K;
+#pragma unroll
+      for (int i = 0; i < FR; ++i) {
+        float sc, y;
+        if constexpr (KIND == kChannelwise) {
+          sc = row_scale[i];
+          y = row_inv[i];
+        } else {  // group of 128 = 16 consecutive threads
+          sc = fmaxf(max16_dpp(absmax8_bf16(xr[i])), qa.eps) / kE4M3Max;
+          y = 1.0f / sc;
+        }
+        // rows >= M quantize zeros; K past the end gives zero codes, as in
+        // the unfused path
+        const uint2 c = kin ? quant8_bf16(xr[i], sc, y) : make_uint2(0, 0);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(codes) + i * (CPR * 16) +
+                                  (pos ^ (i << 4))) = c;
+        if (KIND == kBlockwise && (tid & 15) == 0) blk_scale[i * (kStreamChunk / 128) + (tid >> 4)] = sc;
+        if (writer && kin && i < p.M) {
+          *reinterpret_cast<uint2*>(qa.q + i * qa.ldq + k) = c;
+          if (KIND == kBlockwise && (tid & 15) == 0) qa.scale[(k / 128) * qa.scale_ld + i] = sc;
+        }
+      }
+    }
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int r = 2 * wave + rr;
 #pragma unroll
       for (int sgm = 0; sgm < 4; ++sgm) {
         const int c = sgm * 64 + lane;
-        wt[r * (kStreamChunk / 16) + (c ^ r)] = cur.b[rr][sgm];
+        wt[r * CPR + (c ^ r)] = cur.b[rr][sgm];
       }
     }
     __syncthreads();
     StreamRegs<MT> use = cur;
-    if (k0 + kStreamChunk < p.K) stream_load<MT>(p, cur, k0 + kStreamChunk, n0, wave, lane);
+    if (k0 + kStreamChunk < p.K) {
+      if constexpr (FQ) fused_load_x<FR>(p, qa, xr, k0 + kStreamChunk, tid);
+      stream_load<MT, FQ>(p, cur, k0 + kStreamChunk, n0, wave, lane);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t kbase = k0 + wave * 512 + j * 128;
       if (kbase >= p.K) break;
       const int c0 = (wave * 512 + j * 128 + g * 32) / 16;
-      const uint4 lo = wt[r16 * (kStreamChunk / 16) + (c0 ^ r16)];
-      const uint4 hi = wt[r16 * (kStreamChunk / 16) + ((c0 + 1) ^ r16)];
+      const uint4 lo = wt[r16 * CPR + (c0 ^ r16)];
+      const uint4 hi = wt[r16 * CPR + ((c0 + 1) ^ r16)];
       const i32x8 bf = join(lo, hi);
+      // activation codes of this K block and (blockwise) their group scales
+      i32x8 af[MT];
+      float sa_blk[MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int64_t m = t * 16 + r16;
+        if constexpr (FQ) {
+          af[t] = join(codes[r16 * CPR + (c0 ^ r16)], codes[r16 * CPR + ((c0 + 1) ^ r16)]);
+          if (KIND == kBlockwise) sa_blk[t] = blk_scale[r16 * (kStreamChunk / 128) + wave * 4 + j];
+        } else {
+          af[t] = join(use.a[t][j][0], use.a[t][j][1]);
+          if (KIND == kBlockwise) sa_blk[t] = (m < p.M) ? p.sa[(kbase / 128) * p.sa_ld + m] : 0.0f;
+        }
+      }
       if (KIND == kChannelwise) {
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[t] = mfma_fp8(bf, join(use.a[t][j][0], use.a[t][j][1]), acc[t]);
+        for (int t = 0; t < MT; ++t) acc[t] = mfma_fp8(bf, af[t], acc[t]);
       } else {
-        const int64_t kb = kbase / 128;
-        const float sb = p.sb[(n0 / 128) * kb_all + kb];
+        const float sb = p.sb[(n0 / 128) * kb_all + kbase / 128];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          const int64_t m = t * 16 + r16;
-          const float sa = (m < p.M) ? p.sa[kb * p.sa_ld + m] : 0.0f;
-          const f32x4 part =
-              mfma_fp8(bf, join(use.a[t][j][0], use.a[t][j][1]), f32x4{0.f, 0.f, 0.f, 0.f});
-          acc[t] += part * (sa * sb);
+          const f32x4 part = mfma_fp8(bf, af[t], f32x4{0.f, 0.f, 0.f, 0.f});
+          acc[t] += part * (sa_blk[t] * sb);
         }
       }
     }
@@ -1135,7 +1262,8 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs
 #pragma unroll
   for (int w = 1; w < kStreamWaves; ++w) sum += red[(w * MT + t) * 64 + lane];
   const int64_t m = t * 16 + r16;
-  const float sa_m = (KIND == kChannelwise && m < p.M) ? p.sa[m] : 1.0f;
+  float sa_m = 1.0f;
+  if (KIND == kChannelwise && m < p.M) sa_m = FQ ? row_scale[r16] : p.sa[m];
   store_out4<KIND>(p, m, n0 + 4 * g, sum, sa_m);
 }
 
@@ -1223,10 +1351,11 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
   switch (variant) {
     case 0: {  // FP8_VARIANT_SKINNY
       const dim3 grid((unsigned)((p.N + 15) / 16)), block(kStreamWaves * 64);
+      const QuantArgs none{};
       if (p.M <= 16)
-        hipLaunchKernelGGL((gemm_skinny_kernel<1, KIND>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((gemm_skinny_kernel<1, KIND, 0>), grid, block, 0, stream, p, none);
       else
-        hipLaunchKernelGGL((gemm_skinny_kernel<2, KIND>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((gemm_skinny_kernel<2, KIND, 0>), grid, block, 0, stream, p, none);
       return hipGetLastError();
     }
     case 1: return launch_tile<64, 64, 2, 2, 512, KIND>(p, stream);
@@ -1335,6 +1464,29 @@ size_t variant_workspace_bytes(int variant, int split_k, int64_t M, int64_t N) {
   const VariantInfo v = variant_info(variant);
   const int64_t tiles = variant_tiles(variant, M, N);
   return kCounterBytes + (size_t)tiles * split_k * v.bm * v.bn * sizeof(float);
+}
+
+namespace {
+template <int KIND, int FR>
+hipError_t launch_fused_rows(const GemmArgs& p, const QuantArgs& qa, hipStream_t stream) {
+  const dim3 grid((unsigned)((p.N + 15) / 16)), block(kStreamWaves * 64);
+  hipLaunchKernelGGL((gemm_skinny_kernel<1, KIND, FR>), grid, block, 0, stream, p, qa);
+  return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_fused_kind(const GemmArgs& p, const QuantArgs& qa, hipStream_t stream) {
+  if (p.M <= 1) return launch_fused_rows<KIND, 1>(p, qa, stream);
+  if (p.M <= 2) return launch_fused_rows<KIND, 2>(p, qa, stream);
+  if (p.M <= 4) return launch_fused_rows<KIND, 4>(p, qa, stream);
+  static_assert(kFusedRows == 4, "fused row buckets");
+  return hipErrorInvalidValue;
+}
+}  // namespace
+
+hipError_t launch_linear_fused(int kind, const GemmArgs& p, const QuantArgs& qa, hipStream_t stream) {
+  return kind == kChannelwise ? launch_fused_kind<kChannelwise>(p, qa, stream)
+                              : launch_fused_kind<kBlockwise>(p, qa, stream);
 }
 
 hipError_t launch_gemm(int kind, int variant, const GemmArgs& p, hipStream_t stream) {

@@ -31,6 +31,28 @@ struct GemmArgs {
   int k_tiles_per_split;  // 128-deep K steps handled by one split
 };
 
+// Activation quantization fused into the skinny GEMM (M <= kFusedRows): the
+// kernel reads bf16 x instead of codes and scales, quantizes it as the
+// quantization kernels do, and workgroup 0 also stores the codes (rows < M of
+// q) and the scales (per token: scale[m]; per group of 128: scale[kb *
+// scale_ld + m]). Every workgroup quantizes the whole activation, so the
+// fused launch beats the two launches only while M is small: measured on the
+// N = K = 4096 linear, ahead by 2-4.5 us at M <= 4, even at M = 8, behind at
+// M = 16.
+struct QuantArgs {
+  const uint16_t* x;
+  int64_t ldx;
+  uint8_t* q;
+  int64_t ldq;
+  float* scale;
+  int64_t scale_ld;
+  float eps;
+};
+constexpr int64_t kFusedRows = 4;
+
+hipError_t launch_linear_fused(int kind, const GemmArgs& args, const QuantArgs& qa,
+                               hipStream_t stream);
+
 // Geometry of a compiled kernel variant.
 struct VariantInfo {
   int bm, bn, bk, waves;

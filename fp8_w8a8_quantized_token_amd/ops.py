@@ -26,7 +26,7 @@ from ._lib import KIND_BLOCKWISE, KIND_CHANNELWISE, TileConfig, VARIANTS, check
 __all__ = [
     "prepare", "padded_rows", "quant_per_token", "quant_per_token_group", "scaled_mm_channelwise",
     "scaled_mm_blockwise", "linear_channelwise", "linear_blockwise", "tile_config",
-    "default_tile_config", "set_config_dir", "workspace_bytes", "make_config",
+    "default_tile_config", "set_config_dir", "workspace_bytes", "make_config", "linear_launches",
 ]
 
 
@@ -199,27 +199,82 @@ def scaled_mm_blockwise(a, b, a_scale, b_scale, bias=None, m=None, out=None, con
 
 
 # ---------------------------------------------------------------- linears
-def linear_channelwise(x, w_q, w_s, bias=None, eps=1e-10, config=None):
+def _linear_args(kind, x, w_q, w_s, bias, eps, row_alignment, config, out, q, scale):
+    """Validated ctypes argument tuple of fp8_linear_{channelwise,blockwise}
+    for 2-D x, plus the tensors it points to."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise TypeError("x must be a 2-D bf16 tensor with contiguous rows")
+    w_q = _as_codes(w_q, "w_q")
+    _need_cuda(x, w_q, w_s, bias)
+    m, k = x.shape
+    n = w_q.shape[0]
+    if w_q.shape[1] != k:
+        raise ValueError("x and w_q disagree on K")
+    if w_s.dtype != torch.float32 or not w_s.is_contiguous():
+        raise ValueError("w_s must be a contiguous fp32 tensor")
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() < n or
+                             not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous bf16 [N] tensor")
+    dev = x.device
+    if kind == KIND_CHANNELWISE:
+        m_pad = m
+        q = q if q is not None else torch.empty((m, k), dtype=torch.uint8, device=dev)
+        scale = scale if scale is not None else torch.empty((m,), dtype=torch.float32, device=dev)
+    else:
+        m_pad = padded_rows(m, row_alignment)
+        q = q if q is not None else torch.empty((m_pad, k), dtype=torch.uint8, device=dev)
+        scale = scale if scale is not None else torch.empty((k // 128, m_pad), dtype=torch.float32,
+                                                            device=dev)
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    cfg = config if config is not None else TileConfig(-1, 0, 0, 0, 1, 0)
+    nws = workspace_bytes(kind, m, n, k, cfg)
+    ws = _ws.get(dev, nws)
+    head = (_p(x), _p(w_q), _p(w_s), _p(bias), _p(out), m, n, k, x.stride(0), w_q.stride(0),
+            out.stride(0))
+    mid = (ctypes.c_float(eps),) if kind == KIND_CHANNELWISE else (row_alignment, ctypes.c_float(eps))
+    args = head + mid + (_p(q), q.stride(0), _p(scale), _p(ws), nws, ctypes.byref(cfg), _stream(x))
+    return args, (out, q, scale, cfg, ws)
+
+
+def linear_channelwise(x, w_q, w_s, bias=None, eps=1e-10, config=None, return_quant=False):
     """y = x @ W^T with per-token FP8 activation quant and per-channel weight
-    scales. x bf16 [..., K]; w_q codes [N, K]; w_s fp32 [N]; bias bf16 [N]."""
+    scales. x bf16 [..., K]; w_q codes [N, K]; w_s fp32 [N]; bias bf16 [N].
+    One kernel launch for M <= 4 (quant fused into the skinny GEMM), two
+    otherwise. return_quant=True also returns the codes [M, K] and scales [M]."""
     shape = x.shape
     x2 = x.reshape(-1, shape[-1])
-    q, s = quant_per_token(x2, eps)
-    out = scaled_mm_channelwise(q, w_q, s, w_s, bias, config=config)
-    return out.view(*shape[:-1], w_q.shape[0])
+    args, (out, q, s, _, _) = _linear_args(KIND_CHANNELWISE, x2, w_q, w_s, bias, eps, 1, config,
+                                          None, None, None)
+    check(_lib.load().fp8_linear_channelwise(*args))
+    out = out.view(*shape[:-1], out.shape[1])
+    return (out, q, s) if return_quant else out
 
 
 def linear_blockwise(x, w_q, w_s, bias=None, block_size=(128, 128), eps=1e-10,
-                     row_alignment=4, config=None):
+                     row_alignment=4, config=None, return_quant=False):
     """Blockwise FP8 linear: group-128 activation quant into row-padded buffers,
-    then the blockwise GEMM over the first M rows with the bias fused."""
+    then the blockwise GEMM over the first M rows with the bias fused. One
+    launch for M <= 4, two otherwise. return_quant=True also returns the codes
+    [M_pad, K] and the scales as an [M_pad, K/128] view of [K/128, M_pad]."""
     if tuple(block_size) != (128, 128):
         raise _lib.Fp8Error(_lib.FP8_ERR_UNSUPPORTED, "only 128x128 weight blocks are supported")
     shape = x.shape
     x2 = x.reshape(-1, shape[-1])
-    q, s = quant_per_token_group(x2, block_size[1], eps, row_alignment)
-    out = scaled_mm_blockwise(q, w_q, s, w_s, bias, m=x2.shape[0], config=config)
-    return out.view(*shape[:-1], w_q.shape[0])
+    args, (out, q, st, _, _) = _linear_args(KIND_BLOCKWISE, x2, w_q, w_s, bias, eps, row_alignment,
+                                           config, None, None, None)
+    check(_lib.load().fp8_linear_blockwise(*args))
+    out = out.view(*shape[:-1], out.shape[1])
+    return (out, q, st.transpose(0, 1)) if return_quant else out
+
+
+def linear_launches(kind, m, n, k, config=None):
+    """Kernel launches one linear call makes: 1 (fused), 2, or 0 for M == 0."""
+    cfg = ctypes.byref(config) if config is not None else None
+    r = _lib.load().fp8_linear_launches(kind, m, n, k, cfg)
+    if r < 0:
+        check(r)
+    return r
 
 
 # ---------------------------------------------------------------- tile table
@@ -262,9 +317,16 @@ def prepare(op, *args, **kwargs):
     x, group_size, row_alignment=4, out=q, scale_storage=st),
     prepare("scaled_mm_channelwise", a, b, a_scale, b_scale, bias=None, out=out, config=None),
     prepare("scaled_mm_blockwise", a, b, a_scale, b_scale, bias=None, m=None, out=out,
-    config=None): validate once (by running the op once) and return a Prepared."""
+    config=None), prepare("linear_channelwise", x, w_q, w_s, bias=None, out=out, q=q,
+    scale=s, config=None), prepare("linear_blockwise", x, w_q, w_s, bias=None,
+    row_alignment=4, out=out, q=q, scale=st, config=None) (st: [K/128, M_pad]
+    storage): validate once (by running the op once) and return a Prepared."""
     lib = _lib.load()
-    globals()[op](*args, **kwargs)  # validates and raises on bad arguments
+    if op in ("linear_channelwise", "linear_blockwise"):
+        kw = {k_: v for k_, v in kwargs.items() if k_ not in ("out", "q", "scale")}
+        globals()[op](*args, **kw)  # validates and raises on bad arguments
+    else:
+        globals()[op](*args, **kwargs)
     if op == "quant_per_token":
         x = args[0]
         q, s = kwargs["out"], kwargs["scale"]
@@ -277,6 +339,17 @@ def prepare(op, *args, **kwargs):
         a = (_p(x), x.shape[0], x.shape[1], x.stride(0), g, kwargs.get("row_alignment", 4), _p(q),
              q.stride(0), _p(st), ctypes.c_float(kwargs.get("eps", 1e-10)), _stream(x))
         return Prepared(lib.fp8_quant_per_token_group, a, op)
+    if op in ("linear_channelwise", "linear_blockwise"):
+        kind = KIND_CHANNELWISE if op == "linear_channelwise" else KIND_BLOCKWISE
+        x, w_q, w_s = args[0], args[1], args[2]
+        cfg = kwargs.get("config") or TileConfig(-1, 0, 0, 0, 1, 0)
+        a, keep = _linear_args(kind, x, w_q, w_s, kwargs.get("bias"), kwargs.get("eps", 1e-10),
+                               kwargs.get("row_alignment", 4), cfg, kwargs["out"], kwargs["q"],
+                               kwargs["scale"])
+        pr = Prepared(lib.fp8_linear_channelwise if op == "linear_channelwise"
+                      else lib.fp8_linear_blockwise, a, op)
+        pr._keep = keep
+        return pr
     if op in ("scaled_mm_channelwise", "scaled_mm_blockwise"):
         a_, b_, sa, sb = _as_codes(args[0], "a"), _as_codes(args[1], "b"), args[2], args[3]
         bias, out = kwargs.get("bias"), kwargs["out"]

@@ -241,6 +241,64 @@ size_t fp8_scaled_mm_workspace_size(int32_t kind, int64_t M, int64_t N, int64_t 
                                     const fp8_tile_config* cfg);
 
 /* ------------------------------------------------------------------------ */
+/* Linears: activation quantization and scaled GEMM in one call              */
+/* ------------------------------------------------------------------------ */
+
+/* Channelwise FP8 linear. [PR34331, "Key source excerpts", apply_fp8_linear:
+ * the input is quantized per token with a dynamic scale, and the codes and
+ * that scale go to the scaled matmul with the per-channel weight scale and
+ * the bias.] On success q rows < M and a_scale[0..M) hold exactly what
+ * fp8_quant_per_token writes for x, and out exactly what
+ * fp8_scaled_mm_channelwise computes from them (the same bits).
+ * For M <= 4 with the skinny kernel selected (the default at small M) both
+ * happen in ONE launch: every workgroup quantizes the activation rows it
+ * multiplies (x is read from cache by each of them) and workgroup 0 also
+ * stores q and a_scale. Otherwise the quantizer and the GEMM run as two
+ * launches on `stream`. FP8W8A8_FUSED_LINEAR=0 in the environment turns the
+ * single launch off.
+ *   x        bf16 [M][ldx], ldx >= K (input)
+ *   q        E4M3 [M][ldq], ldq >= K (output codes; the GEMM's input)
+ *   a_scale  fp32 [M] (output per-token scales)
+ *   b, b_scale, bias, out, ws, ws_bytes  as for fp8_scaled_mm_channelwise
+ *   cfg      tile config or NULL (table lookup / default heuristic)
+ * Errors as for the quantizer and the GEMM; nothing is launched on error. */
+int fp8_linear_channelwise(const uint16_t* x, const uint8_t* b, const float* b_scale,
+                           const uint16_t* bias, uint16_t* out,
+                           int64_t M, int64_t N, int64_t K,
+                           int64_t ldx, int64_t ldb, int64_t ldc, float eps,
+                           uint8_t* q, int64_t ldq, float* a_scale,
+                           void* ws, size_t ws_bytes,
+                           const fp8_tile_config* cfg, hipStream_t stream);
+
+/* Blockwise FP8 linear. [PR27896, "Key source excerpts", the blockwise
+ * linear: group-128 activation quant into row-padded buffers, then the
+ * blockwise scaled matmul with 128x128 weight blocks over the first M rows,
+ * bias added.] On success q rows < M and the scale entries of rows < M hold
+ * exactly what fp8_quant_per_token_group(x, group 128, row_alignment) writes,
+ * and out exactly what fp8_scaled_mm_blockwise computes from them; pad rows
+ * M..M_pad-1 are not written. One launch for M <= 4 with the skinny kernel
+ * selected, as above; two otherwise.
+ *   x        bf16 [M][ldx], ldx >= K
+ *   q        E4M3 [M_pad][ldq], M_pad = fp8_padded_rows(M, row_alignment)
+ *   a_scale  fp32 [K/128][M_pad] (column-major scales, (m, kb) at kb*M_pad + m)
+ *   b, b_scale, bias, out, ws, ws_bytes  as for fp8_scaled_mm_blockwise
+ * N and K must be multiples of 128 (else FP8_ERR_UNSUPPORTED). */
+int fp8_linear_blockwise(const uint16_t* x, const uint8_t* b, const float* b_scale,
+                         const uint16_t* bias, uint16_t* out,
+                         int64_t M, int64_t N, int64_t K,
+                         int64_t ldx, int64_t ldb, int64_t ldc,
+                         int32_t row_alignment, float eps,
+                         uint8_t* q, int64_t ldq, float* a_scale,
+                         void* ws, size_t ws_bytes,
+                         const fp8_tile_config* cfg, hipStream_t stream);
+
+/* Kernel launches an fp8_linear_* call of `kind` makes for (M, N, K, cfg):
+ * 1 (fused), 2 (quantizer, then GEMM) or 0 (M == 0); FP8_ERR_INVALID on bad
+ * arguments. Host only. */
+int fp8_linear_launches(int32_t kind, int64_t M, int64_t N, int64_t K,
+                        const fp8_tile_config* cfg);
+
+/* ------------------------------------------------------------------------ */
 /* Tile-config table                                                         */
 /* ------------------------------------------------------------------------ */
 

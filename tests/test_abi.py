@@ -92,6 +92,36 @@ def test_gemm_argument_errors(lib):
     assert "a_scale_ld" in _err(lib)
 
 
+def test_linear_argument_errors(lib):
+    cw = lib.fp8_linear_channelwise
+    # x, b, b_scale, bias, out, M, N, K, ldx, ldb, ldc, eps, q, ldq, a_scale, ws, ws_bytes, cfg, stream
+    ok = (FAKE, FAKE, FAKE, None, FAKE, 4, 256, 512, 512, 512, 256, 1e-10, FAKE, 512, FAKE, None, 0, None, None)
+    assert cw(*((None,) + ok[1:])) == _lib.FP8_ERR_INVALID                      # null x
+    assert cw(*(ok[:12] + (None,) + ok[13:])) == _lib.FP8_ERR_INVALID           # null q
+    assert cw(*(ok[:7] + (500, 500, 512) + ok[10:])) == _lib.FP8_ERR_INVALID    # K % 16
+    assert cw(*(ok[:13] + (256,) + ok[14:])) == _lib.FP8_ERR_INVALID            # ldq < K
+    assert cw(*(ok[:11] + (-1.0,) + ok[12:])) == _lib.FP8_ERR_INVALID           # eps < 0
+    assert cw(*((None,) * 5 + (0,) + ok[6:12] + (None, 512, None, None, 0, None, None))) == _lib.FP8_OK
+    bw = lib.fp8_linear_blockwise
+    # ..., ldc, row_alignment, eps, q, ...
+    okb = (FAKE, FAKE, FAKE, None, FAKE, 4, 256, 512, 512, 512, 256, 4, 1e-10, FAKE, 512, FAKE, None, 0, None,
+           None)
+    assert bw(*(okb[:6] + (200,) + okb[7:10] + (200,) + okb[11:])) == _lib.FP8_ERR_UNSUPPORTED  # N % 128
+    assert bw(*(okb[:7] + (528, 528, 528) + okb[10:14] + (528,) + okb[15:])) == _lib.FP8_ERR_UNSUPPORTED  # K % 128
+    assert bw(*(okb[:11] + (0,) + okb[12:])) == _lib.FP8_ERR_INVALID                             # row_alignment
+
+
+def test_linear_launch_counts(lib):
+    n = lib.fp8_linear_launches
+    for kind in (_lib.KIND_CHANNELWISE, _lib.KIND_BLOCKWISE):
+        assert n(kind, 0, 4096, 4096, None) == 0
+        assert [n(kind, m, 4096, 4096, None) for m in (1, 2, 3, 4)] == [1, 1, 1, 1]
+        assert [n(kind, m, 4096, 4096, None) for m in (5, 16, 32, 8192)] == [2, 2, 2, 2]
+        cfg = _lib.TileConfig(_lib.VARIANTS["t64x64panel"], 0, 0, 0, 1, 0)
+        assert n(kind, 4, 4096, 4096, ctypes.byref(cfg)) == 2
+    assert n(7, 1, 4096, 4096, None) == _lib.FP8_ERR_INVALID
+
+
 def test_workspace_errors(lib):
     cfg = _lib.TileConfig(_lib.VARIANTS["t64x64"], 0, 0, 0, 4, 0)
     # t64x64 runs 512-deep K stages: K = 2048 holds 4 stages, so 4 splits

@@ -1,0 +1,139 @@
+"""GPU parity of the linears: activation quantization and scaled GEMM in one
+call (fp8_linear_channelwise / fp8_linear_blockwise through the C ABI).
+
+For M <= 4 with the skinny kernel selected the call is a single launch that
+quantizes the activation inside the GEMM. Each case checks, on the same
+seeded bf16 input:
+* the codes and scales the call leaves in q / a_scale are bit-exact against
+  the oracle's quantizer (rows < M; pad rows keep their poison);
+* the output is within the GEMM tolerance of the fp64 oracle applied to the
+  oracle's codes and scales;
+* the output is bit-identical to the two-launch path (the quantizer, then the
+  GEMM with the same tile config) -- the fused launch changes where the codes
+  come from, not the arithmetic.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_w8a8_quantized_token_amd import ops, synth
+from gpu_common import (activations, bf16_to_f64, device, gpu, say, weight_blockwise,
+                        weight_channelwise)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(out, ref, tau, label):
+    res = oracle.check_gemm(bf16_to_f64(out), ref, tau)
+    say(label, {k: (round(v, 8) if isinstance(v, float) else v) for k, v in res.items()})
+    assert res["ok"], (label, res)
+    assert res["cosine"] > 0.9999
+
+
+def _same_bits(a, b):
+    return torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+CW_CASES = ([("o_proj", m, 4096, 4096, 0.01, False) for m in (1, 2, 3, 4, 5, 16, 64)]
+            + [("qwen3_8b", m, 4096, 12288, 0.0, True) for m in (1, 4)]
+            + [("qwen3_8b", 3, 24576, 4096, 0.0, True)]
+            + [("ragged", m, 392, 1040, 0.0, True) for m in (3, 16)]
+            + [("small", m, 256, 512, 0.0, False) for m in (2, 16)])
+
+
+@pytest.mark.parametrize("wl,m,n,k,outl,with_bias", CW_CASES,
+                         ids=[f"{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in CW_CASES])
+def test_linear_channelwise(wl, m, n, k, outl, with_bias):
+    x = activations(wl, m, k, outl)
+    b, sb = weight_channelwise(wl, n, k)
+    bias = synth.bias(wl, n) if with_bias else None
+    bias_d = gpu(bias) if bias is not None else None
+    launches = ops.linear_launches(ops.KIND_CHANNELWISE, m, n, k)
+    assert launches == (1 if m <= 4 else 2)
+    say("linear_channelwise", wl, m, n, k, f"launches={launches}")
+    out, q, s = ops.linear_channelwise(gpu(x), gpu(b), gpu(sb), bias_d, return_quant=True)
+    torch.cuda.synchronize()
+    want_q, want_s = oracle.quant_per_token(x.float().numpy())
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), want_q)
+    bias64 = bias.float().numpy() if bias is not None else None
+    ref = oracle.scaled_mm_channelwise(want_q, b, want_s, sb, bias64)
+    tau = oracle.summation_bound_channelwise(want_q, b, want_s, sb)
+    _check(out, ref, tau, f"linear cw {wl} M={m} N={n} K={k}")
+    # the two-launch path with the config the linear resolved
+    cfg = ops.make_config("skinny") if launches == 1 else None
+    q2, s2 = ops.quant_per_token(gpu(x))
+    out2 = ops.scaled_mm_channelwise(q2, gpu(b), s2, gpu(sb), bias_d, config=cfg)
+    torch.cuda.synchronize()
+    assert _same_bits(out, out2)
+
+
+BW_CASES = ([("block_7168", m, 7168, 7168) for m in (1, 2, 3, 7, 13)]
+            + [("block_moe", m, 3072, 4096) for m in (1, 4, 16, 64)]
+            + [("block_moe", m, 4096, 1536) for m in (1, 3, 16)])
+
+
+@pytest.mark.parametrize("wl,m,n,k", BW_CASES, ids=[f"{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in BW_CASES])
+def test_linear_blockwise(wl, m, n, k):
+    x = activations(wl, m, k)
+    b, sb = weight_blockwise(wl, n, k)
+    bias = synth.bias(wl, n)
+    launches = ops.linear_launches(ops.KIND_BLOCKWISE, m, n, k)
+    assert launches == (1 if m <= 4 else 2)
+    m_pad = ops.padded_rows(m, 4)
+    q_buf = torch.full((m_pad, k), 0x7F, dtype=torch.uint8, device=device())
+    s_buf = torch.full((k // 128, m_pad), float("nan"), dtype=torch.float32, device=device())
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=device())
+    x_d, b_d, sb_d, bias_d = gpu(x), gpu(b), gpu(sb), gpu(bias)
+    say("linear_blockwise", wl, m, n, k, f"launches={launches}")
+    run = ops.prepare("linear_blockwise", x_d, b_d, sb_d, bias=bias_d, row_alignment=4, out=out,
+                      q=q_buf, scale=s_buf)
+    run()
+    torch.cuda.synchronize()
+    want_q, want_s = oracle.quant_per_token_group(x.float().numpy(), 128)
+    got_q = q_buf.cpu().numpy()
+    assert np.array_equal(got_q[:m], want_q)
+    assert (got_q[m:] == 0x7F).all(), "pad rows of q were written"
+    flat_want = oracle.scales_col_major(want_s, m_pad)
+    got_s = s_buf.cpu().numpy().ravel()
+    live = ~np.isnan(flat_want)
+    assert np.array_equal(got_s[live].view(np.uint32), flat_want[live].view(np.uint32))
+    assert np.isnan(got_s[~live]).all(), "pad-row scales were written"
+    ref = oracle.scaled_mm_blockwise(want_q, b, want_s, sb, bias.float().numpy())
+    tau = oracle.summation_bound_blockwise(want_q, b, want_s, sb)
+    _check(out, ref, tau, f"linear bw {wl} M={m} N={n} K={k}")
+    cfg = ops.make_config("skinny") if launches == 1 else None
+    q2, s2 = ops.quant_per_token_group(x_d, 128, row_alignment=4)
+    out2 = ops.scaled_mm_blockwise(q2, b_d, s2, sb_d, bias_d, m=m, config=cfg)
+    torch.cuda.synchronize()
+    assert _same_bits(out, out2)
+
+
+def test_linear_explicit_config_takes_two_launches():
+    """A non-skinny config at M <= 4 runs the quantizer and that GEMM."""
+    m, n, k = 4, 512, 1024
+    cfg = ops.make_config("t64x64panel", 2)
+    assert ops.linear_launches(ops.KIND_CHANNELWISE, m, n, k, cfg) == 2
+    x = activations("cfg2", m, k)
+    b, sb = weight_channelwise("cfg2", n, k)
+    say("linear_channelwise explicit config", m, n, k)
+    out, q, s = ops.linear_channelwise(gpu(x), gpu(b), gpu(sb), config=cfg, return_quant=True)
+    torch.cuda.synchronize()
+    want_q, want_s = oracle.quant_per_token(x.float().numpy())
+    assert np.array_equal(q.cpu().numpy(), want_q)
+    ref = oracle.scaled_mm_channelwise(want_q, b, want_s, sb)
+    _check(out, ref, oracle.summation_bound_channelwise(want_q, b, want_s, sb), "linear cw cfg")
+
+
+def test_linear_zero_rows_and_3d_input():
+    n, k = 256, 512
+    b, sb = weight_channelwise("small", n, k)
+    x0 = torch.empty((0, k), dtype=torch.bfloat16, device=device())
+    assert ops.linear_channelwise(x0, gpu(b), gpu(sb)).shape == (0, n)
+    x = activations("small", 6, k)
+    say("linear_channelwise 3-D", 6, n, k)
+    y = ops.linear_channelwise(gpu(x).view(2, 3, k), gpu(b), gpu(sb))
+    y2 = ops.linear_channelwise(gpu(x), gpu(b), gpu(sb))
+    torch.cuda.synchronize()
+    assert y.shape == (2, 3, n) and _same_bits(y.reshape(6, n), y2)
