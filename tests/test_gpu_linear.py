@@ -137,3 +137,50 @@ def test_linear_zero_rows_and_3d_input():
     y2 = ops.linear_channelwise(gpu(x), gpu(b), gpu(sb))
     torch.cuda.synchronize()
     assert y.shape == (2, 3, n) and _same_bits(y.reshape(6, n), y2)
+
+
+EDGE_CW = [(1, 256, 4112), (3, 384, 8224), (4, 256, 1040), (2, 136, 4096)]
+
+
+@pytest.mark.parametrize("m,n,k", EDGE_CW, ids=[f"M{c[0]}-N{c[1]}-K{c[2]}" for c in EDGE_CW])
+def test_linear_channelwise_ragged_k_and_strides(m, n, k):
+    """Fused path with K past a 4 KB chunk by one 16-element piece, three
+    chunks with a ragged tail, N not a multiple of 16, and x and q rows with
+    leading dimensions above K."""
+    x = activations("edge-lin", m, k, 0.01)
+    b, sb = weight_channelwise("edge-lin", n, k)
+    x_wide = torch.zeros((m, k + 64), dtype=torch.bfloat16, device=device())
+    x_wide[:, :k] = gpu(x)
+    xs = x_wide[:, :k]
+    q_buf = torch.full((m, k + 32), 0x7F, dtype=torch.uint8, device=device())
+    s_buf = torch.full((m,), float("nan"), dtype=torch.float32, device=device())
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=device())
+    say("linear_channelwise edge", m, n, k)
+    ops.prepare("linear_channelwise", xs, gpu(b), gpu(sb), out=out, q=q_buf[:, :k], scale=s_buf)()
+    torch.cuda.synchronize()
+    want_q, want_s = oracle.quant_per_token(x.float().numpy())
+    got_q = q_buf.cpu().numpy()
+    assert np.array_equal(got_q[:, :k], want_q)
+    assert (got_q[:, k:] == 0x7F).all(), "q written past K"
+    assert np.array_equal(s_buf.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    ref = oracle.scaled_mm_channelwise(want_q, b, want_s, sb)
+    _check(out, ref, oracle.summation_bound_channelwise(want_q, b, want_s, sb), f"linear cw edge K={k}")
+    q2, s2 = ops.quant_per_token(gpu(x))
+    out2 = ops.scaled_mm_channelwise(q2, gpu(b), s2, gpu(sb), config=ops.make_config("skinny"))
+    torch.cuda.synchronize()
+    assert _same_bits(out, out2)
+
+
+def test_linear_blockwise_three_chunks_row_alignment_8():
+    m, n, k = 3, 256, 8320
+    x = activations("edge-lin-bw", m, k)
+    b, sb = weight_blockwise("edge-lin-bw", n, k)
+    say("linear_blockwise edge", m, n, k)
+    out, q, s = ops.linear_blockwise(gpu(x), gpu(b), gpu(sb), row_alignment=8, return_quant=True)
+    torch.cuda.synchronize()
+    assert q.shape == (8, k) and s.shape == (8, k // 128) and s.stride() == (1, 8)
+    want_q, want_s = oracle.quant_per_token_group(x.float().numpy(), 128)
+    assert np.array_equal(q[:m].cpu().numpy(), want_q)
+    assert np.array_equal(s[:m].cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    ref = oracle.scaled_mm_blockwise(want_q, b, want_s, sb)
+    _check(out, ref, oracle.summation_bound_blockwise(want_q, b, want_s, sb), "linear bw 3 chunks")
