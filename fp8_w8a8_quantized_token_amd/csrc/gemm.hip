@@ -1033,39 +1033,72 @@ constexpr int kStreamWaves = 8;
 constexpr int kStreamChunk = 4096;
 }  // namespace
 
-template <int MT>
+// v where ok, else zero (component-wise: a select on the whole struct goes
+// through scratch memory)
+__device__ __forceinline__ uint4 keep_if(bool ok, const uint4& v) {
+  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
+
+template <int MT, int KIND>
 struct StreamRegs {
   uint4 b[2][4];          // rows 2w, 2w+1; four 1 KB segments
   uint4 a[MT][4][2];      // activation fragments: 4 K blocks x 32 bytes
+  // blockwise: this wave's four K blocks' weight scales and this lane's
+  // activation scales (0 for rows >= M)
+  float sb[KIND == kBlockwise ? 4 : 1];
+  float sa[KIND == kBlockwise ? MT : 1][4];
 };
 
-// Loads of one chunk: the weight rows always; the activation code fragments
-// unless the quantization is fused (FQ), where the codes come from LDS.
-template <int MT, bool FQ>
-__device__ __forceinline__ void stream_load(const GemmArgs& p, StreamRegs<MT>& r, int64_t k0,
+// Loads of one chunk: the weight rows and (blockwise) the scales of the K
+// blocks this wave multiplies, and, unless the quantization is fused (FQ),
+// the activation code fragments. Every load is issued unconditionally from a
+// clamped in-bounds address and the value selected afterwards: with no
+// branches around loads the compiler's waits count exactly the loads still
+// needed, so the next chunk's loads stay in flight across the MFMAs.
+template <int MT, int KIND, bool FQ>
+__device__ __forceinline__ void stream_load(const GemmArgs& p, StreamRegs<MT, KIND>& r, int64_t k0,
                                             int64_t n0, int wave, int lane) {
 #pragma unroll
   for (int rr = 0; rr < 2; ++rr) {
     const int64_t n = n0 + 2 * wave + rr;
-    const uint8_t* row = p.b + (n < p.N ? n : 0) * p.ldb;
+    const uint8_t* row = p.b + (n < p.N ? n : p.N - 1) * p.ldb;
 #pragma unroll
     for (int sgm = 0; sgm < 4; ++sgm) {
       const int64_t off = k0 + sgm * 1024 + lane * 16;
-      r.b[rr][sgm] = (n < p.N && off < p.K) ? load16_nt(row + off) : make_uint4(0, 0, 0, 0);
+      const bool ok = n < p.N && off < p.K;
+      r.b[rr][sgm] = keep_if(ok, load16_nt(row + (ok ? off : 0)));
+    }
+  }
+  const int g = lane >> 4;
+  if constexpr (KIND == kBlockwise) {
+    const int64_t kb_all = p.K / 128;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int64_t kb = (k0 + wave * 512 + j * 128) / 128;
+      kb = kb < kb_all ? kb : kb_all - 1;  // blocks past K are never used
+      r.sb[j] = p.sb[(n0 / 128) * kb_all + kb];
+      if constexpr (!FQ) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const int64_t m = t * 16 + (lane & 15);
+          const float v = p.sa[kb * p.sa_ld + (m < p.M ? m : p.M - 1)];
+          r.sa[t][j] = m < p.M ? v : 0.0f;
+        }
+      }
     }
   }
   if constexpr (FQ) return;
-  const int g = lane >> 4;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int64_t m = t * 16 + (lane & 15);
+    const uint8_t* arow = p.a + (m < p.M ? m : p.M - 1) * p.lda;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t off = k0 + wave * 512 + j * 128 + g * 32;
       const bool ok0 = m < p.M && off < p.K;        // K is a multiple of 16 only
       const bool ok1 = m < p.M && off + 16 < p.K;
-      r.a[t][j][0] = ok0 ? load16(p.a + m * p.lda + off) : make_uint4(0, 0, 0, 0);
-      r.a[t][j][1] = ok1 ? load16(p.a + m * p.lda + off + 16) : make_uint4(0, 0, 0, 0);
+      r.a[t][j][0] = keep_if(ok0, load16(arow + (ok0 ? off : 0)));
+      r.a[t][j][1] = keep_if(ok1, load16(arow + (ok1 ? off + 16 : 0)));
     }
   }
 }
@@ -1080,9 +1113,12 @@ template <int FR>
 __device__ __forceinline__ void fused_load_x(const GemmArgs& p, const QuantArgs& qa, uint4 (&xr)[FR],
                                              int64_t k0, int tid) {
   const int64_t k = k0 + 8 * tid;
+  const bool kin = k < p.K;
 #pragma unroll
-  for (int i = 0; i < FR; ++i)
-    xr[i] = (i < p.M && k < p.K) ? load16(qa.x + i * qa.ldx + k) : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < FR; ++i) {
+    const bool ok = i < p.M && kin;
+    xr[i] = keep_if(ok, load16(qa.x + (i < p.M ? i : p.M - 1) * qa.ldx + (kin ? k : 0)));
+  }
 }
 
 // Max over each aligned group of 16 lanes, with DPP lane moves (no LDS
@@ -1108,11 +1144,12 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs
   constexpr bool FQ = FR > 0;
   static_assert(!FQ || (MT == 1 && FR <= 16), "the fused quantization serves one 16-row tile");
   constexpr int CPR = kStreamChunk / 16;  // 16-byte LDS chunks per chunk row
+  constexpr int BPC = kStreamChunk / 128; // K blocks per chunk
   __shared__ uint4 wt[16 * CPR];          // 64 KB: one weight chunk
   // FQ: the activation codes of the chunk in the weight chunk's layout, their
   // group scales (blockwise) and the row scales (per token)
   __shared__ uint4 codes[FQ ? 16 * CPR : 1];
-  __shared__ float blk_scale[FQ ? 16 * (kStreamChunk / 128) : 1];
+  __shared__ float blk_scale[FQ ? 16 * BPC : 1];
   __shared__ float row_scale[FQ ? 16 : 1], row_inv[FQ ? 16 : 1];
   __shared__ float row_part[FQ ? kStreamWaves * 16 : 1];
   const int tid = threadIdx.x;
@@ -1121,7 +1158,6 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs
   const int g = lane >> 4;
   const int r16 = lane & 15;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t kb_all = p.K / 128;
   // with FQ, workgroup 0 also stores the codes and scales it computes
   const bool writer = FQ && blockIdx.x == 0;
 
@@ -1131,15 +1167,46 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs
 
   uint4 xr[FQ ? FR : 1];
   if constexpr (FQ) fused_load_x<FR>(p, qa, xr, 0, tid);
-  StreamRegs<MT> cur;
-  stream_load<MT, FQ>(p, cur, 0, n0, wave, lane);
+  StreamRegs<MT, KIND> cur;
+  stream_load<MT, KIND, FQ>(p, cur, 0, n0, wave, lane);
+
+  // FQ: quantize the chunk whose activation is in xr into `codes` (16-byte
+  // chunk c of row i at position c ^ i, as the weights; unit tid is bytes
+  // 8 tid .. +7 of the row) and, blockwise, its group scales into blk_scale.
+  // Rows M..FR-1 quantize zeros; K past the end gives zero codes, as in the
+  // unfused path.
+  auto quantize_chunk = [&](int64_t k0) {
+    if constexpr (FQ) {
+      const int64_t k = k0 + 8 * tid;
+      const int pos = ((tid >> 1) << 4) + ((tid & 1) << 3);
+      const bool kin = k < p.K;
+#pragma unroll
+      for (int i = 0; i < FR; ++i) {
+        float sc, y;
+        if constexpr (KIND == kChannelwise) {
+          sc = row_scale[i];
+          y = row_inv[i];
+        } else {  // group of 128 = 16 consecutive threads
+          sc = fmaxf(max16_dpp(absmax8_bf16(xr[i])), qa.eps) / kE4M3Max;
+          y = 1.0f / sc;
+        }
+        const uint2 c = kin ? quant8_bf16(xr[i], sc, y) : make_uint2(0, 0);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(codes) + i * (CPR * 16) +
+                                  (pos ^ (i << 4))) = c;
+        if (KIND == kBlockwise && (tid & 15) == 0) blk_scale[i * BPC + (tid >> 4)] = sc;
+        if (writer && kin && i < p.M) {
+          *reinterpret_cast<uint2*>(qa.q + i * qa.ldq + k) = c;
+          if (KIND == kBlockwise && (tid & 15) == 0) qa.scale[(k / 128) * qa.scale_ld + i] = sc;
+        }
+      }
+    }
+  };
 
   if constexpr (FQ) {
-    // code rows FR..15 stay zero (rows M..FR-1 get the codes of zeros); none
-    // of their outputs is stored
+    // code rows FR..15 and their scales stay zero; no output of theirs is stored
     for (int idx = tid + FR * CPR; idx < 16 * CPR; idx += kStreamWaves * 64)
       codes[idx] = make_uint4(0, 0, 0, 0);
-    for (int idx = tid; idx < 16 * (kStreamChunk / 128); idx += kStreamWaves * 64) blk_scale[idx] = 0.0f;
+    for (int idx = tid + FR * BPC; idx < 16 * BPC; idx += kStreamWaves * 64) blk_scale[idx] = 0.0f;
     if constexpr (KIND == kChannelwise) {
       // per-token scales: absmax over the whole row (chunks after the first
       // are read here once more), reduced over the workgroup through LDS
@@ -1166,39 +1233,13 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs
         row_inv[tid] = 1.0f / sc;
         if (writer && tid < p.M) qa.scale[tid] = sc;
       }
+      __syncthreads();
     }
+    quantize_chunk(0);
   }
 
   for (int64_t k0 = 0; k0 < p.K; k0 += kStreamChunk) {
-    __syncthreads();  // the previous chunk's fragment reads are done
-    if constexpr (FQ) {
-      // quantize this chunk's activation into `codes` (16-byte chunk c of row
-      // i at position c ^ i, as the weights); unit tid is bytes 8 tid .. +7
-      const int64_t k = k0 + 8 * tid;
-      const int pos = ((tid >> 1) << 4) + ((tid & 1) << 3);
-      const bool kin = k < p.K;
-#pragma unroll
-      for (int i = 0; i < FR; ++i) {
-        float sc, y;
-        if constexpr (KIND == kChannelwise) {
-          sc = row_scale[i];
-          y = row_inv[i];
-        } else {  // group of 128 = 16 consecutive threads
-          sc = fmaxf(max16_dpp(absmax8_bf16(xr[i])), qa.eps) / kE4M3Max;
-          y = 1.0f / sc;
-        }
-        // rows >= M quantize zeros; K past the end gives zero codes, as in
-        // the unfused path
-        const uint2 c = kin ? quant8_bf16(xr[i], sc, y) : make_uint2(0, 0);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(codes) + i * (CPR * 16) +
-                                  (pos ^ (i << 4))) = c;
-        if (KIND == kBlockwise && (tid & 15) == 0) blk_scale[i * (kStreamChunk / 128) + (tid >> 4)] = sc;
-        if (writer && kin && i < p.M) {
-          *reinterpret_cast<uint2*>(qa.q + i * qa.ldq + k) = c;
-          if (KIND == kBlockwise && (tid & 15) == 0) qa.scale[(k / 128) * qa.scale_ld + i] = sc;
-        }
-      }
-    }
+    __syncthreads();  // the previous chunk's fragment reads are done; (FQ) codes are in
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int r = 2 * wave + rr;
@@ -1209,10 +1250,11 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs
       }
     }
     __syncthreads();
-    StreamRegs<MT> use = cur;
-    if (k0 + kStreamChunk < p.K) {
+    StreamRegs<MT, KIND> use = cur;
+    const bool more = k0 + kStreamChunk < p.K;
+    if (more) {
       if constexpr (FQ) fused_load_x<FR>(p, qa, xr, k0 + kStreamChunk, tid);
-      stream_load<MT, FQ>(p, cur, k0 + kStreamChunk, n0, wave, lane);
+      stream_load<MT, KIND, FQ>(p, cur, k0 + kStreamChunk, n0, wave, lane);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1227,25 +1269,29 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs
       float sa_blk[MT];
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        const int64_t m = t * 16 + r16;
         if constexpr (FQ) {
           af[t] = join(codes[r16 * CPR + (c0 ^ r16)], codes[r16 * CPR + ((c0 + 1) ^ r16)]);
-          if (KIND == kBlockwise) sa_blk[t] = blk_scale[r16 * (kStreamChunk / 128) + wave * 4 + j];
+          if (KIND == kBlockwise) sa_blk[t] = blk_scale[r16 * BPC + wave * 4 + j];
         } else {
           af[t] = join(use.a[t][j][0], use.a[t][j][1]);
-          if (KIND == kBlockwise) sa_blk[t] = (m < p.M) ? p.sa[(kbase / 128) * p.sa_ld + m] : 0.0f;
+          if (KIND == kBlockwise) sa_blk[t] = use.sa[t][j];
         }
       }
-      if (KIND == kChannelwise) {
+      if constexpr (KIND == kChannelwise) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[t] = mfma_fp8(bf, af[t], acc[t]);
       } else {
-        const float sb = p.sb[(n0 / 128) * kb_all + kbase / 128];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           const f32x4 part = mfma_fp8(bf, af[t], f32x4{0.f, 0.f, 0.f, 0.f});
-          acc[t] += part * (sa_blk[t] * sb);
+          acc[t] += part * (sa_blk[t] * use.sb[j]);
         }
+      }
+    }
+    if constexpr (FQ) {
+      if (more) {
+        __syncthreads();  // every wave is done with this chunk's codes
+        quantize_chunk(k0 + kStreamChunk);
       }
     }
   }
