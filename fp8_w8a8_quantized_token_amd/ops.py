@@ -301,10 +301,15 @@ def set_config_dir(path):
 class Prepared:
     """A launch with every argument resolved up front: calling it is one ctypes
     call on the stream that was current when it was prepared. For hot loops
-    whose tensors and shapes do not change (the benchmark, serving loops)."""
+    whose tensors and shapes do not change (the benchmark, serving loops).
+    The ctypes arguments are raw device pointers, so the object holds a
+    reference to every tensor (and config struct) they point into: the
+    memory stays allocated for as long as the launch can be called, also when
+    the caller drops its own references or torch empties its cache."""
 
-    def __init__(self, fn, args, name):
+    def __init__(self, fn, args, name, keep):
         self._fn, self._args, self.name = fn, args, name
+        self._keep = tuple(keep)
 
     def __call__(self):
         st = self._fn(*self._args)
@@ -332,13 +337,13 @@ def prepare(op, *args, **kwargs):
         q, s = kwargs["out"], kwargs["scale"]
         a = (_p(x), x.shape[0], x.shape[1], x.stride(0), _p(q), q.stride(0), _p(s),
              ctypes.c_float(kwargs.get("eps", 1e-10)), _stream(x))
-        return Prepared(lib.fp8_quant_per_token, a, op)
+        return Prepared(lib.fp8_quant_per_token, a, op, (x, q, s))
     if op == "quant_per_token_group":
         x, g = args[0], args[1]
         q, st = kwargs["out"], kwargs["scale_storage"]
         a = (_p(x), x.shape[0], x.shape[1], x.stride(0), g, kwargs.get("row_alignment", 4), _p(q),
              q.stride(0), _p(st), ctypes.c_float(kwargs.get("eps", 1e-10)), _stream(x))
-        return Prepared(lib.fp8_quant_per_token_group, a, op)
+        return Prepared(lib.fp8_quant_per_token_group, a, op, (x, q, st))
     if op in ("linear_channelwise", "linear_blockwise"):
         kind = KIND_CHANNELWISE if op == "linear_channelwise" else KIND_BLOCKWISE
         x, w_q, w_s = args[0], args[1], args[2]
@@ -346,10 +351,8 @@ def prepare(op, *args, **kwargs):
         a, keep = _linear_args(kind, x, w_q, w_s, kwargs.get("bias"), kwargs.get("eps", 1e-10),
                                kwargs.get("row_alignment", 4), cfg, kwargs["out"], kwargs["q"],
                                kwargs["scale"])
-        pr = Prepared(lib.fp8_linear_channelwise if op == "linear_channelwise"
-                      else lib.fp8_linear_blockwise, a, op)
-        pr._keep = keep
-        return pr
+        return Prepared(lib.fp8_linear_channelwise if op == "linear_channelwise"
+                        else lib.fp8_linear_blockwise, a, op, keep + (x, w_q, w_s, kwargs.get("bias")))
     if op in ("scaled_mm_channelwise", "scaled_mm_blockwise"):
         a_, b_, sa, sb = _as_codes(args[0], "a"), _as_codes(args[1], "b"), args[2], args[3]
         bias, out = kwargs.get("bias"), kwargs["out"]
@@ -361,7 +364,7 @@ def prepare(op, *args, **kwargs):
             ws = _ws.get(a_.device, nws)
             a = (_p(a_), _p(b_), _p(sa), _p(sb), _p(bias), _p(out), m, n, k, a_.stride(0),
                  b_.stride(0), out.stride(0), _p(ws), nws, ctypes.byref(cfg), _stream(a_))
-            pr = Prepared(lib.fp8_scaled_mm_channelwise_ex, a, op)
+            pr = Prepared(lib.fp8_scaled_mm_channelwise_ex, a, op, (a_, b_, sa, sb, bias, out, cfg, ws))
         else:
             m = kwargs.get("m") or a_.shape[0]
             nws = workspace_bytes(KIND_BLOCKWISE, m, n, k, cfg)
@@ -369,7 +372,6 @@ def prepare(op, *args, **kwargs):
             a = (_p(a_), _p(b_), _p(sa), sa.stride(1), _p(sb), _p(bias), _p(out), m, n, k,
                  a_.stride(0), b_.stride(0), out.stride(0), _p(ws), nws, ctypes.byref(cfg),
                  _stream(a_))
-            pr = Prepared(lib.fp8_scaled_mm_blockwise_ex, a, op)
-        pr._keep = (cfg, ws)  # keep the config struct and workspace alive
+            pr = Prepared(lib.fp8_scaled_mm_blockwise_ex, a, op, (a_, b_, sa, sb, bias, out, cfg, ws))
         return pr
     raise ValueError(f"unknown op {op}")

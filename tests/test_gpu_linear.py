@@ -184,3 +184,44 @@ def test_linear_blockwise_three_chunks_row_alignment_8():
     assert np.array_equal(s[:m].cpu().numpy().view(np.uint32), want_s.view(np.uint32))
     ref = oracle.scaled_mm_blockwise(want_q, b, want_s, sb)
     _check(out, ref, oracle.summation_bound_blockwise(want_q, b, want_s, sb), "linear bw 3 chunks")
+
+
+def test_prepared_launches_keep_their_buffers():
+    """Prepared launches hold raw device pointers; they must keep every tensor
+    those point into alive. Prepare from temporaries, drop all other
+    references, release torch's cached blocks (graph capture does this), then
+    run: the results must still be right."""
+    import gc
+
+    m, n, k = 3, 256, 512
+    x = activations("keep", m, k)
+    b, sb = weight_channelwise("keep", n, k)
+
+    def make():
+        xd, bd, sbd = gpu(x), gpu(b), gpu(sb)
+        q = torch.empty((m, k), dtype=torch.uint8, device=device())
+        s = torch.empty((m,), dtype=torch.float32, device=device())
+        out_l = torch.empty((m, n), dtype=torch.bfloat16, device=device())
+        out_g = torch.empty((m, n), dtype=torch.bfloat16, device=device())
+        lin = ops.prepare("linear_channelwise", xd, bd, sbd, out=out_l, q=q, scale=s)
+        qz = ops.prepare("quant_per_token", xd, out=q, scale=s)
+        mm = ops.prepare("scaled_mm_channelwise", q, bd, s, sbd, out=out_g,
+                         config=ops.make_config("t64x64panel", 2))
+        return lin, qz, mm, out_l, out_g
+
+    lin, qz, mm, out_l, out_g = make()
+    torch.cuda.synchronize()
+    out_l.zero_()
+    out_g.zero_()
+    gc.collect()
+    torch.cuda.empty_cache()
+    say("prepared launches after empty_cache", m, n, k)
+    lin()
+    qz()
+    mm()
+    torch.cuda.synchronize()
+    want_q, want_s = oracle.quant_per_token(x.float().numpy())
+    ref = oracle.scaled_mm_channelwise(want_q, b, want_s, sb)
+    tau = oracle.summation_bound_channelwise(want_q, b, want_s, sb)
+    _check(out_l, ref, tau, "prepared linear")
+    _check(out_g, ref, tau, "prepared quant + gemm")
