@@ -225,3 +225,36 @@ def test_prepared_launches_keep_their_buffers():
     tau = oracle.summation_bound_channelwise(want_q, b, want_s, sb)
     _check(out_l, ref, tau, "prepared linear")
     _check(out_g, ref, tau, "prepared quant + gemm")
+
+
+TINY = [("cw", 1, 8, 16), ("cw", 4, 24, 48), ("cw", 2, 8, 4112), ("bw", 3, 128, 128), ("bw", 4, 128, 256)]
+
+
+@pytest.mark.parametrize("kind,m,n,k", TINY, ids=[f"{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in TINY])
+def test_linear_tiny_shapes(kind, m, n, k):
+    """Smallest legal shapes through the single-launch path: K of one
+    16-element piece, N below one 16-column weight tile, a last chunk of 16
+    elements; blockwise one and two 128-blocks."""
+    x = activations("tiny-lin", m, k)
+    if kind == "cw":
+        b, sb = weight_channelwise("tiny-lin", n, k)
+        assert ops.linear_launches(ops.KIND_CHANNELWISE, m, n, k) == 1
+        say("linear tiny", kind, m, n, k)
+        out, q, s = ops.linear_channelwise(gpu(x), gpu(b), gpu(sb), return_quant=True)
+        torch.cuda.synchronize()
+        want_q, want_s = oracle.quant_per_token(x.float().numpy())
+        ref = oracle.scaled_mm_channelwise(want_q, b, want_s, sb)
+        tau = oracle.summation_bound_channelwise(want_q, b, want_s, sb)
+    else:
+        b, sb = weight_blockwise("tiny-lin", n, k)
+        assert ops.linear_launches(ops.KIND_BLOCKWISE, m, n, k) == 1
+        say("linear tiny", kind, m, n, k)
+        out, q, s = ops.linear_blockwise(gpu(x), gpu(b), gpu(sb), return_quant=True)
+        torch.cuda.synchronize()
+        want_q, want_s = oracle.quant_per_token_group(x.float().numpy(), 128)
+        s = s[:m]
+        ref = oracle.scaled_mm_blockwise(want_q, b, want_s, sb)
+        tau = oracle.summation_bound_blockwise(want_q, b, want_s, sb)
+    assert np.array_equal(q[:m].cpu().numpy(), want_q)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    _check(out, ref, tau, f"linear tiny {kind} M={m} N={n} K={k}")
