@@ -30,7 +30,7 @@ VARIANTS = {"default": -1, "skinny": 0, "t64x64": 1, "t128x128": 2, "t256x128": 
             "t128x128panel": 16, "t128x64panel": 17, "t64x64panel": 18,
             "t64x64deep": 19, "t128x64deep": 20,
             "t128x128panel8": 21, "t128x64panel8": 22,
-            "t32x32deep": 23, "t64x32deep": 24}
+            "t32x32deep": 23, "t64x32deep": 24, "t256x256bw16": 25}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 
 

@@ -116,6 +116,66 @@ __device__ __forceinline__ uint2 pack_out4(const GemmArgs& p, int64_t n, f32x4 v
 // conflict-free for both phases. The LDS
 // must hold BM * BN * 2 bytes; the function begins with a barrier, so the
 // caller may still be reading it.
+template <int CH>
+__device__ __forceinline__ int out_sw(int r) {
+  static_assert(CH == 4 || CH == 8 || CH == 16 || CH == 32, "tile width");
+  return CH >= 16 ? (r & (CH - 1)) : CH == 8 ? ((r >> 1) & (CH - 1)) : ((r >> 2) & (CH - 1));
+}
+
+// Second phase of the staged epilogue: consecutive threads copy consecutive
+// 16-byte chunks of the [BM][BN] bf16 tile in LDS to rows < M, columns < N.
+template <int BM, int BN, int NT>
+__device__ __forceinline__ void copy_out_tile(const GemmArgs& p, const uint8_t* lds, int64_t m0,
+                                              int64_t n0, int tid) {
+  constexpr int CH = BN / 8;
+  static_assert((BM * CH) % NT == 0, "copy-out split");
+#pragma unroll 4
+  for (int idx = tid; idx < BM * CH; idx += NT) {
+    const int rl = idx / CH, c = idx % CH;
+    const int64_t m = m0 + rl;
+    const int64_t n = n0 + c * 8;
+    if (m >= p.M || n >= p.N) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(lds + rl * (BN * 2) + ((c ^ out_sw<CH>(rl)) << 4));
+    uint16_t* dst = p.out + m * p.ldc + n;
+    if (n + 8 <= p.N) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (n + r < p.N) dst[r] = (uint16_t)(w[r >> 1] >> (16 * (r & 1)));
+    }
+  }
+}
+
+// The same epilogue for 16x16-MFMA accumulators (lane: m = 16 i + l % 16,
+// n = 16 j + 4 (l / 16) .. +3), blockwise (already scaled).
+template <int BM, int BN, int WM, int WN, int KIND>
+__device__ __forceinline__ void store_tile16(const GemmArgs& p,
+                                             const f32x4 (&acc)[BM / WM / 16][BN / WN / 16],
+                                             uint8_t* lds, int64_t m0, int64_t n0, int wm, int wn,
+                                             int lane, int tid) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int CH = BN / 8;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < WTM / 16; ++i) {
+    const int ml = wm * WTM + i * 16 + (lane & 15);
+    const int64_t m = m0 + ml;
+    const float sa_m = (KIND == kChannelwise && m < p.M) ? p.sa[m] : 1.0f;
+    uint8_t* row = lds + ml * (BN * 2);
+#pragma unroll
+    for (int j = 0; j < WTN / 16; ++j) {
+      const int nl = wn * WTN + j * 16 + 4 * (lane >> 4);
+      const uint2 v = pack_out4<KIND>(p, n0 + nl, acc[i][j], sa_m);
+      *reinterpret_cast<uint2*>(row + (((nl >> 3) ^ out_sw<CH>(ml)) << 4) + (((nl >> 2) & 1) << 3)) = v;
+    }
+  }
+  __syncthreads();
+  copy_out_tile<BM, BN, NT>(p, lds, m0, n0, tid);
+}
+
 template <int BM, int BN, int WM, int WN, int KIND>
 __device__ __forceinline__ void store_tile(const GemmArgs& p,
                                            const f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
@@ -125,10 +185,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p,
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int CH = BN / 8;  // 16-byte chunks per tile row
-  static_assert(CH == 4 || CH == 8 || CH == 16 || CH == 32, "tile width");
-  auto sw = [](int r) {
-    return CH >= 16 ? (r & (CH - 1)) : CH == 8 ? ((r >> 1) & (CH - 1)) : ((r >> 2) & (CH - 1));
-  };
+  auto sw = [](int r) { return out_sw<CH>(r); };
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -149,24 +206,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p,
       }
   }
   __syncthreads();
-  static_assert((BM * CH) % NT == 0, "copy-out split");
-#pragma unroll 4
-  for (int idx = tid; idx < BM * CH; idx += NT) {
-    const int rl = idx / CH, c = idx % CH;
-    const int64_t m = m0 + rl;
-    const int64_t n = n0 + c * 8;
-    if (m >= p.M || n >= p.N) continue;
-    const uint4 v = *reinterpret_cast<const uint4*>(lds + rl * (BN * 2) + ((c ^ sw(rl)) << 4));
-    uint16_t* dst = p.out + m * p.ldc + n;
-    if (n + 8 <= p.N) {
-      *reinterpret_cast<uint4*>(dst) = v;
-    } else {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        if (n + r < p.N) dst[r] = (uint16_t)(w[r >> 1] >> (16 * (r & 1)));
-    }
-  }
+  copy_out_tile<BM, BN, NT>(p, lds, m0, n0, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -460,10 +500,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmArgs p) {
 // and counts itself in with one atomic; the last to arrive sums the partials in
 // split order into acc, re-arms the counter and returns true. The others
 // return false and must exit. *flag is workgroup-shared scratch.
-template <int TM, int TN, int NT>
-__device__ __forceinline__ bool splitk_reduce(const GemmArgs& p, f32x16 (&acc)[TM][TN],
+template <int TM, int TN, int NT, typename V>
+__device__ __forceinline__ bool splitk_reduce(const GemmArgs& p, V (&acc)[TM][TN],
                                               int64_t tile, int split, int tid, int* flag) {
-  constexpr int Q = TM * TN * 16;
+  constexpr int VW = sizeof(V) / sizeof(float);  // 16 (32x32 tiles) or 4 (16x16)
+  constexpr int Q = TM * TN * VW;
   float* part = p.ws_part + (tile * p.split_k) * (int64_t)Q * NT;
   float* mine = part + (int64_t)split * Q * NT;
 #pragma unroll
@@ -471,8 +512,8 @@ __device__ __forceinline__ bool splitk_reduce(const GemmArgs& p, f32x16 (&acc)[T
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        __hip_atomic_store(mine + ((i * TN + j) * 16 + r) * NT + tid, acc[i][j][r], __ATOMIC_RELAXED,
+      for (int r = 0; r < VW; ++r)
+        __hip_atomic_store(mine + ((i * TN + j) * VW + r) * NT + tid, acc[i][j][r], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -487,8 +528,8 @@ __device__ __forceinline__ bool splitk_reduce(const GemmArgs& p, f32x16 (&acc)[T
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t idx = (int64_t)((i * TN + j) * 16 + r) * NT + tid;
+      for (int r = 0; r < VW; ++r) {
+        const int64_t idx = (int64_t)((i * TN + j) * VW + r) * NT + tid;
         float v = __hip_atomic_load(part + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (int sp = 1; sp < p.split_k; ++sp)
           v += __hip_atomic_load(part + (int64_t)sp * Q * NT + idx, __ATOMIC_RELAXED,
@@ -773,7 +814,7 @@ __device__ __forceinline__ void wait_panels(int64_t c) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int KIND, int NP>
+template <int BM, int BN, int WM, int WN, int KIND, int NP, bool MF16 = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   using G = PanelGeom<BM, BN, WM, WN, KIND, NP>;
   constexpr bool BW = KIND == kBlockwise;
@@ -874,6 +915,83 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
       }
     }
   };
+  if constexpr (MF16) {
+    // 16x16x128 MFMAs, one per 128-deep block: the blockwise partial of a
+    // (16-row, 16-column) piece is 4 registers, so a 256x256 tile fits in
+    // registers. A stage is one block; at its start every wave reads its four
+    // B fragments, then streams its eight A fragments, promoting each MFMA
+    // result with sa[m] * sb right away. One barrier per stage: it finds every
+    // wave past the previous stage, whose two slots then take the panels NP
+    // ahead (a four-slot ring holds the stage being multiplied and the next).
+    static_assert(BW, "the 16x16 body serves the blockwise kind");
+    constexpr int FI = WTM / 16, FJ = WTN / 16;
+    const int g = lane >> 4, r16 = lane & 15;
+    // lane's chunks of a 16-row fragment: row r16, K bytes [32g, 32g + 32)
+    uint32_t fo16[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) fo16[t] = (uint32_t)(r16 * BK + (swz<8>(r16, 2 * g + t) << 4));
+    auto frag16 = [&](const uint8_t* base) {
+      return join(*reinterpret_cast<const uint4*>(base + fo16[0]),
+                  *reinterpret_cast<const uint4*>(base + fo16[1]));
+    };
+    auto wrap = [](int x) { return x >= NP ? x - NP : x; };
+    const int64_t np_all = 2 * nst;
+    auto issue_panel = [&](int64_t q, int slot) {
+      if (q & 1) issue_a(kt_begin + (q >> 1), slot);
+      else issue_b(kt_begin + (q >> 1), slot);
+    };
+    f32x4 acc16[FI][FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) acc16[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int64_t issued = 0;
+    if (nst > 0) {
+      issued = np_all < NP ? np_all : NP;
+      for (int64_t q = 0; q < issued; ++q) issue_panel(q, (int)q);
+    }
+    int cs = 0;  // slot of stage s's B panel; its A panel is in wrap(cs + 1)
+    for (int64_t s = 0; s < nst; ++s) {
+      const int cs1 = wrap(cs + 1);
+      // stage s complete: the panels issued after it (from a B panel on) may
+      // still be outstanding
+      {
+        const int64_t later = issued - 2 * s - 2;
+        wait_panels<NP - 2, PPB_ALL, PPA>(later < NP - 2 ? later : NP - 2);
+      }
+      wait_vmcnt_lgkm0<63>();
+      __builtin_amdgcn_s_barrier();
+      if (s > 0) {  // every wave is past stage s-1: its slots take the next panels
+        const int ps = wrap(cs + NP - 2);
+        if (issued < np_all) { issue_panel(issued, ps); ++issued; }
+        if (issued < np_all) { issue_panel(issued, wrap(ps + 1)); ++issued; }
+      }
+      const uint8_t* pb = lds + cs * SLOT;
+      const uint8_t* pa = lds + cs1 * SLOT + (wm * WTM) * BK;
+      const float sb = *reinterpret_cast<const float*>(pb + SB_OFF + wave * 16 + ((wn * WTN) >> 7) * 4);
+      i32x8 fb[FJ];
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) fb[j] = frag16(pb + (wn * WTN + j * 16) * BK);
+      i32x8 fa = frag16(pa);
+#pragma unroll
+      for (int i = 0; i < FI; ++i) {
+        const float sc = *reinterpret_cast<const float*>(pb + SA_OFF + (wm * WTM + i * 16 + r16) * 4) * sb;
+        i32x8 fn;
+        if (i + 1 < FI) fn = frag16(pa + (i + 1) * 16 * BK);
+        f32x4 t[FJ];
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) t[j] = mfma_fp8(fb[j], fa, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) acc16[i][j] += t[j] * sc;
+        if (i + 1 < FI) fa = fn;
+      }
+      cs = wrap(cs + 2);
+    }
+    // the ring is idle from here on: its first word serves as the split flag
+    if (p.split_k > 1 && !splitk_reduce<FI, FJ, NT>(p, acc16, tile, split, tid, reinterpret_cast<int*>(lds)))
+      return;
+    store_tile16<BM, BN, WM, WN, KIND>(p, acc16, lds, m0, n0, wm, wn, lane, tid);
+  } else {
   // Per-lane byte offsets, within a panel, of the two 16-byte chunks of this
   // lane's A fragment row for each 64-deep half kh (chunks 4kh + 2h, +1). The
   // swizzle depends on the row only through row % 16, the same for every
@@ -1009,6 +1127,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   if (p.split_k > 1 && !splitk_reduce<TM, TN, NT>(p, acc, tile, split, tid, reinterpret_cast<int*>(lds)))
     return;
   store_tile<BM, BN, WM, WN, KIND>(p, acc, lds, m0, n0, wm, wn, h, r32, tid);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1335,11 +1454,11 @@ hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int KIND, int NP>
+template <int BM, int BN, int WM, int WN, int KIND, int NP, bool MF16 = false>
 hipError_t launch_panel(const GemmArgs& p, hipStream_t stream) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   const size_t lds = (size_t)PanelGeom<BM, BN, WM, WN, KIND, NP>::LDS;
-  auto kern = gemm_panel_kernel<BM, BN, WM, WN, KIND, NP>;
+  auto kern = gemm_panel_kernel<BM, BN, WM, WN, KIND, NP, MF16>;
   static bool lds_attr_set = false;
   if (lds > 65536 && !lds_attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1459,6 +1578,12 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
     case 24:
       if (!panel_eligible<KIND>(p)) return launch_tile<64, 32, 2, 1, 128, KIND>(p, stream);
       return launch_panel<64, 32, 2, 1, KIND, 7>(p, stream);
+    // blockwise 256x256 on 16x16x128 MFMAs (four-slot ring); channelwise
+    // requests run the 256x256 panel tile
+    case 25:
+      if (!panel_eligible<KIND>(p)) return launch_tile<256, 256, 2, 4, 128, KIND>(p, stream);
+      if constexpr (KIND == kBlockwise) return launch_panel<256, 256, 2, 4, kBlockwise, 4, true>(p, stream);
+      else return launch_panel<256, 256, 2, 4, kChannelwise, 5>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1494,6 +1619,7 @@ VariantInfo variant_info(int variant) {
     case 22: return {128, 64, 128, 8, true};
     case 23: return {32, 32, 128, 1, true};
     case 24: return {64, 32, 128, 2, true};
+    case 25: return {256, 256, 128, 8, true};
     default: return {0, 0, 0, 0, false};
   }
 }

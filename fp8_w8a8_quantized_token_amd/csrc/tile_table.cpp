@@ -191,6 +191,7 @@ int variant_from_name(const std::string& n) {
   if (n == "t128x64panel8") return FP8_VARIANT_T128x64PANEL8;
   if (n == "t32x32deep") return FP8_VARIANT_T32x32DEEP;
   if (n == "t64x32deep") return FP8_VARIANT_T64x32DEEP;
+  if (n == "t256x256bw16") return FP8_VARIANT_T256x256BW16;
   return -100;
 }
 
@@ -284,9 +285,10 @@ int default_config(int kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* o
   // HBM-resident weights): the weight-streaming kernel up to 32 rows, then,
   // for K % 128 == 0, the panel-ring LDS-DMA tiles: 64x64 up to M = 256 (deep
   // ring for channelwise), 128x64 up to 512 (deep ring for channelwise), the
-  // 8-wave 128x128 up to 1024, then 256x128, or channelwise 256x256 where it
-  // gives at least 192 workgroups (at M <= 1024 only if it fills all 256
-  // compute units). Without that K the register-staged tiles run
+  // 8-wave 128x128 up to 1024, then 256x128, or 256x256 where it gives at
+  // least 192 workgroups (channelwise at M <= 1024 only if it fills all 256
+  // compute units; blockwise the 16x16x128-MFMA tile, 8-15% ahead of 256x128
+  // at M = 4096-8192). Without that K the register-staged tiles run
   // (channelwise with K % 64 == 0: the 64-byte-stage DMA tiles at large M); a
   // large tile is taken only if it gives at least half the compute units a
   // workgroup, the 64x64 tile being the fallback. Split-K rarely won in those
@@ -306,7 +308,8 @@ int default_config(int kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* o
     if (cw && variant_tiles(FP8_VARIANT_T256x256PANEL, M, N) >= 256) c.variant = FP8_VARIANT_T256x256PANEL;
   } else if (k128) {
     c.variant = FP8_VARIANT_T256x128PANEL;
-    if (cw && variant_tiles(FP8_VARIANT_T256x256PANEL, M, N) >= 192) c.variant = FP8_VARIANT_T256x256PANEL;
+    if (variant_tiles(FP8_VARIANT_T256x256PANEL, M, N) >= 192)
+      c.variant = cw ? FP8_VARIANT_T256x256PANEL : FP8_VARIANT_T256x256BW16;
   } else {
     struct Cand {
       int variant;

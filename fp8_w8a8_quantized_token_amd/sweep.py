@@ -64,6 +64,8 @@ def candidates(kind, m, n, k):
         c += [("t256x128", 1)]
         if k128:
             c += [("t256x128panel", 2)]
+        if kind == "blockwise" and k128:
+            c += [("t256x256bw16", 1), ("t256x256bw16", 2)]
         if kind == "channelwise":
             c += [("t256x256w8", 1)]
             if k % 64 == 0:

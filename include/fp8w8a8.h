@@ -101,7 +101,8 @@ enum {
    * per compute unit); fallbacks: register-staged tiles of the same shape. */
   FP8_VARIANT_T32x32DEEP = 23,     /* 32x32 block tile, 1 wave, 9-slot ring */
   FP8_VARIANT_T64x32DEEP = 24,     /* 64x32 block tile, 2 waves, 7-slot ring */
-  FP8_VARIANT_COUNT = 25,
+  FP8_VARIANT_T256x256BW16 = 25,   /* blockwise 256x256, 8 waves, 16x16x128 MFMAs, 4-slot ring */
+  FP8_VARIANT_COUNT = 26,
 };
 
 /* One tile configuration of the scaled GEMM. The PR34331 digest ("Key source

@@ -286,6 +286,24 @@ def test_blockwise_panel_variant(split_k, m, n, k, bias):
     _blockwise_case("bw-panel", m, n, k, config=ops.make_config("t256x128panel", split_k), with_bias=bias)
 
 
+@pytest.mark.parametrize("split_k,m,n,k,bias", BW_PANEL_CASES,
+                         ids=[f"sk{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}{'-bias' if c[4] else ''}"
+                              for c in BW_PANEL_CASES])
+def test_blockwise_256x256_mfma16(split_k, m, n, k, bias):
+    """The blockwise 256x256 tile on 16x16x128 MFMAs (four-slot ring, one
+    promotion per MFMA): the same stage counts, ragged shapes and splits."""
+    _blockwise_case("bw16", m, n, k, config=ops.make_config("t256x256bw16", split_k), with_bias=bias)
+
+
+def test_blockwise_256x256_mfma16_poison_and_fallbacks():
+    """NaN pad rows stay out; an unaligned scale column takes the register
+    tile of the same shape; a channelwise request runs the 256x256 panel tile."""
+    _blockwise_case("bw16-poison", 301, 512, 1024, config=ops.make_config("t256x256bw16", 2), poison=True)
+    _blockwise_case("bw16-ld", 301, 384, 1024, config=ops.make_config("t256x256bw16", 2), row_align=1)
+    _channelwise_case("bw16-cw", 300, 392, 1024, 0.0, True, config=ops.make_config("t256x256bw16", 2),
+                      sample=False)
+
+
 def test_blockwise_panel_poisoned_padding():
     """Padded activation rows hold NaN codes and NaN scales; no valid row may see them."""
     _blockwise_case("bw-panel-poison", 301, 384, 1024, config=ops.make_config("t256x128panel", 2),
