@@ -790,15 +790,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma_kernel(GemmArgs p) {
 // scales of block kb (the waves split them) and, per wave, the tile's weight
 // block scales into the spare end of the B slot.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int KIND, int NP>
+// SC_IN_A: the blockwise scales travel with the A panel instead of the B panel.
+template <int BM, int BN, int WM, int WN, int KIND, int NP, bool SC_IN_A = false>
 struct PanelGeom {
   static constexpr int NW = WM * WN;
   static constexpr int NBLK = (BN + 127) / 128;                // weight scale blocks per tile
   static constexpr int SA_BYTES = KIND == kBlockwise ? BM * 4 : 0;
   static constexpr int SB_BYTES = KIND == kBlockwise ? NW * 16 : 0;
-  static constexpr int B_BYTES = BN * 128 + SA_BYTES + SB_BYTES;
-  static constexpr int SLOT = (BM * 128 > B_BYTES ? BM * 128 : B_BYTES + 1023) / 1024 * 1024;
+  static constexpr int A_BYTES = BM * 128 + (SC_IN_A ? SA_BYTES + SB_BYTES : 0);
+  static constexpr int B_BYTES = BN * 128 + (SC_IN_A ? 0 : SA_BYTES + SB_BYTES);
+  static constexpr int SLOT = ((A_BYTES > B_BYTES ? A_BYTES : B_BYTES) + 1023) / 1024 * 1024;
   static constexpr int LDS = NP * SLOT;
+  static constexpr int SC_OFF = SC_IN_A ? BM * 128 : BN * 128;  // scales inside their slot
 };
 
 // Wait until at most the c newest DMA panels of this wave are outstanding,
@@ -816,7 +819,7 @@ __device__ __forceinline__ void wait_panels(int64_t c) {
 
 template <int BM, int BN, int WM, int WN, int KIND, int NP, bool MF16 = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
-  using G = PanelGeom<BM, BN, WM, WN, KIND, NP>;
+  using G = PanelGeom<BM, BN, WM, WN, KIND, NP, MF16>;
   constexpr bool BW = KIND == kBlockwise;
   constexpr int NT = WM * WN * 64;
   constexpr int NW = WM * WN;
@@ -826,15 +829,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   constexpr int SLOT = G::SLOT;
   constexpr int PPA = BM / 8 / NW;     // DMA instructions per wave per A panel
   constexpr int PPB = BN / 8 / NW;     // ... per B panel (rows only)
-  constexpr int PPB_ALL = PPB + (BW ? 2 : 0);  // B panel with its scale copies
-  constexpr int SA_OFF = BN * BK;      // scale area inside a B slot
+  // blockwise: the per-stage scale copies ride with the B panel, or with the
+  // A panel in the 16x16 body
+  constexpr int PPB_ALL = PPB + (BW && !MF16 ? 2 : 0);
+  constexpr int PPA_ALL = PPA + (BW && MF16 ? 2 : 0);
+  constexpr int SA_OFF = G::SC_OFF;    // scale area inside its slot
   constexpr int SB_OFF = SA_OFF + G::SA_BYTES;
   constexpr int SA_LANES = BM / 4 / NW;  // lanes of a wave's 16-byte activation-scale DMA
   static_assert(TM >= 1 && TN >= 1, "wave tile");
   static_assert(PPA >= 1 && PPB >= 1 && (BM / 8) % NW == 0 && (BN / 8) % NW == 0, "panel rows per wave");
   static_assert(G::LDS <= 163840, "ring fits the LDS");
   static_assert(NP >= 4, "ring depth");
-  static_assert(((NP - 1) / 2) * PPB_ALL + ((NP - 2) / 2) * PPA < 64, "vmcnt range");
+  static_assert(((NP - 1) / 2) * PPB_ALL + ((NP - 2) / 2) * PPA_ALL < 64 &&
+                ((NP - 1) / 2) * PPA_ALL + ((NP - 2) / 2) * PPB_ALL < 64, "vmcnt range");
   static_assert(BM * BN * 2 <= G::LDS, "output tile fits the ring");
   static_assert(!BW || (SA_LANES >= 1 && SA_LANES <= 64 && BM % (4 * NW) == 0 && G::NBLK <= 4 &&
                         WTN <= 128 && 128 % WTN == 0),
@@ -884,45 +891,49 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
       lds_dma16_s(src, row * ld + lchunk[(wave * PP + i) & 1], dst + i * 1024);
     }
   };
+  // blockwise scales of block kt into the scale area of the slot at sbase
+  auto issue_scales = [&](int64_t kt, uint32_t sbase) {
+    // activation scales of block kt, rows m0 .. m0+BM-1 (column-major, ld
+    // sa_ld; 16-byte pieces clamped into the column): wave w copies rows
+    // [w * BM / NW, (w + 1) * BM / NW) with SA_LANES lanes
+    {
+      int64_t r = m0 + (int64_t)(wave * SA_LANES + (lane < SA_LANES ? lane : 0)) * 4;
+      if (r > p.sa_ld - 4) r = p.sa_ld - 4;
+      // lane 0 is always active, so the instruction always issues and
+      // counts once in this wave's vmcnt
+      if (lane < SA_LANES)
+        lds_dma16_s(reinterpret_cast<const uint8_t*>(p.sa + kt * p.sa_ld), (uint32_t)(r * 4),
+                    sbase + SA_OFF + wave * SA_LANES * 16);
+    }
+    // weight block scales b_scale[n0 / 128 + l][kt], lanes l < NBLK, one
+    // 16-byte copy per wave (lane 0 always active, as above)
+    {
+      const int64_t kb_all = p.K / 128;
+      if (lane < G::NBLK)
+        lds_dma4_s(reinterpret_cast<const uint8_t*>(p.sb + kt),
+                   (uint32_t)(((n0 >> 7) + lane) * kb_all * 4), sbase + SB_OFF + wave * 16);
+    }
+  };
   auto issue_a = [&](int64_t kt, int slot) {
+    const uint32_t sbase = lds_base + (uint32_t)slot * SLOT;
     issue_rows(p.a + kt * BK, (uint32_t)m0, (uint32_t)(p.M - 1), (uint32_t)p.lda,
-               lds_base + (uint32_t)slot * SLOT + wave * PPA * 1024, IntC<PPA>());
+               sbase + wave * PPA * 1024, IntC<PPA>());
+    if constexpr (BW && MF16) issue_scales(kt, sbase);
   };
   auto issue_b = [&](int64_t kt, int slot) {
     const uint32_t sbase = lds_base + (uint32_t)slot * SLOT;
     issue_rows(p.b + kt * BK, (uint32_t)n0, (uint32_t)(p.N - 1), (uint32_t)p.ldb,
                sbase + wave * PPB * 1024, IntC<PPB>());
-    if constexpr (BW) {
-      // activation scales of block kt, rows m0 .. m0+BM-1 (column-major, ld
-      // sa_ld; 16-byte pieces clamped into the column): wave w copies rows
-      // [w * BM / NW, (w + 1) * BM / NW) with SA_LANES lanes
-      {
-        int64_t r = m0 + (int64_t)(wave * SA_LANES + (lane < SA_LANES ? lane : 0)) * 4;
-        if (r > p.sa_ld - 4) r = p.sa_ld - 4;
-        // lane 0 is always active, so the instruction always issues and
-        // counts once in this wave's vmcnt
-        if (lane < SA_LANES)
-          lds_dma16_s(reinterpret_cast<const uint8_t*>(p.sa + kt * p.sa_ld), (uint32_t)(r * 4),
-                      sbase + SA_OFF + wave * SA_LANES * 16);
-      }
-      // weight block scales b_scale[n0 / 128 + l][kt], lanes l < NBLK, one
-      // 16-byte copy per wave (lane 0 always active, as above)
-      {
-        const int64_t kb_all = p.K / 128;
-        if (lane < G::NBLK)
-          lds_dma4_s(reinterpret_cast<const uint8_t*>(p.sb + kt),
-                     (uint32_t)(((n0 >> 7) + lane) * kb_all * 4), sbase + SB_OFF + wave * 16);
-      }
-    }
+    if constexpr (BW && !MF16) issue_scales(kt, sbase);
   };
   if constexpr (MF16) {
     // 16x16x128 MFMAs, one per 128-deep block: the blockwise partial of a
     // (16-row, 16-column) piece is 4 registers, so a 256x256 tile fits in
     // registers. A stage is one block; at its start every wave reads its four
     // B fragments, then streams its eight A fragments, promoting each MFMA
-    // result with sa[m] * sb right away. One barrier per stage: it finds every
-    // wave past the previous stage, whose two slots then take the panels NP
-    // ahead (a four-slot ring holds the stage being multiplied and the next).
+    // result with sa[m] * sb right away. The per-stage scales ride with the A
+    // panel, so the B slot can be refilled as soon as the B fragments are in
+    // registers (see the issue order below).
     static_assert(BW, "the 16x16 body serves the blockwise kind");
     constexpr int FI = WTM / 16, FJ = WTN / 16;
     const int g = lane >> 4, r16 = lane & 15;
@@ -945,6 +956,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
     for (int i = 0; i < FI; ++i)
 #pragma unroll
       for (int j = 0; j < FJ; ++j) acc16[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Panel q = B (q even) or A (q odd) of stage q / 2 goes to slot q % 4, in
+    // order. Stage s's B slot is free once every wave has its B fragments in
+    // registers (second barrier of the stage): it takes B(s+2). Its A slot,
+    // which also holds the stage's scales, is free at the next stage's first
+    // barrier: it takes A(s+2) then. So A panels get one stage of lead and B
+    // panels nearly two.
+    static_assert(NP == 4, "the 16x16 body's issue order assumes a four-slot ring");
     int64_t issued = 0;
     if (nst > 0) {
       issued = np_all < NP ? np_all : NP;
@@ -953,29 +971,39 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
     int cs = 0;  // slot of stage s's B panel; its A panel is in wrap(cs + 1)
     for (int64_t s = 0; s < nst; ++s) {
       const int cs1 = wrap(cs + 1);
-      // stage s complete: the panels issued after it (from a B panel on) may
+      // stage s complete: what was issued after it (from a B panel on) may
       // still be outstanding
       {
         const int64_t later = issued - 2 * s - 2;
-        wait_panels<NP - 2, PPB_ALL, PPA>(later < NP - 2 ? later : NP - 2);
+        wait_panels<NP - 2, PPB_ALL, PPA_ALL>(later < NP - 2 ? later : NP - 2);
       }
       wait_vmcnt_lgkm0<63>();
       __builtin_amdgcn_s_barrier();
-      if (s > 0) {  // every wave is past stage s-1: its slots take the next panels
-        const int ps = wrap(cs + NP - 2);
-        if (issued < np_all) { issue_panel(issued, ps); ++issued; }
-        if (issued < np_all) { issue_panel(issued, wrap(ps + 1)); ++issued; }
+      // every wave is past stage s-1: its A slot (wrap(cs + 3)) takes A(s+1)
+      if (s > 0 && issued < np_all) {
+        issue_panel(issued, wrap(cs + 3));
+        ++issued;
       }
       const uint8_t* pb = lds + cs * SLOT;
-      const uint8_t* pa = lds + cs1 * SLOT + (wm * WTM) * BK;
-      const float sb = *reinterpret_cast<const float*>(pb + SB_OFF + wave * 16 + ((wn * WTN) >> 7) * 4);
+      const uint8_t* pslot_a = lds + cs1 * SLOT;
+      const uint8_t* pa = pslot_a + (wm * WTM) * BK;
       i32x8 fb[FJ];
 #pragma unroll
       for (int j = 0; j < FJ; ++j) fb[j] = frag16(pb + (wn * WTN + j * 16) * BK);
+      // the B fragments are read before the wait below and the slot's refill
+      __asm__ volatile("" ::: "memory");
+      wait_vmcnt_lgkm0<63>();
+      __builtin_amdgcn_s_barrier();
+      if (issued < np_all) {  // every wave has its B fragments: the B slot takes B(s+2)
+        issue_panel(issued, cs);
+        ++issued;
+      }
+      const float sb = *reinterpret_cast<const float*>(pslot_a + SB_OFF + wave * 16 + ((wn * WTN) >> 7) * 4);
       i32x8 fa = frag16(pa);
 #pragma unroll
       for (int i = 0; i < FI; ++i) {
-        const float sc = *reinterpret_cast<const float*>(pb + SA_OFF + (wm * WTM + i * 16 + r16) * 4) * sb;
+        const float sc =
+            *reinterpret_cast<const float*>(pslot_a + SA_OFF + (wm * WTM + i * 16 + r16) * 4) * sb;
         i32x8 fn;
         if (i + 1 < FI) fn = frag16(pa + (i + 1) * 16 * BK);
         f32x4 t[FJ];
@@ -1084,7 +1112,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
     // B panel
     const int64_t first = np_all < NP ? np_all : NP;
     for (int64_t q = 0; q < first; ++q) issue_panel(q, (int)q);
-    wait_panels<NP - 2, PPB_ALL, PPA>(first - 2);
+    wait_panels<NP - 2, PPB_ALL, PPA_ALL>(first - 2);
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int i = 0; i < TM; ++i) fa[i] = frag_at(lds + SLOT + i * 32 * BK, 0);
@@ -1100,7 +1128,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
     // issued, so panels 2s+4 .. (from a B panel on) may still be outstanding
     {
       const int64_t later = np_all - 2 * s - 4;
-      wait_panels<NP - 4, PPB_ALL, PPA>(later < NP - 4 ? later : NP - 4);
+      wait_panels<NP - 4, PPB_ALL, PPA_ALL>(later < NP - 4 ? later : NP - 4);
     }
     wait_vmcnt_lgkm0<63>();
     __builtin_amdgcn_s_barrier();
@@ -1457,7 +1485,7 @@ hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
 template <int BM, int BN, int WM, int WN, int KIND, int NP, bool MF16 = false>
 hipError_t launch_panel(const GemmArgs& p, hipStream_t stream) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  const size_t lds = (size_t)PanelGeom<BM, BN, WM, WN, KIND, NP>::LDS;
+  const size_t lds = (size_t)PanelGeom<BM, BN, WM, WN, KIND, NP, MF16>::LDS;
   auto kern = gemm_panel_kernel<BM, BN, WM, WN, KIND, NP, MF16>;
   static bool lds_attr_set = false;
   if (lds > 65536 && !lds_attr_set) {
