@@ -122,6 +122,17 @@ def test_linear_launch_counts(lib):
     assert n(7, 1, 4096, 4096, None) == _lib.FP8_ERR_INVALID
 
 
+def test_fused_linear_kill_switch(lib, monkeypatch):
+    n = lib.fp8_linear_launches
+    monkeypatch.setenv("FP8W8A8_FUSED_LINEAR", "0")
+    assert n(_lib.KIND_CHANNELWISE, 1, 4096, 4096, None) == 2
+    assert n(_lib.KIND_BLOCKWISE, 4, 4096, 4096, None) == 2
+    monkeypatch.setenv("FP8W8A8_FUSED_LINEAR", "1")
+    assert n(_lib.KIND_CHANNELWISE, 1, 4096, 4096, None) == 1
+    monkeypatch.delenv("FP8W8A8_FUSED_LINEAR")
+    assert n(_lib.KIND_BLOCKWISE, 4, 4096, 4096, None) == 1
+
+
 def test_workspace_errors(lib):
     cfg = _lib.TileConfig(_lib.VARIANTS["t64x64"], 0, 0, 0, 4, 0)
     # t64x64 runs 512-deep K stages: K = 2048 holds 4 stages, so 4 splits
