@@ -906,12 +906,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
                     sbase + SA_OFF + wave * SA_LANES * 16);
     }
     // weight block scales b_scale[n0 / 128 + l][kt], lanes l < NBLK, one
-    // 16-byte copy per wave (lane 0 always active, as above)
+    // 16-byte copy per wave (lane 0 always active, as above); a block past
+    // the last one (a tile overhanging N) reads the last block instead, its
+    // columns are never stored
     {
       const int64_t kb_all = p.K / 128;
+      const int64_t nb_last = (p.N + 127) / 128 - 1;
+      int64_t nb = (n0 >> 7) + lane;
+      nb = nb < nb_last ? nb : nb_last;
       if (lane < G::NBLK)
-        lds_dma4_s(reinterpret_cast<const uint8_t*>(p.sb + kt),
-                   (uint32_t)(((n0 >> 7) + lane) * kb_all * 4), sbase + SB_OFF + wave * 16);
+        lds_dma4_s(reinterpret_cast<const uint8_t*>(p.sb + kt), (uint32_t)(nb * kb_all * 4),
+                   sbase + SB_OFF + wave * 16);
     }
   };
   auto issue_a = [&](int64_t kt, int slot) {
