@@ -1,0 +1,216 @@
+"""Per-shape measurement of the FP8 linear on one MI355X (gfx950).
+
+For every (kind, N, K, M) of the workloads in ``synth.WORKLOADS`` this times,
+call by call with HIP events on the launch stream (warm-up calls first, then
+the timed ones):
+
+* ``gemm``   -- the scaled GEMM alone (the metric),
+* ``quant``  -- the activation quantizer alone (per token for channelwise,
+  group 128 with row alignment 4 for blockwise),
+* ``linear`` -- the whole linear through ``fp8_linear_*`` (quantizer then GEMM,
+  or the single fused launch where M is small),
+
+cycling through enough distinct buffer sets (activations, codes, scales,
+weights) that at least 1 GiB of weights is touched, four times the 256 MB
+last-level cache, so every call's weight comes from HBM; and ``hot``, the
+same GEMM repeated on one buffer set. Reported per row: medians with p10 and
+p90 over the timed calls, TFLOP/s, algorithmic GB/s (the bytes the method
+must move: codes, weight, scales, bias, output; no padding rows or re-reads)
+and the fractions of HBM (8 TB/s) and dense FP8 MFMA (5.0 PFLOP/s) peak.
+
+Inputs are the seeded synthetic tensors of ``synth`` (no dataset); weights
+are quantized by the library itself, blockwise weight scales are synthetic
+(timing does not depend on their values).
+
+Usage: python -m fp8_w8a8_quantized_token_amd.measure [--workloads small,o_proj,...]
+       [--calls 100] [--warmup 20] [--out FILE]
+"""
+import argparse
+import math
+import sys
+import time
+
+import torch
+
+from . import _lib, ops, synth
+
+PEAK_GBPS = 8000.0
+PEAK_TFLOPS = 5000.0
+ROTATE_BYTES = 1 << 30
+MAX_SETS = 64
+
+
+def gemm_bytes(kind, m, n, k, bias):
+    b = m * k + n * k + 2 * m * n + (2 * n if bias else 0)
+    if kind == "channelwise":
+        return b + 4 * m + 4 * n
+    return b + 4 * m * (k // 128) + 4 * (n // 128) * (k // 128)
+
+
+def quant_bytes(kind, m, k):
+    return 3 * m * k + 4 * m * (1 if kind == "channelwise" else k // 128)
+
+
+def percentile(xs, p):
+    xs = sorted(xs)
+    i = min(len(xs) - 1, max(0, int(round(p / 100.0 * (len(xs) - 1)))))
+    return xs[i]
+
+
+class _Filler:
+    """Device copies queued ahead of the timed calls, so the host has enqueued
+    every call before the GPU reaches the first one: the events then time the
+    kernels, not the host's launch rate."""
+
+    def __init__(self, dev):
+        self.a = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+        self.b = torch.empty_like(self.a)
+
+    def __call__(self, calls):
+        for _ in range(max(4, calls // 3)):  # ~90 us per 256 MiB copy
+            self.b.copy_(self.a)
+
+
+def time_calls(fns, warmup, calls, filler):
+    """Per-call durations (us) of fns cycled round-robin: events around each call."""
+    for i in range(warmup):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    filler(calls)
+    for i, (e0, e1) in enumerate(ev):
+        e0.record()
+        fns[i % len(fns)]()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+
+
+class ShapeBuffers:
+    """Weight copies of one (kind, N, K), enough of them to cover >= 1 GiB."""
+
+    def __init__(self, cfg, kind, n, k, with_bias, dev):
+        self.kind, self.n, self.k, self.dev = kind, n, k, dev
+        self.sets = max(2, min(MAX_SETS, math.ceil(ROTATE_BYTES / (n * k))))
+        w = synth.weights(f"measure/{cfg}", n, k).to(torch.bfloat16).to(dev)
+        if kind == "channelwise":
+            wq, ws = ops.quant_per_token(w)
+        else:
+            wq, _ = ops.quant_per_token_group(w, 128, row_alignment=1)
+            wq = wq.contiguous()
+            ws = synth.positive_scales(f"measure/{cfg}/{n}/{k}", (n // 128, k // 128)).to(dev)
+        del w
+        self.w = [(wq.clone(), ws.clone()) for _ in range(self.sets)]
+        self.bias = synth.bias(f"measure/{cfg}", n).to(dev) if with_bias else None
+
+
+def measure_m(buf, cfg, m, outliers, warmup, calls, filler):
+    kind, n, k, dev, sets = buf.kind, buf.n, buf.k, buf.dev, buf.sets
+    x0 = synth.activations(f"measure/{cfg}", m, k, outlier_frac=outliers).to(dev)
+    m_pad = ops.padded_rows(m, 4) if kind == "blockwise" else m
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    xs, qs, ss = [], [], []
+    for _ in range(sets):
+        xs.append(x0.clone())
+        qs.append(torch.empty((m_pad, k), dtype=torch.uint8, device=dev))
+        ss.append(torch.empty((m,), dtype=torch.float32, device=dev) if kind == "channelwise"
+                  else torch.empty((k // 128, m_pad), dtype=torch.float32, device=dev))
+    quant, gemm, linear = [], [], []
+    for i in range(sets):
+        wq, ws = buf.w[i]
+        if kind == "channelwise":
+            quant.append(ops.prepare("quant_per_token", xs[i], out=qs[i], scale=ss[i]))
+            quant[-1]()
+            gemm.append(ops.prepare("scaled_mm_channelwise", qs[i], wq, ss[i], ws, bias=buf.bias,
+                                    out=out))
+            linear.append(ops.prepare("linear_channelwise", xs[i], wq, ws, bias=buf.bias, out=out,
+                                      q=qs[i], scale=ss[i]))
+        else:
+            quant.append(ops.prepare("quant_per_token_group", xs[i], 128, row_alignment=4,
+                                     out=qs[i], scale_storage=ss[i]))
+            quant[-1]()
+            gemm.append(ops.prepare("scaled_mm_blockwise", qs[i], wq, ss[i].transpose(0, 1), ws,
+                                    bias=buf.bias, m=m, out=out))
+            linear.append(ops.prepare("linear_blockwise", xs[i], wq, ws, bias=buf.bias,
+                                      row_alignment=4, out=out, q=qs[i], scale=ss[i]))
+    torch.cuda.synchronize()
+    kid = ops.KIND_CHANNELWISE if kind == "channelwise" else ops.KIND_BLOCKWISE
+    cfg_d, hit = ops.tile_config(kid, n, k, m)
+    res = {
+        "gemm": time_calls(gemm, warmup, calls, filler),
+        "quant": time_calls(quant, warmup, calls, filler),
+        "linear": time_calls(linear, warmup, calls, filler),
+        "hot": time_calls(gemm[:1], warmup, calls, filler),
+        "rot_gib": min(sets, calls) * n * k / (1 << 30),
+        "variant": cfg_d["variant"], "split_k": cfg_d["split_k"], "table": hit,
+        "launches": ops.linear_launches(kid, m, n, k),
+    }
+    return res
+
+
+HEADER = ("| workload | kind | N×K | M | tile config | weight GiB rotated | GEMM µs p50 (p10–p90) | "
+          "TFLOP/s | GB/s | frac HBM | frac MFMA | quant µs p50 (GB/s) | linear µs p50 (launches) | "
+          "hot GEMM µs p50 |")
+
+
+def row(cfg, kind, n, k, m, r, bias):
+    g = r["gemm"]
+    p50 = percentile(g, 50)
+    qp50 = percentile(r["quant"], 50)
+    fl = 2 * m * n * k
+    by = gemm_bytes(kind, m, n, k, bias)
+    tf = fl / p50 / 1e6
+    gb = by / p50 / 1e3
+    conf = f"{r['variant']}" + (f" sk{r['split_k']}" if r["split_k"] > 1 else "") + \
+        (" (table)" if r["table"] else "")
+    return (f"| {cfg} | {kind} | {n}×{k} | {m} | `{conf}` | {r['rot_gib']:.2f} | "
+            f"{p50:.1f} ({percentile(g, 10):.1f}–"
+            f"{percentile(g, 90):.1f}) | {tf:.0f} | {gb:.0f} | {gb / PEAK_GBPS:.2f} | "
+            f"{tf / PEAK_TFLOPS:.3f} | {qp50:.1f} ({quant_bytes(kind, m, k) / qp50 / 1e3:.0f} GB/s) | "
+            f"{percentile(r['linear'], 50):.1f} ({r['launches']}) | {percentile(r['hot'], 50):.1f} |")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workloads", default=",".join(synth.WORKLOADS))
+    ap.add_argument("--calls", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--out", default="")
+    args = ap.parse_args(argv)
+    _lib.load()
+    dev = torch.device("cuda:0")
+    want = args.workloads.split(",")
+    filler = _Filler(dev)
+    lines = [HEADER, "|" + "---|" * 14]
+    print(HEADER, flush=True)
+    print(lines[1], flush=True)
+    t0 = time.time()
+    floor = percentile(time_calls([lambda: None], args.warmup, args.calls, filler), 50)
+    for cfg in want:
+        w = synth.WORKLOADS[cfg]
+        kind, with_bias = w["kind"], w["bias"]
+        for n, k in w["shapes"]:
+            buf = ShapeBuffers(cfg, kind, n, k, with_bias, dev)
+            for m in w["ms"]:
+                r = measure_m(buf, cfg, m, w["outliers"], args.warmup, args.calls, filler)
+                line = row(cfg, kind, n, k, m, r, with_bias)
+                lines.append(line)
+                print(line, flush=True)
+                torch.cuda.empty_cache()
+            del buf
+            torch.cuda.empty_cache()
+    note = (f"\n{args.calls} timed calls after {args.warmup} warm-up calls per mode; HIP events "
+            f"around each call, all calls queued behind device copies; up to {MAX_SETS} weight "
+            f"sets rotated (GiB column: distinct weight bytes the timed calls touch; hot: one "
+            f"set repeated). An event pair around no launch measures {floor:.1f} us (p50). "
+            f"{time.time() - t0:.0f} s.")
+    print(note, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write("\n".join(lines) + "\n" + note + "\n")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
