@@ -41,17 +41,23 @@ def candidates(kind, m, n, k):
     the LDS-DMA tiles where their K condition holds (64-byte stages:
     channelwise, K % 64 == 0; panel rings: K % 128 == 0); the blockwise
     256x256 register-staged tiles run out of registers and are left out."""
-    if m <= 32:
-        return [("skinny", 1)]
-    c = []
     k128 = k % 128 == 0
+    if m <= 32:
+        # the skinny kernel re-reads all M activation rows per 16 weight rows;
+        # from M = 8 the 32- and 64-wide deep-ring tiles can win on large N
+        c = [("skinny", 1)]
+        if m >= 8 and k128:
+            c += [("t32x32deep", 1), ("t32x32deep", 2), ("t64x32deep", 1), ("t64x32deep", 2),
+                  ("t64x64deep", 1), ("t64x64deep", 2), ("t64x64panel", 1)]
+        return c
+    c = []
     if m <= 1024:
         c += [("t64x64", 1), ("t128x64k256", 1), ("t64x128k256", 1), ("t128x128k256", 1)]
         if k128:
             c += [("t64x64panel", 1), ("t64x64panel", 2), ("t128x64panel", 1),
                   ("t64x64deep", 1), ("t64x64deep", 2), ("t128x64deep", 1)]
             if m <= 256:
-                c += [("t32x32deep", 1), ("t64x32deep", 1)]
+                c += [("t32x32deep", 1), ("t32x32deep", 2), ("t64x32deep", 1), ("t64x32deep", 2)]
     if m >= 256:
         c += [("t128x128", 1), ("t128x128k256", 1), ("t256x128w8", 1)]
         if kind == "channelwise" and k % 64 == 0:

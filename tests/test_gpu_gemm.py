@@ -49,6 +49,11 @@ CW_CASES = (
        for m in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192)]
     + [("qwen3_8b", m, n, k, 0.0, True) for n, k in ((6144, 4096), (4096, 12288), (24576, 4096))
        for m in (1, 64, 512, 8192)]
+    # M between the skinny kernel and the 64-row tiles: the tile table sends
+    # some of these to the 32- and 64-wide deep-ring tiles
+    + [("qwen3_8b", m, n, k, 0.0, True) for n, k in ((6144, 4096), (4096, 12288), (24576, 4096))
+       for m in (8, 21, 32)]
+    + [("small", m, 256, 512, 0.0, False) for m in (8, 32, 100)]
 )
 
 
@@ -81,7 +86,8 @@ def _blockwise_case(wl, m, n, k, config=None, with_bias=False, poison=False, row
 
 
 BW_CASES = ([("block_7168", m, 7168, 7168) for m in (1, 2, 3, 5, 7, 13, 31, 64, 256)]
-            + [("block_moe", m, n, k) for n, k in ((3072, 4096), (4096, 1536)) for m in (1, 4, 16, 64, 4096)])
+            + [("block_moe", m, n, k) for n, k in ((3072, 4096), (4096, 1536)) for m in (1, 4, 16, 64, 4096)]
+            + [("block_7168", m, 7168, 7168) for m in (16, 32, 48)])
 
 
 @pytest.mark.parametrize("wl,m,n,k", BW_CASES, ids=[f"{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in BW_CASES])
