@@ -25,13 +25,24 @@ notes with its reason): OCP E4M3 with saturation at +-448, round to nearest
 even, scale = max(absmax, eps) / 448 in fp32, element codes from a true fp32
 division x / scale, signed zero kept, fp64 GEMM references.
 
+Variants the pages name without a body, with the readings taken: the
+quantizer's ``fuse_silu_and_mul`` flag (input [gate | up], quantized row
+bf16(silu(gate) * up)), its ``scale_ue8m0`` flag (each fp32 scale rounded up
+to a power of two), and a static per-tensor quantization with a given scale
+(codes only) -- see ``activation.py`` and ``quant.py``.
+
 Parity unpinned: behaviour on non-finite inputs (Inf/NaN), which the pages do
 not define; every workload here is finite.
 """
 
 from .e4m3 import E4M3_MAX, decode, decode_table, encode  # noqa: F401
+from .activation import bf16_round_exact, silu_mul_bf16  # noqa: F401
 from .quant import (  # noqa: F401
     padded_rows,
+    pow2_ceil,
+    quant_static,
+    silu_mul_quant_per_token,
+    silu_mul_quant_per_token_group,
     quant_per_token,
     quant_per_token_group,
     quant_weight_blockwise,

@@ -23,8 +23,11 @@ GEMM of the PR 34331 digest but is produced off-page there, is the same
 operation with a single group spanning the whole row.
 """
 
+import math
+
 import numpy as np
 
+from .activation import silu_mul_bf16
 from .e4m3 import E4M3_MAX, encode
 
 F32 = np.float32
@@ -37,11 +40,26 @@ def padded_rows(m: int, row_alignment: int) -> int:
     return -(-m // row_alignment) * row_alignment
 
 
-def quant_per_token_group(x, group_size: int, eps: float = 1e-10):
+def pow2_ceil(s) -> np.float32:
+    """The smallest power of two >= s (s a positive finite fp32 value).
+
+    UE8M0 scales (the ``scale_ue8m0`` flag of the group quantizer's kernel call,
+    PR 27896 digest, "Key source excerpts"; the digest prints no body for it).
+    Reading taken: the fp32 scale of the plain method is rounded UP to a power
+    of two, so x / scale still lies within +-448 and the scale is an 8-bit
+    exponent with no mantissa.
+    """
+    mant, expo = math.frexp(float(s))  # s = mant * 2^expo, 0.5 <= mant < 1
+    return F32(s) if mant == 0.5 else F32(math.ldexp(1.0, expo))
+
+
+def quant_per_token_group(x, group_size: int, eps: float = 1e-10, scale_ue8m0: bool = False):
     """Quantize rows of x group by group.
 
     x: array-like [M, K] of bf16 values (any dtype that holds them exactly;
     converted to fp32, which is exact for bf16).
+    scale_ue8m0: round every scale up to a power of two (see pow2_ceil) before
+    the codes are formed.
     Returns (codes uint8 [M, K], scales float32 [M, K // group_size]).
     """
     xf = np.asarray(x, dtype=F32)
@@ -61,6 +79,8 @@ def quant_per_token_group(x, group_size: int, eps: float = 1e-10):
             amax = np.max(np.abs(seg)) if group_size > 0 else F32(0)
             amax = max(F32(amax), eps32)
             s = F32(F32(amax) / fmax)
+            if scale_ue8m0:
+                s = pow2_ceil(s)
             scales[row, g] = s
             ratio = (seg / s).astype(F32)  # IEEE fp32 division per element
             codes[row, g * group_size:(g + 1) * group_size] = encode(ratio)
@@ -72,6 +92,41 @@ def quant_per_token(x, eps: float = 1e-10):
     xf = np.asarray(x, dtype=F32)
     codes, scales = quant_per_token_group(xf, xf.shape[1], eps)
     return codes, scales[:, 0].copy()
+
+
+def silu_mul_quant_per_token_group(x, group_size: int, eps: float = 1e-10,
+                                   scale_ue8m0: bool = False):
+    """The group quantizer with SiLU-and-mul fused in front (``fuse_silu_and_mul``
+    in the quantizer's kernel call, PR 27896 digest, "Key source excerpts"):
+    x is [M, 2K] = [gate | up]; the quantized row is bf16(silu(gate) * up).
+    Returns (codes uint8 [M, K], scales float32 [M, K // group_size])."""
+    return quant_per_token_group(silu_mul_bf16(x), group_size, eps, scale_ue8m0)
+
+
+def silu_mul_quant_per_token(x, eps: float = 1e-10):
+    """Per-token form of the above: (codes uint8 [M, K], scales float32 [M])."""
+    y = silu_mul_bf16(x)
+    codes, scales = quant_per_token_group(y, y.shape[1], eps)
+    return codes, scales[:, 0].copy()
+
+
+def quant_static(x, scale):
+    """Static per-tensor quantization with a given fp32 scale.
+
+    The PR 31340 digest ("Fix FP8 Triton dtype selection on A100",
+    "Implementation" and "Key files") names a static FP8 quantization kernel and
+    the ModelOpt FP8 linear's precomputed ``input_scale``, without a body.
+    Reading taken: the same element step as the dynamic quantizer with the scale
+    supplied instead of derived, code = E4M3_RNE(clamp(fp32(x / scale), +-448)),
+    IEEE fp32 division; no scale is produced.
+    x: [M, K] bf16 values; scale: one positive finite fp32 value.
+    Returns codes uint8 [M, K].
+    """
+    xf = np.asarray(x, dtype=F32)
+    s = F32(scale)
+    if not (np.isfinite(s) and s > 0):
+        raise ValueError("scale must be a positive finite fp32 value")
+    return encode((xf / s).astype(F32))
 
 
 def scales_col_major(scales, m_pad: int) -> np.ndarray:

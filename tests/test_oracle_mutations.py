@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle.activation as activation
 import oracle.e4m3 as e4m3
 import oracle.gemm as gemm
 import oracle.quant as quant
@@ -15,6 +16,7 @@ import oracle.quant as quant
 import test_oracle_e4m3 as pins_codec
 import test_oracle_gemm as pins_gemm
 import test_oracle_quant as pins_quant
+import test_oracle_quant_variants as pins_variants
 
 _orig_encode = e4m3.encode
 
@@ -110,6 +112,39 @@ def _decode_table_subnormal_off():
 
 _orig_mm_cw = gemm.scaled_mm_channelwise
 
+
+def _silu_mul_halves_swapped(x):
+    xf = np.asarray(x, np.float64)
+    k = xf.shape[1] // 2
+    up, gate = xf[:, :k], xf[:, k:]
+    with np.errstate(over="ignore"):
+        return activation.bf16_round_exact(gate / (1.0 + np.exp(-gate)) * up).astype(np.float32)
+
+
+def _silu_mul_no_bf16_rounding(x):
+    xf = np.asarray(x, np.float64)
+    k = xf.shape[1] // 2
+    gate, up = xf[:, :k], xf[:, k:]
+    with np.errstate(over="ignore"):
+        return (gate / (1.0 + np.exp(-gate)) * up).astype(np.float32)
+
+
+def _bf16_round_via_fp32(v):
+    v32 = np.asarray(v, np.float64).astype(np.float32)
+    mant, expo = np.frexp(v32.astype(np.float64))
+    return np.ldexp(np.rint(mant * 256.0) / 256.0, expo)
+
+
+def _pow2_floor(s):
+    import math
+    mant, expo = math.frexp(float(s))
+    return np.float32(s) if mant == 0.5 else np.float32(math.ldexp(1.0, expo - 1))
+
+
+def _quant_static_reciprocal(x, scale):
+    s = np.float32(scale)
+    return e4m3.encode((np.asarray(x, np.float32) * (np.float32(1) / s)).astype(np.float32))
+
 MUTATIONS = [
     ("encode ties away from zero", [(e4m3, "encode", _encode_ties_away), (oracle, "encode", _encode_ties_away),
                                    (quant, "encode", _encode_ties_away)],
@@ -133,6 +168,18 @@ MUTATIONS = [
      pins_quant.test_scales_col_major_layout),
     ("decode subnormal step wrong", [(oracle, "decode_table", _decode_table_subnormal_off)],
      pins_codec.test_landmark_values),
+    ("silu applied to the up half", [(oracle, "silu_mul_bf16", _silu_mul_halves_swapped),
+                                     (quant, "silu_mul_bf16", _silu_mul_halves_swapped)],
+     pins_variants.test_worked_examples),
+    ("silu product not rounded to bf16", [(oracle, "silu_mul_bf16", _silu_mul_no_bf16_rounding),
+                                          (quant, "silu_mul_bf16", _silu_mul_no_bf16_rounding)],
+     pins_variants.test_worked_examples),
+    ("bf16 rounding through fp32", [(oracle, "bf16_round_exact", _bf16_round_via_fp32)],
+     pins_variants.test_bf16_round_exact_between_fp32_values),
+    ("ue8m0 rounds the scale down", [(quant, "pow2_ceil", _pow2_floor)],
+     pins_variants.test_worked_examples),
+    ("static quant multiplies by reciprocal", [(oracle, "quant_static", _quant_static_reciprocal)],
+     pins_variants.test_worked_examples),
 ]
 
 
