@@ -23,6 +23,9 @@ FP8_ERR_HIP = -4
 KIND_CHANNELWISE = 0
 KIND_BLOCKWISE = 1
 
+QUANT_FUSE_SILU_MUL = 1
+QUANT_SCALE_UE8M0 = 2
+
 VARIANTS = {"default": -1, "skinny": 0, "t64x64": 1, "t128x128": 2, "t256x128": 3, "t256x256": 4,
             "t256x256w8": 5, "t256x128w8": 6, "t128x128w8": 7, "t128x64k256": 8,
             "t64x128k256": 9, "t128x128k256": 10, "t256x256dma": 11, "t256x128dma": 12,
@@ -49,6 +52,11 @@ SIGNATURES = {
     "fp8_quant_per_token": (c_i32, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_f32, c_vp]),
     "fp8_quant_per_token_group": (c_i32, [c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_i64,
                                           c_vp, c_f32, c_vp]),
+    "fp8_quant_per_token_ex": (c_i32, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_f32, c_i32,
+                                       c_vp]),
+    "fp8_quant_per_token_group_ex": (c_i32, [c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_i64,
+                                             c_vp, c_f32, c_i32, c_vp]),
+    "fp8_quant_static": (c_i32, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp]),
     "fp8_scaled_mm_channelwise": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
                                           c_i64, c_i64, c_i64, c_vp, c_size, c_vp]),
     "fp8_scaled_mm_channelwise_ex": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64,

@@ -39,18 +39,26 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
-// Common checks of the quantizer arguments.
-int check_quant(const char* fn, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+// Common checks of the quantizer arguments; every row of x holds xcols values
+// (K, or 2K with SiLU-and-mul).
+int check_quant(const char* fn, const uint16_t* x, int64_t M, int64_t K, int64_t xcols, int64_t ldx,
                 const uint8_t* q, int64_t ldq, const float* scale, float eps) {
   if (M < 0 || K < 0) return fail(FP8_ERR_INVALID, "%s: negative size (M=%lld K=%lld)", fn, (long long)M, (long long)K);
   if (M == 0) return FP8_OK;
   if (!x || !q || !scale) return fail(FP8_ERR_INVALID, "%s: null pointer", fn);
   if (K == 0 || K % 16 != 0) return fail(FP8_ERR_INVALID, "%s: K=%lld must be a positive multiple of 16", fn, (long long)K);
-  if (ldx < K || ldq < K) return fail(FP8_ERR_INVALID, "%s: leading dimension smaller than K", fn);
+  if (ldx < xcols || ldq < K) return fail(FP8_ERR_INVALID, "%s: leading dimension too small", fn);
   if (ldx % 8 != 0 || ldq % 16 != 0 || !aligned(x, 16) || !aligned(q, 16))
     return fail(FP8_ERR_INVALID, "%s: rows of x and q must be 16-byte aligned", fn);
   if (!aligned(scale, 4)) return fail(FP8_ERR_INVALID, "%s: scale must be 4-byte aligned", fn);
   if (!(eps >= 0.0f)) return fail(FP8_ERR_INVALID, "%s: eps must be >= 0", fn);
+  return FP8_OK;
+}
+
+// Flag check of the quantizers: known bits only.
+int check_quant_flags(const char* fn, int32_t flags) {
+  if (flags & ~(FP8_QUANT_FUSE_SILU_MUL | FP8_QUANT_SCALE_UE8M0))
+    return fail(FP8_ERR_INVALID, "%s: unknown flags 0x%x", fn, (unsigned)flags);
   return FP8_OK;
 }
 
@@ -150,7 +158,7 @@ int run_linear(const char* fn, int kind, const uint16_t* x, const uint8_t* b, co
                hipStream_t stream) {
   const bool bw = kind == FP8_KIND_BLOCKWISE;
   if (bw && row_alignment < 1) return fail(FP8_ERR_INVALID, "%s: row_alignment must be >= 1", fn);
-  int st = check_quant(fn, x, M, K, ldx, q, ldq, a_scale, eps);
+  int st = check_quant(fn, x, M, K, K, ldx, q, ldq, a_scale, eps);
   if (st) return st;
   st = check_gemm(fn, q, b, a_scale, b_scale, bias, out, M, N, K, ldq, ldb, ldc);
   if (st) return st;
@@ -171,8 +179,8 @@ int run_linear(const char* fn, int kind, const uint16_t* x, const uint8_t* b, co
     const QuantArgs qa{x, ldx, q, ldq, a_scale, m_pad, eps};
     return hip_status(launch_linear_fused(kind, p, qa, stream), fn);
   }
-  const hipError_t e = bw ? launch_quant_per_token_group(x, M, K, ldx, 128, m_pad, q, ldq, a_scale, eps, stream)
-                          : launch_quant_per_token(x, M, K, ldx, q, ldq, a_scale, eps, stream);
+  const hipError_t e = bw ? launch_quant_per_token_group(x, M, K, ldx, 128, m_pad, q, ldq, a_scale, eps, 0, stream)
+                          : launch_quant_per_token(x, M, K, ldx, q, ldq, a_scale, eps, 0, stream);
   st = hip_status(e, fn);
   if (st) return st;
   return run_gemm(fn, kind, q, b, a_scale, m_pad, b_scale, bias, out, M, N, K, ldq, ldb, ldc, ws,
@@ -188,18 +196,27 @@ int64_t fp8_padded_rows(int64_t M, int32_t row_alignment) {
   return (M + row_alignment - 1) / row_alignment * row_alignment;
 }
 
-int fp8_quant_per_token(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
-                        int64_t ldq, float* scale, float eps, hipStream_t stream) {
-  int st = check_quant("fp8_quant_per_token", x, M, K, ldx, q, ldq, scale, eps);
+int fp8_quant_per_token_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                           int64_t ldq, float* scale, float eps, int32_t flags, hipStream_t stream) {
+  const char* fn = "fp8_quant_per_token";
+  int st = check_quant_flags(fn, flags);
+  if (st) return st;
+  st = check_quant(fn, x, M, K, (flags & FP8_QUANT_FUSE_SILU_MUL) ? 2 * K : K, ldx, q, ldq, scale,
+                   eps);
   if (st) return st;
   if (M == 0) return ok();
-  return hip_status(launch_quant_per_token(x, M, K, ldx, q, ldq, scale, eps, stream),
-                    "fp8_quant_per_token");
+  return hip_status(launch_quant_per_token(x, M, K, ldx, q, ldq, scale, eps, flags, stream), fn);
 }
 
-int fp8_quant_per_token_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                              int32_t group_size, int32_t row_alignment, uint8_t* q, int64_t ldq,
-                              float* scale, float eps, hipStream_t stream) {
+int fp8_quant_per_token(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                        int64_t ldq, float* scale, float eps, hipStream_t stream) {
+  return fp8_quant_per_token_ex(x, M, K, ldx, q, ldq, scale, eps, 0, stream);
+}
+
+int fp8_quant_per_token_group_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                 int32_t group_size, int32_t row_alignment, uint8_t* q,
+                                 int64_t ldq, float* scale, float eps, int32_t flags,
+                                 hipStream_t stream) {
   const char* fn = "fp8_quant_per_token_group";
   if (row_alignment < 1) return fail(FP8_ERR_INVALID, "%s: row_alignment must be >= 1", fn);
   if (group_size <= 0) return fail(FP8_ERR_INVALID, "%s: group_size must be positive", fn);
@@ -207,13 +224,32 @@ int fp8_quant_per_token_group(const uint16_t* x, int64_t M, int64_t K, int64_t l
     return fail(FP8_ERR_INVALID, "%s: K=%lld must be divisible by group_size=%d", fn, (long long)K, group_size);
   if (!(group_size == 16 || group_size == 32 || group_size == 64 || group_size == 128))
     return fail(FP8_ERR_UNSUPPORTED, "%s: group_size %d not in {16, 32, 64, 128}", fn, group_size);
-  int st = check_quant(fn, x, M, K, ldx, q, ldq, scale, eps);
+  int st = check_quant_flags(fn, flags);
+  if (st) return st;
+  st = check_quant(fn, x, M, K, (flags & FP8_QUANT_FUSE_SILU_MUL) ? 2 * K : K, ldx, q, ldq, scale,
+                   eps);
   if (st) return st;
   if (M == 0) return ok();
   const int64_t m_pad = fp8_padded_rows(M, row_alignment);
   return hip_status(launch_quant_per_token_group(x, M, K, ldx, group_size, m_pad, q, ldq, scale,
-                                                 eps, stream),
+                                                 eps, flags, stream),
                     fn);
+}
+
+int fp8_quant_per_token_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                              int32_t group_size, int32_t row_alignment, uint8_t* q, int64_t ldq,
+                              float* scale, float eps, hipStream_t stream) {
+  return fp8_quant_per_token_group_ex(x, M, K, ldx, group_size, row_alignment, q, ldq, scale, eps,
+                                      0, stream);
+}
+
+int fp8_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const float* scale,
+                     uint8_t* q, int64_t ldq, hipStream_t stream) {
+  const char* fn = "fp8_quant_static";
+  int st = check_quant(fn, x, M, K, K, ldx, q, ldq, scale, 0.0f);
+  if (st) return st;
+  if (M == 0) return ok();
+  return hip_status(launch_quant_static(x, M, K, ldx, scale, q, ldq, stream), fn);
 }
 
 int fp8_scaled_mm_channelwise_ex(const uint8_t* a, const uint8_t* b, const float* a_scale,

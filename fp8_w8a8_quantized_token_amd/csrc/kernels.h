@@ -6,13 +6,21 @@
 
 namespace fp8w8a8 {
 
+// Quantizer flags (the values of FP8_QUANT_* in the C header). With
+// kQuantSiluMul the input rows hold 2K values [gate | up] and K is the width
+// of the quantized row.
+enum QuantFlag { kQuantSiluMul = 1, kQuantUe8m0 = 2 };
+
 hipError_t launch_quant_per_token(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                                  uint8_t* q, int64_t ldq, float* scale, float eps,
+                                  uint8_t* q, int64_t ldq, float* scale, float eps, int flags,
                                   hipStream_t stream);
 
 hipError_t launch_quant_per_token_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                         int group_size, int64_t m_pad, uint8_t* q, int64_t ldq,
-                                        float* scale, float eps, hipStream_t stream);
+                                        float* scale, float eps, int flags, hipStream_t stream);
+
+hipError_t launch_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                               const float* scale, uint8_t* q, int64_t ldq, hipStream_t stream);
 
 enum GemmKind { kChannelwise = 0, kBlockwise = 1 };
 

@@ -8,14 +8,101 @@
 // rows at or beyond M untouched. Per-token quantization is the same with one
 // group per row.
 //
-// Both kernels are HBM-bound streaming kernels: 2 bytes read and 1 byte
-// written per element (plus 4 bytes per group). Every thread owns 16 elements
-// (two 16-byte loads, one 16-byte store) so global accesses are 128-bit and
-// contiguous across lanes.
+// All kernels here are HBM-bound streaming kernels: 2 bytes read (4 with
+// SiLU-and-mul) and 1 byte written per element, plus 4 bytes per group. Every
+// thread owns 16 elements (16-byte loads, one 16-byte store) so global
+// accesses are 128-bit and contiguous across lanes.
 #include "common.h"
 #include "kernels.h"
 
 namespace fp8w8a8 {
+
+// ---------------------------------------------------------------------------
+// Variants named by the quantizer's kernel call on the same page
+// (fuse_silu_and_mul, scale_ue8m0 flags) and by the A100 dtype page (a static
+// FP8 quantization kernel), whose bodies the pages do not show. Readings:
+//  * SiLU-and-mul: the input row is [gate | up] (2K values); the row that is
+//    quantized is y = bf16(silu(gate) * up), silu(g) = g / (1 + e^-g), so the
+//    fused call equals SiLU-and-mul (bf16 out) followed by the quantizer.
+//  * UE8M0: each fp32 scale is rounded up to a power of two.
+//  * Static: a given fp32 scale, codes E4M3(clamp(x / s)), no scale written.
+// ---------------------------------------------------------------------------
+
+// Smallest power of two >= s, for a positive normal fp32 s.
+__device__ __forceinline__ float pow2_ceil(float s) {
+  uint32_t b = __float_as_uint(s);
+  if (b & 0x007FFFFFu) b = (b & 0xFF800000u) + 0x00800000u;
+  return __uint_as_float(b);
+}
+
+// Nearest bf16 (ties to even) of a double, without double rounding: the
+// conversion to fp32 is made round-to-odd (inexact results get their last bit
+// set after truncation), which keeps 16 guard bits for the bf16 rounding.
+__device__ __forceinline__ uint32_t bf16_of_f64(double d) {
+  const float f = (float)d;  // round to nearest
+  uint32_t b = __float_as_uint(f);
+  const double back = (double)f;
+  if (back != d) {
+    if (fabs(back) > fabs(d)) b -= 1u;  // rounded away from zero: step back
+    b |= 1u;
+  }
+  return f32_to_bf16(__uint_as_float(b));
+}
+
+// bf16 bits of silu(g) * u, correctly rounded. The fp32 evaluation (expf,
+// reciprocal, two products) is within 12 fp32 ulps of the exact value (expf
+// within 3 ulps, each other step within 1), so unless it lies within 32 ulps
+// of a bf16 rounding midpoint (low 16 bits near 0x8000) its bf16 rounding is
+// that of the exact value. The rest (about 1 value in 1000 on normal data),
+// and gates below -80 where e^-g nears fp32 overflow, are evaluated in fp64.
+__device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
+  const float t = expf(-g);
+  const float y = (g * __builtin_amdgcn_rcpf(1.0f + t)) * u;
+  const uint32_t low = __float_as_uint(y) & 0xFFFFu;
+  if (g >= -80.0f && (low - 0x7FE0u) > 0x40u) return f32_to_bf16(y);
+  const double gd = (double)g;
+  return bf16_of_f64(gd / (1.0 + exp(-gd)) * (double)u);
+}
+
+// 8 gate and 8 up bf16 values -> 8 bf16 values of silu(gate) * up.
+__device__ __forceinline__ uint4 silu_mul8(const uint4& g, const uint4& u) {
+  const uint32_t gp[4] = {g.x, g.y, g.z, g.w};
+  const uint32_t up[4] = {u.x, u.y, u.z, u.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = silu_mul_bf16(bf16_to_f32(gp[i] & 0xffffu), bf16_to_f32(up[i] & 0xffffu));
+    const uint32_t hi = silu_mul_bf16(bf16_to_f32(gp[i] >> 16), bf16_to_f32(up[i] >> 16));
+    o[i] = lo | (hi << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// The 16 values of unit u of a row as bf16: the input itself, or (SiLU-and-mul)
+// silu(gate) * up from the two halves of a 2K-wide row.
+template <int FLAGS>
+__device__ __forceinline__ void load_unit(const uint16_t* xr, int64_t K, int64_t u, uint4& v0,
+                                          uint4& v1) {
+  const uint4* src = reinterpret_cast<const uint4*>(xr + u * 16);
+  if constexpr ((FLAGS & kQuantSiluMul) != 0) {
+    const uint4* up = reinterpret_cast<const uint4*>(xr + K + u * 16);
+    const uint4 g0 = load16_nt(src), g1 = load16_nt(src + 1);
+    const uint4 u0 = load16_nt(up), u1 = load16_nt(up + 1);
+    v0 = silu_mul8(g0, u0);
+    v1 = silu_mul8(g1, u1);
+  } else {
+    v0 = load16_nt(src);
+    v1 = load16_nt(src + 1);
+  }
+}
+
+// Scale of a group from its absmax: fp32 (absmax floored at eps) / 448,
+// rounded up to a power of two for UE8M0.
+template <int FLAGS>
+__device__ __forceinline__ float group_scale(float amax, float eps) {
+  const float s = fmaxf(amax, eps) / kE4M3Max;
+  return (FLAGS & kQuantUe8m0) != 0 ? pow2_ceil(s) : s;
+}
 
 // ---------------------------------------------------------------------------
 // Per-token: one workgroup per row; the row's 16-element units are spread over
@@ -23,7 +110,7 @@ namespace fp8w8a8 {
 // absmax is reduced wave-wise then across waves through LDS, and the codes are
 // produced from the registers, so the row is read from HBM once.
 // ---------------------------------------------------------------------------
-template <int UNITS>
+template <int UNITS, int FLAGS>
 __global__ __launch_bounds__(256) void quant_per_token_kernel(
     const uint16_t* __restrict__ x, int64_t K, int64_t ldx, uint8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale, float eps) {
@@ -40,9 +127,7 @@ __global__ __launch_bounds__(256) void quant_per_token_kernel(
   for (int i = 0; i < UNITS; ++i) {
     const int u = threadIdx.x + i * nthr;
     if (u < units) {
-      const uint4* src = reinterpret_cast<const uint4*>(xr + (int64_t)u * 16);
-      v[i][0] = load16_nt(src);
-      v[i][1] = load16_nt(src + 1);
+      load_unit<FLAGS>(xr, K, u, v[i][0], v[i][1]);
       amax = fmaxf(amax, fmaxf(absmax8_bf16(v[i][0]), absmax8_bf16(v[i][1])));
     }
   }
@@ -52,7 +137,7 @@ __global__ __launch_bounds__(256) void quant_per_token_kernel(
   __syncthreads();
   float m = wave_part[0];
   for (int w = 1; w < (nthr >> 6); ++w) m = fmaxf(m, wave_part[w]);
-  const float s = fmaxf(m, eps) / kE4M3Max;
+  const float s = group_scale<FLAGS>(m, eps);
   const float y = 1.0f / s;
   if (threadIdx.x == 0) scale[row] = s;
 #pragma unroll
@@ -67,7 +152,8 @@ __global__ __launch_bounds__(256) void quant_per_token_kernel(
 }
 
 // Rows longer than 256 threads x 8 units: two passes over the row (the second
-// pass re-reads it from cache).
+// pass re-reads it from cache; SiLU-and-mul is evaluated again, to the same bits).
+template <int FLAGS>
 __global__ __launch_bounds__(256) void quant_per_token_long_kernel(
     const uint16_t* __restrict__ x, int64_t K, int64_t ldx, uint8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale, float eps) {
@@ -78,21 +164,23 @@ __global__ __launch_bounds__(256) void quant_per_token_long_kernel(
   const int64_t units = K >> 4;
   float amax = 0.0f;
   for (int64_t u = threadIdx.x; u < units; u += blockDim.x) {
-    const uint4* src = reinterpret_cast<const uint4*>(xr + u * 16);
-    amax = fmaxf(amax, fmaxf(absmax8_bf16(src[0]), absmax8_bf16(src[1])));
+    uint4 v0, v1;
+    load_unit<FLAGS>(xr, K, u, v0, v1);
+    amax = fmaxf(amax, fmaxf(absmax8_bf16(v0), absmax8_bf16(v1)));
   }
   amax = wave_max(amax);
   if ((threadIdx.x & 63) == 0) wave_part[threadIdx.x >> 6] = amax;
   __syncthreads();
   float m = wave_part[0];
   for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, wave_part[w]);
-  const float s = fmaxf(m, eps) / kE4M3Max;
+  const float s = group_scale<FLAGS>(m, eps);
   const float y = 1.0f / s;
   if (threadIdx.x == 0) scale[row] = s;
   for (int64_t u = threadIdx.x; u < units; u += blockDim.x) {
-    const uint4* src = reinterpret_cast<const uint4*>(xr + u * 16);
-    const uint2 lo = quant8_bf16(src[0], s, y);
-    const uint2 hi = quant8_bf16(src[1], s, y);
+    uint4 v0, v1;
+    load_unit<FLAGS>(xr, K, u, v0, v1);
+    const uint2 lo = quant8_bf16(v0, s, y);
+    const uint2 hi = quant8_bf16(v1, s, y);
     *reinterpret_cast<uint4*>(qr + u * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
 }
@@ -103,7 +191,7 @@ __global__ __launch_bounds__(256) void quant_per_token_long_kernel(
 // absmax is an xor-shuffle reduction over TPG lanes). Units are numbered
 // row-major over [M, K/16]; a group never straddles a row since G divides K.
 // ---------------------------------------------------------------------------
-template <int TPG>
+template <int TPG, int FLAGS>
 __global__ __launch_bounds__(256) void quant_group_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, uint8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale, int64_t m_pad, float eps) {
@@ -114,15 +202,11 @@ __global__ __launch_bounds__(256) void quant_group_kernel(
   const int64_t col_unit = live ? u - row * units_per_row : 0;
 
   uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-  if (live) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + row * ldx + col_unit * 16);
-    v0 = load16_nt(src);
-    v1 = load16_nt(src + 1);
-  }
+  if (live) load_unit<FLAGS>(x + row * ldx, K, col_unit, v0, v1);
   float amax = fmaxf(absmax8_bf16(v0), absmax8_bf16(v1));
 #pragma unroll
   for (int off = TPG / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  const float s = fmaxf(amax, eps) / kE4M3Max;
+  const float s = group_scale<FLAGS>(amax, eps);
   const float y = 1.0f / s;
   if (live) {
     const uint2 lo = quant8_bf16(v0, s, y);
@@ -136,11 +220,50 @@ __global__ __launch_bounds__(256) void quant_group_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Static per-tensor quantization: one thread per 16-element unit, the scale
+// read from device memory, codes from IEEE fp32 division x / s (the scale is
+// arbitrary here, so the reciprocal-and-correction sequence of the dynamic
+// kernels, checked only for scales derived from a bf16 absmax, is not used).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint2 quant8_bf16_div(const uint4& w, float s) {
+  const uint32_t p[4] = {w.x, w.y, w.z, w.w};
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[2 * i] = __fdiv_rn(bf16_to_f32(p[i] & 0xffffu), s);
+    r[2 * i + 1] = __fdiv_rn(bf16_to_f32(p[i] >> 16), s);
+  }
+  int lo = e4m3_pack2<false>(r[0], r[1], 0);
+  lo = e4m3_pack2<true>(r[2], r[3], lo);
+  int hi = e4m3_pack2<false>(r[4], r[5], 0);
+  hi = e4m3_pack2<true>(r[6], r[7], hi);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+__global__ __launch_bounds__(256) void quant_static_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, const float* __restrict__ scale,
+    uint8_t* __restrict__ q, int64_t ldq) {
+  const int64_t units_per_row = K >> 4;
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= M * units_per_row) return;
+  const int64_t row = u / units_per_row;
+  const int64_t col_unit = u - row * units_per_row;
+  const float s = scale[0];
+  const uint4* src = reinterpret_cast<const uint4*>(x + row * ldx + col_unit * 16);
+  const uint4 v0 = load16_nt(src), v1 = load16_nt(src + 1);
+  const uint2 lo = quant8_bf16_div(v0, s);
+  const uint2 hi = quant8_bf16_div(v1, s);
+  *reinterpret_cast<uint4*>(q + row * ldq + col_unit * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// ---------------------------------------------------------------------------
 // Launchers (arguments already validated by the C ABI layer).
 // ---------------------------------------------------------------------------
-hipError_t launch_quant_per_token(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                                  uint8_t* q, int64_t ldq, float* scale, float eps,
-                                  hipStream_t stream) {
+namespace {
+
+template <int FLAGS>
+void launch_per_token_flags(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                            int64_t ldq, float* scale, float eps, hipStream_t stream) {
   const int64_t units = K >> 4;
   // threads: a multiple of 64, at most 256, enough to keep UNITS <= 8
   int threads = (int)((units + 63) / 64) * 64;
@@ -148,37 +271,79 @@ hipError_t launch_quant_per_token(const uint16_t* x, int64_t M, int64_t K, int64
   const int64_t per = (units + threads - 1) / threads;
   const dim3 grid((unsigned)M), block((unsigned)threads);
   if (per <= 1)
-    hipLaunchKernelGGL(quant_per_token_kernel<1>, grid, block, 0, stream, x, K, ldx, q, ldq, scale, eps);
+    hipLaunchKernelGGL((quant_per_token_kernel<1, FLAGS>), grid, block, 0, stream, x, K, ldx, q, ldq, scale, eps);
   else if (per <= 2)
-    hipLaunchKernelGGL(quant_per_token_kernel<2>, grid, block, 0, stream, x, K, ldx, q, ldq, scale, eps);
+    hipLaunchKernelGGL((quant_per_token_kernel<2, FLAGS>), grid, block, 0, stream, x, K, ldx, q, ldq, scale, eps);
   else if (per <= 4)
-    hipLaunchKernelGGL(quant_per_token_kernel<4>, grid, block, 0, stream, x, K, ldx, q, ldq, scale, eps);
+    hipLaunchKernelGGL((quant_per_token_kernel<4, FLAGS>), grid, block, 0, stream, x, K, ldx, q, ldq, scale, eps);
   else if (per <= 8)
-    hipLaunchKernelGGL(quant_per_token_kernel<8>, grid, block, 0, stream, x, K, ldx, q, ldq, scale, eps);
+    hipLaunchKernelGGL((quant_per_token_kernel<8, FLAGS>), grid, block, 0, stream, x, K, ldx, q, ldq, scale, eps);
   else
-    hipLaunchKernelGGL(quant_per_token_long_kernel, grid, dim3(256), 0, stream, x, K, ldx, q, ldq, scale, eps);
+    hipLaunchKernelGGL((quant_per_token_long_kernel<FLAGS>), grid, dim3(256), 0, stream, x, K, ldx, q, ldq, scale, eps);
+}
+
+template <int FLAGS>
+void launch_group_flags(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int group_size,
+                        int64_t m_pad, uint8_t* q, int64_t ldq, float* scale, float eps,
+                        hipStream_t stream) {
+  const int64_t units = M * (K >> 4);
+  const dim3 block(256), grid((unsigned)((units + 255) / 256));
+  switch (group_size) {
+    case 16:
+      hipLaunchKernelGGL((quant_group_kernel<1, FLAGS>), grid, block, 0, stream, x, M, K, ldx, q, ldq, scale, m_pad, eps);
+      break;
+    case 32:
+      hipLaunchKernelGGL((quant_group_kernel<2, FLAGS>), grid, block, 0, stream, x, M, K, ldx, q, ldq, scale, m_pad, eps);
+      break;
+    case 64:
+      hipLaunchKernelGGL((quant_group_kernel<4, FLAGS>), grid, block, 0, stream, x, M, K, ldx, q, ldq, scale, m_pad, eps);
+      break;
+    default:
+      hipLaunchKernelGGL((quant_group_kernel<8, FLAGS>), grid, block, 0, stream, x, M, K, ldx, q, ldq, scale, m_pad, eps);
+      break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_per_token(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                  uint8_t* q, int64_t ldq, float* scale, float eps, int flags,
+                                  hipStream_t stream) {
+  switch (flags & (kQuantSiluMul | kQuantUe8m0)) {
+    case 0: launch_per_token_flags<0>(x, M, K, ldx, q, ldq, scale, eps, stream); break;
+    case kQuantSiluMul: launch_per_token_flags<kQuantSiluMul>(x, M, K, ldx, q, ldq, scale, eps, stream); break;
+    case kQuantUe8m0: launch_per_token_flags<kQuantUe8m0>(x, M, K, ldx, q, ldq, scale, eps, stream); break;
+    default:
+      launch_per_token_flags<kQuantSiluMul | kQuantUe8m0>(x, M, K, ldx, q, ldq, scale, eps, stream);
+      break;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_quant_per_token_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                         int group_size, int64_t m_pad, uint8_t* q, int64_t ldq,
-                                        float* scale, float eps, hipStream_t stream) {
-  const int64_t units = M * (K >> 4);
-  const dim3 block(256), grid((unsigned)((units + 255) / 256));
-  switch (group_size) {
-    case 16:
-      hipLaunchKernelGGL(quant_group_kernel<1>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scale, m_pad, eps);
+                                        float* scale, float eps, int flags, hipStream_t stream) {
+  switch (flags & (kQuantSiluMul | kQuantUe8m0)) {
+    case 0: launch_group_flags<0>(x, M, K, ldx, group_size, m_pad, q, ldq, scale, eps, stream); break;
+    case kQuantSiluMul:
+      launch_group_flags<kQuantSiluMul>(x, M, K, ldx, group_size, m_pad, q, ldq, scale, eps, stream);
       break;
-    case 32:
-      hipLaunchKernelGGL(quant_group_kernel<2>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scale, m_pad, eps);
-      break;
-    case 64:
-      hipLaunchKernelGGL(quant_group_kernel<4>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scale, m_pad, eps);
+    case kQuantUe8m0:
+      launch_group_flags<kQuantUe8m0>(x, M, K, ldx, group_size, m_pad, q, ldq, scale, eps, stream);
       break;
     default:
-      hipLaunchKernelGGL(quant_group_kernel<8>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scale, m_pad, eps);
+      launch_group_flags<kQuantSiluMul | kQuantUe8m0>(x, M, K, ldx, group_size, m_pad, q, ldq, scale,
+                                                      eps, stream);
       break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                               const float* scale, uint8_t* q, int64_t ldq, hipStream_t stream) {
+  const int64_t units = M * (K >> 4);
+  const dim3 block(256), grid((unsigned)((units + 255) / 256));
+  hipLaunchKernelGGL(quant_static_kernel, grid, block, 0, stream, x, M, K, ldx, scale, q, ldq);
   return hipGetLastError();
 }
 

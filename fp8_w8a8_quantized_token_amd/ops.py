@@ -14,6 +14,10 @@ User-facing calls mirror the pages' functions:
   [M_pad, K/G] view of [K/G, M_pad] storage.
 * ``linear_blockwise`` -- the blockwise linear of the same digest, with the
   row slice and the bias folded into the GEMM's epilogue.
+* ``silu_mul_quant_per_token(_group)``, ``scale_ue8m0=True`` -- the quantizer
+  flags that digest's kernel call names (fuse_silu_and_mul, scale_ue8m0).
+* ``quant_static`` -- the static per-tensor quantization named by the PR 31340
+  digest ("Fix FP8 Triton dtype selection on A100", "Implementation").
 """
 import ctypes
 import threading
@@ -24,7 +28,8 @@ from . import _lib
 from ._lib import KIND_BLOCKWISE, KIND_CHANNELWISE, TileConfig, VARIANTS, check
 
 __all__ = [
-    "prepare", "padded_rows", "quant_per_token", "quant_per_token_group", "scaled_mm_channelwise",
+    "prepare", "padded_rows", "quant_per_token", "quant_per_token_group", "silu_mul_quant_per_token",
+    "silu_mul_quant_per_token_group", "quant_static", "scaled_mm_channelwise",
     "scaled_mm_blockwise", "linear_channelwise", "linear_blockwise", "tile_config",
     "default_tile_config", "set_config_dir", "workspace_bytes", "make_config", "linear_launches",
 ]
@@ -99,41 +104,85 @@ def padded_rows(m, row_alignment=4):
     return v
 
 
-def quant_per_token(x, eps=1e-10, out=None, scale=None):
-    """bf16 [M, K] -> (E4M3 codes uint8 [M, K], fp32 scales [M])."""
+def _quant_input(x, silu_mul):
+    """Validate a quantizer input; returns K (the quantized row width)."""
     if x.dtype != torch.bfloat16 or x.dim() != 2:
         raise TypeError("x must be a 2-D bf16 tensor")
     _need_cuda(x)
-    m, k = x.shape
     if x.stride(1) != 1:
         raise ValueError("x rows must be contiguous")
+    k = x.shape[1]
+    if silu_mul:
+        if k % 2 != 0:
+            raise ValueError("a SiLU-and-mul input holds [gate | up]: an even number of columns")
+        k //= 2
+    return k
+
+
+def _flags(silu_mul, scale_ue8m0):
+    return (_lib.QUANT_FUSE_SILU_MUL if silu_mul else 0) | (_lib.QUANT_SCALE_UE8M0 if scale_ue8m0 else 0)
+
+
+def quant_per_token(x, eps=1e-10, out=None, scale=None, silu_mul=False, scale_ue8m0=False):
+    """bf16 [M, K] -> (E4M3 codes uint8 [M, K], fp32 scales [M]).
+
+    silu_mul: x is [M, 2K] = [gate | up] and the quantized row is
+    bf16(silu(gate) * up); scale_ue8m0: scales rounded up to powers of two."""
+    k = _quant_input(x, silu_mul)
+    m = x.shape[0]
     q = out if out is not None else torch.empty((m, k), dtype=torch.uint8, device=x.device)
     s = scale if scale is not None else torch.empty((m,), dtype=torch.float32, device=x.device)
-    check(_lib.load().fp8_quant_per_token(_p(x), m, k, x.stride(0), _p(q), q.stride(0), _p(s),
-                                          float(eps), _stream(x)))
+    check(_lib.load().fp8_quant_per_token_ex(_p(x), m, k, x.stride(0), _p(q), q.stride(0), _p(s),
+                                             float(eps), _flags(silu_mul, scale_ue8m0), _stream(x)))
     return q, s
 
 
 def quant_per_token_group(x, group_size=128, eps=1e-10, row_alignment=4, out=None,
-                          scale_storage=None):
+                          scale_storage=None, silu_mul=False, scale_ue8m0=False):
     """bf16 [M, K] -> (codes uint8 [M_pad, K], scales fp32 [M_pad, K/G] with
-    stride (1, M_pad)). Rows M..M_pad-1 of both are left unwritten."""
-    if x.dtype != torch.bfloat16 or x.dim() != 2:
-        raise TypeError("x must be a 2-D bf16 tensor")
-    _need_cuda(x)
-    if x.stride(1) != 1:
-        raise ValueError("x rows must be contiguous")
-    m, k = x.shape
+    stride (1, M_pad)). Rows M..M_pad-1 of both are left unwritten.
+    silu_mul / scale_ue8m0 as for quant_per_token."""
+    k = _quant_input(x, silu_mul)
+    m = x.shape[0]
     if group_size <= 0 or k % group_size != 0:
         raise ValueError("the last dimension of x must be divisible by group_size")
     m_pad = padded_rows(m, row_alignment)
     q = out if out is not None else torch.empty((m_pad, k), dtype=torch.uint8, device=x.device)
     st = scale_storage if scale_storage is not None else torch.empty(
         (k // group_size, m_pad), dtype=torch.float32, device=x.device)
-    check(_lib.load().fp8_quant_per_token_group(_p(x), m, k, x.stride(0), group_size,
-                                                row_alignment, _p(q), q.stride(0), _p(st),
-                                                float(eps), _stream(x)))
+    check(_lib.load().fp8_quant_per_token_group_ex(_p(x), m, k, x.stride(0), group_size,
+                                                   row_alignment, _p(q), q.stride(0), _p(st),
+                                                   float(eps), _flags(silu_mul, scale_ue8m0),
+                                                   _stream(x)))
     return q, st.transpose(0, 1)
+
+
+def silu_mul_quant_per_token(x, eps=1e-10, out=None, scale=None):
+    """[gate | up] bf16 [M, 2K] -> per-token codes [M, K] and scales [M] of
+    bf16(silu(gate) * up), in one pass over x."""
+    return quant_per_token(x, eps, out, scale, silu_mul=True)
+
+
+def silu_mul_quant_per_token_group(x, group_size=128, eps=1e-10, row_alignment=4, out=None,
+                                   scale_storage=None, scale_ue8m0=False):
+    """[gate | up] bf16 [M, 2K] -> row-padded group codes and column-major
+    scales (as quant_per_token_group) of bf16(silu(gate) * up)."""
+    return quant_per_token_group(x, group_size, eps, row_alignment, out, scale_storage,
+                                 silu_mul=True, scale_ue8m0=scale_ue8m0)
+
+
+def quant_static(x, scale, out=None):
+    """bf16 [M, K] and a given fp32 scale (a 1-element device tensor, positive
+    and finite) -> E4M3 codes uint8 [M, K]; no scale is produced."""
+    k = _quant_input(x, False)
+    m = x.shape[0]
+    _need_cuda(scale)
+    if scale.dtype != torch.float32 or scale.numel() != 1:
+        raise TypeError("scale must be a 1-element fp32 tensor")
+    q = out if out is not None else torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    check(_lib.load().fp8_quant_static(_p(x), m, k, x.stride(0), _p(scale), _p(q), q.stride(0),
+                                       _stream(x)))
+    return q
 
 
 # ---------------------------------------------------------------- GEMMs

@@ -162,6 +162,50 @@ int fp8_quant_per_token_group(const uint16_t* x, int64_t M, int64_t K, int64_t l
                               uint8_t* q, int64_t ldq, float* scale, float eps,
                               hipStream_t stream);
 
+/* Flags of the _ex quantizers. [PR27896, "Key source excerpts": the row-padded
+ * quant function's kernel call passes scale_ue8m0 and fuse_silu_and_mul flags
+ * (both off there); the digest shows no body for either. The readings below
+ * are this library's.]
+ *   FP8_QUANT_FUSE_SILU_MUL  x rows hold 2K values [gate | up]; the row that is
+ *     quantized is y[k] = bf16_RNE(silu(x[m,k]) * x[m,K+k]), silu(g) = g/(1+e^-g),
+ *     correctly rounded to bf16 (the value a separate SiLU-and-mul writing bf16
+ *     would pass on), so codes and scales equal those of the unfused pair.
+ *   FP8_QUANT_SCALE_UE8M0    every scale s is rounded up to a power of two
+ *     (the smallest 2^e >= s) before the codes are formed; the scale buffer
+ *     still holds fp32 values (exact powers of two). */
+enum { FP8_QUANT_FUSE_SILU_MUL = 1, FP8_QUANT_SCALE_UE8M0 = 2 };
+
+/* fp8_quant_per_token with flags (FP8_QUANT_*; unknown bits: FP8_ERR_INVALID).
+ * With FP8_QUANT_FUSE_SILU_MUL, x is bf16 [M][ldx] with ldx >= 2K; q, scale and
+ * K describe the quantized K-wide rows as before. */
+int fp8_quant_per_token_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                           uint8_t* q, int64_t ldq, float* scale, float eps,
+                           int32_t flags, hipStream_t stream);
+
+/* fp8_quant_per_token_group with flags, as fp8_quant_per_token_ex. The SiLU-
+ * and-mul form is the step between the gate/up projection (N = 2K) and the
+ * down projection (K). */
+int fp8_quant_per_token_group_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                 int32_t group_size, int32_t row_alignment,
+                                 uint8_t* q, int64_t ldq, float* scale, float eps,
+                                 int32_t flags, hipStream_t stream);
+
+/* Static per-tensor FP8 quantization with a given scale.
+ * [PR31340, "Implementation" step 2 and "Key files": a static FP8
+ * quantization kernel; the ModelOpt FP8 linear carries a precomputed
+ * input_scale. The digest shows no body; reading: the dynamic quantizer's
+ * element step with the scale supplied.]
+ *   q[m,k] = E4M3_RNE(clamp(fp32(x[m,k] / s), -448, 448)),  s = scale[0],
+ * IEEE fp32 division; no scale is written.
+ *   x      bf16 [M][ldx], ldx >= K
+ *   scale  fp32 [1], device memory, read by the kernel: a positive finite
+ *          value (others give unspecified codes; it cannot be checked on
+ *          the host without a device read)
+ *   q      E4M3 [M][ldq], ldq >= K
+ * K must be a positive multiple of 16. */
+int fp8_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                     const float* scale, uint8_t* q, int64_t ldq, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Scaled GEMMs                                                              */
 /* ------------------------------------------------------------------------ */

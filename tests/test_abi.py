@@ -77,6 +77,29 @@ def test_quant_argument_errors(lib):
     assert g(None, 0, 7168, 7168, 128, 4, None, 7168, None, 1e-10, None) == _lib.FP8_OK
 
 
+def test_quant_variant_argument_errors(lib):
+    qe = lib.fp8_quant_per_token_ex
+    silu, ue = _lib.QUANT_FUSE_SILU_MUL, _lib.QUANT_SCALE_UE8M0
+    assert qe(FAKE, 4, 128, 128, FAKE, 128, FAKE, 1e-10, 4, None) == _lib.FP8_ERR_INVALID
+    assert "flags" in _err(lib)
+    # SiLU-and-mul reads 2K values per row
+    assert qe(FAKE, 4, 128, 128, FAKE, 128, FAKE, 1e-10, silu, None) == _lib.FP8_ERR_INVALID
+    assert "leading dimension" in _err(lib)
+    assert qe(None, 4, 128, 256, FAKE, 128, FAKE, 1e-10, silu | ue, None) == _lib.FP8_ERR_INVALID
+    assert qe(None, 0, 128, 256, None, 128, None, 1e-10, silu, None) == _lib.FP8_OK
+    ge = lib.fp8_quant_per_token_group_ex
+    assert ge(FAKE, 4, 7168, 7168, 128, 4, FAKE, 7168, FAKE, 1e-10, silu, None) == _lib.FP8_ERR_INVALID
+    assert ge(FAKE, 4, 6144, 12288, 96, 4, FAKE, 6144, FAKE, 1e-10, silu, None) == _lib.FP8_ERR_UNSUPPORTED
+    assert ge(FAKE, 4, 7168, 14336, 128, 4, FAKE, 7168, FAKE, 1e-10, 8, None) == _lib.FP8_ERR_INVALID
+    assert ge(None, 0, 7168, 14336, 128, 4, None, 7168, None, 1e-10, silu | ue, None) == _lib.FP8_OK
+    st = lib.fp8_quant_static
+    assert st(FAKE, 4, 128, 128, None, FAKE, 128, None) == _lib.FP8_ERR_INVALID
+    assert "null" in _err(lib)
+    assert st(FAKE, 4, 120, 128, FAKE, FAKE, 128, None) == _lib.FP8_ERR_INVALID
+    assert st(FAKE, 4, 128, 128, FAKE, ctypes.c_void_p(0x10008), 128, None) == _lib.FP8_ERR_INVALID
+    assert st(None, 0, 128, 128, None, None, 128, None) == _lib.FP8_OK
+
+
 def test_gemm_argument_errors(lib):
     cw = lib.fp8_scaled_mm_channelwise
     assert cw(None, FAKE, FAKE, FAKE, None, FAKE, 4, 256, 512, 512, 512, 256, None, 0, None) == _lib.FP8_ERR_INVALID
