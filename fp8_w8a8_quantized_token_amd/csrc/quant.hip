@@ -49,31 +49,69 @@ __device__ __forceinline__ uint32_t bf16_of_f64(double d) {
   return f32_to_bf16(__uint_as_float(b));
 }
 
-// bf16 bits of silu(g) * u, correctly rounded. The fp32 evaluation (expf,
-// reciprocal, two products) is within 12 fp32 ulps of the exact value (expf
-// within 3 ulps, each other step within 1), so unless it lies within 32 ulps
-// of a bf16 rounding midpoint (low 16 bits near 0x8000) its bf16 rounding is
-// that of the exact value. The rest (about 1 value in 1000 on normal data),
-// and gates below -80 where e^-g nears fp32 overflow, are evaluated in fp64.
-__device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
-  const float t = expf(-g);
-  const float y = (g * __builtin_amdgcn_rcpf(1.0f + t)) * u;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> two bf16 (a in the low half), round to nearest even: the
+// packed hardware convert of gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// silu(g) * u in fp32: e^-g as 2^(-g log2 e) on the hardware exp2 (within 1
+// ulp), then the reciprocal (1 ulp) and two products. Relative error at most
+// (|g| + 7) 2^-24 for g >= -16: rounding -g log2 e costs |g| 2^-24 once the
+// exponent is taken, the other steps 7 2^-24 together; for g > 16.6 the
+// e^-g term is below half an ulp of 1 and its error drops out.
+__device__ __forceinline__ float silu_mul_f32(float g, float u) {
+  const float t = __builtin_amdgcn_exp2f(g * -1.44269504088896340736f);
+  return (g * __builtin_amdgcn_rcpf(1.0f + t)) * u;
+}
+
+// True where the fp32 value y = silu_mul_f32(g, u) may round to a different
+// bf16 than the exact product: y lies within 48 fp32 ulps of a bf16 rounding
+// midpoint (low 16 bits near 0x8000; the error bound above is at most 23 ulps
+// for g >= -16), or g < -16, outside that bound.
+__device__ __forceinline__ bool silu_needs_f64(float g, float y) {
   const uint32_t low = __float_as_uint(y) & 0xFFFFu;
-  if (g >= -80.0f && (low - 0x7FE0u) > 0x40u) return f32_to_bf16(y);
+  return !(g >= -16.0f) || (low - (0x8000u - 48u)) <= 96u;
+}
+
+// bf16 bits of silu(g) * u from fp64 (exp in fp64 within 1 ulp, IEEE
+// division): correctly rounded unless the exact value lies within ~2^-50
+// relative of a bf16 midpoint.
+__device__ __noinline__ uint32_t silu_mul_bf16_f64(float g, float u) {
   const double gd = (double)g;
   return bf16_of_f64(gd / (1.0 + exp(-gd)) * (double)u);
 }
 
-// 8 gate and 8 up bf16 values -> 8 bf16 values of silu(gate) * up.
+// 8 gate and 8 up bf16 values -> 8 bf16 values of silu(gate) * up, correctly
+// rounded. All eight fp32 evaluations run first, straight-line; the few that
+// sit too close to a bf16 rounding midpoint (about 1 in 700 on normal data)
+// are redone in fp64 behind one branch per 8 values.
 __device__ __forceinline__ uint4 silu_mul8(const uint4& g, const uint4& u) {
   const uint32_t gp[4] = {g.x, g.y, g.z, g.w};
   const uint32_t up[4] = {u.x, u.y, u.z, u.w};
+  float gf[8], uf[8], y[8];
+  uint32_t redo = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    gf[i] = bf16_to_f32((i & 1) ? (gp[i >> 1] >> 16) : (gp[i >> 1] & 0xffffu));
+    uf[i] = bf16_to_f32((i & 1) ? (up[i >> 1] >> 16) : (up[i >> 1] & 0xffffu));
+    y[i] = silu_mul_f32(gf[i], uf[i]);
+    redo |= silu_needs_f64(gf[i], y[i]) ? (1u << i) : 0u;
+  }
   uint32_t o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = silu_mul_bf16(bf16_to_f32(gp[i] & 0xffffu), bf16_to_f32(up[i] & 0xffffu));
-    const uint32_t hi = silu_mul_bf16(bf16_to_f32(gp[i] >> 16), bf16_to_f32(up[i] >> 16));
-    o[i] = lo | (hi << 16);
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
+  if (redo) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (redo & (1u << i)) {
+        const uint32_t b = silu_mul_bf16_f64(gf[i], uf[i]);
+        o[i >> 1] = (i & 1) ? ((o[i >> 1] & 0xffffu) | (b << 16)) : ((o[i >> 1] & 0xffff0000u) | b);
+      }
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
@@ -111,10 +149,10 @@ __device__ __forceinline__ float group_scale(float amax, float eps) {
 // produced from the registers, so the row is read from HBM once.
 // ---------------------------------------------------------------------------
 template <int UNITS, int FLAGS>
-__global__ __launch_bounds__(256) void quant_per_token_kernel(
+__global__ __launch_bounds__((FLAGS & kQuantSiluMul) != 0 ? 1024 : 256) void quant_per_token_kernel(
     const uint16_t* __restrict__ x, int64_t K, int64_t ldx, uint8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale, float eps) {
-  __shared__ float wave_part[4];
+  __shared__ float wave_part[16];
   const int64_t row = blockIdx.x;
   const uint16_t* xr = x + row * ldx;
   uint8_t* qr = q + row * ldq;
@@ -265,9 +303,13 @@ template <int FLAGS>
 void launch_per_token_flags(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                             int64_t ldq, float* scale, float eps, hipStream_t stream) {
   const int64_t units = K >> 4;
-  // threads: a multiple of 64, at most 256, enough to keep UNITS <= 8
+  // threads: a multiple of 64, enough to keep UNITS <= 8, at most 256 -- or,
+  // with SiLU-and-mul, whose per-element work is several times larger, at most
+  // 1024 while there are too few rows to fill the chip, so that a short batch
+  // of long rows still spreads over many waves
+  const int cap = (FLAGS & kQuantSiluMul) != 0 && M < 1024 ? 1024 : 256;
   int threads = (int)((units + 63) / 64) * 64;
-  if (threads > 256) threads = 256;
+  if (threads > cap) threads = cap;
   const int64_t per = (units + threads - 1) / threads;
   const dim3 grid((unsigned)M), block((unsigned)threads);
   if (per <= 1)

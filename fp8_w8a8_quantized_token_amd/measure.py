@@ -149,6 +149,90 @@ def measure_m(buf, cfg, m, outliers, warmup, calls, filler):
     return res
 
 
+# Quantizer variants: (name, K, M values). SiLU-and-mul inputs are [M, 2K]
+# (the gate/up projection's output), the quantized rows K wide.
+QUANT_VARIANTS = [
+    ("silu_per_token", 12288, (1, 64, 512, 8192)),     # Qwen3-8B 24576 -> down K = 12288
+    ("per_token", 12288, (1, 64, 512, 8192)),          # the same rows without SiLU-and-mul
+    ("silu_group128", 12288, (1, 64, 512, 8192)),
+    ("silu_group128", 1536, (1, 4, 16, 64, 4096)),     # MoE expert 3072 -> down K = 1536
+    ("group128", 1536, (1, 4, 16, 64, 4096)),
+    ("ue8m0_group128", 7168, (1, 64, 256)),
+    ("ue8m0_group128", 4096, (4096,)),
+    ("static", 4096, (1, 64, 1024, 8192)),
+]
+
+
+def quant_variant_bytes(name, m, k):
+    """Algorithmic bytes: bf16 input (2K wide with SiLU-and-mul), codes, scales."""
+    read = (4 if name.startswith("silu") else 2) * m * k
+    if name == "static":
+        return read + m * k + 4
+    scales = 4 * m * (k // 128) if "group128" in name else 4 * m
+    return read + m * k + scales
+
+
+def _quant_variant_call(name, x, q, s, scale):
+    if name == "silu_per_token":
+        return ops.prepare("silu_mul_quant_per_token", x, out=q, scale=s)
+    if name == "per_token":
+        return ops.prepare("quant_per_token", x, out=q, scale=s)
+    if name == "static":
+        return ops.prepare("quant_static", x, scale, out=q)
+    kw = dict(row_alignment=4, out=q, scale_storage=s)
+    if name == "silu_group128":
+        return ops.prepare("silu_mul_quant_per_token_group", x, 128, **kw)
+    if name == "ue8m0_group128":
+        return ops.prepare("quant_per_token_group", x, 128, scale_ue8m0=True, **kw)
+    return ops.prepare("quant_per_token_group", x, 128, **kw)
+
+
+def measure_quant_variants(warmup, calls, filler):
+    """Average launch time of each quantizer variant over `calls` back-to-back
+    launches cycling through buffer sets that cover >= 1 GiB of input where
+    the shape allows (at most MAX_SETS sets), timed as one batch with HIP
+    events: per-call event pairs would add their own ~4 us."""
+    dev = torch.device("cuda:0")
+    head = ("| variant | K | M | input MB | sets | µs per launch | GB/s | frac HBM |")
+    lines = [head, "|---|---|---|---|---|---|---|---|"]
+    print(head, flush=True)
+    print(lines[1], flush=True)
+    scale = torch.tensor([0.02], dtype=torch.float32, device=dev)
+    for name, k, ms in QUANT_VARIANTS:
+        width = 2 * k if name.startswith("silu") else k
+        for m in ms:
+            x0 = synth.activations(f"measure/quant/{name}", m, width).to(dev)
+            sets = max(2, min(MAX_SETS, math.ceil(ROTATE_BYTES / x0.numel() / 2)))
+            m_pad = ops.padded_rows(m, 4)
+            fns, keep = [], []
+            for _ in range(sets):
+                x = x0.clone()
+                q = torch.empty((m_pad, k), dtype=torch.uint8, device=dev)
+                s = torch.empty((k // 128, m_pad) if "group" in name else (m,), dtype=torch.float32,
+                                device=dev)
+                keep.append((x, q, s))
+                fns.append(_quant_variant_call(name, x, q, s, scale))
+            for i in range(warmup):
+                fns[i % sets]()
+            torch.cuda.synchronize()
+            filler(calls)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(calls):
+                fns[i % sets]()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / calls
+            gb = quant_variant_bytes(name, m, k) / us / 1e3
+            line = (f"| {name} | {k} | {m} | {x0.numel() * 2 / 1e6:.2f} | {sets} | {us:.2f} | "
+                    f"{gb:.0f} | {gb / PEAK_GBPS:.2f} |")
+            lines.append(line)
+            print(line, flush=True)
+            del keep, fns, x0
+            torch.cuda.empty_cache()
+    return lines
+
+
 HEADER = ("| workload | kind | N×K | M | tile config | weight GiB rotated | GEMM µs p50 (p10–p90) | "
           "TFLOP/s | GB/s | frac HBM | frac MFMA | quant µs p50 (GB/s) | linear µs p50 (launches) | "
           "hot GEMM µs p50 |")
@@ -177,11 +261,24 @@ def main(argv=None):
     ap.add_argument("--calls", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--out", default="")
+    ap.add_argument("--quant-variants", action="store_true",
+                    help="time the quantizer variants (SiLU-and-mul, UE8M0, static) instead")
     args = ap.parse_args(argv)
     _lib.load()
     dev = torch.device("cuda:0")
     want = args.workloads.split(",")
     filler = _Filler(dev)
+    if args.quant_variants:
+        t0 = time.time()
+        lines = measure_quant_variants(args.warmup, args.calls, filler)
+        note = (f"\n{args.calls} launches per row after {args.warmup} warm-up launches, timed as "
+                f"one batch with HIP events (average per launch); GB/s from algorithmic bytes "
+                f"(bf16 input, codes, scales). {time.time() - t0:.0f} s.")
+        print(note, flush=True)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write("\n".join(lines) + "\n" + note + "\n")
+        return 0
     lines = [HEADER, "|" + "---|" * 14]
     print(HEADER, flush=True)
     print(lines[1], flush=True)

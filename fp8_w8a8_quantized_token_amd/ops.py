@@ -368,7 +368,9 @@ class Prepared:
 
 def prepare(op, *args, **kwargs):
     """prepare("quant_per_token", x, out=q, scale=s), prepare("quant_per_token_group",
-    x, group_size, row_alignment=4, out=q, scale_storage=st),
+    x, group_size, row_alignment=4, out=q, scale_storage=st) (both also as
+    "silu_mul_quant_per_token(_group)" and with scale_ue8m0=True),
+    prepare("quant_static", x, scale, out=q),
     prepare("scaled_mm_channelwise", a, b, a_scale, b_scale, bias=None, out=out, config=None),
     prepare("scaled_mm_blockwise", a, b, a_scale, b_scale, bias=None, m=None, out=out,
     config=None), prepare("linear_channelwise", x, w_q, w_s, bias=None, out=out, q=q,
@@ -381,18 +383,30 @@ def prepare(op, *args, **kwargs):
         globals()[op](*args, **kw)  # validates and raises on bad arguments
     else:
         globals()[op](*args, **kwargs)
-    if op == "quant_per_token":
+    if op in ("quant_per_token", "silu_mul_quant_per_token"):
         x = args[0]
         q, s = kwargs["out"], kwargs["scale"]
-        a = (_p(x), x.shape[0], x.shape[1], x.stride(0), _p(q), q.stride(0), _p(s),
-             ctypes.c_float(kwargs.get("eps", 1e-10)), _stream(x))
-        return Prepared(lib.fp8_quant_per_token, a, op, (x, q, s))
-    if op == "quant_per_token_group":
+        silu = op == "silu_mul_quant_per_token"
+        k = x.shape[1] // 2 if silu else x.shape[1]
+        a = (_p(x), x.shape[0], k, x.stride(0), _p(q), q.stride(0), _p(s),
+             ctypes.c_float(kwargs.get("eps", 1e-10)),
+             _flags(silu or kwargs.get("silu_mul", False), kwargs.get("scale_ue8m0", False)),
+             _stream(x))
+        return Prepared(lib.fp8_quant_per_token_ex, a, op, (x, q, s))
+    if op in ("quant_per_token_group", "silu_mul_quant_per_token_group"):
         x, g = args[0], args[1]
         q, st = kwargs["out"], kwargs["scale_storage"]
-        a = (_p(x), x.shape[0], x.shape[1], x.stride(0), g, kwargs.get("row_alignment", 4), _p(q),
-             q.stride(0), _p(st), ctypes.c_float(kwargs.get("eps", 1e-10)), _stream(x))
-        return Prepared(lib.fp8_quant_per_token_group, a, op, (x, q, st))
+        silu = op == "silu_mul_quant_per_token_group" or kwargs.get("silu_mul", False)
+        k = x.shape[1] // 2 if silu else x.shape[1]
+        a = (_p(x), x.shape[0], k, x.stride(0), g, kwargs.get("row_alignment", 4), _p(q),
+             q.stride(0), _p(st), ctypes.c_float(kwargs.get("eps", 1e-10)),
+             _flags(silu, kwargs.get("scale_ue8m0", False)), _stream(x))
+        return Prepared(lib.fp8_quant_per_token_group_ex, a, op, (x, q, st))
+    if op == "quant_static":
+        x, scale = args[0], args[1]
+        q = kwargs["out"]
+        a = (_p(x), x.shape[0], x.shape[1], x.stride(0), _p(scale), _p(q), q.stride(0), _stream(x))
+        return Prepared(lib.fp8_quant_static, a, op, (x, scale, q))
     if op in ("linear_channelwise", "linear_blockwise"):
         kind = KIND_CHANNELWISE if op == "linear_channelwise" else KIND_BLOCKWISE
         x, w_q, w_s = args[0], args[1], args[2]
