@@ -148,11 +148,14 @@ def quant_weight_per_channel(w, eps: float = 1e-10):
     return quant_per_token(w, eps)
 
 
-def quant_weight_blockwise(w, block_n: int = 128, block_k: int = 128, eps: float = 1e-10):
+def quant_weight_blockwise(w, block_n: int = 128, block_k: int = 128, eps: float = 1e-10,
+                           scale_ue8m0: bool = False):
     """128x128-block weight quantization of W[N, K].
 
     Each (block_n x block_k) tile gets scale = max(absmax, eps) / 448 and its
     entries are encoded as E4M3(w / scale), in fp32 like the activations.
+    scale_ue8m0 rounds each block scale up to a power of two first, as for the
+    activations (see pow2_ceil).
     Returns (codes uint8 [N, K], scales float32 [ceil(N/bn), ceil(K/bk)]).
     """
     wf = np.asarray(w, dtype=F32)
@@ -168,6 +171,8 @@ def quant_weight_blockwise(w, block_n: int = 128, block_k: int = 128, eps: float
             tile = wf[i * block_n:(i + 1) * block_n, j * block_k:(j + 1) * block_k]
             amax = max(F32(np.max(np.abs(tile))), eps32)
             s = F32(amax / fmax)
+            if scale_ue8m0:
+                s = pow2_ceil(s)
             scales[i, j] = s
             codes[i * block_n:(i + 1) * block_n, j * block_k:(j + 1) * block_k] = encode(
                 (tile / s).astype(F32))

@@ -213,6 +213,22 @@ def test_ue8m0_scales_and_codes():
         assert np.all((top[live] >= 224) & (top[live] <= 448))
 
 
+def test_ue8m0_weight_blocks():
+    w = synth.weights("pin-ue8m0-w", 256, 384).numpy()
+    q0, s0 = oracle.quant_weight_blockwise(w)
+    q1, s1 = oracle.quant_weight_blockwise(w, scale_ue8m0=True)
+    assert np.array_equal(s1, np.vectorize(oracle.pow2_ceil, otypes=[np.float32])(s0))
+    # one-row blocks are the per-token-group quantizer with the same flag
+    qa, sa = oracle.quant_weight_blockwise(w[:8], block_n=1, block_k=128, scale_ue8m0=True)
+    qb, sb = oracle.quant_per_token_group(w[:8], 128, scale_ue8m0=True)
+    assert np.array_equal(qa, qb) and np.array_equal(sa, sb)
+    # codes: torch's float8 conversion of the exact quotient by the block scale
+    srep = np.repeat(np.repeat(s1, 128, axis=0), 128, axis=1)
+    want = torch.from_numpy(np.clip(w / srep, -448, 448).astype(np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q1, want)
+
+
 # ---------------------------------------------------------------- static
 def test_static_equals_dynamic_with_its_scale():
     x = synth.activations("pin-static", 16, 256).float().numpy()
