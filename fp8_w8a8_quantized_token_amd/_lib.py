@@ -22,6 +22,7 @@ FP8_ERR_HIP = -4
 
 KIND_CHANNELWISE = 0
 KIND_BLOCKWISE = 1
+KIND_BLOCKWISE_UE8M0 = 2
 
 QUANT_FUSE_SILU_MUL = 1
 QUANT_SCALE_UE8M0 = 2
@@ -67,6 +68,11 @@ SIGNATURES = {
     "fp8_scaled_mm_blockwise_ex": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64,
                                            c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_size,
                                            ctypes.POINTER(TileConfig), c_vp]),
+    "fp8_scaled_mm_blockwise_ue8m0": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64,
+                                              c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_size, c_vp]),
+    "fp8_scaled_mm_blockwise_ue8m0_ex": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64,
+                                                 c_i64, c_i64, c_i64, c_i64, c_i64, c_vp, c_size,
+                                                 ctypes.POINTER(TileConfig), c_vp]),
     "fp8_scaled_mm_workspace_size": (c_size, [c_i32, c_i64, c_i64, c_i64,
                                               ctypes.POINTER(TileConfig)]),
     "fp8_linear_channelwise": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64,

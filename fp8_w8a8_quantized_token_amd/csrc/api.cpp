@@ -114,7 +114,9 @@ int run_gemm(const char* fn, int kind, const uint8_t* a, const uint8_t* b, const
              int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, void* ws,
              size_t ws_bytes, const fp8_tile_config* cfg_in, hipStream_t stream) {
   fp8_tile_config cfg;
-  int st = resolve_config(kind, M, N, K, cfg_in, &cfg);
+  // UE8M0-scaled blockwise GEMMs share the blockwise tiles and tables
+  int st = resolve_config(kind == FP8_KIND_BLOCKWISE_UE8M0 ? FP8_KIND_BLOCKWISE : kind, M, N, K, cfg_in,
+                          &cfg);
   if (st) return st;
   GemmArgs p{};
   p.a = a; p.b = b; p.sa = sa; p.sa_ld = sa_ld; p.sb = sb; p.bias = bias; p.out = out;
@@ -299,8 +301,35 @@ int fp8_scaled_mm_blockwise(const uint8_t* a, const uint8_t* b, const float* a_s
                                     ldb, ldc, ws, ws_bytes, nullptr, stream);
 }
 
+int fp8_scaled_mm_blockwise_ue8m0_ex(const uint8_t* a, const uint8_t* b, const float* a_scale,
+                                     int64_t a_scale_ld, const float* b_scale, const uint16_t* bias,
+                                     uint16_t* out, int64_t M, int64_t N, int64_t K, int64_t lda,
+                                     int64_t ldb, int64_t ldc, void* ws, size_t ws_bytes,
+                                     const fp8_tile_config* cfg, hipStream_t stream) {
+  const char* fn = "fp8_scaled_mm_blockwise_ue8m0";
+  int st = check_gemm(fn, a, b, a_scale, b_scale, bias, out, M, N, K, lda, ldb, ldc);
+  if (st) return st;
+  if (M == 0) return ok();
+  if (N % 128 != 0 || K % 128 != 0)
+    return fail(FP8_ERR_UNSUPPORTED, "%s: N=%lld and K=%lld must be multiples of 128", fn, (long long)N,
+                (long long)K);
+  if (a_scale_ld < M) return fail(FP8_ERR_INVALID, "%s: a_scale_ld=%lld < M=%lld", fn, (long long)a_scale_ld, (long long)M);
+  return run_gemm(fn, FP8_KIND_BLOCKWISE_UE8M0, a, b, a_scale, a_scale_ld, b_scale, bias, out, M, N,
+                  K, lda, ldb, ldc, ws, ws_bytes, cfg, stream);
+}
+
+int fp8_scaled_mm_blockwise_ue8m0(const uint8_t* a, const uint8_t* b, const float* a_scale,
+                                  int64_t a_scale_ld, const float* b_scale, const uint16_t* bias,
+                                  uint16_t* out, int64_t M, int64_t N, int64_t K, int64_t lda,
+                                  int64_t ldb, int64_t ldc, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  return fp8_scaled_mm_blockwise_ue8m0_ex(a, b, a_scale, a_scale_ld, b_scale, bias, out, M, N, K,
+                                          lda, ldb, ldc, ws, ws_bytes, nullptr, stream);
+}
+
 size_t fp8_scaled_mm_workspace_size(int32_t kind, int64_t M, int64_t N, int64_t K,
                                     const fp8_tile_config* cfg_in) {
+  if (kind == FP8_KIND_BLOCKWISE_UE8M0) kind = FP8_KIND_BLOCKWISE;  // same tiles
   if ((kind != FP8_KIND_CHANNELWISE && kind != FP8_KIND_BLOCKWISE) || M < 0 || N < 0 || K < 0)
     return (size_t)-1;
   if (M == 0 || N == 0 || K == 0) return 0;

@@ -34,6 +34,17 @@ __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& w, const i32x8& x, const 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, c, 0, 0, 0, 0, 0, 0);
 }
 
+// The same with E8M0 block scales applied by the matrix core (gfx950's
+// block-scaled MFMA): every product is multiplied by 2^(ew - 127) 2^(ex - 127),
+// ew the exponent of the first operand's row (the weight row n), ex that of the
+// second's (the activation row m). Each lane passes, in the low byte, the
+// exponent for its row and the 32-deep K piece it supplies (lane group l / 16);
+// with one scale per 128-deep block all four pieces of a row pass the same one.
+__device__ __forceinline__ f32x4 mfma_fp8_e8(const i32x8& w, const i32x8& x, const f32x4& c, int ew,
+                                             int ex) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, c, 0, 0, 0, ew, 0, ex);
+}
+
 __device__ __forceinline__ i32x8 join(const uint4& lo, const uint4& hi) {
   i32x8 r;
   r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
@@ -795,8 +806,8 @@ template <int BM, int BN, int WM, int WN, int KIND, int NP, bool SC_IN_A = false
 struct PanelGeom {
   static constexpr int NW = WM * WN;
   static constexpr int NBLK = (BN + 127) / 128;                // weight scale blocks per tile
-  static constexpr int SA_BYTES = KIND == kBlockwise ? BM * 4 : 0;
-  static constexpr int SB_BYTES = KIND == kBlockwise ? NW * 16 : 0;
+  static constexpr int SA_BYTES = KIND != kChannelwise ? BM * 4 : 0;
+  static constexpr int SB_BYTES = KIND != kChannelwise ? NW * 16 : 0;
   static constexpr int A_BYTES = BM * 128 + (SC_IN_A ? SA_BYTES + SB_BYTES : 0);
   static constexpr int B_BYTES = BN * 128 + (SC_IN_A ? 0 : SA_BYTES + SB_BYTES);
   static constexpr int SLOT = ((A_BYTES > B_BYTES ? A_BYTES : B_BYTES) + 1023) / 1024 * 1024;
@@ -820,7 +831,8 @@ __device__ __forceinline__ void wait_panels(int64_t c) {
 template <int BM, int BN, int WM, int WN, int KIND, int NP, bool MF16 = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   using G = PanelGeom<BM, BN, WM, WN, KIND, NP, MF16>;
-  constexpr bool BW = KIND == kBlockwise;
+  constexpr bool BW = KIND != kChannelwise;
+  static_assert(KIND != kBlockwiseE8 || MF16, "E8M0 scales are served by the 16x16 body");
   constexpr int NT = WM * WN * 64;
   constexpr int NW = WM * WN;
   constexpr int BK = 128;
@@ -939,7 +951,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
     // result with sa[m] * sb right away. The per-stage scales ride with the A
     // panel, so the B slot can be refilled as soon as the B fragments are in
     // registers (see the issue order below).
-    static_assert(BW, "the 16x16 body serves the blockwise kind");
+    static_assert(BW, "the 16x16 body serves the blockwise kinds");
     constexpr int FI = WTM / 16, FJ = WTN / 16;
     const int g = lane >> 4, r16 = lane & 15;
     // lane's chunks of a 16-row fragment: row r16, K bytes [32g, 32g + 32)
@@ -1002,6 +1014,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
       if (issued < np_all) {  // every wave has its B fragments: the B slot takes B(s+2)
         issue_panel(issued, cs);
         ++issued;
+      }
+      if constexpr (KIND == kBlockwiseE8) {
+        // power-of-two scales: their biased exponents go to the MFMA, which
+        // scales the products itself; one accumulator, no promotion step
+        const int eb = (int)(*reinterpret_cast<const uint32_t*>(pslot_a + SB_OFF + wave * 16 +
+                                                                ((wn * WTN) >> 7) * 4) >> 23);
+        i32x8 fa = frag16(pa);
+#pragma unroll
+        for (int i = 0; i < FI; ++i) {
+          const int ea = (int)(*reinterpret_cast<const uint32_t*>(
+                                   pslot_a + SA_OFF + (wm * WTM + i * 16 + r16) * 4) >> 23);
+          i32x8 fn;
+          if (i + 1 < FI) fn = frag16(pa + (i + 1) * 16 * BK);
+#pragma unroll
+          for (int j = 0; j < FJ; ++j) acc16[i][j] = mfma_fp8_e8(fb[j], fa, acc16[i][j], eb, ea);
+          if (i + 1 < FI) fa = fn;
+        }
+        cs = wrap(cs + 2);
+        continue;
       }
       const float sb = *reinterpret_cast<const float*>(pslot_a + SB_OFF + wave * 16 + ((wn * WTN) >> 7) * 4);
       i32x8 fa = frag16(pa);
@@ -1695,6 +1726,13 @@ hipError_t launch_linear_fused(int kind, const GemmArgs& p, const QuantArgs& qa,
 }
 
 hipError_t launch_gemm(int kind, int variant, const GemmArgs& p, hipStream_t stream) {
+  if (kind == kBlockwiseE8) {
+    // the block-scaled MFMA serves the 16x16 256x256 tile; every other tile
+    // promotes in fp32, which is exact for power-of-two scales
+    if (variant == 25 && panel_eligible<kBlockwise>(p))
+      return launch_panel<256, 256, 2, 4, kBlockwiseE8, 4, true>(p, stream);
+    return launch_kind<kBlockwise>(variant, p, stream);
+  }
   return kind == kChannelwise ? launch_kind<kChannelwise>(variant, p, stream)
                               : launch_kind<kBlockwise>(variant, p, stream);
 }

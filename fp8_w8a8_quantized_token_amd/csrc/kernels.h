@@ -22,7 +22,11 @@ hipError_t launch_quant_per_token_group(const uint16_t* x, int64_t M, int64_t K,
 hipError_t launch_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                const float* scale, uint8_t* q, int64_t ldq, hipStream_t stream);
 
-enum GemmKind { kChannelwise = 0, kBlockwise = 1 };
+// kBlockwiseE8: blockwise with power-of-two (UE8M0) scales, held as fp32
+// powers of two; the 16x16 256x256 tile hands their exponents to the
+// block-scaled MFMA, every other tile runs the kBlockwise kernels (their fp32
+// promotion is exact for powers of two).
+enum GemmKind { kChannelwise = 0, kBlockwise = 1, kBlockwiseE8 = 2 };
 
 struct GemmArgs {
   const uint8_t* a;

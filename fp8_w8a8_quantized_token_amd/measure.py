@@ -233,6 +233,57 @@ def measure_quant_variants(warmup, calls, filler):
     return lines
 
 
+# Blockwise GEMMs timed with fp32 scales (promotion per 128-deep block) and
+# with power-of-two scales (block-scaled MFMA), on the 16x16 256x256 tile.
+UE8M0_SHAPES = [(4096, 4096, (2048, 4096, 8192)), (3072, 4096, (4096,)), (4096, 1536, (4096,)),
+                (7168, 7168, (4096,))]
+
+
+def measure_ue8m0_gemm(warmup, calls, filler):
+    dev = torch.device("cuda:0")
+    head = "| N×K | M | tile | scales | weight sets | µs per launch | TFLOP/s | frac MFMA |"
+    lines = [head, "|---|---|---|---|---|---|---|---|"]
+    print(head, flush=True)
+    print(lines[1], flush=True)
+    cfg = ops.make_config("t256x256bw16")
+    for n, k, ms in UE8M0_SHAPES:
+        sets = max(2, min(MAX_SETS, math.ceil(ROTATE_BYTES / (n * k))))
+        w = synth.weights("measure/ue8m0", n, k).to(torch.bfloat16).to(dev)
+        wq, _ = ops.quant_per_token_group(w, 128, row_alignment=1)
+        wq = wq.contiguous()
+        del w
+        ws = synth.positive_scales(f"measure/ue8m0/{n}/{k}", (n // 128, k // 128)).to(dev)
+        ws_e8 = torch.exp2(torch.ceil(torch.log2(ws)))  # powers of two
+        weights = [wq.clone() for _ in range(sets)]
+        for m in ms:
+            x = synth.activations("measure/ue8m0", m, k).to(dev)
+            out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            for ue8m0 in (False, True):
+                q, st = ops.quant_per_token_group(x, 128, row_alignment=4, scale_ue8m0=ue8m0)
+                bs = ws_e8 if ue8m0 else ws
+                fns = [ops.prepare("scaled_mm_blockwise", q, wt, st, bs, m=m, out=out, config=cfg,
+                                   scale_ue8m0=ue8m0) for wt in weights]
+                for i in range(warmup):
+                    fns[i % sets]()
+                torch.cuda.synchronize()
+                filler(calls)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(calls):
+                    fns[i % sets]()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / calls
+                tf = 2 * m * n * k / us / 1e6
+                line = (f"| {n}×{k} | {m} | t256x256bw16 | {'ue8m0 (MFMA-scaled)' if ue8m0 else 'fp32 (promotion)'} "
+                        f"| {sets} | {us:.1f} | {tf:.0f} | {tf / PEAK_TFLOPS:.3f} |")
+                lines.append(line)
+                print(line, flush=True)
+        del weights
+        torch.cuda.empty_cache()
+    return lines
+
+
 HEADER = ("| workload | kind | N×K | M | tile config | weight GiB rotated | GEMM µs p50 (p10–p90) | "
           "TFLOP/s | GB/s | frac HBM | frac MFMA | quant µs p50 (GB/s) | linear µs p50 (launches) | "
           "hot GEMM µs p50 |")
@@ -263,17 +314,21 @@ def main(argv=None):
     ap.add_argument("--out", default="")
     ap.add_argument("--quant-variants", action="store_true",
                     help="time the quantizer variants (SiLU-and-mul, UE8M0, static) instead")
+    ap.add_argument("--ue8m0-gemm", action="store_true",
+                    help="time the 16x16 blockwise tile with fp32 and with power-of-two scales")
     args = ap.parse_args(argv)
     _lib.load()
     dev = torch.device("cuda:0")
     want = args.workloads.split(",")
     filler = _Filler(dev)
-    if args.quant_variants:
+    if args.quant_variants or args.ue8m0_gemm:
         t0 = time.time()
-        lines = measure_quant_variants(args.warmup, args.calls, filler)
+        lines = (measure_quant_variants if args.quant_variants else measure_ue8m0_gemm)(
+            args.warmup, args.calls, filler)
         note = (f"\n{args.calls} launches per row after {args.warmup} warm-up launches, timed as "
                 f"one batch with HIP events (average per launch); GB/s from algorithmic bytes "
-                f"(bf16 input, codes, scales). {time.time() - t0:.0f} s.")
+                f"(bf16 input, codes, scales); weight sets rotated to cover >= 1 GiB. "
+                f"{time.time() - t0:.0f} s.")
         print(note, flush=True)
         if args.out:
             with open(args.out, "w") as f:

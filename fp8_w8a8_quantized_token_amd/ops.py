@@ -215,10 +215,13 @@ def scaled_mm_channelwise(a, b, a_scale, b_scale, bias=None, out=None, config=No
     return out
 
 
-def scaled_mm_blockwise(a, b, a_scale, b_scale, bias=None, m=None, out=None, config=None):
+def scaled_mm_blockwise(a, b, a_scale, b_scale, bias=None, m=None, out=None, config=None,
+                        scale_ue8m0=False):
     """a codes [>=M, K]; b codes [N, K]; a_scale an [M_pad, K/128] view with
     stride(0) == 1 (as returned by quant_per_token_group); b_scale fp32
-    [N/128, K/128]; only the first m rows (default: all of a) are computed."""
+    [N/128, K/128]; only the first m rows (default: all of a) are computed.
+    scale_ue8m0: every scale is a power of two (the quantizers' scale_ue8m0
+    output); the large-M tile then applies them inside the block-scaled MFMA."""
     a = _as_codes(a, "a")
     b = _as_codes(b, "b")
     _need_cuda(a, b, a_scale, b_scale, bias)
@@ -241,9 +244,10 @@ def scaled_mm_blockwise(a, b, a_scale, b_scale, bias=None, m=None, out=None, con
     cfg = config if config is not None else TileConfig(-1, 0, 0, 0, 1, 0)
     nws = workspace_bytes(KIND_BLOCKWISE, m, n, k, cfg)
     ws = _ws.get(a.device, nws)
-    check(_lib.load().fp8_scaled_mm_blockwise_ex(
-        _p(a), _p(b), _p(a_scale), a_scale.stride(1), _p(b_scale), _p(bias), _p(out), m, n, k,
-        a.stride(0), b.stride(0), out.stride(0), _p(ws), nws, ctypes.byref(cfg), _stream(a)))
+    lib = _lib.load()
+    fn = lib.fp8_scaled_mm_blockwise_ue8m0_ex if scale_ue8m0 else lib.fp8_scaled_mm_blockwise_ex
+    check(fn(_p(a), _p(b), _p(a_scale), a_scale.stride(1), _p(b_scale), _p(bias), _p(out), m, n, k,
+             a.stride(0), b.stride(0), out.stride(0), _p(ws), nws, ctypes.byref(cfg), _stream(a)))
     return out
 
 
@@ -435,6 +439,8 @@ def prepare(op, *args, **kwargs):
             a = (_p(a_), _p(b_), _p(sa), sa.stride(1), _p(sb), _p(bias), _p(out), m, n, k,
                  a_.stride(0), b_.stride(0), out.stride(0), _p(ws), nws, ctypes.byref(cfg),
                  _stream(a_))
-            pr = Prepared(lib.fp8_scaled_mm_blockwise_ex, a, op, (a_, b_, sa, sb, bias, out, cfg, ws))
+            fn = lib.fp8_scaled_mm_blockwise_ue8m0_ex if kwargs.get("scale_ue8m0") else \
+                lib.fp8_scaled_mm_blockwise_ex
+            pr = Prepared(fn, a, op, (a_, b_, sa, sb, bias, out, cfg, ws))
         return pr
     raise ValueError(f"unknown op {op}")

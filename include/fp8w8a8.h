@@ -54,7 +54,9 @@ enum {
   FP8_ERR_HIP = -4,
 };
 
-enum { FP8_KIND_CHANNELWISE = 0, FP8_KIND_BLOCKWISE = 1 };
+/* FP8_KIND_BLOCKWISE_UE8M0: blockwise with power-of-two scales (see
+ * fp8_scaled_mm_blockwise_ue8m0); it shares the blockwise tiles and tables. */
+enum { FP8_KIND_CHANNELWISE = 0, FP8_KIND_BLOCKWISE = 1, FP8_KIND_BLOCKWISE_UE8M0 = 2 };
 
 /* Kernel variants a tile config can name. */
 enum {
@@ -278,6 +280,33 @@ int fp8_scaled_mm_blockwise_ex(const uint8_t* a, const uint8_t* b,
                                int64_t lda, int64_t ldb, int64_t ldc,
                                void* ws, size_t ws_bytes,
                                const fp8_tile_config* cfg, hipStream_t stream);
+
+/* Blockwise FP8 scaled GEMM with UE8M0 (power-of-two) scales.
+ * [PR27896, "Key source excerpts": the group quantizer's scale_ue8m0 flag;
+ * the scales it makes (FP8_QUANT_SCALE_UE8M0) and 128x128 weight block scales
+ * rounded up the same way feed this GEMM.] Same operation, arguments, layouts
+ * and errors as fp8_scaled_mm_blockwise, and the same tile configs; every
+ * a_scale and b_scale value must be a positive power of two held as fp32
+ * (only its exponent field is used: other values give wrong results). On
+ * gfx950 the large-M tile (FP8_VARIANT_T256x256BW16) hands the exponents to
+ * the block-scaled MFMA, which applies them to the products itself instead of
+ * promoting every 128-deep block's partial sum in fp32; other tiles run the
+ * blockwise kernels, exact for powers of two. fp8_scaled_mm_workspace_size
+ * takes FP8_KIND_BLOCKWISE_UE8M0 or FP8_KIND_BLOCKWISE alike. */
+int fp8_scaled_mm_blockwise_ue8m0(const uint8_t* a, const uint8_t* b,
+                                  const float* a_scale, int64_t a_scale_ld,
+                                  const float* b_scale, const uint16_t* bias, uint16_t* out,
+                                  int64_t M, int64_t N, int64_t K,
+                                  int64_t lda, int64_t ldb, int64_t ldc,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+int fp8_scaled_mm_blockwise_ue8m0_ex(const uint8_t* a, const uint8_t* b,
+                                     const float* a_scale, int64_t a_scale_ld,
+                                     const float* b_scale, const uint16_t* bias, uint16_t* out,
+                                     int64_t M, int64_t N, int64_t K,
+                                     int64_t lda, int64_t ldb, int64_t ldc,
+                                     void* ws, size_t ws_bytes, const fp8_tile_config* cfg,
+                                     hipStream_t stream);
 
 /* Workspace bytes the GEMM of `kind` needs for (M, N, K) with `cfg` (NULL =
  * the config the library would pick). 0 when no workspace is needed.
