@@ -29,7 +29,9 @@ Variants the pages name without a body, with the readings taken: the
 quantizer's ``fuse_silu_and_mul`` flag (input [gate | up], quantized row
 bf16(silu(gate) * up)), its ``scale_ue8m0`` flag (each fp32 scale rounded up
 to a power of two), and a static per-tensor quantization with a given scale
-(codes only) -- see ``activation.py`` and ``quant.py``.
+(codes only) -- see ``activation.py`` and ``quant.py``; and its ``masked_m``
+argument (per-expert valid row counts of an [E, M_max, K] batch, feeding a
+grouped blockwise GEMM) -- see ``moe.py``.
 
 Parity unpinned: behaviour on non-finite inputs (Inf/NaN), which the pages do
 not define; every workload here is finite.
@@ -57,3 +59,4 @@ from .gemm import (  # noqa: F401
     summation_bound_channelwise,
 )
 from .check import check_gemm  # noqa: F401
+from .moe import masked_quant_per_token_group, scaled_mm_blockwise_masked  # noqa: F401

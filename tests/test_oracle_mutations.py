@@ -17,6 +17,8 @@ import test_oracle_e4m3 as pins_codec
 import test_oracle_gemm as pins_gemm
 import test_oracle_quant as pins_quant
 import test_oracle_quant_variants as pins_variants
+import test_oracle_moe as pins_moe
+import oracle.moe as moe
 
 _orig_encode = e4m3.encode
 
@@ -141,6 +143,28 @@ def _pow2_floor(s):
     return np.float32(s) if mant == 0.5 else np.float32(math.ldexp(1.0, expo - 1))
 
 
+def _masked_quant_off_by_one(x, masked_m, group_size, eps=1e-10, scale_ue8m0=False):
+    xf = np.asarray(x, np.float32)
+    e_n, m_max, k = xf.shape
+    codes = np.zeros((e_n, m_max, k), np.uint8)
+    scales = np.full((e_n, m_max, k // group_size), np.nan, np.float32)
+    for e in range(e_n):
+        rows = min(int(masked_m[e]) + 1, m_max)  # one row too many
+        codes[e, :rows], scales[e, :rows] = quant.quant_per_token_group(xf[e, :rows], group_size, eps)
+    return codes, scales
+
+
+def _grouped_mm_first_expert_weights(a, b, sa, sb, masked_m, block_n=128, block_k=128):
+    a = np.asarray(a)
+    e_n, m_max, _ = a.shape
+    out = np.full((e_n, m_max, np.asarray(b).shape[1]), np.nan)
+    for e in range(e_n):
+        rows = int(masked_m[e])
+        if rows:
+            out[e, :rows] = gemm.scaled_mm_blockwise(a[e, :rows], b[0], sa[e, :rows], sb[0])
+    return out
+
+
 def _quant_static_reciprocal(x, scale):
     s = np.float32(scale)
     return e4m3.encode((np.asarray(x, np.float32) * (np.float32(1) / s)).astype(np.float32))
@@ -180,6 +204,12 @@ MUTATIONS = [
      pins_variants.test_worked_examples),
     ("static quant multiplies by reciprocal", [(oracle, "quant_static", _quant_static_reciprocal)],
      pins_variants.test_worked_examples),
+    ("masked quant writes one row too many", [(oracle, "masked_quant_per_token_group",
+                                               _masked_quant_off_by_one)],
+     pins_moe.test_masked_quant_rows),
+    ("grouped GEMM uses expert 0's weights", [(oracle, "scaled_mm_blockwise_masked",
+                                               _grouped_mm_first_expert_weights)],
+     pins_moe.test_grouped_gemm_exact_rational),
 ]
 
 
