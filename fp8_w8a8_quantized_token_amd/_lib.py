@@ -57,6 +57,11 @@ SIGNATURES = {
                                        c_vp]),
     "fp8_quant_per_token_group_ex": (c_i32, [c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_i64,
                                              c_vp, c_f32, c_i32, c_vp]),
+    "fp8_quant_per_token_group_masked": (c_i32, [c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_i32, c_i32,
+                                                 c_vp, c_i64, c_vp, c_f32, c_i32, c_vp]),
+    "fp8_scaled_mm_blockwise_masked": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                               c_i64, c_i64, c_i64, c_i64, c_i64, c_i32,
+                                               ctypes.POINTER(TileConfig), c_vp]),
     "fp8_quant_static": (c_i32, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp]),
     "fp8_scaled_mm_channelwise": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
                                           c_i64, c_i64, c_i64, c_vp, c_size, c_vp]),

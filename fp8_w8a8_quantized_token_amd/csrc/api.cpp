@@ -245,6 +245,80 @@ int fp8_quant_per_token_group(const uint16_t* x, int64_t M, int64_t K, int64_t l
                                       0, stream);
 }
 
+int fp8_quant_per_token_group_masked(const uint16_t* x, int64_t E, int64_t M_max, int64_t K,
+                                     int64_t ldx, const int32_t* masked_m, int32_t group_size,
+                                     int32_t row_alignment, uint8_t* q, int64_t ldq, float* scale,
+                                     float eps, int32_t flags, hipStream_t stream) {
+  const char* fn = "fp8_quant_per_token_group_masked";
+  if (E < 0 || E > 65535) return fail(FP8_ERR_INVALID, "%s: E=%lld outside [0, 65535]", fn, (long long)E);
+  if (E == 0) return ok();
+  if (row_alignment < 1) return fail(FP8_ERR_INVALID, "%s: row_alignment must be >= 1", fn);
+  if (group_size <= 0) return fail(FP8_ERR_INVALID, "%s: group_size must be positive", fn);
+  if (K % group_size != 0)
+    return fail(FP8_ERR_INVALID, "%s: K=%lld must be divisible by group_size=%d", fn, (long long)K, group_size);
+  if (!(group_size == 16 || group_size == 32 || group_size == 64 || group_size == 128))
+    return fail(FP8_ERR_UNSUPPORTED, "%s: group_size %d not in {16, 32, 64, 128}", fn, group_size);
+  int st = check_quant_flags(fn, flags);
+  if (st) return st;
+  st = check_quant(fn, x, M_max, K, (flags & FP8_QUANT_FUSE_SILU_MUL) ? 2 * K : K, ldx, q, ldq, scale,
+                   eps);
+  if (st) return st;
+  if (M_max == 0 || E == 0) return ok();
+  if (!masked_m || !aligned(masked_m, 4)) return fail(FP8_ERR_INVALID, "%s: masked_m must be a 4-byte aligned pointer", fn);
+  const int64_t m_pad = fp8_padded_rows(M_max, row_alignment);
+  const MaskArgs mask{masked_m, M_max * ldx, m_pad * ldq, (K / group_size) * m_pad};
+  return hip_status(launch_quant_per_token_group_masked(x, E, M_max, K, ldx, group_size, m_pad, q, ldq,
+                                                        scale, eps, flags, mask, stream),
+                    fn);
+}
+
+int fp8_scaled_mm_blockwise_masked(const uint8_t* a, const uint8_t* b, const float* a_scale,
+                                   int64_t a_scale_ld, const float* b_scale, uint16_t* out,
+                                   const int32_t* masked_m, int64_t E, int64_t M_max, int64_t N,
+                                   int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                                   int32_t scale_ue8m0, const fp8_tile_config* cfg_in,
+                                   hipStream_t stream) {
+  const char* fn = "fp8_scaled_mm_blockwise_masked";
+  if (E < 0 || E > 65535) return fail(FP8_ERR_INVALID, "%s: E=%lld outside [0, 65535]", fn, (long long)E);
+  if (E == 0) return ok();
+  int st = check_gemm(fn, a, b, a_scale, b_scale, nullptr, out, M_max, N, K, lda, ldb, ldc);
+  if (st) return st;
+  if (M_max == 0 || E == 0) return ok();
+  if (!masked_m || !aligned(masked_m, 4)) return fail(FP8_ERR_INVALID, "%s: masked_m must be a 4-byte aligned pointer", fn);
+  if (N % 128 != 0 || K % 128 != 0)
+    return fail(FP8_ERR_UNSUPPORTED, "%s: N=%lld and K=%lld must be multiples of 128", fn, (long long)N,
+                (long long)K);
+  if (a_scale_ld < M_max || a_scale_ld % 4 != 0)
+    return fail(FP8_ERR_INVALID, "%s: a_scale_ld=%lld must be >= M_max=%lld and a multiple of 4", fn,
+                (long long)a_scale_ld, (long long)M_max);
+  fp8_tile_config cfg;
+  st = resolve_config(FP8_KIND_BLOCKWISE, M_max, N, K, cfg_in, &cfg);
+  if (st) return st;
+  if (cfg.split_k != 1) return fail(FP8_ERR_INVALID, "%s: grouped GEMMs take split_k == 1", fn);
+  if (!cfg_in || cfg_in->variant == FP8_VARIANT_DEFAULT) {
+    // the table or heuristic may name a tile without the grouped path: take
+    // the deep-ring tile of a similar size instead
+    if (cfg.variant < 15 || cfg.variant > 25)
+      cfg.variant = M_max <= 32 ? 23 : (M_max <= 128 ? 24 : (M_max <= 512 ? 19 : 25));
+  }
+  GemmArgs p{};
+  p.a = a; p.b = b; p.sa = a_scale; p.sa_ld = a_scale_ld; p.sb = b_scale; p.bias = nullptr; p.out = out;
+  p.M = M_max; p.N = N; p.K = K; p.lda = lda; p.ldb = ldb; p.ldc = ldc;
+  p.split_k = 1;
+  p.k_tiles_per_split = (int)(K / 128);
+  p.masked_m = masked_m;
+  p.experts = (int)E;
+  p.a_es = a_scale_ld * lda;
+  p.sa_es = (K / 128) * a_scale_ld;
+  p.b_es = N * ldb;
+  p.sb_es = (N / 128) * (K / 128);
+  p.out_es = M_max * ldc;
+  if (!grouped_launchable(cfg.variant, p))
+    return fail(FP8_ERR_UNSUPPORTED, "%s: variant %d is not a blockwise panel tile, or the offsets exceed "
+                "its 32-bit DMA range", fn, cfg.variant);
+  return hip_status(launch_gemm(scale_ue8m0 ? kBlockwiseE8 : kBlockwise, cfg.variant, p, stream), fn);
+}
+
 int fp8_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const float* scale,
                      uint8_t* q, int64_t ldq, hipStream_t stream) {
   const char* fn = "fp8_quant_static";

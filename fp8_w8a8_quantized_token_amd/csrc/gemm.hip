@@ -877,6 +877,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   tile_coords(tile, tiles_m, tiles_n, &tile_m, &tile_n);
   const int64_t m0 = tile_m * BM;
   const int64_t n0 = tile_n * BN;
+  // grouped (MoE experts): expert blockIdx.z has masked_m[e] valid rows of
+  // its own M-row slab; the tile order covers all M rows, and tiles wholly
+  // past the valid rows leave here, before any barrier or LDS use
+  if (p.masked_m) {
+    const int64_t e = blockIdx.z;
+    int64_t rows = p.masked_m[e];
+    rows = rows < 0 ? 0 : (rows > p.M ? p.M : rows);
+    if (m0 >= rows) return;
+    p.M = rows;
+    p.a += e * p.a_es;
+    p.sa += e * p.sa_es;
+    p.b += e * p.b_es;
+    p.sb += e * p.sb_es;
+    p.out += e * p.out_es;
+  }
   const int split = blockIdx.y;
   const int64_t kt_all = p.K / BK;
   const int64_t kt_begin = (int64_t)split * p.k_tiles_per_split;
@@ -1530,8 +1545,9 @@ hipError_t launch_panel(const GemmArgs& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     lds_attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)tiles, (unsigned)p.split_k), dim3(WM * WN * 64), lds,
-                     stream, p);
+  const unsigned experts = p.masked_m ? (unsigned)p.experts : 1u;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles, (unsigned)p.split_k, experts), dim3(WM * WN * 64),
+                     lds, stream, p);
   return hipGetLastError();
 }
 
@@ -1725,7 +1741,13 @@ hipError_t launch_linear_fused(int kind, const GemmArgs& p, const QuantArgs& qa,
                               : launch_fused_kind<kBlockwise>(p, qa, stream);
 }
 
+bool grouped_launchable(int variant, const GemmArgs& p) {
+  return variant >= 15 && variant <= 25 && p.split_k == 1 && panel_eligible<kBlockwise>(p);
+}
+
 hipError_t launch_gemm(int kind, int variant, const GemmArgs& p, hipStream_t stream) {
+  // grouped calls may reach only the panel tiles (the kernels that read masked_m)
+  if (p.masked_m && (kind == kChannelwise || !grouped_launchable(variant, p))) return hipErrorInvalidValue;
   if (kind == kBlockwiseE8) {
     // the block-scaled MFMA serves the 16x16 256x256 tile; every other tile
     // promotes in fp32, which is exact for power-of-two scales

@@ -11,6 +11,14 @@ namespace fp8w8a8 {
 // of the quantized row.
 enum QuantFlag { kQuantSiluMul = 1, kQuantUe8m0 = 2 };
 
+// Masked per-expert quantization: expert e (grid y) has masked_m[e] valid
+// rows (clamped to [0, M]) of an M-row slab; slabs are x_es, q_es and s_es
+// elements apart. Null masked_m: one plain batch.
+struct MaskArgs {
+  const int* masked_m;
+  int64_t x_es, q_es, s_es;
+};
+
 hipError_t launch_quant_per_token(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                   uint8_t* q, int64_t ldq, float* scale, float eps, int flags,
                                   hipStream_t stream);
@@ -18,6 +26,13 @@ hipError_t launch_quant_per_token(const uint16_t* x, int64_t M, int64_t K, int64
 hipError_t launch_quant_per_token_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                         int group_size, int64_t m_pad, uint8_t* q, int64_t ldq,
                                         float* scale, float eps, int flags, hipStream_t stream);
+
+// The same over `experts` slabs with per-expert valid row counts (M = M_max).
+hipError_t launch_quant_per_token_group_masked(const uint16_t* x, int64_t experts, int64_t M,
+                                               int64_t K, int64_t ldx, int group_size,
+                                               int64_t m_pad, uint8_t* q, int64_t ldq, float* scale,
+                                               float eps, int flags, const MaskArgs& mask,
+                                               hipStream_t stream);
 
 hipError_t launch_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                const float* scale, uint8_t* q, int64_t ldq, hipStream_t stream);
@@ -41,7 +56,14 @@ struct GemmArgs {
   int* ws_count;       // split-K arrival counters, one per output tile
   int split_k;
   int k_tiles_per_split;  // 128-deep K steps handled by one split
+  // Grouped (MoE experts, panel tiles only, split_k == 1): `experts` GEMMs,
+  // expert e (blockIdx.z) on slabs offset by e times the strides below
+  // (elements), with masked_m[e] valid rows of M (= M_max); null: one GEMM.
+  const int* masked_m;
+  int experts;
+  int64_t a_es, sa_es, b_es, sb_es, out_es;
 };
+
 
 // Activation quantization fused into the skinny GEMM (M <= kFusedRows): the
 // kernel reads bf16 x instead of codes and scales, quantizes it as the
@@ -87,5 +109,9 @@ constexpr size_t kCounterBytes = (size_t)kMaxSplitTiles * sizeof(int);
 size_t variant_workspace_bytes(int variant, int split_k, int64_t M, int64_t N);
 
 hipError_t launch_gemm(int kind, int variant, const GemmArgs& args, hipStream_t stream);
+
+// Grouped blockwise GEMMs run only on the blockwise panel tiles (variants
+// 15-25) with split_k == 1; true when `variant` and the arguments allow it.
+bool grouped_launchable(int variant, const GemmArgs& args);
 
 }  // namespace fp8w8a8

@@ -229,11 +229,23 @@ __global__ __launch_bounds__(256) void quant_per_token_long_kernel(
 // absmax is an xor-shuffle reduction over TPG lanes). Units are numbered
 // row-major over [M, K/16]; a group never straddles a row since G divides K.
 // ---------------------------------------------------------------------------
-template <int TPG, int FLAGS>
+// MASKED: grid y runs over experts; expert e quantizes the first masked_m[e]
+// rows (clamped to [0, M]) of its own slab and leaves the rest untouched.
+template <int TPG, int FLAGS, bool MASKED = false>
 __global__ __launch_bounds__(256) void quant_group_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, uint8_t* __restrict__ q,
-    int64_t ldq, float* __restrict__ scale, int64_t m_pad, float eps) {
+    int64_t ldq, float* __restrict__ scale, int64_t m_pad, float eps, MaskArgs mask) {
   const int64_t units_per_row = K >> 4;
+  if constexpr (MASKED) {
+    const int64_t e = blockIdx.y;
+    int64_t rows = mask.masked_m[e];
+    rows = rows < 0 ? 0 : (rows > M ? M : rows);
+    if ((int64_t)blockIdx.x * blockDim.x >= rows * units_per_row) return;  // whole block past the rows
+    M = rows;
+    x += e * mask.x_es;
+    q += e * mask.q_es;
+    scale += e * mask.s_es;
+  }
   const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const bool live = u < M * units_per_row;
   const int64_t row = live ? u / units_per_row : 0;
@@ -324,24 +336,47 @@ void launch_per_token_flags(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
     hipLaunchKernelGGL((quant_per_token_long_kernel<FLAGS>), grid, dim3(256), 0, stream, x, K, ldx, q, ldq, scale, eps);
 }
 
-template <int FLAGS>
-void launch_group_flags(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int group_size,
-                        int64_t m_pad, uint8_t* q, int64_t ldq, float* scale, float eps,
-                        hipStream_t stream) {
+template <int FLAGS, bool MASKED>
+void launch_group_flags(const uint16_t* x, int64_t experts, int64_t M, int64_t K, int64_t ldx,
+                        int group_size, int64_t m_pad, uint8_t* q, int64_t ldq, float* scale,
+                        float eps, const MaskArgs& mask, hipStream_t stream) {
   const int64_t units = M * (K >> 4);
-  const dim3 block(256), grid((unsigned)((units + 255) / 256));
+  const dim3 block(256), grid((unsigned)((units + 255) / 256), (unsigned)(MASKED ? experts : 1));
   switch (group_size) {
     case 16:
-      hipLaunchKernelGGL((quant_group_kernel<1, FLAGS>), grid, block, 0, stream, x, M, K, ldx, q, ldq, scale, m_pad, eps);
+      hipLaunchKernelGGL((quant_group_kernel<1, FLAGS, MASKED>), grid, block, 0, stream, x, M, K, ldx, q, ldq, scale, m_pad, eps, mask);
       break;
     case 32:
-      hipLaunchKernelGGL((quant_group_kernel<2, FLAGS>), grid, block, 0, stream, x, M, K, ldx, q, ldq, scale, m_pad, eps);
+      hipLaunchKernelGGL((quant_group_kernel<2, FLAGS, MASKED>), grid, block, 0, stream, x, M, K, ldx, q, ldq, scale, m_pad, eps, mask);
       break;
     case 64:
-      hipLaunchKernelGGL((quant_group_kernel<4, FLAGS>), grid, block, 0, stream, x, M, K, ldx, q, ldq, scale, m_pad, eps);
+      hipLaunchKernelGGL((quant_group_kernel<4, FLAGS, MASKED>), grid, block, 0, stream, x, M, K, ldx, q, ldq, scale, m_pad, eps, mask);
       break;
     default:
-      hipLaunchKernelGGL((quant_group_kernel<8, FLAGS>), grid, block, 0, stream, x, M, K, ldx, q, ldq, scale, m_pad, eps);
+      hipLaunchKernelGGL((quant_group_kernel<8, FLAGS, MASKED>), grid, block, 0, stream, x, M, K, ldx, q, ldq, scale, m_pad, eps, mask);
+      break;
+  }
+}
+
+template <bool MASKED>
+void launch_group_any(const uint16_t* x, int64_t experts, int64_t M, int64_t K, int64_t ldx,
+                      int group_size, int64_t m_pad, uint8_t* q, int64_t ldq, float* scale,
+                      float eps, int flags, const MaskArgs& mask, hipStream_t stream) {
+  switch (flags & (kQuantSiluMul | kQuantUe8m0)) {
+    case 0:
+      launch_group_flags<0, MASKED>(x, experts, M, K, ldx, group_size, m_pad, q, ldq, scale, eps, mask, stream);
+      break;
+    case kQuantSiluMul:
+      launch_group_flags<kQuantSiluMul, MASKED>(x, experts, M, K, ldx, group_size, m_pad, q, ldq, scale,
+                                                eps, mask, stream);
+      break;
+    case kQuantUe8m0:
+      launch_group_flags<kQuantUe8m0, MASKED>(x, experts, M, K, ldx, group_size, m_pad, q, ldq, scale,
+                                              eps, mask, stream);
+      break;
+    default:
+      launch_group_flags<kQuantSiluMul | kQuantUe8m0, MASKED>(x, experts, M, K, ldx, group_size, m_pad,
+                                                              q, ldq, scale, eps, mask, stream);
       break;
   }
 }
@@ -365,19 +400,18 @@ hipError_t launch_quant_per_token(const uint16_t* x, int64_t M, int64_t K, int64
 hipError_t launch_quant_per_token_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                         int group_size, int64_t m_pad, uint8_t* q, int64_t ldq,
                                         float* scale, float eps, int flags, hipStream_t stream) {
-  switch (flags & (kQuantSiluMul | kQuantUe8m0)) {
-    case 0: launch_group_flags<0>(x, M, K, ldx, group_size, m_pad, q, ldq, scale, eps, stream); break;
-    case kQuantSiluMul:
-      launch_group_flags<kQuantSiluMul>(x, M, K, ldx, group_size, m_pad, q, ldq, scale, eps, stream);
-      break;
-    case kQuantUe8m0:
-      launch_group_flags<kQuantUe8m0>(x, M, K, ldx, group_size, m_pad, q, ldq, scale, eps, stream);
-      break;
-    default:
-      launch_group_flags<kQuantSiluMul | kQuantUe8m0>(x, M, K, ldx, group_size, m_pad, q, ldq, scale,
-                                                      eps, stream);
-      break;
-  }
+  const MaskArgs none{};
+  launch_group_any<false>(x, 1, M, K, ldx, group_size, m_pad, q, ldq, scale, eps, flags, none, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_per_token_group_masked(const uint16_t* x, int64_t experts, int64_t M,
+                                               int64_t K, int64_t ldx, int group_size,
+                                               int64_t m_pad, uint8_t* q, int64_t ldq, float* scale,
+                                               float eps, int flags, const MaskArgs& mask,
+                                               hipStream_t stream) {
+  launch_group_any<true>(x, experts, M, K, ldx, group_size, m_pad, q, ldq, scale, eps, flags, mask,
+                         stream);
   return hipGetLastError();
 }
 

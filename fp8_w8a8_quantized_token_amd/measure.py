@@ -284,6 +284,73 @@ def measure_ue8m0_gemm(warmup, calls, filler):
     return lines
 
 
+# MoE experts (the blockwise workload's expert shapes): E experts of M_max
+# rows each, every expert full or a seeded random count in [0, M_max].
+MOE_SHAPES = [(3072, 4096), (4096, 1536)]
+MOE_MAX = (4, 16, 64, 256, 512)
+MOE_E = 8
+
+
+def measure_moe(warmup, calls, filler):
+    """Grouped blockwise GEMM (and the masked quantizer feeding it) over
+    MOE_E experts, weight sets rotated to cover >= 1 GiB, batch-timed."""
+    dev = torch.device("cuda:0")
+    head = ("| N×K | E | M_max | rows (valid) | GEMM µs | TFLOP/s (valid rows) | weight GB/s | "
+            "masked quant µs |")
+    lines = [head, "|---|---|---|---|---|---|---|---|"]
+    print(head, flush=True)
+    print(lines[1], flush=True)
+    gen = torch.Generator().manual_seed(5)
+    for n, k in MOE_SHAPES:
+        wbytes = MOE_E * n * k
+        sets = max(2, min(MAX_SETS, math.ceil(ROTATE_BYTES / wbytes)))
+        w = synth.weights("measure/moe", n, k).to(torch.bfloat16).to(dev)
+        wq, _ = ops.quant_per_token_group(w, 128, row_alignment=1)
+        wq = wq.contiguous()
+        del w
+        ws = synth.positive_scales(f"measure/moe/{n}/{k}", (n // 128, k // 128)).to(dev)
+        weights = [(wq.unsqueeze(0).repeat(MOE_E, 1, 1), ws.unsqueeze(0).repeat(MOE_E, 1, 1).contiguous())
+                   for _ in range(sets)]
+        for m_max in MOE_MAX:
+            for full in (True, False):
+                counts = torch.full((MOE_E,), m_max, dtype=torch.int32) if full else \
+                    torch.randint(0, m_max + 1, (MOE_E,), generator=gen, dtype=torch.int32)
+                valid = int(counts.sum())
+                cd = counts.to(dev)
+                x = torch.stack([synth.activations(f"measure/moe/{e}", m_max, k) for e in range(MOE_E)]).to(dev)
+                q, st = ops.masked_quant_per_token_group(x, cd, 128)
+                out = torch.empty((MOE_E, m_max, n), dtype=torch.bfloat16, device=dev)
+                fns = [lambda wt=wt, sc=sc: ops.scaled_mm_blockwise_masked(q, wt, st, sc, cd, m_max=m_max,
+                                                                          out=out)
+                       for wt, sc in weights]
+                tq = []
+                for fn_set, dst in ((fns, None), ([lambda: ops.masked_quant_per_token_group(x, cd, 128, out=q,
+                                                  scale_storage=st.transpose(1, 2))], tq)):
+                    for i in range(warmup):
+                        fn_set[i % len(fn_set)]()
+                    torch.cuda.synchronize()
+                    filler(calls)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for i in range(calls):
+                        fn_set[i % len(fn_set)]()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    t = e0.elapsed_time(e1) * 1e3 / calls
+                    if dst is None:
+                        us = t
+                    else:
+                        dst.append(t)
+                line = (f"| {n}×{k} | {MOE_E} | {m_max} | {valid} ({'full' if full else 'random'}) | "
+                        f"{us:.1f} | {2 * valid * n * k / us / 1e6:.0f} | "
+                        f"{wbytes / us / 1e3:.0f} | {tq[0]:.1f} |")
+                lines.append(line)
+                print(line, flush=True)
+        del weights
+        torch.cuda.empty_cache()
+    return lines
+
+
 HEADER = ("| workload | kind | N×K | M | tile config | weight GiB rotated | GEMM µs p50 (p10–p90) | "
           "TFLOP/s | GB/s | frac HBM | frac MFMA | quant µs p50 (GB/s) | linear µs p50 (launches) | "
           "hot GEMM µs p50 |")
@@ -316,15 +383,18 @@ def main(argv=None):
                     help="time the quantizer variants (SiLU-and-mul, UE8M0, static) instead")
     ap.add_argument("--ue8m0-gemm", action="store_true",
                     help="time the 16x16 blockwise tile with fp32 and with power-of-two scales")
+    ap.add_argument("--moe", action="store_true",
+                    help="time the masked quantizer and grouped blockwise GEMM over MoE experts")
     args = ap.parse_args(argv)
     _lib.load()
     dev = torch.device("cuda:0")
     want = args.workloads.split(",")
     filler = _Filler(dev)
-    if args.quant_variants or args.ue8m0_gemm:
+    if args.quant_variants or args.ue8m0_gemm or args.moe:
         t0 = time.time()
-        lines = (measure_quant_variants if args.quant_variants else measure_ue8m0_gemm)(
-            args.warmup, args.calls, filler)
+        mode = measure_quant_variants if args.quant_variants else (
+            measure_ue8m0_gemm if args.ue8m0_gemm else measure_moe)
+        lines = mode(args.warmup, args.calls, filler)
         note = (f"\n{args.calls} launches per row after {args.warmup} warm-up launches, timed as "
                 f"one batch with HIP events (average per launch); GB/s from algorithmic bytes "
                 f"(bf16 input, codes, scales); weight sets rotated to cover >= 1 GiB. "

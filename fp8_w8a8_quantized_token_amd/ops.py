@@ -29,7 +29,8 @@ from ._lib import KIND_BLOCKWISE, KIND_CHANNELWISE, TileConfig, VARIANTS, check
 
 __all__ = [
     "prepare", "padded_rows", "quant_per_token", "quant_per_token_group", "silu_mul_quant_per_token",
-    "silu_mul_quant_per_token_group", "quant_static", "scaled_mm_channelwise",
+    "silu_mul_quant_per_token_group", "quant_static", "masked_quant_per_token_group",
+    "scaled_mm_blockwise_masked", "scaled_mm_channelwise",
     "scaled_mm_blockwise", "linear_channelwise", "linear_blockwise", "tile_config",
     "default_tile_config", "set_config_dir", "workspace_bytes", "make_config", "linear_launches",
 ]
@@ -169,6 +170,74 @@ def silu_mul_quant_per_token_group(x, group_size=128, eps=1e-10, row_alignment=4
     scales (as quant_per_token_group) of bf16(silu(gate) * up)."""
     return quant_per_token_group(x, group_size, eps, row_alignment, out, scale_storage,
                                  silu_mul=True, scale_ue8m0=scale_ue8m0)
+
+
+def masked_quant_per_token_group(x, masked_m, group_size=128, eps=1e-10, row_alignment=4, out=None,
+                                 scale_storage=None, silu_mul=False, scale_ue8m0=False):
+    """MoE experts: x bf16 [E, M_max, K] (or [E, M_max, 2K] = [gate | up] with
+    silu_mul), masked_m int32 [E] on the device (valid rows per expert) ->
+    (codes uint8 [E, M_pad, K], scales fp32 [E, M_pad, K/G] as a view of
+    [E, K/G, M_pad] storage). Rows at or beyond masked_m[e] are left unwritten."""
+    if x.dtype != torch.bfloat16 or x.dim() != 3:
+        raise TypeError("x must be a 3-D bf16 tensor [E, M_max, K]")
+    _need_cuda(x, masked_m)
+    if x.stride(2) != 1 or x.stride(0) != x.shape[1] * x.stride(1):
+        raise ValueError("x must hold contiguous rows and expert slabs of M_max rows")
+    if masked_m.dtype != torch.int32 or masked_m.numel() != x.shape[0] or not masked_m.is_contiguous():
+        raise TypeError("masked_m must be a contiguous int32 tensor of E counts")
+    e_n, m_max, k = x.shape
+    if silu_mul:
+        if k % 2:
+            raise ValueError("a SiLU-and-mul input holds [gate | up]: an even number of columns")
+        k //= 2
+    if group_size <= 0 or k % group_size != 0:
+        raise ValueError("the last dimension of x must be divisible by group_size")
+    m_pad = padded_rows(m_max, row_alignment)
+    q = out if out is not None else torch.empty((e_n, m_pad, k), dtype=torch.uint8, device=x.device)
+    st = scale_storage if scale_storage is not None else torch.empty(
+        (e_n, k // group_size, m_pad), dtype=torch.float32, device=x.device)
+    if q.shape != (e_n, m_pad, k) or not q.is_contiguous() or st.shape != (e_n, k // group_size, m_pad) \
+            or not st.is_contiguous():
+        raise ValueError("out must be [E, M_pad, K] and scale_storage [E, K/G, M_pad], contiguous")
+    check(_lib.load().fp8_quant_per_token_group_masked(
+        _p(x), e_n, m_max, k, x.stride(1), _p(masked_m), group_size, row_alignment, _p(q), k, _p(st),
+        float(eps), _flags(silu_mul, scale_ue8m0), _stream(x)))
+    return q, st.transpose(1, 2)
+
+
+def scaled_mm_blockwise_masked(a, b, a_scale, b_scale, masked_m, m_max=None, out=None, config=None,
+                               scale_ue8m0=False):
+    """Grouped blockwise GEMM over E experts: a codes [E, M_pad, K], a_scale an
+    [E, M_pad, K/128] view of [E, K/128, M_pad] storage (as returned by
+    masked_quant_per_token_group), b codes [E, N, K], b_scale fp32
+    [E, N/128, K/128], masked_m int32 [E] on the device -> bf16 [E, M_max, N]
+    whose rows at or beyond masked_m[e] are left unwritten (m_max defaults
+    to M_pad)."""
+    a = _as_codes(a, "a")
+    b = _as_codes(b, "b")
+    _need_cuda(a, b, a_scale, b_scale, masked_m)
+    e_n, m_pad, k = a.shape
+    n = b.shape[1]
+    m_max = m_pad if m_max is None else int(m_max)
+    if b.shape != (e_n, n, k) or not a.is_contiguous() or not b.is_contiguous():
+        raise ValueError("a [E, M_pad, K] and b [E, N, K] must be contiguous and agree on E and K")
+    if a_scale.dtype != torch.float32 or b_scale.dtype != torch.float32:
+        raise TypeError("scales must be fp32")
+    if a_scale.shape != (e_n, m_pad, k // 128) or a_scale.stride() != ((k // 128) * m_pad, 1, m_pad):
+        raise ValueError("a_scale must be an [E, M_pad, K/128] view of [E, K/128, M_pad] storage")
+    if b_scale.shape != (e_n, n // 128, k // 128) or not b_scale.is_contiguous():
+        raise ValueError("b_scale must be contiguous [E, N/128, K/128]")
+    if masked_m.dtype != torch.int32 or masked_m.numel() != e_n or not masked_m.is_contiguous():
+        raise TypeError("masked_m must be a contiguous int32 tensor of E counts")
+    if out is None:
+        out = torch.empty((e_n, m_max, n), dtype=torch.bfloat16, device=a.device)
+    if out.shape != (e_n, m_max, n) or not out.is_contiguous():
+        raise ValueError("out must be contiguous [E, M_max, N]")
+    cfg = config if config is not None else TileConfig(-1, 0, 0, 0, 1, 0)
+    check(_lib.load().fp8_scaled_mm_blockwise_masked(
+        _p(a), _p(b), _p(a_scale), m_pad, _p(b_scale), _p(out), _p(masked_m), e_n, m_max, n, k, k, k,
+        n, 1 if scale_ue8m0 else 0, ctypes.byref(cfg), _stream(a)))
+    return out
 
 
 def quant_static(x, scale, out=None):

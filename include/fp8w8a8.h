@@ -192,6 +192,50 @@ int fp8_quant_per_token_group_ex(const uint16_t* x, int64_t M, int64_t K, int64_
                                  uint8_t* q, int64_t ldq, float* scale, float eps,
                                  int32_t flags, hipStream_t stream);
 
+/* Masked per-expert group quantization (MoE experts).
+ * [PR27896, "Key source excerpts": the group quantizer's kernel call takes a
+ * masked_m argument (None there; no body shown). Reading: an [E, M_max, K]
+ * batch of expert slabs whose first masked_m[e] rows are valid.] For every
+ * expert e and row m < masked_m[e], exactly fp8_quant_per_token_group_ex on
+ * that row (flags as there); all other rows of q and scale are NOT written.
+ *   x         bf16 [E][M_max][ldx] (ldx >= K, or >= 2K with SiLU-and-mul)
+ *   masked_m  int32 [E], DEVICE memory, read by the kernel; each value is
+ *             clamped to [0, M_max] (so a bad count cannot write out of bounds)
+ *   q         E4M3 [E][M_pad][ldq], M_pad = fp8_padded_rows(M_max, row_alignment)
+ *   scale     fp32 [E][K/G][M_pad]  (column-major per expert)
+ * E <= 65535; other arguments and errors as fp8_quant_per_token_group_ex. */
+int fp8_quant_per_token_group_masked(const uint16_t* x, int64_t E, int64_t M_max, int64_t K,
+                                     int64_t ldx, const int32_t* masked_m, int32_t group_size,
+                                     int32_t row_alignment, uint8_t* q, int64_t ldq, float* scale,
+                                     float eps, int32_t flags, hipStream_t stream);
+
+/* Grouped blockwise FP8 GEMM over E experts with per-expert valid rows.
+ * [PR27896: the masked_m argument above; each expert is the blockwise GEMM
+ * of that digest on its own weight.] For every expert e and row m <
+ * masked_m[e] (clamped to [0, M_max]):
+ *   out[e][m][n] = bf16_RNE(sum_kb a_scale[e][kb][m] b_scale[e][n/128][kb]
+ *                          sum_{k in kb} dec(a[e][m][k]) dec(b[e][n][k])),
+ * no bias; other rows of out are NOT written.
+ *   a         E4M3 [E][a_scale_ld][lda] (the masked quantizer's q, M_pad rows)
+ *   a_scale   fp32 [E][K/128][a_scale_ld], a_scale_ld >= M_max, a multiple of 4
+ *   b         E4M3 [E][N][ldb];  b_scale fp32 [E][N/128][K/128]
+ *   out       bf16 [E][M_max][ldc]
+ *   masked_m  int32 [E], device memory
+ *   scale_ue8m0  non-zero: every scale is a power of two (as
+ *             fp8_scaled_mm_blockwise_ue8m0)
+ *   cfg       NULL or FP8_VARIANT_DEFAULT: the blockwise table at (N, K, M_max),
+ *             any tile without a grouped path replaced by a deep-ring tile of
+ *             similar size; else one of the blockwise panel tiles
+ *             (FP8_VARIANT_T256x128PANEL .. FP8_VARIANT_T256x256BW16), split_k 1.
+ * Errors as fp8_scaled_mm_blockwise; FP8_ERR_UNSUPPORTED for a tile without
+ * the grouped path. E <= 65535. */
+int fp8_scaled_mm_blockwise_masked(const uint8_t* a, const uint8_t* b, const float* a_scale,
+                                   int64_t a_scale_ld, const float* b_scale, uint16_t* out,
+                                   const int32_t* masked_m, int64_t E, int64_t M_max, int64_t N,
+                                   int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                                   int32_t scale_ue8m0, const fp8_tile_config* cfg,
+                                   hipStream_t stream);
+
 /* Static per-tensor FP8 quantization with a given scale.
  * [PR31340, "Implementation" step 2 and "Key files": a static FP8
  * quantization kernel; the ModelOpt FP8 linear carries a precomputed

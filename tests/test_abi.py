@@ -100,6 +100,35 @@ def test_quant_variant_argument_errors(lib):
     assert st(None, 0, 128, 128, None, None, 128, None) == _lib.FP8_OK
 
 
+def test_moe_argument_errors(lib):
+    mq = lib.fp8_quant_per_token_group_masked
+    assert mq(FAKE, 70000, 4, 256, 256, FAKE, 128, 4, FAKE, 256, FAKE, 1e-10, 0, None) == _lib.FP8_ERR_INVALID
+    assert mq(FAKE, 8, 4, 256, 256, None, 128, 4, FAKE, 256, FAKE, 1e-10, 0, None) == _lib.FP8_ERR_INVALID
+    assert "masked_m" in _err(lib)
+    assert mq(FAKE, 8, 4, 256, 256, FAKE, 96, 4, FAKE, 256, FAKE, 1e-10, 0, None) == _lib.FP8_ERR_INVALID
+    assert mq(FAKE, 8, 4, 256, 256, FAKE, 128, 4, FAKE, 256, FAKE, 1e-10, 1, None) == _lib.FP8_ERR_INVALID
+    assert mq(None, 0, 4, 256, 256, None, 128, 4, None, 256, None, 1e-10, 0, None) == _lib.FP8_OK
+    mm = lib.fp8_scaled_mm_blockwise_masked
+    args = dict(a=FAKE, b=FAKE, sa=FAKE, ld=64, sb=FAKE, out=FAKE, mask=FAKE, E=8, M=64, N=512, K=1024)
+
+    def call(cfg=None, **kw):
+        a = dict(args, **kw)
+        return mm(a["a"], a["b"], a["sa"], a["ld"], a["sb"], a["out"], a["mask"], a["E"], a["M"], a["N"],
+                  a["K"], a["K"], a["K"], a["N"], 0, ctypes.byref(cfg) if cfg is not None else None, None)
+
+    assert call(mask=None) == _lib.FP8_ERR_INVALID
+    assert call(ld=62) == _lib.FP8_ERR_INVALID
+    assert call(ld=66) == _lib.FP8_ERR_INVALID  # a multiple of 4 is required
+    assert call(N=504) == _lib.FP8_ERR_UNSUPPORTED
+    assert call(E=70000) == _lib.FP8_ERR_INVALID
+    split2 = _lib.TileConfig(_lib.VARIANTS["t64x64deep"], 0, 0, 0, 2, 0)
+    assert call(cfg=split2) == _lib.FP8_ERR_INVALID
+    assert "split_k" in _err(lib)
+    tile = _lib.TileConfig(_lib.VARIANTS["t128x128"], 0, 0, 0, 1, 0)
+    assert call(cfg=tile) == _lib.FP8_ERR_UNSUPPORTED
+    assert call(E=0) == _lib.FP8_OK and call(M=0) == _lib.FP8_OK
+
+
 def test_gemm_argument_errors(lib):
     cw = lib.fp8_scaled_mm_channelwise
     assert cw(None, FAKE, FAKE, FAKE, None, FAKE, 4, 256, 512, 512, 512, 256, None, 0, None) == _lib.FP8_ERR_INVALID
