@@ -189,3 +189,38 @@ def test_static_bit_exact(wl, m, k, sc):
     rows = sample_rows(m, count=256)
     want = oracle.quant_static(x[rows].float().numpy(), np.float32(sc))
     _assert_codes(q.cpu().numpy()[rows], want)
+
+
+# ---------------------------------------------------------------- composed with the GEMMs
+@pytest.mark.parametrize("m", [1, 4, 64, 512])
+def test_silu_quant_feeds_down_projection(m):
+    """The gate/up output of Qwen3-8B (24576 wide) through the fused SiLU-and-mul
+    per-token quantizer into the channelwise down projection (N=4096, K=12288),
+    and the MoE expert's 3072-wide output through the group-128 form into its
+    blockwise down projection (N=4096, K=1536): GEMM outputs within the GEMM
+    tolerance of the oracle's composition."""
+    from gpu_common import bf16_to_f64, weight_blockwise, weight_channelwise
+
+    x = activations("silu_down", m, 2 * 12288)
+    say("silu -> channelwise down", m)
+    q, s = ops.silu_mul_quant_per_token(gpu(x))
+    bq, bs = weight_channelwise("silu_down_w", 4096, 12288)
+    out = ops.scaled_mm_channelwise(q, gpu(bq), s, gpu(bs))
+    torch.cuda.synchronize()
+    aq, as_ = oracle.silu_mul_quant_per_token(x.float().numpy())
+    ref = oracle.scaled_mm_channelwise(aq, bq, as_, bs)
+    tau = oracle.summation_bound_channelwise(aq, bq, as_, bs)
+    res = oracle.check_gemm(bf16_to_f64(out), ref, tau)
+    assert res["ok"] and res["cosine"] > 0.9999, res
+
+    x2 = activations("silu_down_moe", m, 2 * 1536)
+    say("silu -> blockwise down", m)
+    q2, s2 = ops.silu_mul_quant_per_token_group(gpu(x2), 128)
+    wq, ws = weight_blockwise("silu_down_moe_w", 4096, 1536)
+    out2 = ops.scaled_mm_blockwise(q2, gpu(wq), s2, gpu(ws), m=m)
+    torch.cuda.synchronize()
+    aq2, as2 = oracle.silu_mul_quant_per_token_group(x2.float().numpy(), 128)
+    ref2 = oracle.scaled_mm_blockwise(aq2, wq, as2, ws)
+    tau2 = oracle.summation_bound_blockwise(aq2, wq, as2, ws)
+    res2 = oracle.check_gemm(bf16_to_f64(out2), ref2, tau2)
+    assert res2["ok"] and res2["cosine"] > 0.9999, res2
