@@ -71,7 +71,7 @@ def test_silu_per_token_full_size_sampled_rows():
 
 SILU_GROUP_CASES = (
     [("block_moe_down_in", m, 1536, 128, 4) for m in (1, 4, 16, 64, 4096)]
-    + [("qwen3_8b_down_in", m, 12288, 128, 4) for m in (1, 13, 256)]
+    + [("qwen3_8b_down_in", m, 12288, 128, 4) for m in (1, 13, 256, 2048)]
     + [("silu_groups", m, 1024, g, ra) for g in (16, 32, 64) for m, ra in ((1, 4), (37, 4), (9, 8))]
 )
 
