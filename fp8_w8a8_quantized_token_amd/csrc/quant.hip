@@ -94,13 +94,13 @@ __device__ __forceinline__ uint4 silu_mul8(const uint4& g, const uint4& u) {
   const uint32_t gp[4] = {g.x, g.y, g.z, g.w};
   const uint32_t up[4] = {u.x, u.y, u.z, u.w};
   float gf[8], uf[8], y[8];
-  uint32_t redo = 0;
+  bool redo = false;  // a lane mask: the per-value tests are repeated in the rare branch
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     gf[i] = bf16_to_f32((i & 1) ? (gp[i >> 1] >> 16) : (gp[i >> 1] & 0xffffu));
     uf[i] = bf16_to_f32((i & 1) ? (up[i >> 1] >> 16) : (up[i >> 1] & 0xffffu));
     y[i] = silu_mul_f32(gf[i], uf[i]);
-    redo |= silu_needs_f64(gf[i], y[i]) ? (1u << i) : 0u;
+    redo = redo || silu_needs_f64(gf[i], y[i]);
   }
   uint32_t o[4];
 #pragma unroll
@@ -108,7 +108,7 @@ __device__ __forceinline__ uint4 silu_mul8(const uint4& g, const uint4& u) {
   if (redo) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (redo & (1u << i)) {
+      if (silu_needs_f64(gf[i], y[i])) {
         const uint32_t b = silu_mul_bf16_f64(gf[i], uf[i]);
         o[i >> 1] = (i & 1) ? ((o[i >> 1] & 0xffffu) | (b << 16)) : ((o[i >> 1] & 0xffff0000u) | b);
       }
