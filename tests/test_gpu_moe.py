@@ -114,3 +114,47 @@ def test_grouped_gemm(e_n, m_max, n, k, variant, ue8m0):
         res = oracle.check_gemm(got[e, rows], ref, tau)
         assert res["ok"], (e, res)
         assert res["cosine"] > 0.9999, (e, res)
+
+
+def test_out_of_range_counts_are_clamped():
+    """masked_m lives in device memory, so the host cannot check it: the
+    kernels clamp every count into [0, M_max]. Negative counts act as 0, counts
+    past M_max as M_max, and nothing outside the expert slabs is written (the
+    buffers carry a guard expert on each side)."""
+    e_n, m_max, n, k = 4, 24, 256, 512
+    raw = np.array([-3, 30, 7, m_max + 1000], dtype=np.int32)
+    clamped = np.clip(raw, 0, m_max)
+    x = _batch("moe-clamp", e_n, m_max, k)
+    say("clamped counts", raw.tolist())
+    m_pad = ops.padded_rows(m_max, 4)
+    # experts 1..e_n of e_n + 2 slabs; slabs 0 and e_n + 1 are guards
+    q_all = torch.full((e_n + 2, m_pad, k), 0x7F, dtype=torch.uint8, device=device())
+    s_all = torch.full((e_n + 2, k // 128, m_pad), float("nan"), dtype=torch.float32, device=device())
+    q, s = ops.masked_quant_per_token_group(gpu(x), gpu(raw), 128, out=q_all[1:e_n + 1],
+                                            scale_storage=s_all[1:e_n + 1])
+    torch.cuda.synchronize()
+    want_q, want_s = oracle.masked_quant_per_token_group(x.float().numpy(), clamped, 128)
+    got_q, got_s = q.cpu().numpy(), s.cpu().numpy()
+    for e in range(e_n):
+        r = clamped[e]
+        assert np.array_equal(got_q[e, :r], want_q[e, :r])
+        assert np.array_equal(got_s[e, :r].view(np.uint32), want_s[e, :r].view(np.uint32))
+        assert np.all(got_q[e, r:] == 0x7F) and np.all(np.isnan(got_s[e, r:]))
+    for guard in (0, e_n + 1):
+        assert np.all(q_all[guard].cpu().numpy() == 0x7F)
+        assert np.all(np.isnan(s_all[guard].cpu().numpy()))
+
+    b, sb = _weights("moe-clamp-w", e_n, n, k, False)
+    out_all = torch.full((e_n + 2, m_max, n), float("nan"), dtype=torch.bfloat16, device=device())
+    ops.scaled_mm_blockwise_masked(q, gpu(b), s, gpu(sb), gpu(raw), m_max=m_max,
+                                   out=out_all[1:e_n + 1])
+    torch.cuda.synchronize()
+    got = bf16_to_f64(out_all.reshape(-1, n)).reshape(e_n + 2, m_max, n)
+    assert np.all(np.isnan(got[0])) and np.all(np.isnan(got[e_n + 1]))
+    for e in range(e_n):
+        r = int(clamped[e])
+        assert np.all(np.isnan(got[e + 1, r:]))
+        if r:
+            ref = oracle.scaled_mm_blockwise(want_q[e, :r], b[e], want_s[e, :r], sb[e])
+            tau = oracle.summation_bound_blockwise(want_q[e, :r], b[e], want_s[e, :r], sb[e])
+            assert oracle.check_gemm(got[e + 1, :r], ref, tau)["ok"]
