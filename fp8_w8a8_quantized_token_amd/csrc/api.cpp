@@ -294,13 +294,15 @@ int fp8_scaled_mm_blockwise_masked(const uint8_t* a, const uint8_t* b, const flo
   fp8_tile_config cfg;
   st = resolve_config(FP8_KIND_BLOCKWISE, M_max, N, K, cfg_in, &cfg);
   if (st) return st;
-  if (cfg.split_k != 1) return fail(FP8_ERR_INVALID, "%s: grouped GEMMs take split_k == 1", fn);
   if (!cfg_in || cfg_in->variant == FP8_VARIANT_DEFAULT) {
-    // the table or heuristic may name a tile without the grouped path: take
-    // the deep-ring tile of a similar size instead
+    // the table or heuristic may name a tile without the grouped path (take
+    // the deep-ring tile of a similar size instead) or a split-K factor (the
+    // grouped path runs unsplit; its per-tile counters are not per expert)
     if (cfg.variant < 15 || cfg.variant > 25)
       cfg.variant = M_max <= 32 ? 23 : (M_max <= 128 ? 24 : (M_max <= 512 ? 19 : 25));
+    cfg.split_k = 1;
   }
+  if (cfg.split_k != 1) return fail(FP8_ERR_INVALID, "%s: grouped GEMMs take split_k == 1", fn);
   GemmArgs p{};
   p.a = a; p.b = b; p.sa = a_scale; p.sa_ld = a_scale_ld; p.sb = b_scale; p.bias = nullptr; p.out = out;
   p.M = M_max; p.N = N; p.K = K; p.lda = lda; p.ldb = ldb; p.ldc = ldc;

@@ -122,8 +122,13 @@ def test_moe_argument_errors(lib):
     assert call(N=504) == _lib.FP8_ERR_UNSUPPORTED
     assert call(E=70000) == _lib.FP8_ERR_INVALID
     split2 = _lib.TileConfig(_lib.VARIANTS["t64x64deep"], 0, 0, 0, 2, 0)
-    assert call(cfg=split2) == _lib.FP8_ERR_INVALID
+    assert call(cfg=split2) == _lib.FP8_ERR_INVALID  # an explicit split is refused ...
     assert "split_k" in _err(lib)
+    # ... while a table entry with a split runs unsplit under the default config
+    # (exercised on the GPU at 7168x7168); here: that table entry does split
+    cfg = _lib.TileConfig()
+    assert lib.fp8_tile_config_lookup(_lib.KIND_BLOCKWISE, 7168, 7168, 64, ctypes.byref(cfg)) == 1
+    assert cfg.split_k == 2
     tile = _lib.TileConfig(_lib.VARIANTS["t128x128"], 0, 0, 0, 1, 0)
     assert call(cfg=tile) == _lib.FP8_ERR_UNSUPPORTED
     assert call(E=0) == _lib.FP8_OK and call(M=0) == _lib.FP8_OK

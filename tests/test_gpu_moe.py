@@ -78,7 +78,10 @@ GEMM_CASES = [  # (E, M_max, N, K, variant, ue8m0)
     (8, 16, 4096, 1536, "t32x32deep", False), (8, 100, 3072, 4096, "t64x32deep", False),
     (6, 300, 384, 1024, "t256x256bw16", False), (6, 300, 384, 1024, "t256x256bw16", True),
     (4, 200, 1024, 2048, "t128x128panel", False), (4, 200, 1024, 2048, "t256x128panel", True),
-    (2, 4096, 3072, 4096, None, True)]
+    (2, 4096, 3072, 4096, None, True),
+    # the 7168x7168 blockwise table names split-K tiles at these M: the grouped
+    # path drops the split under the default config
+    (3, 16, 7168, 7168, None, False), (2, 64, 7168, 7168, None, True)]
 
 
 @pytest.mark.parametrize("e_n,m_max,n,k,variant,ue8m0", GEMM_CASES,
