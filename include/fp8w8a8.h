@@ -223,10 +223,10 @@ int fp8_quant_per_token_group_masked(const uint16_t* x, int64_t E, int64_t M_max
  *   masked_m  int32 [E], device memory
  *   scale_ue8m0  non-zero: every scale is a power of two (as
  *             fp8_scaled_mm_blockwise_ue8m0)
- *   cfg       NULL or FP8_VARIANT_DEFAULT: the blockwise table at (N, K, M_max),
- *             any tile without a grouped path replaced by a deep-ring tile of
- *             similar size and any split-K factor dropped; else one of the
- *             blockwise panel tiles
+ *   cfg       NULL or FP8_VARIANT_DEFAULT: a tile chosen by rows per expert
+ *             (64x64 panel up to M_max 64, 128x128 8-wave panel up to 128,
+ *             256x128 panel up to 256, the 16x16 256x256 tile above), unsplit;
+ *             else one of the blockwise panel tiles
  *             (FP8_VARIANT_T256x128PANEL .. FP8_VARIANT_T256x256BW16), split_k 1.
  * Errors as fp8_scaled_mm_blockwise; FP8_ERR_UNSUPPORTED for a tile without
  * the grouped path. E <= 65535. */
