@@ -276,6 +276,14 @@ __device__ __forceinline__ f32x16 mfma32_fp8(const i32x8& w, const i32x8& x, con
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, x, c, 0, 0, 0, 0, 0, 0);
 }
 
+// The 32x32x64 form with E8M0 block scales applied by the matrix core (as
+// mfma_fp8_e8): lane l passes the exponent of its row (l % 32) for the 32-deep
+// K piece it supplies (l / 32).
+__device__ __forceinline__ f32x16 mfma32_fp8_e8(const i32x8& w, const i32x8& x, const f32x16& c, int ew,
+                                                int ex) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, x, c, 0, 0, 0, ew, 0, ex);
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -832,7 +840,10 @@ template <int BM, int BN, int WM, int WN, int KIND, int NP, bool MF16 = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   using G = PanelGeom<BM, BN, WM, WN, KIND, NP, MF16>;
   constexpr bool BW = KIND != kChannelwise;
-  static_assert(KIND != kBlockwiseE8 || MF16, "E8M0 scales are served by the 16x16 body");
+  // blockwise fp32 scales: per-stage partial tiles promoted in fp32; E8M0
+  // scales: exponents handed to the block-scaled MFMA, no partial tile
+  constexpr bool PROMOTE = KIND == kBlockwise;
+  constexpr bool E8 = KIND == kBlockwiseE8;
   constexpr int NT = WM * WN * 64;
   constexpr int NW = WM * WN;
   constexpr int BK = 128;
@@ -1093,9 +1104,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = zero16();
-  // blockwise: the current stage's partial tile and scales
-  f32x16 part[BW ? TM : 1][BW ? TN : 1];
-  float sc_a[BW ? TM : 1], sc_b[BW ? TN : 1];
+  // blockwise: the current stage's partial tile and scales (E8M0: the
+  // scales' exponents only)
+  f32x16 part[PROMOTE ? TM : 1][PROMOTE ? TN : 1];
+  float sc_a[PROMOTE ? TM : 1], sc_b[PROMOTE ? TN : 1];
+  int ex_a[E8 ? TM : 1], ex_b[E8 ? TN : 1];
 
   i32x8 fa[TM], fb0[TN], fb1[TN];
   // MFMAs on (fa, fb0) while the next half's fragments are read from the
@@ -1106,7 +1119,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   auto half = [&](int sa, int sb, int kh) {
     const uint8_t* pa = lds + sa * SLOT;
     const uint8_t* pb = lds + sb * SLOT + b_shift;
-    if constexpr (BW) {
+    if constexpr (PROMOTE) {
       if (kh == 1) {  // this stage's scales, while its B slot is still ours
         const uint8_t* sc = lds + sb * SLOT;
 #pragma unroll
@@ -1118,14 +1131,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
                                                      ((wn * WTN + j * 32) >> 7) * 4);
       }
     }
+    if constexpr (E8) {
+      if (kh == 1) {  // the same reads, keeping the biased exponents
+        const uint8_t* sc = lds + sb * SLOT;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          ex_a[i] = (int)(*reinterpret_cast<const uint32_t*>(sc + SA_OFF + (wm * WTM + i * 32 + r32) * 4) >> 23);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          ex_b[j] = (int)(*reinterpret_cast<const uint32_t*>(sc + SB_OFF + wave * 16 +
+                                                            ((wn * WTN + j * 32) >> 7) * 4) >> 23);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb1[j] = frag_at(pb + j * 32 * BK, kh);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        if constexpr (BW) {
+        if constexpr (PROMOTE) {
           part[i][j] = mfma32_fp8(fb0[j], fa[i], kh == 1 ? zero16() : part[i][j]);
+        } else if constexpr (E8) {
+          acc[i][j] = mfma32_fp8_e8(fb0[j], fa[i], acc[i][j], ex_b[j], ex_a[i]);
         } else {
           acc[i][j] = mfma32_fp8(fb0[j], fa[i], acc[i][j]);
         }
@@ -1143,7 +1170,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   };
   // blockwise: the finished stage's partial tile joins the accumulator
   auto promote = [&]() {
-    if constexpr (BW) {
+    if constexpr (PROMOTE) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -1196,7 +1223,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        if constexpr (BW) part[i][j] = mfma32_fp8(fb0[j], fa[i], part[i][j]);
+        if constexpr (PROMOTE) part[i][j] = mfma32_fp8(fb0[j], fa[i], part[i][j]);
+        else if constexpr (E8) acc[i][j] = mfma32_fp8_e8(fb0[j], fa[i], acc[i][j], ex_b[j], ex_a[i]);
         else acc[i][j] = mfma32_fp8(fb0[j], fa[i], acc[i][j]);
       }
     promote();
@@ -1741,6 +1769,27 @@ hipError_t launch_linear_fused(int kind, const GemmArgs& p, const QuantArgs& qa,
                               : launch_fused_kind<kBlockwise>(p, qa, stream);
 }
 
+namespace {
+// UE8M0 blockwise on the block-scaled MFMA: the tiles where that measured
+// faster than promoting each 128-deep block in fp32 on the same inputs (HBM-
+// resident weights): 256x128 panel 1.16-1.20x (4096x4096 M = 2048,
+// 7168x7168 M = 1024), 128x64 8-wave panel 1.11x (3072x4096 M = 512), 16x16
+// 256x256 tile 1.13x. The 128x128 8-wave panel measured 0.94-1.04x and the
+// other tiles were not measured: they keep the fp32 promotion, which is
+// exact for power-of-two scales. Shapes and ring depths as in launch_kind's
+// panel cases; panel-eligible arguments only.
+bool e8_tile(int variant) { return variant == 15 || variant == 22 || variant == 25; }
+
+hipError_t launch_e8(int variant, const GemmArgs& p, hipStream_t stream) {
+  switch (variant) {
+    case 15: return launch_panel<256, 128, 4, 2, kBlockwiseE8, 5>(p, stream);
+    case 22: return launch_panel<128, 64, 4, 2, kBlockwiseE8, 5>(p, stream);
+    case 25: return launch_panel<256, 256, 2, 4, kBlockwiseE8, 4, true>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+}  // namespace
+
 bool grouped_launchable(int variant, const GemmArgs& p) {
   return variant >= 15 && variant <= 25 && p.split_k == 1 && panel_eligible<kBlockwise>(p);
 }
@@ -1749,10 +1798,10 @@ hipError_t launch_gemm(int kind, int variant, const GemmArgs& p, hipStream_t str
   // grouped calls may reach only the panel tiles (the kernels that read masked_m)
   if (p.masked_m && (kind == kChannelwise || !grouped_launchable(variant, p))) return hipErrorInvalidValue;
   if (kind == kBlockwiseE8) {
-    // the block-scaled MFMA serves the 16x16 256x256 tile; every other tile
-    // promotes in fp32, which is exact for power-of-two scales
-    if (variant == 25 && panel_eligible<kBlockwise>(p))
-      return launch_panel<256, 256, 2, 4, kBlockwiseE8, 4, true>(p, stream);
+    // the block-scaled MFMA serves the tiles of e8_tile; every other tile
+    // (and arguments the panel tiles cannot take) promotes in fp32, which is
+    // exact for power-of-two scales
+    if (e8_tile(variant) && panel_eligible<kBlockwise>(p)) return launch_e8(variant, p, stream);
     return launch_kind<kBlockwise>(variant, p, stream);
   }
   return kind == kChannelwise ? launch_kind<kChannelwise>(variant, p, stream)

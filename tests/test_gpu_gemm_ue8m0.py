@@ -4,8 +4,9 @@ the fp64 blockwise oracle.
 Activations and weights are quantized by the oracle with scale_ue8m0 (the
 quantizer flag of the PR 27896 digest's kernel call; the GPU quantizer is
 checked bit-exact against the same oracle elsewhere), and the same bytes go to
-both sides. The large-M 16x16 tile applies the scales inside gfx950's
-block-scaled MFMA; the other tiles run the fp32-promotion kernels. Acceptance
+both sides. The 16x16 256x256 tile and the 256x128 and 128x64 (8-wave)
+panel tiles apply the scales inside gfx950's block-scaled MFMA; the other
+tiles run the fp32-promotion kernels. Acceptance
 as for every GEMM (oracle.check_gemm): max|err| <= 1e-2 max|ref| and per
 element |err| <= 2^-6 |ref| + tau.
 """
@@ -110,3 +111,17 @@ def test_ue8m0_matches_fp32_promotion_tile():
     d = (out_e8.float() - out_f32.float()).abs().max().item()
     ref_max = out_f32.float().abs().max().item()
     assert d <= 1e-2 * ref_max, (d, ref_max)
+
+
+E8_PANEL_VARIANTS = [("t256x128panel", 1), ("t256x128panel", 3), ("t128x128panel", 1), ("t128x64panel", 2),
+                     ("t64x64panel", 1), ("t64x64deep", 2), ("t128x64deep", 1), ("t128x128panel8", 2),
+                     ("t128x64panel8", 1), ("t32x32deep", 2), ("t64x32deep", 1)]
+
+
+@pytest.mark.parametrize("variant,split_k", E8_PANEL_VARIANTS, ids=[f"{v}-sk{s}" for v, s in E8_PANEL_VARIANTS])
+def test_ue8m0_panel_tiles(variant, split_k):
+    """Every 32x32-MFMA panel tile on power-of-two scales (the 256x128 and
+    8-wave 128x64 tiles on the block-scaled MFMA, with no per-stage partial
+    tile; the others promoting in fp32): ragged M, N not a multiple of the
+    tile, several stages, split-K, bias."""
+    _case("ue8m0-panel", 203, 384, 1536, config=ops.make_config(variant, split_k), with_bias=True)
