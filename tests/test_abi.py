@@ -190,6 +190,25 @@ def test_fused_linear_kill_switch(lib, monkeypatch):
     assert n(_lib.KIND_BLOCKWISE, 4, 4096, 4096, None) == 1
 
 
+def test_ue8m0_gemm_shares_blockwise_tiles(lib):
+    # workspace queries take the UE8M0 kind and answer as for blockwise
+    cfg = _lib.TileConfig(_lib.VARIANTS["t256x128panel"], 0, 0, 0, 2, 0)
+    for m, n, k in ((300, 384, 1024), (64, 7168, 7168), (4096, 4096, 4096)):
+        assert lib.fp8_scaled_mm_workspace_size(_lib.KIND_BLOCKWISE_UE8M0, m, n, k, ctypes.byref(cfg)) == \
+            lib.fp8_scaled_mm_workspace_size(_lib.KIND_BLOCKWISE, m, n, k, ctypes.byref(cfg))
+        assert lib.fp8_scaled_mm_workspace_size(_lib.KIND_BLOCKWISE_UE8M0, m, n, k, None) == \
+            lib.fp8_scaled_mm_workspace_size(_lib.KIND_BLOCKWISE, m, n, k, None)
+    assert lib.fp8_scaled_mm_workspace_size(3, 64, 256, 1024, None) == ctypes.c_size_t(-1).value
+    # the same argument checks as the blockwise GEMM
+    mm = lib.fp8_scaled_mm_blockwise_ue8m0
+    assert mm(FAKE, FAKE, FAKE, 64, FAKE, None, FAKE, 64, 504, 1024, 1024, 1024, 504, None, 0, None) == \
+        _lib.FP8_ERR_UNSUPPORTED
+    assert mm(FAKE, FAKE, FAKE, 32, FAKE, None, FAKE, 64, 512, 1024, 1024, 1024, 512, None, 0, None) == \
+        _lib.FP8_ERR_INVALID
+    assert "a_scale_ld" in _err(lib)
+    assert mm(None, None, None, 0, None, None, None, 0, 512, 1024, 1024, 1024, 512, None, 0, None) == _lib.FP8_OK
+
+
 def test_workspace_errors(lib):
     cfg = _lib.TileConfig(_lib.VARIANTS["t64x64"], 0, 0, 0, 4, 0)
     # t64x64 runs 512-deep K stages: K = 2048 holds 4 stages, so 4 splits
