@@ -86,6 +86,12 @@ SIGNATURES = {
     "fp8_linear_blockwise": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64,
                                      c_i64, c_i64, c_i32, c_f32, c_vp, c_i64, c_vp, c_vp, c_size,
                                      ctypes.POINTER(TileConfig), c_vp]),
+    "fp8_linear_channelwise_ex": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64,
+                                          c_i64, c_i64, c_f32, c_vp, c_i64, c_vp, c_vp, c_size,
+                                          ctypes.POINTER(TileConfig), c_i32, c_vp]),
+    "fp8_linear_blockwise_ex": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64,
+                                        c_i64, c_i64, c_i32, c_f32, c_vp, c_i64, c_vp, c_vp, c_size,
+                                        ctypes.POINTER(TileConfig), c_i32, c_vp]),
     "fp8_linear_launches": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(TileConfig)]),
     "fp8_tile_config_lookup": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(TileConfig)]),
     "fp8_tile_config_default": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(TileConfig)]),

@@ -157,10 +157,12 @@ int run_linear(const char* fn, int kind, const uint16_t* x, const uint8_t* b, co
                const uint16_t* bias, uint16_t* out, int64_t M, int64_t N, int64_t K, int64_t ldx,
                int64_t ldb, int64_t ldc, int32_t row_alignment, float eps, uint8_t* q, int64_t ldq,
                float* a_scale, void* ws, size_t ws_bytes, const fp8_tile_config* cfg_in,
-               hipStream_t stream) {
+               int32_t flags, hipStream_t stream) {
   const bool bw = kind == FP8_KIND_BLOCKWISE;
   if (bw && row_alignment < 1) return fail(FP8_ERR_INVALID, "%s: row_alignment must be >= 1", fn);
-  int st = check_quant(fn, x, M, K, K, ldx, q, ldq, a_scale, eps);
+  int st = check_quant_flags(fn, flags);
+  if (st) return st;
+  st = check_quant(fn, x, M, K, (flags & FP8_QUANT_FUSE_SILU_MUL) ? 2 * K : K, ldx, q, ldq, a_scale, eps);
   if (st) return st;
   st = check_gemm(fn, q, b, a_scale, b_scale, bias, out, M, N, K, ldq, ldb, ldc);
   if (st) return st;
@@ -172,7 +174,7 @@ int run_linear(const char* fn, int kind, const uint16_t* x, const uint8_t* b, co
   fp8_tile_config cfg;
   st = resolve_config(kind, M, N, K, cfg_in, &cfg);
   if (st) return st;
-  if (linear_fuses(cfg, M)) {
+  if (flags == 0 && linear_fuses(cfg, M)) {
     GemmArgs p{};
     p.a = q; p.b = b; p.sa = a_scale; p.sa_ld = m_pad; p.sb = b_scale; p.bias = bias; p.out = out;
     p.M = M; p.N = N; p.K = K; p.lda = ldq; p.ldb = ldb; p.ldc = ldc;
@@ -181,11 +183,13 @@ int run_linear(const char* fn, int kind, const uint16_t* x, const uint8_t* b, co
     const QuantArgs qa{x, ldx, q, ldq, a_scale, m_pad, eps};
     return hip_status(launch_linear_fused(kind, p, qa, stream), fn);
   }
-  const hipError_t e = bw ? launch_quant_per_token_group(x, M, K, ldx, 128, m_pad, q, ldq, a_scale, eps, 0, stream)
-                          : launch_quant_per_token(x, M, K, ldx, q, ldq, a_scale, eps, 0, stream);
+  const hipError_t e = bw ? launch_quant_per_token_group(x, M, K, ldx, 128, m_pad, q, ldq, a_scale, eps, flags, stream)
+                          : launch_quant_per_token(x, M, K, ldx, q, ldq, a_scale, eps, flags, stream);
   st = hip_status(e, fn);
   if (st) return st;
-  return run_gemm(fn, kind, q, b, a_scale, m_pad, b_scale, bias, out, M, N, K, ldq, ldb, ldc, ws,
+  // blockwise with power-of-two scales: the block-scaled MFMA tiles
+  const int gemm_kind = bw && (flags & FP8_QUANT_SCALE_UE8M0) ? FP8_KIND_BLOCKWISE_UE8M0 : kind;
+  return run_gemm(fn, gemm_kind, q, b, a_scale, m_pad, b_scale, bias, out, M, N, K, ldq, ldb, ldc, ws,
                   ws_bytes, &cfg, stream);
 }
 
@@ -423,13 +427,32 @@ size_t fp8_scaled_mm_workspace_size(int32_t kind, int64_t M, int64_t N, int64_t 
   return variant_workspace_bytes(cfg.variant, splits, M, N);
 }
 
+int fp8_linear_channelwise_ex(const uint16_t* x, const uint8_t* b, const float* b_scale,
+                              const uint16_t* bias, uint16_t* out, int64_t M, int64_t N, int64_t K,
+                              int64_t ldx, int64_t ldb, int64_t ldc, float eps, uint8_t* q,
+                              int64_t ldq, float* a_scale, void* ws, size_t ws_bytes,
+                              const fp8_tile_config* cfg, int32_t flags, hipStream_t stream) {
+  return run_linear("fp8_linear_channelwise", FP8_KIND_CHANNELWISE, x, b, b_scale, bias, out, M, N,
+                    K, ldx, ldb, ldc, 1, eps, q, ldq, a_scale, ws, ws_bytes, cfg, flags, stream);
+}
+
 int fp8_linear_channelwise(const uint16_t* x, const uint8_t* b, const float* b_scale,
                            const uint16_t* bias, uint16_t* out, int64_t M, int64_t N, int64_t K,
                            int64_t ldx, int64_t ldb, int64_t ldc, float eps, uint8_t* q,
                            int64_t ldq, float* a_scale, void* ws, size_t ws_bytes,
                            const fp8_tile_config* cfg, hipStream_t stream) {
-  return run_linear("fp8_linear_channelwise", FP8_KIND_CHANNELWISE, x, b, b_scale, bias, out, M, N,
-                    K, ldx, ldb, ldc, 1, eps, q, ldq, a_scale, ws, ws_bytes, cfg, stream);
+  return fp8_linear_channelwise_ex(x, b, b_scale, bias, out, M, N, K, ldx, ldb, ldc, eps, q, ldq,
+                                   a_scale, ws, ws_bytes, cfg, 0, stream);
+}
+
+int fp8_linear_blockwise_ex(const uint16_t* x, const uint8_t* b, const float* b_scale,
+                            const uint16_t* bias, uint16_t* out, int64_t M, int64_t N, int64_t K,
+                            int64_t ldx, int64_t ldb, int64_t ldc, int32_t row_alignment, float eps,
+                            uint8_t* q, int64_t ldq, float* a_scale, void* ws, size_t ws_bytes,
+                            const fp8_tile_config* cfg, int32_t flags, hipStream_t stream) {
+  return run_linear("fp8_linear_blockwise", FP8_KIND_BLOCKWISE, x, b, b_scale, bias, out, M, N, K,
+                    ldx, ldb, ldc, row_alignment, eps, q, ldq, a_scale, ws, ws_bytes, cfg, flags,
+                    stream);
 }
 
 int fp8_linear_blockwise(const uint16_t* x, const uint8_t* b, const float* b_scale,
@@ -437,8 +460,8 @@ int fp8_linear_blockwise(const uint16_t* x, const uint8_t* b, const float* b_sca
                          int64_t ldx, int64_t ldb, int64_t ldc, int32_t row_alignment, float eps,
                          uint8_t* q, int64_t ldq, float* a_scale, void* ws, size_t ws_bytes,
                          const fp8_tile_config* cfg, hipStream_t stream) {
-  return run_linear("fp8_linear_blockwise", FP8_KIND_BLOCKWISE, x, b, b_scale, bias, out, M, N, K,
-                    ldx, ldb, ldc, row_alignment, eps, q, ldq, a_scale, ws, ws_bytes, cfg, stream);
+  return fp8_linear_blockwise_ex(x, b, b_scale, bias, out, M, N, K, ldx, ldb, ldc, row_alignment, eps,
+                                 q, ldq, a_scale, ws, ws_bytes, cfg, 0, stream);
 }
 
 int fp8_linear_launches(int32_t kind, int64_t M, int64_t N, int64_t K, const fp8_tile_config* cfg_in) {

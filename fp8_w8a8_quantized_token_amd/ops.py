@@ -321,14 +321,19 @@ def scaled_mm_blockwise(a, b, a_scale, b_scale, bias=None, m=None, out=None, con
 
 
 # ---------------------------------------------------------------- linears
-def _linear_args(kind, x, w_q, w_s, bias, eps, row_alignment, config, out, q, scale):
-    """Validated ctypes argument tuple of fp8_linear_{channelwise,blockwise}
-    for 2-D x, plus the tensors it points to."""
+def _linear_args(kind, x, w_q, w_s, bias, eps, row_alignment, config, out, q, scale, flags=0):
+    """Validated ctypes argument tuple of fp8_linear_{channelwise,blockwise}_ex
+    for 2-D x (rows of 2K [gate | up] values under the SiLU-and-mul flag), plus
+    the tensors it points to."""
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
         raise TypeError("x must be a 2-D bf16 tensor with contiguous rows")
     w_q = _as_codes(w_q, "w_q")
     _need_cuda(x, w_q, w_s, bias)
     m, k = x.shape
+    if flags & _lib.QUANT_FUSE_SILU_MUL:
+        if k % 2:
+            raise ValueError("the SiLU-and-mul input needs an even row width [gate | up]")
+        k //= 2
     n = w_q.shape[0]
     if w_q.shape[1] != k:
         raise ValueError("x and w_q disagree on K")
@@ -355,37 +360,46 @@ def _linear_args(kind, x, w_q, w_s, bias, eps, row_alignment, config, out, q, sc
     head = (_p(x), _p(w_q), _p(w_s), _p(bias), _p(out), m, n, k, x.stride(0), w_q.stride(0),
             out.stride(0))
     mid = (ctypes.c_float(eps),) if kind == KIND_CHANNELWISE else (row_alignment, ctypes.c_float(eps))
-    args = head + mid + (_p(q), q.stride(0), _p(scale), _p(ws), nws, ctypes.byref(cfg), _stream(x))
+    args = (head + mid + (_p(q), q.stride(0), _p(scale), _p(ws), nws, ctypes.byref(cfg), flags,
+                          _stream(x)))
     return args, (out, q, scale, cfg, ws)
 
 
-def linear_channelwise(x, w_q, w_s, bias=None, eps=1e-10, config=None, return_quant=False):
+def linear_channelwise(x, w_q, w_s, bias=None, eps=1e-10, config=None, return_quant=False,
+                       silu_mul=False, scale_ue8m0=False):
     """y = x @ W^T with per-token FP8 activation quant and per-channel weight
     scales. x bf16 [..., K]; w_q codes [N, K]; w_s fp32 [N]; bias bf16 [N].
     One kernel launch for M <= 4 (quant fused into the skinny GEMM), two
-    otherwise. return_quant=True also returns the codes [M, K] and scales [M]."""
+    otherwise. return_quant=True also returns the codes [M, K] and scales [M].
+    silu_mul=True: x is [..., 2K] = [gate | up] and the quantized row is
+    SiLU(gate) * up rounded to bf16 (the down projection after a gated MLP);
+    scale_ue8m0=True: power-of-two activation scales. Either flag: two launches."""
     shape = x.shape
     x2 = x.reshape(-1, shape[-1])
     args, (out, q, s, _, _) = _linear_args(KIND_CHANNELWISE, x2, w_q, w_s, bias, eps, 1, config,
-                                          None, None, None)
-    check(_lib.load().fp8_linear_channelwise(*args))
+                                          None, None, None, _flags(silu_mul, scale_ue8m0))
+    check(_lib.load().fp8_linear_channelwise_ex(*args))
     out = out.view(*shape[:-1], out.shape[1])
     return (out, q, s) if return_quant else out
 
 
 def linear_blockwise(x, w_q, w_s, bias=None, block_size=(128, 128), eps=1e-10,
-                     row_alignment=4, config=None, return_quant=False):
+                     row_alignment=4, config=None, return_quant=False, silu_mul=False,
+                     scale_ue8m0=False):
     """Blockwise FP8 linear: group-128 activation quant into row-padded buffers,
     then the blockwise GEMM over the first M rows with the bias fused. One
     launch for M <= 4, two otherwise. return_quant=True also returns the codes
-    [M_pad, K] and the scales as an [M_pad, K/128] view of [K/128, M_pad]."""
+    [M_pad, K] and the scales as an [M_pad, K/128] view of [K/128, M_pad].
+    silu_mul as for linear_channelwise; scale_ue8m0=True makes the activation
+    scales powers of two and runs the GEMM on the block-scaled MFMA tiles (the
+    weight block scales must then be powers of two too)."""
     if tuple(block_size) != (128, 128):
         raise _lib.Fp8Error(_lib.FP8_ERR_UNSUPPORTED, "only 128x128 weight blocks are supported")
     shape = x.shape
     x2 = x.reshape(-1, shape[-1])
     args, (out, q, st, _, _) = _linear_args(KIND_BLOCKWISE, x2, w_q, w_s, bias, eps, row_alignment,
-                                           config, None, None, None)
-    check(_lib.load().fp8_linear_blockwise(*args))
+                                           config, None, None, None, _flags(silu_mul, scale_ue8m0))
+    check(_lib.load().fp8_linear_blockwise_ex(*args))
     out = out.view(*shape[:-1], out.shape[1])
     return (out, q, st.transpose(0, 1)) if return_quant else out
 
@@ -486,9 +500,10 @@ def prepare(op, *args, **kwargs):
         cfg = kwargs.get("config") or TileConfig(-1, 0, 0, 0, 1, 0)
         a, keep = _linear_args(kind, x, w_q, w_s, kwargs.get("bias"), kwargs.get("eps", 1e-10),
                                kwargs.get("row_alignment", 4), cfg, kwargs["out"], kwargs["q"],
-                               kwargs["scale"])
-        return Prepared(lib.fp8_linear_channelwise if op == "linear_channelwise"
-                        else lib.fp8_linear_blockwise, a, op, keep + (x, w_q, w_s, kwargs.get("bias")))
+                               kwargs["scale"], _flags(kwargs.get("silu_mul", False),
+                                                       kwargs.get("scale_ue8m0", False)))
+        return Prepared(lib.fp8_linear_channelwise_ex if op == "linear_channelwise"
+                        else lib.fp8_linear_blockwise_ex, a, op, keep + (x, w_q, w_s, kwargs.get("bias")))
     if op in ("scaled_mm_channelwise", "scaled_mm_blockwise"):
         a_, b_, sa, sb = _as_codes(args[0], "a"), _as_codes(args[1], "b"), args[2], args[3]
         bias, out = kwargs.get("bias"), kwargs["out"]

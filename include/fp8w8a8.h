@@ -411,6 +411,33 @@ int fp8_linear_blockwise(const uint16_t* x, const uint8_t* b, const float* b_sca
                          void* ws, size_t ws_bytes,
                          const fp8_tile_config* cfg, hipStream_t stream);
 
+/* The linears with quantizer flags (FP8_QUANT_*, as for fp8_quant_per_token_ex;
+ * unknown bits: FP8_ERR_INVALID). With FP8_QUANT_FUSE_SILU_MUL, x is bf16
+ * [M][ldx] with ldx >= 2K holding [gate | up] rows, so the down projection
+ * runs straight from the gate/up projection's output; K is the width of the
+ * quantized rows (the GEMM's depth) as before. With FP8_QUANT_SCALE_UE8M0 the
+ * activation scales are powers of two, and the blockwise linear then runs the
+ * GEMM as fp8_scaled_mm_blockwise_ue8m0 (its weight block scales must be powers
+ * of two as well). q, a_scale and out hold exactly what the flagged quantizer
+ * and that GEMM write. Any flag set: always two launches (quantizer, GEMM).
+ * flags == 0 is exactly fp8_linear_channelwise / fp8_linear_blockwise. */
+int fp8_linear_channelwise_ex(const uint16_t* x, const uint8_t* b, const float* b_scale,
+                              const uint16_t* bias, uint16_t* out,
+                              int64_t M, int64_t N, int64_t K,
+                              int64_t ldx, int64_t ldb, int64_t ldc, float eps,
+                              uint8_t* q, int64_t ldq, float* a_scale,
+                              void* ws, size_t ws_bytes,
+                              const fp8_tile_config* cfg, int32_t flags, hipStream_t stream);
+
+int fp8_linear_blockwise_ex(const uint16_t* x, const uint8_t* b, const float* b_scale,
+                            const uint16_t* bias, uint16_t* out,
+                            int64_t M, int64_t N, int64_t K,
+                            int64_t ldx, int64_t ldb, int64_t ldc,
+                            int32_t row_alignment, float eps,
+                            uint8_t* q, int64_t ldq, float* a_scale,
+                            void* ws, size_t ws_bytes,
+                            const fp8_tile_config* cfg, int32_t flags, hipStream_t stream);
+
 /* Kernel launches an fp8_linear_* call of `kind` makes for (M, N, K, cfg):
  * 1 (fused), 2 (quantizer, then GEMM) or 0 (M == 0); FP8_ERR_INVALID on bad
  * arguments. Host only. */

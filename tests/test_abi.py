@@ -168,6 +168,26 @@ def test_linear_argument_errors(lib):
     assert bw(*(okb[:11] + (0,) + okb[12:])) == _lib.FP8_ERR_INVALID                             # row_alignment
 
 
+def test_linear_flag_errors(lib):
+    cw, bw = lib.fp8_linear_channelwise_ex, lib.fp8_linear_blockwise_ex
+    # as fp8_linear_channelwise, with flags before the stream
+    ok = (FAKE, FAKE, FAKE, None, FAKE, 4, 256, 512, 512, 512, 256, 1e-10, FAKE, 512, FAKE, None, 0, None)
+    assert cw(*(ok + (8, None))) == _lib.FP8_ERR_INVALID                          # unknown flag bit
+    assert "flags" in _err(lib)
+    # [gate | up] rows are 2K wide: ldx = K is too short under SiLU-and-mul
+    assert cw(*(ok + (_lib.QUANT_FUSE_SILU_MUL, None))) == _lib.FP8_ERR_INVALID
+    assert "leading dimension" in _err(lib)
+    okb = (FAKE, FAKE, FAKE, None, FAKE, 4, 256, 512, 512, 512, 256, 4, 1e-10, FAKE, 512, FAKE, None, 0, None)
+    assert bw(*(okb + (-1, None))) == _lib.FP8_ERR_INVALID
+    assert bw(*(okb + (_lib.QUANT_FUSE_SILU_MUL | _lib.QUANT_SCALE_UE8M0, None))) == _lib.FP8_ERR_INVALID
+    assert "leading dimension" in _err(lib)
+    assert bw(*(okb[:6] + (200,) + okb[7:10] + (200,) + okb[11:] + (_lib.QUANT_SCALE_UE8M0, None))) == \
+        _lib.FP8_ERR_UNSUPPORTED                                                  # N % 128
+    for f in (0, 1, 2, 3):  # M == 0 launches nothing under any flag
+        assert cw(*((None,) * 5 + (0,) + ok[6:12] + (None, 512, None, None, 0, None, f, None))) == _lib.FP8_OK
+        assert bw(*((None,) * 5 + (0,) + okb[6:13] + (None, 512, None, None, 0, None, f, None))) == _lib.FP8_OK
+
+
 def test_linear_launch_counts(lib):
     n = lib.fp8_linear_launches
     for kind in (_lib.KIND_CHANNELWISE, _lib.KIND_BLOCKWISE):

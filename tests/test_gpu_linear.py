@@ -18,7 +18,7 @@ import torch
 
 import oracle
 from fp8_w8a8_quantized_token_amd import ops, synth
-from gpu_common import (activations, bf16_to_f64, device, gpu, say, weight_blockwise,
+from gpu_common import (activations, bf16_to_f64, device, gpu, sample_rows, say, weight_blockwise,
                         weight_channelwise)
 
 pytestmark = pytest.mark.gpu
@@ -258,3 +258,65 @@ def test_linear_tiny_shapes(kind, m, n, k):
     assert np.array_equal(q[:m].cpu().numpy(), want_q)
     assert np.array_equal(s.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
     _check(out, ref, tau, f"linear tiny {kind} M={m} N={n} K={k}")
+
+
+FLAG_CASES = [  # (kind, M, N, K, silu_mul, scale_ue8m0)
+    ("cw", 1, 4096, 1536, True, False), ("cw", 37, 4096, 1536, True, False),
+    ("cw", 300, 4096, 4096, True, True), ("cw", 3, 512, 1024, False, True),
+    ("bw", 1, 4096, 1536, True, False), ("bw", 4, 4096, 1536, True, True),
+    ("bw", 64, 4096, 1536, False, True), ("bw", 513, 4096, 1536, True, True),
+    ("bw", 2048, 7168, 2048, False, True)]
+
+
+@pytest.mark.parametrize("kind,m,n,k,silu,ue8m0", FLAG_CASES,
+                         ids=[f"{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}{'-silu' if c[4] else ''}{'-ue8m0' if c[5] else ''}"
+                              for c in FLAG_CASES])
+def test_linear_with_quant_flags(kind, m, n, k, silu, ue8m0):
+    """The linears with quantizer flags: SiLU-and-mul takes [gate | up] rows
+    of 2K values (the down projection straight from the gate/up output) and
+    UE8M0 makes the activation scales powers of two (blockwise: the GEMM then
+    runs on the block-scaled MFMA tiles, weights quantized with power-of-two
+    block scales too). Codes and scales bit-exact against the oracle's flagged
+    quantizer, the output within the GEMM tolerance of the oracle GEMM on them
+    and bit-identical to the flagged quantizer followed by the GEMM entry."""
+    x = activations("flag-lin", m, 2 * k if silu else k)
+    xf = x.float().numpy()
+    y = oracle.silu_mul_bf16(xf) if silu else xf
+    bias = synth.bias("flag-lin", n)
+    bias64 = bias.float().numpy()
+    x_d, bias_d = gpu(x), gpu(bias)
+    rows = sample_rows(m) if m * n > 4_000_000 else np.arange(m)
+    say("linear with flags", kind, m, n, k, "silu" if silu else "", "ue8m0" if ue8m0 else "")
+    if kind == "cw":
+        b, sb = weight_channelwise("flag-lin", n, k)
+        out, q, s = ops.linear_channelwise(x_d, gpu(b), gpu(sb), bias_d, return_quant=True,
+                                           silu_mul=silu, scale_ue8m0=ue8m0)
+        torch.cuda.synchronize()
+        if ue8m0:  # per-token = one group spanning the row
+            want_q, want_s = oracle.quant_per_token_group(y, k, scale_ue8m0=True)
+            want_s = want_s.reshape(m)
+        else:
+            want_q, want_s = oracle.quant_per_token(y)
+        ref = oracle.scaled_mm_channelwise(want_q[rows], b, want_s[rows], sb, bias64)
+        tau = oracle.summation_bound_channelwise(want_q[rows], b, want_s[rows], sb)
+        q2, s2 = ops.quant_per_token(x_d, silu_mul=silu, scale_ue8m0=ue8m0)
+        out2 = ops.scaled_mm_channelwise(q2, gpu(b), s2, gpu(sb), bias_d)
+    else:
+        b, sb = oracle.quant_weight_blockwise(synth.weights("flag-lin", n, k).numpy(), scale_ue8m0=ue8m0)
+        out, q, s = ops.linear_blockwise(x_d, gpu(b), gpu(sb), bias_d, return_quant=True,
+                                         silu_mul=silu, scale_ue8m0=ue8m0)
+        torch.cuda.synchronize()
+        want_q, want_s = oracle.quant_per_token_group(y, 128, scale_ue8m0=ue8m0)
+        ref = oracle.scaled_mm_blockwise(want_q[rows], b, want_s[rows], sb, bias64)
+        tau = oracle.summation_bound_blockwise(want_q[rows], b, want_s[rows], sb)
+        q2, s2 = ops.quant_per_token_group(x_d, 128, row_alignment=4, silu_mul=silu, scale_ue8m0=ue8m0)
+        out2 = ops.scaled_mm_blockwise(q2, gpu(b), s2, gpu(sb), bias_d, m=m, scale_ue8m0=ue8m0)
+        s = s[:m]
+    assert np.array_equal(q[:m].cpu().numpy(), want_q)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    if ue8m0:
+        assert np.all((want_s.view(np.uint32) & 0x7FFFFF) == 0)
+    _check(out[torch.as_tensor(rows, device=out.device)], ref, tau,
+           f"linear {kind} flags M={m} N={n} K={k}")
+    torch.cuda.synchronize()
+    assert _same_bits(out, out2)
