@@ -356,6 +356,73 @@ HEADER = ("| workload | kind | N×K | M | tile config | weight GiB rotated | GEM
           "hot GEMM µs p50 |")
 
 
+def _batch_us(fns, warmup, calls, filler):
+    """Average µs per call of `calls` back-to-back calls cycling through fns,
+    timed as one batch with HIP events behind queued device copies."""
+    for i in range(warmup):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    filler(calls)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(calls):
+        fns[i % len(fns)]()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / calls
+
+
+def measure_stream_ceiling(warmup, calls, filler):
+    """What plain HBM streams reach at the byte counts the small-M linears
+    move, beside the skinny GEMM itself: torch's device copy (reads and writes
+    the size) and max-reduction (reads it once) from 8.4 MB to 268 MB, and the
+    o_proj channelwise GEMM (N = K = 4096, a 16.8 MB weight) at M = 1 and 16,
+    each over distinct buffers covering >= 1 GiB so every call starts from
+    HBM."""
+    dev = torch.device("cuda:0")
+    head = "| op | MB moved per call | buffers | µs per call | GB/s | frac of 8 TB/s |"
+    lines = [head, "|---|---|---|---|---|---|"]
+    print(head, flush=True)
+    print(lines[1], flush=True)
+
+    def emit(name, nbytes, sets, us):
+        line = (f"| {name} | {nbytes / 1e6:.1f} | {sets} | {us:.2f} | {nbytes / us / 1e3:.0f} | "
+                f"{nbytes / us / 1e3 / PEAK_GBPS:.2f} |")
+        lines.append(line)
+        print(line, flush=True)
+
+    n = k = 4096
+    sets = max(2, min(MAX_SETS, math.ceil(ROTATE_BYTES / (n * k))))
+    w = synth.weights("measure/stream", n, k).to(torch.bfloat16).to(dev)
+    wq, ws = ops.quant_per_token(w)
+    del w
+    weights = [(wq.clone(), ws.clone()) for _ in range(sets)]
+    for m in (1, 16):
+        a, sa = ops.quant_per_token(synth.activations("measure/stream", m, k).to(dev))
+        outs = [torch.empty((m, n), dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+        fns = [ops.prepare("scaled_mm_channelwise", a, wb, sa, wsb, out=o)
+               for (wb, wsb), o in zip(weights, outs)]
+        emit(f"channelwise GEMM M={m} N=K=4096", gemm_bytes("channelwise", m, n, k, False),
+             sets, _batch_us(fns, warmup, calls, filler))
+        del fns, outs
+    del weights
+    torch.cuda.empty_cache()
+    for size in (2048 * 4096, 4096 * 4096, 2 * 4096 * 4096, 4 * 4096 * 4096, 8 * 4096 * 4096,
+                 16 * 4096 * 4096):
+        sets = max(2, min(MAX_SETS, math.ceil(ROTATE_BYTES / size)))
+        src = [torch.full((size // 4,), i, dtype=torch.int32, device=dev) for i in range(sets)]
+        dst = [torch.empty_like(t) for t in src]
+        red = torch.empty((), dtype=torch.int32, device=dev)
+        emit(f"copy {size / 1e6:.1f} MB", 2 * size, sets,
+             _batch_us([lambda i=i: dst[i].copy_(src[i]) for i in range(sets)], warmup, calls, filler))
+        emit(f"max-reduce {size / 1e6:.1f} MB", size, sets,
+             _batch_us([lambda i=i: torch.amax(src[i], dim=0, out=red) for i in range(sets)],
+                       warmup, calls, filler))
+        del src, dst
+        torch.cuda.empty_cache()
+    return lines
+
+
 def row(cfg, kind, n, k, m, r, bias):
     g = r["gemm"]
     p50 = percentile(g, 50)
@@ -385,20 +452,28 @@ def main(argv=None):
                     help="time the 16x16 blockwise tile with fp32 and with power-of-two scales")
     ap.add_argument("--moe", action="store_true",
                     help="time the masked quantizer and grouped blockwise GEMM over MoE experts")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="time plain device copies and reductions at the small-M linears' byte counts")
     args = ap.parse_args(argv)
     _lib.load()
     dev = torch.device("cuda:0")
     want = args.workloads.split(",")
     filler = _Filler(dev)
-    if args.quant_variants or args.ue8m0_gemm or args.moe:
+    if args.quant_variants or args.ue8m0_gemm or args.moe or args.stream_ceiling:
         t0 = time.time()
-        mode = measure_quant_variants if args.quant_variants else (
-            measure_ue8m0_gemm if args.ue8m0_gemm else measure_moe)
+        mode = (measure_quant_variants if args.quant_variants else
+                measure_ue8m0_gemm if args.ue8m0_gemm else
+                measure_moe if args.moe else measure_stream_ceiling)
         lines = mode(args.warmup, args.calls, filler)
-        note = (f"\n{args.calls} launches per row after {args.warmup} warm-up launches, timed as "
-                f"one batch with HIP events (average per launch); GB/s from algorithmic bytes "
-                f"(bf16 input, codes, scales); weight sets rotated to cover >= 1 GiB. "
-                f"{time.time() - t0:.0f} s.")
+        if args.stream_ceiling:
+            note = (f"\n{args.calls} calls per row after {args.warmup} warm-up calls, timed as one "
+                    f"batch with HIP events behind queued device copies (average per call); "
+                    f"buffers rotated to cover >= 1 GiB. {time.time() - t0:.0f} s.")
+        else:
+            note = (f"\n{args.calls} launches per row after {args.warmup} warm-up launches, timed as "
+                    f"one batch with HIP events (average per launch); GB/s from algorithmic bytes "
+                    f"(bf16 input, codes, scales); weight sets rotated to cover >= 1 GiB. "
+                    f"{time.time() - t0:.0f} s.")
         print(note, flush=True)
         if args.out:
             with open(args.out, "w") as f:
