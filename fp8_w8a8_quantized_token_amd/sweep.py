@@ -47,17 +47,20 @@ def candidates(kind, m, n, k):
         # from M = 8 the 32- and 64-wide deep-ring tiles can win on large N
         c = [("skinny", 1)]
         if m >= 8 and k128:
-            c += [("t32x32deep", 1), ("t32x32deep", 2), ("t64x32deep", 1), ("t64x32deep", 2),
-                  ("t64x64deep", 1), ("t64x64deep", 2), ("t64x64panel", 1)]
+            c += [("t32x32deep", 1), ("t32x32deep", 2), ("t32x32deep", 4), ("t64x32deep", 1),
+                  ("t64x32deep", 2), ("t64x32deep", 4), ("t64x64deep", 1), ("t64x64deep", 2),
+                  ("t64x64deep", 4), ("t64x64panel", 1), ("t64x64panel", 2), ("t64x64panel", 4)]
         return c
     c = []
     if m <= 1024:
         c += [("t64x64", 1), ("t128x64k256", 1), ("t64x128k256", 1), ("t128x128k256", 1)]
         if k128:
-            c += [("t64x64panel", 1), ("t64x64panel", 2), ("t128x64panel", 1),
-                  ("t64x64deep", 1), ("t64x64deep", 2), ("t128x64deep", 1)]
+            c += [("t64x64panel", 1), ("t64x64panel", 2), ("t64x64panel", 4), ("t128x64panel", 1),
+                  ("t128x64panel", 2), ("t128x64panel", 4), ("t64x64deep", 1), ("t64x64deep", 2),
+                  ("t64x64deep", 4), ("t128x64deep", 1), ("t128x64deep", 2)]
             if m <= 256:
-                c += [("t32x32deep", 1), ("t32x32deep", 2), ("t64x32deep", 1), ("t64x32deep", 2)]
+                c += [("t32x32deep", 1), ("t32x32deep", 2), ("t32x32deep", 4), ("t64x32deep", 1),
+                      ("t64x32deep", 2), ("t64x32deep", 4)]
     if m >= 256:
         c += [("t128x128", 1), ("t128x128k256", 1), ("t256x128w8", 1)]
         if kind == "channelwise" and k % 64 == 0:
