@@ -291,6 +291,79 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// Fence-free deterministic split-K, shared by the tiled kernels: every split
+// stores its partial tile to the workspace with device-coherent stores (the
+// SC1 cache-policy bit that agent-scope atomics also use, here on dwordx4
+// buffer stores, so the data reaches the device coherence point and no
+// L2-wide write-back or invalidate fence is needed between XCDs), the
+// workgroup drains its stores and counts itself in with one atomic; the last
+// to arrive reads the partials back with device-coherent loads, sums them in
+// split order into acc, re-arms the counter and returns true. The others
+// return false and must exit. *flag is workgroup-shared scratch.
+// Workspace layout of one tile: [split][piece][thread] 16-byte pieces, so each
+// wave's store or load covers 1 KB contiguously.
+namespace {
+constexpr int kBufDword3 = 0x00020000;  // gfx9 raw buffer: 32-bit dwords, no format conversion
+constexpr int kCacheSc1 = 16;           // cache policy: device-coherent (SC1)
+}  // namespace
+
+template <int TM, int TN, int NT, typename V>
+__device__ __forceinline__ bool splitk_reduce(const GemmArgs& p, V (&acc)[TM][TN],
+                                              int64_t tile, int split, int tid, int* flag) {
+  constexpr int VW = sizeof(V) / sizeof(float);  // 16 (32x32 tiles) or 4 (16x16)
+  static_assert(VW % 4 == 0, "whole 16-byte pieces");
+  constexpr int PV = VW / 4;                     // pieces per accumulator register group
+  constexpr int Q4 = TM * TN * PV;               // pieces per thread
+  constexpr uint32_t SPLIT_BYTES = (uint32_t)Q4 * NT * 16;
+  float* part = p.ws_part + (tile * p.split_k) * (int64_t)Q4 * 4 * NT;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(part, 0, (int)(SPLIT_BYTES * (uint32_t)p.split_k), kBufDword3);
+  using v4i = int __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int c = 0; c < PV; ++c) {
+        const v4i v = {__float_as_int(acc[i][j][4 * c]), __float_as_int(acc[i][j][4 * c + 1]),
+                       __float_as_int(acc[i][j][4 * c + 2]), __float_as_int(acc[i][j][4 * c + 3])};
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, (uint32_t)(((i * TN + j) * PV + c) * NT + tid) * 16,
+                                               (uint32_t)split * SPLIT_BYTES, kCacheSc1);
+      }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const int old = atomicAdd(p.ws_count + tile, 1);
+    *flag = (old == p.split_k - 1);
+  }
+  __syncthreads();
+  if (!*flag) return false;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int c = 0; c < PV; ++c) {
+        const uint32_t off = (uint32_t)(((i * TN + j) * PV + c) * NT + tid) * 16;
+        v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCacheSc1);
+        float s0 = __int_as_float(v.x), s1 = __int_as_float(v.y), s2 = __int_as_float(v.z),
+              s3 = __int_as_float(v.w);
+        for (int sp = 1; sp < p.split_k; ++sp) {
+          v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, (uint32_t)sp * SPLIT_BYTES, kCacheSc1);
+          s0 += __int_as_float(v.x);
+          s1 += __int_as_float(v.y);
+          s2 += __int_as_float(v.z);
+          s3 += __int_as_float(v.w);
+        }
+        acc[i][j][4 * c] = s0;
+        acc[i][j][4 * c + 1] = s1;
+        acc[i][j][4 * c + 2] = s2;
+        acc[i][j][4 * c + 3] = s3;
+      }
+  if (tid == 0) __hip_atomic_store(p.ws_count + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
 template <int BM, int BN, int WM, int WN, int BK, int KIND>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmArgs p) {
   constexpr int NT = WM * WN * 64;
@@ -467,122 +540,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmArgs p) {
     __syncthreads();
   }
 
-  if (p.split_k > 1) {
-    // Partial tiles live in the workspace as [tile][split][TM*TN*16][NT]
-    // floats (register order, so every store and load is coalesced). Every
-    // access to them is an agent-scope atomic: stores write through to the
-    // device coherence point and loads read from it, so no L2-wide
-    // write-back or invalidate fence is needed between XCDs.
-    constexpr int Q = TM * TN * 16;
-    float* part = p.ws_part + (tile * p.split_k) * (int64_t)Q * NT;
-    float* mine = part + (int64_t)split * Q * NT;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          __hip_atomic_store(mine + ((i * TN + j) * 16 + r) * NT + tid, acc[i][j][r],
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
-    __syncthreads();                 // ... and so have the whole workgroup's
-    if (tid == 0) {
-      const int old = atomicAdd(p.ws_count + tile, 1);
-      last_flag = (old == p.split_k - 1);
-    }
-    __syncthreads();
-    if (!last_flag) return;
-    // last split to arrive: sum the partials in split order (deterministic)
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t idx = (int64_t)((i * TN + j) * 16 + r) * NT + tid;
-          float v = __hip_atomic_load(part + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          for (int sp = 1; sp < p.split_k; ++sp)
-            v += __hip_atomic_load(part + (int64_t)sp * Q * NT + idx, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-          acc[i][j][r] = v;
-        }
-    if (tid == 0) __hip_atomic_store(p.ws_count + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (p.split_k > 1 && !splitk_reduce<TM, TN, NT>(p, acc, tile, split, tid, &last_flag)) return;
 
   static_assert(BM * BN * 2 <= 2 * (BM + BN) * BK, "output tile fits the LDS stages");
   store_tile<BM, BN, WM, WN, KIND>(p, acc, lds, m0, n0, wm, wn, h, r32, tid);
-}
-
-// Fence-free deterministic split-K for the panel kernels (the scheme of the
-// tiled kernel above, with 16-byte transfers): every split stores its partial
-// tile to the workspace with device-coherent stores (the SC1 cache-policy bit
-// that agent-scope atomics also use, here on dwordx4 buffer stores), the
-// workgroup drains its stores and counts itself in with one atomic; the last
-// to arrive reads the partials back with device-coherent loads, sums them in
-// split order into acc, re-arms the counter and returns true. The others
-// return false and must exit. *flag is workgroup-shared scratch.
-// Workspace layout of one tile: [split][piece][thread] 16-byte pieces, so each
-// wave's store or load covers 1 KB contiguously.
-namespace {
-constexpr int kBufDword3 = 0x00020000;  // gfx9 raw buffer: 32-bit dwords, no format conversion
-constexpr int kCacheSc1 = 16;           // cache policy: device-coherent (SC1)
-}  // namespace
-
-template <int TM, int TN, int NT, typename V>
-__device__ __forceinline__ bool splitk_reduce(const GemmArgs& p, V (&acc)[TM][TN],
-                                              int64_t tile, int split, int tid, int* flag) {
-  constexpr int VW = sizeof(V) / sizeof(float);  // 16 (32x32 tiles) or 4 (16x16)
-  static_assert(VW % 4 == 0, "whole 16-byte pieces");
-  constexpr int PV = VW / 4;                     // pieces per accumulator register group
-  constexpr int Q4 = TM * TN * PV;               // pieces per thread
-  constexpr uint32_t SPLIT_BYTES = (uint32_t)Q4 * NT * 16;
-  float* part = p.ws_part + (tile * p.split_k) * (int64_t)Q4 * 4 * NT;
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(part, 0, (int)(SPLIT_BYTES * (uint32_t)p.split_k), kBufDword3);
-  using v4i = int __attribute__((ext_vector_type(4)));
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int c = 0; c < PV; ++c) {
-        const v4i v = {__float_as_int(acc[i][j][4 * c]), __float_as_int(acc[i][j][4 * c + 1]),
-                       __float_as_int(acc[i][j][4 * c + 2]), __float_as_int(acc[i][j][4 * c + 3])};
-        __builtin_amdgcn_raw_buffer_store_b128(v, rs, (uint32_t)(((i * TN + j) * PV + c) * NT + tid) * 16,
-                                               (uint32_t)split * SPLIT_BYTES, kCacheSc1);
-      }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const int old = atomicAdd(p.ws_count + tile, 1);
-    *flag = (old == p.split_k - 1);
-  }
-  __syncthreads();
-  if (!*flag) return false;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int c = 0; c < PV; ++c) {
-        const uint32_t off = (uint32_t)(((i * TN + j) * PV + c) * NT + tid) * 16;
-        v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCacheSc1);
-        float s0 = __int_as_float(v.x), s1 = __int_as_float(v.y), s2 = __int_as_float(v.z),
-              s3 = __int_as_float(v.w);
-        for (int sp = 1; sp < p.split_k; ++sp) {
-          v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, (uint32_t)sp * SPLIT_BYTES, kCacheSc1);
-          s0 += __int_as_float(v.x);
-          s1 += __int_as_float(v.y);
-          s2 += __int_as_float(v.z);
-          s3 += __int_as_float(v.w);
-        }
-        acc[i][j][4 * c] = s0;
-        acc[i][j][4 * c + 1] = s1;
-        acc[i][j][4 * c + 2] = s2;
-        acc[i][j][4 * c + 3] = s3;
-      }
-  if (tid == 0) __hip_atomic_store(p.ws_count + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return true;
 }
 
 // ---------------------------------------------------------------------------
