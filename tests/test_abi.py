@@ -355,3 +355,18 @@ def test_shipped_tables_parse(lib):
                 assert r == 0
             else:
                 assert r == 1 and c["variant"] == val["variant"], (name, key)
+
+
+def test_split_requests_above_k_stages_are_lowered(lib):
+    # a split never gets an empty K range: split 4 over two 128-deep stages
+    # sizes its workspace as split 2, three stages as split 3
+    ws = lib.fp8_scaled_mm_workspace_size
+
+    def size(variant, split, k, kind=_lib.KIND_CHANNELWISE, m=64, n=256):
+        cfg = _lib.TileConfig(_lib.VARIANTS[variant], 0, 0, 0, split, 0)
+        return ws(kind, m, n, k, ctypes.byref(cfg))
+
+    for v in ("t64x32deep", "t64x64panel", "t32x32deep"):
+        assert size(v, 4, 256) == size(v, 2, 256) > size(v, 1, 256)
+        assert size(v, 4, 384) == size(v, 3, 384) > size(v, 2, 384)
+        assert size(v, 4, 640, kind=_lib.KIND_BLOCKWISE) == size(v, 3, 640, kind=_lib.KIND_BLOCKWISE)

@@ -376,3 +376,37 @@ def test_narrow_tiles_fall_back_when_k_not_multiple_of_128():
                       sample=False)
     _channelwise_case("narrow-fallback", 70, 200, 1088, 0.0, True, config=ops.make_config("t64x32deep", 3),
                       sample=False)
+
+
+SPLIT4_CASES = [  # (variant, kind, split_k, M, N, K): split 4 as the tile tables choose it at M <= 128,
+    # and requests the host clamps (more splits than 128-deep stages: K = 256 -> 2 splits,
+    # K = 384 -> 3, K = 640 -> 3 uneven splits of 2, 2, 1 stages)
+    ("t64x32deep", "cw", 4, 64, 392, 4096), ("t64x64deep", "cw", 4, 61, 256, 12288),
+    ("t64x64panel", "bw", 4, 37, 384, 1024), ("t32x32deep", "bw", 4, 16, 7168, 7168),
+    ("t128x64panel", "cw", 4, 100, 512, 4096), ("t32x32deep", "cw", 4, 20, 200, 256),
+    ("t64x64deep", "bw", 4, 64, 256, 384), ("t64x32deep", "cw", 4, 33, 136, 640),
+    ("t64x64", "cw", 8, 33, 128, 512), ("t128x64k256", "bw", 3, 70, 256, 256)]
+
+
+@pytest.mark.parametrize("variant,kind,split_k,m,n,k", SPLIT4_CASES,
+                         ids=[f"{c[0]}-{c[1]}-sk{c[2]}-M{c[3]}-N{c[4]}-K{c[5]}" for c in SPLIT4_CASES])
+def test_split_k_four_and_clamped(variant, kind, split_k, m, n, k):
+    """Split-K partials exchanged in 16-byte device-coherent pieces: split 4
+    on the narrow deep-ring and panel tiles, and split requests above the
+    number of K stages (the host lowers them)."""
+    cfg = ops.make_config(variant, split_k)
+    if kind == "cw":
+        _channelwise_case("split4", m, n, k, 0.0, True, config=cfg)
+    else:
+        _blockwise_case("split4", m, n, k, config=cfg, with_bias=True)
+
+
+def test_panel_split_k_deterministic_and_fresh_partials():
+    """Panel-tile split-K: the same call twice gives the same bits, and calls
+    on other data in between (same workspace, same tile count) leave nothing
+    behind that the next call reads."""
+    for cfg in (ops.make_config("t64x32deep", 4), ops.make_config("t64x64panel", 2)):
+        _, o1 = _channelwise_case("o_proj", 96, 4096, 4096, 0.01, False, config=cfg, sample=False)
+        _channelwise_case("qwen3_8b", 96, 4096, 4096, 0.0, True, config=cfg, sample=False)
+        _, o2 = _channelwise_case("o_proj", 96, 4096, 4096, 0.01, False, config=cfg, sample=False)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
