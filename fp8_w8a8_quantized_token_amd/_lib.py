@@ -93,6 +93,7 @@ SIGNATURES = {
                                         c_i64, c_i64, c_i32, c_f32, c_vp, c_i64, c_vp, c_vp, c_size,
                                         ctypes.POINTER(TileConfig), c_i32, c_vp]),
     "fp8_linear_launches": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(TileConfig)]),
+    "fp8_linear_launches_ex": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(TileConfig), c_i32]),
     "fp8_tile_config_lookup": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(TileConfig)]),
     "fp8_tile_config_default": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(TileConfig)]),
     "fp8_tile_config_set_dir": (c_i32, [ctypes.c_char_p]),

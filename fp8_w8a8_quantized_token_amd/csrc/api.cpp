@@ -147,8 +147,16 @@ bool fused_linear_enabled() {
   return !(v && v[0] == '0' && v[1] == '\0');
 }
 
-bool linear_fuses(const fp8_tile_config& cfg, int64_t M) {
-  return cfg.variant == FP8_VARIANT_SKINNY && M <= kFusedRows && fused_linear_enabled();
+// With SiLU-and-mul every workgroup of the fused launch evaluates SiLU over
+// the whole activation (per token twice: the row maximum first), which pays
+// off only for the fewest rows: measured on the down projections (4096x12288
+// channelwise, 4096x1536 and 7168x2048 blockwise), one launch is 1.7 us
+// faster at M = 1 channelwise and 1.2-3.9 us at M <= 2 blockwise, but 4-15 us
+// slower at M = 2 and 4 channelwise and up to 2 us slower at M = 4 blockwise.
+bool linear_fuses(int kind, const fp8_tile_config& cfg, int64_t M, int32_t flags) {
+  if (cfg.variant != FP8_VARIANT_SKINNY || M > kFusedRows || !fused_linear_enabled()) return false;
+  if (flags & FP8_QUANT_FUSE_SILU_MUL) return M <= (kind == FP8_KIND_CHANNELWISE ? 1 : 2);
+  return true;
 }
 
 // Activation quantization then scaled GEMM; one fused launch when the skinny
@@ -174,14 +182,14 @@ int run_linear(const char* fn, int kind, const uint16_t* x, const uint8_t* b, co
   fp8_tile_config cfg;
   st = resolve_config(kind, M, N, K, cfg_in, &cfg);
   if (st) return st;
-  if (flags == 0 && linear_fuses(cfg, M)) {
+  if (linear_fuses(kind, cfg, M, flags)) {
     GemmArgs p{};
     p.a = q; p.b = b; p.sa = a_scale; p.sa_ld = m_pad; p.sb = b_scale; p.bias = bias; p.out = out;
     p.M = M; p.N = N; p.K = K; p.lda = ldq; p.ldb = ldb; p.ldc = ldc;
     p.split_k = 1;
     p.k_tiles_per_split = (int)((K + 127) / 128);
     const QuantArgs qa{x, ldx, q, ldq, a_scale, m_pad, eps};
-    return hip_status(launch_linear_fused(kind, p, qa, stream), fn);
+    return hip_status(launch_linear_fused(kind, p, qa, flags, stream), fn);
   }
   const hipError_t e = bw ? launch_quant_per_token_group(x, M, K, ldx, 128, m_pad, q, ldq, a_scale, eps, flags, stream)
                           : launch_quant_per_token(x, M, K, ldx, q, ldq, a_scale, eps, flags, stream);
@@ -464,14 +472,21 @@ int fp8_linear_blockwise(const uint16_t* x, const uint8_t* b, const float* b_sca
                                  q, ldq, a_scale, ws, ws_bytes, cfg, 0, stream);
 }
 
-int fp8_linear_launches(int32_t kind, int64_t M, int64_t N, int64_t K, const fp8_tile_config* cfg_in) {
+int fp8_linear_launches_ex(int32_t kind, int64_t M, int64_t N, int64_t K, const fp8_tile_config* cfg_in,
+                           int32_t flags) {
   if ((kind != FP8_KIND_CHANNELWISE && kind != FP8_KIND_BLOCKWISE) || M < 0 || N <= 0 || K <= 0)
     return fail(FP8_ERR_INVALID, "fp8_linear_launches: bad arguments");
+  int st = check_quant_flags("fp8_linear_launches", flags);
+  if (st) return st;
   if (M == 0) return 0;
   fp8_tile_config cfg;
-  const int st = resolve_config(kind, M, N, K, cfg_in, &cfg);
+  st = resolve_config(kind, M, N, K, cfg_in, &cfg);
   if (st) return st;
-  return linear_fuses(cfg, M) ? 1 : 2;
+  return linear_fuses(kind, cfg, M, flags) ? 1 : 2;
+}
+
+int fp8_linear_launches(int32_t kind, int64_t M, int64_t N, int64_t K, const fp8_tile_config* cfg_in) {
+  return fp8_linear_launches_ex(kind, M, N, K, cfg_in, 0);
 }
 
 int fp8_tile_config_lookup(int32_t kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* out) {

@@ -1321,17 +1321,40 @@ __device__ __forceinline__ void stream_load(const GemmArgs& p, StreamRegs<MT, KI
 // quantizing work grows with M, not with the 16-row MFMA tile. Its bf16 loads
 // are issued before the chunk's weight loads: loads complete in issue order,
 // so the quantization waits only for the (cache-resident) activation while
-// the weight chunk is still arriving from HBM.
-template <int FR>
+// the weight chunk is still arriving from HBM. QF holds the quantizer flags:
+// with SiLU-and-mul the rows are [gate | up] (2K wide) and the up half of the
+// unit is loaded into xu beside the gate; the SiLU itself runs when the unit
+// is quantized, so these loads stay ahead of the weight loads.
+template <int QF>
+constexpr int fused_up_regs(int fr) { return (QF & kQuantSiluMul) != 0 ? fr : 1; }
+
+template <int FR, int QF>
 __device__ __forceinline__ void fused_load_x(const GemmArgs& p, const QuantArgs& qa, uint4 (&xr)[FR],
-                                             int64_t k0, int tid) {
+                                             uint4 (&xu)[fused_up_regs<QF>(FR)], int64_t k0, int tid) {
   const int64_t k = k0 + 8 * tid;
   const bool kin = k < p.K;
 #pragma unroll
   for (int i = 0; i < FR; ++i) {
     const bool ok = i < p.M && kin;
-    xr[i] = keep_if(ok, load16(qa.x + (i < p.M ? i : p.M - 1) * qa.ldx + (kin ? k : 0)));
+    const uint16_t* row = qa.x + (i < p.M ? i : p.M - 1) * qa.ldx;
+    xr[i] = keep_if(ok, load16(row + (kin ? k : 0)));
+    if constexpr ((QF & kQuantSiluMul) != 0) xu[i] = keep_if(ok, load16(row + p.K + (kin ? k : 0)));
   }
+}
+
+// The 8 bf16 values of a fused unit that are quantized: the loaded values, or
+// silu(gate) * up correctly rounded to bf16 (zero where nothing was loaded).
+template <int QF>
+__device__ __forceinline__ uint4 fused_values(const uint4& g, const uint4& u) {
+  if constexpr ((QF & kQuantSiluMul) != 0) return silu_mul8(g, u);
+  else return g;
+}
+
+// Scale of a fused row or group from its |x| maximum, as the quantizers form it.
+template <int QF>
+__device__ __forceinline__ float fused_scale(float amax, float eps) {
+  const float s = fmaxf(amax, eps) / kE4M3Max;
+  return (QF & kQuantUe8m0) != 0 ? pow2_ceil(s) : s;
 }
 
 // Max over each aligned group of 16 lanes, with DPP lane moves (no LDS
@@ -1351,11 +1374,13 @@ __device__ __forceinline__ float max16_dpp(float v) {
 
 // FR > 0: the activation quantization is fused, for M <= FR rows (FR a power
 // of two, a compile-time row count so that the per-row work is straight-line
-// code the compiler can interleave).
-template <int MT, int KIND, int FR>
+// code the compiler can interleave), with the quantizer flags QF.
+template <int MT, int KIND, int FR, int QF = 0>
 __global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs p, QuantArgs qa) {
   constexpr bool FQ = FR > 0;
+  constexpr bool SILU = (QF & kQuantSiluMul) != 0;
   static_assert(!FQ || (MT == 1 && FR <= 16), "the fused quantization serves one 16-row tile");
+  static_assert(FQ || QF == 0, "quantizer flags belong to the fused quantization");
   constexpr int CPR = kStreamChunk / 16;  // 16-byte LDS chunks per chunk row
   constexpr int BPC = kStreamChunk / 128; // K blocks per chunk
   __shared__ uint4 wt[16 * CPR];          // 64 KB: one weight chunk
@@ -1379,7 +1404,8 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs
   for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   uint4 xr[FQ ? FR : 1];
-  if constexpr (FQ) fused_load_x<FR>(p, qa, xr, 0, tid);
+  uint4 xu[FQ ? fused_up_regs<QF>(FR) : 1];
+  if constexpr (FQ) fused_load_x<FR, QF>(p, qa, xr, xu, 0, tid);
   StreamRegs<MT, KIND> cur;
   stream_load<MT, KIND, FQ>(p, cur, 0, n0, wave, lane);
 
@@ -1395,15 +1421,16 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs
       const bool kin = k < p.K;
 #pragma unroll
       for (int i = 0; i < FR; ++i) {
+        const uint4 v = fused_values<QF>(xr[i], xu[SILU ? i : 0]);
         float sc, y;
         if constexpr (KIND == kChannelwise) {
           sc = row_scale[i];
           y = row_inv[i];
         } else {  // group of 128 = 16 consecutive threads
-          sc = fmaxf(max16_dpp(absmax8_bf16(xr[i])), qa.eps) / kE4M3Max;
+          sc = fused_scale<QF>(max16_dpp(absmax8_bf16(v)), qa.eps);
           y = 1.0f / sc;
         }
-        const uint2 c = kin ? quant8_bf16(xr[i], sc, y) : make_uint2(0, 0);
+        const uint2 c = kin ? quant8_bf16(v, sc, y) : make_uint2(0, 0);
         *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(codes) + i * (CPR * 16) +
                                   (pos ^ (i << 4))) = c;
         if (KIND == kBlockwise && (tid & 15) == 0) blk_scale[i * BPC + (tid >> 4)] = sc;
@@ -1425,12 +1452,14 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs
       // are read here once more), reduced over the workgroup through LDS
       float am[FR];
 #pragma unroll
-      for (int i = 0; i < FR; ++i) am[i] = absmax8_bf16(xr[i]);  // zero where not loaded
+      for (int i = 0; i < FR; ++i)  // zero where not loaded
+        am[i] = absmax8_bf16(fused_values<QF>(xr[i], xu[SILU ? i : 0]));
       for (int64_t k1 = kStreamChunk; k1 < p.K; k1 += kStreamChunk) {
-        uint4 xn[FR];
-        fused_load_x<FR>(p, qa, xn, k1, tid);
+        uint4 xn[FR], xnu[fused_up_regs<QF>(FR)];
+        fused_load_x<FR, QF>(p, qa, xn, xnu, k1, tid);
 #pragma unroll
-        for (int i = 0; i < FR; ++i) am[i] = fmaxf(am[i], absmax8_bf16(xn[i]));
+        for (int i = 0; i < FR; ++i)
+          am[i] = fmaxf(am[i], absmax8_bf16(fused_values<QF>(xn[i], xnu[SILU ? i : 0])));
       }
 #pragma unroll
       for (int i = 0; i < FR; ++i) {
@@ -1441,7 +1470,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs
       if (tid < FR) {
         float mx = row_part[tid];
         for (int w = 1; w < kStreamWaves; ++w) mx = fmaxf(mx, row_part[w * 16 + tid]);
-        const float sc = fmaxf(mx, qa.eps) / kE4M3Max;
+        const float sc = fused_scale<QF>(mx, qa.eps);
         row_scale[tid] = sc;
         row_inv[tid] = 1.0f / sc;
         if (writer && tid < p.M) qa.scale[tid] = sc;
@@ -1466,7 +1495,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs
     StreamRegs<MT, KIND> use = cur;
     const bool more = k0 + kStreamChunk < p.K;
     if (more) {
-      if constexpr (FQ) fused_load_x<FR>(p, qa, xr, k0 + kStreamChunk, tid);
+      if constexpr (FQ) fused_load_x<FR, QF>(p, qa, xr, xu, k0 + kStreamChunk, tid);
       stream_load<MT, KIND, FQ>(p, cur, k0 + kStreamChunk, n0, wave, lane);
     }
 #pragma unroll
@@ -1734,26 +1763,37 @@ size_t variant_workspace_bytes(int variant, int split_k, int64_t M, int64_t N) {
 }
 
 namespace {
-template <int KIND, int FR>
+template <int KIND, int FR, int QF>
 hipError_t launch_fused_rows(const GemmArgs& p, const QuantArgs& qa, hipStream_t stream) {
   const dim3 grid((unsigned)((p.N + 15) / 16)), block(kStreamWaves * 64);
-  hipLaunchKernelGGL((gemm_skinny_kernel<1, KIND, FR>), grid, block, 0, stream, p, qa);
+  hipLaunchKernelGGL((gemm_skinny_kernel<1, KIND, FR, QF>), grid, block, 0, stream, p, qa);
   return hipGetLastError();
 }
 
-template <int KIND>
+template <int KIND, int QF>
 hipError_t launch_fused_kind(const GemmArgs& p, const QuantArgs& qa, hipStream_t stream) {
-  if (p.M <= 1) return launch_fused_rows<KIND, 1>(p, qa, stream);
-  if (p.M <= 2) return launch_fused_rows<KIND, 2>(p, qa, stream);
-  if (p.M <= 4) return launch_fused_rows<KIND, 4>(p, qa, stream);
+  if (p.M <= 1) return launch_fused_rows<KIND, 1, QF>(p, qa, stream);
+  if (p.M <= 2) return launch_fused_rows<KIND, 2, QF>(p, qa, stream);
+  if (p.M <= 4) return launch_fused_rows<KIND, 4, QF>(p, qa, stream);
   static_assert(kFusedRows == 4, "fused row buckets");
   return hipErrorInvalidValue;
 }
+
+template <int KIND>
+hipError_t launch_fused_flags(const GemmArgs& p, const QuantArgs& qa, int flags, hipStream_t stream) {
+  switch (flags & (kQuantSiluMul | kQuantUe8m0)) {
+    case 0: return launch_fused_kind<KIND, 0>(p, qa, stream);
+    case kQuantSiluMul: return launch_fused_kind<KIND, kQuantSiluMul>(p, qa, stream);
+    case kQuantUe8m0: return launch_fused_kind<KIND, kQuantUe8m0>(p, qa, stream);
+    default: return launch_fused_kind<KIND, kQuantSiluMul | kQuantUe8m0>(p, qa, stream);
+  }
+}
 }  // namespace
 
-hipError_t launch_linear_fused(int kind, const GemmArgs& p, const QuantArgs& qa, hipStream_t stream) {
-  return kind == kChannelwise ? launch_fused_kind<kChannelwise>(p, qa, stream)
-                              : launch_fused_kind<kBlockwise>(p, qa, stream);
+hipError_t launch_linear_fused(int kind, const GemmArgs& p, const QuantArgs& qa, int flags,
+                               hipStream_t stream) {
+  return kind == kChannelwise ? launch_fused_flags<kChannelwise>(p, qa, flags, stream)
+                              : launch_fused_flags<kBlockwise>(p, qa, flags, stream);
 }
 
 namespace {

@@ -84,7 +84,9 @@ struct QuantArgs {
 };
 constexpr int64_t kFusedRows = 4;
 
-hipError_t launch_linear_fused(int kind, const GemmArgs& args, const QuantArgs& qa,
+// flags: the quantizer flags (kQuantSiluMul: x rows are [gate | up], 2K wide,
+// and silu(gate) * up is quantized; kQuantUe8m0: power-of-two scales).
+hipError_t launch_linear_fused(int kind, const GemmArgs& args, const QuantArgs& qa, int flags,
                                hipStream_t stream);
 
 // Geometry of a compiled kernel variant.

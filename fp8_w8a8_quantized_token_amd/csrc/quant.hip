@@ -28,94 +28,6 @@ namespace fp8w8a8 {
 //  * Static: a given fp32 scale, codes E4M3(clamp(x / s)), no scale written.
 // ---------------------------------------------------------------------------
 
-// Smallest power of two >= s, for a positive normal fp32 s.
-__device__ __forceinline__ float pow2_ceil(float s) {
-  uint32_t b = __float_as_uint(s);
-  if (b & 0x007FFFFFu) b = (b & 0xFF800000u) + 0x00800000u;
-  return __uint_as_float(b);
-}
-
-// Nearest bf16 (ties to even) of a double, without double rounding: the
-// conversion to fp32 is made round-to-odd (inexact results get their last bit
-// set after truncation), which keeps 16 guard bits for the bf16 rounding.
-__device__ __forceinline__ uint32_t bf16_of_f64(double d) {
-  const float f = (float)d;  // round to nearest
-  uint32_t b = __float_as_uint(f);
-  const double back = (double)f;
-  if (back != d) {
-    if (fabs(back) > fabs(d)) b -= 1u;  // rounded away from zero: step back
-    b |= 1u;
-  }
-  return f32_to_bf16(__uint_as_float(b));
-}
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// Two fp32 values -> two bf16 (a in the low half), round to nearest even: the
-// packed hardware convert of gfx950.
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const f32x2_t v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-
-// silu(g) * u in fp32: e^-g as 2^(-g log2 e) on the hardware exp2 (within 1
-// ulp), then the reciprocal (1 ulp) and two products. Relative error at most
-// (|g| + 7) 2^-24 for g >= -16: rounding -g log2 e costs |g| 2^-24 once the
-// exponent is taken, the other steps 7 2^-24 together; for g > 16.6 the
-// e^-g term is below half an ulp of 1 and its error drops out.
-__device__ __forceinline__ float silu_mul_f32(float g, float u) {
-  const float t = __builtin_amdgcn_exp2f(g * -1.44269504088896340736f);
-  return (g * __builtin_amdgcn_rcpf(1.0f + t)) * u;
-}
-
-// True where the fp32 value y = silu_mul_f32(g, u) may round to a different
-// bf16 than the exact product: y lies within 48 fp32 ulps of a bf16 rounding
-// midpoint (low 16 bits near 0x8000; the error bound above is at most 23 ulps
-// for g >= -16), or g < -16, outside that bound.
-__device__ __forceinline__ bool silu_needs_f64(float g, float y) {
-  const uint32_t low = __float_as_uint(y) & 0xFFFFu;
-  return !(g >= -16.0f) || (low - (0x8000u - 48u)) <= 96u;
-}
-
-// bf16 bits of silu(g) * u from fp64 (exp in fp64 within 1 ulp, IEEE
-// division): correctly rounded unless the exact value lies within ~2^-50
-// relative of a bf16 midpoint.
-__device__ __noinline__ uint32_t silu_mul_bf16_f64(float g, float u) {
-  const double gd = (double)g;
-  return bf16_of_f64(gd / (1.0 + exp(-gd)) * (double)u);
-}
-
-// 8 gate and 8 up bf16 values -> 8 bf16 values of silu(gate) * up, correctly
-// rounded. All eight fp32 evaluations run first, straight-line; the few that
-// sit too close to a bf16 rounding midpoint (about 1 in 700 on normal data)
-// are redone in fp64 behind one branch per 8 values.
-__device__ __forceinline__ uint4 silu_mul8(const uint4& g, const uint4& u) {
-  const uint32_t gp[4] = {g.x, g.y, g.z, g.w};
-  const uint32_t up[4] = {u.x, u.y, u.z, u.w};
-  float gf[8], uf[8], y[8];
-  bool redo = false;  // a lane mask: the per-value tests are repeated in the rare branch
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    gf[i] = bf16_to_f32((i & 1) ? (gp[i >> 1] >> 16) : (gp[i >> 1] & 0xffffu));
-    uf[i] = bf16_to_f32((i & 1) ? (up[i >> 1] >> 16) : (up[i >> 1] & 0xffffu));
-    y[i] = silu_mul_f32(gf[i], uf[i]);
-    redo = redo || silu_needs_f64(gf[i], y[i]);
-  }
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
-  if (redo) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (silu_needs_f64(gf[i], y[i])) {
-        const uint32_t b = silu_mul_bf16_f64(gf[i], uf[i]);
-        o[i >> 1] = (i & 1) ? ((o[i >> 1] & 0xffffu) | (b << 16)) : ((o[i >> 1] & 0xffff0000u) | b);
-      }
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
 // The 16 values of unit u of a row as bf16: the input itself, or (SiLU-and-mul)
 // silu(gate) * up from the two halves of a 2K-wide row.
 template <int FLAGS>

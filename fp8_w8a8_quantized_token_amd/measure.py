@@ -423,6 +423,63 @@ def measure_stream_ceiling(warmup, calls, filler):
     return lines
 
 
+# Down projections fed straight from a gated MLP's [gate | up] output: the
+# decode linears with SiLU-and-mul, as one launch (quantization inside the
+# weight-streaming GEMM) and as the flagged quantizer followed by the GEMM.
+SILU_LINEAR_SHAPES = [("channelwise", 4096, 12288), ("blockwise", 4096, 1536), ("blockwise", 7168, 2048)]
+
+
+def measure_silu_linear(warmup, calls, filler):
+    dev = torch.device("cuda:0")
+    head = "| kind | N×K | M | path | launches | weight sets | µs per call | GB/s (weight + 2K-wide input) |"
+    lines = [head, "|---|---|---|---|---|---|---|---|"]
+    print(head, flush=True)
+    print(lines[1], flush=True)
+    for kind, n, k in SILU_LINEAR_SHAPES:
+        sets = max(2, min(MAX_SETS, math.ceil(ROTATE_BYTES / (n * k))))
+        w = synth.weights(f"measure/silu/{kind}", n, k).to(torch.bfloat16).to(dev)
+        if kind == "channelwise":
+            wq, ws = ops.quant_per_token(w)
+        else:
+            wq, _ = ops.quant_per_token_group(w, 128, row_alignment=1)
+            wq = wq.contiguous()
+            ws = synth.positive_scales(f"measure/silu/{n}/{k}", (n // 128, k // 128)).to(dev)
+        del w
+        weights = [(wq.clone(), ws.clone()) for _ in range(sets)]
+        for m in (1, 2, 4):
+            x = synth.activations(f"measure/silu/{kind}", m, 2 * k).to(dev)
+            m_pad = ops.padded_rows(m, 4)
+            out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            q = torch.empty((m if kind == "channelwise" else m_pad, k), dtype=torch.uint8, device=dev)
+            s = torch.empty((m,) if kind == "channelwise" else (k // 128, m_pad), dtype=torch.float32,
+                            device=dev)
+            if kind == "channelwise":
+                one = [ops.prepare("linear_channelwise", x, wb, wsb, out=out, q=q, scale=s, silu_mul=True)
+                       for wb, wsb in weights]
+                quant = ops.prepare("silu_mul_quant_per_token", x, out=q, scale=s)
+                gemms = [ops.prepare("scaled_mm_channelwise", q, wb, s, wsb, out=out) for wb, wsb in weights]
+            else:
+                one = [ops.prepare("linear_blockwise", x, wb, wsb, out=out, q=q, scale=s, row_alignment=4,
+                                   silu_mul=True) for wb, wsb in weights]
+                quant = ops.prepare("silu_mul_quant_per_token_group", x, 128, row_alignment=4, out=q,
+                                    scale_storage=s)
+                gemms = [ops.prepare("scaled_mm_blockwise", q, wb, s.transpose(0, 1), wsb, m=m, out=out)
+                         for wb, wsb in weights]
+            two = []
+            for g in gemms:
+                two.append(lambda g=g: (quant(), g()))
+            nbytes = n * k + 4 * m * k
+            for name, fns, nl in (("single launch", one, 1), ("quantizer + GEMM", two, 2)):
+                us = _batch_us(fns, warmup, calls, filler)
+                line = (f"| {kind} | {n}×{k} | {m} | {name} | {nl} | {sets} | {us:.2f} | "
+                        f"{nbytes / us / 1e3:.0f} |")
+                lines.append(line)
+                print(line, flush=True)
+        del weights
+        torch.cuda.empty_cache()
+    return lines
+
+
 def row(cfg, kind, n, k, m, r, bias):
     g = r["gemm"]
     p50 = percentile(g, 50)
@@ -452,6 +509,8 @@ def main(argv=None):
                     help="time the 16x16 blockwise tile with fp32 and with power-of-two scales")
     ap.add_argument("--moe", action="store_true",
                     help="time the masked quantizer and grouped blockwise GEMM over MoE experts")
+    ap.add_argument("--silu-linear", action="store_true",
+                    help="time the decode down projection with SiLU-and-mul: one launch against two")
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="time plain device copies and reductions at the small-M linears' byte counts")
     args = ap.parse_args(argv)
@@ -459,13 +518,14 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     want = args.workloads.split(",")
     filler = _Filler(dev)
-    if args.quant_variants or args.ue8m0_gemm or args.moe or args.stream_ceiling:
+    if args.quant_variants or args.ue8m0_gemm or args.moe or args.stream_ceiling or args.silu_linear:
         t0 = time.time()
         mode = (measure_quant_variants if args.quant_variants else
                 measure_ue8m0_gemm if args.ue8m0_gemm else
-                measure_moe if args.moe else measure_stream_ceiling)
+                measure_moe if args.moe else
+                measure_silu_linear if args.silu_linear else measure_stream_ceiling)
         lines = mode(args.warmup, args.calls, filler)
-        if args.stream_ceiling:
+        if args.stream_ceiling or args.silu_linear:
             note = (f"\n{args.calls} calls per row after {args.warmup} warm-up calls, timed as one "
                     f"batch with HIP events behind queued device copies (average per call); "
                     f"buffers rotated to cover >= 1 GiB. {time.time() - t0:.0f} s.")

@@ -373,7 +373,8 @@ def linear_channelwise(x, w_q, w_s, bias=None, eps=1e-10, config=None, return_qu
     otherwise. return_quant=True also returns the codes [M, K] and scales [M].
     silu_mul=True: x is [..., 2K] = [gate | up] and the quantized row is
     SiLU(gate) * up rounded to bf16 (the down projection after a gated MLP);
-    scale_ue8m0=True: power-of-two activation scales. Either flag: two launches."""
+    scale_ue8m0=True: power-of-two activation scales. The single launch takes
+    UE8M0 up to M = 4 and SiLU-and-mul at M = 1 (blockwise: M <= 2)."""
     shape = x.shape
     x2 = x.reshape(-1, shape[-1])
     args, (out, q, s, _, _) = _linear_args(KIND_CHANNELWISE, x2, w_q, w_s, bias, eps, 1, config,
@@ -404,10 +405,10 @@ def linear_blockwise(x, w_q, w_s, bias=None, block_size=(128, 128), eps=1e-10,
     return (out, q, st.transpose(0, 1)) if return_quant else out
 
 
-def linear_launches(kind, m, n, k, config=None):
+def linear_launches(kind, m, n, k, config=None, silu_mul=False, scale_ue8m0=False):
     """Kernel launches one linear call makes: 1 (fused), 2, or 0 for M == 0."""
     cfg = ctypes.byref(config) if config is not None else None
-    r = _lib.load().fp8_linear_launches(kind, m, n, k, cfg)
+    r = _lib.load().fp8_linear_launches_ex(kind, m, n, k, cfg, _flags(silu_mul, scale_ue8m0))
     if r < 0:
         check(r)
     return r

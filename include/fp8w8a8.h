@@ -419,8 +419,14 @@ int fp8_linear_blockwise(const uint16_t* x, const uint8_t* b, const float* b_sca
  * activation scales are powers of two, and the blockwise linear then runs the
  * GEMM as fp8_scaled_mm_blockwise_ue8m0 (its weight block scales must be powers
  * of two as well). q, a_scale and out hold exactly what the flagged quantizer
- * and that GEMM write. Any flag set: always two launches (quantizer, GEMM).
- * flags == 0 is exactly fp8_linear_channelwise / fp8_linear_blockwise. */
+ * and that GEMM write. With the skinny kernel selected the flags apply inside
+ * the single fused launch (SiLU-and-mul evaluated there, correctly rounded as
+ * in the quantizer) for M <= 4 with UE8M0 alone, and with SiLU-and-mul for
+ * M = 1 channelwise and M <= 2 blockwise (every workgroup of that launch
+ * evaluates SiLU over the whole input, which pays only for so few rows); the
+ * other calls run the flagged quantizer and the GEMM as two launches.
+ * fp8_linear_launches_ex tells which. flags == 0 is exactly
+ * fp8_linear_channelwise / fp8_linear_blockwise. */
 int fp8_linear_channelwise_ex(const uint16_t* x, const uint8_t* b, const float* b_scale,
                               const uint16_t* bias, uint16_t* out,
                               int64_t M, int64_t N, int64_t K,
@@ -443,6 +449,11 @@ int fp8_linear_blockwise_ex(const uint16_t* x, const uint8_t* b, const float* b_
  * arguments. Host only. */
 int fp8_linear_launches(int32_t kind, int64_t M, int64_t N, int64_t K,
                         const fp8_tile_config* cfg);
+
+/* The same for an fp8_linear_*_ex call with quantizer `flags` (unknown bits:
+ * FP8_ERR_INVALID). Host only. */
+int fp8_linear_launches_ex(int32_t kind, int64_t M, int64_t N, int64_t K,
+                           const fp8_tile_config* cfg, int32_t flags);
 
 /* ------------------------------------------------------------------------ */
 /* Tile-config table                                                         */

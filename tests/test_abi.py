@@ -199,6 +199,20 @@ def test_linear_launch_counts(lib):
     assert n(7, 1, 4096, 4096, None) == _lib.FP8_ERR_INVALID
 
 
+def test_linear_launch_counts_with_flags(lib):
+    n = lib.fp8_linear_launches_ex
+    silu, ue = _lib.QUANT_FUSE_SILU_MUL, _lib.QUANT_SCALE_UE8M0
+    for kind in (_lib.KIND_CHANNELWISE, _lib.KIND_BLOCKWISE):
+        assert [n(kind, m, 4096, 4096, None, ue) for m in (1, 2, 4, 5)] == [1, 1, 1, 2]
+        assert n(kind, 0, 4096, 4096, None, silu) == 0
+    # SiLU-and-mul stays in the single launch only for the fewest rows
+    assert [n(_lib.KIND_CHANNELWISE, m, 4096, 12288, None, silu) for m in (1, 2, 4)] == [1, 2, 2]
+    assert [n(_lib.KIND_BLOCKWISE, m, 7168, 2048, None, silu | ue) for m in (1, 2, 3, 4)] == [1, 1, 2, 2]
+    assert n(_lib.KIND_CHANNELWISE, 1, 4096, 4096, None, 4) == _lib.FP8_ERR_INVALID
+    assert n(_lib.KIND_CHANNELWISE, 1, 4096, 4096, None, 0) == lib.fp8_linear_launches(
+        _lib.KIND_CHANNELWISE, 1, 4096, 4096, None)
+
+
 def test_fused_linear_kill_switch(lib, monkeypatch):
     n = lib.fp8_linear_launches
     monkeypatch.setenv("FP8W8A8_FUSED_LINEAR", "0")

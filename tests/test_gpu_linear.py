@@ -260,10 +260,14 @@ def test_linear_tiny_shapes(kind, m, n, k):
     _check(out, ref, tau, f"linear tiny {kind} M={m} N={n} K={k}")
 
 
-FLAG_CASES = [  # (kind, M, N, K, silu_mul, scale_ue8m0)
+FLAG_CASES = [  # (kind, M, N, K, silu_mul, scale_ue8m0); M <= 4 is the single launch
     ("cw", 1, 4096, 1536, True, False), ("cw", 37, 4096, 1536, True, False),
     ("cw", 300, 4096, 4096, True, True), ("cw", 3, 512, 1024, False, True),
+    ("cw", 2, 4096, 12288, True, True), ("cw", 4, 392, 4112, True, False),
+    ("cw", 1, 392, 4112, True, True), ("cw", 1, 4096, 12288, True, False),
+    ("cw", 1, 256, 8224, False, True),
     ("bw", 1, 4096, 1536, True, False), ("bw", 4, 4096, 1536, True, True),
+    ("bw", 2, 3072, 4096, False, True), ("bw", 3, 7168, 2048, True, False),
     ("bw", 64, 4096, 1536, False, True), ("bw", 513, 4096, 1536, True, True),
     ("bw", 2048, 7168, 2048, False, True)]
 
@@ -276,9 +280,16 @@ def test_linear_with_quant_flags(kind, m, n, k, silu, ue8m0):
     of 2K values (the down projection straight from the gate/up output) and
     UE8M0 makes the activation scales powers of two (blockwise: the GEMM then
     runs on the block-scaled MFMA tiles, weights quantized with power-of-two
-    block scales too). Codes and scales bit-exact against the oracle's flagged
-    quantizer, the output within the GEMM tolerance of the oracle GEMM on them
-    and bit-identical to the flagged quantizer followed by the GEMM entry."""
+    block scales too). At the smallest M (UE8M0 alone: M <= 4; SiLU-and-mul:
+    M = 1 channelwise, M <= 2 blockwise) the call is one launch that applies
+    the flags inside the weight-streaming GEMM's quantization (per-token rows
+    across 4 KB chunks with a ragged tail included). Codes and scales bit-exact
+    against the oracle's flagged quantizer, the output within the GEMM
+    tolerance of the oracle GEMM on them and bit-identical to the flagged
+    quantizer followed by the GEMM entry."""
+    kid = ops.KIND_CHANNELWISE if kind == "cw" else ops.KIND_BLOCKWISE
+    fused_rows = (1 if kind == "cw" else 2) if silu else 4
+    assert ops.linear_launches(kid, m, n, k, silu_mul=silu, scale_ue8m0=ue8m0) == (1 if m <= fused_rows else 2)
     x = activations("flag-lin", m, 2 * k if silu else k)
     xf = x.float().numpy()
     y = oracle.silu_mul_bf16(xf) if silu else xf
