@@ -126,6 +126,11 @@ int run_gemm(const char* fn, int kind, const uint8_t* a, const uint8_t* b, const
   p.split_k = splits;
   p.k_tiles_per_split = per;
   if (splits > 1) {
+    // the kernels address one tile's partials (all splits) with 32-bit offsets
+    const VariantInfo vi = variant_info(cfg.variant);
+    if ((int64_t)splits * vi.bm * vi.bn * (int64_t)sizeof(float) > INT32_MAX)
+      return fail(FP8_ERR_UNSUPPORTED, "%s: split_k=%d keeps more than 2 GiB of partials per tile", fn,
+                  splits);
     // ws layout: kCounterBytes of arrival counters (zero between calls), then partials
     const size_t need = variant_workspace_bytes(cfg.variant, splits, M, N);
     if (!ws || ws_bytes < need)

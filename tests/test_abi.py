@@ -384,3 +384,14 @@ def test_split_requests_above_k_stages_are_lowered(lib):
         assert size(v, 4, 256) == size(v, 2, 256) > size(v, 1, 256)
         assert size(v, 4, 384) == size(v, 3, 384) > size(v, 2, 384)
         assert size(v, 4, 640, kind=_lib.KIND_BLOCKWISE) == size(v, 3, 640, kind=_lib.KIND_BLOCKWISE)
+
+
+def test_split_k_partials_stay_within_32_bit_offsets(lib):
+    # 9000 splits of a 256x256 tile keep 2.4 GB of partials per tile: refused
+    # before anything is launched (the workspace given is ample)
+    cfg = _lib.TileConfig(_lib.VARIANTS["t256x256panel"], 0, 0, 0, 9000, 0)
+    k = 128 * 9000
+    st = lib.fp8_scaled_mm_channelwise_ex(FAKE, FAKE, FAKE, FAKE, None, FAKE, 256, 256, k, k, k, 256, FAKE,
+                                          1 << 62, ctypes.byref(cfg), None)
+    assert st == _lib.FP8_ERR_UNSUPPORTED
+    assert "partials" in _err(lib)
