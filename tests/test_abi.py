@@ -8,6 +8,7 @@ import json
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -395,3 +396,23 @@ def test_split_k_partials_stay_within_32_bit_offsets(lib):
                                           1 << 62, ctypes.byref(cfg), None)
     assert st == _lib.FP8_ERR_UNSUPPORTED
     assert "partials" in _err(lib)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # no CPU fallback: without the built library every entry point raises
+    code = (
+        "import sys\n"
+        "from fp8_w8a8_quantized_token_amd import _lib, ops\n"
+        f"_lib.LIB_PATH = {str(tmp_path / 'absent.so')!r}\n"
+        "for call in (lambda: _lib.load(), lambda: ops.tile_config(0, 4096, 4096, 16),\n"
+        "             lambda: ops.linear_launches(0, 1, 4096, 4096)):\n"
+        "    try:\n"
+        "        call()\n"
+        "    except RuntimeError as e:\n"
+        "        assert 'no fallback' in str(e), e\n"
+        "    else:\n"
+        "        sys.exit('no error raised')\n"
+        "print('ok')\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stderr
