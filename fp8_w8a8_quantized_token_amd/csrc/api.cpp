@@ -146,21 +146,26 @@ int run_gemm(const char* fn, int kind, const uint8_t* a, const uint8_t* b, const
   return hip_status(launch_gemm(kind, cfg.variant, p, stream), fn);
 }
 
-// FP8W8A8_FUSED_LINEAR=0 turns the single-launch linear off (read per call).
-bool fused_linear_enabled() {
+// FP8W8A8_FUSED_LINEAR=0 turns the single-launch linear off; =all takes it at
+// every M <= kFusedRows whatever the quantizer flags (for measuring the
+// flag-dependent limits below). Read per call.
+int fused_linear_mode() {
   const char* v = std::getenv("FP8W8A8_FUSED_LINEAR");
-  return !(v && v[0] == '0' && v[1] == '\0');
+  if (v && v[0] == '0' && v[1] == '\0') return 0;
+  if (v && std::string(v) == "all") return 2;
+  return 1;
 }
 
 // With SiLU-and-mul every workgroup of the fused launch evaluates SiLU over
 // the whole activation (per token twice: the row maximum first), which pays
 // off only for the fewest rows: measured on the down projections (4096x12288
-// channelwise, 4096x1536 and 7168x2048 blockwise), one launch is 1.7 us
-// faster at M = 1 channelwise and 1.2-3.9 us at M <= 2 blockwise, but 4-15 us
-// slower at M = 2 and 4 channelwise and up to 2 us slower at M = 4 blockwise.
+// channelwise, 4096x1536 and 7168x2048 blockwise), one launch is 1.2 us
+// faster at M = 1 channelwise and 0.9-4.0 us at M <= 2 blockwise, but 5-17 us
+// slower at M = 2 and 4 channelwise and up to 3 us slower at M = 4 blockwise.
 bool linear_fuses(int kind, const fp8_tile_config& cfg, int64_t M, int32_t flags) {
-  if (cfg.variant != FP8_VARIANT_SKINNY || M > kFusedRows || !fused_linear_enabled()) return false;
-  if (flags & FP8_QUANT_FUSE_SILU_MUL) return M <= (kind == FP8_KIND_CHANNELWISE ? 1 : 2);
+  const int mode = fused_linear_mode();
+  if (cfg.variant != FP8_VARIANT_SKINNY || M > kFusedRows || mode == 0) return false;
+  if ((flags & FP8_QUANT_FUSE_SILU_MUL) && mode == 1) return M <= (kind == FP8_KIND_CHANNELWISE ? 1 : 2);
   return true;
 }
 

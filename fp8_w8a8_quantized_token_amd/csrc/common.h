@@ -131,21 +131,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 // silu(g) * u in fp32: e^-g as 2^(-g log2 e) on the hardware exp2 (within 1
 // ulp), then the reciprocal (1 ulp) and two products. Relative error at most
-// (|g| + 7) 2^-24 for g >= -16: rounding -g log2 e costs |g| 2^-24 once the
-// exponent is taken, the other steps 7 2^-24 together; for g > 16.6 the
-// e^-g term is below half an ulp of 1 and its error drops out.
+// (1.23 |g| + 7) 2^-24 for g >= -16: the exponent -g log2 e is off by its
+// rounding (2^-24 relative) plus that of the fp32 log2 e (0.22 2^-24), which
+// 2^x turns into 1.23 |g| 2^-24 of e^-g and at most as much of the result;
+// the other steps cost 7 2^-24 together. For g > 16.6 the e^-g term is below
+// half an ulp of 1 and its error drops out.
 __device__ __forceinline__ float silu_mul_f32(float g, float u) {
   const float t = __builtin_amdgcn_exp2f(g * -1.44269504088896340736f);
   return (g * __builtin_amdgcn_rcpf(1.0f + t)) * u;
 }
 
 // True where the fp32 value y = silu_mul_f32(g, u) may round to a different
-// bf16 than the exact product: y lies within 48 fp32 ulps of a bf16 rounding
-// midpoint (low 16 bits near 0x8000; the error bound above is at most 23 ulps
-// for g >= -16), or g < -16, outside that bound.
+// bf16 than the exact product: g < -16 (outside the error bound above), or y
+// lies within w fp32 ulps of a bf16 rounding midpoint (low 16 bits near
+// 0x8000). The relative bound above, (1.23 |g| + 7) 2^-24, is under
+// 1.23 |g| + 7 ulps of y (an ulp is at least 2^-24 of |y|); above g = 16.6 y
+// is within 2 ulps. So w = floor(1.25 min(|g|, 17)) + 8 covers it: 8 ulps
+// for |g| < 0.8, 28 at g = -16, where a fixed window would need 27 for every
+// value (fminf also maps a NaN gate, already sent to the fallback by the
+// first test, to 17).
 __device__ __forceinline__ bool silu_needs_f64(float g, float y) {
   const uint32_t low = __float_as_uint(y) & 0xFFFFu;
-  return !(g >= -16.0f) || (low - (0x8000u - 48u)) <= 96u;
+  const uint32_t w = (uint32_t)(1.25f * fminf(fabsf(g), 17.0f)) + 8u;
+  return !(g >= -16.0f) || (low - (0x8000u - w)) <= 2u * w;
 }
 
 // bf16 bits of silu(g) * u from fp64 (exp in fp64 within 1 ulp, IEEE

@@ -424,8 +424,9 @@ def measure_stream_ceiling(warmup, calls, filler):
 
 
 # Down projections fed straight from a gated MLP's [gate | up] output: the
-# decode linears with SiLU-and-mul, as one launch (quantization inside the
-# weight-streaming GEMM) and as the flagged quantizer followed by the GEMM.
+# decode linears with SiLU-and-mul through the linear call (one launch where
+# the library fuses; FP8W8A8_FUSED_LINEAR=all fuses at every M <= 4) and as the
+# flagged quantizer followed by the GEMM.
 SILU_LINEAR_SHAPES = [("channelwise", 4096, 12288), ("blockwise", 4096, 1536), ("blockwise", 7168, 2048)]
 
 
@@ -469,7 +470,10 @@ def measure_silu_linear(warmup, calls, filler):
             for g in gemms:
                 two.append(lambda g=g: (quant(), g()))
             nbytes = n * k + 4 * m * k
-            for name, fns, nl in (("single launch", one, 1), ("quantizer + GEMM", two, 2)):
+            kid = ops.KIND_CHANNELWISE if kind == "channelwise" else ops.KIND_BLOCKWISE
+            nl1 = ops.linear_launches(kid, m, n, k, silu_mul=True)
+            name1 = "linear call" + (" (single launch)" if nl1 == 1 else "")
+            for name, fns, nl in ((name1, one, nl1), ("quantizer + GEMM", two, 2)):
                 us = _batch_us(fns, warmup, calls, filler)
                 line = (f"| {kind} | {n}×{k} | {m} | {name} | {nl} | {sets} | {us:.2f} | "
                         f"{nbytes / us / 1e3:.0f} |")

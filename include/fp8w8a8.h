@@ -374,7 +374,8 @@ size_t fp8_scaled_mm_workspace_size(int32_t kind, int64_t M, int64_t N, int64_t 
  * multiplies (x is read from cache by each of them) and workgroup 0 also
  * stores q and a_scale. Otherwise the quantizer and the GEMM run as two
  * launches on `stream`. FP8W8A8_FUSED_LINEAR=0 in the environment turns the
- * single launch off.
+ * single launch off; =all also takes it with SiLU-and-mul at every M <= 4
+ * (see the _ex forms; for measurement).
  *   x        bf16 [M][ldx], ldx >= K (input)
  *   q        E4M3 [M][ldq], ldq >= K (output codes; the GEMM's input)
  *   a_scale  fp32 [M] (output per-token scales)

@@ -214,6 +214,15 @@ def test_linear_launch_counts_with_flags(lib):
         _lib.KIND_CHANNELWISE, 1, 4096, 4096, None)
 
 
+def test_fused_linear_all_mode(lib, monkeypatch):
+    n = lib.fp8_linear_launches_ex
+    silu = _lib.QUANT_FUSE_SILU_MUL
+    assert n(_lib.KIND_CHANNELWISE, 4, 4096, 12288, None, silu) == 2
+    monkeypatch.setenv("FP8W8A8_FUSED_LINEAR", "all")
+    assert [n(_lib.KIND_CHANNELWISE, m, 4096, 12288, None, silu) for m in (1, 2, 4, 5)] == [1, 1, 1, 2]
+    assert n(_lib.KIND_BLOCKWISE, 4, 7168, 2048, None, silu) == 1
+
+
 def test_fused_linear_kill_switch(lib, monkeypatch):
     n = lib.fp8_linear_launches
     monkeypatch.setenv("FP8W8A8_FUSED_LINEAR", "0")

@@ -224,3 +224,48 @@ def test_silu_quant_feeds_down_projection(m):
     tau2 = oracle.summation_bound_blockwise(aq2, wq, as2, ws)
     res2 = oracle.check_gemm(bf16_to_f64(out2), ref2, tau2)
     assert res2["ok"] and res2["cosine"] > 0.9999, res2
+
+
+def _near_midpoint_pairs(count, seed=7):
+    """bf16 (gate, up) pairs whose silu(gate) * up lies within 40 fp32 ulps of
+    a bf16 rounding midpoint (the values the fp32 SiLU evaluation must hand to
+    its exact fallback), gates over [-16, 20]."""
+    rng = np.random.default_rng(seed)
+    out_g, out_u = [], []
+    while sum(len(a) for a in out_g) < count:
+        g = torch.from_numpy(np.concatenate([rng.normal(0, 2, 1 << 20), rng.uniform(-16, 20, 1 << 18)])
+                             .astype(np.float32)).to(torch.bfloat16).float().numpy().astype(np.float64)
+        u = torch.from_numpy(rng.normal(0, 1, g.size).astype(np.float32)).to(torch.bfloat16).float() \
+            .numpy().astype(np.float64)
+        y = (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
+        low = y.view(np.uint32) & 0xFFFF
+        near = (np.abs(low.astype(np.int64) - 0x8000) <= 40) & (y != 0)
+        out_g.append(g[near])
+        out_u.append(u[near])
+    return np.concatenate(out_g)[:count], np.concatenate(out_u)[:count]
+
+
+def test_silu_near_bf16_midpoints():
+    """Each near-midpoint pair is the only nonzero of its 16-element group and
+    of its row (the other gates are 0, so their products are 0): the group and
+    row scales are then |bf16(silu(g) * u)| / 448 and show any one-ulp error of
+    the bf16 product."""
+    g, u = _near_midpoint_pairs(4096)
+    m, k = g.size, 16
+    x = np.zeros((m, 2 * k), dtype=np.float32)
+    pos = np.arange(m) % k
+    x[np.arange(m), pos] = g
+    x[np.arange(m), k + pos] = u
+    x[:, k:] += np.where(np.arange(k) == pos[:, None], 0.0, 1.0)  # up halves nonzero, gates zero
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    assert np.array_equal(xb.float().numpy(), x)
+    say("silu near midpoints", m)
+    q, s = ops.silu_mul_quant_per_token(gpu(xb))
+    qg, sg = ops.silu_mul_quant_per_token_group(gpu(xb), 16, row_alignment=1)
+    torch.cuda.synchronize()
+    want_q, want_s = oracle.silu_mul_quant_per_token(x)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    _assert_codes(q.cpu().numpy(), want_q)
+    want_qg, want_sg = oracle.silu_mul_quant_per_token_group(x, 16)
+    assert np.array_equal(sg.contiguous().cpu().numpy().view(np.uint32), want_sg.view(np.uint32))
+    _assert_codes(qg.cpu().numpy(), want_qg)
