@@ -159,9 +159,9 @@ int fused_linear_mode() {
 // With SiLU-and-mul every workgroup of the fused launch evaluates SiLU over
 // the whole activation (per token twice: the row maximum first), which pays
 // off only for the fewest rows: measured on the down projections (4096x12288
-// channelwise, 4096x1536 and 7168x2048 blockwise), one launch is 1.2 us
-// faster at M = 1 channelwise and 0.9-4.0 us at M <= 2 blockwise, but 5-17 us
-// slower at M = 2 and 4 channelwise and up to 3 us slower at M = 4 blockwise.
+// channelwise, 4096x1536 and 7168x2048 blockwise), one launch is 1.7 us
+// faster at M = 1 channelwise and 1.4-3.8 us at M <= 2 blockwise, but 4-15 us
+// slower at M = 2 and 4 channelwise and up to 2 us slower at M = 4 blockwise.
 bool linear_fuses(int kind, const fp8_tile_config& cfg, int64_t M, int32_t flags) {
   const int mode = fused_linear_mode();
   if (cfg.variant != FP8_VARIANT_SKINNY || M > kFusedRows || mode == 0) return false;

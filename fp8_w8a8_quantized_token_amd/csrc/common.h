@@ -142,18 +142,15 @@ __device__ __forceinline__ float silu_mul_f32(float g, float u) {
 }
 
 // True where the fp32 value y = silu_mul_f32(g, u) may round to a different
-// bf16 than the exact product: g < -16 (outside the error bound above), or y
-// lies within w fp32 ulps of a bf16 rounding midpoint (low 16 bits near
-// 0x8000). The relative bound above, (1.23 |g| + 7) 2^-24, is under
-// 1.23 |g| + 7 ulps of y (an ulp is at least 2^-24 of |y|); above g = 16.6 y
-// is within 2 ulps. So w = floor(1.25 min(|g|, 17)) + 8 covers it: 8 ulps
-// for |g| < 0.8, 28 at g = -16, where a fixed window would need 27 for every
-// value (fminf also maps a NaN gate, already sent to the fallback by the
-// first test, to 17).
+// bf16 than the exact product: y lies within 48 fp32 ulps of a bf16 rounding
+// midpoint (low 16 bits near 0x8000; the relative bound above is under
+// 1.23 |g| + 7 ulps of y, an ulp being at least 2^-24 of |y|: at most 27 ulps
+// for g >= -16), or g < -16, outside that bound. A window scaled with |g|
+// sends fewer values to the fp64 path but measured slower: its per-value
+// arithmetic costs more than the redo it saves.
 __device__ __forceinline__ bool silu_needs_f64(float g, float y) {
   const uint32_t low = __float_as_uint(y) & 0xFFFFu;
-  const uint32_t w = (uint32_t)(1.25f * fminf(fabsf(g), 17.0f)) + 8u;
-  return !(g >= -16.0f) || (low - (0x8000u - w)) <= 2u * w;
+  return !(g >= -16.0f) || (low - (0x8000u - 48u)) <= 96u;
 }
 
 // bf16 bits of silu(g) * u from fp64 (exp in fp64 within 1 ulp, IEEE
