@@ -331,3 +331,45 @@ def test_linear_with_quant_flags(kind, m, n, k, silu, ue8m0):
            f"linear {kind} flags M={m} N={n} K={k}")
     torch.cuda.synchronize()
     assert _same_bits(out, out2)
+
+
+FORCED_SILU_CASES = [("cw", 2, 4096, 12288), ("cw", 4, 392, 4112), ("bw", 4, 4096, 1536), ("bw", 3, 7168, 2048)]
+
+
+@pytest.mark.parametrize("kind,m,n,k", FORCED_SILU_CASES,
+                         ids=[f"{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in FORCED_SILU_CASES])
+def test_forced_single_launch_silu(kind, m, n, k, monkeypatch):
+    """FP8W8A8_FUSED_LINEAR=all takes the single launch with SiLU-and-mul at
+    every M <= 4 (the library's default keeps it to the fewest rows): the same
+    codes, scales and output bits as the flagged quantizer and the GEMM."""
+    monkeypatch.setenv("FP8W8A8_FUSED_LINEAR", "all")
+    kid = ops.KIND_CHANNELWISE if kind == "cw" else ops.KIND_BLOCKWISE
+    assert ops.linear_launches(kid, m, n, k, silu_mul=True) == 1
+    x = activations("forced-silu", m, 2 * k)
+    xf = x.float().numpy()
+    y = oracle.silu_mul_bf16(xf)
+    bias = synth.bias("forced-silu", n)
+    x_d, bias_d = gpu(x), gpu(bias)
+    say("forced single-launch silu", kind, m, n, k)
+    if kind == "cw":
+        b, sb = weight_channelwise("forced-silu", n, k)
+        out, q, s = ops.linear_channelwise(x_d, gpu(b), gpu(sb), bias_d, return_quant=True, silu_mul=True)
+        want_q, want_s = oracle.quant_per_token(y)
+        ref = oracle.scaled_mm_channelwise(want_q, b, want_s, sb, bias.float().numpy())
+        tau = oracle.summation_bound_channelwise(want_q, b, want_s, sb)
+        q2, s2 = ops.quant_per_token(x_d, silu_mul=True)
+        out2 = ops.scaled_mm_channelwise(q2, gpu(b), s2, gpu(sb), bias_d, config=ops.make_config("skinny"))
+    else:
+        b, sb = weight_blockwise("forced-silu", n, k)
+        out, q, s = ops.linear_blockwise(x_d, gpu(b), gpu(sb), bias_d, return_quant=True, silu_mul=True)
+        want_q, want_s = oracle.quant_per_token_group(y, 128)
+        ref = oracle.scaled_mm_blockwise(want_q, b, want_s, sb, bias.float().numpy())
+        tau = oracle.summation_bound_blockwise(want_q, b, want_s, sb)
+        q2, s2 = ops.quant_per_token_group(x_d, 128, row_alignment=4, silu_mul=True)
+        out2 = ops.scaled_mm_blockwise(q2, gpu(b), s2, gpu(sb), bias_d, m=m, config=ops.make_config("skinny"))
+        s = s[:m]
+    torch.cuda.synchronize()
+    assert np.array_equal(q[:m].cpu().numpy(), want_q)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    _check(out, ref, tau, f"forced silu {kind} M={m} N={n} K={k}")
+    assert _same_bits(out, out2)
