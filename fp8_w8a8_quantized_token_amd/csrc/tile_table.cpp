@@ -291,8 +291,11 @@ int default_config(int kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* o
   // at M = 4096-8192). Without that K the register-staged tiles run
   // (channelwise with K % 64 == 0: the 64-byte-stage DMA tiles at large M); a
   // large tile is taken only if it gives at least half the compute units a
-  // workgroup, the 64x64 tile being the fallback. Split-K rarely won in those
-  // measurements, so it is left to the tuned tables.
+  // workgroup, the 64x64 tile being the fallback. Split-K at 32 < M <= 128
+  // (64x64 tiles, K % 128 == 0): with at most 128 output tiles and at least 24
+  // 128-deep K stages, 2 splits, and 4 with at most 64 tiles and at least 48
+  // stages (measured on tabled and untabled shapes, 4096-8192 wide: 10-45%
+  // faster there; unsplit stays ahead from ~160 tiles or below ~24 stages).
   const bool cw = kind != FP8_KIND_BLOCKWISE;
   const bool k128 = K % 128 == 0, k64 = cw && K % 64 == 0;
   fp8_tile_config c{};
@@ -301,6 +304,8 @@ int default_config(int kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* o
     c.variant = FP8_VARIANT_SKINNY;
   } else if (k128 && M <= 256) {
     c.variant = cw ? FP8_VARIANT_T64x64DEEP : FP8_VARIANT_T64x64PANEL;
+    const int64_t tiles = variant_tiles(c.variant, M, N), stages = K / 128;
+    if (M <= 128 && tiles <= 128 && stages >= 24) c.split_k = tiles <= 64 && stages >= 48 ? 4 : 2;
   } else if (k128 && M <= 512) {
     c.variant = cw ? FP8_VARIANT_T128x64DEEP : FP8_VARIANT_T128x64PANEL;
   } else if (k128 && M <= 1024) {

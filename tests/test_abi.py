@@ -425,3 +425,21 @@ def test_missing_library_fails_loudly(tmp_path):
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
                          cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert out.returncode == 0 and out.stdout.strip() == "ok", out.stderr
+
+
+def test_default_split_k_at_small_m(lib):
+    # split-K in the default heuristic: 64x64 tiles at 32 < M <= 128 split when
+    # few output tiles share a long K
+    def d(kind, n, k, m):
+        c = _default(lib, kind, n, k, m)
+        return c["variant"], c["split_k"]
+    cw, bw = _lib.KIND_CHANNELWISE, _lib.KIND_BLOCKWISE
+    dv, pv = "t64x64deep", "t64x64panel"
+    assert d(cw, 2048, 8192, 64) == (dv, 4)      # 32 tiles, 64 stages
+    assert d(cw, 5120, 5120, 64) == (dv, 2)      # 80 tiles, 40 stages
+    assert d(cw, 4096, 4096, 128) == (dv, 2)     # 128 tiles
+    assert d(cw, 5120, 5120, 128) == (dv, 1)     # 160 tiles
+    assert d(cw, 4096, 4096, 256) == (dv, 1)     # beyond M = 128
+    assert d(bw, 1536, 7168, 96) == (pv, 4)
+    assert d(bw, 4096, 2048, 64) == (pv, 1)      # 16 stages
+    assert d(cw, 4096, 4096, 32)[0] == "skinny"

@@ -410,3 +410,20 @@ def test_panel_split_k_deterministic_and_fresh_partials():
         _channelwise_case("qwen3_8b", 96, 4096, 4096, 0.0, True, config=cfg, sample=False)
         _, o2 = _channelwise_case("o_proj", 96, 4096, 4096, 0.01, False, config=cfg, sample=False)
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+DEFAULT_SPLIT_CASES = [("cw", 64, 2048, 8192), ("cw", 100, 4096, 5120), ("bw", 96, 1536, 7168), ("bw", 48, 5120, 5120)]
+
+
+@pytest.mark.parametrize("kind,m,n,k", DEFAULT_SPLIT_CASES,
+                         ids=[f"{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in DEFAULT_SPLIT_CASES])
+def test_default_heuristic_split_k(kind, m, n, k):
+    """Shapes with no tile table, where the default heuristic splits K (2 or 4
+    splits of the 64x64 tiles at 32 < M <= 128)."""
+    kid = ops.KIND_CHANNELWISE if kind == "cw" else ops.KIND_BLOCKWISE
+    cfg, hit = ops.tile_config(kid, n, k, m)
+    assert not hit and cfg["split_k"] > 1, cfg
+    if kind == "cw":
+        _channelwise_case("default-split", m, n, k, 0.0, True)
+    else:
+        _blockwise_case("default-split", m, n, k, with_bias=True)
