@@ -302,6 +302,17 @@ int default_config(int kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* o
   c.split_k = 1;
   if (M <= 32) {
     c.variant = FP8_VARIANT_SKINNY;
+    // From M = 8, on wide weights whose N/16 weight-streaming workgroups run
+    // in uneven rounds over the 256 compute units (or N >= 12288), the 32x32
+    // deep-ring tile is ahead: 14336x4096 M = 16 15.8 against 20.2 us, 5120^2
+    // 12.1 against 18.1, blockwise 12288x7168 20.6 against 31.6; 2 splits
+    // over 40 or more K stages (blockwise: 24). M <= 4 keeps the weight-
+    // streaming kernel, which the single-launch linear needs.
+    const int64_t groups = (N + 15) / 16;
+    if (M >= 8 && k128 && ((groups > 256 && groups % 256 != 0) || N >= 12288)) {
+      c.variant = FP8_VARIANT_T32x32DEEP;
+      c.split_k = K / 128 >= (cw ? 40 : 24) ? 2 : 1;
+    }
   } else if (k128 && M <= 256) {
     c.variant = cw ? FP8_VARIANT_T64x64DEEP : FP8_VARIANT_T64x64PANEL;
     const int64_t tiles = variant_tiles(c.variant, M, N), stages = K / 128;

@@ -443,3 +443,18 @@ def test_default_split_k_at_small_m(lib):
     assert d(bw, 1536, 7168, 96) == (pv, 4)
     assert d(bw, 4096, 2048, 64) == (pv, 1)      # 16 stages
     assert d(cw, 4096, 4096, 32)[0] == "skinny"
+
+
+def test_default_narrow_tile_on_uneven_skinny_rounds(lib):
+    cw, bw = _lib.KIND_CHANNELWISE, _lib.KIND_BLOCKWISE
+
+    def d(kind, n, k, m):
+        c = _default(lib, kind, n, k, m)
+        return c["variant"], c["split_k"]
+    assert d(cw, 14336, 4096, 16) == ("t32x32deep", 1)   # 896 groups: 3.5 rounds
+    assert d(cw, 5120, 5120, 8) == ("t32x32deep", 2)     # 320 groups, 40 stages
+    assert d(bw, 12288, 7168, 32) == ("t32x32deep", 2)   # N >= 12288
+    assert d(cw, 4096, 4096, 16)[0] == "skinny"          # whole rounds
+    assert d(cw, 8192, 8192, 16)[0] == "skinny"
+    assert d(bw, 3072, 4096, 16)[0] == "skinny"          # one partial round
+    assert d(cw, 14336, 4096, 4)[0] == "skinny"          # M <= 4: single-launch linear

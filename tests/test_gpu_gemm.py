@@ -427,3 +427,21 @@ def test_default_heuristic_split_k(kind, m, n, k):
         _channelwise_case("default-split", m, n, k, 0.0, True)
     else:
         _blockwise_case("default-split", m, n, k, with_bias=True)
+
+
+NARROW_DEFAULT_CASES = [("cw", 16, 14336, 4096), ("cw", 8, 5120, 5120), ("bw", 32, 12288, 7168), ("bw", 12, 5120, 5120)]
+
+
+@pytest.mark.parametrize("kind,m,n,k", NARROW_DEFAULT_CASES,
+                         ids=[f"{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in NARROW_DEFAULT_CASES])
+def test_default_narrow_tile_on_wide_weights(kind, m, n, k):
+    """Untabled wide weights at M = 8..32: the default heuristic takes the
+    32x32 deep-ring tile (split over long K) instead of the weight-streaming
+    kernel."""
+    kid = ops.KIND_CHANNELWISE if kind == "cw" else ops.KIND_BLOCKWISE
+    cfg, hit = ops.tile_config(kid, n, k, m)
+    assert not hit and cfg["variant"] == "t32x32deep", cfg
+    if kind == "cw":
+        _channelwise_case("narrow-default", m, n, k, 0.0, True)
+    else:
+        _blockwise_case("narrow-default", m, n, k, with_bias=True)
