@@ -11,6 +11,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8w8a8.so")
+# the device compiler's per-kernel register / scratch / LDS report of the
+# last build (one "remark" block per kernel)
+RESOURCE_REPORT = os.path.join(PKG, "_build", "resource_usage.txt")
 SOURCES = ["quant.hip", "gemm.hip", "tile_table.cpp", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -28,6 +31,8 @@ FLAGS = [
     "-Wno-unused-function",
     # M0 is clobbered on purpose by the LDS-DMA loads (see gemm.hip)
     "-Wno-inline-asm",
+    # per-kernel resource usage (VGPRs, scratch, LDS), kept in RESOURCE_REPORT
+    "-Rpass-analysis=kernel-resource-usage",
 ]
 
 
@@ -41,10 +46,17 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    noisy = [ln for ln in (res.stdout + res.stderr).splitlines()
-             if ln.strip() and "packed-fp32-ops" not in ln and "is not a recognized feature" not in ln]
+    lines = (res.stdout + res.stderr).splitlines()
+    remarks = [ln for ln in lines if "[-Rpass-analysis=kernel-resource-usage]" in ln]
+    noisy = [ln for ln in lines
+             if ln.strip() and "packed-fp32-ops" not in ln and "is not a recognized feature" not in ln
+             and "kernel-resource-usage" not in ln and not ln.lstrip().startswith(("|", "^"))
+             and not ln.lstrip()[:1].isdigit()]
     if verbose and noisy:
         print("\n".join(noisy))
+    os.makedirs(os.path.dirname(RESOURCE_REPORT), exist_ok=True)
+    with open(RESOURCE_REPORT, "w") as f:
+        f.write("\n".join(remarks) + "\n")
     os.replace(tmp, LIB)
     return LIB
 

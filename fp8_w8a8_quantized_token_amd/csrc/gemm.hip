@@ -853,7 +853,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   static_assert(((NP - 1) / 2) * PPB_ALL + ((NP - 2) / 2) * PPA_ALL < 64 &&
                 ((NP - 1) / 2) * PPA_ALL + ((NP - 2) / 2) * PPB_ALL < 64, "vmcnt range");
   static_assert(BM * BN * 2 <= G::LDS, "output tile fits the ring");
-  static_assert(!BW || (SA_LANES >= 1 && SA_LANES <= 64 && BM % (4 * NW) == 0 && G::NBLK <= 4 &&
+  static_assert(!BW || (SA_LANES >= 1 && SA_LANES * 4 <= 64 && BM % (4 * NW) == 0 && G::NBLK <= 4 &&
                         WTN <= 128 && 128 % WTN == 0),
                 "blockwise scale layout");
 
@@ -917,18 +917,29 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
     }
   };
   // blockwise scales of block kt into the scale area of the slot at sbase
+  // activation-scale columns that start on 16 bytes (ld a multiple of 4)
+  // travel in 16-byte pieces, others one scale per lane; either way one DMA
+  // instruction per wave with the same LDS image
+  const bool sa_vec = (p.sa_ld & 3) == 0 && (reinterpret_cast<uintptr_t>(p.sa) & 15) == 0;
   auto issue_scales = [&](int64_t kt, uint32_t sbase) {
     // activation scales of block kt, rows m0 .. m0+BM-1 (column-major, ld
-    // sa_ld; 16-byte pieces clamped into the column): wave w copies rows
-    // [w * BM / NW, (w + 1) * BM / NW) with SA_LANES lanes
+    // sa_ld; pieces clamped into the column): wave w copies rows
+    // [w * BM / NW, (w + 1) * BM / NW), SA_LANES lanes of 4 rows or BM / NW
+    // lanes of one row
     {
-      int64_t r = m0 + (int64_t)(wave * SA_LANES + (lane < SA_LANES ? lane : 0)) * 4;
-      if (r > p.sa_ld - 4) r = p.sa_ld - 4;
+      const uint8_t* col = reinterpret_cast<const uint8_t*>(p.sa + kt * p.sa_ld);
+      const uint32_t dst = sbase + SA_OFF + wave * SA_LANES * 16;
       // lane 0 is always active, so the instruction always issues and
       // counts once in this wave's vmcnt
-      if (lane < SA_LANES)
-        lds_dma16_s(reinterpret_cast<const uint8_t*>(p.sa + kt * p.sa_ld), (uint32_t)(r * 4),
-                    sbase + SA_OFF + wave * SA_LANES * 16);
+      if (sa_vec) {
+        int64_t r = m0 + (int64_t)(wave * SA_LANES + (lane < SA_LANES ? lane : 0)) * 4;
+        if (r > p.sa_ld - 4) r = p.sa_ld - 4;
+        if (lane < SA_LANES) lds_dma16_s(col, (uint32_t)(r * 4), dst);
+      } else {
+        int64_t r = m0 + (int64_t)wave * (SA_LANES * 4) + (lane < SA_LANES * 4 ? lane : 0);
+        if (r > p.sa_ld - 1) r = p.sa_ld - 1;
+        if (lane < SA_LANES * 4) lds_dma4_s(col, (uint32_t)(r * 4), dst);
+      }
     }
     // weight block scales b_scale[n0 / 128 + l][kt], lanes l < NBLK, one
     // 16-byte copy per wave (lane 0 always active, as above); a block past
@@ -1621,19 +1632,27 @@ bool dma_eligible(const GemmArgs& p) {
          (uint64_t)(p.N - 1) * (uint64_t)p.ldb <= lim;
 }
 
-// The panel tiles take whole 128-byte K stages and 32-bit DMA row offsets;
-// blockwise also 16-byte aligned activation-scale columns (ld % 4 == 0).
+// The panel tiles take whole 128-byte K stages and 32-bit DMA row offsets
+// (blockwise: also within each activation-scale column).
 template <int KIND>
 bool panel_eligible(const GemmArgs& p) {
   const uint64_t lim = 0xFFFFFFFFull - 128;
   if (p.K % 128 != 0 || (uint64_t)(p.M - 1) * (uint64_t)p.lda > lim ||
       (uint64_t)(p.N - 1) * (uint64_t)p.ldb > lim)
     return false;
-  if (KIND == kBlockwise)
-    return p.sa_ld % 4 == 0 && (reinterpret_cast<uintptr_t>(p.sa) & 15) == 0 &&
-           (uint64_t)p.sa_ld * 4 <= lim;
+  if (KIND == kBlockwise) return (uint64_t)p.sa_ld * 4 <= lim;
   return true;
 }
+
+// The 256x256 tile where nothing else is asked for by name: channelwise the
+// 8-wave register-staged kernel; blockwise the 16x16-MFMA panel tile, or,
+// past the panel tiles' 32-bit DMA offsets, the 8-wave 128x128
+// register-staged kernel (the register-staged 256x256 blockwise kernels do
+// not fit their registers). Its split-K partials of 128x128 tiles fill the
+// workspace planned for 256x256 ones exactly or less.
+template <int KIND>
+hipError_t launch_256(const GemmArgs& p, hipStream_t stream);
+
 
 template <int KIND>
 hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
@@ -1650,15 +1669,17 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
     case 1: return launch_tile<64, 64, 2, 2, 512, KIND>(p, stream);
     case 2: return launch_tile<128, 128, 2, 2, 128, KIND>(p, stream);
     case 3: return launch_tile<256, 128, 2, 2, 128, KIND>(p, stream);
-    case 4: return launch_tile<256, 256, 2, 2, 128, KIND>(p, stream);
-    case 5: return launch_tile<256, 256, 2, 4, 128, KIND>(p, stream);
+    // the 4-wave 256x256 tile spilled its accumulators: both names take the
+    // 8-wave one
+    case 4:
+    case 5: return launch_256<KIND>(p, stream);
     case 6: return launch_tile<256, 128, 4, 2, 128, KIND>(p, stream);
     case 7: return launch_tile<128, 128, 2, 4, 128, KIND>(p, stream);
     case 8: return launch_tile<128, 64, 2, 2, 256, KIND>(p, stream);
     case 9: return launch_tile<64, 128, 2, 2, 256, KIND>(p, stream);
     case 10: return launch_tile<128, 128, 2, 2, 256, KIND>(p, stream);
     case 11:
-      if (!dma_eligible<KIND>(p)) return launch_tile<256, 256, 2, 4, 128, KIND>(p, stream);
+      if (!dma_eligible<KIND>(p)) return launch_256<KIND>(p, stream);
       return launch_dma<256, 256, 2, 4, 4>(p, stream);
     case 12:
       if (!dma_eligible<KIND>(p)) return launch_tile<256, 128, 4, 2, 128, KIND>(p, stream);
@@ -1669,7 +1690,7 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
     // panel variants: the fallbacks keep the tile shape and the 128-deep
     // stages the split plan counts in
     case 14:
-      if (KIND != kChannelwise || !panel_eligible<KIND>(p)) return launch_tile<256, 256, 2, 4, 128, KIND>(p, stream);
+      if (KIND != kChannelwise || !panel_eligible<KIND>(p)) return launch_256<KIND>(p, stream);
       return launch_panel<256, 256, 2, 4, kChannelwise, 5>(p, stream);
     case 15:
       if (!panel_eligible<KIND>(p)) return launch_tile<256, 128, 4, 2, 128, KIND>(p, stream);
@@ -1705,10 +1726,20 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
     // blockwise 256x256 on 16x16x128 MFMAs (four-slot ring); channelwise
     // requests run the 256x256 panel tile
     case 25:
-      if (!panel_eligible<KIND>(p)) return launch_tile<256, 256, 2, 4, 128, KIND>(p, stream);
-      if constexpr (KIND == kBlockwise) return launch_panel<256, 256, 2, 4, kBlockwise, 4, true>(p, stream);
-      else return launch_panel<256, 256, 2, 4, kChannelwise, 5>(p, stream);
+      if (KIND == kBlockwise || !panel_eligible<KIND>(p)) return launch_256<KIND>(p, stream);
+      return launch_panel<256, 256, 2, 4, kChannelwise, 5>(p, stream);
     default: return hipErrorInvalidValue;
+  }
+}
+
+template <int KIND>
+hipError_t launch_256(const GemmArgs& p, hipStream_t stream) {
+  if constexpr (KIND == kChannelwise) {
+    return launch_tile<256, 256, 2, 4, 128, KIND>(p, stream);
+  } else {
+    if (panel_eligible<KIND>(p)) return launch_panel<256, 256, 2, 4, kBlockwise, 4, true>(p, stream);
+    if (p.split_k > 1 && ((p.M + 127) / 128) * ((p.N + 127) / 128) > kMaxSplitTiles) return hipErrorInvalidValue;
+    return launch_tile<128, 128, 2, 4, 128, KIND>(p, stream);
   }
 }
 }  // namespace
@@ -1719,7 +1750,7 @@ VariantInfo variant_info(int variant) {
     case 1: return {64, 64, 512, 4, true};
     case 2: return {128, 128, 128, 4, true};
     case 3: return {256, 128, 128, 4, true};
-    case 4: return {256, 256, 128, 4, true};
+    case 4: return {256, 256, 128, 8, true};
     case 5: return {256, 256, 128, 8, true};
     case 6: return {256, 128, 128, 8, true};
     case 7: return {128, 128, 128, 8, true};

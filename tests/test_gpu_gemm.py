@@ -19,8 +19,8 @@ from gpu_common import (act_group, act_per_token, bf16_to_f64, device, gpu, samp
 pytestmark = pytest.mark.gpu
 
 
-def _check(out_rows, ref, tau, label):
-    res = oracle.check_gemm(out_rows, ref, tau)
+def _check(out_rows, ref, tau, label, k):
+    res = oracle.check_gemm(out_rows, ref, tau, k=k)
     say(label, {k: (round(v, 8) if isinstance(v, float) else v) for k, v in res.items()})
     assert res["ok"], (label, res)
     assert res["cosine"] > 0.9999
@@ -40,7 +40,7 @@ def _channelwise_case(wl, m, n, k, outliers, with_bias, config=None, sample=True
     ref = oracle.scaled_mm_channelwise(a[rows], b, sa[rows], sb, bias64)
     tau = oracle.summation_bound_channelwise(a[rows], b, sa[rows], sb)
     got = bf16_to_f64(out)[rows]
-    return _check(got, ref, tau, f"cw {wl} M={m} N={n} K={k}"), out
+    return _check(got, ref, tau, f"cw {wl} M={m} N={n} K={k}", k), out
 
 
 CW_CASES = (
@@ -82,7 +82,7 @@ def _blockwise_case(wl, m, n, k, config=None, with_bias=False, poison=False, row
     tau = oracle.summation_bound_blockwise(a[rows], b, sa[rows], sb)
     got = bf16_to_f64(out)[rows]
     assert out.shape == (m, n)
-    return _check(got, ref, tau, f"bw {wl} M={m} N={n} K={k}"), out
+    return _check(got, ref, tau, f"bw {wl} M={m} N={n} K={k}", k), out
 
 
 BW_CASES = ([("block_7168", m, 7168, 7168) for m in (1, 2, 3, 5, 7, 13, 31, 64, 256)]
@@ -214,7 +214,7 @@ def test_linear_wrappers_match_oracle():
     aq, as_ = oracle.quant_per_token(x.float().numpy())
     ref = oracle.scaled_mm_channelwise(aq, wq, as_, ws, bias.float().numpy())
     tau = oracle.summation_bound_channelwise(aq, wq, as_, ws)
-    _check(bf16_to_f64(y), ref, tau, "linear_channelwise")
+    _check(bf16_to_f64(y), ref, tau, "linear_channelwise", aq.shape[1])
     bq, bs = oracle.quant_weight_blockwise(w)
     say("linear_blockwise")
     y = ops.linear_blockwise(gpu(x), gpu(bq), gpu(bs), gpu(bias))
@@ -223,7 +223,7 @@ def test_linear_wrappers_match_oracle():
     ref = oracle.scaled_mm_blockwise(gq, bq, gs, bs, bias.float().numpy())
     tau = oracle.summation_bound_blockwise(gq, bq, gs, bs)
     assert y.shape == (37, 384)
-    _check(bf16_to_f64(y), ref, tau, "linear_blockwise")
+    _check(bf16_to_f64(y), ref, tau, "linear_blockwise", gq.shape[1])
 
 
 def test_split_k_back_to_back_calls_see_fresh_partials():
@@ -302,8 +302,9 @@ def test_blockwise_256x256_mfma16(split_k, m, n, k, bias):
 
 
 def test_blockwise_256x256_mfma16_poison_and_fallbacks():
-    """NaN pad rows stay out; an unaligned scale column takes the register
-    tile of the same shape; a channelwise request runs the 256x256 panel tile."""
+    """NaN pad rows stay out; an unaligned scale column (stride not a multiple
+    of 4) runs the same tile with its scales copied one per lane; a
+    channelwise request runs the 256x256 panel tile."""
     _blockwise_case("bw16-poison", 301, 512, 1024, config=ops.make_config("t256x256bw16", 2), poison=True)
     _blockwise_case("bw16-ld", 301, 384, 1024, config=ops.make_config("t256x256bw16", 2), row_align=1)
     _channelwise_case("bw16-cw", 300, 392, 1024, 0.0, True, config=ops.make_config("t256x256bw16", 2),
@@ -316,10 +317,27 @@ def test_blockwise_panel_poisoned_padding():
                     poison=True)
 
 
-def test_blockwise_panel_falls_back_on_unaligned_scale_column():
-    """An activation-scale column stride that is not a multiple of 4 takes the
-    register-staged kernel of the same tile."""
-    _blockwise_case("bw-panel-ld", 301, 384, 1024, config=ops.make_config("t256x128panel", 2), row_align=1)
+UNALIGNED_SCALE_CASES = [(v, sk, m, ra) for v, sk, m, ra in (
+    ("t256x128panel", 2, 301, 1), ("t256x256bw16", 1, 517, 1), ("t256x256bw16", 2, 301, 2),
+    ("t128x128panel", 1, 131, 3), ("t128x64panel8", 3, 197, 1), ("t64x64panel", 2, 77, 2),
+    ("t64x64deep", 1, 61, 1), ("t32x32deep", 2, 45, 3), ("t64x32deep", 1, 33, 1),
+    ("t128x128panel8", 1, 129, 2), ("t128x64deep", 2, 150, 1))]
+
+
+@pytest.mark.parametrize("variant,split_k,m,row_align", UNALIGNED_SCALE_CASES,
+                         ids=[f"{c[0]}-sk{c[1]}-M{c[2]}-ra{c[3]}" for c in UNALIGNED_SCALE_CASES])
+def test_blockwise_panel_unaligned_scale_column(variant, split_k, m, row_align):
+    """Activation-scale column strides that are not a multiple of 4 (row
+    alignment 1, 2 or 3 on a ragged M) on every blockwise panel tile: the
+    per-stage scales travel one per lane instead of in 16-byte pieces."""
+    _blockwise_case("bw-panel-ld", m, 384, 1024, config=ops.make_config(variant, split_k), row_align=row_align,
+                    poison=True)
+
+
+def test_blockwise_default_unaligned_scale_column_large_m():
+    """M = 4097 with row alignment 1 at the default tile (the 16x16-MFMA
+    256x256 tile): a column stride of 4097 scales."""
+    _blockwise_case("bw-ld-4097", 4097, 4096, 4096, row_align=1)
 
 
 CW_PANEL128_CASES = [(1, 300, 392, 1024), (2, 300, 392, 1024), (1, 2048, 4096, 4096)]

@@ -231,3 +231,94 @@ def test_check_gemm_accepts_and_rejects():
     nan = ref.copy()
     nan[0, 0] = np.nan
     assert not oracle.check_gemm(nan, ref, tau)["ok"]
+
+
+def test_blockwise_summation_bound_closed_form():
+    # All codes 0x38 (1.0), K = 256 (two K blocks), N = 256 (two N blocks):
+    # every product is 1, so sum_k |dec(A) dec(B)| over block kb is 128 and
+    # tau[m, n] = K 2^-23 sum_kb 128 sa[m, kb] sb[n // 128, kb] exactly.
+    M, N, K = 2, 256, 256
+    a = np.full((M, K), 0x38, np.uint8)
+    b = np.full((N, K), 0x38, np.uint8)
+    sa = np.array([[1.0, 2.0], [0.5, 4.0]], np.float32)
+    sb = np.array([[1.0, 4.0], [8.0, 16.0]], np.float32)
+    tau = oracle.summation_bound_blockwise(a, b, sa, sb)
+    per_block = np.array([[128 * (1 * 1 + 2 * 4), 128 * (1 * 8 + 2 * 16)],
+                          [128 * (0.5 * 1 + 4 * 4), 128 * (0.5 * 8 + 4 * 16)]], np.float64)
+    want = K * 2.0 ** -23 * np.repeat(per_block, 128, axis=1)
+    assert np.array_equal(tau, want)
+
+
+def test_blockwise_summation_bound_uniform_scales_equals_channelwise():
+    # with one scale per row and one per 128-row weight block, the block-scaled
+    # bound is the channelwise bound with the block scale spread over its rows
+    M, N, K = 5, 384, 512
+    a = synth.random_codes("pin-tb-a", (M, K)).numpy()
+    b = synth.random_codes("pin-tb-b", (N, K)).numpy()
+    sa_row = synth.positive_scales("pin-tb-sa", (M,)).numpy()
+    sb_blk = synth.positive_scales("pin-tb-sb", (N // 128,)).numpy()
+    tau_b = oracle.summation_bound_blockwise(a, b, np.repeat(sa_row[:, None], K // 128, axis=1),
+                                             np.repeat(sb_blk[:, None], K // 128, axis=1))
+    tau_c = oracle.summation_bound_channelwise(a, b, sa_row, np.repeat(sb_blk, 128))
+    np.testing.assert_allclose(tau_b, tau_c, rtol=1e-12, atol=0)
+    assert np.all(tau_b > 0)
+
+
+def test_blockwise_summation_bound_covers_promoted_fp32_accumulation():
+    # The blockwise kernels' arithmetic done in fp32 on the CPU: each 128-deep
+    # block summed sequentially in fp32, scaled by fp32(sa * sb), added to an
+    # fp32 accumulator. Scales differ per row, per K block and per N block.
+    M, N, K = 3, 256, 1024
+    a = synth.random_codes("pin-tp-a", (M, K)).numpy()
+    b = synth.random_codes("pin-tp-b", (N, K)).numpy()
+    sa = synth.positive_scales("pin-tp-sa", (M, K // 128)).numpy()
+    sb = synth.positive_scales("pin-tp-sb", (N // 128, K // 128)).numpy()
+    ref = oracle.scaled_mm_blockwise(a, b, sa, sb)
+    tau = oracle.summation_bound_blockwise(a, b, sa, sb)
+    prod = (_torch_decode(a)[:, None, :] * _torch_decode(b)[None, :, :]).astype(np.float32)
+    acc = np.zeros((M, N), np.float32)
+    nb = np.arange(N) // 128
+    for kb in range(K // 128):
+        part = np.zeros((M, N), np.float32)
+        for k in range(kb * 128, (kb + 1) * 128):
+            part = (part + prod[:, :, k]).astype(np.float32)
+        sc = (sa[:, kb][:, None] * sb[nb, kb][None, :]).astype(np.float32)
+        acc = (acc + (part * sc).astype(np.float32)).astype(np.float32)
+    err = np.abs(acc.astype(np.float64) - ref)
+    assert np.all(err <= tau)
+    # the bound is a bound, not noise: it is within a few hundred times the
+    # error actually made (K 2^-23 against ~sqrt(K) 2^-24 for random signs)
+    assert np.max(err) > 0 and np.max(err / tau) > 1e-3
+
+
+def test_check_gemm_probabilistic_floor_and_pure_relative_cap():
+    # an fp32 sequential (round-to-nearest) accumulation passes the tighter
+    # probabilistic floor and the pure-relative cap
+    M, N, K = 4, 64, 4096
+    a = synth.random_codes("pin-pf-a", (M, K)).numpy()
+    b = synth.random_codes("pin-pf-b", (N, K)).numpy()
+    sa = np.ones(M, np.float32)
+    sb = np.ones(N, np.float32)
+    ref = oracle.scaled_mm_channelwise(a, b, sa, sb)
+    tau = oracle.summation_bound_channelwise(a, b, sa, sb)
+    prod = (_torch_decode(a)[:, None, :] * _torch_decode(b)[None, :, :]).astype(np.float32)
+    acc = np.zeros((M, N), np.float32)
+    for k in range(K):
+        acc = (acc + prod[:, :, k]).astype(np.float32)
+    res = oracle.check_gemm(acc, ref, tau, k=K)
+    assert res["ok"] and res["n_prob_floor_fail"] == 0 and res["prob_floor_used"] < 1.0, res
+    floor = tau * 8.0 / (2.0 * np.sqrt(K))
+    # one element off by twice the floor beyond 2^-6 |ref|: inside the
+    # worst-case bound (floor << tau), outside the probabilistic one
+    bad = ref.copy()
+    bad[1, 3] += 2.0 ** -6 * abs(ref[1, 3]) + 2.0 * floor[1, 3]
+    assert oracle.check_gemm(bad, ref, tau)["ok"]
+    res = oracle.check_gemm(bad, ref, tau, k=K)
+    assert not res["ok"] and res["n_prob_floor_fail"] == 1
+    # 2% of the elements off by 1.5 * 2^-6 relative but inside the floor:
+    # each passes the per-element test, the pure-relative cap fails
+    idx = np.unravel_index(np.arange(0, M * N, 50), (M, N))
+    off = ref.copy()
+    off[idx] += np.minimum(1.5 * 2.0 ** -6 * np.abs(ref[idx]), 2.0 ** -6 * np.abs(ref[idx]) + 0.5 * floor[idx])
+    res = oracle.check_gemm(off, ref, tau, k=K)
+    assert res["n_prob_floor_fail"] == 0 and res["frac_pure_rel_fail"] > 0.01 and not res["ok"], res

@@ -91,6 +91,29 @@ def _mm_blockwise_kblock_scale_index(a, b, sa, sb, bias=None, block_n=128, block
     return out
 
 
+def _bound_blockwise_no_scales(a, b, sa, sb, block_n=128, block_k=128):
+    # mistake: the block scales are left out of the magnitude sum
+    A = np.abs(e4m3.decode(a))
+    B = np.abs(e4m3.decode(b))
+    return A.shape[1] * 2.0 ** -23 * (A @ B.T)
+
+
+def _bound_blockwise_n_over_64(a, b, sa, sb, block_n=128, block_k=128):
+    # mistake: weight block index n // 64 (clamped into the scale table)
+    A = np.abs(e4m3.decode(a))
+    B = np.abs(e4m3.decode(b))
+    sa = np.abs(np.asarray(sa, np.float64))
+    sb = np.abs(np.asarray(sb, np.float64))
+    m, k = A.shape
+    n = B.shape[0]
+    nb = np.minimum(np.arange(n) // 64, sb.shape[0] - 1)
+    mag = np.zeros((m, n))
+    for kb in range(-(-k // block_k)):
+        ks = slice(kb * block_k, min(k, (kb + 1) * block_k))
+        mag += (A[:, ks] @ B[:, ks].T) * sa[:, kb][:, None] * sb[nb, kb][None, :]
+    return k * 2.0 ** -23 * mag
+
+
 def _padded_rows_floor(m, ra):
     return (m // ra) * ra
 
@@ -186,6 +209,14 @@ MUTATIONS = [
      pins_gemm.test_worked_example),
     ("blockwise uses one N-block scale", [(oracle, "scaled_mm_blockwise", _mm_blockwise_kblock_scale_index)],
      lambda: pins_gemm.test_blockwise_exact_rational(3, 5, 256, 2, 128)),
+    ("blockwise bound drops the block scales", [(oracle, "summation_bound_blockwise",
+                                                 _bound_blockwise_no_scales)],
+     pins_gemm.test_blockwise_summation_bound_closed_form),
+    ("blockwise bound drops the block scales (fp32 run)", [(oracle, "summation_bound_blockwise",
+                                                            _bound_blockwise_no_scales)],
+     pins_gemm.test_blockwise_summation_bound_covers_promoted_fp32_accumulation),
+    ("blockwise bound indexes n // 64", [(oracle, "summation_bound_blockwise", _bound_blockwise_n_over_64)],
+     pins_gemm.test_blockwise_summation_bound_uniform_scales_equals_channelwise),
     ("padded rows rounds down", [(oracle, "padded_rows", _padded_rows_floor)],
      lambda: pins_quant.test_padded_rows(5, 4, 8)),
     ("col-major scales use ld M", [(oracle, "scales_col_major", _scales_col_major_wrong_ld)],
