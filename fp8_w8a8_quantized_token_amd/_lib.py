@@ -19,6 +19,8 @@ FP8_ERR_INVALID = -1
 FP8_ERR_UNSUPPORTED = -2
 FP8_ERR_WORKSPACE = -3
 FP8_ERR_HIP = -4
+# bytes of the library's static split-K scratch per device (fp8_scaled_mm_noalloc)
+NOALLOC_SCRATCH_BYTES = (256 << 10) + (64 << 20)
 
 KIND_CHANNELWISE = 0
 KIND_BLOCKWISE = 1
@@ -68,6 +70,8 @@ SIGNATURES = {
     "fp8_scaled_mm_channelwise_ex": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64,
                                              c_i64, c_i64, c_i64, c_i64, c_vp, c_size,
                                              ctypes.POINTER(TileConfig), c_vp]),
+    "fp8_scaled_mm_noalloc": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                      c_i64, c_i64, c_i64, c_i64, ctypes.POINTER(TileConfig), c_vp]),
     "fp8_scaled_mm_blockwise": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64,
                                         c_i64, c_i64, c_i64, c_i64, c_vp, c_size, c_vp]),
     "fp8_scaled_mm_blockwise_ex": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64,

@@ -13,6 +13,8 @@
 
 using namespace fp8w8a8;
 
+static_assert(FP8_NOALLOC_SCRATCH_BYTES == kStaticScratchBytes, "the header states the static scratch size");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -429,6 +431,44 @@ int fp8_scaled_mm_blockwise_ue8m0(const uint8_t* a, const uint8_t* b, const floa
                                   hipStream_t stream) {
   return fp8_scaled_mm_blockwise_ue8m0_ex(a, b, a_scale, a_scale_ld, b_scale, bias, out, M, N, K,
                                           lda, ldb, ldc, ws, ws_bytes, nullptr, stream);
+}
+
+int fp8_scaled_mm_noalloc(int32_t kind, const uint8_t* a, const uint8_t* b, const float* a_scale,
+                          int64_t a_scale_ld, const float* b_scale, const uint16_t* bias,
+                          uint16_t* out, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                          int64_t ldc, const fp8_tile_config* cfg, hipStream_t stream) {
+  const char* fn = "fp8_scaled_mm_noalloc";
+  if (kind != FP8_KIND_CHANNELWISE && kind != FP8_KIND_BLOCKWISE && kind != FP8_KIND_BLOCKWISE_UE8M0)
+    return fail(FP8_ERR_INVALID, "%s: unknown kind %d", fn, (int)kind);
+  int st = check_gemm(fn, a, b, a_scale, b_scale, bias, out, M, N, K, lda, ldb, ldc);
+  if (st) return st;
+  if (M == 0) return ok();
+  const bool bw = kind != FP8_KIND_CHANNELWISE;
+  if (bw) {
+    if (N % 128 != 0 || K % 128 != 0)
+      return fail(FP8_ERR_UNSUPPORTED, "%s: N=%lld and K=%lld must be multiples of 128", fn, (long long)N,
+                  (long long)K);
+    if (a_scale_ld < M)
+      return fail(FP8_ERR_INVALID, "%s: a_scale_ld=%lld < M=%lld", fn, (long long)a_scale_ld, (long long)M);
+  }
+  // the scratch this call's split-K plan needs, decided on the host before
+  // any device work
+  fp8_tile_config plan;
+  st = resolve_config(bw ? FP8_KIND_BLOCKWISE : FP8_KIND_CHANNELWISE, M, N, K, cfg, &plan);
+  if (st) return st;
+  const size_t need = fp8_scaled_mm_workspace_size(kind, M, N, K, &plan);
+  if (need > kStaticScratchBytes)
+    return fail(FP8_ERR_WORKSPACE,
+                "%s: the split-K plan of this call (variant %d, split_k %d) needs %zu bytes of scratch; "
+                "the library's static scratch holds %zu (ask for fewer splits or a larger tile, or call "
+                "the workspace-taking GEMM)", fn, plan.variant, plan.split_k, need, kStaticScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = hip_status(static_scratch(stream, &ws), fn);
+    if (st) return st;
+  }
+  return run_gemm(fn, kind, a, b, a_scale, bw ? a_scale_ld : 0, b_scale, bias, out, M, N, K, lda, ldb, ldc,
+                  ws, need > 0 ? kStaticScratchBytes : 0, &plan, stream);
 }
 
 size_t fp8_scaled_mm_workspace_size(int32_t kind, int64_t M, int64_t N, int64_t K,

@@ -23,6 +23,8 @@
 // and register slot, so any assignment of K bytes to (group, slot) that is the
 // same for both operands yields the same dot product; the kernels give group g
 // the bytes [32g, 32g + 32) of each 128-byte K block.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -1847,6 +1849,47 @@ hipError_t launch_e8(int variant, const GemmArgs& p, hipStream_t stream) {
   }
 }
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Static split-K scratch (see static_scratch in kernels.h). In host code the
+// array's name stands for a host-side shadow, not a device address: only the
+// address hipGetSymbolAddress returns for the current device is passed on.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    // the arrival counters must start at zero (each call leaves them so)
+    constexpr int64_t words = (int64_t)(kCounterBytes / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)(words / 256)), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(p), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 bool grouped_launchable(int variant, const GemmArgs& p) {
   return variant >= 15 && variant <= 25 && p.split_k == 1 && panel_eligible<kBlockwise>(p);

@@ -110,6 +110,15 @@ constexpr size_t kCounterBytes = (size_t)kMaxSplitTiles * sizeof(int);
 // Bytes of split-K workspace for (variant, split_k, M, N); 0 when split_k == 1.
 size_t variant_workspace_bytes(int variant, int split_k, int64_t M, int64_t N);
 
+// The library's own split-K workspace, for callers that cannot allocate: a
+// static device array of kStaticScratchBytes (arrival counters, then 64 MiB
+// of partial tiles), one per device, held until the process ends. The first
+// call on a device looks up that device's copy and clears its counters (a
+// fill kernel on `stream`); *ptr receives the device address to pass to the
+// kernels. Calls that overlap on one device share the array and race.
+constexpr size_t kStaticScratchBytes = kCounterBytes + ((size_t)64 << 20);
+hipError_t static_scratch(hipStream_t stream, void** ptr);
+
 hipError_t launch_gemm(int kind, int variant, const GemmArgs& args, hipStream_t stream);
 
 // Grouped blockwise GEMMs run only on the blockwise panel tiles (variants

@@ -353,6 +353,30 @@ int fp8_scaled_mm_blockwise_ue8m0_ex(const uint8_t* a, const uint8_t* b,
                                      void* ws, size_t ws_bytes, const fp8_tile_config* cfg,
                                      hipStream_t stream);
 
+/* The scaled GEMMs without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same operation, arguments, layouts, tile
+ * configs and errors as fp8_scaled_mm_channelwise_ex (kind
+ * FP8_KIND_CHANNELWISE; a_scale_ld is ignored), fp8_scaled_mm_blockwise_ex
+ * (FP8_KIND_BLOCKWISE) and fp8_scaled_mm_blockwise_ue8m0_ex
+ * (FP8_KIND_BLOCKWISE_UE8M0), and bit-identical outputs, but the split-K
+ * partial tiles and arrival counters live in a library-owned static device
+ * array of FP8_NOALLOC_SCRATCH_BYTES per device (held until the process
+ * ends). No device memory is allocated. A call whose split-K plan needs more
+ * than that returns FP8_ERR_WORKSPACE (checked on the host before any device
+ * work); plans without split-K need none. The first call on a device looks up
+ * that device's copy and clears its counters with a small kernel on `stream`.
+ * Every call on one device shares the array and leaves the counters at zero;
+ * calls that overlap in time on one device (different streams) race and give
+ * undefined results. */
+#define FP8_NOALLOC_SCRATCH_BYTES ((size_t)(256u << 10) + ((size_t)64 << 20))
+int fp8_scaled_mm_noalloc(int32_t kind, const uint8_t* a, const uint8_t* b,
+                          const float* a_scale, int64_t a_scale_ld,
+                          const float* b_scale, const uint16_t* bias, uint16_t* out,
+                          int64_t M, int64_t N, int64_t K,
+                          int64_t lda, int64_t ldb, int64_t ldc,
+                          const fp8_tile_config* cfg, hipStream_t stream);
+
 /* Workspace bytes the GEMM of `kind` needs for (M, N, K) with `cfg` (NULL =
  * the config the library would pick). 0 when no workspace is needed.
  * Returns (size_t)-1 on invalid arguments. */

@@ -277,6 +277,28 @@ def test_workspace_errors(lib):
     assert r == _lib.FP8_ERR_INVALID
 
 
+def test_noalloc_argument_errors_and_scratch_limit(lib):
+    """fp8_scaled_mm_noalloc validates on the host like the workspace GEMMs and
+    refuses a split-K plan larger than its static scratch before any device
+    work (so these calls run without a GPU)."""
+    f = lib.fp8_scaled_mm_noalloc
+    big = _lib.TileConfig(_lib.VARIANTS["t256x256panel"], 0, 0, 0, 8, 0)
+    need = lib.fp8_scaled_mm_workspace_size(0, 4096, 4096, 4096, ctypes.byref(big))
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    r = f(0, FAKE, FAKE, FAKE, 0, FAKE, None, FAKE, 4096, 4096, 4096, 4096, 4096, 4096, ctypes.byref(big), None)
+    assert r == _lib.FP8_ERR_WORKSPACE and "static scratch" in _err(lib)
+    r = f(1, FAKE, FAKE, FAKE, 4096, FAKE, None, FAKE, 4096, 4096, 4096, 4096, 4096, 4096, ctypes.byref(big), None)
+    assert r == _lib.FP8_ERR_WORKSPACE
+    assert f(7, FAKE, FAKE, FAKE, 0, FAKE, None, FAKE, 4, 256, 256, 256, 256, 256, None, None) == _lib.FP8_ERR_INVALID
+    assert f(0, None, FAKE, FAKE, 0, FAKE, None, FAKE, 4, 256, 256, 256, 256, 256, None, None) == _lib.FP8_ERR_INVALID
+    # blockwise: N, K multiples of 128 and a_scale_ld >= M
+    assert f(1, FAKE, FAKE, FAKE, 4, FAKE, None, FAKE, 4, 200, 256, 256, 256, 200, None, None) == \
+        _lib.FP8_ERR_UNSUPPORTED
+    assert f(1, FAKE, FAKE, FAKE, 3, FAKE, None, FAKE, 4, 256, 256, 256, 256, 256, None, None) == \
+        _lib.FP8_ERR_INVALID
+    assert f(0, FAKE, FAKE, FAKE, 0, FAKE, None, FAKE, 0, 256, 256, 256, 256, 256, None, None) == _lib.FP8_OK
+
+
 # ---------------------------------------------------------------- tile table
 def _lookup(lib, kind, n, k, m):
     c = _lib.TileConfig()
