@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the per-(shape, M) pass over the other workloads")
     ap.add_argument("--per-m", action="store_true", help="also print a per-(M, kind) table")
     ap.add_argument("--profile-label", default="",
                     help="run only the step's launches with this label (after a plain 256 MiB "
@@ -160,6 +162,100 @@ def measured_traffic(label):
         if kv.get("label") == label and kv.get("source_sha256") == cur:
             return float(kv["traffic_bytes_per_launch"])
     return None
+
+
+# The other workloads, measured after the timed steps (not part of `value`):
+# (config label, kind, N, K, M values, bias, outlier fraction)
+PER_CONFIG = [
+    ("small 256x512", "channelwise", 256, 512, [16], False, 0.0),
+    ("qkv 6144x4096", "channelwise", 6144, 4096, [1, 64, 512, 8192], True, 0.0),
+    ("down 4096x12288", "channelwise", 4096, 12288, [1, 64, 512, 8192], True, 0.0),
+    ("gate_up 24576x4096", "channelwise", 24576, 4096, [1, 64, 512, 8192], True, 0.0),
+    ("block 7168x7168", "blockwise", 7168, 7168, [1, 2, 3, 5, 7, 13, 31, 64, 256], False, 0.0),
+    ("block 3072x4096", "blockwise", 3072, 4096, [1, 4, 16, 64, 4096], False, 0.0),
+    ("block 4096x1536", "blockwise", 4096, 1536, [1, 4, 16, 64, 4096], False, 0.0),
+]
+
+
+def _sig(x, d=4):
+    return float(f"{x:.{d}g}")
+
+
+def per_config(torch, ops, synth, dev, warmup=10, calls=40):
+    """GEMM, quantizer and whole-linear time of every (shape, M) of the other
+    workloads: each timed as one batch of back-to-back calls behind queued
+    device copies (HIP events around the batch, not per call), the GEMM's
+    weight rotating over copies that cover >= 1 GiB so every call reads it
+    from HBM. frac = roofline time (max of 2MNK / 5 PFLOP/s and algorithmic
+    bytes / 8 TB/s) / GEMM time."""
+    import math
+
+    from fp8_w8a8_quantized_token_amd import measure
+
+    filler = measure._Filler(dev)
+    out = {}
+    rows = []
+    for label, kind, n, k, ms, with_bias, outl in PER_CONFIG:
+        sets = max(2, min(64, math.ceil((1 << 30) / (n * k))))
+        w = synth.weights(f"bench/{label}", n, k).to(torch.bfloat16).to(dev)
+        if kind == "channelwise":
+            wq, ws = ops.quant_per_token(w)
+        else:
+            wq, _ = ops.quant_per_token_group(w, 128, row_alignment=1)
+            wq = wq.contiguous()
+            ws = synth.positive_scales(f"bench/{label}/wblk", (n // 128, k // 128)).to(dev)
+        del w
+        weights = [(wq.clone(), ws.clone()) for _ in range(sets)]
+        bias = synth.bias(f"bench/{label}", n).to(dev) if with_bias else None
+        rec = {"kind": kind, "M": [], "variant": [], "gemm_us": [], "quant_us": [], "linear_us": [],
+               "tflops": [], "gbps": [], "bound": [], "frac": []}
+        for m in ms:
+            x = synth.activations(f"bench/{label}", m, k, outlier_frac=outl).to(dev)
+            m_pad = ops.padded_rows(m, 4) if kind == "blockwise" else m
+            o = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            q = torch.empty((m_pad, k), dtype=torch.uint8, device=dev)
+            st = (torch.empty((m,), dtype=torch.float32, device=dev) if kind == "channelwise"
+                  else torch.empty((k // 128, m_pad), dtype=torch.float32, device=dev))
+            if kind == "channelwise":
+                fq = ops.prepare("quant_per_token", x, out=q, scale=st)
+                fq()
+                fg = [ops.prepare("scaled_mm_channelwise", q, wb, st, wsb, bias=bias, out=o)
+                      for wb, wsb in weights]
+                fl = [ops.prepare("linear_channelwise", x, wb, wsb, bias=bias, out=o, q=q, scale=st)
+                      for wb, wsb in weights]
+            else:
+                fq = ops.prepare("quant_per_token_group", x, 128, row_alignment=4, out=q, scale_storage=st)
+                fq()
+                fg = [ops.prepare("scaled_mm_blockwise", q, wb, st.transpose(0, 1), wsb, bias=bias, m=m,
+                                  out=o) for wb, wsb in weights]
+                fl = [ops.prepare("linear_blockwise", x, wb, wsb, bias=bias, row_alignment=4, out=o, q=q,
+                                  scale=st) for wb, wsb in weights]
+            g_us = measure._batch_us(fg, warmup, calls, filler)
+            q_us = measure._batch_us([fq], warmup, calls, filler)
+            l_us = measure._batch_us(fl, warmup, calls, filler)
+            flops = 2 * m * n * k
+            nbytes = gemm_bytes(kind, m, n, k, with_bias)
+            t_roof = max(flops / (PEAK_TFLOPS_FP8 * 1e12), nbytes / (PEAK_GBPS * 1e9))
+            cfg, _ = ops.tile_config(ops.KIND_CHANNELWISE if kind == "channelwise" else ops.KIND_BLOCKWISE,
+                                     n, k, m)
+            rec["M"].append(m)
+            rec["variant"].append(cfg["variant"] + (f"/sk{cfg['split_k']}" if cfg["split_k"] > 1 else ""))
+            rec["gemm_us"].append(_sig(g_us))
+            rec["quant_us"].append(_sig(q_us))
+            rec["linear_us"].append(_sig(l_us))
+            rec["tflops"].append(_sig(flops / g_us / 1e6))
+            rec["gbps"].append(_sig(nbytes / g_us / 1e3))
+            rec["bound"].append("mfma" if flops / nbytes >= RIDGE else "hbm")
+            rec["frac"].append(_sig(t_roof * 1e6 / g_us, 3))
+            rows.append(f"{label:20s} {kind:11s} M={m:5d} {rec['variant'][-1]:18s} gemm {g_us:8.2f} us  "
+                        f"quant {q_us:6.2f}  linear {l_us:8.2f}  {flops / g_us / 1e6:7.1f} TF/s  "
+                        f"{nbytes / g_us / 1e3:6.0f} GB/s  frac {t_roof * 1e6 / g_us:.3f} ({rec['bound'][-1]})")
+            print(rows[-1], file=sys.stderr, flush=True)
+            del fq, fg, fl
+        out[label] = rec
+        del weights
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline():
@@ -313,6 +409,8 @@ def main():
     }
     if args.per_m:
         result["per_m"] = per_m
+    if not args.no_per_config:
+        result["per_config"] = per_config(torch, ops, synth, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)

@@ -101,6 +101,11 @@ SIGNATURES = {
     "fp8_tile_config_lookup": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(TileConfig)]),
     "fp8_tile_config_default": (c_i32, [c_i32, c_i64, c_i64, c_i64, ctypes.POINTER(TileConfig)]),
     "fp8_tile_config_set_dir": (c_i32, [ctypes.c_char_p]),
+    "fp8_probe_stream_read": (c_i32, [c_vp, c_size, c_vp, c_i32, c_vp]),
+    "fp8_probe_strided_read": (c_i32, [c_vp, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp]),
+    "fp8_probe_l2_feed": (c_i32, [c_vp, c_size, c_i32, c_i32, c_vp, c_i32, c_vp]),
+    "fp8_probe_mfma": (c_i32, [c_i32, c_vp, c_i32, c_vp]),
+    "fp8_probe_lds": (c_i32, [c_i32, c_i32, c_vp, c_i32, c_vp]),
     "fp8_last_error": (ctypes.c_char_p, []),
     "fp8_version": (c_i32, []),
 }

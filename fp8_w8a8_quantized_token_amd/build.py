@@ -14,7 +14,7 @@ LIB = os.path.join(PKG, "libfp8w8a8.so")
 # the device compiler's per-kernel register / scratch / LDS report of the
 # last build (one "remark" block per kernel)
 RESOURCE_REPORT = os.path.join(PKG, "_build", "resource_usage.txt")
-SOURCES = ["quant.hip", "gemm.hip", "tile_table.cpp", "api.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "probes.hip", "tile_table.cpp", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -556,6 +556,51 @@ int fp8_tile_config_set_dir(const char* dir) {
   return FP8_OK;
 }
 
+int fp8_probe_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
+                          hipStream_t stream) {
+  const char* fn = "fp8_probe_stream_read";
+  if (!src || !sink || bytes < 16 || bytes % 16 != 0 || !aligned(src, 16) || workgroups < 1)
+    return fail(FP8_ERR_INVALID, "%s: src 16-byte aligned, bytes a positive multiple of 16, workgroups >= 1", fn);
+  return hip_status(launch_probe_stream_read(src, bytes, sink, workgroups, stream), fn);
+}
+
+int fp8_probe_strided_read(const void* src, int64_t rows, int64_t row_bytes, int32_t rows_per_wg,
+                           int32_t piece, uint32_t* sink, hipStream_t stream) {
+  const char* fn = "fp8_probe_strided_read";
+  const bool piece_ok = piece == 16 || piece == 32 || piece == 64 || piece == 128 || piece == 256 ||
+                        piece == 512 || piece == 1024;
+  if (!src || !sink || !aligned(src, 16) || !piece_ok || rows_per_wg < 1 || rows < rows_per_wg ||
+      rows % rows_per_wg != 0 || row_bytes % piece != 0 || row_bytes % 16 != 0 ||
+      (rows_per_wg * piece) % 1024 != 0 || rows / rows_per_wg > 65535)
+    return fail(FP8_ERR_INVALID, "%s: piece a power of two in [16, 1024] dividing row_bytes, rows a multiple "
+                "of rows_per_wg, rows_per_wg * piece a multiple of 1024", fn);
+  return hip_status(launch_probe_strided_read(src, rows, row_bytes, rows_per_wg, piece, sink, stream), fn);
+}
+
+int fp8_probe_l2_feed(const void* src, size_t window_bytes, int32_t reps, int32_t dma, uint32_t* sink,
+                      int32_t workgroups, hipStream_t stream) {
+  const char* fn = "fp8_probe_l2_feed";
+  if (!src || !sink || window_bytes < 4096 || window_bytes % 1024 != 0 || !aligned(src, 16) || reps < 1 ||
+      workgroups < 1)
+    return fail(FP8_ERR_INVALID, "%s: src 16-byte aligned, window a multiple of 1 KB (>= 4 KB), reps and "
+                "workgroups >= 1", fn);
+  return hip_status(launch_probe_l2_feed(src, window_bytes, reps, dma != 0, sink, workgroups, stream), fn);
+}
+
+int fp8_probe_mfma(int32_t iters, float* sink, int32_t workgroups, hipStream_t stream) {
+  const char* fn = "fp8_probe_mfma";
+  if (!sink || iters < 1 || workgroups < 1)
+    return fail(FP8_ERR_INVALID, "%s: iters and workgroups >= 1, sink non-null", fn);
+  return hip_status(launch_probe_mfma(iters, sink, workgroups, stream), fn);
+}
+
+int fp8_probe_lds(int32_t iters, int32_t threads, uint32_t* sink, int32_t workgroups, hipStream_t stream) {
+  const char* fn = "fp8_probe_lds";
+  if (!sink || iters < 1 || workgroups < 1 || (threads != 256 && threads != 512))
+    return fail(FP8_ERR_INVALID, "%s: iters and workgroups >= 1, threads 256 or 512, sink non-null", fn);
+  return hip_status(launch_probe_lds(iters, threads, sink, workgroups, stream), fn);
+}
+
 const char* fp8_last_error(void) { return g_last_error.c_str(); }
 
 int32_t fp8_version(void) { return 100; }

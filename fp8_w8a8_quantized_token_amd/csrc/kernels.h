@@ -125,4 +125,14 @@ hipError_t launch_gemm(int kind, int variant, const GemmArgs& args, hipStream_t 
 // 15-25) with split_k == 1; true when `variant` and the arguments allow it.
 bool grouped_launchable(int variant, const GemmArgs& args);
 
+// Measurement probes (probes.hip): sink holds workgroups * 256 words.
+hipError_t launch_probe_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups,
+                                    hipStream_t stream);
+hipError_t launch_probe_strided_read(const void* src, int64_t rows, int64_t row_bytes, int rows_per_wg,
+                                     int piece, uint32_t* sink, hipStream_t stream);
+hipError_t launch_probe_l2_feed(const void* src, size_t window, int reps, int dma, uint32_t* sink,
+                                int workgroups, hipStream_t stream);
+hipError_t launch_probe_mfma(int iters, float* sink, int workgroups, hipStream_t stream);
+hipError_t launch_probe_lds(int iters, int threads, uint32_t* sink, int workgroups, hipStream_t stream);
+
 }  // namespace fp8w8a8

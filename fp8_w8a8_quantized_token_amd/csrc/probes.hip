@@ -1,0 +1,213 @@
+// Measurement probes for gfx950: the ceilings the GEMM and quantizer kernels
+// are compared with. None of them is part of the linear itself.
+//
+//  * stream_read_kernel: reads a buffer once from HBM (16-byte non-temporal
+//    loads, U per lane in flight), the read-only ceiling of the weight stream
+//    of the small-M GEMMs.
+//  * l2_feed_kernel: every workgroup re-reads the same L2-resident window,
+//    with register loads or with LDS-DMA loads (global_load_lds_dwordx4, the
+//    form the panel-ring GEMM tiles use): the per-compute-unit feed rate from
+//    L2.
+//  * mfma_probe_kernel: back-to-back independent 32x32x64 FP8 MFMAs: the
+//    dense FP8 matrix rate and, from it, the clock the matrix cores ran at.
+//
+// Every probe folds what it reads into a value that is stored only when it
+// equals a key the host passes (never met in practice), so no load or MFMA
+// can be removed by the compiler, and only vector stores write memory.
+#include "common.h"
+#include "kernels.h"
+
+namespace fp8w8a8 {
+
+namespace {
+constexpr int kProbeThreads = 256;
+constexpr int kReadUnroll = 8;
+}  // namespace
+
+__global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const uint4* src, int64_t n16,
+                                                                    uint32_t* sink, uint32_t key) {
+  uint32_t acc = 0;
+  const int64_t step = (int64_t)gridDim.x * kProbeThreads * kReadUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kProbeThreads * kReadUnroll + threadIdx.x; base < n16;
+       base += step) {
+    uint4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) {
+      const int64_t i = base + (int64_t)u * kProbeThreads;
+      v[u] = load16_nt(src + (i < n16 ? i : n16 - 1));
+    }
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == key) sink[blockIdx.x * kProbeThreads + threadIdx.x] = acc;
+}
+
+// A [rows][row_bytes] matrix read once in pieces of `piece` bytes per row:
+// workgroup w owns rows [w R, w R + R) and walks the row length in steps of
+// `piece` bytes, each step reading its R rows' pieces (one 1 KB load
+// instruction covers 1024 / piece rows); kReadUnroll instructions of a lane in
+// flight. piece = 128 is the access pattern of the panel-ring GEMM tiles'
+// weight panels, piece >= 1024 that of the weight-streaming kernel.
+__global__ __launch_bounds__(kProbeThreads) void strided_read_kernel(const uint8_t* src, int64_t row_bytes,
+                                                                     int rows_per_wg, int piece,
+                                                                     uint32_t* sink, uint32_t key) {
+  uint32_t acc = 0;
+  const int tid = threadIdx.x;
+  const int lanes_per_row = piece / 16;       // lanes covering one row's piece
+  const int rows_per_inst = 1024 / piece;     // rows per 64-lane instruction
+  const int wave = tid >> 6, lane = tid & 63;
+  const int inst_per_step = rows_per_wg / rows_per_inst;  // instructions per K step (all waves)
+  const uint8_t* base = src + (int64_t)blockIdx.x * rows_per_wg * row_bytes;
+  const int64_t total = (row_bytes / piece) * inst_per_step;  // instructions of this workgroup
+  for (int64_t i0 = wave; i0 < total; i0 += 4 * kReadUnroll) {
+    uint4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) {
+      int64_t i = i0 + 4 * u;
+      i = i < total ? i : total - 1;
+      const int64_t step = i / inst_per_step;
+      const int r = (int)(i % inst_per_step) * rows_per_inst + lane / lanes_per_row;
+      v[u] = load16_nt(base + (int64_t)r * row_bytes + step * piece + (lane % lanes_per_row) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == key) sink[blockIdx.x * kProbeThreads + tid] = acc;
+}
+
+// DMA == 0: register loads; DMA == 1: LDS-DMA loads into a 16-slot ring of
+// 1 KB per wave (at most 15 slots in flight per wave, so a slot's previous
+// load has landed before it is issued into again).
+template <int DMA>
+__global__ __launch_bounds__(kProbeThreads) void l2_feed_kernel(const uint8_t* src, int64_t window,
+                                                                int reps, uint32_t* sink, uint32_t key) {
+  uint32_t acc = 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n1k = window / 1024;  // 1 KB pieces of the window
+  if constexpr (DMA == 0) {
+    for (int r = 0; r < reps; ++r) {
+      for (int64_t p = wave; p < n1k; p += 4 * kReadUnroll) {
+        uint4 v[kReadUnroll];
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u) {
+          int64_t q = p + 4 * u;
+          q = q < n1k ? q : n1k - 1;
+          v[u] = load16(src + q * 1024 + lane * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+      }
+    }
+  } else {
+    __shared__ __attribute__((aligned(16))) uint8_t ring[4][16][1024];
+    const uint32_t base = (uint32_t)(uintptr_t)&ring[wave][0][0];
+    int slot = 0;
+    int64_t issued = 0;
+    for (int r = 0; r < reps; ++r) {
+      for (int64_t p = wave; p < n1k; p += 4) {
+        const uint32_t m0v = __builtin_amdgcn_readfirstlane(base + (uint32_t)slot * 1024);
+        const uint8_t* g = src + p * 1024 + lane * 16;
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0v) : "memory", "m0");
+        slot = (slot + 1) & 15;
+        ++issued;
+        // keep at most 15 pieces of this wave in flight
+        __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (15 << 8));
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    acc = *reinterpret_cast<const uint32_t*>(&ring[wave][lane & 15][0]) + (uint32_t)issued;
+  }
+  if (acc == key) sink[blockIdx.x * kProbeThreads + threadIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(int iters, float* sink, uint32_t key) {
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  const int lane = threadIdx.x & 63;
+  i32x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    // E4M3 codes of 0.5 and 0.25 with the lane folded into the low bits
+    a[i] = 0x30303030 + (lane & 1);
+    b[i] = 0x28282828 + ((lane >> 1) & 1);
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[j], 0, 0, 0, 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[j][e];
+  if (__float_as_uint(s) == key) sink[blockIdx.x * kProbeThreads + threadIdx.x] = s;
+}
+
+// LDS read rate: every lane reads 16 bytes per step (ds_read_b128), the 64
+// lanes of a wave one contiguous 1 KB row of a 64 KB buffer (conflict-free),
+// the row moving with the step and the wave; THREADS threads per workgroup.
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void lds_read_kernel(int iters, uint32_t* sink, uint32_t key) {
+  __shared__ __attribute__((aligned(16))) uint4 buf[4096];  // 64 KB
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 4096; i += THREADS) buf[i] = make_uint4(i, i ^ 0x55u, i + 7u, ~i);
+  __syncthreads();
+  uint4 acc = make_uint4(0, 0, 0, 0);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint4 v = buf[(((it * 8 + u) * 5 + wave) & 63) * 64 + lane];
+      acc.x ^= v.x; acc.y += v.y; acc.z ^= v.z; acc.w += v.w;
+    }
+  }
+  const uint32_t r = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (r == key) sink[blockIdx.x * THREADS + tid] = r;
+}
+
+hipError_t launch_probe_lds(int iters, int threads, uint32_t* sink, int workgroups, hipStream_t stream) {
+  if (threads == 512)
+    hipLaunchKernelGGL(lds_read_kernel<512>, dim3((unsigned)workgroups), dim3(512), 0, stream, iters, sink,
+                       0x9E3779B9u);
+  else
+    hipLaunchKernelGGL(lds_read_kernel<256>, dim3((unsigned)workgroups), dim3(256), 0, stream, iters, sink,
+                       0x9E3779B9u);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups,
+                                    hipStream_t stream) {
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)workgroups), dim3(kProbeThreads), 0, stream,
+                     static_cast<const uint4*>(src), (int64_t)(bytes / 16), sink, 0x9E3779B9u);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_strided_read(const void* src, int64_t rows, int64_t row_bytes, int rows_per_wg,
+                                     int piece, uint32_t* sink, hipStream_t stream) {
+  hipLaunchKernelGGL(strided_read_kernel, dim3((unsigned)(rows / rows_per_wg)), dim3(kProbeThreads), 0, stream,
+                     static_cast<const uint8_t*>(src), row_bytes, rows_per_wg, piece, sink, 0x9E3779B9u);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_l2_feed(const void* src, size_t window, int reps, int dma, uint32_t* sink,
+                                int workgroups, hipStream_t stream) {
+  if (dma)
+    hipLaunchKernelGGL(l2_feed_kernel<1>, dim3((unsigned)workgroups), dim3(kProbeThreads), 0, stream,
+                       static_cast<const uint8_t*>(src), (int64_t)window, reps, sink, 0x9E3779B9u);
+  else
+    hipLaunchKernelGGL(l2_feed_kernel<0>, dim3((unsigned)workgroups), dim3(kProbeThreads), 0, stream,
+                       static_cast<const uint8_t*>(src), (int64_t)window, reps, sink, 0x9E3779B9u);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_mfma(int iters, float* sink, int workgroups, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3((unsigned)workgroups), dim3(kProbeThreads), 0, stream, iters,
+                     sink, 0x9E3779B9u);
+  return hipGetLastError();
+}
+
+}  // namespace fp8w8a8

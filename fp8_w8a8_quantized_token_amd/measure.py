@@ -423,6 +423,93 @@ def measure_stream_ceiling(warmup, calls, filler):
     return lines
 
 
+def measure_probes(warmup, calls, filler):
+    """Ceilings from the library's own probe kernels (batch-timed, HIP events
+    around each batch): the read-only HBM stream at the small-M weight sizes
+    (cold: distinct buffers covering >= 1 GiB, at two grid sizes), the
+    L2-to-compute-unit feed with register and LDS-DMA loads (one and two
+    workgroups per compute unit, a 512 KB window every workgroup re-reads),
+    and the dense FP8 MFMA rate with the clock it implies."""
+    import ctypes
+    dev = torch.device("cuda:0")
+    lib = _lib.load()
+    stream = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)  # noqa: E731
+    sink = torch.zeros(4096 * 256, dtype=torch.int32, device=dev)
+    sp = ctypes.c_void_p(sink.data_ptr())
+    head = "| probe | size | grid | µs per call | rate | note |"
+    lines = [head, "|---|---|---|---|---|---|"]
+    print(head, flush=True)
+    print(lines[1], flush=True)
+
+    def emit(*cells):
+        line = "| " + " | ".join(str(c) for c in cells) + " |"
+        lines.append(line)
+        print(line, flush=True)
+
+    # read-only HBM stream at the weight sizes of the small-M linears (and above)
+    for size in (6291456, 16777216, 50331648, 100663296, 268435456):
+        sets = max(2, min(MAX_SETS, math.ceil(ROTATE_BYTES / size)))
+        bufs = [torch.full((size // 4,), i, dtype=torch.int32, device=dev) for i in range(sets)]
+        for wgs in (1024, 2048):
+            fns = [lambda b=b, w=wgs: _lib.check(lib.fp8_probe_stream_read(
+                ctypes.c_void_p(b.data_ptr()), size, sp, w, stream())) for b in bufs]
+            us = _batch_us(fns, warmup, calls, filler)
+            emit("HBM read (cold)", f"{size / 1e6:.1f} MB", f"{wgs}x256", f"{us:.2f}",
+                 f"{size / us / 1e3:.0f} GB/s ({size / us / 1e3 / PEAK_GBPS:.2f} of 8 TB/s)", f"{sets} buffers")
+        del bufs
+        torch.cuda.empty_cache()
+    # the same bytes read as row pieces: the weight-panel access of the GEMM tiles
+    for rows, rb in ((4096, 4096), (4096, 12288)):
+        size = rows * rb
+        sets = max(2, min(MAX_SETS, math.ceil(ROTATE_BYTES / size)))
+        bufs = [torch.full((size // 4,), i, dtype=torch.int32, device=dev) for i in range(sets)]
+        for rpw in (16, 32):
+            for piece in (64, 128, 256, 512, 1024):
+                if (rpw * piece) % 1024:
+                    continue
+                fns = [lambda b=b, r=rpw, pc=piece: _lib.check(lib.fp8_probe_strided_read(
+                    ctypes.c_void_p(b.data_ptr()), rows, rb, r, pc, sp, stream())) for b in bufs]
+                us = _batch_us(fns, warmup, calls, filler)
+                emit("HBM read in row pieces (cold)", f"{rows}x{rb} B, {piece} B pieces",
+                     f"{rows // rpw}x256 ({rpw} rows each)", f"{us:.2f}",
+                     f"{size / us / 1e3:.0f} GB/s ({size / us / 1e3 / PEAK_GBPS:.2f} of 8 TB/s)", f"{sets} buffers")
+        del bufs
+        torch.cuda.empty_cache()
+    # L2 -> compute unit feed: every workgroup re-reads a 512 KB window
+    win = 512 << 10
+    src = torch.full((win // 4,), 3, dtype=torch.int32, device=dev)
+    for dma in (0, 1):
+        for wgs in (256, 512):
+            reps = 64
+            fn = lambda w=wgs, d=dma: _lib.check(lib.fp8_probe_l2_feed(  # noqa: E731
+                ctypes.c_void_p(src.data_ptr()), win, reps, d, sp, w, stream()))
+            us = _batch_us([fn], max(2, warmup // 4), max(4, calls // 10), filler)
+            moved = wgs * reps * win
+            emit("L2 feed, " + ("LDS-DMA" if dma else "register") + " loads", "512 KB window",
+                 f"{wgs}x256", f"{us:.1f}", f"{moved / us / 1e3:.0f} GB/s total, "
+                 f"{moved / us / 1e3 / 256:.1f} GB/s per CU", f"{reps} passes per workgroup")
+    # LDS read rate per compute unit
+    for threads, wgs in ((256, 256), (512, 256), (256, 512), (256, 1024)):
+        iters = 4000
+        fn = lambda t=threads, w=wgs: _lib.check(lib.fp8_probe_lds(iters, t, sp, w, stream()))  # noqa: E731
+        us = _batch_us([fn], 2, 5, filler)
+        moved = wgs * threads * iters * 128
+        emit("LDS reads (ds_read_b128)", "64 KB per workgroup", f"{wgs}x{threads}", f"{us:.1f}",
+             f"{moved / us / 1e3 / 256:.0f} GB/s per CU", "divide by the clock for bytes per cycle")
+    # dense FP8 MFMA
+    iters = 20000
+    for wgs in (256, 512, 1024):
+        fn = lambda w=wgs: _lib.check(lib.fp8_probe_mfma(iters, ctypes.c_void_p(sink.data_ptr()), w,  # noqa: E731
+                                                          stream()))
+        us = _batch_us([fn], 2, 5, filler)
+        flops = wgs * 4 * iters * 4 * 131072
+        tf = flops / us / 1e6
+        emit("FP8 MFMA 32x32x64", f"{iters} x 4 per wave", f"{wgs}x256", f"{us:.1f}",
+             f"{tf:.0f} TFLOP/s ({tf / PEAK_TFLOPS:.2f} of 5.0 PF)",
+             f"clock {tf * 1e12 / (256 * 8192) / 1e9:.2f} GHz")
+    return lines
+
+
 # Down projections fed straight from a gated MLP's [gate | up] output: the
 # decode linears with SiLU-and-mul through the linear call (one launch where
 # the library fuses; FP8W8A8_FUSED_LINEAR=all fuses at every M <= 4) and as the
@@ -517,19 +604,23 @@ def main(argv=None):
                     help="time the decode down projection with SiLU-and-mul: one launch against two")
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="time plain device copies and reductions at the small-M linears' byte counts")
+    ap.add_argument("--probes", action="store_true",
+                    help="run the probe kernels: HBM read stream, L2 feed, FP8 MFMA rate and clock")
     args = ap.parse_args(argv)
     _lib.load()
     dev = torch.device("cuda:0")
     want = args.workloads.split(",")
     filler = _Filler(dev)
-    if args.quant_variants or args.ue8m0_gemm or args.moe or args.stream_ceiling or args.silu_linear:
+    if (args.quant_variants or args.ue8m0_gemm or args.moe or args.stream_ceiling or args.silu_linear
+            or args.probes):
         t0 = time.time()
         mode = (measure_quant_variants if args.quant_variants else
                 measure_ue8m0_gemm if args.ue8m0_gemm else
                 measure_moe if args.moe else
+                measure_probes if args.probes else
                 measure_silu_linear if args.silu_linear else measure_stream_ceiling)
         lines = mode(args.warmup, args.calls, filler)
-        if args.stream_ceiling or args.silu_linear:
+        if args.stream_ceiling or args.silu_linear or args.probes:
             note = (f"\n{args.calls} calls per row after {args.warmup} warm-up calls, timed as one "
                     f"batch with HIP events behind queued device copies (average per call); "
                     f"buffers rotated to cover >= 1 GiB. {time.time() - t0:.0f} s.")

@@ -506,6 +506,51 @@ int fp8_tile_config_default(int32_t kind, int64_t N, int64_t K, int64_t M,
  * drop every cached table. Returns FP8_OK. */
 int fp8_tile_config_set_dir(const char* dir);
 
+/* ------------------------------------------------------------------------ */
+/* Measurement probes (not part of the linear): the ceilings the kernels      */
+/* above are compared with. Each returns FP8_OK or an error code; `sink`      */
+/* (device memory, workgroups * 256 words) only receives a value if a folded  */
+/* checksum happens to equal an internal key, which keeps the compiler from   */
+/* dropping the work; its contents are meaningless.                            */
+/* ------------------------------------------------------------------------ */
+
+/* Reads `bytes` of device memory once (16-byte non-temporal loads, eight per
+ * lane in flight, `workgroups` workgroups of 256 threads striding over the
+ * buffer): the HBM read ceiling for a weight stream of that size. src 16-byte
+ * aligned, bytes a positive multiple of 16. */
+int fp8_probe_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
+                          hipStream_t stream);
+
+/* Reads a [rows][row_bytes] matrix once, `piece` bytes of a row at a time:
+ * workgroup w (of rows / rows_per_wg) owns rows_per_wg consecutive rows and
+ * walks them along the row in steps of `piece` bytes, reading all its rows'
+ * pieces each step (16-byte non-temporal loads; one 64-lane instruction covers
+ * 1024 / piece rows). The HBM cost of the row-piece size a GEMM tile's weight
+ * stream uses. piece a power of two in [16, 1024]; rows_per_wg * piece a
+ * multiple of 1024; the grid is rows / rows_per_wg workgroups (<= 65535). */
+int fp8_probe_strided_read(const void* src, int64_t rows, int64_t row_bytes, int32_t rows_per_wg,
+                           int32_t piece, uint32_t* sink, hipStream_t stream);
+
+/* Every workgroup reads the same `window_bytes` (a multiple of 1 KB; small
+ * enough to stay in L2) `reps` times: with dma == 0 through 16-byte register
+ * loads, with dma != 0 through LDS-DMA loads (global_load_lds_dwordx4) into a
+ * ring in LDS. Bytes moved = workgroups * reps * window_bytes; divided by the
+ * duration and the compute units it gives the L2-to-compute-unit feed rate. */
+int fp8_probe_l2_feed(const void* src, size_t window_bytes, int32_t reps, int32_t dma, uint32_t* sink,
+                      int32_t workgroups, hipStream_t stream);
+
+/* Back-to-back independent V_MFMA_F32_32X32X64_F8F6F4 (four accumulators per
+ * wave, four waves per workgroup): FLOPs = workgroups * 4 * iters * 4 * 131072.
+ * The dense FP8 matrix rate; rate / (256 CUs * 8192 FLOP per clock per CU)
+ * is the clock the matrix cores ran at. */
+int fp8_probe_mfma(int32_t iters, float* sink, int32_t workgroups, hipStream_t stream);
+
+/* LDS read rate: every lane of `workgroups` workgroups of `threads` (256 or
+ * 512) threads reads 16 bytes per step (ds_read_b128, a wave reading one
+ * contiguous 1 KB row: no bank conflicts), iters * 8 steps. Bytes read =
+ * workgroups * threads * iters * 128. */
+int fp8_probe_lds(int32_t iters, int32_t threads, uint32_t* sink, int32_t workgroups, hipStream_t stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* fp8_last_error(void);
 

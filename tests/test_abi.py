@@ -299,6 +299,17 @@ def test_noalloc_argument_errors_and_scratch_limit(lib):
     assert f(0, FAKE, FAKE, FAKE, 0, FAKE, None, FAKE, 0, 256, 256, 256, 256, 256, None, None) == _lib.FP8_OK
 
 
+def test_probe_argument_errors(lib):
+    """The measurement probes validate on the host (no device needed)."""
+    assert lib.fp8_probe_stream_read(FAKE, 100, FAKE, 4, None) == _lib.FP8_ERR_INVALID  # not x16
+    assert lib.fp8_probe_stream_read(None, 1024, FAKE, 4, None) == _lib.FP8_ERR_INVALID
+    assert lib.fp8_probe_strided_read(FAKE, 4096, 4096, 16, 48, FAKE, None) == _lib.FP8_ERR_INVALID
+    assert lib.fp8_probe_strided_read(FAKE, 4096, 4096, 3, 128, FAKE, None) == _lib.FP8_ERR_INVALID
+    assert lib.fp8_probe_l2_feed(FAKE, 1000, 4, 0, FAKE, 4, None) == _lib.FP8_ERR_INVALID
+    assert lib.fp8_probe_mfma(0, FAKE, 4, None) == _lib.FP8_ERR_INVALID
+    assert lib.fp8_probe_lds(4, 128, FAKE, 4, None) == _lib.FP8_ERR_INVALID
+
+
 # ---------------------------------------------------------------- tile table
 def _lookup(lib, kind, n, k, m):
     c = _lib.TileConfig()

@@ -371,13 +371,14 @@ DEEP_CASES = [(v, kind, sk, m, n, k) for v in ("t64x64deep", "t128x64deep", "t12
                                                 "t32x32deep", "t64x32deep")
               for kind, sk, m, n, k in (("cw", 1, 300, 392, 1024), ("cw", 2, 129, 392, 4096),
                                         ("cw", 1, 1, 64, 128), ("cw", 1, 65, 256, 768),
-                                        ("bw", 2, 300, 384, 1024), ("bw", 1, 65, 256, 768))]
+                                        ("bw", 2, 300, 384, 1024), ("bw", 1, 65, 256, 768),
+                                        ("bw", 1, 70, 256, 4096))]
 
 
 @pytest.mark.parametrize("variant,kind,split_k,m,n,k", DEEP_CASES,
                          ids=[f"{c[0]}-{c[1]}-sk{c[2]}-M{c[3]}-N{c[4]}-K{c[5]}" for c in DEEP_CASES])
 def test_deep_ring_variants(variant, kind, split_k, m, n, k):
-    """Deep-ring (9- and 7-slot) and 8-wave small panel tiles: stage counts
+    """Deep-ring (7- to 17-slot) and 8-wave small panel tiles: stage counts
     below, at and above the ring depth, ragged M and N, split-K."""
     cfg = ops.make_config(variant, split_k)
     if kind == "cw":
