@@ -594,6 +594,18 @@ int fp8_probe_mfma(int32_t iters, float* sink, int32_t workgroups, hipStream_t s
   return hip_status(launch_probe_mfma(iters, sink, workgroups, stream), fn);
 }
 
+int fp8_probe_wave_read(const void* src, size_t bytes, int32_t threads, int32_t depth, int32_t dma,
+                        uint32_t* sink, int32_t workgroups, hipStream_t stream) {
+  const char* fn = "fp8_probe_wave_read";
+  const bool shape_ok = (threads == 256 && (depth == 4 || depth == 8 || depth == 16)) ||
+                        (threads == 512 && (depth == 4 || depth == 8 || depth == 16)) ||
+                        (threads == 1024 && (depth == 4 || depth == 8));
+  if (!src || !sink || !aligned(src, 16) || bytes < 1024 || bytes % 1024 != 0 || workgroups < 1 || !shape_ok)
+    return fail(FP8_ERR_INVALID, "%s: bytes a positive multiple of 1 KB, (threads, depth) in {256, 512} x {4, 8, "
+                "16} or 1024 x {4, 8}", fn);
+  return hip_status(launch_probe_wave_read(src, bytes, threads, depth, dma != 0, sink, workgroups, stream), fn);
+}
+
 int fp8_probe_lds(int32_t iters, int32_t threads, uint32_t* sink, int32_t workgroups, hipStream_t stream) {
   const char* fn = "fp8_probe_lds";
   if (!sink || iters < 1 || workgroups < 1 || (threads != 256 && threads != 512))

@@ -133,6 +133,8 @@ hipError_t launch_probe_strided_read(const void* src, int64_t rows, int64_t row_
 hipError_t launch_probe_l2_feed(const void* src, size_t window, int reps, int dma, uint32_t* sink,
                                 int workgroups, hipStream_t stream);
 hipError_t launch_probe_mfma(int iters, float* sink, int workgroups, hipStream_t stream);
+hipError_t launch_probe_wave_read(const void* src, size_t bytes, int threads, int depth, int dma, uint32_t* sink,
+                                  int workgroups, hipStream_t stream);
 hipError_t launch_probe_lds(int iters, int threads, uint32_t* sink, int workgroups, hipStream_t stream);
 
 }  // namespace fp8w8a8

@@ -179,6 +179,78 @@ hipError_t launch_probe_lds(int iters, int threads, uint32_t* sink, int workgrou
   return hipGetLastError();
 }
 
+// One pass over `bytes` in 1 KB pieces (a wave's 64 lanes x 16 bytes), piece
+// i of workgroup w at (i * gridDim.x + w) * 1 KB... strided by wave: each
+// wave of THREADS / 64 keeps U pieces in flight, into registers (DMA == 0)
+// or into a U-slot LDS ring of its own by LDS-DMA (DMA == 1, waiting before a
+// slot is reused). For the scaling of the read rate with waves per compute
+// unit and copies in flight per wave.
+template <int THREADS, int U, int DMA>
+__global__ __launch_bounds__(THREADS) void wave_read_kernel(const uint8_t* src, int64_t pieces, uint32_t* sink,
+                                                            uint32_t key) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
+  constexpr int NWV = THREADS / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t stride = (int64_t)gridDim.x * NWV;
+  uint32_t acc = 0;
+  int64_t p0 = (int64_t)blockIdx.x * NWV + wave;
+  if constexpr (DMA == 0) {
+    for (; p0 < pieces; p0 += stride * U) {
+      uint4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        int64_t q = p0 + u * stride;
+        q = q < pieces ? q : pieces - 1;
+        v[u] = load16_nt(src + q * 1024 + lane * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+  } else {
+    const uint32_t base = (uint32_t)(uintptr_t)ring + (uint32_t)wave * U * 1024;
+    int slot = 0;
+    for (; p0 < pieces; p0 += stride) {
+      const uint32_t m0v = __builtin_amdgcn_readfirstlane(base + (uint32_t)slot * 1024);
+      const uint8_t* g = src + p0 * 1024 + lane * 16;
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0v) : "memory", "m0");
+      slot = slot + 1 == U ? 0 : slot + 1;
+      // at most U - 1 of this wave's pieces in flight: the slot issued next
+      // has landed
+      __builtin_amdgcn_s_waitcnt(((U - 1) & 15) | (((U - 1) >> 4) << 14) | (7 << 4) | (15 << 8));
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    acc = *reinterpret_cast<const uint32_t*>(ring + wave * U * 1024 + (lane & 15) * 16);
+  }
+  if (acc == key) sink[blockIdx.x * THREADS + threadIdx.x] = acc;
+}
+
+template <int THREADS, int U, int DMA>
+hipError_t launch_wave_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t stream) {
+  auto kern = wave_read_kernel<THREADS, U, DMA>;
+  const size_t lds = DMA ? (size_t)(THREADS / 64) * U * 1024 : 0;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)workgroups), dim3(THREADS), lds, stream,
+                     static_cast<const uint8_t*>(src), (int64_t)(bytes / 1024), sink, 0x9E3779B9u);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_wave_read(const void* src, size_t bytes, int threads, int depth, int dma, uint32_t* sink,
+                                  int workgroups, hipStream_t stream) {
+#define FP8_WAVE_READ(T, U)                                                           \
+  if (threads == T && depth == U)                                                     \
+    return dma ? launch_wave_read<T, U, 1>(src, bytes, sink, workgroups, stream)      \
+               : launch_wave_read<T, U, 0>(src, bytes, sink, workgroups, stream);
+  FP8_WAVE_READ(256, 4) FP8_WAVE_READ(256, 8) FP8_WAVE_READ(256, 16)
+  FP8_WAVE_READ(512, 4) FP8_WAVE_READ(512, 8) FP8_WAVE_READ(512, 16)
+  FP8_WAVE_READ(1024, 4) FP8_WAVE_READ(1024, 8)
+#undef FP8_WAVE_READ
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_probe_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups,
                                     hipStream_t stream) {
   hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)workgroups), dim3(kProbeThreads), 0, stream,

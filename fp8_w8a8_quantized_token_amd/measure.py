@@ -475,6 +475,23 @@ def measure_probes(warmup, calls, filler):
                      f"{size / us / 1e3:.0f} GB/s ({size / us / 1e3 / PEAK_GBPS:.2f} of 8 TB/s)", f"{sets} buffers")
         del bufs
         torch.cuda.empty_cache()
+    # read rate against waves per compute unit and pieces in flight per wave
+    size = 50331648
+    sets = max(2, min(MAX_SETS, math.ceil(ROTATE_BYTES / size)))
+    bufs = [torch.full((size // 4,), i, dtype=torch.int32, device=dev) for i in range(sets)]
+    for dma in (0, 1):
+        for threads, depth in ((256, 4), (256, 8), (256, 16), (512, 4), (512, 8), (512, 16), (1024, 4), (1024, 8)):
+            for wgs in (256, 512):
+                fns = [lambda b=b, t=threads, d=depth, w=wgs, dm=dma: _lib.check(lib.fp8_probe_wave_read(
+                    ctypes.c_void_p(b.data_ptr()), size, t, d, dm, sp, w, stream())) for b in bufs]
+                us = _batch_us(fns, warmup, calls, filler)
+                waves_cu = wgs * threads // 64 // 256
+                emit("HBM read by waves (cold)", f"{size / 1e6:.1f} MB", f"{wgs}x{threads}", f"{us:.2f}",
+                     f"{size / us / 1e3:.0f} GB/s ({size / us / 1e3 / PEAK_GBPS:.2f})",
+                     f"{'LDS-DMA' if dma else 'register'}; {waves_cu} waves/CU x {depth} KB in flight "
+                     f"= {waves_cu * depth} KB/CU")
+    del bufs
+    torch.cuda.empty_cache()
     # L2 -> compute unit feed: every workgroup re-reads a 512 KB window
     win = 512 << 10
     src = torch.full((win // 4,), 3, dtype=torch.int32, device=dev)

@@ -545,6 +545,15 @@ int fp8_probe_l2_feed(const void* src, size_t window_bytes, int32_t reps, int32_
  * is the clock the matrix cores ran at. */
 int fp8_probe_mfma(int32_t iters, float* sink, int32_t workgroups, hipStream_t stream);
 
+/* Reads `bytes` (a multiple of 1 KB) once in 1 KB pieces, each wave of
+ * `workgroups` workgroups of `threads` threads (256, 512 or 1024) keeping
+ * `depth` pieces in flight (4, 8 or 16; 4 or 8 at 1024 threads): into
+ * registers (dma == 0) or, by LDS-DMA, into a depth-slot LDS ring per wave
+ * (dma != 0). How the HBM read rate scales with waves per compute unit and
+ * copies in flight per wave. */
+int fp8_probe_wave_read(const void* src, size_t bytes, int32_t threads, int32_t depth, int32_t dma,
+                        uint32_t* sink, int32_t workgroups, hipStream_t stream);
+
 /* LDS read rate: every lane of `workgroups` workgroups of `threads` (256 or
  * 512) threads reads 16 bytes per step (ds_read_b128, a wave reading one
  * contiguous 1 KB row: no bank conflicts), iters * 8 steps. Bytes read =

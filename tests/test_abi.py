@@ -308,6 +308,8 @@ def test_probe_argument_errors(lib):
     assert lib.fp8_probe_l2_feed(FAKE, 1000, 4, 0, FAKE, 4, None) == _lib.FP8_ERR_INVALID
     assert lib.fp8_probe_mfma(0, FAKE, 4, None) == _lib.FP8_ERR_INVALID
     assert lib.fp8_probe_lds(4, 128, FAKE, 4, None) == _lib.FP8_ERR_INVALID
+    assert lib.fp8_probe_wave_read(FAKE, 1 << 20, 1024, 16, 0, FAKE, 4, None) == _lib.FP8_ERR_INVALID
+    assert lib.fp8_probe_wave_read(FAKE, 1000, 256, 8, 1, FAKE, 4, None) == _lib.FP8_ERR_INVALID
 
 
 # ---------------------------------------------------------------- tile table
