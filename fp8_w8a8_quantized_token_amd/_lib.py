@@ -36,7 +36,8 @@ VARIANTS = {"default": -1, "skinny": 0, "t64x64": 1, "t128x128": 2, "t256x128": 
             "t128x128panel": 16, "t128x64panel": 17, "t64x64panel": 18,
             "t64x64deep": 19, "t128x64deep": 20,
             "t128x128panel8": 21, "t128x64panel8": 22,
-            "t32x32deep": 23, "t64x32deep": 24, "t256x256bw16": 25}
+            "t32x32deep": 23, "t64x32deep": 24, "t256x256bw16": 25,
+            "decode": 26}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 
 
@@ -107,6 +108,7 @@ SIGNATURES = {
     "fp8_probe_mfma": (c_i32, [c_i32, c_vp, c_i32, c_vp]),
     "fp8_probe_wave_read": (c_i32, [c_vp, c_size, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp]),
     "fp8_probe_lds": (c_i32, [c_i32, c_i32, c_vp, c_i32, c_vp]),
+    "fp8_probe_mfma_dot": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp]),
     "fp8_last_error": (ctypes.c_char_p, []),
     "fp8_version": (c_i32, []),
 }

@@ -86,7 +86,8 @@ int resolve_config(int kind, int64_t M, int64_t N, int64_t K, const fp8_tile_con
   if (!cfg || cfg->variant == FP8_VARIANT_DEFAULT) {
     lookup_config(kind, N, K, M, out);
     // a table entry snapped from a nearby M may not fit this M
-    if (out->variant == FP8_VARIANT_SKINNY && M > variant_info(FP8_VARIANT_SKINNY).bm)
+    if ((out->variant == FP8_VARIANT_SKINNY || out->variant == FP8_VARIANT_DECODE) &&
+        (M > variant_info(out->variant).bm || (out->variant == FP8_VARIANT_DECODE && K % 128 != 0)))
       default_config(kind, N, K, M, out);
     return FP8_OK;
   }
@@ -95,6 +96,8 @@ int resolve_config(int kind, int64_t M, int64_t N, int64_t K, const fp8_tile_con
   if (cfg->split_k < 1) return fail(FP8_ERR_INVALID, "split_k must be >= 1");
   if (cfg->variant == FP8_VARIANT_SKINNY && (M > vi.bm || cfg->split_k != 1))
     return fail(FP8_ERR_INVALID, "the skinny variant takes M <= %d and split_k == 1", vi.bm);
+  if (cfg->variant == FP8_VARIANT_DECODE && (M > vi.bm || K % 128 != 0 || cfg->split_k != 1))
+    return fail(FP8_ERR_INVALID, "the decode variant takes M <= %d, K %% 128 == 0 and split_k == 1", vi.bm);
   *out = *cfg;
   out->bm = vi.bm; out->bn = vi.bn; out->bk = vi.bk; out->waves = vi.waves;
   return FP8_OK;
@@ -124,7 +127,8 @@ int run_gemm(const char* fn, int kind, const uint8_t* a, const uint8_t* b, const
   p.a = a; p.b = b; p.sa = sa; p.sa_ld = sa_ld; p.sb = sb; p.bias = bias; p.out = out;
   p.M = M; p.N = N; p.K = K; p.lda = lda; p.ldb = ldb; p.ldc = ldc;
   int splits = 1, per = (int)((K + 127) / 128);
-  if (cfg.variant != FP8_VARIANT_SKINNY) split_plan(K, cfg.bk, cfg.split_k, &splits, &per);
+  if (cfg.variant != FP8_VARIANT_SKINNY && cfg.variant != FP8_VARIANT_DECODE)
+    split_plan(K, cfg.bk, cfg.split_k, &splits, &per);
   p.split_k = splits;
   p.k_tiles_per_split = per;
   if (splits > 1) {
@@ -479,7 +483,7 @@ size_t fp8_scaled_mm_workspace_size(int32_t kind, int64_t M, int64_t N, int64_t 
   if (M == 0 || N == 0 || K == 0) return 0;
   fp8_tile_config cfg;
   if (resolve_config(kind, M, N, K, cfg_in, &cfg)) return (size_t)-1;
-  if (cfg.variant == FP8_VARIANT_SKINNY) return 0;
+  if (cfg.variant == FP8_VARIANT_SKINNY || cfg.variant == FP8_VARIANT_DECODE) return 0;
   int splits, per;
   split_plan(K, cfg.bk, cfg.split_k, &splits, &per);
   return variant_workspace_bytes(cfg.variant, splits, M, N);
@@ -611,6 +615,15 @@ int fp8_probe_lds(int32_t iters, int32_t threads, uint32_t* sink, int32_t workgr
   if (!sink || iters < 1 || workgroups < 1 || (threads != 256 && threads != 512))
     return fail(FP8_ERR_INVALID, "%s: iters and workgroups >= 1, threads 256 or 512, sink non-null", fn);
   return hip_status(launch_probe_lds(iters, threads, sink, workgroups, stream), fn);
+}
+
+int fp8_probe_mfma_dot(const void* w, const void* x, const float* c, float* d, int32_t count, int32_t form,
+                       hipStream_t stream) {
+  const char* fn = "fp8_probe_mfma_dot";
+  if (!w || !x || !c || !d || count < 1 || count > 65535 || (form != 0 && form != 1) || !aligned(w, 16) ||
+      !aligned(x, 16))
+    return fail(FP8_ERR_INVALID, "%s: non-null 16-byte-aligned operands, 1 <= count <= 65535, form 0 or 1", fn);
+  return hip_status(launch_probe_mfma_dot(w, x, c, d, count, form, stream), fn);
 }
 
 const char* fp8_last_error(void) { return g_last_error.c_str(); }

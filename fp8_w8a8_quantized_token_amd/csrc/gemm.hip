@@ -1237,6 +1237,166 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   }
 }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n in [LO, HI] (a branch tree over
+// the immediate forms); n above HI waits for HI, which only waits longer.
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  if constexpr (LO == HI) {
+    wait_vmcnt<LO>();
+  } else {
+    constexpr int MID = (LO + HI) / 2;
+    if (n <= MID) wait_vmcnt_upto<LO, MID>(n);
+    else wait_vmcnt_upto<MID + 1, HI>(n);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode-size weight stream (M <= 16, K % 128 == 0). One workgroup of 8 waves
+// per 16 weight rows (16 output columns), walking K in 1 KB stages (eight
+// 128-deep K blocks, one V_MFMA_F32_16X16X128_F8F6F4 each; which wave
+// multiplies which block is set out below). The stages travel by LDS-DMA straight into
+// an LDS ring (no register staging) -- the weight rows as contiguous 1 KB
+// row segments, the M activation rows beside them -- with all but one of
+// the ring's slots in flight; a measured LDS-DMA stream of 1 KB pieces
+// reads at 0.64 of HBM peak from only 16 KB in flight per compute unit. Inside a segment the
+// lane fetches the 16-byte chunk that belongs at its LDS position: chunk c of
+// row r sits at position c ^ r, so the 16 rows of a fragment read hit
+// distinct banks. Activation rows at or past M are read as row M - 1 (their
+// outputs are never stored). The ring depth is a launch parameter: where the
+// grid covers the compute units once, the deepest ring the LDS holds (the
+// whole weight share of a workgroup in flight); beyond, a ring of at most
+// 80 KB, so that two workgroups share a compute unit and one's latency hides
+// behind the other's stream. Each wave counts the copies it issued (two
+// weight rows, and activation rows w and w + 8 below M) and waits for its own
+// copies of a stage before the stage's barrier. The blockwise scales of the
+// whole K range go to LDS before the first copy is issued, so no compiler
+// wait for an ordinary load can also hold back the copies. The eight waves'
+// partial tiles are summed through LDS in wave order (deterministic).
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kDecWaves = 8;
+constexpr int kDecStageK = kDecWaves * 128;  // K bytes per stage
+constexpr int kDecMaxSlots = 8;
+}  // namespace
+
+// LDS bytes of the decode kernel's scale table (blockwise) and of one ring slot.
+__host__ __device__ inline size_t decode_scale_bytes(int64_t K, int kind) {
+  return kind != kChannelwise ? (size_t)(K / 128) * 17 * 4 : 0;
+}
+__host__ __device__ inline size_t decode_slot_bytes(int64_t M) { return (size_t)(16 + M) * 1024; }
+
+template <int KIND>
+__global__ __launch_bounds__(kDecWaves * 64) void gemm_decode_kernel(GemmArgs p) {
+  static_assert(KIND == kChannelwise || KIND == kBlockwise, "fp32 scales");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int M = (int)p.M;
+  const uint32_t slot_bytes = (uint32_t)(16 + M) * 1024;
+  const int ns = p.ring_slots;  // 2 .. kDecMaxSlots
+  const int64_t kb_all = p.K / 128;
+  const int nst = (int)((p.K + kDecStageK - 1) / kDecStageK);
+  // blockwise: scale of (row r, block kb) at sc[17 kb + r] (0 for rows >= M),
+  // the weight block scale of block kb at sc[17 kb + 16]
+  float* sc = reinterpret_cast<float*>(lds + (size_t)ns * slot_bytes);
+  if constexpr (KIND == kBlockwise) {
+    const int64_t nb = n0 >> 7;
+    for (int64_t i = tid; i < kb_all * 17; i += kDecWaves * 64) {
+      const int64_t kb = i / 17;
+      const int r = (int)(i - kb * 17);
+      sc[i] = r < 16 ? (r < M ? p.sa[kb * p.sa_ld + r] : 0.0f) : p.sb[nb * kb_all + kb];
+    }
+    __syncthreads();
+  }
+
+  // this wave's copies per stage: weight rows 2w, 2w+1; activation rows w, w+8 below M
+  const int cnt = 2 + (wave < M ? 1 : 0) + (wave + 8 < M ? 1 : 0);
+  auto issue = [&](int s) {
+    const uint32_t slot = lds_base + (uint32_t)(s % ns) * slot_bytes;
+    const int64_t k0 = (int64_t)s * kDecStageK;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = 2 * wave + rr;
+      int64_t n = n0 + r;
+      n = n < p.N ? n : p.N - 1;
+      int64_t kc = k0 + (int64_t)(lane ^ r) * 16;
+      kc = kc < p.K - 16 ? kc : p.K - 16;
+      lds_dma16_s(p.b, (uint32_t)(n * p.ldb + kc), slot + (uint32_t)r * 1024);
+    }
+#pragma unroll
+    for (int ra = 0; ra < 2; ++ra) {
+      const int r = wave + 8 * ra;
+      if (r < M) {
+        int64_t kc = k0 + (int64_t)(lane ^ r) * 16;
+        kc = kc < p.K - 16 ? kc : p.K - 16;
+        lds_dma16_s(p.a, (uint32_t)(r * p.lda + kc), slot + (uint32_t)(16 + r) * 1024);
+      }
+    }
+  };
+
+  // K blocks: as in the register-staged weight-streaming kernel, wave w takes
+  // blocks 4w .. 4w+3 of every 4 KB of K, in that order, so that the fp32 sums
+  // and the outputs are bit-identical to its (and to the single-launch
+  // linear's); those four blocks are the half (w & 1) of stage 4c + (w >> 1).
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int am = r16 < M ? r16 : M - 1;  // activation row this lane reads
+  uint32_t fb[4][2], fa[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int c = 8 * (4 * (wave & 1) + j) + 2 * g + t;  // lane's 16-byte chunk of block j
+      fb[j][t] = (uint32_t)r16 * 1024 + ((c ^ r16) << 4);
+      fa[j][t] = (uint32_t)(16 + am) * 1024 + ((c ^ am) << 4);
+    }
+
+  for (int s = 0; s < ns - 1 && s < nst; ++s) issue(s);
+  for (int s = 0; s < nst; ++s) {
+    // this wave's copies of stage s have landed; those of later stages may not
+    const int last = s + ns - 2 < nst - 1 ? s + ns - 2 : nst - 1;
+    wait_vmcnt_upto<0, 63>((last - s) * cnt);
+    wait_vmcnt_lgkm0<63>();
+    __builtin_amdgcn_s_barrier();
+    // every wave is past stage s-1: its slot takes stage s + ns - 1
+    if (s + ns - 1 < nst) issue(s + ns - 1);
+    if ((s & 3) == (wave >> 1)) {
+      const uint8_t* slot = lds + (size_t)(s % ns) * slot_bytes;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t kb = (int64_t)s * kDecWaves + 4 * (wave & 1) + j;
+        if (kb >= kb_all) break;
+        const i32x8 bf = join(*reinterpret_cast<const uint4*>(slot + fb[j][0]),
+                              *reinterpret_cast<const uint4*>(slot + fb[j][1]));
+        const i32x8 af = join(*reinterpret_cast<const uint4*>(slot + fa[j][0]),
+                              *reinterpret_cast<const uint4*>(slot + fa[j][1]));
+        if constexpr (KIND == kChannelwise) {
+          acc = mfma_fp8(bf, af, acc);
+        } else {
+          const f32x4 part = mfma_fp8(bf, af, f32x4{0.f, 0.f, 0.f, 0.f});
+          acc += part * (sc[kb * 17 + r16] * sc[kb * 17 + 16]);
+        }
+      }
+    }
+  }
+
+  // the eight partial tiles summed through LDS in wave order
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(lds);  // [wave][64]
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  f32x4 sum = red[lane];
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) sum += red[w * 64 + lane];
+  const int64_t m = r16;
+  const float sa_m = (KIND == kChannelwise && m < p.M) ? p.sa[m] : 1.0f;
+  store_out4<KIND>(p, m, n0 + 4 * g, sum, sa_m);
+}
+
 // ---------------------------------------------------------------------------
 // Skinny kernel for M <= 16*MT: the weight is streamed from HBM exactly once.
 // A workgroup of 8 waves owns one 16-row weight tile (16 output columns) and
@@ -1608,6 +1768,41 @@ hipError_t launch_panel(const GemmArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The decode stream takes whole 128-deep K blocks and 32-bit DMA offsets.
+bool decode_eligible(const GemmArgs& p) {
+  const uint64_t lim = 0xFFFFFFFFull - 1024;
+  return p.K % 128 == 0 && (uint64_t)(p.N - 1) * (uint64_t)p.ldb <= lim && (uint64_t)15 * (uint64_t)p.lda <= lim;
+}
+
+template <int KIND>
+hipError_t launch_decode(const GemmArgs& p, hipStream_t stream) {
+  auto kern = gemm_decode_kernel<KIND>;
+  static bool lds_attr_set = false;
+  if (!lds_attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+    if (e != hipSuccess) return e;
+    lds_attr_set = true;
+  }
+  // Ring depth, measured: with one round of workgroups over the compute units
+  // four slots (deeper rings were slower); with more workgroups than compute
+  // units as many slots as fit 80 KB, so two workgroups share a compute unit.
+  const int64_t tiles = (p.N + 15) / 16;
+  const size_t fixed = decode_scale_bytes(p.K, KIND), slot = decode_slot_bytes(p.M);
+  const size_t budget = (tiles <= 256 ? (size_t)163840 : (size_t)81920);
+  int64_t ns = budget > fixed ? (int64_t)((budget - fixed) / slot) : 0;
+  const int64_t nst = (p.K + kDecStageK - 1) / kDecStageK;
+  if (ns > nst + 1) ns = nst + 1;  // no slot beyond the stages there are
+  if (ns > (tiles <= 256 ? 4 : kDecMaxSlots)) ns = tiles <= 256 ? 4 : kDecMaxSlots;
+  if (ns < 2) ns = 2;
+  const size_t lds = (size_t)ns * slot + fixed;
+  if (lds > 163840) return hipErrorInvalidValue;
+  GemmArgs q = p;
+  q.ring_slots = (int)ns;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kDecWaves * 64), lds, stream, q);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, int NSTAGE>
 hipError_t launch_dma(const GemmArgs& p, hipStream_t stream) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
@@ -1730,6 +1925,12 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
     case 25:
       if (KIND == kBlockwise || !panel_eligible<KIND>(p)) return launch_256<KIND>(p, stream);
       return launch_panel<256, 256, 2, 4, kChannelwise, 5>(p, stream);
+    case 26:  // FP8_VARIANT_DECODE; past its DMA offsets the skinny kernel (same sums)
+      if (p.M > 16) return hipErrorInvalidValue;
+      if (decode_eligible(p)) return launch_decode<KIND>(p, stream);
+      hipLaunchKernelGGL((gemm_skinny_kernel<1, KIND, 0>), dim3((unsigned)((p.N + 15) / 16)),
+                         dim3(kStreamWaves * 64), 0, stream, p, QuantArgs{});
+      return hipGetLastError();
     default: return hipErrorInvalidValue;
   }
 }
@@ -1777,6 +1978,7 @@ VariantInfo variant_info(int variant) {
     case 23: return {32, 32, 128, 1, true};
     case 24: return {64, 32, 128, 2, true};
     case 25: return {256, 256, 128, 8, true};
+    case 26: return {16, 16, 1024, 8, true};
     default: return {0, 0, 0, 0, false};
   }
 }
@@ -1784,12 +1986,12 @@ VariantInfo variant_info(int variant) {
 int64_t variant_tiles(int variant, int64_t M, int64_t N) {
   const VariantInfo v = variant_info(variant);
   if (!v.exists) return 0;
-  if (variant == 0) return (N + 15) / 16;
+  if (variant == 0 || variant == 26) return (N + 15) / 16;
   return ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
 }
 
 size_t variant_workspace_bytes(int variant, int split_k, int64_t M, int64_t N) {
-  if (split_k <= 1 || variant == 0) return 0;
+  if (split_k <= 1 || variant == 0 || variant == 26) return 0;
   const VariantInfo v = variant_info(variant);
   const int64_t tiles = variant_tiles(variant, M, N);
   return kCounterBytes + (size_t)tiles * split_k * v.bm * v.bn * sizeof(float);

@@ -62,6 +62,8 @@ struct GemmArgs {
   const int* masked_m;
   int experts;
   int64_t a_es, sa_es, b_es, sb_es, out_es;
+  // decode weight stream (M <= 16): LDS ring slots, set by its launcher
+  int ring_slots;
 };
 
 
@@ -135,6 +137,8 @@ hipError_t launch_probe_l2_feed(const void* src, size_t window, int reps, int dm
 hipError_t launch_probe_mfma(int iters, float* sink, int workgroups, hipStream_t stream);
 hipError_t launch_probe_wave_read(const void* src, size_t bytes, int threads, int depth, int dma, uint32_t* sink,
                                   int workgroups, hipStream_t stream);
+hipError_t launch_probe_mfma_dot(const void* w, const void* x, const float* c, float* d, int count, int form,
+                                 hipStream_t stream);
 hipError_t launch_probe_lds(int iters, int threads, uint32_t* sink, int workgroups, hipStream_t stream);
 
 }  // namespace fp8w8a8

@@ -251,6 +251,59 @@ hipError_t launch_probe_wave_read(const void* src, size_t bytes, int threads, in
   return hipErrorInvalidValue;
 }
 
+// One MFMA per wave on given operands, D = W X^T + C, in the operand layout
+// the GEMM kernels use. FORM 0: V_MFMA_F32_16X16X128_F8F6F4, W and X [16][128]
+// E4M3 codes, C and D [16][16] fp32 (element [n][m]: row n of W, row m of X);
+// lane l supplies row l % 16 and the K bytes [32 (l / 16), +32) of both
+// operands and owns D[4 (l / 16) + v][l % 16]. FORM 1:
+// V_MFMA_F32_32X32X64_F8F6F4, W and X [32][64], C and D [32][32]; lane l
+// supplies row l % 32 and K bytes [32 (l / 32), +32) and owns
+// D[8 q + 4 (l / 32) + v][l % 32] in accumulator 4 q + v. Shows the matrix
+// core's own rounding of an FP8 dot product and of its addition to C.
+template <int FORM>
+__global__ __launch_bounds__(64) void mfma_dot_probe_kernel(const uint8_t* w, const uint8_t* x, const float* c,
+                                                            float* d) {
+  constexpr int R = FORM == 0 ? 16 : 32, KD = FORM == 0 ? 128 : 64;
+  const int lane = threadIdx.x, r = lane % R, g = lane / R;
+  const size_t op = (size_t)blockIdx.x * R * KD, mat = (size_t)blockIdx.x * R * R;
+  const uint4* wp = reinterpret_cast<const uint4*>(w + op + (size_t)r * KD + 32 * g);
+  const uint4* xp = reinterpret_cast<const uint4*>(x + op + (size_t)r * KD + 32 * g);
+  const uint4 w0 = wp[0], w1 = wp[1], x0 = xp[0], x1 = xp[1];
+  i32x8 wv, xv;
+  wv[0] = (int)w0.x; wv[1] = (int)w0.y; wv[2] = (int)w0.z; wv[3] = (int)w0.w;
+  wv[4] = (int)w1.x; wv[5] = (int)w1.y; wv[6] = (int)w1.z; wv[7] = (int)w1.w;
+  xv[0] = (int)x0.x; xv[1] = (int)x0.y; xv[2] = (int)x0.z; xv[3] = (int)x0.w;
+  xv[4] = (int)x1.x; xv[5] = (int)x1.y; xv[6] = (int)x1.z; xv[7] = (int)x1.w;
+  if constexpr (FORM == 0) {
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    f32x4v acc;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] = c[mat + (size_t)(4 * g + v) * R + r];
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, xv, acc, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) d[mat + (size_t)(4 * g + v) * R + r] = acc[v];
+  } else {
+    typedef float f32x16v __attribute__((ext_vector_type(16)));
+    f32x16v acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = c[mat + (size_t)(8 * (i >> 2) + 4 * g + (i & 3)) * R + r];
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, xv, acc, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) d[mat + (size_t)(8 * (i >> 2) + 4 * g + (i & 3)) * R + r] = acc[i];
+  }
+}
+
+hipError_t launch_probe_mfma_dot(const void* w, const void* x, const float* c, float* d, int count, int form,
+                                 hipStream_t stream) {
+  if (form == 0)
+    hipLaunchKernelGGL(mfma_dot_probe_kernel<0>, dim3((unsigned)count), dim3(64), 0, stream,
+                       static_cast<const uint8_t*>(w), static_cast<const uint8_t*>(x), c, d);
+  else
+    hipLaunchKernelGGL(mfma_dot_probe_kernel<1>, dim3((unsigned)count), dim3(64), 0, stream,
+                       static_cast<const uint8_t*>(w), static_cast<const uint8_t*>(x), c, d);
+  return hipGetLastError();
+}
+
 hipError_t launch_probe_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups,
                                     hipStream_t stream) {
   hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)workgroups), dim3(kProbeThreads), 0, stream,

@@ -192,6 +192,7 @@ int variant_from_name(const std::string& n) {
   if (n == "t32x32deep") return FP8_VARIANT_T32x32DEEP;
   if (n == "t64x32deep") return FP8_VARIANT_T64x32DEEP;
   if (n == "t256x256bw16") return FP8_VARIANT_T256x256BW16;
+  if (n == "decode") return FP8_VARIANT_DECODE;
   return -100;
 }
 

@@ -104,7 +104,12 @@ enum {
   FP8_VARIANT_T32x32DEEP = 23,     /* 32x32 block tile, 1 wave, 9-slot ring */
   FP8_VARIANT_T64x32DEEP = 24,     /* 64x32 block tile, 2 waves, 7-slot ring */
   FP8_VARIANT_T256x256BW16 = 25,   /* blockwise 256x256, 8 waves, 16x16x128 MFMAs, 4-slot ring */
-  FP8_VARIANT_COUNT = 26,
+  /* M <= 16, K % 128 == 0: the weight stream of the skinny variant (same K
+   * order and sums, so the same bits) with 1 KB row segments copied by
+   * LDS-DMA into a ring of 2-8 slots; split_k 1. Requests past its 32-bit
+   * DMA offsets run the skinny kernel. */
+  FP8_VARIANT_DECODE = 26,         /* 16 output columns per workgroup, 8 waves */
+  FP8_VARIANT_COUNT = 27,
 };
 
 /* One tile configuration of the scaled GEMM. The PR34331 digest ("Key source
@@ -559,6 +564,17 @@ int fp8_probe_wave_read(const void* src, size_t bytes, int32_t threads, int32_t 
  * contiguous 1 KB row: no bank conflicts), iters * 8 steps. Bytes read =
  * workgroups * threads * iters * 128. */
 int fp8_probe_lds(int32_t iters, int32_t threads, uint32_t* sink, int32_t workgroups, hipStream_t stream);
+
+/* `count` independent MFMAs, one wave each: for problem i, D_i = W_i X_i^T +
+ * C_i. form 0: V_MFMA_F32_16X16X128_F8F6F4, W_i and X_i [16][128] E4M3 codes,
+ * C_i and D_i [16][16] fp32; form 1: V_MFMA_F32_32X32X64_F8F6F4, W_i and X_i
+ * [32][64], C_i and D_i [32][32]. All row-major and consecutive over i;
+ * element [n][m] of C and D pairs row n of W with row m of X. The matrix
+ * core's own rounding of an FP8 dot product and of its addition to the
+ * accumulator, which sets the error model of every GEMM here. w and x 16-byte
+ * aligned; 1 <= count <= 65535. */
+int fp8_probe_mfma_dot(const void* w, const void* x, const float* c, float* d, int32_t count, int32_t form,
+                       hipStream_t stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* fp8_last_error(void);

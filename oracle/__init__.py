@@ -58,5 +58,12 @@ from .gemm import (  # noqa: F401
     summation_bound_blockwise,
     summation_bound_channelwise,
 )
-from .check import check_gemm  # noqa: F401
+from .check import (  # noqa: F401
+    Tolerance,
+    check_gemm,
+    gemm_tolerance_blockwise,
+    gemm_tolerance_channelwise,
+    mfma_truncation_blockwise,
+    mfma_truncation_channelwise,
+)
 from .moe import masked_quant_per_token_group, scaled_mm_blockwise_masked  # noqa: F401

@@ -27,17 +27,115 @@ is passed:
 * the pure relative criterion ``|out - ref| <= 2^-6 |ref|`` may fail only on
   a small fraction of the elements (``max_pure_rel_frac``, 1%): those whose
   true value is cancelled far below the size of its terms.
+
+The matrix core does not sum a 128-term FP8 dot product in IEEE fp32. Measured
+on gfx950 (V_MFMA_F32_16X16X128_F8F6F4, through the library's MFMA probe and
+pinned by a GPU test): the products of each run of 8 consecutive K positions
+are aligned to the largest of them and truncated toward zero below 2^-13 of
+its leading bit (a product 2^-14 of a larger one in its run is lost, one
+2^-13 below is kept, one in another run is kept); the runs' sums and the
+accumulator input are then added with fp32-like precision. So each product of
+a run whose largest magnitude is t_max errs by less than 2^-13 t_max, which
+``gemm_tolerance_*`` adds to tau: with a_g, b_g the largest magnitudes of the
+run in A and B (t_max <= a_g b_g), 7 2^-13 sum_runs a_g b_g (only 7 of the 8
+products can lose bits) times the scales, and, for the floor, Hoeffding's
+bound for the sum of these bounded errors: lambda 2^-13 sqrt(7 sum_runs
+(a_g b_g)^2) times the scales (the errors' signs follow the products', which
+are independent on the random workloads). On N(0, 1)-like operands this floor
+is about 0.4% of a typical |ref| whatever K, below the 2^-6 criterion.
 """
 
 import math
+from typing import NamedTuple
 
 import numpy as np
 
+from .e4m3 import decode
+from .gemm import summation_bound_blockwise, summation_bound_channelwise
+
 PROB_LAMBDA = 8.0
+MFMA_RUN = 8           # K positions the matrix core aligns together
+MFMA_KEEP_BITS = 13    # bits kept below the leading bit of the run's largest product
+
+
+class Tolerance(NamedTuple):
+    """Per-element error allowances of a GEMM output (beyond 2^-6 |ref|):
+    ``tau`` the worst case, ``floor`` the probabilistic one."""
+    tau: np.ndarray
+    floor: np.ndarray
+
+
+def _run_abs_max(codes) -> np.ndarray:
+    """|dec(codes)| [R, K] -> [R, ceil(K / 8)]: the largest magnitude of every
+    run of 8 consecutive K positions (zero-padded at the end)."""
+    x = np.abs(decode(codes))
+    r, k = x.shape
+    kp = -(-k // MFMA_RUN) * MFMA_RUN
+    y = np.zeros((r, kp))
+    y[:, :k] = x
+    return y.reshape(r, kp // MFMA_RUN, MFMA_RUN).max(axis=2)
+
+
+def mfma_truncation_channelwise(a_codes, b_codes, a_scale, b_scale):
+    """(tau_t, sigma_t) [M, N]: the matrix core's truncation bound and the
+    Hoeffding scale of its sum, channelwise scales applied."""
+    ag, bg = _run_abs_max(a_codes), _run_abs_max(b_codes)
+    s = np.abs(np.asarray(a_scale, np.float64))[:, None] * np.abs(np.asarray(b_scale, np.float64))[None, :]
+    c = 2.0 ** -MFMA_KEEP_BITS
+    lossy = MFMA_RUN - 1
+    tau_t = lossy * c * (ag @ bg.T) * s
+    sigma_t = c * np.sqrt(lossy * ((ag ** 2) @ (bg ** 2).T)) * s
+    return tau_t, sigma_t
+
+
+def mfma_truncation_blockwise(a_codes, b_codes, a_scale, b_scale, block_n: int = 128, block_k: int = 128):
+    """As mfma_truncation_channelwise with a_scale [M, ceil(K/128)] and b_scale
+    [ceil(N/128), ceil(K/128)] applied per K block."""
+    ag, bg = _run_abs_max(a_codes), _run_abs_max(b_codes)
+    a_scale = np.abs(np.asarray(a_scale, np.float64))
+    b_scale = np.abs(np.asarray(b_scale, np.float64))
+    n = bg.shape[0]
+    nb = np.arange(n) // block_n
+    per = block_k // MFMA_RUN
+    c = 2.0 ** -MFMA_KEEP_BITS
+    lossy = MFMA_RUN - 1
+    tau_t = np.zeros((ag.shape[0], n))
+    var = np.zeros((ag.shape[0], n))
+    for kb in range(a_scale.shape[1]):
+        g = slice(kb * per, min(ag.shape[1], (kb + 1) * per))
+        s = a_scale[:, kb][:, None] * b_scale[nb, kb][None, :]
+        tau_t += lossy * c * (ag[:, g] @ bg[:, g].T) * s
+        var += lossy * c * c * ((ag[:, g] ** 2) @ (bg[:, g] ** 2).T) * s * s
+    return tau_t, np.sqrt(var)
+
+
+def _tolerance(tau32, trunc, k) -> Tolerance:
+    tau_t, sigma_t = trunc
+    floor = tau32 * (PROB_LAMBDA / (2.0 * math.sqrt(float(k)))) + PROB_LAMBDA * sigma_t
+    return Tolerance(tau32 + tau_t, floor)
+
+
+def gemm_tolerance_channelwise(a_codes, b_codes, a_scale, b_scale) -> Tolerance:
+    """fp32 accumulation (worst case and Higham-Mary floor) plus the matrix
+    core's truncation (worst case and Hoeffding floor)."""
+    k = np.asarray(a_codes).shape[1]
+    return _tolerance(summation_bound_channelwise(a_codes, b_codes, a_scale, b_scale),
+                      mfma_truncation_channelwise(a_codes, b_codes, a_scale, b_scale), k)
+
+
+def gemm_tolerance_blockwise(a_codes, b_codes, a_scale, b_scale) -> Tolerance:
+    k = np.asarray(a_codes).shape[1]
+    return _tolerance(summation_bound_blockwise(a_codes, b_codes, a_scale, b_scale),
+                      mfma_truncation_blockwise(a_codes, b_codes, a_scale, b_scale), k)
 
 
 def check_gemm(out, ref, tau, rel: float = 2.0 ** -6, max_frac: float = 1e-2, k=None,
                max_pure_rel_frac: float = 1e-2) -> dict:
+    """tau: a Tolerance (worst case and floor), or the fp32 worst case alone,
+    whose floor then needs the depth k of the sum."""
+    floor = None
+    if isinstance(tau, Tolerance):
+        tau, floor = np.asarray(tau.tau, np.float64), np.asarray(tau.floor, np.float64)
     out = np.asarray(out, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     tau = np.asarray(tau, dtype=np.float64)
@@ -59,8 +157,9 @@ def check_gemm(out, ref, tau, rel: float = 2.0 ** -6, max_frac: float = 1e-2, k=
         "frac_pure_rel_fail": pure_rel_fail,
         "cosine": cosine,
     }
-    if k is not None and err.size:
+    if floor is None and k is not None:
         floor = tau * (PROB_LAMBDA / (2.0 * math.sqrt(float(k))))
+    if floor is not None and err.size:
         excess = np.maximum(err - rel * np.abs(ref), 0.0)
         with np.errstate(divide="ignore", invalid="ignore"):
             used = np.where(floor > 0, excess / floor, np.where(excess > 0, np.inf, 0.0))

@@ -271,6 +271,13 @@ def test_workspace_errors(lib):
     r = lib.fp8_scaled_mm_channelwise_ex(FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 256, 1024, 1024,
                                          1024, 256, None, 0, ctypes.byref(bad), None)
     assert r == _lib.FP8_ERR_INVALID and "skinny" in _err(lib)
+    dec = _lib.TileConfig(_lib.VARIANTS["decode"], 0, 0, 0, 1, 0)
+    assert lib.fp8_scaled_mm_workspace_size(0, 16, 4096, 4096, ctypes.byref(dec)) == 0
+    for m, k, sk in ((17, 1024, 1), (16, 1040, 1), (16, 1024, 2)):   # M, K % 128, split_k
+        bad = _lib.TileConfig(_lib.VARIANTS["decode"], 0, 0, 0, sk, 0)
+        r = lib.fp8_scaled_mm_channelwise_ex(FAKE, FAKE, FAKE, FAKE, None, FAKE, m, 256, k, k,
+                                             k, 256, None, 0, ctypes.byref(bad), None)
+        assert r == _lib.FP8_ERR_INVALID and "decode" in _err(lib), (m, k, sk)
     unknown = _lib.TileConfig(99, 0, 0, 0, 1, 0)
     r = lib.fp8_scaled_mm_channelwise_ex(FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 256, 1024, 1024,
                                          1024, 256, None, 0, ctypes.byref(unknown), None)
@@ -310,6 +317,11 @@ def test_probe_argument_errors(lib):
     assert lib.fp8_probe_lds(4, 128, FAKE, 4, None) == _lib.FP8_ERR_INVALID
     assert lib.fp8_probe_wave_read(FAKE, 1 << 20, 1024, 16, 0, FAKE, 4, None) == _lib.FP8_ERR_INVALID
     assert lib.fp8_probe_wave_read(FAKE, 1000, 256, 8, 1, FAKE, 4, None) == _lib.FP8_ERR_INVALID
+    odd = ctypes.c_void_p(0x10008)   # 8-byte aligned only
+    assert lib.fp8_probe_mfma_dot(FAKE, FAKE, FAKE, FAKE, 1, 2, None) == _lib.FP8_ERR_INVALID   # form
+    assert lib.fp8_probe_mfma_dot(FAKE, FAKE, FAKE, FAKE, 0, 0, None) == _lib.FP8_ERR_INVALID   # count
+    assert lib.fp8_probe_mfma_dot(odd, FAKE, FAKE, FAKE, 1, 0, None) == _lib.FP8_ERR_INVALID
+    assert lib.fp8_probe_mfma_dot(FAKE, None, FAKE, FAKE, 1, 1, None) == _lib.FP8_ERR_INVALID
 
 
 # ---------------------------------------------------------------- tile table

@@ -53,8 +53,8 @@ def _case(wl, m, n, k, config=None, with_bias=False, poison=False, row_align=4):
     rows = sample_rows(m) if m * n > 4_000_000 else np.arange(m)
     bias64 = bias.float().numpy() if bias is not None else None
     ref = oracle.scaled_mm_blockwise(a[rows], b, sa[rows], sb, bias64)
-    tau = oracle.summation_bound_blockwise(a[rows], b, sa[rows], sb)
-    res = oracle.check_gemm(bf16_to_f64(out)[rows], ref, tau, k=k)
+    tau = oracle.gemm_tolerance_blockwise(a[rows], b, sa[rows], sb)
+    res = oracle.check_gemm(bf16_to_f64(out)[rows], ref, tau)
     say("ue8m0", wl, m, n, k, {kk: (round(v, 8) if isinstance(v, float) else v) for kk, v in res.items()})
     assert out.shape == (m, n)
     assert res["ok"], res

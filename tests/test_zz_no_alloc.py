@@ -67,7 +67,7 @@ def _run_case(kind_s, variant, split_k, m, n, k):
         b, sb = weight_channelwise("noalloc", n, k)
         a_d, sa_d, sa_ld = gpu(a), gpu(sa), 0
         ref = oracle.scaled_mm_channelwise(a, b, sa, sb)
-        tau = oracle.summation_bound_channelwise(a, b, sa, sb)
+        tau = oracle.gemm_tolerance_channelwise(a, b, sa, sb)
     else:
         kind = ops.KIND_BLOCKWISE
         a, sa = act_group("noalloc", m, k)
@@ -79,7 +79,7 @@ def _run_case(kind_s, variant, split_k, m, n, k):
         s_store[:, :m] = gpu(sa.T.copy())
         sa_d, sa_ld = s_store, m_pad
         ref = oracle.scaled_mm_blockwise(a, b, sa, sb)
-        tau = oracle.summation_bound_blockwise(a, b, sa, sb)
+        tau = oracle.gemm_tolerance_blockwise(a, b, sa, sb)
     b_d, sb_d = gpu(b), gpu(sb)
     out_ws = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=device())
     out_na = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=device())
@@ -90,7 +90,7 @@ def _run_case(kind_s, variant, split_k, m, n, k):
     assert st == 0, _lib.load().fp8_last_error()
     torch.cuda.synchronize()
     assert torch.equal(out_na.view(torch.int16), out_ws.view(torch.int16)), "differs from the workspace entry"
-    res = oracle.check_gemm(bf16_to_f64(out_na), ref, tau, k=k)
+    res = oracle.check_gemm(bf16_to_f64(out_na), ref, tau)
     assert res["ok"] and res["cosine"] > 0.9999, res
 
 
