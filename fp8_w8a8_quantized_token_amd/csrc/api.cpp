@@ -168,15 +168,26 @@ int fused_linear_mode() {
 // channelwise, 4096x1536 and 7168x2048 blockwise), one launch is 1.7 us
 // faster at M = 1 channelwise and 1.4-3.8 us at M <= 2 blockwise, but 4-15 us
 // slower at M = 2 and 4 channelwise and up to 2 us slower at M = 4 blockwise.
-bool linear_fuses(int kind, const fp8_tile_config& cfg, int64_t M, int32_t flags) {
+// The decode stream's fused form computes SiLU once per value (it keeps the
+// activation in registers between the row maximum and the quantization) and
+// fuses every flag.
+bool linear_fuses(int kind, const fp8_tile_config& cfg, int64_t M, int64_t N, int64_t K, int64_t ldb,
+                  int32_t flags) {
   const int mode = fused_linear_mode();
-  if (cfg.variant != FP8_VARIANT_SKINNY || M > kFusedRows || mode == 0) return false;
+  if (M > kFusedRows || mode == 0) return false;
+  if (cfg.variant == FP8_VARIANT_DECODE) {
+    GemmArgs p{};
+    p.M = M; p.N = N; p.K = K; p.ldb = ldb;
+    return decode_fused_launchable(p, (flags & FP8_QUANT_FUSE_SILU_MUL) != 0);
+  }
+  if (cfg.variant != FP8_VARIANT_SKINNY) return false;
   if ((flags & FP8_QUANT_FUSE_SILU_MUL) && mode == 1) return M <= (kind == FP8_KIND_CHANNELWISE ? 1 : 2);
   return true;
 }
 
 // Activation quantization then scaled GEMM; one fused launch when the skinny
-// kernel serves M <= kFusedRows, else the quantizer and the GEMM back to back.
+// kernel or the decode stream serves M <= kFusedRows, else the quantizer and
+// the GEMM back to back.
 int run_linear(const char* fn, int kind, const uint16_t* x, const uint8_t* b, const float* b_scale,
                const uint16_t* bias, uint16_t* out, int64_t M, int64_t N, int64_t K, int64_t ldx,
                int64_t ldb, int64_t ldc, int32_t row_alignment, float eps, uint8_t* q, int64_t ldq,
@@ -198,14 +209,14 @@ int run_linear(const char* fn, int kind, const uint16_t* x, const uint8_t* b, co
   fp8_tile_config cfg;
   st = resolve_config(kind, M, N, K, cfg_in, &cfg);
   if (st) return st;
-  if (linear_fuses(kind, cfg, M, flags)) {
+  if (linear_fuses(kind, cfg, M, N, K, ldb, flags)) {
     GemmArgs p{};
     p.a = q; p.b = b; p.sa = a_scale; p.sa_ld = m_pad; p.sb = b_scale; p.bias = bias; p.out = out;
     p.M = M; p.N = N; p.K = K; p.lda = ldq; p.ldb = ldb; p.ldc = ldc;
     p.split_k = 1;
     p.k_tiles_per_split = (int)((K + 127) / 128);
     const QuantArgs qa{x, ldx, q, ldq, a_scale, m_pad, eps};
-    return hip_status(launch_linear_fused(kind, p, qa, flags, stream), fn);
+    return hip_status(launch_linear_fused(kind, p, qa, flags, cfg.variant == FP8_VARIANT_DECODE, stream), fn);
   }
   const hipError_t e = bw ? launch_quant_per_token_group(x, M, K, ldx, 128, m_pad, q, ldq, a_scale, eps, flags, stream)
                           : launch_quant_per_token(x, M, K, ldx, q, ldq, a_scale, eps, flags, stream);
@@ -536,7 +547,7 @@ int fp8_linear_launches_ex(int32_t kind, int64_t M, int64_t N, int64_t K, const 
   fp8_tile_config cfg;
   st = resolve_config(kind, M, N, K, cfg_in, &cfg);
   if (st) return st;
-  return linear_fuses(kind, cfg, M, flags) ? 1 : 2;
+  return linear_fuses(kind, cfg, M, N, K, K, flags) ? 1 : 2;  // a contiguous weight
 }
 
 int fp8_linear_launches(int32_t kind, int64_t M, int64_t N, int64_t K, const fp8_tile_config* cfg_in) {

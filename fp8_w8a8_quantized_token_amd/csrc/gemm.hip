@@ -589,6 +589,13 @@ __device__ __forceinline__ void lds_dma16_s(const uint8_t* sbase, uint32_t voff,
                : "memory", "m0");
 }
 
+// The 4-byte form from a per-lane 64-bit address: lane l's 4 bytes land at
+// M0 + 4 l (gathers from several arrays in one instruction).
+__device__ __forceinline__ void lds_dma4_v(const void* gptr, uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(m0v) : "memory", "m0");
+}
+
 // The 4-byte form: each lane's 4 bytes land at M0 + 4 * lane.
 __device__ __forceinline__ void lds_dma4_s(const uint8_t* sbase, uint32_t voff, uint32_t lds_addr) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
@@ -1263,15 +1270,14 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
 // row r sits at position c ^ r, so the 16 rows of a fragment read hit
 // distinct banks. Activation rows at or past M are read as row M - 1 (their
 // outputs are never stored). The ring depth is a launch parameter: where the
-// grid covers the compute units once, the deepest ring the LDS holds (the
-// whole weight share of a workgroup in flight); beyond, a ring of at most
-// 80 KB, so that two workgroups share a compute unit and one's latency hides
-// behind the other's stream. Each wave counts the copies it issued (two
-// weight rows, and activation rows w and w + 8 below M) and waits for its own
-// copies of a stage before the stage's barrier. The blockwise scales of the
-// whole K range go to LDS before the first copy is issued, so no compiler
-// wait for an ordinary load can also hold back the copies. The eight waves'
-// partial tiles are summed through LDS in wave order (deterministic).
+// grid covers the compute units once, four slots (deeper rings measured
+// slower); beyond, a ring of at most 80 KB, so that two workgroups share a
+// compute unit and one's latency hides behind the other's stream. Each wave
+// counts the copies it issued (two weight rows, and activation rows w and
+// w + 8 below M) and waits for its own copies of a stage before the stage's
+// barrier. The blockwise scales of the whole K range go to an LDS table
+// while the first stages are in flight. The eight waves' partial tiles are
+// summed through LDS in wave order (deterministic).
 // ---------------------------------------------------------------------------
 namespace {
 constexpr int kDecWaves = 8;
@@ -1279,9 +1285,11 @@ constexpr int kDecStageK = kDecWaves * 128;  // K bytes per stage
 constexpr int kDecMaxSlots = 8;
 }  // namespace
 
-// LDS bytes of the decode kernel's scale table (blockwise) and of one ring slot.
+// LDS bytes of the decode kernel's scale table (blockwise: 17 floats per K
+// block, in whole 64-float pieces, one LDS-DMA instruction each) and of one
+// ring slot.
 __host__ __device__ inline size_t decode_scale_bytes(int64_t K, int kind) {
-  return kind != kChannelwise ? (size_t)(K / 128) * 17 * 4 : 0;
+  return kind != kChannelwise ? (size_t)(((K / 128) * 17 + 63) / 64) * 256 : 0;
 }
 __host__ __device__ inline size_t decode_slot_bytes(int64_t M) { return (size_t)(16 + M) * 1024; }
 
@@ -1303,15 +1311,6 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_decode_kernel(GemmArgs p)
   // blockwise: scale of (row r, block kb) at sc[17 kb + r] (0 for rows >= M),
   // the weight block scale of block kb at sc[17 kb + 16]
   float* sc = reinterpret_cast<float*>(lds + (size_t)ns * slot_bytes);
-  if constexpr (KIND == kBlockwise) {
-    const int64_t nb = n0 >> 7;
-    for (int64_t i = tid; i < kb_all * 17; i += kDecWaves * 64) {
-      const int64_t kb = i / 17;
-      const int r = (int)(i - kb * 17);
-      sc[i] = r < 16 ? (r < M ? p.sa[kb * p.sa_ld + r] : 0.0f) : p.sb[nb * kb_all + kb];
-    }
-    __syncthreads();
-  }
 
   // this wave's copies per stage: weight rows 2w, 2w+1; activation rows w, w+8 below M
   const int cnt = 2 + (wave < M ? 1 : 0) + (wave + 8 < M ? 1 : 0);
@@ -1354,6 +1353,24 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_decode_kernel(GemmArgs p)
       fa[j][t] = (uint32_t)(16 + am) * 1024 + ((c ^ am) << 4);
     }
 
+  if constexpr (KIND == kBlockwise) {
+    // The scale table travels by LDS-DMA too, 64 entries per instruction,
+    // issued before the first stage: its copies are the oldest of each wave,
+    // so the first stage's wait covers them, and no compiler wait for an
+    // ordinary load ever holds back the stream. Rows at or past M take row
+    // M - 1's scale (their outputs are never stored); entries past the table
+    // fill its padding from a valid address.
+    const int64_t nb = n0 >> 7, total = kb_all * 17, pieces = (total + 63) / 64;
+    for (int64_t i = wave; i < pieces; i += kDecWaves) {
+      const int64_t e = i * 64 + lane;
+      const int64_t kb = e / 17;
+      const int r = (int)(e - kb * 17);
+      const float* src = e >= total ? p.sb + nb * kb_all
+                         : r == 16  ? p.sb + nb * kb_all + kb
+                                    : p.sa + kb * p.sa_ld + (r < M ? r : M - 1);
+      lds_dma4_v(src, lds_base + (uint32_t)(ns * slot_bytes + i * 256));
+    }
+  }
   for (int s = 0; s < ns - 1 && s < nst; ++s) issue(s);
   for (int s = 0; s < nst; ++s) {
     // this wave's copies of stage s have landed; those of later stages may not
@@ -1729,6 +1746,267 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs
 }
 
 // ---------------------------------------------------------------------------
+// The decode stream with the activation quantization fused, for the single-
+// launch linear (M <= FR rows, FR in {1, 2, 4}; quantizer flags QF). Every
+// workgroup quantizes the whole activation and then streams the weight as
+// gemm_decode_kernel does, with ring slots of weight rows only and the
+// activation fragments read from an LDS copy of the codes ([FR][K], 16-byte
+// chunk c of row i at position c ^ i). Codes, scales and MFMAs, and their
+// order, are those of the quantization kernels followed by
+// gemm_decode_kernel, so the outputs are the same bits; workgroup 0 also
+// stores the codes (rows < M) and scales. The bf16 rows travel by LDS-DMA
+// into a staging area (which the codes then overwrite), issued before the
+// weight's first stages: each wave waits for its own activation copies
+// only, so the quantization runs while those stages are in flight and no
+// compiler wait for an ordinary load ever holds back the stream. Thread t
+// owns the 8-value units t + 512 u of every row (K positions 8 (t + 512 u)
+// .. +7), held in registers from the row maximum to the quantization: at
+// most kDecFusedUnits units over the FR rows (FR ceil(K / 4096) <= 8).
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kDecFusedUnits = 8;
+}  // namespace
+
+__host__ __device__ inline int64_t decode_fused_rows(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
+
+// Bytes of LDS past the ring: the staging area of the bf16 rows ([FR][2K],
+// with SiLU-and-mul [FR][4K]; the codes [FR][K] overwrite its start), the
+// scale tables (blockwise: weight block scales in 64-float pieces, activation
+// group scales [K/128][FR]; per token: row scales and their inverses) and the
+// row-maximum partials.
+__host__ __device__ inline size_t decode_fused_fixed_bytes(int64_t K, int kind, int64_t fr, bool silu) {
+  const int64_t kb = K / 128;
+  size_t b = (size_t)(fr * K * (silu ? 4 : 2));
+  if (kind != kChannelwise) b += (size_t)((kb + 63) / 64) * 256 + (size_t)(kb * fr) * 4;
+  b += (size_t)(2 * fr + kDecWaves * fr) * 4;
+  return b;
+}
+
+// The 16-byte LDS-DMA from a per-lane 64-bit address (lane l's 16 bytes land
+// at M0 + 16 l).
+__device__ __forceinline__ void lds_dma16_v(const void* gptr, uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0v) : "memory", "m0");
+}
+
+template <int KIND, int FR, int QF>
+__global__ __launch_bounds__(kDecWaves * 64) void gemm_decode_fused_kernel(GemmArgs p, QuantArgs qa) {
+  static_assert(KIND == kChannelwise || KIND == kBlockwise, "fp32 scales");
+  static_assert(FR == 1 || FR == 2 || FR == 4, "row buckets");
+  constexpr bool SILU = (QF & kQuantSiluMul) != 0;
+  constexpr int UM = kDecFusedUnits / FR;  // units per thread and row, at most
+  constexpr int NT = kDecWaves * 64;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int M = (int)p.M;
+  const int64_t K = p.K, kb_all = K / 128;
+  const int ns = p.ring_slots;  // 2 .. kDecMaxSlots, slots of 16 KB
+  const int nst = (int)((K + kDecStageK - 1) / kDecStageK);
+  const int nu = (int)((K / 8 + NT - 1) / NT);  // <= UM (checked on the host)
+  const bool writer = blockIdx.x == 0;
+  const int64_t RB = K * (SILU ? 4 : 2);  // staged bytes per row
+  uint8_t* stage = lds + (size_t)ns * 16384;
+  uint8_t* codes = stage;  // after the staged rows are read
+  float* tail = reinterpret_cast<float*>(stage + (size_t)FR * RB);
+  const int64_t sb_pieces = KIND == kBlockwise ? (kb_all + 63) / 64 : 0;
+  float* sbt = tail;                      // blockwise: weight block scales [kb_all]
+  float* sat = tail + sb_pieces * 64;     // blockwise: group scales [kb_all][FR]
+  float* row_scale = sat + (KIND == kBlockwise ? kb_all * FR : 0);
+  float* row_inv = row_scale + FR;
+  float* row_part = row_inv + FR;         // [wave][FR]
+
+  // 1. the bf16 rows < M ([M][RB] bytes, 1 KB per copy), the weight block
+  // scales (blockwise) and the weight's first stages, in that order
+  const int64_t xbytes = (int64_t)M * RB, xpieces = (xbytes + 1023) / 1024;
+  const uint32_t stage_lds = lds_base + (uint32_t)ns * 16384;
+  for (int64_t pc = wave; pc < xpieces; pc += kDecWaves) {
+    const int64_t b = pc * 1024 + lane * 16;
+    if (b < xbytes) {
+      const int64_t row = b / RB;
+      lds_dma16_v(reinterpret_cast<const uint8_t*>(qa.x) + row * qa.ldx * 2 + (b - row * RB),
+                  stage_lds + (uint32_t)(pc * 1024));
+    }
+  }
+  int younger = 0;  // this wave's copies issued after its activation copies
+  if constexpr (KIND == kBlockwise) {
+    const int64_t nb = n0 >> 7;
+    for (int64_t i = wave; i < sb_pieces; i += kDecWaves) {
+      const int64_t kb = i * 64 + lane;
+      lds_dma4_v(p.sb + nb * kb_all + (kb < kb_all ? kb : 0),
+                 (uint32_t)(uintptr_t)sbt + (uint32_t)(i * 256));
+      ++younger;
+    }
+  }
+  auto issue = [&](int s) {
+    const uint32_t slot = lds_base + (uint32_t)(s % ns) * 16384;
+    const int64_t k0 = (int64_t)s * kDecStageK;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = 2 * wave + rr;
+      int64_t n = n0 + r;
+      n = n < p.N ? n : p.N - 1;
+      int64_t kc = k0 + (int64_t)(lane ^ r) * 16;
+      kc = kc < K - 16 ? kc : K - 16;
+      lds_dma16_s(p.b, (uint32_t)(n * p.ldb + kc), slot + (uint32_t)r * 1024);
+    }
+  };
+  for (int s = 0; s < ns - 1 && s < nst; ++s) {
+    issue(s);
+    younger += 2;
+  }
+  wait_vmcnt_upto<0, 63>(younger);  // this wave's activation copies have landed
+  wait_vmcnt_lgkm0<63>();
+  __syncthreads();
+
+  // 2. this thread's units (zero outside rows < M and K)
+  uint4 xv[FR][UM];
+#pragma unroll
+  for (int i = 0; i < FR; ++i)
+#pragma unroll
+    for (int u = 0; u < UM; ++u) {
+      if (u < nu) {
+        const int64_t j = (int64_t)tid + (int64_t)NT * u;
+        const bool ok = i < M && 8 * j < K;
+        const uint8_t* src = stage + (size_t)(i < M ? i : 0) * RB + (size_t)(8 * j < K ? j : 0) * 16;
+        const uint4 gv = *reinterpret_cast<const uint4*>(src);
+        if constexpr (SILU) {
+          const uint4 uv = *reinterpret_cast<const uint4*>(src + 2 * K);
+          xv[i][u] = keep_if(ok, fused_values<QF>(gv, uv));
+        } else {
+          xv[i][u] = keep_if(ok, gv);
+        }
+      }
+    }
+
+  // 3. quantize into `codes` (over the staging area: every thread has read
+  // its units before the first code is written; rows M..FR-1 and K past the
+  // end give zero codes)
+  auto put = [&](int i, int64_t k, uint2 c) {
+    const int64_t cc = k >> 4;  // 16-byte chunk
+    *reinterpret_cast<uint2*>(codes + (size_t)i * K + (size_t)((cc ^ i) << 4) + ((k >> 3) & 1) * 8) = c;
+    if (writer && i < M) *reinterpret_cast<uint2*>(qa.q + (int64_t)i * qa.ldq + k) = c;
+  };
+  if constexpr (KIND == kChannelwise) {
+    float am[FR];
+#pragma unroll
+    for (int i = 0; i < FR; ++i) {
+      am[i] = 0.0f;
+#pragma unroll
+      for (int u = 0; u < UM; ++u)
+        if (u < nu) am[i] = fmaxf(am[i], absmax8_bf16(xv[i][u]));
+    }
+#pragma unroll
+    for (int i = 0; i < FR; ++i) {
+      const float w = wave_max(am[i]);
+      if (lane == 0) row_part[wave * FR + i] = w;
+    }
+    __syncthreads();
+    if (tid < FR) {
+      float mx = row_part[tid];
+      for (int w = 1; w < kDecWaves; ++w) mx = fmaxf(mx, row_part[w * FR + tid]);
+      const float sc = fused_scale<QF>(mx, qa.eps);
+      row_scale[tid] = sc;
+      row_inv[tid] = 1.0f / sc;
+      if (writer && tid < M) qa.scale[tid] = sc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < FR; ++i) {
+      const float sc = row_scale[i], y = row_inv[i];
+#pragma unroll
+      for (int u = 0; u < UM; ++u) {
+        if (u < nu) {
+          const int64_t k = 8 * ((int64_t)tid + (int64_t)NT * u);
+          if (k < K) put(i, k, quant8_bf16(xv[i][u], sc, y));
+        }
+      }
+    }
+  } else {
+    __syncthreads();  // the staged rows are read
+#pragma unroll
+    for (int i = 0; i < FR; ++i) {
+#pragma unroll
+      for (int u = 0; u < UM; ++u) {
+        if (u < nu) {
+          // a group of 128 values is 16 consecutive threads' units
+          const int64_t k = 8 * ((int64_t)tid + (int64_t)NT * u);
+          const float sc = fused_scale<QF>(max16_dpp(absmax8_bf16(xv[i][u])), qa.eps);
+          const float y = 1.0f / sc;
+          if (k < K) {
+            put(i, k, quant8_bf16(xv[i][u], sc, y));
+            if ((tid & 15) == 0) {
+              sat[(k >> 7) * FR + i] = sc;
+              if (writer && i < M) qa.scale[(k >> 7) * qa.scale_ld + i] = sc;
+            }
+          }
+        }
+      }
+    }
+  }
+  // workgroup 0's stores of codes and scales count with its copies; they
+  // are waited for here, so that the stream's waits count copies only
+  if (writer) wait_vmcnt<0>();
+  __syncthreads();
+
+  // 5. the weight stream (as gemm_decode_kernel: the same K blocks per wave
+  // in the same order)
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int am = r16 < M ? r16 : M - 1;
+  uint32_t fb[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int c = 8 * (4 * (wave & 1) + j) + 2 * g + t;
+      fb[j][t] = (uint32_t)r16 * 1024 + ((c ^ r16) << 4);
+    }
+  const uint8_t* arow = codes + (size_t)am * K;
+  for (int s = 0; s < nst; ++s) {
+    const int last = s + ns - 2 < nst - 1 ? s + ns - 2 : nst - 1;
+    wait_vmcnt_upto<0, 63>((last - s) * 2);
+    wait_vmcnt_lgkm0<63>();
+    __builtin_amdgcn_s_barrier();
+    if (s + ns - 1 < nst) issue(s + ns - 1);
+    if ((s & 3) == (wave >> 1)) {
+      const uint8_t* slot = lds + (size_t)(s % ns) * 16384;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t kb = (int64_t)s * kDecWaves + 4 * (wave & 1) + j;
+        if (kb >= kb_all) break;
+        const i32x8 bf = join(*reinterpret_cast<const uint4*>(slot + fb[j][0]),
+                              *reinterpret_cast<const uint4*>(slot + fb[j][1]));
+        const int64_t c0 = kb * 8 + 2 * g;
+        const i32x8 af = join(*reinterpret_cast<const uint4*>(arow + ((c0 ^ am) << 4)),
+                              *reinterpret_cast<const uint4*>(arow + (((c0 + 1) ^ am) << 4)));
+        if constexpr (KIND == kChannelwise) {
+          acc = mfma_fp8(bf, af, acc);
+        } else {
+          const f32x4 part = mfma_fp8(bf, af, f32x4{0.f, 0.f, 0.f, 0.f});
+          acc += part * (sat[kb * FR + am] * sbt[kb]);
+        }
+      }
+    }
+  }
+
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(lds);  // [wave][64]
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  f32x4 sum = red[lane];
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) sum += red[w * 64 + lane];
+  const int64_t m = r16;
+  const float sa_m = (KIND == kChannelwise && m < p.M) ? row_scale[r16] : 1.0f;
+  store_out4<KIND>(p, m, n0 + 4 * g, sum, sa_m);
+}
+
+// ---------------------------------------------------------------------------
 // Variant table and launch.
 // ---------------------------------------------------------------------------
 namespace {
@@ -2005,6 +2283,41 @@ hipError_t launch_fused_rows(const GemmArgs& p, const QuantArgs& qa, hipStream_t
   return hipGetLastError();
 }
 
+template <int KIND, int FR, int QF>
+hipError_t launch_decode_fused_rows(const GemmArgs& p, const QuantArgs& qa, hipStream_t stream) {
+  auto kern = gemm_decode_fused_kernel<KIND, FR, QF>;
+  static bool lds_attr_set = false;
+  if (!lds_attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+    if (e != hipSuccess) return e;
+    lds_attr_set = true;
+  }
+  // ring depth as for the unfused stream (slots of 16 KB: weight rows only)
+  const int64_t tiles = (p.N + 15) / 16;
+  const size_t fixed = decode_fused_fixed_bytes(p.K, KIND, FR, (QF & kQuantSiluMul) != 0);
+  const size_t budget = tiles <= 256 ? (size_t)163840 : (size_t)81920;
+  int64_t ns = budget > fixed ? (int64_t)((budget - fixed) / 16384) : 0;
+  const int64_t nst = (p.K + kDecStageK - 1) / kDecStageK;
+  if (ns > nst + 1) ns = nst + 1;
+  if (ns > (tiles <= 256 ? 4 : kDecMaxSlots)) ns = tiles <= 256 ? 4 : kDecMaxSlots;
+  if (ns < 2) ns = 2;
+  const size_t lds = (size_t)ns * 16384 + fixed;
+  if (lds > 163840) return hipErrorInvalidValue;
+  GemmArgs q = p;
+  q.ring_slots = (int)ns;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kDecWaves * 64), lds, stream, q, qa);
+  return hipGetLastError();
+}
+
+template <int KIND, int QF>
+hipError_t launch_decode_fused_kind(const GemmArgs& p, const QuantArgs& qa, hipStream_t stream) {
+  if (p.M <= 1) return launch_decode_fused_rows<KIND, 1, QF>(p, qa, stream);
+  if (p.M <= 2) return launch_decode_fused_rows<KIND, 2, QF>(p, qa, stream);
+  if (p.M <= 4) return launch_decode_fused_rows<KIND, 4, QF>(p, qa, stream);
+  return hipErrorInvalidValue;
+}
+
 template <int KIND, int QF>
 hipError_t launch_fused_kind(const GemmArgs& p, const QuantArgs& qa, hipStream_t stream) {
   if (p.M <= 1) return launch_fused_rows<KIND, 1, QF>(p, qa, stream);
@@ -2015,7 +2328,16 @@ hipError_t launch_fused_kind(const GemmArgs& p, const QuantArgs& qa, hipStream_t
 }
 
 template <int KIND>
-hipError_t launch_fused_flags(const GemmArgs& p, const QuantArgs& qa, int flags, hipStream_t stream) {
+hipError_t launch_fused_flags(const GemmArgs& p, const QuantArgs& qa, int flags, bool decode,
+                              hipStream_t stream) {
+  if (decode) {
+    switch (flags & (kQuantSiluMul | kQuantUe8m0)) {
+      case 0: return launch_decode_fused_kind<KIND, 0>(p, qa, stream);
+      case kQuantSiluMul: return launch_decode_fused_kind<KIND, kQuantSiluMul>(p, qa, stream);
+      case kQuantUe8m0: return launch_decode_fused_kind<KIND, kQuantUe8m0>(p, qa, stream);
+      default: return launch_decode_fused_kind<KIND, kQuantSiluMul | kQuantUe8m0>(p, qa, stream);
+    }
+  }
   switch (flags & (kQuantSiluMul | kQuantUe8m0)) {
     case 0: return launch_fused_kind<KIND, 0>(p, qa, stream);
     case kQuantSiluMul: return launch_fused_kind<KIND, kQuantSiluMul>(p, qa, stream);
@@ -2025,10 +2347,24 @@ hipError_t launch_fused_flags(const GemmArgs& p, const QuantArgs& qa, int flags,
 }
 }  // namespace
 
-hipError_t launch_linear_fused(int kind, const GemmArgs& p, const QuantArgs& qa, int flags,
+// The fused form fits its registers (FR ceil(K / 4096) <= 8) and its LDS:
+// with more workgroups than compute units it must leave room for two per
+// compute unit (80 KB with two ring slots; measured: blockwise 7168^2 at
+// M = 4 with one workgroup per compute unit ran 29 us, the two launches 17).
+bool decode_fused_launchable(const GemmArgs& p, bool silu) {
+  const uint64_t lim = 0xFFFFFFFFull - 1024;
+  const int64_t fr = decode_fused_rows(p.M);
+  const size_t budget = (p.N + 15) / 16 <= 256 ? 163840 : 81920;
+  return p.M >= 1 && p.M <= kFusedRows && p.K % 128 == 0 && fr * ((p.K + 4095) / 4096) <= kDecFusedUnits &&
+         (uint64_t)(p.N - 1) * (uint64_t)p.ldb <= lim &&
+         decode_fused_fixed_bytes(p.K, kBlockwise, fr, silu) + 2 * 16384 <= budget;
+}
+
+hipError_t launch_linear_fused(int kind, const GemmArgs& p, const QuantArgs& qa, int flags, bool decode,
                                hipStream_t stream) {
-  return kind == kChannelwise ? launch_fused_flags<kChannelwise>(p, qa, flags, stream)
-                              : launch_fused_flags<kBlockwise>(p, qa, flags, stream);
+  if (decode && !decode_fused_launchable(p, (flags & kQuantSiluMul) != 0)) return hipErrorInvalidValue;
+  return kind == kChannelwise ? launch_fused_flags<kChannelwise>(p, qa, flags, decode, stream)
+                              : launch_fused_flags<kBlockwise>(p, qa, flags, decode, stream);
 }
 
 namespace {

@@ -88,8 +88,11 @@ constexpr int64_t kFusedRows = 4;
 
 // flags: the quantizer flags (kQuantSiluMul: x rows are [gate | up], 2K wide,
 // and silu(gate) * up is quantized; kQuantUe8m0: power-of-two scales).
-hipError_t launch_linear_fused(int kind, const GemmArgs& args, const QuantArgs& qa, int flags,
+// decode: the decode weight stream with the quantization fused (when
+// decode_fused_launchable), else the skinny kernel with it fused.
+hipError_t launch_linear_fused(int kind, const GemmArgs& args, const QuantArgs& qa, int flags, bool decode,
                                hipStream_t stream);
+bool decode_fused_launchable(const GemmArgs& args, bool silu);
 
 // Geometry of a compiled kernel variant.
 struct VariantInfo {

@@ -283,7 +283,8 @@ bool tables_enabled() {
 
 int default_config(int kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* out) {
   // Measured on MI355X (o_proj, qkv, down, gate_up and the blockwise shapes,
-  // HBM-resident weights): the weight-streaming kernel up to 32 rows, then,
+  // HBM-resident weights): up to 16 rows the decode stream or the
+  // register-staged weight stream (below), up to 32 rows the latter, then,
   // for K % 128 == 0, the panel-ring LDS-DMA tiles: 64x64 up to M = 256 (deep
   // ring for channelwise), 128x64 up to 512 (deep ring for channelwise), the
   // 8-wave 128x128 up to 1024, then 256x128, or 256x256 where it gives at
@@ -301,15 +302,25 @@ int default_config(int kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* o
   const bool k128 = K % 128 == 0, k64 = cw && K % 64 == 0;
   fp8_tile_config c{};
   c.split_k = 1;
-  if (M <= 32) {
+  const int64_t groups = (N + 15) / 16;  // weight-streaming workgroups
+  if (M <= 16 && k128 && (groups > 256 ? (M <= 4 || groups < 896) : K >= 6144)) {
+    // The LDS-DMA decode stream, measured against the register-staged
+    // weight stream and the 32x32 deep-ring tile (HBM-resident weights): with
+    // more workgroups than compute units (two share one) ahead everywhere up
+    // to ~3.5 rounds (5120^2 9.2-9.5 against 11.5-14.8 us, blockwise 7168^2
+    // 13.9-14.7 against 16.6-18.2, qkv 6144x4096 9.1-9.5 against 9.4-11.0)
+    // and at M <= 4 beyond (gate_up 24576x4096 22.2 against 25.8); within one
+    // round from 6 KB deep rows (down 4096x12288 12.0-13.2 against 13.9-16.6,
+    // 4096x7168 8.2-8.7 against 9.2-11.1); on shallower ones (o_proj
+    // 4096x4096, 3072x4096) the register-staged stream, 0.3-0.8 us ahead.
+    c.variant = FP8_VARIANT_DECODE;
+  } else if (M <= 32) {
     c.variant = FP8_VARIANT_SKINNY;
     // From M = 8, on wide weights whose N/16 weight-streaming workgroups run
     // in uneven rounds over the 256 compute units (or N >= 12288), the 32x32
-    // deep-ring tile is ahead: 14336x4096 M = 16 15.8 against 20.2 us, 5120^2
-    // 12.1 against 18.1, blockwise 12288x7168 20.6 against 31.6; 2 splits
-    // over 40 or more K stages (blockwise: 24). M <= 4 keeps the weight-
-    // streaming kernel, which the single-launch linear needs.
-    const int64_t groups = (N + 15) / 16;
+    // deep-ring tile is ahead: 14336x4096 M = 16 15.9 against 19.0 us (decode
+    // stream) and 20.4 (register-staged), blockwise 12288x7168 M = 32 20.6
+    // against 31.6; 2 splits over 40 or more K stages (blockwise: 24).
     if (M >= 8 && k128 && ((groups > 256 && groups % 256 != 0) || N >= 12288)) {
       c.variant = FP8_VARIANT_T32x32DEEP;
       c.split_k = K / 128 >= (cw ? 40 : 24) ? 2 : 1;

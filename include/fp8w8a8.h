@@ -398,13 +398,16 @@ size_t fp8_scaled_mm_workspace_size(int32_t kind, int64_t M, int64_t N, int64_t 
  * the bias.] On success q rows < M and a_scale[0..M) hold exactly what
  * fp8_quant_per_token writes for x, and out exactly what
  * fp8_scaled_mm_channelwise computes from them (the same bits).
- * For M <= 4 with the skinny kernel selected (the default at small M) both
- * happen in ONE launch: every workgroup quantizes the activation rows it
- * multiplies (x is read from cache by each of them) and workgroup 0 also
- * stores q and a_scale. Otherwise the quantizer and the GEMM run as two
- * launches on `stream`. FP8W8A8_FUSED_LINEAR=0 in the environment turns the
- * single launch off; =all also takes it with SiLU-and-mul at every M <= 4
- * (see the _ex forms; for measurement).
+ * For M <= 4 with the skinny or the decode variant selected (the defaults
+ * at small M) both happen in ONE launch: every workgroup quantizes the
+ * activation rows it multiplies (x is read from cache by each of them) and
+ * workgroup 0 also stores q and a_scale (the decode variant: while
+ * 4 ceil(K / 4096) <= 8 at M = 3..4, 2 ceil(K / 4096) <= 8 at M = 2,
+ * ceil(K / 4096) <= 8 at M = 1, K % 128 == 0). Otherwise the quantizer and
+ * the GEMM run as two launches on `stream`. FP8W8A8_FUSED_LINEAR=0 in the
+ * environment turns the single launch off; =all also takes it on the skinny
+ * kernel with SiLU-and-mul at every M <= 4 (see the _ex forms; for
+ * measurement).
  *   x        bf16 [M][ldx], ldx >= K (input)
  *   q        E4M3 [M][ldq], ldq >= K (output codes; the GEMM's input)
  *   a_scale  fp32 [M] (output per-token scales)
@@ -425,8 +428,8 @@ int fp8_linear_channelwise(const uint16_t* x, const uint8_t* b, const float* b_s
  * bias added.] On success q rows < M and the scale entries of rows < M hold
  * exactly what fp8_quant_per_token_group(x, group 128, row_alignment) writes,
  * and out exactly what fp8_scaled_mm_blockwise computes from them; pad rows
- * M..M_pad-1 are not written. One launch for M <= 4 with the skinny kernel
- * selected, as above; two otherwise.
+ * M..M_pad-1 are not written. One launch for M <= 4 with the skinny or the
+ * decode variant selected, as above; two otherwise.
  *   x        bf16 [M][ldx], ldx >= K
  *   q        E4M3 [M_pad][ldq], M_pad = fp8_padded_rows(M, row_alignment)
  *   a_scale  fp32 [K/128][M_pad] (column-major scales, (m, kb) at kb*M_pad + m)
@@ -453,8 +456,10 @@ int fp8_linear_blockwise(const uint16_t* x, const uint8_t* b, const float* b_sca
  * the single fused launch (SiLU-and-mul evaluated there, correctly rounded as
  * in the quantizer) for M <= 4 with UE8M0 alone, and with SiLU-and-mul for
  * M = 1 channelwise and M <= 2 blockwise (every workgroup of that launch
- * evaluates SiLU over the whole input, which pays only for so few rows); the
- * other calls run the flagged quantizer and the GEMM as two launches.
+ * evaluates SiLU over the whole input, which pays only for so few rows); with
+ * the decode variant selected, for every flag at M <= 4 (it evaluates SiLU
+ * once per value); the other calls run the flagged quantizer and the GEMM as
+ * two launches.
  * fp8_linear_launches_ex tells which. flags == 0 is exactly
  * fp8_linear_channelwise / fp8_linear_blockwise. */
 int fp8_linear_channelwise_ex(const uint16_t* x, const uint8_t* b, const float* b_scale,

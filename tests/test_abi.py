@@ -206,9 +206,14 @@ def test_linear_launch_counts_with_flags(lib):
     for kind in (_lib.KIND_CHANNELWISE, _lib.KIND_BLOCKWISE):
         assert [n(kind, m, 4096, 4096, None, ue) for m in (1, 2, 4, 5)] == [1, 1, 1, 2]
         assert n(kind, 0, 4096, 4096, None, silu) == 0
-    # SiLU-and-mul stays in the single launch only for the fewest rows
-    assert [n(_lib.KIND_CHANNELWISE, m, 4096, 12288, None, silu) for m in (1, 2, 4)] == [1, 2, 2]
-    assert [n(_lib.KIND_BLOCKWISE, m, 7168, 2048, None, silu | ue) for m in (1, 2, 3, 4)] == [1, 1, 2, 2]
+    # SiLU-and-mul stays in the single launch only for the fewest rows (on the
+    # skinny kernel; the decode stream fuses every flag while its registers
+    # hold the activation: M = 4 at K = 12288 does not fit)
+    sk = ctypes.byref(_lib.TileConfig(_lib.VARIANTS["skinny"], 0, 0, 0, 1, 0))
+    assert [n(_lib.KIND_CHANNELWISE, m, 4096, 12288, sk, silu) for m in (1, 2, 4)] == [1, 2, 2]
+    assert [n(_lib.KIND_BLOCKWISE, m, 7168, 2048, sk, silu | ue) for m in (1, 2, 3, 4)] == [1, 1, 2, 2]
+    assert [n(_lib.KIND_CHANNELWISE, m, 4096, 12288, None, f) for m in (1, 2, 4) for f in (0, silu)] == \
+        [1, 1, 1, 1, 2, 2]
     assert n(_lib.KIND_CHANNELWISE, 1, 4096, 4096, None, 4) == _lib.FP8_ERR_INVALID
     assert n(_lib.KIND_CHANNELWISE, 1, 4096, 4096, None, 0) == lib.fp8_linear_launches(
         _lib.KIND_CHANNELWISE, 1, 4096, 4096, None)
@@ -217,10 +222,11 @@ def test_linear_launch_counts_with_flags(lib):
 def test_fused_linear_all_mode(lib, monkeypatch):
     n = lib.fp8_linear_launches_ex
     silu = _lib.QUANT_FUSE_SILU_MUL
-    assert n(_lib.KIND_CHANNELWISE, 4, 4096, 12288, None, silu) == 2
+    sk = ctypes.byref(_lib.TileConfig(_lib.VARIANTS["skinny"], 0, 0, 0, 1, 0))
+    assert n(_lib.KIND_CHANNELWISE, 4, 4096, 12288, sk, silu) == 2
     monkeypatch.setenv("FP8W8A8_FUSED_LINEAR", "all")
-    assert [n(_lib.KIND_CHANNELWISE, m, 4096, 12288, None, silu) for m in (1, 2, 4, 5)] == [1, 1, 1, 2]
-    assert n(_lib.KIND_BLOCKWISE, 4, 7168, 2048, None, silu) == 1
+    assert [n(_lib.KIND_CHANNELWISE, m, 4096, 12288, sk, silu) for m in (1, 2, 4)] == [1, 1, 1]
+    assert n(_lib.KIND_BLOCKWISE, 4, 7168, 2048, sk, silu) == 1
 
 
 def test_fused_linear_kill_switch(lib, monkeypatch):
@@ -499,9 +505,27 @@ def test_default_narrow_tile_on_uneven_skinny_rounds(lib):
         c = _default(lib, kind, n, k, m)
         return c["variant"], c["split_k"]
     assert d(cw, 14336, 4096, 16) == ("t32x32deep", 1)   # 896 groups: 3.5 rounds
-    assert d(cw, 5120, 5120, 8) == ("t32x32deep", 2)     # 320 groups, 40 stages
+    assert d(cw, 14336, 4096, 8) == ("t32x32deep", 1)
+    assert d(cw, 5120, 5120, 32) == ("t32x32deep", 2)    # 320 groups, 40 stages
     assert d(bw, 12288, 7168, 32) == ("t32x32deep", 2)   # N >= 12288
-    assert d(cw, 4096, 4096, 16)[0] == "skinny"          # whole rounds
-    assert d(cw, 8192, 8192, 16)[0] == "skinny"
-    assert d(bw, 3072, 4096, 16)[0] == "skinny"          # one partial round
-    assert d(cw, 14336, 4096, 4)[0] == "skinny"          # M <= 4: single-launch linear
+    assert d(cw, 4096, 4096, 32)[0] == "skinny"          # whole rounds
+
+
+def test_default_decode_stream_at_decode_sizes(lib):
+    cw, bw = _lib.KIND_CHANNELWISE, _lib.KIND_BLOCKWISE
+
+    def d(kind, n, k, m):
+        c = _default(lib, kind, n, k, m)
+        return c["variant"], c["split_k"]
+    dec = ("decode", 1)
+    assert d(cw, 5120, 5120, 8) == dec                   # 320 groups: two workgroups per CU
+    assert d(bw, 7168, 7168, 16) == dec
+    assert d(cw, 14336, 4096, 4) == dec                  # past 3.5 rounds only at M <= 4
+    assert d(cw, 24576, 4096, 1) == dec
+    assert d(cw, 4096, 12288, 16) == dec                 # one round, 6 KB or deeper rows
+    assert d(cw, 4096, 6144, 1) == dec
+    assert d(cw, 4096, 4096, 16)[0] == "skinny"          # one round, shallow rows
+    assert d(bw, 3072, 4096, 1)[0] == "skinny"
+    assert d(cw, 4096, 5120, 1)[0] == "skinny"
+    assert d(cw, 4096, 12304, 1)[0] == "skinny"          # K % 128 != 0
+    assert d(cw, 4096, 12288, 17)[0] == "skinny"         # M > 16

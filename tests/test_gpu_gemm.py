@@ -486,18 +486,22 @@ def test_default_heuristic_split_k(kind, m, n, k):
         _blockwise_case("default-split", m, n, k, with_bias=True)
 
 
-NARROW_DEFAULT_CASES = [("cw", 16, 14336, 4096), ("cw", 8, 5120, 5120), ("bw", 32, 12288, 7168), ("bw", 12, 5120, 5120)]
+NARROW_DEFAULT_CASES = [("cw", 16, 14336, 4096, "t32x32deep"), ("cw", 32, 5120, 5120, "t32x32deep"),
+                        ("bw", 32, 12288, 7168, "t32x32deep"), ("cw", 8, 5120, 5120, "decode"),
+                        ("bw", 12, 5120, 5120, "decode"), ("cw", 3, 14336, 4096, "decode")]
 
 
-@pytest.mark.parametrize("kind,m,n,k", NARROW_DEFAULT_CASES,
+@pytest.mark.parametrize("kind,m,n,k,variant", NARROW_DEFAULT_CASES,
                          ids=[f"{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in NARROW_DEFAULT_CASES])
-def test_default_narrow_tile_on_wide_weights(kind, m, n, k):
-    """Untabled wide weights at M = 8..32: the default heuristic takes the
-    32x32 deep-ring tile (split over long K) instead of the weight-streaming
-    kernel."""
+def test_default_narrow_tile_on_wide_weights(kind, m, n, k, variant):
+    """Untabled wide weights at M = 3..32: the default heuristic takes the
+    decode stream (two workgroups per compute unit) up to 16 rows where the
+    column groups run in at most ~3.5 rounds (any round count at M <= 4),
+    else the 32x32 deep-ring tile (split over long K), instead of the
+    register-staged weight stream."""
     kid = ops.KIND_CHANNELWISE if kind == "cw" else ops.KIND_BLOCKWISE
     cfg, hit = ops.tile_config(kid, n, k, m)
-    assert not hit and cfg["variant"] == "t32x32deep", cfg
+    assert not hit and cfg["variant"] == variant, cfg
     if kind == "cw":
         _channelwise_case("narrow-default", m, n, k, 0.0, True)
     else:

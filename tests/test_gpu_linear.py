@@ -1,9 +1,9 @@
 """GPU parity of the linears: activation quantization and scaled GEMM in one
 call (fp8_linear_channelwise / fp8_linear_blockwise through the C ABI).
 
-For M <= 4 with the skinny kernel selected the call is a single launch that
-quantizes the activation inside the GEMM. Each case checks, on the same
-seeded bf16 input:
+For M <= 4 with the skinny kernel or the decode stream selected the call is
+a single launch that quantizes the activation inside the GEMM. Each case
+checks, on the same seeded bf16 input:
 * the codes and scales the call leaves in q / a_scale are bit-exact against
   the oracle's quantizer (rows < M; pad rows keep their poison);
 * the output is within the GEMM tolerance of the fp64 oracle applied to the
@@ -35,6 +35,31 @@ def _same_bits(a, b):
     return torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def _resolved(kid, m, n, k):
+    """The tile config a linear call with no config resolves to."""
+    c, _ = ops.tile_config(kid, n, k, m)
+    return ops.make_config(c["variant"], c["split_k"]), c["variant"]
+
+
+def _fused_launch_expected(kind, variant, m, n, k, silu=False):
+    """One launch: the skinny kernel at M <= 4 (SiLU-and-mul: M = 1
+    channelwise, M <= 2 blockwise); the decode stream at M <= 4 while its
+    register-held activation fits (rows bucket times ceil(K / 4096) <= 8)
+    and its LDS does (staged rows, tables and two 16 KB ring slots within
+    160 KB, or 80 KB with more than 256 column groups)."""
+    if m > 4:
+        return False
+    if variant == "skinny":
+        return not silu or m <= (1 if kind == "cw" else 2)
+    if variant == "decode":
+        rows = 1 if m <= 1 else 2 if m <= 2 else 4
+        kb = k // 128
+        lds = rows * k * (4 if silu else 2) + -(-kb // 64) * 256 + kb * rows * 4 + 10 * rows * 4 + 2 * 16384
+        budget = 163840 if -(-n // 16) <= 256 else 81920
+        return k % 128 == 0 and rows * -(-k // 4096) <= 8 and lds <= budget
+    return False
+
+
 CW_CASES = ([("o_proj", m, 4096, 4096, 0.01, False) for m in (1, 2, 3, 4, 5, 16, 64)]
             + [("qwen3_8b", m, 4096, 12288, 0.0, True) for m in (1, 4)]
             + [("qwen3_8b", 3, 24576, 4096, 0.0, True)]
@@ -50,8 +75,9 @@ def test_linear_channelwise(wl, m, n, k, outl, with_bias):
     bias = synth.bias(wl, n) if with_bias else None
     bias_d = gpu(bias) if bias is not None else None
     launches = ops.linear_launches(ops.KIND_CHANNELWISE, m, n, k)
-    assert launches == (1 if m <= 4 else 2)
-    say("linear_channelwise", wl, m, n, k, f"launches={launches}")
+    cfg, variant = _resolved(ops.KIND_CHANNELWISE, m, n, k)
+    assert launches == (1 if _fused_launch_expected("cw", variant, m, n, k) else 2)
+    say("linear_channelwise", wl, m, n, k, variant, f"launches={launches}")
     out, q, s = ops.linear_channelwise(gpu(x), gpu(b), gpu(sb), bias_d, return_quant=True)
     torch.cuda.synchronize()
     want_q, want_s = oracle.quant_per_token(x.float().numpy())
@@ -62,7 +88,6 @@ def test_linear_channelwise(wl, m, n, k, outl, with_bias):
     tau = oracle.gemm_tolerance_channelwise(want_q, b, want_s, sb)
     _check(out, ref, tau, f"linear cw {wl} M={m} N={n} K={k}")
     # the two-launch path with the config the linear resolved
-    cfg = ops.make_config("skinny") if launches == 1 else None
     q2, s2 = ops.quant_per_token(gpu(x))
     out2 = ops.scaled_mm_channelwise(q2, gpu(b), s2, gpu(sb), bias_d, config=cfg)
     torch.cuda.synchronize()
@@ -80,13 +105,14 @@ def test_linear_blockwise(wl, m, n, k):
     b, sb = weight_blockwise(wl, n, k)
     bias = synth.bias(wl, n)
     launches = ops.linear_launches(ops.KIND_BLOCKWISE, m, n, k)
-    assert launches == (1 if m <= 4 else 2)
+    cfg, variant = _resolved(ops.KIND_BLOCKWISE, m, n, k)
+    assert launches == (1 if _fused_launch_expected("bw", variant, m, n, k) else 2)
     m_pad = ops.padded_rows(m, 4)
     q_buf = torch.full((m_pad, k), 0x7F, dtype=torch.uint8, device=device())
     s_buf = torch.full((k // 128, m_pad), float("nan"), dtype=torch.float32, device=device())
     out = torch.empty((m, n), dtype=torch.bfloat16, device=device())
     x_d, b_d, sb_d, bias_d = gpu(x), gpu(b), gpu(sb), gpu(bias)
-    say("linear_blockwise", wl, m, n, k, f"launches={launches}")
+    say("linear_blockwise", wl, m, n, k, variant, f"launches={launches}")
     run = ops.prepare("linear_blockwise", x_d, b_d, sb_d, bias=bias_d, row_alignment=4, out=out,
                       q=q_buf, scale=s_buf)
     run()
@@ -103,7 +129,6 @@ def test_linear_blockwise(wl, m, n, k):
     ref = oracle.scaled_mm_blockwise(want_q, b, want_s, sb, bias.float().numpy())
     tau = oracle.gemm_tolerance_blockwise(want_q, b, want_s, sb)
     _check(out, ref, tau, f"linear bw {wl} M={m} N={n} K={k}")
-    cfg = ops.make_config("skinny") if launches == 1 else None
     q2, s2 = ops.quant_per_token_group(x_d, 128, row_alignment=4)
     out2 = ops.scaled_mm_blockwise(q2, b_d, s2, sb_d, bias_d, m=m, config=cfg)
     torch.cuda.synchronize()
@@ -280,16 +305,18 @@ def test_linear_with_quant_flags(kind, m, n, k, silu, ue8m0):
     of 2K values (the down projection straight from the gate/up output) and
     UE8M0 makes the activation scales powers of two (blockwise: the GEMM then
     runs on the block-scaled MFMA tiles, weights quantized with power-of-two
-    block scales too). At the smallest M (UE8M0 alone: M <= 4; SiLU-and-mul:
-    M = 1 channelwise, M <= 2 blockwise) the call is one launch that applies
-    the flags inside the weight-streaming GEMM's quantization (per-token rows
-    across 4 KB chunks with a ragged tail included). Codes and scales bit-exact
+    block scales too). At the smallest M (skinny kernel: UE8M0 alone M <= 4,
+    SiLU-and-mul M = 1 channelwise, M <= 2 blockwise; decode stream: every
+    flag at M <= 4) the call is one launch that applies the flags inside the
+    weight-streaming GEMM's quantization (per-token rows across 4 KB chunks
+    with a ragged tail included). Codes and scales bit-exact
     against the oracle's flagged quantizer, the output within the GEMM
     tolerance of the oracle GEMM on them and bit-identical to the flagged
     quantizer followed by the GEMM entry."""
     kid = ops.KIND_CHANNELWISE if kind == "cw" else ops.KIND_BLOCKWISE
-    fused_rows = (1 if kind == "cw" else 2) if silu else 4
-    assert ops.linear_launches(kid, m, n, k, silu_mul=silu, scale_ue8m0=ue8m0) == (1 if m <= fused_rows else 2)
+    _, variant = _resolved(kid, m, n, k)
+    assert ops.linear_launches(kid, m, n, k, silu_mul=silu, scale_ue8m0=ue8m0) == \
+        (1 if _fused_launch_expected(kind, variant, m, n, k, silu) else 2)
     x = activations("flag-lin", m, 2 * k if silu else k)
     xf = x.float().numpy()
     y = oracle.silu_mul_bf16(xf) if silu else xf
@@ -344,7 +371,8 @@ def test_forced_single_launch_silu(kind, m, n, k, monkeypatch):
     codes, scales and output bits as the flagged quantizer and the GEMM."""
     monkeypatch.setenv("FP8W8A8_FUSED_LINEAR", "all")
     kid = ops.KIND_CHANNELWISE if kind == "cw" else ops.KIND_BLOCKWISE
-    assert ops.linear_launches(kid, m, n, k, silu_mul=True) == 1
+    sk = ops.make_config("skinny")
+    assert ops.linear_launches(kid, m, n, k, config=sk, silu_mul=True) == 1
     x = activations("forced-silu", m, 2 * k)
     xf = x.float().numpy()
     y = oracle.silu_mul_bf16(xf)
@@ -353,7 +381,8 @@ def test_forced_single_launch_silu(kind, m, n, k, monkeypatch):
     say("forced single-launch silu", kind, m, n, k)
     if kind == "cw":
         b, sb = weight_channelwise("forced-silu", n, k)
-        out, q, s = ops.linear_channelwise(x_d, gpu(b), gpu(sb), bias_d, return_quant=True, silu_mul=True)
+        out, q, s = ops.linear_channelwise(x_d, gpu(b), gpu(sb), bias_d, return_quant=True, silu_mul=True,
+                                           config=sk)
         want_q, want_s = oracle.quant_per_token(y)
         ref = oracle.scaled_mm_channelwise(want_q, b, want_s, sb, bias.float().numpy())
         tau = oracle.gemm_tolerance_channelwise(want_q, b, want_s, sb)
@@ -361,7 +390,8 @@ def test_forced_single_launch_silu(kind, m, n, k, monkeypatch):
         out2 = ops.scaled_mm_channelwise(q2, gpu(b), s2, gpu(sb), bias_d, config=ops.make_config("skinny"))
     else:
         b, sb = weight_blockwise("forced-silu", n, k)
-        out, q, s = ops.linear_blockwise(x_d, gpu(b), gpu(sb), bias_d, return_quant=True, silu_mul=True)
+        out, q, s = ops.linear_blockwise(x_d, gpu(b), gpu(sb), bias_d, return_quant=True, silu_mul=True,
+                                         config=sk)
         want_q, want_s = oracle.quant_per_token_group(y, 128)
         ref = oracle.scaled_mm_blockwise(want_q, b, want_s, sb, bias.float().numpy())
         tau = oracle.gemm_tolerance_blockwise(want_q, b, want_s, sb)
@@ -373,3 +403,81 @@ def test_forced_single_launch_silu(kind, m, n, k, monkeypatch):
     assert np.array_equal(s.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
     _check(out, ref, tau, f"forced silu {kind} M={m} N={n} K={k}")
     assert _same_bits(out, out2)
+
+
+DECODE_FUSED = [  # (kind, M, N, K, silu_mul, scale_ue8m0)
+    ("cw", 1, 4096, 4096, False, False), ("cw", 2, 392, 1152, False, False),
+    ("cw", 3, 4096, 8192, False, False), ("cw", 4, 512, 128, False, False),
+    ("cw", 1, 1024, 32768, False, False), ("cw", 2, 4096, 16384, False, True),
+    ("cw", 1, 4096, 4096, True, False), ("cw", 4, 392, 4096, True, True),
+    ("cw", 2, 4224, 2048, True, False),
+    ("bw", 1, 7168, 7168, False, False), ("bw", 3, 4224, 2048, True, False),
+    ("bw", 4, 384, 1152, False, True), ("bw", 2, 4096, 16384, False, False),
+    ("bw", 1, 256, 128, True, True), ("bw", 4, 4096, 8192, False, False), ("bw", 2, 7168, 7168, False, True)]
+
+
+@pytest.mark.parametrize("kind,m,n,k,silu,ue8m0", DECODE_FUSED,
+                         ids=[f"{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}{'-silu' if c[4] else ''}{'-ue8m0' if c[5] else ''}"
+                              for c in DECODE_FUSED])
+def test_linear_decode_stream_single_launch(kind, m, n, k, silu, ue8m0):
+    """The decode stream with the quantization fused: one 128-deep block up to
+    the largest K its registers hold for the row bucket (M = 1: 32768, M = 2:
+    16384, M = 3-4: 8192), a ragged last column group, one round of workgroups
+    and more (two workgroups per compute unit), with SiLU-and-mul and UE8M0. Codes and scales
+    bit-exact against the oracle's flagged quantizer, the output within the
+    GEMM tolerance and bit-identical to the flagged quantizer followed by the
+    decode GEMM."""
+    kid = ops.KIND_CHANNELWISE if kind == "cw" else ops.KIND_BLOCKWISE
+    dec = ops.make_config("decode")
+    assert ops.linear_launches(kid, m, n, k, config=dec, silu_mul=silu, scale_ue8m0=ue8m0) == 1
+    x = activations("dec-lin", m, 2 * k if silu else k, 0.01)
+    xf = x.float().numpy()
+    y = oracle.silu_mul_bf16(xf) if silu else xf
+    bias = synth.bias("dec-lin", n)
+    bias64 = bias.float().numpy()
+    x_d, bias_d = gpu(x), gpu(bias)
+    say("decode single launch", kind, m, n, k, "silu" if silu else "", "ue8m0" if ue8m0 else "")
+    if kind == "cw":
+        b, sb = weight_channelwise("dec-lin", n, k)
+        out, q, s = ops.linear_channelwise(x_d, gpu(b), gpu(sb), bias_d, return_quant=True, config=dec,
+                                           silu_mul=silu, scale_ue8m0=ue8m0)
+        torch.cuda.synchronize()
+        if ue8m0:
+            want_q, want_s = oracle.quant_per_token_group(y, k, scale_ue8m0=True)
+            want_s = want_s.reshape(m)
+        else:
+            want_q, want_s = oracle.quant_per_token(y)
+        ref = oracle.scaled_mm_channelwise(want_q, b, want_s, sb, bias64)
+        tol = oracle.gemm_tolerance_channelwise(want_q, b, want_s, sb)
+        q2, s2 = ops.quant_per_token(x_d, silu_mul=silu, scale_ue8m0=ue8m0)
+        out2 = ops.scaled_mm_channelwise(q2, gpu(b), s2, gpu(sb), bias_d, config=dec)
+    else:
+        b, sb = oracle.quant_weight_blockwise(synth.weights("dec-lin", n, k).numpy(), scale_ue8m0=ue8m0)
+        out, q, s = ops.linear_blockwise(x_d, gpu(b), gpu(sb), bias_d, return_quant=True, config=dec,
+                                         silu_mul=silu, scale_ue8m0=ue8m0)
+        torch.cuda.synchronize()
+        want_q, want_s = oracle.quant_per_token_group(y, 128, scale_ue8m0=ue8m0)
+        ref = oracle.scaled_mm_blockwise(want_q, b, want_s, sb, bias64)
+        tol = oracle.gemm_tolerance_blockwise(want_q, b, want_s, sb)
+        q2, s2 = ops.quant_per_token_group(x_d, 128, row_alignment=4, silu_mul=silu, scale_ue8m0=ue8m0)
+        out2 = ops.scaled_mm_blockwise(q2, gpu(b), s2, gpu(sb), bias_d, m=m, scale_ue8m0=ue8m0, config=dec)
+        s = s[:m]
+    torch.cuda.synchronize()
+    assert np.array_equal(q[:m].cpu().numpy(), want_q)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    _check(out, ref, tol, f"decode single launch {kind} M={m} N={n} K={k}")
+    assert _same_bits(out, out2)
+
+
+def test_linear_decode_stream_past_its_registers_takes_two_launches():
+    """M = 4 with K = 12288 (three units per row and thread): the quantizer,
+    then the decode GEMM."""
+    dec = ops.make_config("decode")
+    assert ops.linear_launches(ops.KIND_CHANNELWISE, 4, 4096, 12288, config=dec) == 2
+    assert ops.linear_launches(ops.KIND_CHANNELWISE, 2, 4096, 16384, config=dec) == 1
+    assert ops.linear_launches(ops.KIND_CHANNELWISE, 2, 4096, 16512, config=dec) == 2
+    # more workgroups than compute units: the fused form must fit two per
+    # compute unit (80 KB), which M = 3-4 at K = 7168 does not
+    assert ops.linear_launches(ops.KIND_BLOCKWISE, 2, 7168, 7168, config=dec) == 1
+    assert ops.linear_launches(ops.KIND_BLOCKWISE, 4, 7168, 7168, config=dec) == 2
+    assert ops.linear_launches(ops.KIND_BLOCKWISE, 4, 4096, 7168, config=dec) == 1
