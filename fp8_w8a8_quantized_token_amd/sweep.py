@@ -15,7 +15,7 @@ read from HBM as in a real forward pass; HIP events around the whole sequence
 on the launch stream; the median of several repetitions.
 
 Usage: python -m fp8_w8a8_quantized_token_amd.sweep [--kinds channelwise,blockwise]
-       [--shapes 4096x4096,...] [--ms 1,2,4,...] [--out DIR]
+       [--shapes 4096x4096,...] [--ms 1,2,4,...] [--out DIR] [--merge]
 """
 import argparse
 import json
@@ -44,8 +44,11 @@ def candidates(kind, m, n, k):
     k128 = k % 128 == 0
     if m <= 32:
         # the skinny kernel re-reads all M activation rows per 16 weight rows;
-        # from M = 8 the 32- and 64-wide deep-ring tiles can win on large N
+        # from M = 8 the 32- and 64-wide deep-ring tiles can win on large N;
+        # up to 16 rows the LDS-DMA decode stream
         c = [("skinny", 1)]
+        if m <= 16 and k128:
+            c += [("decode", 1)]
         if m >= 8 and k128:
             c += [("t32x32deep", 1), ("t32x32deep", 2), ("t32x32deep", 4), ("t64x32deep", 1),
                   ("t64x32deep", 2), ("t64x32deep", 4), ("t64x64deep", 1), ("t64x64deep", 2),
@@ -178,6 +181,8 @@ def main(argv=None):
     ap.add_argument("--shapes", default="", help="NxK list, e.g. 4096x4096,6144x4096")
     ap.add_argument("--ms", default=",".join(map(str, MS)))
     ap.add_argument("--out", default=os.path.join(PKG, "configs"))
+    ap.add_argument("--merge", action="store_true",
+                    help="keep the existing table's entries for the M not swept")
     args = ap.parse_args(argv)
     dev = torch.device("cuda:0")
     ms = [int(x) for x in args.ms.split(",")]
@@ -196,6 +201,11 @@ def main(argv=None):
             log(f"sweeping {kind} N={n} K={k}")
             table = sweep_shape(kind, n, k, ms, dev, log)
             path = os.path.join(args.out, f"N={n},K={k},device_name=gfx950,dtype=fp8_w8a8_{kind}.json")
+            if args.merge and os.path.exists(path):
+                with open(path) as f:
+                    old = json.load(f)
+                old.update(table)
+                table = {str(m): old[str(m)] for m in sorted(int(x) for x in old)}
             with open(path, "w") as f:
                 json.dump(table, f, indent=1)
             log(f"wrote {path}")
