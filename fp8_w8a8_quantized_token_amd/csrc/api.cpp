@@ -96,8 +96,8 @@ int resolve_config(int kind, int64_t M, int64_t N, int64_t K, const fp8_tile_con
   if (cfg->split_k < 1) return fail(FP8_ERR_INVALID, "split_k must be >= 1");
   if (cfg->variant == FP8_VARIANT_SKINNY && (M > vi.bm || cfg->split_k != 1))
     return fail(FP8_ERR_INVALID, "the skinny variant takes M <= %d and split_k == 1", vi.bm);
-  if (cfg->variant == FP8_VARIANT_DECODE && (M > vi.bm || K % 128 != 0 || cfg->split_k != 1))
-    return fail(FP8_ERR_INVALID, "the decode variant takes M <= %d, K %% 128 == 0 and split_k == 1", vi.bm);
+  if (cfg->variant == FP8_VARIANT_DECODE && (M > vi.bm || K % 128 != 0))
+    return fail(FP8_ERR_INVALID, "the decode variant takes M <= %d and K %% 128 == 0", vi.bm);
   *out = *cfg;
   out->bm = vi.bm; out->bn = vi.bn; out->bk = vi.bk; out->waves = vi.waves;
   return FP8_OK;
@@ -127,8 +127,8 @@ int run_gemm(const char* fn, int kind, const uint8_t* a, const uint8_t* b, const
   p.a = a; p.b = b; p.sa = sa; p.sa_ld = sa_ld; p.sb = sb; p.bias = bias; p.out = out;
   p.M = M; p.N = N; p.K = K; p.lda = lda; p.ldb = ldb; p.ldc = ldc;
   int splits = 1, per = (int)((K + 127) / 128);
-  if (cfg.variant != FP8_VARIANT_SKINNY && cfg.variant != FP8_VARIANT_DECODE)
-    split_plan(K, cfg.bk, cfg.split_k, &splits, &per);
+  if (cfg.variant == FP8_VARIANT_DECODE) decode_split_plan(K, cfg.split_k, &splits, &per);
+  else if (cfg.variant != FP8_VARIANT_SKINNY) split_plan(K, cfg.bk, cfg.split_k, &splits, &per);
   p.split_k = splits;
   p.k_tiles_per_split = per;
   if (splits > 1) {
@@ -150,6 +150,19 @@ int run_gemm(const char* fn, int kind, const uint8_t* a, const uint8_t* b, const
     p.ws_part = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
   }
   return hip_status(launch_gemm(kind, cfg.variant, p, stream), fn);
+}
+
+// The linear's config: as the GEMM's, except that with none given the decode
+// stream runs unsplit at M <= kFusedRows (its single-launch form does not
+// split K; the two launches then compute the same bits).
+int resolve_linear_config(int kind, int64_t M, int64_t N, int64_t K, const fp8_tile_config* cfg_in,
+                          fp8_tile_config* out) {
+  const int st = resolve_config(kind, M, N, K, cfg_in, out);
+  if (st) return st;
+  if ((!cfg_in || cfg_in->variant == FP8_VARIANT_DEFAULT) && out->variant == FP8_VARIANT_DECODE &&
+      M <= kFusedRows)
+    out->split_k = 1;
+  return FP8_OK;
 }
 
 // FP8W8A8_FUSED_LINEAR=0 turns the single-launch linear off; =all takes it at
@@ -176,6 +189,7 @@ bool linear_fuses(int kind, const fp8_tile_config& cfg, int64_t M, int64_t N, in
   const int mode = fused_linear_mode();
   if (M > kFusedRows || mode == 0) return false;
   if (cfg.variant == FP8_VARIANT_DECODE) {
+    if (cfg.split_k > 1) return false;
     GemmArgs p{};
     p.M = M; p.N = N; p.K = K; p.ldb = ldb;
     return decode_fused_launchable(p, (flags & FP8_QUANT_FUSE_SILU_MUL) != 0);
@@ -207,7 +221,7 @@ int run_linear(const char* fn, int kind, const uint16_t* x, const uint8_t* b, co
                 (long long)K);
   const int64_t m_pad = bw ? fp8_padded_rows(M, row_alignment) : M;
   fp8_tile_config cfg;
-  st = resolve_config(kind, M, N, K, cfg_in, &cfg);
+  st = resolve_linear_config(kind, M, N, K, cfg_in, &cfg);
   if (st) return st;
   if (linear_fuses(kind, cfg, M, N, K, ldb, flags)) {
     GemmArgs p{};
@@ -494,9 +508,10 @@ size_t fp8_scaled_mm_workspace_size(int32_t kind, int64_t M, int64_t N, int64_t 
   if (M == 0 || N == 0 || K == 0) return 0;
   fp8_tile_config cfg;
   if (resolve_config(kind, M, N, K, cfg_in, &cfg)) return (size_t)-1;
-  if (cfg.variant == FP8_VARIANT_SKINNY || cfg.variant == FP8_VARIANT_DECODE) return 0;
+  if (cfg.variant == FP8_VARIANT_SKINNY) return 0;
   int splits, per;
-  split_plan(K, cfg.bk, cfg.split_k, &splits, &per);
+  if (cfg.variant == FP8_VARIANT_DECODE) decode_split_plan(K, cfg.split_k, &splits, &per);
+  else split_plan(K, cfg.bk, cfg.split_k, &splits, &per);
   return variant_workspace_bytes(cfg.variant, splits, M, N);
 }
 
@@ -545,7 +560,7 @@ int fp8_linear_launches_ex(int32_t kind, int64_t M, int64_t N, int64_t K, const 
   if (st) return st;
   if (M == 0) return 0;
   fp8_tile_config cfg;
-  st = resolve_config(kind, M, N, K, cfg_in, &cfg);
+  st = resolve_linear_config(kind, M, N, K, cfg_in, &cfg);
   if (st) return st;
   return linear_fuses(kind, cfg, M, N, K, K, flags) ? 1 : 2;  // a contiguous weight
 }

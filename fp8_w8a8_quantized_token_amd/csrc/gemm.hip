@@ -1259,39 +1259,49 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
 
 // ---------------------------------------------------------------------------
 // Decode-size weight stream (M <= 16, K % 128 == 0). One workgroup of 8 waves
-// per 16 weight rows (16 output columns), walking K in 1 KB stages (eight
-// 128-deep K blocks, one V_MFMA_F32_16X16X128_F8F6F4 each; which wave
-// multiplies which block is set out below). The stages travel by LDS-DMA straight into
-// an LDS ring (no register staging) -- the weight rows as contiguous 1 KB
-// row segments, the M activation rows beside them -- with all but one of
-// the ring's slots in flight; a measured LDS-DMA stream of 1 KB pieces
-// reads at 0.64 of HBM peak from only 16 KB in flight per compute unit. Inside a segment the
-// lane fetches the 16-byte chunk that belongs at its LDS position: chunk c of
-// row r sits at position c ^ r, so the 16 rows of a fragment read hit
-// distinct banks. Activation rows at or past M are read as row M - 1 (their
-// outputs are never stored). The ring depth is a launch parameter: where the
-// grid covers the compute units once, four slots (deeper rings measured
-// slower); beyond, a ring of at most 80 KB, so that two workgroups share a
-// compute unit and one's latency hides behind the other's stream. Each wave
-// counts the copies it issued (two weight rows, and activation rows w and
-// w + 8 below M) and waits for its own copies of a stage before the stage's
-// barrier. The blockwise scales of the whole K range go to an LDS table
-// while the first stages are in flight. The eight waves' partial tiles are
-// summed through LDS in wave order (deterministic).
+// per 16 weight rows (16 output columns). Every wave streams its own 128-deep
+// K blocks through its own LDS ring and multiplies each with one
+// V_MFMA_F32_16X16X128_F8F6F4: no barrier until the final reduction, so no
+// wave waits for another while it has copies in flight. A block is the 16
+// weight rows' 128-byte pieces (two LDS-DMA instructions, one cache line per
+// row) and the activation rows' pieces (one instruction per 8 rows, rows at
+// or past M read as row M - 1, whose outputs are never stored); in LDS chunk
+// c of row r sits at position c ^ (r % 8), so the 16 rows of a fragment read
+// hit distinct banks. Wave w takes blocks 4w .. 4w + 3 of every 32 (4 KB of
+// K), in that order, as the register-staged weight-streaming kernel does, so
+// the fp32 sums and the outputs are bit-identical to its (and to the
+// single-launch linear's). Each wave counts its own copies and waits for the
+// block it multiplies next; a slot is refilled by the wave that read it, one
+// block after its fragments went to registers. Ring depth (slots per wave)
+// is a launch parameter: with one round of workgroups over the compute units
+// as many as fit 160 KB (at most 6), beyond that as many as fit 80 KB (two
+// workgroups per compute unit). The blockwise scales of the whole K range
+// go to an LDS table by LDS-DMA ahead of the first blocks. The eight waves'
+// partial tiles are summed through LDS in wave order (deterministic).
 // ---------------------------------------------------------------------------
 namespace {
 constexpr int kDecWaves = 8;
-constexpr int kDecStageK = kDecWaves * 128;  // K bytes per stage
-constexpr int kDecMaxSlots = 8;
+constexpr int kDecMaxWaveSlots = 6;
 }  // namespace
 
 // LDS bytes of the decode kernel's scale table (blockwise: 17 floats per K
 // block, in whole 64-float pieces, one LDS-DMA instruction each) and of one
-// ring slot.
+// wave's ring slot (16 weight rows, then 8 or 16 activation rows, 128 bytes
+// each).
 __host__ __device__ inline size_t decode_scale_bytes(int64_t K, int kind) {
   return kind != kChannelwise ? (size_t)(((K / 128) * 17 + 63) / 64) * 256 : 0;
 }
-__host__ __device__ inline size_t decode_slot_bytes(int64_t M) { return (size_t)(16 + M) * 1024; }
+__host__ __device__ inline size_t decode_slot_bytes(int64_t M) { return M > 8 ? 4096 : 3072; }
+
+// Blocks of wave w: i -> K block 32 (i / 4) + 4 w + i % 4, for i < the count.
+__device__ __forceinline__ int decode_wave_blocks(int64_t kb_all, int wave) {
+  int tail = (int)(kb_all % 32) - 4 * wave;
+  tail = tail < 0 ? 0 : (tail > 4 ? 4 : tail);
+  return (int)(kb_all / 32) * 4 + tail;
+}
+__device__ __forceinline__ int64_t decode_wave_kb(int i, int wave) {
+  return (int64_t)(i >> 2) * 32 + 4 * wave + (i & 3);
+}
 
 template <int KIND>
 __global__ __launch_bounds__(kDecWaves * 64) void gemm_decode_kernel(GemmArgs p) {
@@ -1304,104 +1314,102 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_decode_kernel(GemmArgs p)
   const int g = lane >> 4, r16 = lane & 15;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int M = (int)p.M;
-  const uint32_t slot_bytes = (uint32_t)(16 + M) * 1024;
-  const int ns = p.ring_slots;  // 2 .. kDecMaxSlots
+  const int R = p.ring_slots;  // slots per wave, 2 .. kDecMaxWaveSlots
+  const uint32_t sbytes = (uint32_t)decode_slot_bytes(M);
+  const int arows = M > 8 ? 2 : 1;  // activation DMA instructions per block
+  const int cnt = 2 + arows;        // this wave's copies per block
   const int64_t kb_all = p.K / 128;
-  const int nst = (int)((p.K + kDecStageK - 1) / kDecStageK);
-  // blockwise: scale of (row r, block kb) at sc[17 kb + r] (0 for rows >= M),
-  // the weight block scale of block kb at sc[17 kb + 16]
-  float* sc = reinterpret_cast<float*>(lds + (size_t)ns * slot_bytes);
-
-  // this wave's copies per stage: weight rows 2w, 2w+1; activation rows w, w+8 below M
-  const int cnt = 2 + (wave < M ? 1 : 0) + (wave + 8 < M ? 1 : 0);
-  auto issue = [&](int s) {
-    const uint32_t slot = lds_base + (uint32_t)(s % ns) * slot_bytes;
-    const int64_t k0 = (int64_t)s * kDecStageK;
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int r = 2 * wave + rr;
-      int64_t n = n0 + r;
-      n = n < p.N ? n : p.N - 1;
-      int64_t kc = k0 + (int64_t)(lane ^ r) * 16;
-      kc = kc < p.K - 16 ? kc : p.K - 16;
-      lds_dma16_s(p.b, (uint32_t)(n * p.ldb + kc), slot + (uint32_t)r * 1024);
-    }
-#pragma unroll
-    for (int ra = 0; ra < 2; ++ra) {
-      const int r = wave + 8 * ra;
-      if (r < M) {
-        int64_t kc = k0 + (int64_t)(lane ^ r) * 16;
-        kc = kc < p.K - 16 ? kc : p.K - 16;
-        lds_dma16_s(p.a, (uint32_t)(r * p.lda + kc), slot + (uint32_t)(16 + r) * 1024);
-      }
-    }
-  };
-
-  // K blocks: as in the register-staged weight-streaming kernel, wave w takes
-  // blocks 4w .. 4w+3 of every 4 KB of K, in that order, so that the fp32 sums
-  // and the outputs are bit-identical to its (and to the single-launch
-  // linear's); those four blocks are the half (w & 1) of stage 4c + (w >> 1).
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int am = r16 < M ? r16 : M - 1;  // activation row this lane reads
-  uint32_t fb[4][2], fa[4][2];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int c = 8 * (4 * (wave & 1) + j) + 2 * g + t;  // lane's 16-byte chunk of block j
-      fb[j][t] = (uint32_t)r16 * 1024 + ((c ^ r16) << 4);
-      fa[j][t] = (uint32_t)(16 + am) * 1024 + ((c ^ am) << 4);
-    }
+  // split-K: split s takes this wave's blocks [s per, (s + 1) per)
+  const int split = blockIdx.y;
+  const int nb_all = decode_wave_blocks(kb_all, wave);
+  const int i0 = split * p.k_tiles_per_split < nb_all ? split * p.k_tiles_per_split : nb_all;
+  const int i1 = i0 + p.k_tiles_per_split < nb_all ? i0 + p.k_tiles_per_split : nb_all;
+  const int nb = i1 - i0;
+  const uint32_t ring = (uint32_t)kDecWaves * R * sbytes;
+  const uint32_t wbase = lds_base + (uint32_t)wave * R * sbytes;
+  // blockwise: scale of (row r, block kb) at sc[17 kb + r], the weight block
+  // scale of block kb at sc[17 kb + 16]
+  const float* sc = reinterpret_cast<const float*>(lds + ring);
 
   if constexpr (KIND == kBlockwise) {
-    // The scale table travels by LDS-DMA too, 64 entries per instruction,
-    // issued before the first stage: its copies are the oldest of each wave,
-    // so the first stage's wait covers them, and no compiler wait for an
-    // ordinary load ever holds back the stream. Rows at or past M take row
-    // M - 1's scale (their outputs are never stored); entries past the table
-    // fill its padding from a valid address.
-    const int64_t nb = n0 >> 7, total = kb_all * 17, pieces = (total + 63) / 64;
+    // 64 entries per instruction; rows at or past M take row M - 1's scale,
+    // entries past the table fill its padding from a valid address
+    const int64_t nbk = n0 >> 7, total = kb_all * 17, pieces = (total + 63) / 64;
     for (int64_t i = wave; i < pieces; i += kDecWaves) {
       const int64_t e = i * 64 + lane;
       const int64_t kb = e / 17;
       const int r = (int)(e - kb * 17);
-      const float* src = e >= total ? p.sb + nb * kb_all
-                         : r == 16  ? p.sb + nb * kb_all + kb
+      const float* src = e >= total ? p.sb + nbk * kb_all
+                         : r == 16  ? p.sb + nbk * kb_all + kb
                                     : p.sa + kb * p.sa_ld + (r < M ? r : M - 1);
-      lds_dma4_v(src, lds_base + (uint32_t)(ns * slot_bytes + i * 256));
+      lds_dma4_v(src, lds_base + ring + (uint32_t)(i * 256));
     }
   }
-  for (int s = 0; s < ns - 1 && s < nst; ++s) issue(s);
-  for (int s = 0; s < nst; ++s) {
-    // this wave's copies of stage s have landed; those of later stages may not
-    const int last = s + ns - 2 < nst - 1 ? s + ns - 2 : nst - 1;
-    wait_vmcnt_upto<0, 63>((last - s) * cnt);
-    wait_vmcnt_lgkm0<63>();
-    __builtin_amdgcn_s_barrier();
-    // every wave is past stage s-1: its slot takes stage s + ns - 1
-    if (s + ns - 1 < nst) issue(s + ns - 1);
-    if ((s & 3) == (wave >> 1)) {
-      const uint8_t* slot = lds + (size_t)(s % ns) * slot_bytes;
+  // lane l of a DMA instruction fills LDS row 8 t + l / 8 (t the instruction)
+  // at chunk position l % 8 with logical chunk (l % 8) ^ (row % 8)
+  const int lr = lane >> 3;
+  const uint32_t chunk = (uint32_t)(((lane & 7) ^ lr) << 4);  // row % 8 == lr for both instructions
+  auto issue = [&](int i) {  // i counts this split's blocks from 0
+    const int64_t kb = decode_wave_kb(i0 + i, wave);
+    const uint32_t slot = wbase + (uint32_t)(i % R) * sbytes;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t kb = (int64_t)s * kDecWaves + 4 * (wave & 1) + j;
-        if (kb >= kb_all) break;
-        const i32x8 bf = join(*reinterpret_cast<const uint4*>(slot + fb[j][0]),
-                              *reinterpret_cast<const uint4*>(slot + fb[j][1]));
-        const i32x8 af = join(*reinterpret_cast<const uint4*>(slot + fa[j][0]),
-                              *reinterpret_cast<const uint4*>(slot + fa[j][1]));
-        if constexpr (KIND == kChannelwise) {
-          acc = mfma_fp8(bf, af, acc);
-        } else {
-          const f32x4 part = mfma_fp8(bf, af, f32x4{0.f, 0.f, 0.f, 0.f});
-          acc += part * (sc[kb * 17 + r16] * sc[kb * 17 + 16]);
-        }
-      }
+    for (int t = 0; t < 2; ++t) {
+      int64_t n = n0 + 8 * t + lr;
+      n = n < p.N ? n : p.N - 1;
+      lds_dma16_s(p.b, (uint32_t)(n * p.ldb + kb * 128) + chunk, slot + (uint32_t)t * 1024);
+    }
+    for (int t = 0; t < arows; ++t) {
+      int r = 8 * t + lr;
+      r = r < M ? r : M - 1;
+      lds_dma16_s(p.a, (uint32_t)(r * p.lda + kb * 128) + chunk, slot + 2048 + (uint32_t)t * 1024);
+    }
+  };
+  // this lane's fragment chunks: row r16 (weights) and row am (activation),
+  // 16-byte chunks 2g and 2g + 1 of the block
+  const int am = r16 < M ? r16 : M - 1;
+  const uint32_t fb0 = (uint32_t)r16 * 128 + (uint32_t)(((2 * g) ^ (r16 & 7)) << 4);
+  const uint32_t fb1 = (uint32_t)r16 * 128 + (uint32_t)(((2 * g + 1) ^ (r16 & 7)) << 4);
+  const uint32_t fa0 = 2048 + (uint32_t)am * 128 + (uint32_t)(((2 * g) ^ (am & 7)) << 4);
+  const uint32_t fa1 = 2048 + (uint32_t)am * 128 + (uint32_t)(((2 * g + 1) ^ (am & 7)) << 4);
+
+  const int pro = R - 1 < nb ? R - 1 : nb;
+  for (int i = 0; i < pro; ++i) issue(i);
+  if constexpr (KIND == kBlockwise) {
+    // the table's copies are this wave's oldest: wait for them, then for
+    // every wave's
+    wait_vmcnt_upto<0, 63>(pro * cnt);
+    __syncthreads();
+  }
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint8_t* wl = lds + (size_t)wave * R * sbytes;
+  for (int i = 0; i < nb; ++i) {
+    const int last = i + R - 2 < nb - 1 ? i + R - 2 : nb - 1;
+    wait_vmcnt_upto<0, 63>((last - i) * cnt);  // block i has landed
+    // the slot of block i - 1, whose fragments are in registers, takes block i + R - 1
+    if (i + R - 1 < nb) issue(i + R - 1);
+    const uint8_t* slot = wl + (size_t)(i % R) * sbytes;
+    const i32x8 bf = join(*reinterpret_cast<const uint4*>(slot + fb0), *reinterpret_cast<const uint4*>(slot + fb1));
+    const i32x8 af = join(*reinterpret_cast<const uint4*>(slot + fa0), *reinterpret_cast<const uint4*>(slot + fa1));
+    if constexpr (KIND == kChannelwise) {
+      acc = mfma_fp8(bf, af, acc);
+    } else {
+      const int64_t kb = decode_wave_kb(i0 + i, wave);
+      const f32x4 part = mfma_fp8(bf, af, f32x4{0.f, 0.f, 0.f, 0.f});
+      acc += part * (sc[kb * 17 + r16] * sc[kb * 17 + 16]);
     }
   }
 
+  // split-K: every thread's partial goes to the workspace; the last split
+  // to arrive sums them in split order (per thread, so per wave) and goes on
+  __syncthreads();  // the ring is idle: its first word serves as the flag
+  if (p.split_k > 1) {
+    f32x4 part[1][1] = {{acc}};
+    if (!splitk_reduce<1, 1, kDecWaves * 64>(p, part, blockIdx.x, split, tid, reinterpret_cast<int*>(lds)))
+      return;
+    acc = part[0][0];
+    __syncthreads();
+  }
   // the eight partial tiles summed through LDS in wave order
-  __syncthreads();
   f32x4* red = reinterpret_cast<f32x4*>(lds);  // [wave][64]
   red[wave * 64 + lane] = acc;
   __syncthreads();
@@ -1749,15 +1757,15 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_skinny_kernel(GemmArgs
 // The decode stream with the activation quantization fused, for the single-
 // launch linear (M <= FR rows, FR in {1, 2, 4}; quantizer flags QF). Every
 // workgroup quantizes the whole activation and then streams the weight as
-// gemm_decode_kernel does, with ring slots of weight rows only and the
-// activation fragments read from an LDS copy of the codes ([FR][K], 16-byte
+// gemm_decode_kernel does (per-wave rings), with slots of weight rows only and
+// the activation fragments read from an LDS copy of the codes ([FR][K], 16-byte
 // chunk c of row i at position c ^ i). Codes, scales and MFMAs, and their
 // order, are those of the quantization kernels followed by
 // gemm_decode_kernel, so the outputs are the same bits; workgroup 0 also
 // stores the codes (rows < M) and scales. The bf16 rows travel by LDS-DMA
 // into a staging area (which the codes then overwrite), issued before the
-// weight's first stages: each wave waits for its own activation copies
-// only, so the quantization runs while those stages are in flight and no
+// weight's first blocks: each wave waits for its own activation copies
+// only, so the quantization runs while those blocks are in flight and no
 // compiler wait for an ordinary load ever holds back the stream. Thread t
 // owns the 8-value units t + 512 u of every row (K positions 8 (t + 512 u)
 // .. +7), held in registers from the row maximum to the quantization: at
@@ -1805,12 +1813,13 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_decode_fused_kernel(GemmA
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int M = (int)p.M;
   const int64_t K = p.K, kb_all = K / 128;
-  const int ns = p.ring_slots;  // 2 .. kDecMaxSlots, slots of 16 KB
-  const int nst = (int)((K + kDecStageK - 1) / kDecStageK);
+  const int R = p.ring_slots;  // slots per wave (2 KB of weight rows each), 2 .. kDecMaxWaveSlots
+  const int nb = decode_wave_blocks(kb_all, wave);
   const int nu = (int)((K / 8 + NT - 1) / NT);  // <= UM (checked on the host)
   const bool writer = blockIdx.x == 0;
   const int64_t RB = K * (SILU ? 4 : 2);  // staged bytes per row
-  uint8_t* stage = lds + (size_t)ns * 16384;
+  const uint32_t ring = (uint32_t)kDecWaves * R * 2048;
+  uint8_t* stage = lds + ring;
   uint8_t* codes = stage;  // after the staged rows are read
   float* tail = reinterpret_cast<float*>(stage + (size_t)FR * RB);
   const int64_t sb_pieces = KIND == kBlockwise ? (kb_all + 63) / 64 : 0;
@@ -1821,9 +1830,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_decode_fused_kernel(GemmA
   float* row_part = row_inv + FR;         // [wave][FR]
 
   // 1. the bf16 rows < M ([M][RB] bytes, 1 KB per copy), the weight block
-  // scales (blockwise) and the weight's first stages, in that order
+  // scales (blockwise) and this wave's first weight blocks, in that order
   const int64_t xbytes = (int64_t)M * RB, xpieces = (xbytes + 1023) / 1024;
-  const uint32_t stage_lds = lds_base + (uint32_t)ns * 16384;
+  const uint32_t stage_lds = lds_base + ring;
   for (int64_t pc = wave; pc < xpieces; pc += kDecWaves) {
     const int64_t b = pc * 1024 + lane * 16;
     if (b < xbytes) {
@@ -1842,21 +1851,25 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_decode_fused_kernel(GemmA
       ++younger;
     }
   }
-  auto issue = [&](int s) {
-    const uint32_t slot = lds_base + (uint32_t)(s % ns) * 16384;
-    const int64_t k0 = (int64_t)s * kDecStageK;
+  // this wave's blocks as in gemm_decode_kernel, weight rows only (lane l
+  // of instruction t: row 8 t + l / 8, chunk position l % 8 holding logical
+  // chunk (l % 8) ^ (l / 8))
+  const int lr = lane >> 3;
+  const uint32_t chunk = (uint32_t)(((lane & 7) ^ lr) << 4);
+  const uint32_t wbase = lds_base + (uint32_t)wave * R * 2048;
+  auto issue = [&](int i) {
+    const int64_t kb = decode_wave_kb(i, wave);
+    const uint32_t slot = wbase + (uint32_t)(i % R) * 2048;
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int r = 2 * wave + rr;
-      int64_t n = n0 + r;
+    for (int t = 0; t < 2; ++t) {
+      int64_t n = n0 + 8 * t + lr;
       n = n < p.N ? n : p.N - 1;
-      int64_t kc = k0 + (int64_t)(lane ^ r) * 16;
-      kc = kc < K - 16 ? kc : K - 16;
-      lds_dma16_s(p.b, (uint32_t)(n * p.ldb + kc), slot + (uint32_t)r * 1024);
+      lds_dma16_s(p.b, (uint32_t)(n * p.ldb + kb * 128) + chunk, slot + (uint32_t)t * 1024);
     }
   };
-  for (int s = 0; s < ns - 1 && s < nst; ++s) {
-    issue(s);
+  const int pro = R - 1 < nb ? R - 1 : nb;
+  for (int i = 0; i < pro; ++i) {
+    issue(i);
     younger += 2;
   }
   wait_vmcnt_upto<0, 63>(younger);  // this wave's activation copies have landed
@@ -1957,39 +1970,25 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_decode_fused_kernel(GemmA
   // in the same order)
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   const int am = r16 < M ? r16 : M - 1;
-  uint32_t fb[4][2];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int c = 8 * (4 * (wave & 1) + j) + 2 * g + t;
-      fb[j][t] = (uint32_t)r16 * 1024 + ((c ^ r16) << 4);
-    }
+  const uint32_t fb0 = (uint32_t)r16 * 128 + (uint32_t)(((2 * g) ^ (r16 & 7)) << 4);
+  const uint32_t fb1 = (uint32_t)r16 * 128 + (uint32_t)(((2 * g + 1) ^ (r16 & 7)) << 4);
   const uint8_t* arow = codes + (size_t)am * K;
-  for (int s = 0; s < nst; ++s) {
-    const int last = s + ns - 2 < nst - 1 ? s + ns - 2 : nst - 1;
-    wait_vmcnt_upto<0, 63>((last - s) * 2);
-    wait_vmcnt_lgkm0<63>();
-    __builtin_amdgcn_s_barrier();
-    if (s + ns - 1 < nst) issue(s + ns - 1);
-    if ((s & 3) == (wave >> 1)) {
-      const uint8_t* slot = lds + (size_t)(s % ns) * 16384;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t kb = (int64_t)s * kDecWaves + 4 * (wave & 1) + j;
-        if (kb >= kb_all) break;
-        const i32x8 bf = join(*reinterpret_cast<const uint4*>(slot + fb[j][0]),
-                              *reinterpret_cast<const uint4*>(slot + fb[j][1]));
-        const int64_t c0 = kb * 8 + 2 * g;
-        const i32x8 af = join(*reinterpret_cast<const uint4*>(arow + ((c0 ^ am) << 4)),
-                              *reinterpret_cast<const uint4*>(arow + (((c0 + 1) ^ am) << 4)));
-        if constexpr (KIND == kChannelwise) {
-          acc = mfma_fp8(bf, af, acc);
-        } else {
-          const f32x4 part = mfma_fp8(bf, af, f32x4{0.f, 0.f, 0.f, 0.f});
-          acc += part * (sat[kb * FR + am] * sbt[kb]);
-        }
-      }
+  const uint8_t* wl = lds + (size_t)wave * R * 2048;
+  for (int i = 0; i < nb; ++i) {
+    const int last = i + R - 2 < nb - 1 ? i + R - 2 : nb - 1;
+    wait_vmcnt_upto<0, 63>((last - i) * 2);
+    if (i + R - 1 < nb) issue(i + R - 1);
+    const int64_t kb = decode_wave_kb(i, wave);
+    const uint8_t* slot = wl + (size_t)(i % R) * 2048;
+    const i32x8 bf = join(*reinterpret_cast<const uint4*>(slot + fb0), *reinterpret_cast<const uint4*>(slot + fb1));
+    const int64_t c0 = kb * 8 + 2 * g;
+    const i32x8 af = join(*reinterpret_cast<const uint4*>(arow + ((c0 ^ am) << 4)),
+                          *reinterpret_cast<const uint4*>(arow + (((c0 + 1) ^ am) << 4)));
+    if constexpr (KIND == kChannelwise) {
+      acc = mfma_fp8(bf, af, acc);
+    } else {
+      const f32x4 part = mfma_fp8(bf, af, f32x4{0.f, 0.f, 0.f, 0.f});
+      acc += part * (sat[kb * FR + am] * sbt[kb]);
     }
   }
 
@@ -2046,10 +2045,12 @@ hipError_t launch_panel(const GemmArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The decode stream takes whole 128-deep K blocks and 32-bit DMA offsets.
+// The decode stream takes whole 128-deep K blocks and 32-bit DMA offsets
+// (the last byte of the last row of either operand within 2^32 - 1).
 bool decode_eligible(const GemmArgs& p) {
-  const uint64_t lim = 0xFFFFFFFFull - 1024;
-  return p.K % 128 == 0 && (uint64_t)(p.N - 1) * (uint64_t)p.ldb <= lim && (uint64_t)15 * (uint64_t)p.lda <= lim;
+  const uint64_t lim = 0xFFFFFFFFull;
+  return p.K % 128 == 0 && (uint64_t)(p.N - 1) * (uint64_t)p.ldb + (uint64_t)p.K <= lim &&
+         (uint64_t)(p.M - 1) * (uint64_t)p.lda + (uint64_t)p.K <= lim;
 }
 
 template <int KIND>
@@ -2062,22 +2063,26 @@ hipError_t launch_decode(const GemmArgs& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     lds_attr_set = true;
   }
-  // Ring depth, measured: with one round of workgroups over the compute units
-  // four slots (deeper rings were slower); with more workgroups than compute
-  // units as many slots as fit 80 KB, so two workgroups share a compute unit.
+  // slots per wave: one round of workgroups over the compute units, as many
+  // as fit 160 KB (at most kDecMaxWaveSlots); more workgroups, as many as fit
+  // 80 KB (two per compute unit); never more than a wave has blocks, plus one
   const int64_t tiles = (p.N + 15) / 16;
-  const size_t fixed = decode_scale_bytes(p.K, KIND), slot = decode_slot_bytes(p.M);
+  const size_t fixed = decode_scale_bytes(p.K, KIND), slot = decode_slot_bytes(p.M) * kDecWaves;
   const size_t budget = (tiles <= 256 ? (size_t)163840 : (size_t)81920);
   int64_t ns = budget > fixed ? (int64_t)((budget - fixed) / slot) : 0;
-  const int64_t nst = (p.K + kDecStageK - 1) / kDecStageK;
-  if (ns > nst + 1) ns = nst + 1;  // no slot beyond the stages there are
-  if (ns > (tiles <= 256 ? 4 : kDecMaxSlots)) ns = tiles <= 256 ? 4 : kDecMaxSlots;
+  int64_t per_wave = ((p.K / 128) + kDecWaves - 1) / kDecWaves;
+  if (p.split_k > 1 && p.k_tiles_per_split < per_wave) per_wave = p.k_tiles_per_split;
+  if (ns > per_wave + 1) ns = per_wave + 1;
+  if (ns > kDecMaxWaveSlots) ns = kDecMaxWaveSlots;
   if (ns < 2) ns = 2;
   const size_t lds = (size_t)ns * slot + fixed;
   if (lds > 163840) return hipErrorInvalidValue;
   GemmArgs q = p;
   q.ring_slots = (int)ns;
-  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kDecWaves * 64), lds, stream, q);
+  if (q.split_k < 1) q.split_k = 1;
+  if (q.split_k == 1) q.k_tiles_per_split = (int)(4 * ((p.K / 128 + 31) / 32));  // every block
+  if (q.split_k > 1 && tiles > kMaxSplitTiles) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles, (unsigned)q.split_k), dim3(kDecWaves * 64), lds, stream, q);
   return hipGetLastError();
 }
 
@@ -2268,8 +2273,22 @@ int64_t variant_tiles(int variant, int64_t M, int64_t N) {
   return ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
 }
 
+// Blocks per wave of the decode stream (wave 0 has the most) and the split
+// plan over them: `per` blocks per split, `splits` splits (<= split_k).
+void decode_split_plan(int64_t K, int split_k, int* splits, int* per) {
+  const int64_t kb_all = K / 128;
+  const int64_t nbw = 4 * (kb_all / 32) + (kb_all % 32 < 4 ? kb_all % 32 : 4);
+  int64_t s = split_k < 1 ? 1 : split_k;
+  if (s > nbw) s = nbw > 0 ? nbw : 1;
+  const int64_t pr = nbw > 0 ? (nbw + s - 1) / s : 1;
+  *per = (int)pr;
+  *splits = (int)(nbw > 0 ? (nbw + pr - 1) / pr : 1);
+}
+
 size_t variant_workspace_bytes(int variant, int split_k, int64_t M, int64_t N) {
-  if (split_k <= 1 || variant == 0 || variant == 26) return 0;
+  if (split_k <= 1 || variant == 0) return 0;
+  if (variant == 26)  // one 16-byte partial per thread of the 512 per tile and split
+    return kCounterBytes + (size_t)((N + 15) / 16) * split_k * kDecWaves * 64 * 16;
   const VariantInfo v = variant_info(variant);
   const int64_t tiles = variant_tiles(variant, M, N);
   return kCounterBytes + (size_t)tiles * split_k * v.bm * v.bn * sizeof(float);
@@ -2293,16 +2312,16 @@ hipError_t launch_decode_fused_rows(const GemmArgs& p, const QuantArgs& qa, hipS
     if (e != hipSuccess) return e;
     lds_attr_set = true;
   }
-  // ring depth as for the unfused stream (slots of 16 KB: weight rows only)
+  // ring depth as for the unfused stream (slots of 2 KB per wave: weight rows only)
   const int64_t tiles = (p.N + 15) / 16;
   const size_t fixed = decode_fused_fixed_bytes(p.K, KIND, FR, (QF & kQuantSiluMul) != 0);
   const size_t budget = tiles <= 256 ? (size_t)163840 : (size_t)81920;
-  int64_t ns = budget > fixed ? (int64_t)((budget - fixed) / 16384) : 0;
-  const int64_t nst = (p.K + kDecStageK - 1) / kDecStageK;
-  if (ns > nst + 1) ns = nst + 1;
-  if (ns > (tiles <= 256 ? 4 : kDecMaxSlots)) ns = tiles <= 256 ? 4 : kDecMaxSlots;
+  int64_t ns = budget > fixed ? (int64_t)((budget - fixed) / (kDecWaves * 2048)) : 0;
+  const int64_t per_wave = ((p.K / 128) + kDecWaves - 1) / kDecWaves;
+  if (ns > per_wave + 1) ns = per_wave + 1;
+  if (ns > kDecMaxWaveSlots) ns = kDecMaxWaveSlots;
   if (ns < 2) ns = 2;
-  const size_t lds = (size_t)ns * 16384 + fixed;
+  const size_t lds = (size_t)ns * kDecWaves * 2048 + fixed;
   if (lds > 163840) return hipErrorInvalidValue;
   GemmArgs q = p;
   q.ring_slots = (int)ns;
@@ -2349,15 +2368,14 @@ hipError_t launch_fused_flags(const GemmArgs& p, const QuantArgs& qa, int flags,
 
 // The fused form fits its registers (FR ceil(K / 4096) <= 8) and its LDS:
 // with more workgroups than compute units it must leave room for two per
-// compute unit (80 KB with two ring slots; measured: blockwise 7168^2 at
+// compute unit (80 KB with two slots per wave; measured: blockwise 7168^2 at
 // M = 4 with one workgroup per compute unit ran 29 us, the two launches 17).
 bool decode_fused_launchable(const GemmArgs& p, bool silu) {
-  const uint64_t lim = 0xFFFFFFFFull - 1024;
   const int64_t fr = decode_fused_rows(p.M);
   const size_t budget = (p.N + 15) / 16 <= 256 ? 163840 : 81920;
   return p.M >= 1 && p.M <= kFusedRows && p.K % 128 == 0 && fr * ((p.K + 4095) / 4096) <= kDecFusedUnits &&
-         (uint64_t)(p.N - 1) * (uint64_t)p.ldb <= lim &&
-         decode_fused_fixed_bytes(p.K, kBlockwise, fr, silu) + 2 * 16384 <= budget;
+         (uint64_t)(p.N - 1) * (uint64_t)p.ldb + (uint64_t)p.K <= 0xFFFFFFFFull &&
+         decode_fused_fixed_bytes(p.K, kBlockwise, fr, silu) + 2 * kDecWaves * 2048 <= budget;
 }
 
 hipError_t launch_linear_fused(int kind, const GemmArgs& p, const QuantArgs& qa, int flags, bool decode,

@@ -112,6 +112,10 @@ int64_t variant_tiles(int variant, int64_t M, int64_t N);
 constexpr int64_t kMaxSplitTiles = 65536;
 constexpr size_t kCounterBytes = (size_t)kMaxSplitTiles * sizeof(int);
 
+// The decode stream's split plan: its splits cut every wave's block list
+// into `per` blocks each; `splits` (<= split_k) of them.
+void decode_split_plan(int64_t K, int split_k, int* splits, int* per);
+
 // Bytes of split-K workspace for (variant, split_k, M, N); 0 when split_k == 1.
 size_t variant_workspace_bytes(int variant, int split_k, int64_t M, int64_t N);
 

@@ -279,11 +279,21 @@ def test_workspace_errors(lib):
     assert r == _lib.FP8_ERR_INVALID and "skinny" in _err(lib)
     dec = _lib.TileConfig(_lib.VARIANTS["decode"], 0, 0, 0, 1, 0)
     assert lib.fp8_scaled_mm_workspace_size(0, 16, 4096, 4096, ctypes.byref(dec)) == 0
-    for m, k, sk in ((17, 1024, 1), (16, 1040, 1), (16, 1024, 2)):   # M, K % 128, split_k
-        bad = _lib.TileConfig(_lib.VARIANTS["decode"], 0, 0, 0, sk, 0)
+    for m, k in ((17, 1024), (16, 1040)):   # M, K % 128
+        bad = _lib.TileConfig(_lib.VARIANTS["decode"], 0, 0, 0, 1, 0)
         r = lib.fp8_scaled_mm_channelwise_ex(FAKE, FAKE, FAKE, FAKE, None, FAKE, m, 256, k, k,
                                              k, 256, None, 0, ctypes.byref(bad), None)
-        assert r == _lib.FP8_ERR_INVALID and "decode" in _err(lib), (m, k, sk)
+        assert r == _lib.FP8_ERR_INVALID and "decode" in _err(lib), (m, k)
+    # split-K over each wave's block list: K = 12288 gives wave 0 twelve
+    # blocks, so split_k 5 runs 4 splits of 3 (the last partial tile and
+    # split of the 512 threads' 16-byte partials per 16-column tile)
+    dec5 = _lib.TileConfig(_lib.VARIANTS["decode"], 0, 0, 0, 5, 0)
+    assert lib.fp8_scaled_mm_workspace_size(0, 4, 4100, 12288, ctypes.byref(dec5)) == \
+        65536 * 4 + 257 * 4 * 512 * 16
+    dec2 = _lib.TileConfig(_lib.VARIANTS["decode"], 0, 0, 0, 2, 0)
+    r = lib.fp8_scaled_mm_channelwise_ex(FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 256, 1024, 1024,
+                                         1024, 256, None, 0, ctypes.byref(dec2), None)
+    assert r == _lib.FP8_ERR_WORKSPACE
     unknown = _lib.TileConfig(99, 0, 0, 0, 1, 0)
     r = lib.fp8_scaled_mm_channelwise_ex(FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 256, 1024, 1024,
                                          1024, 256, None, 0, ctypes.byref(unknown), None)

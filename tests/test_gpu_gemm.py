@@ -151,6 +151,28 @@ def test_decode_variant_parity_and_same_bits_as_skinny(m, n, k):
         assert torch.equal(b1.view(torch.int16), b2.view(torch.int16))
 
 
+DECODE_SPLIT_CASES = [("cw", 1, 4096, 4096, 2), ("cw", 16, 520, 12288, 3), ("cw", 5, 392, 1152, 2),
+                      ("bw", 3, 4096, 7168, 4), ("bw", 16, 512, 2048, 2), ("bw", 1, 384, 4224, 5)]
+
+
+@pytest.mark.parametrize("kind,m,n,k,split", DECODE_SPLIT_CASES,
+                         ids=[f"{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}-sk{c[4]}" for c in DECODE_SPLIT_CASES])
+def test_decode_variant_split_k(kind, m, n, k, split):
+    """The decode stream split over K (each split a run of every wave's
+    blocks, partials summed in split order): within the tolerance of the
+    oracle, including splits of unequal length and a wave with no block in
+    the last split, and the same bits on a repeat (the arrival counters
+    reset)."""
+    cfg = ops.make_config("decode", split)
+    if kind == "cw":
+        _, o1 = _channelwise_case("decode-split", m, n, k, 0.01, True, config=cfg, sample=False)
+        _, o2 = _channelwise_case("decode-split", m, n, k, 0.01, True, config=cfg, sample=False)
+    else:
+        _, o1 = _blockwise_case("decode-split", m, n, k, config=cfg, with_bias=True)
+        _, o2 = _blockwise_case("decode-split", m, n, k, config=cfg, with_bias=True)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
 def test_decode_variant_pad_rows_and_scale_stride():
     """Blockwise decode with NaN-poisoned pad rows and scales, and with an
     unaligned scale stride (row_alignment 1): the first M rows match a clean

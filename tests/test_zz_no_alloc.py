@@ -56,6 +56,8 @@ CASES = [
     ("cw", "t64x32deep", 2, 100, 256, 1024),
     ("bw", "t256x128panel", 2, 301, 384, 1024),
     ("bw", "t64x64deep", 4, 64, 256, 512),
+    ("cw", "decode", 3, 16, 4104, 12288),
+    ("bw", "decode", 2, 3, 512, 2048),
 ]
 
 
