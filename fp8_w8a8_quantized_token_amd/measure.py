@@ -26,6 +26,7 @@ Usage: python -m fp8_w8a8_quantized_token_amd.measure [--workloads small,o_proj,
        [--calls 100] [--warmup 20] [--out FILE]
 """
 import argparse
+import os
 import math
 import sys
 import time
@@ -605,6 +606,74 @@ def row(cfg, kind, n, k, m, r, bias):
             f"{percentile(r['linear'], 50):.1f} ({r['launches']}) | {percentile(r['hot'], 50):.1f} |")
 
 
+def traffic_summary(fetch_csv, write_csv, label, symbol, n, k, bm, bn, threads, command_tail):
+    """Summary text of two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE,
+    csv) of ``bench.py --profile-label LABEL``: the counters of each labelled
+    dispatch after the 256 MiB calibration copy, scaled by what the copy
+    reads (FETCH_SIZE) and writes (WRITE_SIZE) per KiB, against the
+    algorithmic bytes of the launch (M from its grid: BM x BN tiles of
+    `threads` threads)."""
+    import csv
+    import re
+
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench  # noqa: E402
+
+    def agg(path):
+        d = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = (int(r["Dispatch_Id"]), re.sub(r"\(.*", "", r["Kernel_Name"]), int(r["Grid_Size"]))
+                d[key] = d.get(key, 0.0) + float(r["Counter_Value"])
+        return sorted(d.items())
+
+    copy_grid = (256 << 20) // 16 // 128  # the calibration copy's grid (16 bytes per lane)
+
+    def pick(items):
+        idx = max(i for i, ((_, kn, g), _) in enumerate(items) if "copyBuffer" in kn and g == copy_grid)
+        return items[idx][1], [(kn, g, v) for (_, kn, g), v in items[idx + 1:] if symbol in kn]
+
+    cf, lf = pick(agg(fetch_csv))
+    cw, lw = pick(agg(write_csv))
+    ff, fw = 262144.0 / cf, 262144.0 / cw
+
+    def alg(m):
+        return m * k + n * k + 2 * m * n + 4 * m * (k // 128) + 4 * (n // 128) * (k // 128)
+
+    def m_of(grid):
+        return grid // threads // ((n + bn - 1) // bn) * bm
+
+    rows, tot = [], 0.0
+    for i, ((_, g, f), (_, _, w)) in enumerate(zip(lf, lw)):
+        t = (f * ff + w * fw) * 1024
+        tot += t
+        rows.append(f"  {i:4d}  {m_of(g):6d}  {f:11.1f}  {w:11.1f}  {t / 1e6:10.1f}  {alg(m_of(g)) / 1e6:10.1f}")
+    cmd = f'python -u bench.py --profile-label "{label}"'
+    return "\n".join([
+        f"# HBM traffic of {label} ({command_tail})",
+        "",
+        "commands:",
+        f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o f -- {cmd}",
+        f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o w -- {cmd}",
+        "  python -m fp8_w8a8_quantized_token_amd.measure --traffic-summary "
+        "gpurun_out/pmc_fetch/f_counter_collection.csv gpurun_out/pmc_write/w_counter_collection.csv",
+        "",
+        f"calibration: plain 256 MiB device copy reads FETCH_SIZE {cf:.1f} KiB (factor {ff:.4f}), "
+        f"WRITE_SIZE {cw:.1f} KiB (factor {fw:.4f})",
+        "",
+        "launch       M    FETCH_KiB    WRITE_KiB  traffic_MB  algorithmic_MB",
+        *rows,
+        "",
+        f"label: {label}",
+        f"kernel_symbol: {symbol}",
+        f"traffic_bytes_per_launch: {int(round(tot / max(1, len(lf))))}",
+        f"algorithmic_bytes_per_launch: {int(round(sum(alg(m_of(g)) for _, g, _ in lf) / max(1, len(lf))))}",
+        f"source_sha256: {bench.kernel_source_hash()}",
+        "note: FETCH_SIZE counts L2 misses, which includes reads the 256 MB last-level cache serves",
+        "",
+    ])
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--workloads", default=",".join(synth.WORKLOADS))
@@ -623,7 +692,19 @@ def main(argv=None):
                     help="time plain device copies and reductions at the small-M linears' byte counts")
     ap.add_argument("--probes", action="store_true",
                     help="run the probe kernels: HBM read stream, L2 feed, FP8 MFMA rate and clock")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs of the benchmark's "
+                         "dominant kernel (written to profiles/, no GPU needed)")
     args = ap.parse_args(argv)
+    if args.traffic_summary:
+        txt = traffic_summary(*args.traffic_summary, label="gemm_blockwise[t256x256bw16]",
+                              symbol="gemm_panel_kernel<256, 256, 2, 4, 1, 4, true>", n=4096, k=4096,
+                              bm=256, bn=256, threads=512, command_tail="o_proj N=K=4096 step launches")
+        root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+        with open(os.path.join(root, "profiles", "gemm_blockwise_t256x256bw16_o_proj_traffic.txt"), "w") as f:
+            f.write(txt)
+        print(txt)
+        return 0
     _lib.load()
     dev = torch.device("cuda:0")
     want = args.workloads.split(",")
