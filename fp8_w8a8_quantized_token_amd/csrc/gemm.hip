@@ -1284,14 +1284,17 @@ constexpr int kDecWaves = 8;
 constexpr int kDecMaxWaveSlots = 6;
 }  // namespace
 
-// LDS bytes of the decode kernel's scale table (blockwise: 17 floats per K
+// Activation tiles of 16 rows (1, 2 or 4 for M <= 16, 32, 64); LDS bytes of
+// the decode kernel's scale table (blockwise: 16 x tiles + 1 floats per K
 // block, in whole 64-float pieces, one LDS-DMA instruction each) and of one
-// wave's ring slot (16 weight rows, then 8 or 16 activation rows, 128 bytes
-// each).
-__host__ __device__ inline size_t decode_scale_bytes(int64_t K, int kind) {
-  return kind != kChannelwise ? (size_t)(((K / 128) * 17 + 63) / 64) * 256 : 0;
+// wave's ring slot (16 weight rows, then the activation rows in groups of
+// 8, 128 bytes each).
+__host__ __device__ inline int decode_tiles(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
+__host__ __device__ inline size_t decode_scale_bytes(int64_t K, int kind, int64_t M) {
+  const int64_t st = 16 * decode_tiles(M) + 1;
+  return kind != kChannelwise ? (size_t)(((K / 128) * st + 63) / 64) * 256 : 0;
 }
-__host__ __device__ inline size_t decode_slot_bytes(int64_t M) { return M > 8 ? 4096 : 3072; }
+__host__ __device__ inline size_t decode_slot_bytes(int64_t M) { return 2048 + (size_t)((M + 7) / 8) * 1024; }
 
 // Blocks of wave w: i -> K block 32 (i / 4) + 4 w + i % 4, for i < the count.
 __device__ __forceinline__ int decode_wave_blocks(int64_t kb_all, int wave) {
@@ -1303,9 +1306,10 @@ __device__ __forceinline__ int64_t decode_wave_kb(int i, int wave) {
   return (int64_t)(i >> 2) * 32 + 4 * wave + (i & 3);
 }
 
-template <int KIND>
+template <int KIND, int MT>
 __global__ __launch_bounds__(kDecWaves * 64) void gemm_decode_kernel(GemmArgs p) {
   static_assert(KIND == kChannelwise || KIND == kBlockwise, "fp32 scales");
+  static_assert(MT == 1 || MT == 2 || MT == 4, "16-row activation tiles");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
   const int tid = threadIdx.x;
@@ -1313,11 +1317,11 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_decode_kernel(GemmArgs p)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int M = (int)p.M;
+  const int M = (int)p.M;  // <= 16 MT
   const int R = p.ring_slots;  // slots per wave, 2 .. kDecMaxWaveSlots
   const uint32_t sbytes = (uint32_t)decode_slot_bytes(M);
-  const int arows = M > 8 ? 2 : 1;  // activation DMA instructions per block
-  const int cnt = 2 + arows;        // this wave's copies per block
+  const int arows = (M + 7) / 8;  // activation DMA instructions per block (8 rows each)
+  const int cnt = 2 + arows;      // this wave's copies per block
   const int64_t kb_all = p.K / 128;
   // split-K: split s takes this wave's blocks [s per, (s + 1) per)
   const int split = blockIdx.y;
@@ -1327,28 +1331,29 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_decode_kernel(GemmArgs p)
   const int nb = i1 - i0;
   const uint32_t ring = (uint32_t)kDecWaves * R * sbytes;
   const uint32_t wbase = lds_base + (uint32_t)wave * R * sbytes;
-  // blockwise: scale of (row r, block kb) at sc[17 kb + r], the weight block
-  // scale of block kb at sc[17 kb + 16]
+  // blockwise: scale of (row r, block kb) at sc[ST kb + r] (r < 16 MT), the
+  // weight block scale of block kb at sc[ST kb + 16 MT]
+  constexpr int ST = 16 * MT + 1;
   const float* sc = reinterpret_cast<const float*>(lds + ring);
 
   if constexpr (KIND == kBlockwise) {
     // 64 entries per instruction; rows at or past M take row M - 1's scale,
     // entries past the table fill its padding from a valid address
-    const int64_t nbk = n0 >> 7, total = kb_all * 17, pieces = (total + 63) / 64;
+    const int64_t nbk = n0 >> 7, total = kb_all * ST, pieces = (total + 63) / 64;
     for (int64_t i = wave; i < pieces; i += kDecWaves) {
       const int64_t e = i * 64 + lane;
-      const int64_t kb = e / 17;
-      const int r = (int)(e - kb * 17);
-      const float* src = e >= total ? p.sb + nbk * kb_all
-                         : r == 16  ? p.sb + nbk * kb_all + kb
-                                    : p.sa + kb * p.sa_ld + (r < M ? r : M - 1);
+      const int64_t kb = e / ST;
+      const int r = (int)(e - kb * ST);
+      const float* src = e >= total   ? p.sb + nbk * kb_all
+                         : r == ST - 1 ? p.sb + nbk * kb_all + kb
+                                       : p.sa + kb * p.sa_ld + (r < M ? r : M - 1);
       lds_dma4_v(src, lds_base + ring + (uint32_t)(i * 256));
     }
   }
   // lane l of a DMA instruction fills LDS row 8 t + l / 8 (t the instruction)
   // at chunk position l % 8 with logical chunk (l % 8) ^ (row % 8)
   const int lr = lane >> 3;
-  const uint32_t chunk = (uint32_t)(((lane & 7) ^ lr) << 4);  // row % 8 == lr for both instructions
+  const uint32_t chunk = (uint32_t)(((lane & 7) ^ lr) << 4);  // row % 8 == lr for every instruction
   auto issue = [&](int i) {  // i counts this split's blocks from 0
     const int64_t kb = decode_wave_kb(i0 + i, wave);
     const uint32_t slot = wbase + (uint32_t)(i % R) * sbytes;
@@ -1364,13 +1369,17 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_decode_kernel(GemmArgs p)
       lds_dma16_s(p.a, (uint32_t)(r * p.lda + kb * 128) + chunk, slot + 2048 + (uint32_t)t * 1024);
     }
   };
-  // this lane's fragment chunks: row r16 (weights) and row am (activation),
-  // 16-byte chunks 2g and 2g + 1 of the block
-  const int am = r16 < M ? r16 : M - 1;
+  // this lane's fragment chunks: weight row r16 and, per activation tile t,
+  // LDS row am_t = min(16 t + r16, M - 1); 16-byte chunks 2g and 2g + 1
   const uint32_t fb0 = (uint32_t)r16 * 128 + (uint32_t)(((2 * g) ^ (r16 & 7)) << 4);
   const uint32_t fb1 = (uint32_t)r16 * 128 + (uint32_t)(((2 * g + 1) ^ (r16 & 7)) << 4);
-  const uint32_t fa0 = 2048 + (uint32_t)am * 128 + (uint32_t)(((2 * g) ^ (am & 7)) << 4);
-  const uint32_t fa1 = 2048 + (uint32_t)am * 128 + (uint32_t)(((2 * g + 1) ^ (am & 7)) << 4);
+  uint32_t fa0[MT], fa1[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int am = 16 * t + r16 < M ? 16 * t + r16 : M - 1;
+    fa0[t] = 2048 + (uint32_t)am * 128 + (uint32_t)(((2 * g) ^ (am & 7)) << 4);
+    fa1[t] = 2048 + (uint32_t)am * 128 + (uint32_t)(((2 * g + 1) ^ (am & 7)) << 4);
+  }
 
   const int pro = R - 1 < nb ? R - 1 : nb;
   for (int i = 0; i < pro; ++i) issue(i);
@@ -1380,7 +1389,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_decode_kernel(GemmArgs p)
     wait_vmcnt_upto<0, 63>(pro * cnt);
     __syncthreads();
   }
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint8_t* wl = lds + (size_t)wave * R * sbytes;
   for (int i = 0; i < nb; ++i) {
     const int last = i + R - 2 < nb - 1 ? i + R - 2 : nb - 1;
@@ -1389,35 +1400,44 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_decode_kernel(GemmArgs p)
     if (i + R - 1 < nb) issue(i + R - 1);
     const uint8_t* slot = wl + (size_t)(i % R) * sbytes;
     const i32x8 bf = join(*reinterpret_cast<const uint4*>(slot + fb0), *reinterpret_cast<const uint4*>(slot + fb1));
-    const i32x8 af = join(*reinterpret_cast<const uint4*>(slot + fa0), *reinterpret_cast<const uint4*>(slot + fa1));
-    if constexpr (KIND == kChannelwise) {
-      acc = mfma_fp8(bf, af, acc);
-    } else {
-      const int64_t kb = decode_wave_kb(i0 + i, wave);
-      const f32x4 part = mfma_fp8(bf, af, f32x4{0.f, 0.f, 0.f, 0.f});
-      acc += part * (sc[kb * 17 + r16] * sc[kb * 17 + 16]);
+    const int64_t kb = decode_wave_kb(i0 + i, wave);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const i32x8 af =
+          join(*reinterpret_cast<const uint4*>(slot + fa0[t]), *reinterpret_cast<const uint4*>(slot + fa1[t]));
+      if constexpr (KIND == kChannelwise) {
+        acc[t] = mfma_fp8(bf, af, acc[t]);
+      } else {
+        const f32x4 part = mfma_fp8(bf, af, f32x4{0.f, 0.f, 0.f, 0.f});
+        acc[t] += part * (sc[kb * ST + 16 * t + r16] * sc[kb * ST + ST - 1]);
+      }
     }
   }
 
-  // split-K: every thread's partial goes to the workspace; the last split
+  // split-K: every thread's partials go to the workspace; the last split
   // to arrive sums them in split order (per thread, so per wave) and goes on
   __syncthreads();  // the ring is idle: its first word serves as the flag
   if (p.split_k > 1) {
-    f32x4 part[1][1] = {{acc}};
-    if (!splitk_reduce<1, 1, kDecWaves * 64>(p, part, blockIdx.x, split, tid, reinterpret_cast<int*>(lds)))
+    f32x4 part[MT][1];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) part[t][0] = acc[t];
+    if (!splitk_reduce<MT, 1, kDecWaves * 64>(p, part, blockIdx.x, split, tid, reinterpret_cast<int*>(lds)))
       return;
-    acc = part[0][0];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = part[t][0];
     __syncthreads();
   }
-  // the eight partial tiles summed through LDS in wave order
-  f32x4* red = reinterpret_cast<f32x4*>(lds);  // [wave][64]
-  red[wave * 64 + lane] = acc;
-  __syncthreads();
-  if (wave != 0) return;
-  f32x4 sum = red[lane];
+  // the eight partial tiles summed through LDS in wave order; wave t stores
+  // activation tile t
+  f32x4* red = reinterpret_cast<f32x4*>(lds);  // [wave][tile][64]
 #pragma unroll
-  for (int w = 1; w < kDecWaves; ++w) sum += red[w * 64 + lane];
-  const int64_t m = r16;
+  for (int t = 0; t < MT; ++t) red[(wave * MT + t) * 64 + lane] = acc[t];
+  __syncthreads();
+  if (wave >= MT) return;
+  f32x4 sum = red[wave * 64 + lane];
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) sum += red[(w * MT + wave) * 64 + lane];
+  const int64_t m = 16 * wave + r16;
   const float sa_m = (KIND == kChannelwise && m < p.M) ? p.sa[m] : 1.0f;
   store_out4<KIND>(p, m, n0 + 4 * g, sum, sa_m);
 }
@@ -2045,17 +2065,20 @@ hipError_t launch_panel(const GemmArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The decode stream takes whole 128-deep K blocks and 32-bit DMA offsets
-// (the last byte of the last row of either operand within 2^32 - 1).
+// The decode stream takes whole 128-deep K blocks, 32-bit DMA offsets (the
+// last byte of the last row of either operand within 2^32 - 1) and two ring
+// slots per wave beside its scale table in the LDS.
+template <int KIND>
 bool decode_eligible(const GemmArgs& p) {
   const uint64_t lim = 0xFFFFFFFFull;
   return p.K % 128 == 0 && (uint64_t)(p.N - 1) * (uint64_t)p.ldb + (uint64_t)p.K <= lim &&
-         (uint64_t)(p.M - 1) * (uint64_t)p.lda + (uint64_t)p.K <= lim;
+         (uint64_t)(p.M - 1) * (uint64_t)p.lda + (uint64_t)p.K <= lim &&
+         2 * kDecWaves * decode_slot_bytes(p.M) + decode_scale_bytes(p.K, KIND, p.M) <= 163840;
 }
 
-template <int KIND>
-hipError_t launch_decode(const GemmArgs& p, hipStream_t stream) {
-  auto kern = gemm_decode_kernel<KIND>;
+template <int KIND, int MT>
+hipError_t launch_decode_t(const GemmArgs& p, hipStream_t stream) {
+  auto kern = gemm_decode_kernel<KIND, MT>;
   static bool lds_attr_set = false;
   if (!lds_attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -2067,7 +2090,7 @@ hipError_t launch_decode(const GemmArgs& p, hipStream_t stream) {
   // as fit 160 KB (at most kDecMaxWaveSlots); more workgroups, as many as fit
   // 80 KB (two per compute unit); never more than a wave has blocks, plus one
   const int64_t tiles = (p.N + 15) / 16;
-  const size_t fixed = decode_scale_bytes(p.K, KIND), slot = decode_slot_bytes(p.M) * kDecWaves;
+  const size_t fixed = decode_scale_bytes(p.K, KIND, p.M), slot = decode_slot_bytes(p.M) * kDecWaves;
   const size_t budget = (tiles <= 256 ? (size_t)163840 : (size_t)81920);
   int64_t ns = budget > fixed ? (int64_t)((budget - fixed) / slot) : 0;
   int64_t per_wave = ((p.K / 128) + kDecWaves - 1) / kDecWaves;
@@ -2084,6 +2107,15 @@ hipError_t launch_decode(const GemmArgs& p, hipStream_t stream) {
   if (q.split_k > 1 && tiles > kMaxSplitTiles) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles, (unsigned)q.split_k), dim3(kDecWaves * 64), lds, stream, q);
   return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_decode(const GemmArgs& p, hipStream_t stream) {
+  switch (decode_tiles(p.M)) {
+    case 1: return launch_decode_t<KIND, 1>(p, stream);
+    case 2: return launch_decode_t<KIND, 2>(p, stream);
+    default: return launch_decode_t<KIND, 4>(p, stream);
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int NSTAGE>
@@ -2208,12 +2240,26 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
     case 25:
       if (KIND == kBlockwise || !panel_eligible<KIND>(p)) return launch_256<KIND>(p, stream);
       return launch_panel<256, 256, 2, 4, kChannelwise, 5>(p, stream);
-    case 26:  // FP8_VARIANT_DECODE; past its DMA offsets the skinny kernel (same sums)
-      if (p.M > 16) return hipErrorInvalidValue;
-      if (decode_eligible(p)) return launch_decode<KIND>(p, stream);
-      hipLaunchKernelGGL((gemm_skinny_kernel<1, KIND, 0>), dim3((unsigned)((p.N + 15) / 16)),
-                         dim3(kStreamWaves * 64), 0, stream, p, QuantArgs{});
-      return hipGetLastError();
+    case 26: {  // FP8_VARIANT_DECODE
+      if (p.M > 64) return hipErrorInvalidValue;
+      if (decode_eligible<KIND>(p)) return launch_decode<KIND>(p, stream);
+      // past its DMA offsets or its LDS: the skinny kernel (M <= 32; the same
+      // sums when unsplit), else the 64x64 tile, unsplit
+      GemmArgs q = p;
+      q.split_k = 1;
+      q.k_tiles_per_split = (int)(p.K / 128);
+      if (p.M <= 32) {
+        if (p.M <= 16)
+          hipLaunchKernelGGL((gemm_skinny_kernel<1, KIND, 0>), dim3((unsigned)((p.N + 15) / 16)),
+                             dim3(kStreamWaves * 64), 0, stream, q, QuantArgs{});
+        else
+          hipLaunchKernelGGL((gemm_skinny_kernel<2, KIND, 0>), dim3((unsigned)((p.N + 15) / 16)),
+                             dim3(kStreamWaves * 64), 0, stream, q, QuantArgs{});
+        return hipGetLastError();
+      }
+      q.k_tiles_per_split = (int)((p.K + 511) / 512);
+      return launch_tile<64, 64, 2, 2, 512, KIND>(q, stream);
+    }
     default: return hipErrorInvalidValue;
   }
 }
@@ -2261,7 +2307,7 @@ VariantInfo variant_info(int variant) {
     case 23: return {32, 32, 128, 1, true};
     case 24: return {64, 32, 128, 2, true};
     case 25: return {256, 256, 128, 8, true};
-    case 26: return {16, 16, 1024, 8, true};
+    case 26: return {64, 16, 1024, 8, true};
     default: return {0, 0, 0, 0, false};
   }
 }
@@ -2287,8 +2333,8 @@ void decode_split_plan(int64_t K, int split_k, int* splits, int* per) {
 
 size_t variant_workspace_bytes(int variant, int split_k, int64_t M, int64_t N) {
   if (split_k <= 1 || variant == 0) return 0;
-  if (variant == 26)  // one 16-byte partial per thread of the 512 per tile and split
-    return kCounterBytes + (size_t)((N + 15) / 16) * split_k * kDecWaves * 64 * 16;
+  if (variant == 26)  // one 16-byte partial per thread of the 512 and activation tile, per tile and split
+    return kCounterBytes + (size_t)((N + 15) / 16) * split_k * decode_tiles(M) * kDecWaves * 64 * 16;
   const VariantInfo v = variant_info(variant);
   const int64_t tiles = variant_tiles(variant, M, N);
   return kCounterBytes + (size_t)tiles * split_k * v.bm * v.bn * sizeof(float);

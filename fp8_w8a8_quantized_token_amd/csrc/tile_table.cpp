@@ -283,8 +283,8 @@ bool tables_enabled() {
 
 int default_config(int kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* out) {
   // Measured on MI355X (o_proj, qkv, down, gate_up and the blockwise shapes,
-  // HBM-resident weights): up to 16 rows the decode stream or the
-  // register-staged weight stream (below), up to 32 rows the latter, then,
+  // HBM-resident weights): up to 32 rows the decode stream or the
+  // register-staged weight stream (below), then,
   // for K % 128 == 0, the panel-ring LDS-DMA tiles: 64x64 up to M = 256 (deep
   // ring for channelwise), 128x64 up to 512 (deep ring for channelwise), the
   // 8-wave 128x128 up to 1024, then 256x128, or 256x256 where it gives at
@@ -313,6 +313,13 @@ int default_config(int kind, int64_t N, int64_t K, int64_t M, fp8_tile_config* o
     // round from 6 KB deep rows (down 4096x12288 12.0-13.2 against 13.9-16.6,
     // 4096x7168 8.2-8.7 against 9.2-11.1); on shallower ones (o_proj
     // 4096x4096, 3072x4096) the register-staged stream, 0.3-0.8 us ahead.
+    c.variant = FP8_VARIANT_DECODE;
+  } else if (M > 16 && M <= 32 && k128 && groups <= 256) {
+    // two activation tiles per wave, one round of workgroups: the decode
+    // stream again (o_proj 4096x4096 M = 32 7.3 against 8.7 us, down
+    // 4096x12288 15.7 against 17.9, blockwise 3072x4096 7.7 against 9.3,
+    // 4096x1536 5.6 against 7.9); with more groups its 6 KB slots leave
+    // one workgroup per compute unit and it falls behind
     c.variant = FP8_VARIANT_DECODE;
   } else if (M <= 32) {
     c.variant = FP8_VARIANT_SKINNY;

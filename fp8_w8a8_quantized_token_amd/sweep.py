@@ -45,16 +45,16 @@ def candidates(kind, m, n, k):
     if m <= 32:
         # the skinny kernel re-reads all M activation rows per 16 weight rows;
         # from M = 8 the 32- and 64-wide deep-ring tiles can win on large N;
-        # up to 16 rows the LDS-DMA decode stream
+        # up to 64 rows the LDS-DMA decode stream
         c = [("skinny", 1)]
-        if m <= 16 and k128:
+        if k128:
             c += [("decode", 1)]
         if m >= 8 and k128:
             c += [("t32x32deep", 1), ("t32x32deep", 2), ("t32x32deep", 4), ("t64x32deep", 1),
                   ("t64x32deep", 2), ("t64x32deep", 4), ("t64x64deep", 1), ("t64x64deep", 2),
                   ("t64x64deep", 4), ("t64x64panel", 1), ("t64x64panel", 2), ("t64x64panel", 4)]
         return c
-    c = []
+    c = [("decode", 1)] if (k128 and m <= 64) else []
     if m <= 1024:
         c += [("t64x64", 1), ("t128x64k256", 1), ("t64x128k256", 1), ("t128x128k256", 1)]
         if k128:

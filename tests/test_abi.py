@@ -279,7 +279,7 @@ def test_workspace_errors(lib):
     assert r == _lib.FP8_ERR_INVALID and "skinny" in _err(lib)
     dec = _lib.TileConfig(_lib.VARIANTS["decode"], 0, 0, 0, 1, 0)
     assert lib.fp8_scaled_mm_workspace_size(0, 16, 4096, 4096, ctypes.byref(dec)) == 0
-    for m, k in ((17, 1024), (16, 1040)):   # M, K % 128
+    for m, k in ((65, 1024), (16, 1040)):   # M, K % 128
         bad = _lib.TileConfig(_lib.VARIANTS["decode"], 0, 0, 0, 1, 0)
         r = lib.fp8_scaled_mm_channelwise_ex(FAKE, FAKE, FAKE, FAKE, None, FAKE, m, 256, k, k,
                                              k, 256, None, 0, ctypes.byref(bad), None)
@@ -290,6 +290,9 @@ def test_workspace_errors(lib):
     dec5 = _lib.TileConfig(_lib.VARIANTS["decode"], 0, 0, 0, 5, 0)
     assert lib.fp8_scaled_mm_workspace_size(0, 4, 4100, 12288, ctypes.byref(dec5)) == \
         65536 * 4 + 257 * 4 * 512 * 16
+    # 33-64 rows: four 16-row activation tiles, four partials per thread
+    assert lib.fp8_scaled_mm_workspace_size(0, 40, 4100, 12288, ctypes.byref(dec5)) == \
+        65536 * 4 + 257 * 4 * 4 * 512 * 16
     dec2 = _lib.TileConfig(_lib.VARIANTS["decode"], 0, 0, 0, 2, 0)
     r = lib.fp8_scaled_mm_channelwise_ex(FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 256, 1024, 1024,
                                          1024, 256, None, 0, ctypes.byref(dec2), None)
@@ -418,7 +421,8 @@ def test_table_blockwise_kind(lib, table_dir):
 
 def test_default_heuristic_shapes(lib):
     assert _default(lib, 0, 4096, 4096, 1)["variant"] == "skinny"
-    assert _default(lib, 0, 4096, 4096, 32)["variant"] == "skinny"
+    assert _default(lib, 0, 4096, 4096, 32)["variant"] == "decode"   # 17-32 rows, one round
+    assert _default(lib, 0, 4096, 4100, 32)["variant"] == "skinny"   # K % 128 != 0
     for m in (64, 512, 4096, 8192):
         c = _default(lib, 0, 4096, 4096, m)
         assert c["variant"] != "skinny" and c["split_k"] >= 1
@@ -505,7 +509,7 @@ def test_default_split_k_at_small_m(lib):
     assert d(cw, 4096, 4096, 256) == (dv, 1)     # beyond M = 128
     assert d(bw, 1536, 7168, 96) == (pv, 4)
     assert d(bw, 4096, 2048, 64) == (pv, 1)      # 16 stages
-    assert d(cw, 4096, 4096, 32)[0] == "skinny"
+    assert d(cw, 4096, 4096, 32)[0] == "decode"
 
 
 def test_default_narrow_tile_on_uneven_skinny_rounds(lib):
@@ -518,7 +522,8 @@ def test_default_narrow_tile_on_uneven_skinny_rounds(lib):
     assert d(cw, 14336, 4096, 8) == ("t32x32deep", 1)
     assert d(cw, 5120, 5120, 32) == ("t32x32deep", 2)    # 320 groups, 40 stages
     assert d(bw, 12288, 7168, 32) == ("t32x32deep", 2)   # N >= 12288
-    assert d(cw, 4096, 4096, 32)[0] == "skinny"          # whole rounds
+    assert d(cw, 4096, 4096, 32)[0] == "decode"          # one round: the decode stream
+    assert d(cw, 8192, 4096, 32) == ("skinny", 1)        # two whole rounds
 
 
 def test_default_decode_stream_at_decode_sizes(lib):
@@ -538,4 +543,6 @@ def test_default_decode_stream_at_decode_sizes(lib):
     assert d(bw, 3072, 4096, 1)[0] == "skinny"
     assert d(cw, 4096, 5120, 1)[0] == "skinny"
     assert d(cw, 4096, 12304, 1)[0] == "skinny"          # K % 128 != 0
-    assert d(cw, 4096, 12288, 17)[0] == "skinny"         # M > 16
+    assert d(cw, 4096, 12288, 17)[0] == "decode"         # 17-32 rows, one round
+    assert d(cw, 6144, 4096, 17)[0] != "decode"          # 17-32 rows, more groups than CUs
+    assert d(cw, 4096, 12288, 33)[0] != "decode"

@@ -136,6 +136,28 @@ DECODE_CASES = [(m, n, k) for (m, n, k) in ((1, 256, 128), (3, 384, 1152), (8, 6
                                              (5, 392, 1408))]
 
 
+# Two and four activation tiles (M <= 32, 64): ragged last tile, one and
+# several blocks per wave; the blockwise M = 64 case does not fit its scale
+# table beside the ring and runs the 64x64 tile instead.
+DECODE_WIDE_CASES = [("cw", 17, 392, 1152), ("cw", 32, 4224, 2048), ("cw", 33, 512, 4096),
+                     ("cw", 64, 4096, 1024), ("bw", 24, 384, 4096), ("bw", 40, 512, 1024),
+                     ("bw", 64, 256, 2048)]
+
+
+@pytest.mark.parametrize("kind,m,n,k", DECODE_WIDE_CASES, ids=[f"{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in DECODE_WIDE_CASES])
+def test_decode_variant_wide_m(kind, m, n, k):
+    cfg = ops.make_config("decode")
+    if kind == "cw":
+        _, o1 = _channelwise_case("decode-wide", m, n, k, 0.01, True, config=cfg, sample=False)
+        if m <= 32:
+            _, o2 = _channelwise_case("decode-wide", m, n, k, 0.01, True, config=ops.make_config("skinny"),
+                                      sample=False)
+            assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    else:
+        _, o1 = _blockwise_case("decode-wide", m, n, k, config=cfg, with_bias=True)
+        _, o3 = _blockwise_case("decode-wide", m, n, k, config=ops.make_config("decode", 2), with_bias=True)
+
+
 @pytest.mark.parametrize("m,n,k", DECODE_CASES, ids=[f"M{m}-N{n}-K{k}" for m, n, k in DECODE_CASES])
 def test_decode_variant_parity_and_same_bits_as_skinny(m, n, k):
     """The decode stream against the oracle, and bit-identical to the skinny
