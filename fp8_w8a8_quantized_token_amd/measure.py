@@ -26,6 +26,7 @@ Usage: python -m fp8_w8a8_quantized_token_amd.measure [--workloads small,o_proj,
        [--calls 100] [--warmup 20] [--out FILE]
 """
 import argparse
+import json
 import os
 import math
 import sys
@@ -606,6 +607,109 @@ def row(cfg, kind, n, k, m, r, bias):
             f"{percentile(r['linear'], 50):.1f} ({r['launches']}) | {percentile(r['hot'], 50):.1f} |")
 
 
+COUNTER_CASES = ("cw:4096:4096:64,cw:4096:4096:128,cw:4096:4096:256,bw:4096:4096:64,bw:4096:4096:128,"
+                 "bw:4096:4096:256,bw:3072:4096:64,bw:4096:1536:64,cw:4096:12288:64,bw:7168:7168:64")
+COUNTER_CALLS = 3
+
+
+def counter_run(cases):
+    """Driver for rocprofv3 counter and trace runs: a plain 256 MiB device
+    copy (the byte counters' calibration), then, for every kind:N:K:M case,
+    COUNTER_CALLS GEMMs with the default tile config, each on its own weight
+    copy (so the weight comes from HBM), synchronised one by one."""
+    dev = torch.device("cuda:0")
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    for case in cases.split(","):
+        kind_s, n, k, m = case.split(":")
+        n, k, m = int(n), int(k), int(m)
+        w = synth.weights("counters", n, k).to(torch.bfloat16).to(dev)
+        x = synth.activations("counters", m, k).to(dev)
+        if kind_s == "cw":
+            wq, ws = ops.quant_per_token(w)
+            a, sa = ops.quant_per_token(x)
+            copies = [(wq.clone(), ws.clone()) for _ in range(COUNTER_CALLS)]
+            cfg, _ = ops.tile_config(ops.KIND_CHANNELWISE, n, k, m)
+            run = [lambda b=b, s_=s_: ops.scaled_mm_channelwise(a, b, sa, s_) for b, s_ in copies]
+        else:
+            wq, _ = ops.quant_per_token_group(w, 128, row_alignment=1)
+            ws = synth.positive_scales(f"counters/{n}/{k}", (n // 128, k // 128)).to(dev)
+            a, sa = ops.quant_per_token_group(x, 128, row_alignment=4)
+            copies = [(wq.contiguous().clone(), ws.clone()) for _ in range(COUNTER_CALLS)]
+            cfg, _ = ops.tile_config(ops.KIND_BLOCKWISE, n, k, m)
+            run = [lambda b=b, s_=s_: ops.scaled_mm_blockwise(a, b, sa, s_, m=m) for b, s_ in copies]
+        torch.cuda.synchronize()
+        for f in run:
+            f()
+            torch.cuda.synchronize()
+        print(json.dumps({"case": case, "variant": cfg["variant"], "split_k": cfg["split_k"]}), flush=True)
+        del copies, w, x
+        torch.cuda.empty_cache()
+
+
+def counter_summary(fetch_csv, write_csv, trace_csv, cases, command):
+    """Table of the counter_run dispatches: per case the kernel, its average
+    duration (kernel trace), workgroups, and HBM bytes per call from
+    FETCH_SIZE and WRITE_SIZE scaled by the calibration copy, against the
+    algorithmic bytes."""
+    import csv
+    import re
+
+    def rows(path):
+        with open(path) as f:
+            return list(csv.DictReader(f))
+
+    def per_dispatch(path):
+        d = {}
+        for r in rows(path):
+            key = int(r["Dispatch_Id"])
+            d.setdefault(key, [re.sub(r"\(.*", "", r["Kernel_Name"]), int(r["Grid_Size"]), 0.0])
+            d[key][2] += float(r["Counter_Value"])
+        return [v for _, v in sorted(d.items())]
+
+    def gemm_only(ds):
+        # the calibration copy (the copy dispatch with the largest count)
+        # first, then every case's quantizer launches and GEMMs; keep the GEMMs
+        ci = max((i for i, v in enumerate(ds) if "copyBuffer" in v[0]), key=lambda i: ds[i][2])
+        return ds[ci][2], [v for v in ds[ci + 1:] if "gemm_" in v[0]]
+
+    cf, fetch = gemm_only(per_dispatch(fetch_csv))
+    cw, write = gemm_only(per_dispatch(write_csv))
+    ff, fw = 262144.0 / cf, 262144.0 / cw
+    trace = [r for r in rows(trace_csv)]
+    trace.sort(key=lambda r: int(r["Dispatch_Id"]))
+    ci = max((i for i, r in enumerate(trace) if "copyBuffer" in r["Kernel_Name"]),
+             key=lambda i: int(trace[i]["End_Timestamp"]) - int(trace[i]["Start_Timestamp"]))
+    gemms = [r for r in trace[ci + 1:] if "gemm_" in r["Kernel_Name"]]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in gemms]
+    wgs = [int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])) * int(r["Grid_Size_Y"]) *
+           int(r["Grid_Size_Z"]) for r in gemms]
+    out = [command, "",
+           f"calibration: plain 256 MiB device copy reads FETCH_SIZE {cf:.1f} KiB (factor {ff:.4f}), "
+           f"WRITE_SIZE {cw:.1f} KiB (factor {fw:.4f})", "",
+           "| case | kernel | workgroups | us per call | HBM MB per call | algorithmic MB | ratio | GB/s (algorithmic) |",
+           "|---|---|---|---|---|---|---|---|"]
+    per = COUNTER_CALLS
+    for i, case in enumerate(cases.split(",")):
+        kind_s, n, k, m = case.split(":")
+        n, k, m = int(n), int(k), int(m)
+        sl = slice(i * per, (i + 1) * per)
+        f, w, d = fetch[sl], write[sl], durs[sl]
+        if not f:
+            break
+        hbm = sum(x[2] * ff + y[2] * fw for x, y in zip(f, w)) * 1024 / len(f)
+        alg = m * k + n * k + 2 * m * n + (4 * m + 4 * n if kind_s == "cw" else
+                                             4 * m * (k // 128) + 4 * (n // 128) * (k // 128))
+        us = sum(d) / len(d)
+        name = re.sub(r"^void fp8w8a8::", "", f[0][0])
+        out.append(f"| {kind_s} {n}x{k} M={m} | `{name}` | {wgs[i * per]} | {us:.2f} | {hbm / 1e6:.2f} | "
+                   f"{alg / 1e6:.2f} | {hbm / alg:.2f} | {alg / us / 1e3:.0f} |")
+    return "\n".join(out) + "\n"
+
+
 def traffic_summary(fetch_csv, write_csv, label, symbol, n, k, bm, bn, threads, command_tail):
     """Summary text of two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE,
     csv) of ``bench.py --profile-label LABEL``: the counters of each labelled
@@ -692,10 +796,22 @@ def main(argv=None):
                     help="time plain device copies and reductions at the small-M linears' byte counts")
     ap.add_argument("--probes", action="store_true",
                     help="run the probe kernels: HBM read stream, L2 feed, FP8 MFMA rate and clock")
+    ap.add_argument("--counter-run", nargs="?", const=COUNTER_CASES, default=None,
+                    help="run the kind:N:K:M GEMMs (default: the mid-M cases) after a calibration "
+                         "copy, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE and --kernel-trace runs")
+    ap.add_argument("--counter-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "TRACE_CSV"),
+                    help="summarise those three runs (no GPU needed)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs of the benchmark's "
                          "dominant kernel (written to profiles/, no GPU needed)")
     args = ap.parse_args(argv)
+    if args.counter_summary:
+        print(counter_summary(*args.counter_summary, COUNTER_CASES, ""))
+        return 0
+    if args.counter_run is not None:
+        _lib.load()
+        counter_run(args.counter_run)
+        return 0
     if args.traffic_summary:
         txt = traffic_summary(*args.traffic_summary, label="gemm_blockwise[t256x256bw16]",
                               symbol="gemm_panel_kernel<256, 256, 2, 4, 1, 4, true>", n=4096, k=4096,
