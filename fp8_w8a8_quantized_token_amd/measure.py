@@ -710,6 +710,50 @@ def counter_summary(fetch_csv, write_csv, trace_csv, cases, command):
     return "\n".join(out) + "\n"
 
 
+def step_table(bench_json, trace_csv, steps):
+    """The per-(kind, M) table of the benchmark step from a kernel trace of
+    ``bench.py --per-m --steps S --no-per-config --no-cpu-baseline``: the
+    step's launches (one kernel each, in the order of the JSON's per_m) are
+    the last S x L kernel dispatches; each row is the median over the S timed
+    steps, with the launch's algorithmic flops and bytes."""
+    import csv
+    import re
+    import statistics
+
+    with open(bench_json) as f:
+        line = [ln for ln in f if ln.startswith("{")][-1]
+    per_m = json.loads(line)["per_m"]
+    keys = list(per_m)
+    with open(trace_csv) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+    rows = [r for r in rows if "copyBuffer" not in r["Kernel_Name"] and "zero_words" not in r["Kernel_Name"]]
+    n = len(keys)
+    last = rows[-steps * n:]
+    out = ["| config | kind | M | kernel | GPU median µs | TFLOP/s | GB/s | f_bw | f_mfma | roofline µs | quant µs (GB/s) |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
+    med = {}
+    name = {}
+    for j, key in enumerate(keys):
+        us = [(int(last[s * n + j]["End_Timestamp"]) - int(last[s * n + j]["Start_Timestamp"])) / 1e3
+              for s in range(steps)]
+        med[key] = statistics.median(us)
+        name[key] = re.sub(r"^void fp8w8a8::", "", re.sub(r"\(.*", "", last[j]["Kernel_Name"]))
+    for kind in ("channelwise", "blockwise"):
+        ms = sorted({int(k.split("M=")[1]) for k in keys if k.startswith(kind + "/")})
+        for m in ms:
+            g = f"{kind}/gemm/M={m}" if f"{kind}/gemm/M={m}" in per_m else f"{kind}/linear/M={m}"
+            q = f"{kind}/quant/M={m}"
+            us, fl, by = med[g], per_m[g]["flops"], per_m[g]["bytes"]
+            roof = max(fl / 5e15, by / 8e12) * 1e6
+            qcol = "fused" if q not in per_m else f"{med[q]:.1f} ({per_m[q]['bytes'] / med[q] / 1e3:.0f})"
+            out.append(f"| o_proj 4096×4096 | {kind} | {m} | `{name[g]}` | {us:.1f} | {fl / us / 1e6:.0f} | "
+                       f"{by / us / 1e3:.0f} | {by / us / 8e6:.2f} | {fl / us / 5e9:.3f} | {roof:.2f} | {qcol} |")
+    total = sum(med.values())
+    out.append("")
+    out.append(f"sum of the step's kernel medians: {total:.0f} µs")
+    return "\n".join(out) + "\n"
+
+
 def traffic_summary(fetch_csv, write_csv, label, symbol, n, k, bm, bn, threads, command_tail):
     """Summary text of two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE,
     csv) of ``bench.py --profile-label LABEL``: the counters of each labelled
@@ -801,10 +845,15 @@ def main(argv=None):
                          "copy, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE and --kernel-trace runs")
     ap.add_argument("--counter-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "TRACE_CSV"),
                     help="summarise those three runs (no GPU needed)")
+    ap.add_argument("--step-table", nargs=3, metavar=("BENCH_JSON_LOG", "TRACE_CSV", "STEPS"),
+                    help="per-(kind, M) table of the benchmark step from a kernel trace (no GPU needed)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs of the benchmark's "
                          "dominant kernel (written to profiles/, no GPU needed)")
     args = ap.parse_args(argv)
+    if args.step_table:
+        print(step_table(args.step_table[0], args.step_table[1], int(args.step_table[2])))
+        return 0
     if args.counter_summary:
         print(counter_summary(*args.counter_summary, COUNTER_CASES, ""))
         return 0
