@@ -832,9 +832,9 @@ __device__ __forceinline__ void wait_panels(int64_t c) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int KIND, int NP, bool MF16 = false>
+template <int BM, int BN, int WM, int WN, int KIND, int NP>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
-  using G = PanelGeom<BM, BN, WM, WN, KIND, NP, MF16>;
+  using G = PanelGeom<BM, BN, WM, WN, KIND, NP>;
   constexpr bool BW = KIND != kChannelwise;
   // blockwise fp32 scales: per-stage partial tiles promoted in fp32; E8M0
   // scales: exponents handed to the block-scaled MFMA, no partial tile
@@ -848,10 +848,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   constexpr int SLOT = G::SLOT;
   constexpr int PPA = BM / 8 / NW;     // DMA instructions per wave per A panel
   constexpr int PPB = BN / 8 / NW;     // ... per B panel (rows only)
-  // blockwise: the per-stage scale copies ride with the B panel, or with the
-  // A panel in the 16x16 body
-  constexpr int PPB_ALL = PPB + (BW && !MF16 ? 2 : 0);
-  constexpr int PPA_ALL = PPA + (BW && MF16 ? 2 : 0);
+  // blockwise: the per-stage scale copies ride with the B panel
+  constexpr int PPB_ALL = PPB + (BW ? 2 : 0);
+  constexpr int PPA_ALL = PPA;
   constexpr int SA_OFF = G::SC_OFF;    // scale area inside its slot
   constexpr int SB_OFF = SA_OFF + G::SA_BYTES;
   constexpr int SA_LANES = BM / 4 / NW;  // lanes of a wave's 16-byte activation-scale DMA
@@ -968,127 +967,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
     const uint32_t sbase = lds_base + (uint32_t)slot * SLOT;
     issue_rows(p.a + kt * BK, (uint32_t)m0, (uint32_t)(p.M - 1), (uint32_t)p.lda,
                sbase + wave * PPA * 1024, IntC<PPA>());
-    if constexpr (BW && MF16) issue_scales(kt, sbase);
   };
   auto issue_b = [&](int64_t kt, int slot) {
     const uint32_t sbase = lds_base + (uint32_t)slot * SLOT;
     issue_rows(p.b + kt * BK, (uint32_t)n0, (uint32_t)(p.N - 1), (uint32_t)p.ldb,
                sbase + wave * PPB * 1024, IntC<PPB>());
-    if constexpr (BW && !MF16) issue_scales(kt, sbase);
+    if constexpr (BW) issue_scales(kt, sbase);
   };
-  if constexpr (MF16) {
-    // 16x16x128 MFMAs, one per 128-deep block: the blockwise partial of a
-    // (16-row, 16-column) piece is 4 registers, so a 256x256 tile fits in
-    // registers. A stage is one block; at its start every wave reads its four
-    // B fragments, then streams its eight A fragments, promoting each MFMA
-    // result with sa[m] * sb right away. The per-stage scales ride with the A
-    // panel, so the B slot can be refilled as soon as the B fragments are in
-    // registers (see the issue order below).
-    static_assert(BW, "the 16x16 body serves the blockwise kinds");
-    constexpr int FI = WTM / 16, FJ = WTN / 16;
-    const int g = lane >> 4, r16 = lane & 15;
-    // lane's chunks of a 16-row fragment: row r16, K bytes [32g, 32g + 32)
-    uint32_t fo16[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) fo16[t] = (uint32_t)(r16 * BK + (swz<8>(r16, 2 * g + t) << 4));
-    auto frag16 = [&](const uint8_t* base) {
-      return join(*reinterpret_cast<const uint4*>(base + fo16[0]),
-                  *reinterpret_cast<const uint4*>(base + fo16[1]));
-    };
-    auto wrap = [](int x) { return x >= NP ? x - NP : x; };
-    const int64_t np_all = 2 * nst;
-    auto issue_panel = [&](int64_t q, int slot) {
-      if (q & 1) issue_a(kt_begin + (q >> 1), slot);
-      else issue_b(kt_begin + (q >> 1), slot);
-    };
-    f32x4 acc16[FI][FJ];
-#pragma unroll
-    for (int i = 0; i < FI; ++i)
-#pragma unroll
-      for (int j = 0; j < FJ; ++j) acc16[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // Panel q = B (q even) or A (q odd) of stage q / 2 goes to slot q % 4, in
-    // order. Stage s's B slot is free once every wave has its B fragments in
-    // registers (second barrier of the stage): it takes B(s+2). Its A slot,
-    // which also holds the stage's scales, is free at the next stage's first
-    // barrier: it takes A(s+2) then. So A panels get one stage of lead and B
-    // panels nearly two.
-    static_assert(NP == 4, "the 16x16 body's issue order assumes a four-slot ring");
-    int64_t issued = 0;
-    if (nst > 0) {
-      issued = np_all < NP ? np_all : NP;
-      for (int64_t q = 0; q < issued; ++q) issue_panel(q, (int)q);
-    }
-    int cs = 0;  // slot of stage s's B panel; its A panel is in wrap(cs + 1)
-    for (int64_t s = 0; s < nst; ++s) {
-      const int cs1 = wrap(cs + 1);
-      // stage s complete: what was issued after it (from a B panel on) may
-      // still be outstanding
-      {
-        const int64_t later = issued - 2 * s - 2;
-        wait_panels<NP - 2, PPB_ALL, PPA_ALL>(later < NP - 2 ? later : NP - 2);
-      }
-      wait_vmcnt_lgkm0<63>();
-      __builtin_amdgcn_s_barrier();
-      // every wave is past stage s-1: its A slot (wrap(cs + 3)) takes A(s+1)
-      if (s > 0 && issued < np_all) {
-        issue_panel(issued, wrap(cs + 3));
-        ++issued;
-      }
-      const uint8_t* pb = lds + cs * SLOT;
-      const uint8_t* pslot_a = lds + cs1 * SLOT;
-      const uint8_t* pa = pslot_a + (wm * WTM) * BK;
-      i32x8 fb[FJ];
-#pragma unroll
-      for (int j = 0; j < FJ; ++j) fb[j] = frag16(pb + (wn * WTN + j * 16) * BK);
-      // the B fragments are read before the wait below and the slot's refill
-      __asm__ volatile("" ::: "memory");
-      wait_vmcnt_lgkm0<63>();
-      __builtin_amdgcn_s_barrier();
-      if (issued < np_all) {  // every wave has its B fragments: the B slot takes B(s+2)
-        issue_panel(issued, cs);
-        ++issued;
-      }
-      if constexpr (KIND == kBlockwiseE8) {
-        // power-of-two scales: their biased exponents go to the MFMA, which
-        // scales the products itself; one accumulator, no promotion step
-        const int eb = (int)(*reinterpret_cast<const uint32_t*>(pslot_a + SB_OFF + wave * 16 +
-                                                                ((wn * WTN) >> 7) * 4) >> 23);
-        i32x8 fa = frag16(pa);
-#pragma unroll
-        for (int i = 0; i < FI; ++i) {
-          const int ea = (int)(*reinterpret_cast<const uint32_t*>(
-                                   pslot_a + SA_OFF + (wm * WTM + i * 16 + r16) * 4) >> 23);
-          i32x8 fn;
-          if (i + 1 < FI) fn = frag16(pa + (i + 1) * 16 * BK);
-#pragma unroll
-          for (int j = 0; j < FJ; ++j) acc16[i][j] = mfma_fp8_e8(fb[j], fa, acc16[i][j], eb, ea);
-          if (i + 1 < FI) fa = fn;
-        }
-        cs = wrap(cs + 2);
-        continue;
-      }
-      const float sb = *reinterpret_cast<const float*>(pslot_a + SB_OFF + wave * 16 + ((wn * WTN) >> 7) * 4);
-      i32x8 fa = frag16(pa);
-#pragma unroll
-      for (int i = 0; i < FI; ++i) {
-        const float sc =
-            *reinterpret_cast<const float*>(pslot_a + SA_OFF + (wm * WTM + i * 16 + r16) * 4) * sb;
-        i32x8 fn;
-        if (i + 1 < FI) fn = frag16(pa + (i + 1) * 16 * BK);
-        f32x4 t[FJ];
-#pragma unroll
-        for (int j = 0; j < FJ; ++j) t[j] = mfma_fp8(fb[j], fa, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int j = 0; j < FJ; ++j) acc16[i][j] += t[j] * sc;
-        if (i + 1 < FI) fa = fn;
-      }
-      cs = wrap(cs + 2);
-    }
-    // the ring is idle from here on: its first word serves as the split flag
-    if (p.split_k > 1 && !splitk_reduce<FI, FJ, NT>(p, acc16, tile, split, tid, reinterpret_cast<int*>(lds)))
-      return;
-    store_tile16<BM, BN, WM, WN, KIND>(p, acc16, lds, m0, n0, wm, wn, lane, tid);
-  } else {
   // Per-lane byte offsets, within a panel, of the two 16-byte chunks of this
   // lane's A fragment row for each 64-deep half kh (chunks 4kh + 2h, +1). The
   // swizzle depends on the row only through row % 16, the same for every
@@ -1241,7 +1126,273 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   if (p.split_k > 1 && !splitk_reduce<TM, TN, NT>(p, acc, tile, split, tid, reinterpret_cast<int*>(lds)))
     return;
   store_tile<BM, BN, WM, WN, KIND>(p, acc, lds, m0, n0, wm, wn, h, r32, tid);
+}
+
+
+// ---------------------------------------------------------------------------
+// Ping-pong 256x256 tile (K % 128 == 0) on 16x16x128 MFMAs, for channelwise
+// scales, blockwise fp32 scales (each MFMA covers one 128-deep block, and its
+// result joins the accumulator times a_scale[m][kb] * b_scale[nb][kb]) and
+// blockwise E8M0 scales (applied by the block-scaled MFMA).
+// Eight waves, two per SIMD: waves 0-3 (group 0) own output rows 0-127 of the
+// tile, waves 4-7 (group 1) rows 128-255, each wave a 128x64 piece (8 x 4
+// accumulators of 16x16). Both groups run the same sequence of phases, each
+// ending at a workgroup barrier, group 1 one phase behind group 0 (it starts
+// with one barrier more; group 0 ends with one more). A wave alternates
+// memory phases (its share of the ring refills, the LDS fragment and scale
+// reads for its next 16 MFMAs, the waits) and compute phases (those 16 MFMAs
+// and, for fp32 block scales, their promotion), so on every SIMD one wave
+// multiplies while the other loads. The phases are kept apart for the
+// compiler too: no instruction is scheduled across a phase barrier, and the
+// accumulators a compute phase wrote are pinned before it ends.
+// Stage s (one 128-deep K block) is read in two halves h: (s,0) takes the B
+// fragments and A fragments 0-3 (rows 0-63 of the wave's 128), (s,1) A
+// fragments 4-7; group 0 reads half (s,h) in global phase 4s + 2h, group 1 in
+// 4s + 2h + 1. Ring: four slots, B(s) in slot 2s % 4, A(s) in (2s + 1) % 4
+// together with the stage's scales. A wave issues its share of A(s+1) in its
+// memory phase (s,0) -- A(s-1), in that slot, was last read in phase 4s - 1
+// -- and of B(s+2) in (s,1) -- B(s) was last read in phase 4s + 1. Stage s+1
+// is read from phase 4s + 4 on, so both groups wait for their share of it at
+// the end of phase 4s + 3 (group 0 after its compute phase (s,1), group 1
+// after its memory phase (s,1)), when only their B(s+2) share is younger.
+// Grouped calls (masked_m, one expert per blockIdx.z) as in the panel tiles.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int KIND>
+__global__ __launch_bounds__(512) void gemm_pingpong_kernel(GemmArgs p) {
+  constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NP = 4, BK = 128;
+  using G = PanelGeom<BM, BN, WM, WN, KIND, NP, true>;
+  constexpr bool SC = KIND != kChannelwise;  // scales travel with the A panels
+  constexpr bool PROMOTE = KIND == kBlockwise;
+  constexpr bool E8 = KIND == kBlockwiseE8;
+  constexpr int NT = 512, NW = 8;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FI = WTM / 16, FJ = WTN / 16;  // 8 x 4 accumulators per wave
+  constexpr int SLOT = G::SLOT;
+  constexpr int PPA = BM / 8 / NW, PPB = BN / 8 / NW;  // DMA instructions per wave per panel
+  constexpr int SA_OFF = G::SC_OFF;
+  constexpr int SB_OFF = SA_OFF + G::SA_BYTES;
+  constexpr int SA_LANES = BM / 4 / NW;
+  static_assert(G::LDS <= 163840 && BM * BN * 2 <= G::LDS, "ring and output tile fit the LDS");
+  static_assert(2 * PPA + 2 < 64, "vmcnt range");
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave / WN;  // the group is the wave's row half
+  const int wm = grp, wn = wave % WN;
+  const int g16 = lane >> 4, r16 = lane & 15;
+
+  const int64_t tiles_n = (p.N + BN - 1) / BN;
+  const int64_t tiles_m = (p.M + BM - 1) / BM;
+  const int64_t tile = blockIdx.x;
+  int64_t tile_m, tile_n;
+  tile_coords(tile, tiles_m, tiles_n, &tile_m, &tile_n);
+  const int64_t m0 = tile_m * BM;
+  const int64_t n0 = tile_n * BN;
+  if (p.masked_m) {  // tiles wholly past the expert's rows leave before any barrier
+    const int64_t e = blockIdx.z;
+    int64_t rows = p.masked_m[e];
+    rows = rows < 0 ? 0 : (rows > p.M ? p.M : rows);
+    if (m0 >= rows) return;
+    p.M = rows;
+    p.a += e * p.a_es;
+    p.sa += e * p.sa_es;
+    p.b += e * p.b_es;
+    p.sb += e * p.sb_es;
+    p.out += e * p.out_es;
   }
+  const int split = blockIdx.y;
+  const int64_t kt_all = p.K / BK;
+  const int64_t kt_begin = (int64_t)split * p.k_tiles_per_split;
+  int64_t kt_end = kt_begin + p.k_tiles_per_split;
+  if (kt_end > kt_all) kt_end = kt_all;
+  const int64_t nst = kt_end - kt_begin;
+
+  // DMA of panel rows, as in the panel tiles (instruction i of a wave: rows
+  // (wave * PP + i) * 8 .. +7, lane l row + l / 8, logical chunk swz<8> landing
+  // at position l % 8). The per-lane offsets are recomputed at every refill:
+  // kept live across the loop they would take eight registers.
+  const int lrow = lane >> 3;
+  auto issue_rows = [&](const uint8_t* src, uint32_t r0, uint32_t last, uint32_t ld, uint32_t dst, auto pp) {
+    constexpr int PP = decltype(pp)::value;
+    int lr = lrow;
+    __asm__ volatile("" : "+v"(lr));
+#pragma unroll
+    for (int i = 0; i < PP; ++i) {
+      uint32_t row = r0 + (wave * PP + i) * 8 + lr;
+      row = row < last ? row : last;
+      const uint32_t chunk = (uint32_t)(swz<8>(((wave * PP + i) & 1) * 8 + lr, lane & 7) << 4);
+      lds_dma16_s(src, row * ld + chunk, dst + i * 1024);
+    }
+  };
+  // the stage's scales into the scale area of its A slot: activation scales
+  // of rows m0 .. m0+255 (16-byte pieces when the column starts on 16 bytes,
+  // else one scale per lane) and, per wave, the tile's two weight block
+  // scales; one DMA instruction each per wave (lane 0 always active)
+  const bool sa_vec = (p.sa_ld & 3) == 0 && (reinterpret_cast<uintptr_t>(p.sa) & 15) == 0;
+  auto issue_scales = [&](int64_t kt, uint32_t sbase) {
+    const uint8_t* col = reinterpret_cast<const uint8_t*>(p.sa + kt * p.sa_ld);
+    const uint32_t dst = sbase + SA_OFF + wave * SA_LANES * 16;
+    if (sa_vec) {
+      int64_t r = m0 + (int64_t)(wave * SA_LANES + (lane < SA_LANES ? lane : 0)) * 4;
+      if (r > p.sa_ld - 4) r = p.sa_ld - 4;
+      if (lane < SA_LANES) lds_dma16_s(col, (uint32_t)(r * 4), dst);
+    } else {
+      int64_t r = m0 + (int64_t)wave * (SA_LANES * 4) + (lane < SA_LANES * 4 ? lane : 0);
+      if (r > p.sa_ld - 1) r = p.sa_ld - 1;
+      if (lane < SA_LANES * 4) lds_dma4_s(col, (uint32_t)(r * 4), dst);
+    }
+    const int64_t kb_all = p.K / 128;
+    const int64_t nb_last = (p.N + 127) / 128 - 1;
+    int64_t nb = (n0 >> 7) + lane;
+    nb = nb < nb_last ? nb : nb_last;
+    if (lane < G::NBLK)
+      lds_dma4_s(reinterpret_cast<const uint8_t*>(p.sb + kt), (uint32_t)(nb * kb_all * 4),
+                 sbase + SB_OFF + wave * 16);
+  };
+  auto issue_a = [&](int64_t s) {
+    const uint32_t sbase = lds_base + (uint32_t)((2 * s + 1) & 3) * SLOT;
+    issue_rows(p.a + (kt_begin + s) * BK, (uint32_t)m0, (uint32_t)(p.M - 1), (uint32_t)p.lda,
+               sbase + wave * PPA * 1024, IntC<PPA>());
+    if constexpr (SC) issue_scales(kt_begin + s, sbase);
+  };
+  auto issue_b = [&](int64_t s) {
+    const uint32_t sbase = lds_base + (uint32_t)((2 * s) & 3) * SLOT;
+    issue_rows(p.b + (kt_begin + s) * BK, (uint32_t)n0, (uint32_t)(p.N - 1), (uint32_t)p.ldb,
+               sbase + wave * PPB * 1024, IntC<PPB>());
+  };
+
+  // lane's chunks of a 16-row fragment: row r16, K bytes [32 g16, 32 g16 + 32)
+  uint32_t fo16[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) fo16[t] = (uint32_t)(r16 * BK + (swz<8>(r16, 2 * g16 + t) << 4));
+  auto frag16 = [&](const uint8_t* base) {
+    return join(*reinterpret_cast<const uint4*>(base + fo16[0]), *reinterpret_cast<const uint4*>(base + fo16[1]));
+  };
+
+  f32x4 acc16[FI][FJ];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) acc16[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  i32x8 fb[FJ], fa[4];
+  float sc[4] = {1.f, 1.f, 1.f, 1.f}, sbv = 1.f;  // fp32 block scales
+  int ea[4] = {0, 0, 0, 0}, eb = 0;                // E8M0 exponents
+
+  // memory phase of half H of stage s
+  auto mem = [&](int64_t s, auto hc) {
+    constexpr int H = decltype(hc)::value;
+    if (H == 0) {
+      if (s + 1 < nst) issue_a(s + 1);
+    } else {
+      if (s + 2 < nst) issue_b(s + 2);
+    }
+    const uint8_t* pa = lds + ((2 * s + 1) & 3) * SLOT;
+    if (H == 0) {
+      const uint8_t* pb = lds + ((2 * s) & 3) * SLOT + (wn * WTN) * BK;
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) fb[j] = frag16(pb + j * 16 * BK);
+      const uint32_t sbw = SC ? *reinterpret_cast<const uint32_t*>(pa + SB_OFF + wave * 16 + ((wn * WTN) >> 7) * 4) : 0u;
+      if constexpr (PROMOTE) sbv = __uint_as_float(sbw);
+      if constexpr (E8) eb = (int)(sbw >> 23);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = frag16(pa + (wm * WTM + (4 * H + i) * 16) * BK);
+    if constexpr (SC) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(pa + SA_OFF + (wm * WTM + (4 * H + i) * 16 + r16) * 4);
+        if constexpr (PROMOTE) sc[i] = __uint_as_float(w) * sbv;
+        if constexpr (E8) ea[i] = (int)(w >> 23);
+      }
+    }
+    if (H == 1 && grp == 1) {  // stage s+1 complete; B(s+2) may be younger
+      if (s + 2 < nst) wait_vmcnt_lgkm0<PPB>();
+      else wait_vmcnt_lgkm0<0>();
+    } else {
+      wait_vmcnt_lgkm0<63>();
+    }
+  };
+  // compute phase of half H of stage s
+  auto comp = [&](int64_t s, auto hc) {
+    constexpr int H = decltype(hc)::value;
+    if constexpr (PROMOTE) {
+      // three-deep pipeline: the promotion of MFMA q follows the issue of
+      // MFMA q+2, so it never waits for a result still in the matrix core
+      constexpr int NQ = 4 * FJ;
+      f32x4 tq[3];
+      tq[0] = mfma_fp8(fb[0], fa[0], f32x4{0.f, 0.f, 0.f, 0.f});
+      tq[1] = mfma_fp8(fb[1 % FJ], fa[1 / FJ], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int q = 2; q < NQ + 2; ++q) {
+        if (q < NQ) tq[q % 3] = mfma_fp8(fb[q % FJ], fa[q / FJ], f32x4{0.f, 0.f, 0.f, 0.f});
+        const int d = q - 2;
+        acc16[4 * H + d / FJ][d % FJ] += tq[d % 3] * sc[d / FJ];
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+#pragma unroll
+      for (int q = 2; q < NQ; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+          if constexpr (E8) acc16[4 * H + i][j] = mfma_fp8_e8(fb[j], fa[i], acc16[4 * H + i][j], eb, ea[i]);
+          else acc16[4 * H + i][j] = mfma_fp8(fb[j], fa[i], acc16[4 * H + i][j]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __asm__ volatile("" : "+v"(acc16[4 * H + i][0]), "+v"(acc16[4 * H + i][1]), "+v"(acc16[4 * H + i][2]),
+                       "+v"(acc16[4 * H + i][3]));
+    if (H == 1 && grp == 0) {  // stage s+1 complete; B(s+2) may be younger
+      if (s + 2 < nst) wait_vmcnt<PPB>();
+      else wait_vmcnt<0>();
+    }
+  };
+
+  if (nst > 0) {
+    issue_b(0);
+    issue_a(0);
+    if (nst > 1) {
+      issue_b(1);
+      wait_vmcnt<PPB>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    phase_barrier();
+    if (grp == 1) phase_barrier();
+    for (int64_t s = 0; s < nst; ++s) {
+      mem(s, IntC<0>());
+      phase_barrier();
+      comp(s, IntC<0>());
+      phase_barrier();
+      mem(s, IntC<1>());
+      phase_barrier();
+      comp(s, IntC<1>());
+      phase_barrier();
+    }
+    if (grp == 0) phase_barrier();
+  }
+  // the ring is idle from here on: its first word serves as the split flag
+  if (p.split_k > 1 && !splitk_reduce<FI, FJ, NT>(p, acc16, tile, split, tid, reinterpret_cast<int*>(lds)))
+    return;
+  store_tile16<BM, BN, WM, WN, KIND>(p, acc16, lds, m0, n0, wm, wn, lane, tid);
 }
 
 // s_waitcnt vmcnt(n) for a wave-uniform n in [LO, HI] (a branch tree over
@@ -2047,11 +2198,11 @@ hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int KIND, int NP, bool MF16 = false>
+template <int BM, int BN, int WM, int WN, int KIND, int NP>
 hipError_t launch_panel(const GemmArgs& p, hipStream_t stream) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  const size_t lds = (size_t)PanelGeom<BM, BN, WM, WN, KIND, NP, MF16>::LDS;
-  auto kern = gemm_panel_kernel<BM, BN, WM, WN, KIND, NP, MF16>;
+  const size_t lds = (size_t)PanelGeom<BM, BN, WM, WN, KIND, NP>::LDS;
+  auto kern = gemm_panel_kernel<BM, BN, WM, WN, KIND, NP>;
   static bool lds_attr_set = false;
   if (lds > 65536 && !lds_attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -2062,6 +2213,24 @@ hipError_t launch_panel(const GemmArgs& p, hipStream_t stream) {
   const unsigned experts = p.masked_m ? (unsigned)p.experts : 1u;
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles, (unsigned)p.split_k, experts), dim3(WM * WN * 64),
                      lds, stream, p);
+  return hipGetLastError();
+}
+
+
+template <int KIND>
+hipError_t launch_pingpong(const GemmArgs& p, hipStream_t stream) {
+  const int64_t tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+  const size_t lds = (size_t)PanelGeom<256, 256, 2, 4, KIND, 4, true>::LDS;
+  auto kern = gemm_pingpong_kernel<KIND>;
+  static bool lds_attr_set = false;
+  if (!lds_attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    lds_attr_set = true;
+  }
+  const unsigned experts = p.masked_m ? (unsigned)p.experts : 1u;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles, (unsigned)p.split_k, experts), dim3(512), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -2157,8 +2326,8 @@ bool panel_eligible(const GemmArgs& p) {
 }
 
 // The 256x256 tile where nothing else is asked for by name: channelwise the
-// 8-wave register-staged kernel; blockwise the 16x16-MFMA panel tile, or,
-// past the panel tiles' 32-bit DMA offsets, the 8-wave 128x128
+// 8-wave register-staged kernel; blockwise the ping-pong tile, or, past the
+// panel tiles' 32-bit DMA offsets, the 8-wave 128x128
 // register-staged kernel (the register-staged 256x256 blockwise kernels do
 // not fit their registers). Its split-K partials of 128x128 tiles fill the
 // workspace planned for 256x256 ones exactly or less.
@@ -2203,7 +2372,7 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
     // stages the split plan counts in
     case 14:
       if (KIND != kChannelwise || !panel_eligible<KIND>(p)) return launch_256<KIND>(p, stream);
-      return launch_panel<256, 256, 2, 4, kChannelwise, 5>(p, stream);
+      return launch_pingpong<kChannelwise>(p, stream);
     case 15:
       if (!panel_eligible<KIND>(p)) return launch_tile<256, 128, 4, 2, 128, KIND>(p, stream);
       return launch_panel<256, 128, 4, 2, KIND, 5>(p, stream);
@@ -2235,11 +2404,11 @@ hipError_t launch_kind(int variant, const GemmArgs& p, hipStream_t stream) {
     case 24:
       if (!panel_eligible<KIND>(p)) return launch_tile<64, 32, 2, 1, 128, KIND>(p, stream);
       return launch_panel<64, 32, 2, 1, KIND, 7>(p, stream);
-    // blockwise 256x256 on 16x16x128 MFMAs (four-slot ring); channelwise
-    // requests run the 256x256 panel tile
+    // the ping-pong 256x256 tile on 16x16x128 MFMAs, either kind (blockwise
+    // through launch_256, which keeps its fallbacks)
     case 25:
       if (KIND == kBlockwise || !panel_eligible<KIND>(p)) return launch_256<KIND>(p, stream);
-      return launch_panel<256, 256, 2, 4, kChannelwise, 5>(p, stream);
+      return launch_pingpong<kChannelwise>(p, stream);
     case 26: {  // FP8_VARIANT_DECODE
       if (p.M > 64) return hipErrorInvalidValue;
       if (decode_eligible<KIND>(p)) return launch_decode<KIND>(p, stream);
@@ -2269,7 +2438,7 @@ hipError_t launch_256(const GemmArgs& p, hipStream_t stream) {
   if constexpr (KIND == kChannelwise) {
     return launch_tile<256, 256, 2, 4, 128, KIND>(p, stream);
   } else {
-    if (panel_eligible<KIND>(p)) return launch_panel<256, 256, 2, 4, kBlockwise, 4, true>(p, stream);
+    if (panel_eligible<KIND>(p)) return launch_pingpong<kBlockwise>(p, stream);
     if (p.split_k > 1 && ((p.M + 127) / 128) * ((p.N + 127) / 128) > kMaxSplitTiles) return hipErrorInvalidValue;
     return launch_tile<128, 128, 2, 4, 128, KIND>(p, stream);
   }
@@ -2446,7 +2615,7 @@ hipError_t launch_e8(int variant, const GemmArgs& p, hipStream_t stream) {
   switch (variant) {
     case 15: return launch_panel<256, 128, 4, 2, kBlockwiseE8, 5>(p, stream);
     case 22: return launch_panel<128, 64, 4, 2, kBlockwiseE8, 5>(p, stream);
-    case 25: return launch_panel<256, 256, 2, 4, kBlockwiseE8, 4, true>(p, stream);
+    case 25: return launch_pingpong<kBlockwiseE8>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

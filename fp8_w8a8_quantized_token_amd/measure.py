@@ -863,7 +863,7 @@ def main(argv=None):
         return 0
     if args.traffic_summary:
         txt = traffic_summary(*args.traffic_summary, label="gemm_blockwise[t256x256bw16]",
-                              symbol="gemm_panel_kernel<256, 256, 2, 4, 1, 4, true>", n=4096, k=4096,
+                              symbol="gemm_pingpong_kernel<1>", n=4096, k=4096,
                               bm=256, bn=256, threads=512, command_tail="o_proj N=K=4096 step launches")
         root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
         with open(os.path.join(root, "profiles", "gemm_blockwise_t256x256bw16_o_proj_traffic.txt"), "w") as f:
