@@ -425,6 +425,51 @@ def measure_stream_ceiling(warmup, calls, filler):
     return lines
 
 
+def measure_library_reference(warmup, calls, filler):
+    """Context for the large-M tiles: the same channelwise GEMMs through the
+    vendor library (torch._scaled_mm, hipBLASLt on ROCm) beside this library's
+    default tile, on the same E4M3 operands with row-wise fp32 scales and with
+    unit tensor-wise scales, weights rotated over >= 1 GiB of copies. Not part
+    of the path; a measurement of the practical ceiling on this chip."""
+    dev = torch.device("cuda:0")
+    head = ("| N×K | M | this library µs (TFLOP/s) | library, row-wise scales µs (TFLOP/s) | "
+            "library, tensor-wise scales µs (TFLOP/s) |")
+    lines = [head, "|---|---|---|---|---|"]
+    print(head, flush=True)
+    print(lines[1], flush=True)
+    for n, k, m in ((4096, 4096, 4096), (4096, 4096, 8192), (6144, 4096, 8192), (4096, 12288, 8192),
+                    (24576, 4096, 8192), (3072, 4096, 4096)):
+        sets = max(2, min(MAX_SETS, math.ceil(ROTATE_BYTES / (n * k))))
+        w = synth.weights("measure/libref", n, k).to(torch.bfloat16).to(dev)
+        wq, ws = ops.quant_per_token(w)
+        del w
+        a, sa = ops.quant_per_token(synth.activations("measure/libref", m, k).to(dev))
+        ws_row = ws.reshape(1, n)
+        sa_col = sa.reshape(m, 1)
+        one = torch.ones((), dtype=torch.float32, device=dev)
+        wts = [wq.clone() for _ in range(sets)]
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        fl = 2.0 * m * n * k
+        ours = _batch_us([ops.prepare("scaled_mm_channelwise", a, wb, sa, ws, out=out) for wb in wts],
+                         warmup, calls, filler)
+        a8 = a.view(torch.float8_e4m3fn)
+        cells = []
+        for sc_a, sc_b in ((sa_col, ws_row), (one, one)):
+            try:
+                fns = [lambda wb=wb: torch._scaled_mm(a8, wb.view(torch.float8_e4m3fn).t(), scale_a=sc_a,
+                                                      scale_b=sc_b, out_dtype=torch.bfloat16) for wb in wts]
+                us = _batch_us(fns, warmup, calls, filler)
+                cells.append(f"{us:.1f} ({fl / us / 1e6:.0f})")
+            except Exception as ex:  # noqa: BLE001 - the library may lack a scaling mode
+                cells.append(f"unavailable ({type(ex).__name__})")
+        line = f"| {n}×{k} | {m} | {ours:.1f} ({fl / ours / 1e6:.0f}) | {cells[0]} | {cells[1]} |"
+        lines.append(line)
+        print(line, flush=True)
+        del wts, out
+        torch.cuda.empty_cache()
+    return lines
+
+
 def measure_probes(warmup, calls, filler):
     """Ceilings from the library's own probe kernels (batch-timed, HIP events
     around each batch): the read-only HBM stream at the small-M weight sizes
@@ -838,6 +883,9 @@ def main(argv=None):
                     help="time the decode down projection with SiLU-and-mul: one launch against two")
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="time plain device copies and reductions at the small-M linears' byte counts")
+    ap.add_argument("--library-reference", action="store_true",
+                    help="time the large-M channelwise GEMMs through torch._scaled_mm (hipBLASLt) "
+                         "beside this library's default tile (context, not part of the path)")
     ap.add_argument("--probes", action="store_true",
                     help="run the probe kernels: HBM read stream, L2 feed, FP8 MFMA rate and clock")
     ap.add_argument("--counter-run", nargs="?", const=COUNTER_CASES, default=None,
@@ -875,15 +923,16 @@ def main(argv=None):
     want = args.workloads.split(",")
     filler = _Filler(dev)
     if (args.quant_variants or args.ue8m0_gemm or args.moe or args.stream_ceiling or args.silu_linear
-            or args.probes):
+            or args.probes or args.library_reference):
         t0 = time.time()
         mode = (measure_quant_variants if args.quant_variants else
                 measure_ue8m0_gemm if args.ue8m0_gemm else
                 measure_moe if args.moe else
                 measure_probes if args.probes else
+                measure_library_reference if args.library_reference else
                 measure_silu_linear if args.silu_linear else measure_stream_ceiling)
         lines = mode(args.warmup, args.calls, filler)
-        if args.stream_ceiling or args.silu_linear or args.probes:
+        if args.stream_ceiling or args.silu_linear or args.probes or args.library_reference:
             note = (f"\n{args.calls} calls per row after {args.warmup} warm-up calls, timed as one "
                     f"batch with HIP events behind queued device copies (average per call); "
                     f"buffers rotated to cover >= 1 GiB. {time.time() - t0:.0f} s.")
