@@ -341,15 +341,15 @@ def test_dma_variant_falls_back_when_k_not_multiple_of_64():
 PANEL_CASES = [
     (1, 300, 392, 1024), (3, 300, 392, 1024), (2, 513, 200, 2048), (1, 1, 256, 128),
     (1, 257, 264, 256), (1, 300, 392, 384), (4, 129, 392, 4096), (3, 64, 520, 1280),
-    (1, 4096, 4096, 4096)]
+    (3, 300, 392, 384), (2, 1, 520, 256), (1, 4096, 4096, 4096)]
 
 
 @pytest.mark.parametrize("split_k,m,n,k", PANEL_CASES,
                          ids=[f"sk{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in PANEL_CASES])
 def test_channelwise_panel_variant(split_k, m, n, k):
-    """The panel-ring LDS-DMA tile (K a multiple of 128): one to many stages
-    (odd and even panel counts against the five-slot ring), ragged M and N,
-    split-K with uneven splits, and a full o_proj tile grid."""
+    """The 256x256 ping-pong tile, channelwise (K a multiple of 128): one to
+    many stages against its four-slot ring, ragged M and N, split-K with
+    uneven splits and with one stage per split, and a full o_proj tile grid."""
     _channelwise_case("panel", m, n, k, 0.0, True, config=ops.make_config("t256x256panel", split_k))
 
 
@@ -362,7 +362,7 @@ def test_panel_variant_falls_back_when_k_not_multiple_of_128():
 BW_PANEL_CASES = [
     (1, 300, 384, 1024, False), (3, 300, 384, 1024, True), (1, 1, 128, 128, False),
     (1, 257, 256, 384, False), (2, 513, 640, 2048, True), (4, 129, 384, 4096, False),
-    (1, 4096, 4096, 4096, False)]
+    (3, 257, 384, 384, True), (2, 2, 256, 256, False), (1, 4096, 4096, 4096, False)]
 
 
 @pytest.mark.parametrize("split_k,m,n,k,bias", BW_PANEL_CASES,
@@ -378,15 +378,16 @@ def test_blockwise_panel_variant(split_k, m, n, k, bias):
                          ids=[f"sk{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}{'-bias' if c[4] else ''}"
                               for c in BW_PANEL_CASES])
 def test_blockwise_256x256_mfma16(split_k, m, n, k, bias):
-    """The blockwise 256x256 tile on 16x16x128 MFMAs (four-slot ring, one
-    promotion per MFMA): the same stage counts, ragged shapes and splits."""
+    """The blockwise 256x256 ping-pong tile on 16x16x128 MFMAs (four-slot
+    ring, one promotion per MFMA): the same stage counts, ragged shapes and
+    splits, down to one stage per split."""
     _blockwise_case("bw16", m, n, k, config=ops.make_config("t256x256bw16", split_k), with_bias=bias)
 
 
 def test_blockwise_256x256_mfma16_poison_and_fallbacks():
     """NaN pad rows stay out; an unaligned scale column (stride not a multiple
     of 4) runs the same tile with its scales copied one per lane; a
-    channelwise request runs the 256x256 panel tile."""
+    channelwise request runs the channelwise form of the tile."""
     _blockwise_case("bw16-poison", 301, 512, 1024, config=ops.make_config("t256x256bw16", 2), poison=True)
     _blockwise_case("bw16-ld", 301, 384, 1024, config=ops.make_config("t256x256bw16", 2), row_align=1)
     _channelwise_case("bw16-cw", 300, 392, 1024, 0.0, True, config=ops.make_config("t256x256bw16", 2),
@@ -417,8 +418,8 @@ def test_blockwise_panel_unaligned_scale_column(variant, split_k, m, row_align):
 
 
 def test_blockwise_default_unaligned_scale_column_large_m():
-    """M = 4097 with row alignment 1 at the default tile (the 16x16-MFMA
-    256x256 tile): a column stride of 4097 scales."""
+    """M = 4097 with row alignment 1 at the default tile (the 256x256
+    ping-pong tile): a column stride of 4097 scales."""
     _blockwise_case("bw-ld-4097", 4097, 4096, 4096, row_align=1)
 
 

@@ -72,7 +72,7 @@ BW16_CASES = [
                          ids=[f"sk{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}{'-bias' if c[4] else ''}"
                               for c in BW16_CASES])
 def test_ue8m0_block_scaled_mfma_tile(split_k, m, n, k, bias):
-    """The 256x256 16x16-MFMA tile with the scales inside the MFMA: one to many
+    """The 256x256 ping-pong tile with the scales inside the MFMA: one to many
     stages, ragged M, N overhanging the tile, uneven split-K, bias, and the
     MoE-expert and o_proj prefill shapes."""
     _case("ue8m0-bw16", m, n, k, config=ops.make_config("t256x256bw16", split_k), with_bias=bias)
@@ -80,7 +80,8 @@ def test_ue8m0_block_scaled_mfma_tile(split_k, m, n, k, bias):
 
 def test_ue8m0_poisoned_pad_rows_and_fallback():
     """NaN pad scales and 0x7F pad codes stay out of the outputs; an unaligned
-    scale column takes the register-staged tile of the same shape."""
+    scale column (row alignment 1) runs the same tile with its scales copied
+    one per lane."""
     _case("ue8m0-poison", 301, 512, 1024, config=ops.make_config("t256x256bw16", 2), poison=True)
     _case("ue8m0-ld", 301, 384, 1024, config=ops.make_config("t256x256bw16", 1), row_align=1)
 
