@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 METRIC = "FP8 scaled-GEMM TFLOP/s and GB/s vs roofline, Qwen3-8B shapes, M=1..8192"
 PEAK_TFLOPS_FP8 = 5000.0  # MI355X dense FP8 MFMA
 PEAK_GBPS = 8000.0        # MI355X HBM3E
+ID_PASSES = 3  # identification steps before the timed region
 RIDGE = PEAK_TFLOPS_FP8 * 1e12 / (PEAK_GBPS * 1e9)
 MS = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192]
 N = K = 4096
@@ -326,22 +327,24 @@ def main():
             l.fn()
     torch.cuda.synchronize()
 
-    # Identification pass (untimed): events around every launch give each
-    # kernel's share of the step and the per-(kind, M) table.
-    probe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in launches]
-    for (e0, e1), l in zip(probe, launches):
-        e0.record()
-        l.fn()
-        e1.record()
+    # Identification passes (untimed): events around every launch give each
+    # kernel's share of the step (summed over ID_PASSES steps, so one slow
+    # launch cannot decide it) and the per-(kind, M) table (median).
+    probe = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in launches] for _ in range(ID_PASSES)]
+    for row in probe:
+        for (e0, e1), l in zip(row, launches):
+            e0.record()
+            l.fn()
+            e1.record()
     torch.cuda.synchronize()
     share = {}
     per_m = {}
-    for (e0, e1), l in zip(probe, launches):
-        us = e0.elapsed_time(e1) * 1e3
-        share[l.label] = share.get(l.label, 0.0) + us
+    for i, l in enumerate(launches):
+        us_all = sorted(row[i][0].elapsed_time(row[i][1]) * 1e3 for row in probe)
+        share[l.label] = share.get(l.label, 0.0) + sum(us_all)
         key = f"{l.kind}/{l.part}/M={l.m}"
-        per_m[key] = {"us_event": us, "flops": l.flops, "bytes": l.nbytes}
+        per_m[key] = {"us_event": us_all[len(us_all) // 2], "flops": l.flops, "bytes": l.nbytes}
     dom_label = max(share, key=share.get)
     dom_idx = [i for i, l in enumerate(launches) if l.label == dom_label]
 

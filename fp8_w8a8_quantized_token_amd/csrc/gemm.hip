@@ -73,20 +73,42 @@ __device__ __forceinline__ void store_out4(const GemmArgs& p, int64_t m, int64_t
       o[0] += bf16_to_f32(bb.x & 0xffffu); o[1] += bf16_to_f32(bb.x >> 16);
       o[2] += bf16_to_f32(bb.y & 0xffffu); o[3] += bf16_to_f32(bb.y >> 16);
     }
-    const uint2 packed = make_uint2(f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16),
-                                    f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16));
+    const uint2 packed = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     *reinterpret_cast<uint2*>(p.out + m * p.ldc + n) = packed;
   } else {
     for (int r = 0; r < 4 && n + r < p.N; ++r) {
       float x = v[r];
       if (KIND == kChannelwise) x = x * sa_m * p.sb[n + r];
       if (p.bias) x += bf16_to_f32(p.bias[n + r]);
-      p.out[m * p.ldc + n + r] = (uint16_t)f32_to_bf16(x);
+      p.out[m * p.ldc + n + r] = (uint16_t)pack_bf16x2(x, 0.0f);
     }
   }
 }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// pack_out4 (below) with the weight scales of columns n..n+3 passed in
+// (channelwise; columns >= N give unspecified values).
+template <int KIND>
+__device__ __forceinline__ uint2 pack_out4s(const GemmArgs& p, int64_t n, f32x4 v, float sa_m, float4 sb) {
+  float o[4] = {v[0], v[1], v[2], v[3]};
+  if (KIND == kChannelwise) {
+    o[0] = o[0] * sa_m * sb.x; o[1] = o[1] * sa_m * sb.y;
+    o[2] = o[2] * sa_m * sb.z; o[3] = o[3] * sa_m * sb.w;
+  }
+  if (p.bias) {
+    if (n + 3 < p.N) {
+      const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n);
+      o[0] += bf16_to_f32(bb.x & 0xffffu); o[1] += bf16_to_f32(bb.x >> 16);
+      o[2] += bf16_to_f32(bb.y & 0xffffu); o[3] += bf16_to_f32(bb.y >> 16);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < p.N) o[r] += bf16_to_f32(p.bias[n + r]);
+    }
+  }
+  return make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+}
 
 // Scale (channelwise), add the bias and round to bf16 the 4 outputs a lane
 // owns at columns n..n+3 of row m; columns >= N give unspecified values.
@@ -113,8 +135,7 @@ __device__ __forceinline__ uint2 pack_out4(const GemmArgs& p, int64_t n, f32x4 v
       }
     }
   }
-  return make_uint2(f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16),
-                    f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16));
+  return make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
 }
 
 // Epilogue of the 32x32-MFMA tile kernels, staged through LDS so that the
@@ -162,26 +183,33 @@ __device__ __forceinline__ void copy_out_tile(const GemmArgs& p, const uint8_t* 
 }
 
 // The same epilogue for 16x16-MFMA accumulators (lane: m = 16 i + l % 16,
-// n = 16 j + 4 (l / 16) .. +3), blockwise (already scaled).
+// n = 16 j + 4 (l / 16) .. +3). Blockwise results are already scaled;
+// channelwise ones take the tile's BM activation and BN weight scales from
+// the fp32 table at byte sc_off of the LDS (staged by the caller while the
+// K loop ran: scale loads issued here would wait a full memory round trip
+// under the output stores of every other workgroup).
 template <int BM, int BN, int WM, int WN, int KIND>
 __device__ __forceinline__ void store_tile16(const GemmArgs& p,
                                              const f32x4 (&acc)[BM / WM / 16][BN / WN / 16],
                                              uint8_t* lds, int64_t m0, int64_t n0, int wm, int wn,
-                                             int lane, int tid) {
+                                             int lane, int tid, int sc_off) {
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int CH = BN / 8;
   __syncthreads();
+  const float* lsa = reinterpret_cast<const float*>(lds + sc_off);
+  const float* lsb = lsa + BM;
 #pragma unroll
   for (int i = 0; i < WTM / 16; ++i) {
     const int ml = wm * WTM + i * 16 + (lane & 15);
-    const int64_t m = m0 + ml;
-    const float sa_m = (KIND == kChannelwise && m < p.M) ? p.sa[m] : 1.0f;
+    const float sa_m = KIND == kChannelwise ? lsa[ml] : 1.0f;
     uint8_t* row = lds + ml * (BN * 2);
 #pragma unroll
     for (int j = 0; j < WTN / 16; ++j) {
       const int nl = wn * WTN + j * 16 + 4 * (lane >> 4);
-      const uint2 v = pack_out4<KIND>(p, n0 + nl, acc[i][j], sa_m);
+      const uint2 v = pack_out4s<KIND>(p, n0 + nl, acc[i][j], sa_m,
+                                       KIND == kChannelwise ? *reinterpret_cast<const float4*>(lsb + nl)
+                                                            : float4{1.f, 1.f, 1.f, 1.f});
       *reinterpret_cast<uint2*>(row + (((nl >> 3) ^ out_sw<CH>(ml)) << 4) + (((nl >> 2) & 1) << 3)) = v;
     }
   }
@@ -189,32 +217,37 @@ __device__ __forceinline__ void store_tile16(const GemmArgs& p,
   copy_out_tile<BM, BN, NT>(p, lds, m0, n0, tid);
 }
 
+// sc_off >= 0 (channelwise): the tile's scales come from the fp32 table at
+// that LDS byte offset (BM activation scales, then BN weight scales), as in
+// store_tile16; otherwise from global memory.
 template <int BM, int BN, int WM, int WN, int KIND>
 __device__ __forceinline__ void store_tile(const GemmArgs& p,
                                            const f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
                                            uint8_t* lds, int64_t m0, int64_t n0, int wm, int wn,
-                                           int h, int r32, int tid) {
+                                           int h, int r32, int tid, int sc_off = -1) {
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int CH = BN / 8;  // 16-byte chunks per tile row
   auto sw = [](int r) { return out_sw<CH>(r); };
   __syncthreads();
+  const bool ls = KIND == kChannelwise && sc_off >= 0;
+  const float* lsa = reinterpret_cast<const float*>(lds + (sc_off > 0 ? sc_off : 0));
+  const float* lsb = lsa + BM;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int ml = wm * WTM + i * 32 + r32;
     const int64_t m = m0 + ml;
-    const float sa_m = (KIND == kChannelwise && m < p.M) ? p.sa[m] : 1.0f;
+    const float sa_m = ls ? lsa[ml] : (KIND == kChannelwise && m < p.M) ? p.sa[m] : 1.0f;
     uint8_t* row = lds + ml * (BN * 2);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int nl = wn * WTN + j * 32 + 8 * q + 4 * h;
-        const uint2 v = pack_out4<KIND>(
-            p, n0 + nl,
-            f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]},
-            sa_m);
+        const f32x4 v4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        const uint2 v = ls ? pack_out4s<KIND>(p, n0 + nl, v4, sa_m, *reinterpret_cast<const float4*>(lsb + nl))
+                           : pack_out4<KIND>(p, n0 + nl, v4, sa_m);
         *reinterpret_cast<uint2*>(row + (((nl >> 3) ^ sw(ml)) << 4) + (h << 3)) = v;
       }
   }
@@ -819,6 +852,17 @@ struct PanelGeom {
   static constexpr int SC_OFF = SC_IN_A ? BM * 128 : BN * 128;  // scales inside their slot
 };
 
+// Channelwise panel tiles whose ring leaves room keep the tile's scales in a
+// table past it for the epilogue (store_tile, sc_off); LDS bytes of a tile.
+template <int BM, int BN, int WM, int WN, int KIND, int NP>
+constexpr bool panel_epi_scales() {
+  return KIND == kChannelwise && PanelGeom<BM, BN, WM, WN, KIND, NP>::LDS + (BM + BN) * 4 <= 163840;
+}
+template <int BM, int BN, int WM, int WN, int KIND, int NP>
+constexpr int panel_lds_bytes() {
+  return PanelGeom<BM, BN, WM, WN, KIND, NP>::LDS + (panel_epi_scales<BM, BN, WM, WN, KIND, NP>() ? (BM + BN) * 4 : 0);
+}
+
 // Wait until at most the c newest DMA panels of this wave are outstanding,
 // c <= C, those panels alternating P0 instructions, P1, P0, ... from the
 // oldest of them.
@@ -1076,6 +1120,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
     if (q & 1) issue_a(kt_begin + (q >> 1), slot);
     else issue_b(kt_begin + (q >> 1), slot);
   };
+  // the epilogue's scale table (entries e < BM: activation scale of row
+  // m0 + e, then weight scale of column n0 + e - BM; indices past the matrix
+  // read its last one), before any panel so that every wait covers it; every
+  // instruction has lane 0 active
+  constexpr bool EPI_SC = panel_epi_scales<BM, BN, WM, WN, KIND, NP>();
+  if constexpr (EPI_SC) {
+    for (int c = wave * 64; c < BM + BN; c += NW * 64) {
+      const int e = c + lane;
+      if (e < BM + BN) {
+        if (e < BM) {
+          int64_t r = m0 + e;
+          r = r < p.M - 1 ? r : p.M - 1;
+          lds_dma4_s(reinterpret_cast<const uint8_t*>(p.sa), (uint32_t)(r * 4), lds_base + G::LDS + c * 4);
+        } else {
+          int64_t n = n0 + (e - BM);
+          n = n < p.N - 1 ? n : p.N - 1;
+          lds_dma4_s(reinterpret_cast<const uint8_t*>(p.sb), (uint32_t)(n * 4), lds_base + G::LDS + c * 4);
+        }
+      }
+    }
+    if (nst <= 0) wait_vmcnt<0>();
+  }
   if (nst > 0) {
     // prologue: panels 0 .. min(NP, 2 nst) - 1 into slots 0 .. NP-1, then
     // stage 0 (panels 0 and 1) complete; the outstanding ones start with a
@@ -1125,7 +1191,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
   // the ring is idle from here on: its first word serves as the split flag
   if (p.split_k > 1 && !splitk_reduce<TM, TN, NT>(p, acc, tile, split, tid, reinterpret_cast<int*>(lds)))
     return;
-  store_tile<BM, BN, WM, WN, KIND>(p, acc, lds, m0, n0, wm, wn, h, r32, tid);
+  store_tile<BM, BN, WM, WN, KIND>(p, acc, lds, m0, n0, wm, wn, h, r32, tid, EPI_SC ? G::LDS : -1);
 }
 
 
@@ -1157,6 +1223,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
 // after its memory phase (s,1)), when only their B(s+2) share is younger.
 // Grouped calls (masked_m, one expert per blockIdx.z) as in the panel tiles.
 // ---------------------------------------------------------------------------
+// LDS of the ping-pong tile: the ring, then (channelwise) the epilogue's
+// scale table, 256 activation and 256 weight scales.
+template <int KIND>
+constexpr int pingpong_lds_bytes() {
+  return PanelGeom<256, 256, 2, 4, KIND, 4, true>::LDS + (KIND == kChannelwise ? 2 * 256 * 4 : 0);
+}
+
 __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   __asm__ volatile("" ::: "memory");
@@ -1180,7 +1253,7 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(GemmArgs p) {
   constexpr int SA_OFF = G::SC_OFF;
   constexpr int SB_OFF = SA_OFF + G::SA_BYTES;
   constexpr int SA_LANES = BM / 4 / NW;
-  static_assert(G::LDS <= 163840 && BM * BN * 2 <= G::LDS, "ring and output tile fit the LDS");
+  static_assert(pingpong_lds_bytes<KIND>() <= 163840 && BM * BN * 2 <= G::LDS, "ring and output tile fit the LDS");
   static_assert(2 * PPA + 2 < 64, "vmcnt range");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -1366,6 +1439,22 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(GemmArgs p) {
     }
   };
 
+  // channelwise: the tile's scales into the table past the ring for the
+  // epilogue, before any panel, so every wait below covers them; waves 0-3
+  // copy activation scales of rows m0 + 64w .., waves 4-7 weight scales of
+  // columns n0 + 64(w - 4) .. (indices past the matrix read its last one)
+  if constexpr (KIND == kChannelwise) {
+    const uint32_t dst = lds_base + (uint32_t)G::LDS + (uint32_t)wave * 256;
+    if (grp == 0) {
+      int64_t r = m0 + wave * 64 + lane;
+      r = r < p.M - 1 ? r : p.M - 1;
+      lds_dma4_s(reinterpret_cast<const uint8_t*>(p.sa), (uint32_t)(r * 4), dst);
+    } else {
+      int64_t c = n0 + (wave - 4) * 64 + lane;
+      c = c < p.N - 1 ? c : p.N - 1;
+      lds_dma4_s(reinterpret_cast<const uint8_t*>(p.sb), (uint32_t)(c * 4), dst);
+    }
+  }
   if (nst > 0) {
     issue_b(0);
     issue_a(0);
@@ -1388,11 +1477,13 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(GemmArgs p) {
       phase_barrier();
     }
     if (grp == 0) phase_barrier();
+  } else {
+    wait_vmcnt<0>();
   }
   // the ring is idle from here on: its first word serves as the split flag
   if (p.split_k > 1 && !splitk_reduce<FI, FJ, NT>(p, acc16, tile, split, tid, reinterpret_cast<int*>(lds)))
     return;
-  store_tile16<BM, BN, WM, WN, KIND>(p, acc16, lds, m0, n0, wm, wn, lane, tid);
+  store_tile16<BM, BN, WM, WN, KIND>(p, acc16, lds, m0, n0, wm, wn, lane, tid, G::LDS);
 }
 
 // s_waitcnt vmcnt(n) for a wave-uniform n in [LO, HI] (a branch tree over
@@ -2201,7 +2292,7 @@ hipError_t launch_tile(const GemmArgs& p, hipStream_t stream) {
 template <int BM, int BN, int WM, int WN, int KIND, int NP>
 hipError_t launch_panel(const GemmArgs& p, hipStream_t stream) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  const size_t lds = (size_t)PanelGeom<BM, BN, WM, WN, KIND, NP>::LDS;
+  const size_t lds = (size_t)panel_lds_bytes<BM, BN, WM, WN, KIND, NP>();
   auto kern = gemm_panel_kernel<BM, BN, WM, WN, KIND, NP>;
   static bool lds_attr_set = false;
   if (lds > 65536 && !lds_attr_set) {
@@ -2220,7 +2311,7 @@ hipError_t launch_panel(const GemmArgs& p, hipStream_t stream) {
 template <int KIND>
 hipError_t launch_pingpong(const GemmArgs& p, hipStream_t stream) {
   const int64_t tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  const size_t lds = (size_t)PanelGeom<256, 256, 2, 4, KIND, 4, true>::LDS;
+  const size_t lds = (size_t)pingpong_lds_bytes<KIND>();
   auto kern = gemm_pingpong_kernel<KIND>;
   static bool lds_attr_set = false;
   if (!lds_attr_set) {
