@@ -158,11 +158,34 @@ __device__ __forceinline__ int out_sw(int r) {
 
 // Second phase of the staged epilogue: consecutive threads copy consecutive
 // 16-byte chunks of the [BM][BN] bf16 tile in LDS to rows < M, columns < N.
+// A tile wholly inside the output takes a branch-free form: a thread's
+// chunks lie NT / CH rows apart, and each batch of them is read from LDS
+// before any is stored, so the LDS round trips overlap.
 template <int BM, int BN, int NT>
 __device__ __forceinline__ void copy_out_tile(const GemmArgs& p, const uint8_t* lds, int64_t m0,
                                               int64_t n0, int tid) {
   constexpr int CH = BN / 8;
-  static_assert((BM * CH) % NT == 0, "copy-out split");
+  static_assert((BM * CH) % NT == 0 && NT % CH == 0, "copy-out split");
+  if (m0 + BM <= p.M && n0 + BN <= p.N) {
+    constexpr int IT = BM * CH / NT;  // chunks per thread
+    constexpr int RSTEP = NT / CH;    // rows between them
+    constexpr int BATCH = IT < 8 ? IT : 8;
+    const int rl0 = tid / CH, c = tid % CH;
+    uint16_t* dst = p.out + (m0 + rl0) * p.ldc + n0 + c * 8;
+    const int64_t step = (int64_t)RSTEP * p.ldc;
+#pragma unroll
+    for (int i0 = 0; i0 < IT; i0 += BATCH) {
+      uint4 v[BATCH];
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        const int rl = rl0 + (i0 + b) * RSTEP;
+        v[b] = *reinterpret_cast<const uint4*>(lds + rl * (BN * 2) + ((c ^ out_sw<CH>(rl)) << 4));
+      }
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) *reinterpret_cast<uint4*>(dst + (i0 + b) * step) = v[b];
+    }
+    return;
+  }
 #pragma unroll 4
   for (int idx = tid; idx < BM * CH; idx += NT) {
     const int rl = idx / CH, c = idx % CH;
