@@ -105,6 +105,7 @@ SIGNATURES = {
     "fp8_probe_stream_read": (c_i32, [c_vp, c_size, c_vp, c_i32, c_vp]),
     "fp8_probe_strided_read": (c_i32, [c_vp, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp]),
     "fp8_probe_l2_feed": (c_i32, [c_vp, c_size, c_i32, c_i32, c_vp, c_i32, c_vp]),
+    "fp8_probe_panel_feed": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp]),
     "fp8_probe_mfma": (c_i32, [c_i32, c_vp, c_i32, c_vp]),
     "fp8_probe_wave_read": (c_i32, [c_vp, c_size, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp]),
     "fp8_probe_lds": (c_i32, [c_i32, c_i32, c_vp, c_i32, c_vp]),

@@ -617,6 +617,17 @@ int fp8_probe_l2_feed(const void* src, size_t window_bytes, int32_t reps, int32_
   return hip_status(launch_probe_l2_feed(src, window_bytes, reps, dma != 0, sink, workgroups, stream), fn);
 }
 
+int fp8_probe_panel_feed(const void* src, int32_t row_bytes, int32_t panels, int32_t stages, int32_t mode,
+                         uint32_t* sink, int32_t workgroups, hipStream_t stream) {
+  const char* fn = "fp8_probe_panel_feed";
+  if (!src || !sink || row_bytes < 128 || row_bytes % 128 != 0 || panels < 1 || stages < 1 || mode < 0 ||
+      mode > 3 || workgroups < 1 || (uint64_t)panels * 64 * (uint64_t)row_bytes > 0xFFFFFFFFull)
+    return fail(FP8_ERR_INVALID, "%s: row_bytes a positive multiple of 128, panels, stages and workgroups >= 1, "
+                "mode 0-3, panels * 64 * row_bytes < 4 GiB", fn);
+  return hip_status(launch_probe_panel_feed(src, (uint32_t)row_bytes, panels, stages, mode, sink, workgroups, stream),
+                    fn);
+}
+
 int fp8_probe_mfma(int32_t iters, float* sink, int32_t workgroups, hipStream_t stream) {
   const char* fn = "fp8_probe_mfma";
   if (!sink || iters < 1 || workgroups < 1)

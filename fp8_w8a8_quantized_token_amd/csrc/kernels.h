@@ -141,6 +141,8 @@ hipError_t launch_probe_strided_read(const void* src, int64_t rows, int64_t row_
                                      int piece, uint32_t* sink, hipStream_t stream);
 hipError_t launch_probe_l2_feed(const void* src, size_t window, int reps, int dma, uint32_t* sink,
                                 int workgroups, hipStream_t stream);
+hipError_t launch_probe_panel_feed(const void* src, uint32_t row_bytes, int panels, int stages, int mode,
+                                   uint32_t* sink, int workgroups, hipStream_t stream);
 hipError_t launch_probe_mfma(int iters, float* sink, int workgroups, hipStream_t stream);
 hipError_t launch_probe_wave_read(const void* src, size_t bytes, int threads, int depth, int dma, uint32_t* sink,
                                   int workgroups, hipStream_t stream);

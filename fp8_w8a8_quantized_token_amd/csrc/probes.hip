@@ -8,6 +8,9 @@
 //    with register loads or with LDS-DMA loads (global_load_lds_dwordx4, the
 //    form the panel-ring GEMM tiles use): the per-compute-unit feed rate from
 //    L2.
+//  * panel_feed_kernel: the panel tiles' LDS-DMA feed (64-row panels, 128
+//    bytes per row and stage) alone, with LDS reads of the landed stages,
+//    with a barrier per stage, or both.
 //  * mfma_probe_kernel: back-to-back independent 32x32x64 FP8 MFMAs: the
 //    dense FP8 matrix rate and, from it, the clock the matrix cores ran at.
 //
@@ -117,6 +120,51 @@ __global__ __launch_bounds__(kProbeThreads) void l2_feed_kernel(const uint8_t* s
     __builtin_amdgcn_s_waitcnt(0);
     acc = *reinterpret_cast<const uint32_t*>(&ring[wave][lane & 15][0]) + (uint32_t)issued;
   }
+  if (acc == key) sink[blockIdx.x * kProbeThreads + threadIdx.x] = acc;
+}
+
+// The panel tiles' feed pattern without their arithmetic: a workgroup of
+// four waves streams 64-row panels (8 rows x 128 bytes per LDS-DMA
+// instruction, two per wave) of its own L2-resident row block, stage s
+// taking the rows' bytes [128 (s mod row_bytes / 128), +128), into an
+// 8-slot ring with at most six stages in flight per wave. MODE bit 0: after
+// each stage's wait every wave also reads 32 rows (4 KB) of the stage that
+// landed six stages back from LDS (the tiles' two readers per panel row);
+// bit 1: a workgroup barrier after each stage's wait.
+template <int MODE>
+__global__ __launch_bounds__(kProbeThreads) void panel_feed_kernel(const uint8_t* src, uint32_t row_bytes,
+                                                                   int panels, int stages, uint32_t* sink,
+                                                                   uint32_t key) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[8][8192];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t base = (uint32_t)(blockIdx.x % panels) * 64u;
+  const uint32_t cols = row_bytes / 128;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&ring[0][0];
+  uint32_t acc = 0;
+  for (int s = 0; s < stages; ++s) {
+    const uint32_t col = (uint32_t)s % cols;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t row = base + (uint32_t)(wave * 2 + i) * 8 + (lane >> 3);
+      const uint32_t off = row * row_bytes + col * 128 + (lane & 7) * 16;
+      const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(s & 7) * 8192 + (wave * 2 + i) * 1024);
+      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(src), "s"(m0v)
+                   : "memory", "m0");
+    }
+    __builtin_amdgcn_s_waitcnt(12 | (7 << 4) | (15 << 8));  // vmcnt <= 12: six stages in flight
+    if (MODE & 2) __syncthreads();
+    if (MODE & 1) {
+      const uint8_t* slot = &ring[(s + 2) & 7][(wave & 1) * 4096];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint4 v = *reinterpret_cast<const uint4*>(slot + r * 1024 + lane * 16);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  acc ^= *reinterpret_cast<const uint32_t*>(&ring[lane & 7][wave * 16]);
   if (acc == key) sink[blockIdx.x * kProbeThreads + threadIdx.x] = acc;
 }
 
@@ -326,6 +374,19 @@ hipError_t launch_probe_l2_feed(const void* src, size_t window, int reps, int dm
   else
     hipLaunchKernelGGL(l2_feed_kernel<0>, dim3((unsigned)workgroups), dim3(kProbeThreads), 0, stream,
                        static_cast<const uint8_t*>(src), (int64_t)window, reps, sink, 0x9E3779B9u);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_panel_feed(const void* src, uint32_t row_bytes, int panels, int stages, int mode,
+                                   uint32_t* sink, int workgroups, hipStream_t stream) {
+  const uint8_t* b = static_cast<const uint8_t*>(src);
+  const dim3 grid((unsigned)workgroups), block(kProbeThreads);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(panel_feed_kernel<0>, grid, block, 0, stream, b, row_bytes, panels, stages, sink, 0x9E3779B9u); break;
+    case 1: hipLaunchKernelGGL(panel_feed_kernel<1>, grid, block, 0, stream, b, row_bytes, panels, stages, sink, 0x9E3779B9u); break;
+    case 2: hipLaunchKernelGGL(panel_feed_kernel<2>, grid, block, 0, stream, b, row_bytes, panels, stages, sink, 0x9E3779B9u); break;
+    default: hipLaunchKernelGGL(panel_feed_kernel<3>, grid, block, 0, stream, b, row_bytes, panels, stages, sink, 0x9E3779B9u); break;
+  }
   return hipGetLastError();
 }
 

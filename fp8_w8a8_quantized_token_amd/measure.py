@@ -552,6 +552,19 @@ def measure_probes(warmup, calls, filler):
             emit("L2 feed, " + ("LDS-DMA" if dma else "register") + " loads", "512 KB window",
                  f"{wgs}x256", f"{us:.1f}", f"{moved / us / 1e3:.0f} GB/s total, "
                  f"{moved / us / 1e3 / 256:.1f} GB/s per CU", f"{reps} passes per workgroup")
+    # the panel tiles' feed pattern: 64-row panels of 4 KB rows, alone, with
+    # LDS reads of the landed stages, with a barrier per stage, with both
+    row_bytes, panels, stages = 4096, 32, 2048
+    pbuf = torch.full((panels * 64 * row_bytes // 4,), 5, dtype=torch.int32, device=dev)
+    for mode, what in ((0, "LDS-DMA alone"), (1, "+ LDS reads"), (2, "+ barrier per stage"),
+                       (3, "+ LDS reads + barrier")):
+        fn = lambda md=mode: _lib.check(lib.fp8_probe_panel_feed(  # noqa: E731
+            ctypes.c_void_p(pbuf.data_ptr()), row_bytes, panels, stages, md, sp, 256, stream()))
+        us = _batch_us([fn], 2, 5, filler)
+        moved = 256 * stages * 8192
+        emit("L2 feed, 64-row panels", "8 MB, 4 KB rows", "256x256", f"{us:.1f}",
+             f"{moved / us / 1e3 / 256:.1f} GB/s per CU", what)
+    del pbuf
     # LDS read rate per compute unit
     for threads, wgs in ((256, 256), (512, 256), (256, 512), (256, 1024)):
         iters = 4000

@@ -549,6 +549,18 @@ int fp8_probe_strided_read(const void* src, int64_t rows, int64_t row_bytes, int
 int fp8_probe_l2_feed(const void* src, size_t window_bytes, int32_t reps, int32_t dma, uint32_t* sink,
                       int32_t workgroups, hipStream_t stream);
 
+/* The panel tiles' feed pattern without their arithmetic: each of
+ * `workgroups` workgroups (four waves) streams the 64-row block
+ * (workgroup % panels) of `src` ([panels * 64][row_bytes] bytes, L2-sized)
+ * in 128-byte-per-row stages by LDS-DMA, six stages in flight per wave,
+ * `stages` times. mode bit 0 adds LDS reads of landed stages (4 KB per wave
+ * and stage), bit 1 a workgroup barrier per stage. Bytes moved =
+ * workgroups * stages * 8192. Invalid arguments (row_bytes not a positive
+ * multiple of 128, mode outside 0-3, the matrix past 4 GiB) return
+ * FP8_ERR_INVALID without a launch. */
+int fp8_probe_panel_feed(const void* src, int32_t row_bytes, int32_t panels, int32_t stages, int32_t mode,
+                         uint32_t* sink, int32_t workgroups, hipStream_t stream);
+
 /* Back-to-back independent V_MFMA_F32_32X32X64_F8F6F4 (four accumulators per
  * wave, four waves per workgroup): FLOPs = workgroups * 4 * iters * 4 * 131072.
  * The dense FP8 matrix rate; rate / (256 CUs * 8192 FLOP per clock per CU)

@@ -332,6 +332,9 @@ def test_probe_argument_errors(lib):
     assert lib.fp8_probe_strided_read(FAKE, 4096, 4096, 16, 48, FAKE, None) == _lib.FP8_ERR_INVALID
     assert lib.fp8_probe_strided_read(FAKE, 4096, 4096, 3, 128, FAKE, None) == _lib.FP8_ERR_INVALID
     assert lib.fp8_probe_l2_feed(FAKE, 1000, 4, 0, FAKE, 4, None) == _lib.FP8_ERR_INVALID
+    assert lib.fp8_probe_panel_feed(FAKE, 100, 4, 8, 0, FAKE, 4, None) == _lib.FP8_ERR_INVALID
+    assert lib.fp8_probe_panel_feed(FAKE, 4096, 4, 8, 4, FAKE, 4, None) == _lib.FP8_ERR_INVALID
+    assert lib.fp8_probe_panel_feed(FAKE, 1 << 24, 8, 8, 0, FAKE, 4, None) == _lib.FP8_ERR_INVALID
     assert lib.fp8_probe_mfma(0, FAKE, 4, None) == _lib.FP8_ERR_INVALID
     assert lib.fp8_probe_lds(4, 128, FAKE, 4, None) == _lib.FP8_ERR_INVALID
     assert lib.fp8_probe_wave_read(FAKE, 1 << 20, 1024, 16, 0, FAKE, 4, None) == _lib.FP8_ERR_INVALID
