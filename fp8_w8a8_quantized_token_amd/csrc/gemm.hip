@@ -1333,19 +1333,17 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(GemmArgs p) {
     }
   };
   // the stage's scales into the scale area of its A slot: activation scales
-  // of rows m0 .. m0+255 (16-byte pieces when the column starts on 16 bytes,
-  // else one scale per lane) and, per wave, the tile's two weight block
-  // scales; one DMA instruction each per wave (lane 0 always active)
-  const bool sa_vec = (p.sa_ld & 3) == 0 && (reinterpret_cast<uintptr_t>(p.sa) & 15) == 0;
+  // of rows m0 .. m0+255, one per lane, placed so that the four a wave needs
+  // for one half of a stage are adjacent (position 128 g + 8 r + f holds
+  // row 128 g + 16 f + r: group g, fragment f, fragment row r), and, per
+  // wave, the tile's two weight block scales; one DMA instruction each per
+  // wave (lane 0 always active)
   auto issue_scales = [&](int64_t kt, uint32_t sbase) {
     const uint8_t* col = reinterpret_cast<const uint8_t*>(p.sa + kt * p.sa_ld);
     const uint32_t dst = sbase + SA_OFF + wave * SA_LANES * 16;
-    if (sa_vec) {
-      int64_t r = m0 + (int64_t)(wave * SA_LANES + (lane < SA_LANES ? lane : 0)) * 4;
-      if (r > p.sa_ld - 4) r = p.sa_ld - 4;
-      if (lane < SA_LANES) lds_dma16_s(col, (uint32_t)(r * 4), dst);
-    } else {
-      int64_t r = m0 + (int64_t)wave * (SA_LANES * 4) + (lane < SA_LANES * 4 ? lane : 0);
+    {
+      const int pos = wave * (SA_LANES * 4) + (lane < SA_LANES * 4 ? lane : 0);
+      int64_t r = m0 + (pos & ~127) + (pos & 7) * 16 + ((pos & 127) >> 3);
       if (r > p.sa_ld - 1) r = p.sa_ld - 1;
       if (lane < SA_LANES * 4) lds_dma4_s(col, (uint32_t)(r * 4), dst);
     }
@@ -1406,11 +1404,13 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[i] = frag16(pa + (wm * WTM + (4 * H + i) * 16) * BK);
     if constexpr (SC) {
+      // this lane's four row scales of the half, adjacent (see issue_scales)
+      const uint4 w4 = *reinterpret_cast<const uint4*>(pa + SA_OFF + (wm * WTM + r16 * 8 + 4 * H) * 4);
+      const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(pa + SA_OFF + (wm * WTM + (4 * H + i) * 16 + r16) * 4);
-        if constexpr (PROMOTE) sc[i] = __uint_as_float(w) * sbv;
-        if constexpr (E8) ea[i] = (int)(w >> 23);
+        if constexpr (PROMOTE) sc[i] = __uint_as_float(w[i]) * sbv;
+        if constexpr (E8) ea[i] = (int)(w[i] >> 23);
       }
     }
     if (H == 1 && grp == 1) {  // stage s+1 complete; B(s+2) may be younger
