@@ -1384,9 +1384,14 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(GemmArgs p) {
   float sc[4] = {1.f, 1.f, 1.f, 1.f}, sbv = 1.f;  // fp32 block scales
   int ea[4] = {0, 0, 0, 0}, eb = 0;                // E8M0 exponents
 
-  // memory phase of half H of stage s
+  // memory phase of half H of stage s. Blockwise, the phase runs at raised
+  // wave priority: the other group's compute phase issues the promotion's
+  // VALU work at the same time, and the memory phases set the stage period
+  // (measured 2-3% faster at M = 4096 and 8192; channelwise unchanged, so
+  // left at the default there)
   auto mem = [&](int64_t s, auto hc) {
     constexpr int H = decltype(hc)::value;
+    if constexpr (PROMOTE) __builtin_amdgcn_s_setprio(1);
     if (H == 0) {
       if (s + 1 < nst) issue_a(s + 1);
     } else {
@@ -1413,6 +1418,7 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(GemmArgs p) {
         if constexpr (E8) ea[i] = (int)(w[i] >> 23);
       }
     }
+    if constexpr (PROMOTE) __builtin_amdgcn_s_setprio(0);
     if (H == 1 && grp == 1) {  // stage s+1 complete; B(s+2) may be younger
       if (s + 2 < nst) wait_vmcnt_lgkm0<PPB>();
       else wait_vmcnt_lgkm0<0>();
