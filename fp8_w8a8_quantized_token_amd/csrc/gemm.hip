@@ -1246,11 +1246,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_panel_kernel(GemmArgs p) {
 // after its memory phase (s,1)), when only their B(s+2) share is younger.
 // Grouped calls (masked_m, one expert per blockIdx.z) as in the panel tiles.
 // ---------------------------------------------------------------------------
-// LDS of the ping-pong tile: the ring, then (channelwise) the epilogue's
-// scale table, 256 activation and 256 weight scales.
+// LDS of the ping-pong tile: the ring, then a 2 KB table: channelwise the
+// epilogue's 256 activation and 256 weight scales, blockwise the tile's two
+// weight block scales of up to 256 K blocks.
 template <int KIND>
 constexpr int pingpong_lds_bytes() {
-  return PanelGeom<256, 256, 2, 4, KIND, 4, true>::LDS + (KIND == kChannelwise ? 2 * 256 * 4 : 0);
+  return PanelGeom<256, 256, 2, 4, KIND, 4, true>::LDS + 2 * 256 * 4;
 }
 
 __device__ __forceinline__ void phase_barrier() {
@@ -1338,6 +1339,10 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(GemmArgs p) {
   // row 128 g + 16 f + r: group g, fragment f, fragment row r), and, per
   // wave, the tile's two weight block scales; one DMA instruction each per
   // wave (lane 0 always active)
+  // blockwise, K <= 256 blocks: the tile's weight block scales of every K
+  // block are copied once, before the first panel, into a table past the
+  // ring ([block][kb], 256 apart), not with every stage
+  const bool sb_table = SC && p.K / 128 <= 256;
   auto issue_scales = [&](int64_t kt, uint32_t sbase) {
     const uint8_t* col = reinterpret_cast<const uint8_t*>(p.sa + kt * p.sa_ld);
     const uint32_t dst = sbase + SA_OFF + wave * SA_LANES * 16;
@@ -1347,6 +1352,7 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(GemmArgs p) {
       if (r > p.sa_ld - 1) r = p.sa_ld - 1;
       if (lane < SA_LANES * 4) lds_dma4_s(col, (uint32_t)(r * 4), dst);
     }
+    if (sb_table) return;
     const int64_t kb_all = p.K / 128;
     const int64_t nb_last = (p.N + 127) / 128 - 1;
     int64_t nb = (n0 >> 7) + lane;
@@ -1402,7 +1408,10 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(GemmArgs p) {
       const uint8_t* pb = lds + ((2 * s) & 3) * SLOT + (wn * WTN) * BK;
 #pragma unroll
       for (int j = 0; j < FJ; ++j) fb[j] = frag16(pb + j * 16 * BK);
-      const uint32_t sbw = SC ? *reinterpret_cast<const uint32_t*>(pa + SB_OFF + wave * 16 + ((wn * WTN) >> 7) * 4) : 0u;
+      const uint32_t sbw =
+          !SC ? 0u
+          : sb_table ? *reinterpret_cast<const uint32_t*>(lds + G::LDS + (((wn * WTN) >> 7) * 256 + kt_begin + s) * 4)
+                     : *reinterpret_cast<const uint32_t*>(pa + SB_OFF + wave * 16 + ((wn * WTN) >> 7) * 4);
       if constexpr (PROMOTE) sbv = __uint_as_float(sbw);
       if constexpr (E8) eb = (int)(sbw >> 23);
     }
@@ -1468,6 +1477,20 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(GemmArgs p) {
     }
   };
 
+  if (SC && sb_table) {
+    // wave w: weight block (n0 >> 7) + (w & 1), K blocks 64 (w >> 1) + lane
+    const int64_t kb_all = p.K / 128;
+    const int64_t nb_last = (p.N + 127) / 128 - 1;
+    int64_t nb = (n0 >> 7) + (wave & 1);
+    nb = nb < nb_last ? nb : nb_last;
+    const int64_t kb0 = (int64_t)(wave >> 1) * 64;
+    if (kb0 < kb_all) {
+      int64_t kb = kb0 + lane;
+      kb = kb < kb_all - 1 ? kb : kb_all - 1;
+      lds_dma4_s(reinterpret_cast<const uint8_t*>(p.sb), (uint32_t)((nb * kb_all + kb) * 4),
+                 lds_base + (uint32_t)G::LDS + (uint32_t)((wave & 1) * 256 + kb0) * 4);
+    }
+  }
   // channelwise: the tile's scales into the table past the ring for the
   // epilogue, before any panel, so every wait below covers them; waves 0-3
   // copy activation scales of rows m0 + 64w .., waves 4-7 weight scales of

@@ -384,6 +384,15 @@ def test_blockwise_256x256_mfma16(split_k, m, n, k, bias):
     _blockwise_case("bw16", m, n, k, config=ops.make_config("t256x256bw16", split_k), with_bias=bias)
 
 
+def test_blockwise_256x256_mfma16_weight_scale_table_limits():
+    """The tile's weight block scales come from a table filled once per tile
+    for up to 256 K blocks (K = 32768: all four 64-block pieces of it), and
+    with every stage beyond that (K = 33024)."""
+    for k in (32768, 33024):
+        _blockwise_case("bw16-kb", 300, 384, k, config=ops.make_config("t256x256bw16"), with_bias=True)
+    _blockwise_case("bw16-kb-split", 257, 256, 32768, config=ops.make_config("t256x256bw16", 3))
+
+
 def test_blockwise_256x256_mfma16_poison_and_fallbacks():
     """NaN pad rows stay out; an unaligned scale column (stride not a multiple
     of 4) runs the same tile with its scales copied one per lane; a

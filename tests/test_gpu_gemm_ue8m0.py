@@ -78,6 +78,13 @@ def test_ue8m0_block_scaled_mfma_tile(split_k, m, n, k, bias):
     _case("ue8m0-bw16", m, n, k, config=ops.make_config("t256x256bw16", split_k), with_bias=bias)
 
 
+def test_ue8m0_weight_scale_table_limits():
+    """UE8M0 exponents from the once-per-tile weight scale table (K = 32768)
+    and from the per-stage copies beyond it (K = 33024)."""
+    for k in (32768, 33024):
+        _case("ue8m0-kb", 300, 384, k, config=ops.make_config("t256x256bw16"))
+
+
 def test_ue8m0_poisoned_pad_rows_and_fallback():
     """NaN pad scales and 0x7F pad codes stay out of the outputs; an unaligned
     scale column (row alignment 1) runs the same tile with its scales copied
